@@ -1,0 +1,139 @@
+"""TEST INFRASTRUCTURE ONLY: Python entry to the fp64 CPU oracle (ssm_oracle.c).
+
+Only the tests, the package smoke check and the benchmark's CPU-baseline leg may use
+this module; the GPU library never does.  Inputs are any float arrays (the exact fp32
+values of fp32 or bf16-rounded tensors); they are widened to fp64 without rounding and
+the C definition is run on them.  See ssm_oracle.c for what is computed and where the
+pages state it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_LIBPATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
+           "-std=c11", "-Wall", "-Wextra"]
+
+
+def build(force: bool = True) -> str:
+    """Compile ssm_oracle.c into liboracle.so with gcc (fp64, no FMA contraction)."""
+    global _lib
+    if force or not os.path.exists(_LIBPATH):
+        tmp = _LIBPATH + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", *_CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIBPATH)
+        _lib = None
+    return _LIBPATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIBPATH) or os.path.getmtime(_LIBPATH) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIBPATH)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        lib.ssm_oracle_scan.argtypes = [I64, I64, I64, I64, P, P, P, P, P, P, P, P, ctypes.c_int,
+                                        P, P, ctypes.c_int]
+        lib.ssm_oracle_scan.restype = ctypes.c_int
+        lib.ssm_oracle_step.argtypes = [I64, I64, I64, P, P, P, P, P, P, P, P, P, ctypes.c_int]
+        lib.ssm_oracle_step.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(a, shape=None) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError(f"shape {a.shape} != {tuple(shape)}")
+    return a
+
+
+def _ptr(a) -> Optional[int]:
+    return None if a is None else a.ctypes.data
+
+
+def default_threads() -> int:
+    return max(1, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count() or 1)
+
+
+def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
+         threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """fp64 selective scan from h = 0.
+
+    u, delta, z: (bsz, L, Dch); B, C: (bsz, L, N); A: (Dch, N); D, delta_bias: (Dch,).
+    Returns (y (bsz, L, Dch), last_state (bsz, Dch, N)), both float64.
+    """
+    u = _f64(u)
+    bsz, L, Dch = u.shape
+    A = _f64(A)
+    N = A.shape[1]
+    delta = _f64(delta, (bsz, L, Dch))
+    A = _f64(A, (Dch, N))
+    B = _f64(B, (bsz, L, N))
+    C = _f64(C, (bsz, L, N))
+    D = _f64(D, (Dch,))
+    z = _f64(z, (bsz, L, Dch))
+    delta_bias = _f64(delta_bias, (Dch,))
+    y = np.empty((bsz, L, Dch), dtype=np.float64)
+    last = np.empty((bsz, Dch, N), dtype=np.float64)
+    rc = _load().ssm_oracle_scan(bsz, L, Dch, N, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
+                                 _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)),
+                                 _ptr(y), _ptr(last), int(threads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle scan rejected N=%d" % N)
+    return y, last
+
+
+def step(state, u, delta, A, B, C, D=None, z=None,
+         threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """fp64 single-token step.  state: (S, Dch, N); u, delta, z: (S, Dch); B, C: (S, N).
+    delta is already activated.  Returns (y (S, Dch), new_state (S, Dch, N))."""
+    st = np.array(state, dtype=np.float64, order="C", copy=True)
+    S, Dch, N = st.shape
+    u = _f64(u, (S, Dch))
+    delta = _f64(delta, (S, Dch))
+    A = _f64(A, (Dch, N))
+    B = _f64(B, (S, N))
+    C = _f64(C, (S, N))
+    D = _f64(D, (Dch,))
+    z = _f64(z, (S, Dch))
+    y = np.empty((S, Dch), dtype=np.float64)
+    rc = _load().ssm_oracle_step(S, Dch, N, _ptr(st), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                                 _ptr(C), _ptr(D), _ptr(z), _ptr(y),
+                                 int(threads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle step rejected N=%d" % N)
+    return y, st
+
+
+def scan_case(case, channels=None, threads: Optional[int] = None):
+    """Run the oracle on a generated ScanCase (from the package's input module).
+
+    channels: optional index array of channels d to evaluate (all batches); the oracle
+    then runs on those channel columns only -- channels are independent, so each
+    sampled output is exactly the full-problem value.
+    Returns (y, last_state) restricted to the sampled channels.
+    """
+    sel = slice(None) if channels is None else np.asarray(channels)
+    u = case.values("u")[:, :, sel]
+    dl = case.values("delta")[:, :, sel]
+    z = case.values("z")
+    z = None if z is None else z[:, :, sel]
+    A = case.A[sel]
+    D = None if case.Dskip is None else case.Dskip[sel]
+    bias = None if case.delta_bias is None else case.delta_bias[sel]
+    return scan(u, dl, A, case.values("B"), case.values("C"), D=D, z=z, delta_bias=bias,
+                softplus=case.softplus, threads=threads)

@@ -1,0 +1,312 @@
+"""Pins of the fp64 oracle: checks against what the pages and the mathematics fix.
+
+Every check takes a `scan` callable with the oracle's signature
+(u, delta, A, B, C, D, z, delta_bias, softplus) -> (y, last_state), so the same checks
+run on the oracle itself (test_oracle_pins.py) and on deliberately broken copies of it
+(test_oracle_mutants.py), which must each fail at least one of them.
+
+None of these re-types the oracle's own loop: each uses a different evaluation of the
+same quantity (a closed form, a convolution, an explicit sum of products, a gated RNN,
+an associative composition) or an exact invariant.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+from scipy.special import expit
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "worked_examples.json")
+
+
+def _rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    scale = max(float(np.sqrt(np.mean(b * b))), 1e-300)
+    return float(np.max(np.abs(a - b))) / scale
+
+
+def _softplus_np(x):
+    return np.logaddexp(0.0, np.asarray(x, np.float64))
+
+
+def _sym(v):
+    if isinstance(v, str):
+        return {"-ln2": -math.log(2.0), "-2ln2": -2.0 * math.log(2.0), "ln3": math.log(3.0)}[v]
+    return float(v)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# --- worked examples (tests/golden/worked_examples.json) -----------------------------
+
+def check_worked_examples(scan):
+    with open(GOLDEN) as f:
+        ex = json.load(f)["examples"]
+    ln2, ln3 = math.log(2.0), math.log(3.0)
+    for e in ex:
+        L, N = len(e["u"]), e["N"]
+        u = np.array(e["u"], np.float64).reshape(1, L, 1)
+        dl = np.array(e["delta"], np.float64).reshape(1, L, 1)
+        A = np.array([[_sym(a) for a in e["A"]]], np.float64)
+        B = np.array(e["B"], np.float64).reshape(1, L, N)
+        C = np.array(e["C"], np.float64).reshape(1, L, N)
+        D = np.array([e["D"]], np.float64)
+        z = None if e["z"] is None else np.array([_sym(v) for v in e["z"]]).reshape(1, L, 1)
+        bias = None if e["delta_bias"] is None else np.array([e["delta_bias"]], np.float64)
+        y, h = scan(u, dl, A, B, C, D, z, bias, e["softplus"])
+        if "y" in e:
+            want_y, want_h = np.array(e["y"]), np.array(e["last_state"])
+        elif "y_in_units_of_ln2" in e:
+            want_y = ln2 * np.array(e["y_in_units_of_ln2"])
+            want_h = ln2 * np.array(e["last_state_in_units_of_ln2"])
+        else:
+            k = np.array(e["k"])
+            want_y = ln3 * (0.75 * ln2 * k + 0.375 * np.array(e["u"]))
+            want_h = None
+        np.testing.assert_allclose(y.reshape(-1), want_y, rtol=e["rtol"], atol=1e-15, err_msg=e["name"])
+        if want_h is not None:
+            np.testing.assert_allclose(h.reshape(-1), want_h, rtol=e["rtol"], atol=1e-15, err_msg=e["name"])
+
+
+# --- LTI: recurrence == convolution with K_k = sum_n C_n dA_n^k delta B_n --------------
+# urworte.de "Methodische Grundlagen" (convolution form for training, recurrence for
+# inference); shakilmahmud.com section 3 (dual form, FFT convolution).
+
+def lti_inputs(seed=11, L=256, D=16, N=4):
+    from selective_state_space_32_amd import inputs
+    c = inputs.scan_case(1, L, D, N, "f32", a_init="s4d", bias=-1.0, delta_scale=1.0, lti=True,
+                         seed=seed)
+    return c
+
+
+def lti_kernel(c):
+    """Per-channel convolution kernel K[d, k] and the per-channel step size."""
+    x = c.values("delta")[0, 0, :].astype(np.float64) + c.delta_bias.astype(np.float64)
+    dt = _softplus_np(x)                                   # (D,)
+    A = c.A.astype(np.float64)                              # (D, N)
+    Bv = c.values("B")[0, 0, :].astype(np.float64)          # (N,)
+    Cv = c.values("C")[0, 0, :].astype(np.float64)
+    k = np.arange(c.L, dtype=np.float64)
+    dA = np.exp(dt[:, None] * A)                            # (D, N)
+    powk = np.power(dA[:, :, None], k[None, None, :])       # (D, N, L)
+    K = np.einsum("n,dnk->dk", Cv * Bv, powk) * dt[:, None]
+    return K
+
+
+def check_lti_bruteforce(scan):
+    c = lti_inputs()
+    u = c.values("u").astype(np.float64)[0]                 # (L, D)
+    K = lti_kernel(c)
+    L = c.L
+    want = np.zeros((L, c.D))
+    for t in range(L):
+        want[t] = np.sum(K[:, t::-1][:, : t + 1] * u[: t + 1].T, axis=1)
+    want += c.Dskip.astype(np.float64)[None, :] * u
+    y, _ = scan(c.values("u"), c.values("delta"), c.A, c.values("B"), c.values("C"), c.Dskip, None,
+                c.delta_bias, True)
+    assert _rel(y[0], want) < 1e-12, _rel(y[0], want)
+
+
+def check_lti_fft(scan):
+    c = lti_inputs(seed=12)
+    u = c.values("u").astype(np.float64)[0]
+    K = lti_kernel(c)
+    L = c.L
+    nfft = 2 * L
+    Y = np.fft.irfft(np.fft.rfft(K, nfft, axis=1) * np.fft.rfft(u.T, nfft, axis=1), nfft, axis=1)[:, :L]
+    want = Y.T + c.Dskip.astype(np.float64)[None, :] * u
+    y, _ = scan(c.values("u"), c.values("delta"), c.A, c.values("B"), c.values("C"), c.Dskip, None,
+                c.delta_bias, True)
+    assert _rel(y[0], want) < 1e-11, _rel(y[0], want)
+
+
+# --- selective (time-varying) case: explicit sum of products ----------------------------
+# h_t = sum_{s<=t} exp(A * sum_{r=s+1..t} delta_r) * delta_s * B_s * u_s  (the recurrence
+# unrolled; the decay is taken as one exponential of a summed step size, not as a
+# product of per-step factors).
+
+def check_product_form(scan, seed=5, bsz=2, L=48, D=3, N=3):
+    rng = _rng(seed)
+    u = rng.standard_normal((bsz, L, D))
+    x = 0.7 * rng.standard_normal((bsz, L, D))
+    bias = rng.uniform(-2.0, 0.5, D)
+    A = -np.exp(rng.normal(0.5, 0.6, (D, N)))
+    B = rng.standard_normal((bsz, L, N))
+    C = rng.standard_normal((bsz, L, N))
+    Dv = rng.standard_normal(D)
+    z = rng.standard_normal((bsz, L, D))
+    y, h = scan(u, x, A, B, C, Dv, z, bias, True)
+    dt = _softplus_np(x + bias[None, None, :])             # (bsz, L, D)
+    cs = np.cumsum(dt, axis=1)                              # S_t
+    want_y = np.zeros((bsz, L, D))
+    want_h = np.zeros((bsz, D, N))
+    for b in range(bsz):
+        for d in range(D):
+            for t in range(L):
+                s = np.arange(t + 1)
+                decay = np.exp(A[d][None, :] * (cs[b, t, d] - cs[b, s, d])[:, None])   # (t+1, N)
+                ht = np.sum(decay * (dt[b, s, d] * u[b, s, d])[:, None] * B[b, s, :], axis=0)
+                yt = float(C[b, t] @ ht) + Dv[d] * u[b, t, d]
+                want_y[b, t, d] = yt * z[b, t, d] * expit(z[b, t, d])
+                if t == L - 1:
+                    want_h[b, d] = ht
+    assert _rel(y, want_y) < 1e-11, _rel(y, want_y)
+    assert _rel(h, want_h) < 1e-11, _rel(h, want_h)
+
+
+# --- Theorem 1 (azimuth.plus/paper/mamba, gating section): N = 1, A = -1 -----------------
+# exp(-softplus(x)) = 1 - sigmoid(x); with B_t chosen as sigmoid(x_t)/softplus(x_t) the
+# input coefficient is g_t = sigmoid(x_t), so the scan is the gated RNN
+# h_t = (1 - g_t) h_{t-1} + g_t u_t.
+
+def check_theorem1(scan, seed=7, L=200, D=4):
+    rng = _rng(seed)
+    x = 2.0 * rng.standard_normal((1, L, D))
+    u = rng.standard_normal((1, L, D))
+    A = -np.ones((D, 1))
+    g = expit(x)
+    y_all = np.zeros((1, L, D))
+    for d in range(D):
+        # B is one vector per token shared by channels, so run one channel at a time
+        B = (g[0, :, d] / _softplus_np(x[0, :, d])).reshape(1, L, 1)
+        C = np.ones((1, L, 1))
+        yd, _ = scan(u[:, :, d:d + 1], x[:, :, d:d + 1], A[d:d + 1], B, C, None, None, None, True)
+        y_all[0, :, d] = yd[0, :, 0]
+    want = np.zeros((1, L, D))
+    h = np.zeros(D)
+    for t in range(L):
+        h = (1.0 - g[0, t]) * h + g[0, t] * u[0, t]
+        want[0, t] = h
+    assert _rel(y_all, want) < 1e-13, _rel(y_all, want)
+
+
+# --- gate limits (azimuth.plus/paper/mamba, selection section, the two gate bullets) ----
+
+def _rand_case(seed, bsz=1, L=64, D=5, N=4):
+    rng = _rng(seed)
+    return dict(u=rng.standard_normal((bsz, L, D)), x=0.5 * rng.standard_normal((bsz, L, D)) + 0.2,
+                A=-np.exp(rng.normal(1.0, 0.5, (D, N))), B=rng.standard_normal((bsz, L, N)),
+                C=rng.standard_normal((bsz, L, N)), Dv=rng.standard_normal(D),
+                z=rng.standard_normal((bsz, L, D)))
+
+
+def check_small_delta_keeps_state(scan):
+    """delta = 0 at token t (softplus off, no bias): exp(0) = 1 and the input term is 0,
+    so the state is carried unchanged -- bitwise."""
+    k = _rand_case(21)
+    t0 = 40
+    x = np.abs(k["x"])
+    x[:, t0, :] = 0.0
+    _, h_before = scan(k["u"][:, :t0], x[:, :t0], k["A"], k["B"][:, :t0], k["C"][:, :t0], k["Dv"], None, None, False)
+    _, h_at = scan(k["u"][:, :t0 + 1], x[:, :t0 + 1], k["A"], k["B"][:, :t0 + 1], k["C"][:, :t0 + 1], k["Dv"], None, None, False)
+    assert np.array_equal(h_before, h_at)
+    y, _ = scan(k["u"][:, :t0 + 1], x[:, :t0 + 1], k["A"], k["B"][:, :t0 + 1], k["C"][:, :t0 + 1], k["Dv"], None, None, False)
+    want = np.einsum("bdn,bn->bd", h_before, k["C"][:, t0]) + k["Dv"][None] * k["u"][:, t0]
+    np.testing.assert_allclose(y[:, t0], want, rtol=1e-13, atol=1e-14)
+
+
+def check_large_delta_resets_state(scan):
+    """delta * A <= -1e4 at token t: exp underflows to exactly 0, the old state is
+    forgotten and the state becomes delta*B_t*u_t; from t on the outputs equal those of
+    the sequence restarted at t -- bitwise."""
+    k = _rand_case(22)
+    t0 = 30
+    x = np.abs(k["x"])
+    x[:, t0, :] = 1e4
+    y, h = scan(k["u"], x, k["A"], k["B"], k["C"], k["Dv"], k["z"], None, False)
+    y2, h2 = scan(k["u"][:, t0:], x[:, t0:], k["A"], k["B"][:, t0:], k["C"][:, t0:], k["Dv"], k["z"][:, t0:], None, False)
+    assert np.array_equal(y[:, t0:], y2)
+    assert np.array_equal(h, h2)
+
+
+# --- linearity, causality, zero input, B = 0 / C = 0 ------------------------------------
+
+def check_linearity(scan):
+    k = _rand_case(23)
+    rng = _rng(24)
+    u2 = rng.standard_normal(k["u"].shape)
+    a, b = 0.75, -1.5
+    args = (k["x"], k["A"], k["B"], k["C"], k["Dv"], k["z"], None, True)
+    y1, h1 = scan(k["u"], *args)
+    y2, h2 = scan(u2, *args)
+    y3, h3 = scan(a * k["u"] + b * u2, *args)
+    assert _rel(y3, a * y1 + b * y2) < 1e-12
+    assert _rel(h3, a * h1 + b * h2) < 1e-12
+
+
+def check_causality(scan):
+    k = _rand_case(25)
+    t0 = 20
+    u2 = k["u"].copy()
+    u2[:, t0 + 1:] += 3.0
+    x2 = k["x"].copy()
+    x2[:, t0 + 1:] -= 1.0
+    y1, _ = scan(k["u"], k["x"], k["A"], k["B"], k["C"], k["Dv"], k["z"], None, True)
+    y2, _ = scan(u2, x2, k["A"], k["B"], k["C"], k["Dv"], k["z"], None, True)
+    assert np.array_equal(y1[:, : t0 + 1], y2[:, : t0 + 1])
+    assert not np.array_equal(y1[:, t0 + 1:], y2[:, t0 + 1:])
+
+
+def check_zero_input(scan):
+    k = _rand_case(26)
+    y, h = scan(np.zeros_like(k["u"]), k["x"], k["A"], k["B"], k["C"], k["Dv"], k["z"], None, True)
+    assert not np.any(y) and not np.any(h)
+
+
+def check_b_or_c_zero(scan):
+    """B = 0 (no input reaches the state) or C = 0 (nothing read out) leaves the gated
+    skip term alone: y = D u silu(z), silu(z) = z * sigmoid(z)."""
+    k = _rand_case(27)
+    want = k["Dv"][None, None, :] * k["u"] * k["z"] * expit(k["z"])
+    for Bz, Cz in ((np.zeros_like(k["B"]), k["C"]), (k["B"], np.zeros_like(k["C"]))):
+        y, h = scan(k["u"], k["x"], k["A"], Bz, Cz, k["Dv"], k["z"], None, True)
+        np.testing.assert_allclose(y, want, rtol=1e-14, atol=1e-15)
+
+
+# --- associativity: chunk summaries composed with (a1,b1)o(a2,b2) = (a1 a2, a2 b1 + b2) --
+# azimuth.plus/paper/mamba, hardware-aware algorithm section, parallel-scan bullet.
+
+def check_chunk_composition(scan, seed=28, L=96, chunk=17):
+    rng = _rng(seed)
+    D, N = 3, 4
+    u = rng.standard_normal((1, L, D))
+    x = 0.6 * rng.standard_normal((1, L, D))
+    A = -np.exp(rng.normal(0.3, 0.5, (D, N)))
+    B = rng.standard_normal((1, L, N))
+    C = rng.standard_normal((1, L, N))
+    _, h_full = scan(u, x, A, B, C, None, None, None, True)
+    carry_a = np.ones((D, N))
+    carry_b = np.zeros((D, N))
+    for s in range(0, L, chunk):
+        e = min(L, s + chunk)
+        _, hc = scan(u[:, s:e], x[:, s:e], A, B[:, s:e], C[:, s:e], None, None, None, True)
+        dsum = np.sum(_softplus_np(x[0, s:e]), axis=0)         # (D,)
+        a = np.exp(A * dsum[:, None])
+        carry_a, carry_b = carry_a * a, a * carry_b + hc[0]
+    assert _rel(h_full[0], carry_b) < 1e-12
+
+
+def check_softplus_values(scan):
+    """softplus through the oracle: N = 1, A = 0 (decay 1), B = C = u = 1, one token, so
+    y = delta = softplus(x).  softplus(0) = ln 2; softplus(x) -> x for large x and -> e^x
+    for very negative x."""
+    xs = np.array([0.0, 50.0, 800.0, -40.0, -800.0, 1.5])
+    want = np.array([math.log(2.0), 50.0 + math.exp(-50.0), 800.0, math.exp(-40.0), 0.0,
+                     math.log1p(math.exp(1.5))])
+    for x, w in zip(xs, want):
+        y, _ = scan(np.ones((1, 1, 1)), np.full((1, 1, 1), x), np.zeros((1, 1)), np.ones((1, 1, 1)),
+                    np.ones((1, 1, 1)), None, None, None, True)
+        assert abs(y[0, 0, 0] - w) <= 1e-15 * max(1.0, abs(w)) + 1e-300, (x, y[0, 0, 0], w)
+
+
+ALL_CHECKS = [
+    check_worked_examples, check_lti_bruteforce, check_lti_fft, check_product_form,
+    check_theorem1, check_small_delta_keeps_state, check_large_delta_resets_state,
+    check_linearity, check_causality, check_zero_input, check_b_or_c_zero,
+    check_chunk_composition, check_softplus_values,
+]

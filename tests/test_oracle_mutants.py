@@ -1,0 +1,85 @@
+"""Each plausible mistake planted in a copy of the oracle (on the CPU) must be caught by
+at least one of the pins in pins.py: a dropped term, a wrong sign, a wrong index, a
+transposed operand.  The copies are compiled into a temporary directory; the real oracle
+is never modified."""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "ssm_oracle.c")
+
+MUTANTS = {
+    "drop_skip_term": ("if (Dv) yt = yt + Dv[d] * ut;", "if (Dv) yt = yt;"),
+    "wrong_sign_of_A": ("double dA = exp(dt * A[d * N + n]);\n                h[n]",
+                        "double dA = exp(-dt * A[d * N + n]);\n                h[n]"),
+    "reversed_state_index_of_A": ("double dA = exp(dt * A[d * N + n]);\n                h[n]",
+                                  "double dA = exp(dt * A[d * N + (N - 1 - n)]);\n                h[n]"),
+    "swap_B_and_C": ("const double *Bt = B + (b * L + t) * N;\n            const double *Ct = C + (b * L + t) * N;",
+                     "const double *Bt = C + (b * L + t) * N;\n            const double *Ct = B + (b * L + t) * N;"),
+    "drop_delta_bias": ("if (delta_bias) x = x + delta_bias[d];", "if (delta_bias) x = x;"),
+    "no_softplus": ("double dt = softplus_flag ? oracle_softplus(x) : x;", "double dt = x;"),
+    "drop_gate": ("if (z) yt = yt * oracle_silu(z[i]);", "if (z) yt = yt;"),
+    "sigmoid_not_silu": ("return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
+    "previous_token_input": ("h[n] = dA * h[n] + dt * Bt[n] * ut;\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];\n            double yt = acc;\n            if (Dv) yt = yt + Dv[d] * ut;\n            if (z) yt = yt * oracle_silu(z[i]);",
+                             "h[n] = dA * h[n] + dt * Bt[n] * u[t > 0 ? i - D : i];\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];\n            double yt = acc;\n            if (Dv) yt = yt + Dv[d] * ut;\n            if (z) yt = yt * oracle_silu(z[i]);"),
+    "drop_delta_in_input_term": ("h[n] = dA * h[n] + dt * Bt[n] * ut;\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];\n            double yt = acc;\n            if (Dv) yt = yt + Dv[d] * ut;\n            if (z) yt = yt * oracle_silu(z[i]);",
+                                 "h[n] = dA * h[n] + Bt[n] * ut;\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];\n            double yt = acc;\n            if (Dv) yt = yt + Dv[d] * ut;\n            if (z) yt = yt * oracle_silu(z[i]);"),
+    "readout_before_update": ("double dA = exp(dt * A[d * N + n]);\n                h[n] = dA * h[n] + dt * Bt[n] * ut;\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];",
+                              "double dA = exp(dt * A[d * N + n]);\n                h[n] = h[n];\n                (void)dA;\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];\n            for (int64_t n = 0; n < N; ++n) h[n] = exp(dt * A[d * N + n]) * h[n] + dt * Bt[n] * ut;"),
+    "last_state_wrong_index": ("last_state[(b * D + d) * N + n] = h[n];", "last_state[(b * D + d) * N + n] = h[0];"),
+    "softplus_wrong_branch": ("if (x > 0.0) return x + log1p(exp(-x));", "if (x > 0.0) return x + log1p(exp(x));"),
+    "decay_squared": ("h[n] = dA * h[n] + dt * Bt[n] * ut;\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];\n            double yt = acc;\n            if (Dv) yt = yt + Dv[d] * ut;\n            if (z) yt = yt * oracle_silu(z[i]);",
+                      "h[n] = dA * dA * h[n] + dt * Bt[n] * ut;\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];\n            double yt = acc;\n            if (Dv) yt = yt + Dv[d] * ut;\n            if (z) yt = yt * oracle_silu(z[i]);"),
+}
+
+
+def _build_mutant(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) >= 1, f"mutation {name} does not apply"
+    text = text.replace(old, new, 1)
+    src = tmp_path / f"{name}.c"
+    src.write_text(text)
+    so = tmp_path / f"{name}.so"
+    subprocess.run(["gcc", "-O1", "-ffp-contract=off", "-fPIC", "-shared", "-std=c11", str(src),
+                    "-o", str(so), "-lm"], check=True)
+    lib = ctypes.CDLL(str(so))
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    lib.ssm_oracle_scan.argtypes = [I64, I64, I64, I64, P, P, P, P, P, P, P, P, ctypes.c_int, P, P, ctypes.c_int]
+    lib.ssm_oracle_scan.restype = ctypes.c_int
+
+    def f64(a):
+        return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+    def ptr(a):
+        return None if a is None else a.ctypes.data
+
+    def scan(u, x, A, B, C, D, z, bias, softplus):
+        u, x, A, B, C, D, z, bias = map(f64, (u, x, A, B, C, D, z, bias))
+        bsz, L, Dch = u.shape
+        N = A.shape[1]
+        y = np.empty((bsz, L, Dch))
+        h = np.empty((bsz, Dch, N))
+        lib.ssm_oracle_scan(bsz, L, Dch, N, ptr(u), ptr(x), ptr(A), ptr(B), ptr(C), ptr(D), ptr(z),
+                            ptr(bias), int(bool(softplus)), ptr(y), ptr(h), 1)
+        return y, h
+    return scan
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(tmp_path, name):
+    old, new = MUTANTS[name]
+    scan = _build_mutant(tmp_path, name, old, new)
+    caught = []
+    with np.errstate(all="ignore"):
+        for check in pins.ALL_CHECKS:
+            try:
+                check(scan)
+            except AssertionError:
+                caught.append(check.__name__)
+    assert caught, f"mutant {name} passed every pin"
