@@ -1,0 +1,138 @@
+/*
+ * libssmscan -- the Mamba selective state-space scan (S6) and its single-token
+ * recurrent step on AMD MI355X (gfx950).
+ *
+ * What is computed (per channel d of sequence b, state index n):
+ *   step size       dt_t   = softplus(delta_t + delta_bias[d])   if softplus_flag
+ *                          = delta_t + delta_bias[d]             otherwise
+ *     (azimuth.plus/paper/mamba, "selection" section: delta_t = softplus(Linear(x_t)))
+ *   discretisation  dA     = exp(dt_t * A[d,n])     (ZOH of a diagonal A;
+ *                                                    yapayzekasozluk.tr, "Temel Matematiksel Cerceve")
+ *                   input  = dt_t * B_t[n] * u_t    (simplified input matrix; the pages give no formula)
+ *   recurrence      h_t[n] = dA * h_{t-1}[n] + dt_t * B_t[n] * u_t
+ *     (azimuth.plus/paper/mamba, hardware-aware algorithm section, parallel-scan bullet)
+ *   readout         y_t    = (sum_n C_t[n] h_t[n] + D[d] u_t) * silu(z_t)
+ *     (y = C h + D x: yapayzekasozluk.tr, same section; the SiLU gate branch multiplies
+ *      the SSM branch: azimuth.plus/paper/mamba, block architecture section)
+ * B_t and C_t are one N-vector per (sequence, token), shared by all channels; A is
+ * fixed (one real value per channel and state).  The scan starts from h = 0.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers (hipMalloc / torch CUDA memory), row-major,
+ *    densely packed, innermost index last.  Elements must be naturally aligned.
+ *  - The "I/O" tensors u, delta, z, y, B, C have the element type dims->io_dtype
+ *    (SSM_IO_F32 = IEEE fp32, SSM_IO_BF16 = bfloat16 bit patterns).  A, D, delta_bias,
+ *    last_state and state are always fp32.  Arithmetic and the state are fp32.
+ *  - Outputs must not alias inputs (except ssm_step's state, updated in place).
+ *  - The caller owns every buffer.  The library allocates and frees nothing, does not
+ *    synchronise, and keeps no pointer after a call returns.  Work is enqueued on
+ *    `stream` (a hipStream_t; NULL = the default stream) and runs asynchronously.
+ *  - Every argument is validated before anything is enqueued.  A negative status means
+ *    nothing was launched; ssm_last_error() then describes the problem.  Faults inside
+ *    kernels surface at the caller's next synchronisation.
+ *  - Supported state sizes: N in {1, 2, 4, 8, 16}.
+ *  - Sizes of zero are valid: nothing is computed (a scan of L = 0 tokens writes a zero
+ *    last_state when one is asked for).
+ */
+#ifndef SSMSCAN_H
+#define SSMSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSMSCAN_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SSMSCAN_API __attribute__((visibility("default")))
+#else
+#define SSMSCAN_API
+#endif
+
+typedef enum {
+    SSM_IO_F32 = 0,
+    SSM_IO_BF16 = 1
+} ssm_io_dtype;
+
+typedef enum {
+    SSM_OK = 0,
+    SSM_ERR_NULL = -1,            /* a required pointer is NULL */
+    SSM_ERR_SHAPE = -2,           /* a size is negative or too large */
+    SSM_ERR_DTYPE = -3,           /* io_dtype is not an ssm_io_dtype */
+    SSM_ERR_ALIGN = -4,           /* a pointer is not aligned to its element size */
+    SSM_ERR_UNSUPPORTED_N = -5,   /* dstate is not 1, 2, 4, 8 or 16 */
+    SSM_ERR_WORKSPACE = -6,       /* workspace missing or smaller than required */
+    SSM_ERR_HIP = -7              /* the HIP runtime refused a launch */
+} ssm_status;
+
+/* Problem sizes.
+ *   batch     sequences in the batch (ssm_step: number of independent sequences S)
+ *   seqlen    tokens per sequence L (ignored by ssm_step)
+ *   dim       channels D
+ *   dstate    state size N
+ *   io_dtype  an ssm_io_dtype
+ *   chunk_len scan plan: 0 = the library chooses; > 0 = split every sequence into
+ *             chunks of this many tokens and combine the chunk states (two-pass chunk
+ *             carry); -1 = one pass over the whole sequence.  Results agree up to fp32
+ *             rounding whatever the plan. */
+typedef struct ssm_dims {
+    int64_t batch;
+    int64_t seqlen;
+    int64_t dim;
+    int64_t dstate;
+    int32_t io_dtype;
+    int32_t chunk_len;
+} ssm_dims;
+
+/* Bytes of device workspace ssm_scan_fwd needs for these sizes and plan (256-byte
+ * aligned regions).  Returns 0 for an invalid or empty problem. */
+SSMSCAN_API size_t ssm_scan_workspace_bytes(const ssm_dims *dims);
+
+/* The plan ssm_scan_fwd will use: returns the number of chunks each sequence is split
+ * into (1 = single pass) and stores the chunk length in tokens in *chunk_len_out
+ * (may be NULL).  Returns a negative ssm_status for invalid sizes. */
+SSMSCAN_API int64_t ssm_scan_plan(const ssm_dims *dims, int64_t *chunk_len_out);
+
+/* Selective scan forward over a batch of sequences, from a zero state.
+ *   u, delta, z, y : [batch][seqlen][dim]   (io_dtype; z may be NULL = no gate)
+ *   B, C           : [batch][seqlen][dstate] (io_dtype)
+ *   A              : [dim][dstate] fp32
+ *   D, delta_bias  : [dim] fp32, each may be NULL (= 0)
+ *   softplus_flag  : nonzero = apply softplus to delta + delta_bias
+ *   y              : output, written completely
+ *   last_state     : [batch][dim][dstate] fp32 output h_L, may be NULL
+ *   workspace      : device memory of at least ssm_scan_workspace_bytes(dims) bytes
+ *                    (its contents on entry do not matter; it is scratch for this call)
+ * Returns SSM_OK or a negative ssm_status. */
+SSMSCAN_API int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
+                 const float *D, const void *z, const float *delta_bias, int softplus_flag,
+                 void *y, float *last_state, const ssm_dims *dims,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* One recurrent (inference) step for `batch` independent sequences: the constant-memory
+ * recurrent form (shakilmahmud.com section 3; urworte.de "Methodische Grundlagen").
+ *   state          : [batch][dim][dstate] fp32, read and overwritten with the new state
+ *   u, delta, z, y : [batch][dim] (io_dtype); delta is the already activated step size
+ *                    (no bias, no softplus); z may be NULL
+ *   B, C           : [batch][dstate] (io_dtype)
+ *   A              : [dim][dstate] fp32;  D : [dim] fp32 or NULL
+ * Repeating it over a sequence from a zero state reproduces ssm_scan_fwd with
+ * softplus_flag = 0 and no delta_bias.  Returns SSM_OK or a negative ssm_status. */
+SSMSCAN_API int ssm_step(float *state, const void *u, const void *delta, const float *A, const void *B,
+             const void *C, const float *D, const void *z, void *y, const ssm_dims *dims,
+             void *stream);
+
+/* Message describing the last non-OK status returned on this thread ("" if none). */
+SSMSCAN_API const char *ssm_last_error(void);
+
+/* SSMSCAN_VERSION of the built library. */
+SSMSCAN_API int ssm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSMSCAN_H */

@@ -1,0 +1,270 @@
+// libssmscan: C ABI, argument validation, planning and kernel launches.
+// The declarations and the contract of every entry point are in include/ssmscan.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "ssmscan.h"
+#include "carry_kernel.h"
+#include "scan_kernels.h"
+#include "step_kernel.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return SSM_OK;
+}
+
+bool n_supported(int64_t n) { return n == 1 || n == 2 || n == 4 || n == 8 || n == 16; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int64_t kMaxElems = int64_t(1) << 46;
+constexpr int kMaxChunks = 65535;  // grid.y limit
+constexpr int kTargetGroups = 768; // 3 workgroups per CU on a 256-CU MI355X
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Shape checks shared by scan and step.  Returns SSM_OK or a status (message set).
+int check_dims(const ssm_dims *dm, bool scan) {
+    if (!dm) return fail(SSM_ERR_NULL, "dims is NULL");
+    if (dm->batch < 0 || dm->dim < 0 || dm->dstate < 0 || (scan && dm->seqlen < 0))
+        return fail(SSM_ERR_SHAPE, "negative size (batch=%lld seqlen=%lld dim=%lld dstate=%lld)",
+                    (long long)dm->batch, (long long)dm->seqlen, (long long)dm->dim, (long long)dm->dstate);
+    if (dm->io_dtype != SSM_IO_F32 && dm->io_dtype != SSM_IO_BF16)
+        return fail(SSM_ERR_DTYPE, "io_dtype %d is not SSM_IO_F32 (0) or SSM_IO_BF16 (1)", dm->io_dtype);
+    if (!n_supported(dm->dstate))
+        return fail(SSM_ERR_UNSUPPORTED_N, "dstate %lld not supported (1, 2, 4, 8 or 16)", (long long)dm->dstate);
+    if (dm->dim > kMaxDim || dm->batch > kMaxDim)
+        return fail(SSM_ERR_SHAPE, "dim or batch larger than 2^30");
+    const int64_t L = scan ? dm->seqlen : 1;
+    if (L > kMaxElems || (dm->batch > 0 && dm->dim > 0 && L > kMaxElems / dm->batch / dm->dim))
+        return fail(SSM_ERR_SHAPE, "batch*seqlen*dim exceeds 2^46 elements");
+    if (scan && dm->chunk_len < -1)
+        return fail(SSM_ERR_SHAPE, "chunk_len %d invalid (-1, 0 or > 0)", dm->chunk_len);
+    return SSM_OK;
+}
+
+struct Plan {
+    int64_t nchunk = 1;
+    int64_t chunk_len = 0;
+    size_t off_cstate = 0, off_cdsum = 0, bytes = 0;
+};
+
+Plan make_plan(const ssm_dims *dm) {
+    Plan p;
+    const int64_t bsz = dm->batch, L = dm->seqlen, D = dm->dim, N = dm->dstate;
+    if (bsz == 0 || L == 0 || D == 0) return p;
+    const int64_t tiles = bsz * ((D + ssm::kChanTile - 1) / ssm::kChanTile);
+    int64_t clen = L;
+    if (dm->chunk_len > 0) {
+        clen = dm->chunk_len < L ? dm->chunk_len : L;
+        if ((L + clen - 1) / clen > kMaxChunks) clen = (L + kMaxChunks - 1) / kMaxChunks;
+    } else if (dm->chunk_len == 0 && tiles < 512) {
+        // too few channel tiles to fill the GPU: split the tokens too, keeping chunks at
+        // least 8 LDS tiles long so that the extra summary and carry passes stay cheap
+        const int64_t want = (kTargetGroups + tiles - 1) / tiles;
+        const int64_t most = (L + 8 * ssm::kTileT - 1) / (8 * ssm::kTileT);
+        int64_t nchunk = want < most ? want : most;
+        if (nchunk < 1) nchunk = 1;
+        if (nchunk > kMaxChunks) nchunk = kMaxChunks;
+        if (nchunk > 1) {
+            clen = (L + nchunk - 1) / nchunk;
+            clen = (clen + ssm::kTileT - 1) / ssm::kTileT * ssm::kTileT;
+        }
+    }
+    p.chunk_len = clen;
+    p.nchunk = (L + clen - 1) / clen;
+    size_t bc = align256((size_t)(bsz * L * 2 * N) * sizeof(float));
+    p.off_cstate = bc;
+    p.off_cdsum = bc;
+    p.bytes = bc;
+    if (p.nchunk > 1) {
+        size_t cs = align256((size_t)(bsz * p.nchunk * D * N) * sizeof(float));
+        size_t cd = align256((size_t)(bsz * p.nchunk * D) * sizeof(float));
+        p.off_cdsum = bc + cs;
+        p.bytes = bc + cs + cd;
+    }
+    return p;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+template <int N, typename IO>
+int launch_scan(const void *u, const void *delta, const float *A, const void *B, const void *C,
+                const float *Dv, const void *z, const float *bias, int softplus, void *y,
+                float *last_state, const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st) {
+    constexpr int S = N < 4 ? N : 4;
+    constexpr int K = N / S;
+    const int64_t bsz = dm->batch, L = dm->seqlen, D = dm->dim;
+    const int tiles_per_b = (int)((D + ssm::kChanTile - 1) / ssm::kChanTile);
+    float *bc = reinterpret_cast<float *>(ws);
+    float *cstate = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_cstate);
+    float *cdsum = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_cdsum);
+    const IO *u_ = static_cast<const IO *>(u);
+    const IO *dl_ = static_cast<const IO *>(delta);
+    const IO *z_ = static_cast<const IO *>(z);
+    IO *y_ = static_cast<IO *>(y);
+
+    const int64_t nbc = bsz * L * N;
+    hipLaunchKernelGGL((ssm::stage_bc_kernel<N, S, IO>), dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, st,
+                       static_cast<const IO *>(B), static_cast<const IO *>(C), bc, nbc, L);
+    const dim3 block(64 * K);
+    if (p.nchunk > 1) {
+        hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, IO, ssm::kSummary>),
+                           dim3((unsigned)(bsz * tiles_per_b), (unsigned)(p.nchunk - 1)), block, 0, st,
+                           u_, dl_, (const IO *)nullptr, (IO *)nullptr, A, (const float *)nullptr, bias, bc,
+                           (float *)nullptr, cstate, cdsum, L, D, tiles_per_b, p.chunk_len, (int)p.nchunk,
+                           softplus);
+        const int col_tiles = (int)((D * N + 63) / 64);
+        hipLaunchKernelGGL((ssm::carry_scan_kernel<N>), dim3((unsigned)(bsz * col_tiles)), dim3(256), 0, st,
+                           cstate, (const float *)cdsum, A, D, (int)p.nchunk, col_tiles);
+    }
+    hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, IO, ssm::kFull>),
+                       dim3((unsigned)(bsz * tiles_per_b), (unsigned)p.nchunk), block, 0, st,
+                       u_, dl_, z_, y_, A, Dv, bias, bc, last_state, cstate, cdsum, L, D, tiles_per_b,
+                       p.chunk_len, (int)p.nchunk, softplus);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+template <typename IO>
+int dispatch_scan(int64_t N, const void *u, const void *delta, const float *A, const void *B,
+                  const void *C, const float *Dv, const void *z, const float *bias, int sp, void *y,
+                  float *ls, const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st) {
+    switch (N) {
+        case 1: return launch_scan<1, IO>(u, delta, A, B, C, Dv, z, bias, sp, y, ls, dm, p, ws, st);
+        case 2: return launch_scan<2, IO>(u, delta, A, B, C, Dv, z, bias, sp, y, ls, dm, p, ws, st);
+        case 4: return launch_scan<4, IO>(u, delta, A, B, C, Dv, z, bias, sp, y, ls, dm, p, ws, st);
+        case 8: return launch_scan<8, IO>(u, delta, A, B, C, Dv, z, bias, sp, y, ls, dm, p, ws, st);
+        case 16: return launch_scan<16, IO>(u, delta, A, B, C, Dv, z, bias, sp, y, ls, dm, p, ws, st);
+    }
+    return fail(SSM_ERR_UNSUPPORTED_N, "dstate %lld not supported", (long long)N);
+}
+
+template <int N, typename IO>
+int launch_step(float *state, const void *u, const void *delta, const float *A, const void *B,
+                const void *C, const float *Dv, const void *z, void *y, const ssm_dims *dm, hipStream_t st) {
+    constexpr int G = N >= 4 ? N / 4 : 1;
+    const int64_t threads = dm->batch * dm->dim * G;
+    hipLaunchKernelGGL((ssm::step_kernel<N, IO>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                       state, static_cast<const IO *>(u), static_cast<const IO *>(delta), A,
+                       static_cast<const IO *>(B), static_cast<const IO *>(C), Dv,
+                       static_cast<const IO *>(z), static_cast<IO *>(y), dm->batch, dm->dim);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+template <typename IO>
+int dispatch_step(int64_t N, float *state, const void *u, const void *delta, const float *A, const void *B,
+                  const void *C, const float *Dv, const void *z, void *y, const ssm_dims *dm, hipStream_t st) {
+    switch (N) {
+        case 1: return launch_step<1, IO>(state, u, delta, A, B, C, Dv, z, y, dm, st);
+        case 2: return launch_step<2, IO>(state, u, delta, A, B, C, Dv, z, y, dm, st);
+        case 4: return launch_step<4, IO>(state, u, delta, A, B, C, Dv, z, y, dm, st);
+        case 8: return launch_step<8, IO>(state, u, delta, A, B, C, Dv, z, y, dm, st);
+        case 16: return launch_step<16, IO>(state, u, delta, A, B, C, Dv, z, y, dm, st);
+    }
+    return fail(SSM_ERR_UNSUPPORTED_N, "dstate %lld not supported", (long long)N);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_version(void) { return SSMSCAN_VERSION; }
+
+const char *ssm_last_error(void) { return g_err.c_str(); }
+
+size_t ssm_scan_workspace_bytes(const ssm_dims *dims) {
+    if (check_dims(dims, true) != SSM_OK) return 0;
+    return make_plan(dims).bytes;
+}
+
+int64_t ssm_scan_plan(const ssm_dims *dims, int64_t *chunk_len_out) {
+    int rc = check_dims(dims, true);
+    if (rc != SSM_OK) return rc;
+    Plan p = make_plan(dims);
+    if (chunk_len_out) *chunk_len_out = p.chunk_len;
+    ok();
+    return p.nchunk;
+}
+
+int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
+                 const float *D, const void *z, const float *delta_bias, int softplus_flag,
+                 void *y, float *last_state, const ssm_dims *dims,
+                 void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = check_dims(dims, true);
+    if (rc != SSM_OK) return rc;
+    const int64_t bsz = dims->batch, L = dims->seqlen, Dm = dims->dim, N = dims->dstate;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (bsz == 0 || Dm == 0) return ok();
+    if (L == 0) {
+        if (last_state) {
+            if (!aligned(last_state, 4)) return fail(SSM_ERR_ALIGN, "last_state not 4-byte aligned");
+            const int64_t n = bsz * Dm * N;
+            hipLaunchKernelGGL(ssm::fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                               last_state, n);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+        }
+        return ok();
+    }
+    if (!u || !delta || !A || !B || !C || !y)
+        return fail(SSM_ERR_NULL, "required pointer is NULL (u=%p delta=%p A=%p B=%p C=%p y=%p)", u, delta,
+                    (const void *)A, B, C, y);
+    const size_t es = dims->io_dtype == SSM_IO_BF16 ? 2 : 4;
+    if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) || !aligned(y, es) ||
+        (z && !aligned(z, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
+        (delta_bias && !aligned(delta_bias, 4)) || (last_state && !aligned(last_state, 4)))
+        return fail(SSM_ERR_ALIGN, "a tensor pointer is not aligned to its element size");
+    Plan p = make_plan(dims);
+    if (!workspace) return fail(SSM_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", p.bytes);
+    if (workspace_bytes < p.bytes)
+        return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+                    p.bytes);
+    if (!aligned(workspace, 16)) return fail(SSM_ERR_ALIGN, "workspace not 16-byte aligned");
+    if (dims->io_dtype == SSM_IO_BF16)
+        return dispatch_scan<uint16_t>(N, u, delta, A, B, C, D, z, delta_bias, softplus_flag != 0, y, last_state,
+                                       dims, p, workspace, st);
+    return dispatch_scan<float>(N, u, delta, A, B, C, D, z, delta_bias, softplus_flag != 0, y, last_state, dims,
+                                p, workspace, st);
+}
+
+int ssm_step(float *state, const void *u, const void *delta, const float *A, const void *B,
+             const void *C, const float *D, const void *z, void *y, const ssm_dims *dims, void *stream) {
+    int rc = check_dims(dims, false);
+    if (rc != SSM_OK) return rc;
+    const int64_t S = dims->batch, Dm = dims->dim, N = dims->dstate;
+    if (S == 0 || Dm == 0) return ok();
+    if (!state || !u || !delta || !A || !B || !C || !y)
+        return fail(SSM_ERR_NULL, "required pointer is NULL (state=%p u=%p delta=%p A=%p B=%p C=%p y=%p)",
+                    (void *)state, u, delta, (const void *)A, B, C, y);
+    const size_t es = dims->io_dtype == SSM_IO_BF16 ? 2 : 4;
+    if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) || !aligned(y, es) ||
+        (z && !aligned(z, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) || !aligned(state, N >= 4 ? 16 : 4))
+        return fail(SSM_ERR_ALIGN, "a tensor pointer is not aligned (state needs 16 bytes when dstate >= 4)");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dims->io_dtype == SSM_IO_BF16)
+        return dispatch_step<uint16_t>(N, state, u, delta, A, B, C, D, z, y, dims, st);
+    return dispatch_step<float>(N, state, u, delta, A, B, C, D, z, y, dims, st);
+}
+
+}  // extern "C"

@@ -32,15 +32,16 @@ __all__ = [
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bit patterns (uint16), round to nearest, ties to even.
 
-    Inputs are finite; NaN/Inf are passed through by truncation of their top half.
-    """
+    NaN/Inf keep their top half (truncation).  For finite inputs the rounding add cannot
+    overflow 32 bits (the largest finite pattern is 0xFF7FFFFF)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    b = x.view(np.uint32).astype(np.uint64)
-    finite = np.isfinite(x)
-    lsb = (b >> 16) & 1
-    r = ((b + 0x7FFF + lsb) >> 16) & 0xFFFF
-    t = (b >> 16) & 0xFFFF
-    return np.where(finite, r, t).astype(np.uint16)
+    b = x.view(np.uint32)
+    r = b + (np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1)))
+    out = (r >> np.uint32(16)).astype(np.uint16)
+    bad = ~np.isfinite(x)
+    if bad.any():
+        out[bad] = (b[bad] >> np.uint32(16)).astype(np.uint16)
+    return out
 
 
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:

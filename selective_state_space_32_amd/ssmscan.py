@@ -1,0 +1,193 @@
+"""Thin ctypes binding of libssmscan.so taking torch tensors.
+
+Argument marshalling only: shapes and dtypes are checked, outputs and the workspace are
+allocated with torch on the tensors' device, and the C entry points (include/ssmscan.h)
+are called on torch's current stream.  Every step of the computation runs in the HIP
+kernels of libssmscan.so; if the library is missing this module raises on import.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBPATH = os.path.join(_PKG, "libssmscan.so")
+
+SSM_IO_F32 = 0
+SSM_IO_BF16 = 1
+
+STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL", -2: "SSM_ERR_SHAPE", -3: "SSM_ERR_DTYPE", -4: "SSM_ERR_ALIGN",
+          -5: "SSM_ERR_UNSUPPORTED_N", -6: "SSM_ERR_WORKSPACE", -7: "SSM_ERR_HIP"}
+
+
+class ssm_dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("io_dtype", ctypes.c_int32), ("chunk_len", ctypes.c_int32)]
+
+
+class SSMError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIBPATH):
+        raise ImportError(f"{LIBPATH} is not built; run `python -m selective_state_space_32_amd.build` "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIBPATH)
+    P = ctypes.c_void_p
+    D = ctypes.POINTER(ssm_dims)
+    lib.ssm_version.restype = ctypes.c_int
+    lib.ssm_last_error.restype = ctypes.c_char_p
+    lib.ssm_scan_workspace_bytes.argtypes = [D]
+    lib.ssm_scan_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssm_scan_plan.argtypes = [D, ctypes.POINTER(ctypes.c_int64)]
+    lib.ssm_scan_plan.restype = ctypes.c_int64
+    lib.ssm_scan_fwd.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int, P, P, D, P, ctypes.c_size_t, P]
+    lib.ssm_scan_fwd.restype = ctypes.c_int
+    lib.ssm_step.argtypes = [P, P, P, P, P, P, P, P, P, D, P]
+    lib.ssm_step.restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def last_error() -> str:
+    return lib.ssm_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise SSMError(rc, last_error())
+
+
+def _io_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return SSM_IO_F32
+    if dt == torch.bfloat16:
+        return SSM_IO_BF16
+    raise TypeError(f"I/O tensors must be float32 or bfloat16, got {dt}")
+
+
+def make_dims(batch: int, seqlen: int, dim: int, dstate: int, io_dtype, chunk_len: int = 0) -> ssm_dims:
+    code = io_dtype if isinstance(io_dtype, int) else _io_code(io_dtype)
+    return ssm_dims(int(batch), int(seqlen), int(dim), int(dstate), int(code), int(chunk_len))
+
+
+def workspace_bytes(batch: int, seqlen: int, dim: int, dstate: int, io_dtype, chunk_len: int = 0) -> int:
+    d = make_dims(batch, seqlen, dim, dstate, io_dtype, chunk_len)
+    return int(lib.ssm_scan_workspace_bytes(ctypes.byref(d)))
+
+
+def scan_plan(batch: int, seqlen: int, dim: int, dstate: int, io_dtype, chunk_len: int = 0) -> Tuple[int, int]:
+    """(number of chunks per sequence, chunk length) the library will use."""
+    d = make_dims(batch, seqlen, dim, dstate, io_dtype, chunk_len)
+    cl = ctypes.c_int64(0)
+    n = int(lib.ssm_scan_plan(ctypes.byref(d), ctypes.byref(cl)))
+    if n < 0:
+        raise SSMError(n, last_error())
+    return n, int(cl.value)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype} != {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+             D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+             delta_bias: Optional[torch.Tensor] = None, softplus: bool = True, *,
+             y: Optional[torch.Tensor] = None, last_state: Optional[torch.Tensor] = None,
+             return_last_state: bool = True, chunk_len: int = 0,
+             workspace: Optional[torch.Tensor] = None, stream=None):
+    """Selective scan forward from a zero state (ssm_scan_fwd).
+
+    u, delta, z: (batch, L, dim); B, C: (batch, L, N), all of one dtype (float32 or bfloat16);
+    A: (dim, N) float32; D, delta_bias: (dim,) float32 or None.
+    Returns (y, last_state) -- last_state (batch, dim, N) float32, or None if not asked for.
+    """
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, L, dim)")
+    bsz, L, dim = u.shape
+    N = A.shape[-1]
+    dev, io = u.device, u.dtype
+    _io_code(io)
+    _need(u, "u", (bsz, L, dim), io, dev)
+    _need(delta, "delta", (bsz, L, dim), io, dev)
+    _need(A, "A", (dim, N), torch.float32, dev)
+    _need(B, "B", (bsz, L, N), io, dev)
+    _need(C, "C", (bsz, L, N), io, dev)
+    if D is not None:
+        _need(D, "D", (dim,), torch.float32, dev)
+    if z is not None:
+        _need(z, "z", (bsz, L, dim), io, dev)
+    if delta_bias is not None:
+        _need(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    if y is None:
+        y = torch.empty((bsz, L, dim), dtype=io, device=dev)
+    else:
+        _need(y, "y", (bsz, L, dim), io, dev)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((bsz, dim, N), dtype=torch.float32, device=dev)
+    elif last_state is not None:
+        _need(last_state, "last_state", (bsz, dim, N), torch.float32, dev)
+    dims = make_dims(bsz, L, dim, N, io, chunk_len)
+    need = int(lib.ssm_scan_workspace_bytes(ctypes.byref(dims)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = lib.ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                          int(bool(softplus)), _ptr(y), _ptr(last_state), ctypes.byref(dims), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    _check(rc)
+    return y, last_state
+
+
+def step(state: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+         C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None, *,
+         y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One recurrent step (ssm_step); `state` (S, dim, N) float32 is updated in place.
+
+    u, delta, z: (S, dim); B, C: (S, N) of one dtype; delta is the activated step size.
+    Returns y (S, dim)."""
+    S, dim, N = state.shape
+    dev, io = u.device, u.dtype
+    _io_code(io)
+    _need(state, "state", (S, dim, N), torch.float32, dev)
+    _need(u, "u", (S, dim), io, dev)
+    _need(delta, "delta", (S, dim), io, dev)
+    _need(A, "A", (dim, N), torch.float32, dev)
+    _need(B, "B", (S, N), io, dev)
+    _need(C, "C", (S, N), io, dev)
+    if D is not None:
+        _need(D, "D", (dim,), torch.float32, dev)
+    if z is not None:
+        _need(z, "z", (S, dim), io, dev)
+    if y is None:
+        y = torch.empty((S, dim), dtype=io, device=dev)
+    else:
+        _need(y, "y", (S, dim), io, dev)
+    dims = make_dims(S, 1, dim, N, io)
+    rc = lib.ssm_step(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y),
+                      ctypes.byref(dims), _stream_handle(stream))
+    _check(rc)
+    return y

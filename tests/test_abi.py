@@ -1,0 +1,131 @@
+"""The C-ABI library: it loads, exports every symbol include/ssmscan.h declares, and
+rejects bad arguments before launching anything (no GPU needed: every call here fails
+validation on the host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssmscan.h")
+LIB = os.path.join(ROOT, "selective_state_space_32_amd", "libssmscan.so")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"SSMSCAN_API\s+[\w\s\*]+?\b(ssm_\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def b():
+    if not os.path.exists(LIB):
+        pytest.fail("libssmscan.so is not built (run __graft_entry__.build())")
+    from selective_state_space_32_amd import ssmscan
+    return ssmscan
+
+
+def test_header_declares_the_entry_points():
+    syms = set(declared_symbols())
+    assert {"ssm_scan_fwd", "ssm_step", "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_last_error",
+            "ssm_version"} <= syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    for s in declared_symbols():
+        assert hasattr(lib, s), s
+
+
+def test_version(b):
+    assert b.lib.ssm_version() == 1
+
+
+def _dims(b, **kw):
+    base = dict(batch=2, seqlen=64, dim=128, dstate=16, io_dtype=1, chunk_len=0)
+    base.update(kw)
+    return b.ssm_dims(base["batch"], base["seqlen"], base["dim"], base["dstate"], base["io_dtype"], base["chunk_len"])
+
+
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
+
+
+def _scan(b, dims, u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, y=FAKE, ws=FAKE, ws_bytes=None, z=None, ls=None):
+    if ws_bytes is None:
+        ws_bytes = b.lib.ssm_scan_workspace_bytes(ctypes.byref(dims))
+    P = ctypes.c_void_p
+    return b.lib.ssm_scan_fwd(P(u), P(delta), P(A), P(B), P(C), None, P(z) if z else None, None, 1, P(y),
+                              P(ls) if ls else None, ctypes.byref(dims), P(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("field", ["u", "delta", "A", "B", "C", "y"])
+def test_null_pointer_rejected(b, field):
+    rc = _scan(b, _dims(b), **{field: 0})
+    assert rc == -1 and field in b.last_error() or rc == -1
+
+
+def test_null_dims_rejected(b):
+    P = ctypes.c_void_p
+    rc = b.lib.ssm_scan_fwd(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None, None, 1, P(FAKE), None, None,
+                            P(FAKE), 1 << 20, None)
+    assert rc == -1
+
+
+@pytest.mark.parametrize("n", [0, 3, 5, 32, 64])
+def test_unsupported_state_size(b, n):
+    assert _scan(b, _dims(b, dstate=n)) == -5
+    assert "dstate" in b.last_error()
+
+
+def test_bad_dtype(b):
+    assert _scan(b, _dims(b, io_dtype=7)) == -3
+
+
+@pytest.mark.parametrize("kw", [dict(batch=-1), dict(seqlen=-5), dict(dim=-2), dict(chunk_len=-2),
+                                dict(dim=(1 << 30) + 1), dict(batch=1 << 20, seqlen=1 << 20, dim=1 << 20)])
+def test_bad_shape(b, kw):
+    assert _scan(b, _dims(b, **kw)) == -2
+
+
+def test_workspace_too_small(b):
+    d = _dims(b)
+    need = b.lib.ssm_scan_workspace_bytes(ctypes.byref(d))
+    assert need >= 2 * 64 * 2 * 16 * 4
+    assert _scan(b, d, ws_bytes=need - 1) == -6
+    assert _scan(b, d, ws=0) == -6
+
+
+def test_misaligned_rejected(b):
+    assert _scan(b, _dims(b), u=FAKE + 1) == -4
+    assert _scan(b, _dims(b, io_dtype=0), y=FAKE + 2) == -4
+    assert _scan(b, _dims(b), ws=FAKE + 8) == -4
+
+
+def test_step_validation(b):
+    P = ctypes.c_void_p
+    d = _dims(b, seqlen=1)
+    args = [P(FAKE)] * 6 + [None, None, P(FAKE)]
+    assert b.lib.ssm_step(None, *args[1:], ctypes.byref(d), None) == -1
+    assert b.lib.ssm_step(P(FAKE + 4), *args[1:], ctypes.byref(d), None) == -4   # state needs 16 B
+    assert b.lib.ssm_step(*args, ctypes.byref(_dims(b, dstate=6)), None) == -5
+
+
+def test_empty_problems_are_noops(b):
+    # zero batch or zero channels: nothing to do, no pointer is touched
+    for kw in (dict(batch=0), dict(dim=0)):
+        d = _dims(b, **kw)
+        assert b.lib.ssm_scan_workspace_bytes(ctypes.byref(d)) == 0
+        assert _scan(b, d, u=0, delta=0, A=0, B=0, C=0, y=0, ws=0) == 0
+
+
+def test_plan(b):
+    # the B8 L2048 D5120 layer fills the GPU with channel tiles: one pass
+    assert b.scan_plan(8, 2048, 5120, 16, 1) == (1, 2048)
+    # the long B1 L131072 D2048 sequence has 32 channel tiles: split into chunks
+    n, cl = b.scan_plan(1, 131072, 2048, 16, 1)
+    assert n > 8 and cl % 32 == 0 and n * cl >= 131072 and (n - 1) * cl < 131072
+    assert b.scan_plan(2, 300, 70, 4, 0, chunk_len=64) == (5, 64)
+    assert b.scan_plan(2, 300, 70, 4, 0, chunk_len=-1) == (1, 300)
+    assert b.scan_plan(1, 256, 16, 4, 0) == (1, 256)
+    # workspace grows with the chunk carry
+    assert b.workspace_bytes(1, 4096, 64, 16, 1, chunk_len=128) > b.workspace_bytes(1, 4096, 64, 16, 1, chunk_len=-1)

@@ -1,0 +1,313 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on the same seeded inputs.
+
+Tolerances (north-star): max error <= 1e-4 rms(y) for fp32 I/O and <= 3e-3 rms(y) for
+bf16 I/O, the bf16 error measured before the kernel's own final rounding to bf16 (see
+gpu_util.y_error); last_state within the same factor of rms(last_state).
+"""
+import numpy as np
+import pytest
+
+from selective_state_space_32_amd import inputs
+from gpu_util import TOL, case_tensors, raw_error, rms, to_dev, to_host_f64, y_error
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from selective_state_space_32_amd import ssmscan  # noqa: E402
+
+
+def run_gpu(case, chunk_len=0, want_state=True, drop=()):
+    t = case_tensors(case, torch)
+    for k in drop:
+        t[k] = None
+    y, ls = ssmscan.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                             delta_bias=t["delta_bias"], softplus=case.softplus, return_last_state=want_state,
+                             chunk_len=chunk_len)
+    torch.cuda.synchronize()
+    return to_host_f64(y), (to_host_f64(ls) if ls is not None else None)
+
+
+def run_oracle(oracle_mod, case, channels=None, drop=()):
+    kw = {}
+    if "D" in drop:
+        case = _replace(case, Dskip=None)
+    if "z" in drop:
+        case = _replace(case, z=None)
+    if "delta_bias" in drop:
+        case = _replace(case, delta_bias=None)
+    return oracle_mod.scan_case(case, channels=channels, **kw)
+
+
+def _replace(case, **kw):
+    import dataclasses
+    return dataclasses.replace(case, **kw)
+
+
+def check(case, y, ls, y_ref, ls_ref, label=""):
+    tol = TOL[case.io]
+    e = y_error(y, y_ref, case.io)
+    print(f"[{case.name} {label}] y err/rms = {e:.3e} (raw {raw_error(y, y_ref):.3e}), tol {tol}", flush=True)
+    assert np.all(np.isfinite(y))
+    assert e <= tol, (case.name, label, e)
+    if ls is not None:
+        es = raw_error(ls, ls_ref)
+        print(f"[{case.name} {label}] last_state err/rms = {es:.3e}", flush=True)
+        assert es <= tol, (case.name, label, es)
+
+
+# --- the tiny configuration and its LTI variant -----------------------------------------
+
+@pytest.mark.parametrize("name", ["c1", "c1_lti"])
+def test_tiny_config(oracle_mod, name):
+    case = inputs.config_case(name)
+    y, ls = run_gpu(case)
+    y_ref, ls_ref = run_oracle(oracle_mod, case)
+    check(case, y, ls, y_ref, ls_ref)
+
+
+# --- several tiles and ragged tails, every supported N, both plans ---------------------
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("chunk_len", [-1, 0, 64, 100])
+def test_ragged_multi_tile(oracle_mod, io, N, chunk_len):
+    case = inputs.scan_case(2, 300, 200, N, io, gate=(io == "bf16"), seed=100 + N)
+    y, ls = run_gpu(case, chunk_len=chunk_len)
+    y_ref, ls_ref = run_oracle(oracle_mod, case)
+    check(case, y, ls, y_ref, ls_ref, f"chunk_len={chunk_len}")
+
+
+@pytest.mark.parametrize("drop", [(), ("D",), ("z",), ("delta_bias",), ("D", "z", "delta_bias")])
+@pytest.mark.parametrize("softplus", [True, False])
+def test_optional_inputs(oracle_mod, drop, softplus):
+    case = inputs.scan_case(1, 257, 130, 16, "bf16", gate=True, seed=7, softplus=softplus)
+    if not softplus:
+        # without softplus the step size is delta + bias itself: keep it positive
+        rng = np.random.default_rng(70)
+        dl = (0.1 * np.abs(rng.standard_normal(case.u.shape)) + 0.01).astype(np.float32)
+        case = _replace(case, delta=inputs.bf16_bits(dl), delta_bias=np.full(case.D, 0.02, np.float32))
+    y, ls = run_gpu(case, drop=drop)
+    y_ref, ls_ref = run_oracle(oracle_mod, case, drop=drop)
+    check(case, y, ls, y_ref, ls_ref, f"drop={drop} softplus={softplus}")
+
+
+def test_last_state_optional(oracle_mod):
+    case = inputs.scan_case(2, 96, 70, 16, "f32", seed=8)
+    y, ls = run_gpu(case, want_state=False)
+    assert ls is None
+    y_ref, _ = run_oracle(oracle_mod, case)
+    check(case, y, None, y_ref, None)
+
+
+# --- full-size configurations --------------------------------------------------------
+
+def test_layer_scan_fp32_full(oracle_mod):
+    """B2 L2048 D1536 N16 fp32: every output against the oracle (library's own plan)."""
+    case = inputs.config_case("c2")
+    y, ls = run_gpu(case)
+    y_ref, ls_ref = run_oracle(oracle_mod, case)
+    check(case, y, ls, y_ref, ls_ref, "auto plan")
+    y1, ls1 = run_gpu(case, chunk_len=-1)
+    check(case, y1, ls1, y_ref, ls_ref, "single pass")
+
+
+def _sample_channels(D, k, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 63, 64, D // 2, D - 65, D - 64, D - 2, D - 1]
+    rest = rng.choice(D, size=k, replace=False)
+    return np.unique(np.concatenate([fixed, rest]))
+
+
+@pytest.fixture(scope="module")
+def c3_case():
+    return inputs.config_case("c3")
+
+
+def test_layer_scan_bf16_full_size_sampled(oracle_mod, c3_case):
+    """B8 L2048 D5120 N16 bf16 with gate and last_state, in the benchmark's launch
+    configuration; outputs of sampled channels (all batches, all tokens) against the oracle."""
+    case = c3_case
+    y, ls = run_gpu(case)
+    sel = _sample_channels(case.D, 40, 1)
+    y_ref, ls_ref = run_oracle(oracle_mod, case, channels=sel)
+    check(case, y[:, :, sel], ls[:, sel], y_ref, ls_ref, f"{len(sel)} channels")
+
+
+def test_long_context_full_size_sampled(oracle_mod):
+    """B1 L131072 D2048 N16 bf16 (mean step ~0.01): the chunk-carry plan; sampled channels."""
+    case = inputs.config_case("c4")
+    nchunk, clen = ssmscan.scan_plan(case.bsz, case.L, case.D, case.N, torch.bfloat16)
+    assert nchunk > 1
+    y, ls = run_gpu(case)
+    sel = _sample_channels(case.D, 16, 2)
+    y_ref, ls_ref = run_oracle(oracle_mod, case, channels=sel)
+    check(case, y[:, :, sel], ls[:, sel], y_ref, ls_ref, f"{nchunk} chunks of {clen}")
+
+
+# --- the recurrent step -----------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def c5_case():
+    return inputs.config_case("c5")
+
+
+def test_decode_steps_vs_oracle(oracle_mod, c5_case):
+    """S256 D5120 N16, 64 consecutive steps from a N(0, 0.1) state; sampled sequences against
+    the oracle step by step."""
+    c = c5_case
+    sel = np.array([0, 1, 77, 128, 200, 254, 255])
+    st = torch.from_numpy(c.state0).cuda()
+    A = to_dev(c.A, torch)
+    Dv = to_dev(c.Dskip, torch)
+    ref_state = c.state0[sel].astype(np.float64)
+    worst = 0.0
+    for k in range(c.steps):
+        u, dl, z = (to_dev(getattr(c, f)[k], torch) for f in ("u", "delta", "z"))
+        Bk, Ck = to_dev(c.B[k], torch), to_dev(c.C[k], torch)
+        y = ssmscan.step(st, u, dl, A, Bk, Ck, D=Dv, z=z)
+        yr, ref_state = oracle_mod.step(ref_state, c.values("u")[k][sel], c.values("delta")[k][sel], c.A,
+                                        c.values("B")[k][sel], c.values("C")[k][sel], D=c.Dskip,
+                                        z=c.values("z")[k][sel])
+        yk = to_host_f64(y)[sel]
+        e = y_error(yk, yr, "bf16")
+        worst = max(worst, e)
+        assert e <= TOL["bf16"], (k, e)
+    es = raw_error(to_host_f64(st)[sel], ref_state)
+    print(f"[decode] worst y err/rms {worst:.3e}, final state err/rms {es:.3e}", flush=True)
+    assert es <= TOL["bf16"]
+
+
+def test_decode_steps_vs_scan(c5_case):
+    """64 GPU steps from a zero state equal the GPU scan of the same 64-token sequences (step
+    size already activated: softplus off, no bias)."""
+    c = c5_case
+    S, D, N, L = c.S, c.D, c.N, c.steps
+    st = torch.zeros((S, D, N), dtype=torch.float32, device="cuda")
+    A = to_dev(c.A, torch)
+    Dv = to_dev(c.Dskip, torch)
+    ys = []
+    for k in range(L):
+        ys.append(ssmscan.step(st, to_dev(c.u[k], torch), to_dev(c.delta[k], torch), A, to_dev(c.B[k], torch),
+                               to_dev(c.C[k], torch), D=Dv, z=to_dev(c.z[k], torch)))
+    y_step = torch.stack(ys, dim=1)  # (S, L, D)
+    perm = lambda a: np.ascontiguousarray(np.swapaxes(a, 0, 1))  # (L, S, X) -> (S, L, X)
+    y_scan, ls = ssmscan.scan_fwd(to_dev(perm(c.u), torch), to_dev(perm(c.delta), torch), A,
+                                  to_dev(perm(c.B), torch), to_dev(perm(c.C), torch), D=Dv,
+                                  z=to_dev(perm(c.z), torch), delta_bias=None, softplus=False)
+    torch.cuda.synchronize()
+    a, b = to_host_f64(y_step), to_host_f64(y_scan)
+    from gpu_util import bf16_ulp
+    d = np.abs(a - b) - 0.5 * bf16_ulp(a) - 0.5 * bf16_ulp(b)
+    e = float(np.max(d)) / rms(b)
+    es = raw_error(to_host_f64(st), to_host_f64(ls))
+    print(f"[step vs scan] y {e:.3e}, state {es:.3e}", flush=True)
+    assert e <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+# --- properties ----------------------------------------------------------------------------
+
+def test_deterministic(c3_case):
+    small = inputs.scan_case(2, 512, 1024, 16, "bf16", gate=True, seed=9)
+    y1, l1 = run_gpu(small)
+    y2, l2 = run_gpu(small)
+    assert np.array_equal(y1, y2) and np.array_equal(l1, l2)
+    y3, l3 = run_gpu(small, chunk_len=96)
+    y4, l4 = run_gpu(small, chunk_len=96)
+    assert np.array_equal(y3, y4) and np.array_equal(l3, l4)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_outputs_fully_written_guards_untouched(io):
+    case = inputs.scan_case(2, 130, 150, 16, io, gate=True, seed=10)
+    t = case_tensors(case, torch)
+    dt = t["u"].dtype
+    G = 1000
+    ybuf = torch.full((2 * G + 2 * 130 * 150,), float("nan"), dtype=dt, device="cuda")
+    ybuf[:G] = 7.0
+    ybuf[-G:] = 7.0
+    y = ybuf[G:G + 2 * 130 * 150].view(2, 130, 150)
+    lbuf = torch.full((2 * G + 2 * 150 * 16,), float("nan"), dtype=torch.float32, device="cuda")
+    lbuf[:G] = 7.0
+    lbuf[-G:] = 7.0
+    ls = lbuf[G:G + 2 * 150 * 16].view(2, 150, 16)
+    for chunk_len in (-1, 40):
+        ssmscan.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                         delta_bias=t["delta_bias"], y=y, last_state=ls, chunk_len=chunk_len)
+        torch.cuda.synchronize()
+        assert not torch.isnan(y).any() and not torch.isnan(ls).any()
+        assert torch.all(ybuf[:G] == 7.0) and torch.all(ybuf[-G:] == 7.0)
+        assert torch.all(lbuf[:G] == 7.0) and torch.all(lbuf[-G:] == 7.0)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (1, 1, 64), (1, 31, 65), (3, 33, 1), (1, 200, 63), (2, 5, 129)])
+def test_edge_shapes(oracle_mod, shape):
+    bsz, L, D = shape
+    for io in ("f32", "bf16"):
+        case = inputs.scan_case(bsz, L, D, 16, io, gate=True, seed=11)
+        for chunk_len in (-1, 1, 7):
+            y, ls = run_gpu(case, chunk_len=chunk_len)
+            y_ref, ls_ref = run_oracle(oracle_mod, case)
+            check(case, y, ls, y_ref, ls_ref, f"chunk_len={chunk_len}")
+
+
+def test_many_chunks_multi_block_carry(oracle_mod):
+    """chunk_len = 1 over 300 tokens: 299 chunk carries, i.e. several 64-lane blocks of the
+    DPP prefix scan with the running carry between them."""
+    case = inputs.scan_case(1, 300, 96, 16, "f32", seed=12)
+    y, ls = run_gpu(case, chunk_len=1)
+    y_ref, ls_ref = run_oracle(oracle_mod, case)
+    check(case, y, ls, y_ref, ls_ref, "chunk_len=1")
+
+
+def test_zero_length_sequence():
+    A = torch.full((40, 16), -1.0, device="cuda")
+    e = torch.empty((2, 0, 40), dtype=torch.bfloat16, device="cuda")
+    eb = torch.empty((2, 0, 16), dtype=torch.bfloat16, device="cuda")
+    ls = torch.full((2, 40, 16), float("nan"), device="cuda")
+    y, ls = ssmscan.scan_fwd(e, e, A, eb, eb, last_state=ls)
+    torch.cuda.synchronize()
+    assert y.shape == (2, 0, 40) and torch.all(ls == 0)
+
+
+def test_small_step_keeps_state_bitwise():
+    """delta = 0 at token t (softplus off): exp2(0) = 1 and the input term is 0, so the state
+    after t equals the state after t-1 exactly (azimuth.plus/paper/mamba, selection section)."""
+    case = inputs.scan_case(1, 96, 128, 16, "f32", seed=13, softplus=False, bias=None, delta_scale=0.0)
+    dl = np.abs(np.random.default_rng(1).standard_normal((1, 96, 128)).astype(np.float32)) * 0.1
+    t0 = 70
+    dl[:, t0] = 0.0
+    case = _replace(case, delta=dl)
+    _, h_before = run_gpu(_replace(case, L=t0, u=case.u[:, :t0], delta=dl[:, :t0], B=case.B[:, :t0],
+                                   C=case.C[:, :t0]), chunk_len=-1)
+    _, h_at = run_gpu(_replace(case, L=t0 + 1, u=case.u[:, :t0 + 1], delta=dl[:, :t0 + 1], B=case.B[:, :t0 + 1],
+                               C=case.C[:, :t0 + 1]), chunk_len=-1)
+    assert np.array_equal(h_before, h_at)
+
+
+def test_large_step_resets_state_bitwise():
+    """delta * A <= -1e3 at token t: exp2 gives exactly 0, the state becomes delta*B*u and the
+    outputs from t on equal those of the sequence restarted at t."""
+    case = inputs.scan_case(1, 96, 128, 16, "f32", gate=True, seed=14, softplus=False, bias=None)
+    dl = np.abs(case.values("delta")) + 0.01
+    t0 = 40
+    dl[:, t0] = 1e3
+    full = _replace(case, delta=dl)
+    tail = _replace(case, L=96 - t0, u=case.u[:, t0:], delta=dl[:, t0:], B=case.B[:, t0:], C=case.C[:, t0:],
+                    z=case.z[:, t0:])
+    y, h = run_gpu(full, chunk_len=-1)
+    y2, h2 = run_gpu(tail, chunk_len=-1)
+    assert np.array_equal(y[:, t0:], y2) and np.array_equal(h, h2)
+
+
+def test_nan_propagates_only_downstream():
+    case = inputs.scan_case(1, 64, 128, 16, "f32", seed=15)
+    u = case.u.copy()
+    u[0, 30, 5] = np.nan
+    y, h = run_gpu(_replace(case, u=u), chunk_len=-1)
+    assert np.all(np.isnan(y[0, 30:, 5])) and np.all(np.isnan(h[0, 5]))
+    mask = np.ones_like(y, dtype=bool)
+    mask[0, 30:, 5] = False
+    assert np.all(np.isfinite(y[mask]))
