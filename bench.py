@@ -1,0 +1,257 @@
+"""Benchmark of the selective scan (S6) forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3|c2|c4|c5] [--no-cpu]
+
+One "step" is one ssm_scan_fwd call over the whole batch (for c5: one ssm_step over the
+256 sequences).  Inputs are generated on the host, copied to HBM before the timed region,
+and stay resident.  W untimed steps, then exactly K steps between two device
+synchronisations; each step is also bracketed by HIP events on the launch stream, which
+gives the kernel's average duration for the roofline.  Prints one JSON line.
+
+The default workload is the B8 L2048 D5120 N16 bf16 layer scan (z gate, last_state).
+The CPU baseline is the fp64 oracle on the host cores, on a channel sample of the same
+workload sized to about 10-20 s of CPU work.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+# VALU issue capacity of MI355X: 256 CUs x 4 SIMDs x 16 lanes per clock x 2.4 GHz, in
+# fp32 lane-operations per second (packed fp32 is not used).
+VALU_PEAK_TLANEOPS = 256 * 64 * 2.4e9 / 1e12
+# Unavoidable VALU issue slots per (token, channel, state): the multiplies delta*A and
+# (delta u)*B, the state FMA and the readout FMA at one slot each, and exp2 at half rate.
+SLOTS_PER_ELEMENT = 6
+
+WORKLOADS = {
+    "c2": "selective scan B2 L2048 D1536 N16, fp32 I/O, fp32 state",
+    "c3": "selective scan B8 L2048 D5120 N16, bf16 I/O, fp32 state, SiLU(z) gate, D skip, last_state",
+    "c4": "selective scan B1 L131072 D2048 N16, bf16 I/O, fp32 state, last_state",
+    "c5": "recurrent step S256 D5120 N16, bf16 I/O, fp32 state in place",
+}
+METRIC = "selective-scan HBM GB/s (% of peak) + channel-tokens/s, B8 L2048 D5120 N16 bf16"
+
+
+def scan_alg_bytes(bsz, L, D, N, io_bytes, gate, skip, bias, last_state):
+    """Bytes the method must move per call: u, delta, (z), y per element; B, C per token;
+    A, D, delta_bias per channel; last_state per (sequence, channel, state)."""
+    per_el = io_bytes * (3 + (1 if gate else 0))
+    b = bsz * L * D * per_el
+    b += 2 * bsz * L * N * io_bytes
+    b += D * N * 4 + D * 4 * ((1 if skip else 0) + (1 if bias else 0))
+    if last_state:
+        b += bsz * D * N * 4
+    return b
+
+
+def step_alg_bytes(S, D, N, io_bytes, gate, skip):
+    """state read + write, u, delta, (z), y per (sequence, channel), B, C per sequence, A, D."""
+    return S * D * (2 * N * 4 + io_bytes * (3 + (1 if gate else 0))) + 2 * S * N * io_bytes + D * N * 4 + \
+        (D * 4 if skip else 0)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "selective_state_space_32_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        c = json.load(f)
+    if c.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline_scan(case, alg_bytes_full, target_s=12.0):
+    """Time the fp64 oracle on a channel sample of the workload on the host cores."""
+    from oracle import oracle
+    oracle.build(force=False)
+    threads = min(16, oracle.default_threads())
+    D = case.D
+    probe = np.arange(0, D, max(1, D // 16))[:16]
+    t = time.perf_counter()
+    oracle.scan_case(case, channels=probe, threads=threads)
+    dt = time.perf_counter() - t
+    per_ch = dt / len(probe)
+    k = int(min(D, max(len(probe), target_s / max(per_ch, 1e-9))))
+    sel = np.linspace(0, D - 1, k).astype(np.int64)
+    sel = np.unique(sel)
+    t = time.perf_counter()
+    oracle.scan_case(case, channels=sel, threads=threads)
+    dt = time.perf_counter() - t
+    frac = len(sel) / D
+    gbps = alg_bytes_full * frac / dt / 1e9
+    chtok = case.bsz * case.L * len(sel) / dt
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "channel_tokens_per_s": round(chtok, 1), "seconds": round(dt, 2),
+            "sample": f"{len(sel)} of {D} channels x all {case.bsz} sequences x {case.L} tokens "
+                      f"(fp64 oracle, OpenMP over channels)"}
+
+
+def cpu_baseline_step(case, alg_bytes_step, target_s=12.0):
+    from oracle import oracle
+    oracle.build(force=False)
+    threads = min(16, oracle.default_threads())
+    st = case.state0.astype(np.float64)
+    done = 0
+    t = time.perf_counter()
+    while time.perf_counter() - t < target_s and done < case.steps:
+        k = done
+        _, st = oracle.step(st, case.values("u")[k], case.values("delta")[k], case.A, case.values("B")[k],
+                            case.values("C")[k], D=case.Dskip, z=case.values("z")[k], threads=threads)
+        done += 1
+    dt = time.perf_counter() - t
+    return {"value": round(alg_bytes_step * done / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 2), "sample": f"{done} of {case.steps} steps over all {case.S} sequences"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the scan shards "
+              "with no communication across sequences and channels, so run one process per GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from selective_state_space_32_amd import inputs, ssmscan
+
+    dev = "cuda"
+    wl = args.workload
+    case = inputs.config_case(wl)
+    io_bytes = 2 if case.io == "bf16" else 4
+
+    def td(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    stream = torch.cuda.current_stream()
+    if wl == "c5":
+        S, D, N = case.S, case.D, case.N
+        A, Dv = td(case.A), td(case.Dskip)
+        st = td(case.state0).clone()
+        ins = [(td(case.u[k]), td(case.delta[k]), td(case.B[k]), td(case.C[k]), td(case.z[k]))
+               for k in range(case.steps)]
+        y = torch.empty((S, D), dtype=torch.bfloat16, device=dev)
+        alg = step_alg_bytes(S, D, N, io_bytes, True, True)
+        chtok = S * D
+        elements = S * D * N
+
+        def one(i):
+            u, dl, Bk, Ck, z = ins[i % case.steps]
+            ssmscan.step(st, u, dl, A, Bk, Ck, D=Dv, z=z, y=y)
+        plan = "one step kernel per call"
+    else:
+        t = {k: td(getattr(case, f)) for k, f in (("u", "u"), ("delta", "delta"), ("A", "A"), ("B", "B"),
+                                                   ("C", "C"), ("D", "Dskip"), ("z", "z"), ("bias", "delta_bias"))}
+        bsz, L, D, N = case.bsz, case.L, case.D, case.N
+        dtype = t["u"].dtype
+        y = torch.empty((bsz, L, D), dtype=dtype, device=dev)
+        ls = torch.empty((bsz, D, N), dtype=torch.float32, device=dev)
+        nchunk, clen = ssmscan.scan_plan(bsz, L, D, N, dtype)
+        ws = torch.empty(max(1, ssmscan.workspace_bytes(bsz, L, D, N, dtype)), dtype=torch.uint8, device=dev)
+        alg = scan_alg_bytes(bsz, L, D, N, io_bytes, case.z is not None, case.Dskip is not None,
+                             case.delta_bias is not None, True)
+        chtok = bsz * L * D
+        elements = chtok * N
+
+        def one(i):
+            ssmscan.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                             delta_bias=t["bias"], softplus=case.softplus, y=y, last_state=ls, workspace=ws)
+        plan = "single pass" if nchunk == 1 else f"{nchunk} chunks of {clen} tokens (summary + carry + scan)"
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        one(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        one(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3  # seconds per launch
+    ms_per_step = wall / args.steps * 1e3
+    kern_s = float(np.mean(per))
+
+    step_s = wall / args.steps
+    gbps = alg / step_s / 1e9          # whole-job throughput over the timed region
+    kern_gbps = alg / kern_s / 1e9     # the kernel's own rate (event-timed launches)
+    lane_ops = elements * SLOTS_PER_ELEMENT / kern_s / 1e12
+    traffic = counter_traffic(wl)
+    if wl == "c5":
+        roof = {"bound": "hbm", "achieved": round(kern_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(kern_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "alu", "achieved": round(lane_ops, 3), "peak": round(VALU_PEAK_TLANEOPS, 3),
+                "unit": "T fp32 VALU lane-ops/s", "frac": round(lane_ops / VALU_PEAK_TLANEOPS, 4),
+                "traffic": traffic,
+                "work": f"{SLOTS_PER_ELEMENT} VALU issue slots per (token, channel, state) x {elements} per launch"}
+
+    cpu = None
+    if not args.no_cpu:
+        try:
+            cpu = cpu_baseline_step(case, alg) if wl == "c5" else cpu_baseline_scan(case, alg)
+        except Exception as e:  # the GPU figures stand without it
+            cpu = {"error": repr(e)}
+
+    out = {
+        "metric": METRIC if wl == "c3" else f"{WORKLOADS[wl]}: HBM GB/s (% of peak) + channel-tokens/s",
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[wl], "io_dtype": case.io, "plan": plan,
+                   "channel_tokens_per_step": chtok, "alg_bytes_per_step": alg},
+        "hbm_pct_of_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "channel_tokens_per_s": round(chtok / step_s, 1),
+        "kernel_gbps": round(kern_gbps, 2),
+        "kernel_us_mean": round(kern_s * 1e6, 3),
+        "kernel_us_p10_p50_p90": [round(float(np.percentile(per, q)) * 1e6, 3) for q in (10, 50, 90)],
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -19,7 +19,8 @@
  *
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers (hipMalloc / torch CUDA memory), row-major,
- *    densely packed, innermost index last.  Elements must be naturally aligned.
+ *    densely packed, innermost index last.  Elements must be naturally aligned; bf16 B
+ *    and C must also be 4-byte aligned when dstate >= 2 (they are read as 32-bit words).
  *  - The "I/O" tensors u, delta, z, y, B, C have the element type dims->io_dtype
  *    (SSM_IO_F32 = IEEE fp32, SSM_IO_BF16 = bfloat16 bit patterns).  A, D, delta_bias,
  *    last_state and state are always fp32.  Arithmetic and the state are fp32.
@@ -76,8 +77,11 @@ typedef enum {
  *   io_dtype  an ssm_io_dtype
  *   chunk_len scan plan: 0 = the library chooses; > 0 = split every sequence into
  *             chunks of this many tokens and combine the chunk states (two-pass chunk
- *             carry); -1 = one pass over the whole sequence.  Results agree up to fp32
- *             rounding whatever the plan. */
+ *             carry); -1 = one pass, one workgroup per 64 channels of a sequence.  With 0
+ *             and enough channels the library also runs one pass, but as a persistent
+ *             grid that hands each sequence's state between workgroups piece by piece so
+ *             that every CU gets the same work.  Results agree up to fp32 rounding
+ *             whatever the plan. */
 typedef struct ssm_dims {
     int64_t batch;
     int64_t seqlen;
@@ -88,12 +92,16 @@ typedef struct ssm_dims {
 } ssm_dims;
 
 /* Bytes of device workspace ssm_scan_fwd needs for these sizes and plan (256-byte
- * aligned regions).  Returns 0 for an invalid or empty problem. */
+ * aligned regions): the per-chunk carry states of a chunked plan, 0 for a single pass.
+ * Returns 0 for an invalid or empty problem. */
 SSMSCAN_API size_t ssm_scan_workspace_bytes(const ssm_dims *dims);
 
-/* The plan ssm_scan_fwd will use: returns the number of chunks each sequence is split
- * into (1 = single pass) and stores the chunk length in tokens in *chunk_len_out
- * (may be NULL).  Returns a negative ssm_status for invalid sizes. */
+/* The plan ssm_scan_fwd will use.  Returns the number of chunks each sequence is split
+ * into for the chunk carry (1 = a single pass: every token's state is computed once) and
+ * stores in *chunk_len_out (may be NULL) the tokens per work item: the carry chunk length,
+ * or, for a single pass, the length of the pieces a sequence is handed over in between
+ * workgroups (the whole sequence when it is not split).  Returns a negative ssm_status for
+ * invalid sizes. */
 SSMSCAN_API int64_t ssm_scan_plan(const ssm_dims *dims, int64_t *chunk_len_out);
 
 /* Selective scan forward over a batch of sequences, from a zero state.
@@ -104,8 +112,9 @@ SSMSCAN_API int64_t ssm_scan_plan(const ssm_dims *dims, int64_t *chunk_len_out);
  *   softplus_flag  : nonzero = apply softplus to delta + delta_bias
  *   y              : output, written completely
  *   last_state     : [batch][dim][dstate] fp32 output h_L, may be NULL
- *   workspace      : device memory of at least ssm_scan_workspace_bytes(dims) bytes
- *                    (its contents on entry do not matter; it is scratch for this call)
+ *   workspace      : device memory of at least ssm_scan_workspace_bytes(dims) bytes, 16-byte
+ *                    aligned (contents on entry do not matter; scratch for this call);
+ *                    may be NULL when that size is 0
  * Returns SSM_OK or a negative ssm_status. */
 SSMSCAN_API int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
                  const float *D, const void *z, const float *delta_bias, int softplus_flag,

@@ -41,16 +41,65 @@ template <> struct io<uint16_t> {
     __device__ __forceinline__ static void st(uint16_t *p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
 };
 
-// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|).
-// log1p(e), e in (0, 1]: for e < 1/16 the alternating series to e^5 (relative error
-// below e^5/6 < 2e-7); otherwise log2(1 + e) ln 2, whose only extra error is the
-// rounding of 1 + e (below 2^-24 absolute, i.e. < 1e-6 relative for e >= 1/16).
+// V consecutive I/O elements moved as raw 32-bit words (W = V * sizeof(IO) / 4 words; bf16
+// pairs share a word, low half first).  Requires V * sizeof(IO) to be 4, 8 or a multiple of
+// 16 bytes and the address to be aligned to min(16, V * sizeof(IO)) bytes.
+template <int V, typename IO> struct vec {
+    static constexpr int W = V * (int)sizeof(IO) / 4;
+    static_assert(W >= 1 && (W <= 2 || W % 4 == 0), "unsupported vector width");
+
+    __device__ __forceinline__ static void load(const IO *p, int64_t idx, uint32_t (&w)[W]) {
+        const uint32_t *q = reinterpret_cast<const uint32_t *>(p + idx);
+        if constexpr (W % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < W / 4; ++i) {
+                const uint4 r = reinterpret_cast<const uint4 *>(q)[i];
+                w[4 * i] = r.x; w[4 * i + 1] = r.y; w[4 * i + 2] = r.z; w[4 * i + 3] = r.w;
+            }
+        } else if constexpr (W == 2) {
+            const uint2 r = *reinterpret_cast<const uint2 *>(q);
+            w[0] = r.x; w[1] = r.y;
+        } else {
+            w[0] = q[0];
+        }
+    }
+    __device__ __forceinline__ static float get(const uint32_t (&w)[W], int v) {
+        if constexpr (sizeof(IO) == 2)
+            return __uint_as_float((v & 1) ? (w[v >> 1] & 0xffff0000u) : (w[v >> 1] << 16));
+        else
+            return __uint_as_float(w[v]);
+    }
+    __device__ __forceinline__ static void store(IO *p, int64_t idx, const float (&y)[V]) {
+        uint32_t w[W];
+        if constexpr (sizeof(IO) == 2) {
+#pragma unroll
+            for (int i = 0; i < W; ++i) w[i] = f32x2_to_bf16x2(y[2 * i], y[2 * i + 1]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < W; ++i) w[i] = __float_as_uint(y[i]);
+        }
+        uint32_t *q = reinterpret_cast<uint32_t *>(p + idx);
+        if constexpr (W % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < W / 4; ++i)
+                reinterpret_cast<uint4 *>(q)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+        } else if constexpr (W == 2) {
+            *reinterpret_cast<uint2 *>(q) = make_uint2(w[0], w[1]);
+        } else {
+            q[0] = w[0];
+        }
+    }
+};
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e), e = e^-|x| in (0, 1].
+// log1p(e): w = 1 + e is rounded; the rounding error r = e - (w - 1) is exact, and
+// log1p(e) = log(w) + r/w.  r/w is taken as r: |r| <= 2^-24 and r only matters when w is
+// close to 1 (for e < 2^-24, w = 1 and the result is e itself).
 __device__ __forceinline__ float softplus_f32(float x) {
-    float e = hw_exp2(-fabsf(x) * kLog2e);
-    float poly = e * (1.0f + e * (-0.5f + e * (0.33333334f + e * (-0.25f + e * 0.2f))));
-    float lg = hw_log2(1.0f + e) * kLn2;
-    float l1p = e < 0.0625f ? poly : lg;
-    return fmaxf(x, 0.0f) + l1p;
+    const float e = hw_exp2(-fabsf(x) * kLog2e);
+    const float w = 1.0f + e;
+    const float r = e - (w - 1.0f);
+    return fmaxf(x, 0.0f) + fmaf(hw_log2(w), kLn2, r);
 }
 
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z).  For z << 0, e^-z = inf and the result is -0.

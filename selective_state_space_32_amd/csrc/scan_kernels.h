@@ -1,13 +1,13 @@
 // Selective-scan kernels for gfx950.
 //
-// Work decomposition (one workgroup = one sequence b x a tile of 64 channels x one chunk of
-// tokens; K = N / S waves):
+// Work decomposition (a work item = one sequence b x a tile of 64 channels x one chunk of
+// tokens, processed by one workgroup of K = N / S waves):
 //  * wave w owns states n in [w*S, (w+1)*S) of all 64 channels, lane = channel.  The
 //    fp32 state h and A*log2(e) for those states live in VGPRs for the whole chunk.
 //  * B_t and C_t are the same for every channel of a sequence, so for a wave they are
-//    uniform: each wave reads its S-wide slice of them with scalar loads into SGPRs from a
-//    small fp32 staging copy (stage_bc_kernel), and every per-(token, state) instruction
-//    takes them as its scalar operand.
+//    uniform: each wave reads its S-wide slice of them with scalar loads into SGPRs
+//    (bf16 pairs are widened to fp32 on the scalar ALU), and every per-(token, state)
+//    instruction takes them as its scalar operand.
 //  * Per-token, per-channel work (the step-size activation, delta*u, the skip term, the
 //    SiLU gate, the output rounding) is done once per element, spread over all K waves:
 //    a "prep" pass writes (delta, delta*u) for a tile of T tokens into LDS, the waves run
@@ -17,156 +17,285 @@
 //    wave touches 64 consecutive elements of one token row.
 // Per (token, channel, state) the recurrence costs one multiply (delta*A), one exp2, one
 // multiply (delta*u*B), one FMA (state) and one FMA (readout) -- no more.
+//
+// Scheduling (MODE):
+//  * kFull / kSummary: one workgroup per (tile, chunk) of the grid -- the single pass and
+//    the first and last passes of the chunk carry (see carry_kernel.h).
+//  * kChained: a persistent grid sized to what is resident at once; workgroups claim
+//    (tile, chunk) items from an atomic counter in chunk-major order and hand the fp32
+//    state of a tile from one chunk to the next through a per-tile slot and a progress
+//    word (release / acquire at device scope).  Every token is still processed exactly
+//    once, but all CUs get equal work whatever the number of tiles.  A workgroup only
+//    waits for an item claimed before its own, whose workgroup is running, so the chain
+//    always drains; the wait is bounded and, if the bound is ever hit, an error word is
+//    raised instead of hanging.
 #pragma once
 
 #include "device_math.h"
 
 namespace ssm {
 
-constexpr int kTileT = 32;       // tokens per LDS tile
 constexpr int kChanTile = 64;    // channels per workgroup (one per lane)
 
-enum ScanMode { kFull = 0, kSummary = 1 };
+enum ScanMode { kFull = 0, kSummary = 1, kChained = 2 };
 
-// fp32 staging copy of B and C, laid out per (sequence, wave slice):
-//   bc[b][w][t][0..S)  = B[b][t][w*S + s],   bc[b][w][t][S..2S) = C[b][t][w*S + s]
-// so that one wave's operands for one token are 2S consecutive floats.
-template <int N, int S, typename IO>
-__global__ void __launch_bounds__(256)
-stage_bc_kernel(const IO *__restrict__ B, const IO *__restrict__ C, float *__restrict__ bc,
-                int64_t total /* bsz*L*N */, int64_t L) {
-    constexpr int K = N / S;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= total) return;
-    const int n = (int)(i % N);
-    const int64_t bt = i / N;
-    const int64_t b = bt / L, t = bt - b * L;
-    const int w = n / S, s = n - w * S;
-    const int64_t o = ((b * K + w) * L + t) * (2 * S);
-    bc[o + s] = io<IO>::ld(B, i);
-    bc[o + S + s] = io<IO>::ld(C, i);
+// Scheduling words of the chained mode, at the start of the workspace:
+//   sched[0] work counter, sched[1 + tile] chunks of the tile completed,
+//   sched[1 + n_tiles] error word (nonzero if a wait hit its bound).
+constexpr unsigned kSpinLimit = 1u << 24;
+
+// S consecutive B or C values starting at element `off` (a wave-uniform offset), widened
+// to fp32.  bf16 pairs are read as 32-bit words (the offset is even whenever S is).
+template <int S, typename IO>
+__device__ __forceinline__ void load_slice(const IO *__restrict__ p, int64_t off, float (&out)[S]) {
+    if constexpr (sizeof(IO) == 2 && S % 2 == 0) {
+        const uint32_t *q = reinterpret_cast<const uint32_t *>(p + off);
+#pragma unroll
+        for (int i = 0; i < S / 2; ++i) {
+            const uint32_t v = q[i];
+            out[2 * i] = __uint_as_float(v << 16);
+            out[2 * i + 1] = __uint_as_float(v & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < S; ++s) out[s] = io<IO>::ld(p, off + s);
+    }
 }
 
-// One chunk of the scan for one (sequence, 64-channel tile).
+// The scan over (tile, chunk) work items.
 //   kFull:    start from h = 0 (chunk 0) or from the carried state cstate[b][c-1]
 //             (the state after chunk c-1), run the recurrence with readout, write y; the
 //             last chunk writes last_state.
 //   kSummary: start from h = 0, no readout; write the chunk's local final state to
 //             cstate[b][c] and the chunk's sum of step sizes to cdsum[b][c].
-template <int N, int S, typename IO, int MODE>
+//   kChained: as kFull, with the state handed between chunks through cstate[tile] slots
+//             (64 x N floats each) and the scheduling words `sched`.
+//   N: state size; S: states per wave (K = N/S waves); T: tokens per LDS tile.
+//   VEC: the prep and epilogue move V consecutive channels of one token per thread
+//        (one 16-byte access for 8 bf16); needs D % 8 == 0 and 16-byte aligned u, delta,
+//        z, y.  Otherwise one element per access.
+template <int N, int S, int T, typename IO, int MODE, bool VEC>
 __global__ void __launch_bounds__(64 * (N / S))
 scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                   const IO *__restrict__ z, IO *__restrict__ y,
                   const float *__restrict__ A, const float *__restrict__ Dv,
-                  const float *__restrict__ bias, const float *__restrict__ bc,
-                  float *__restrict__ last_state, float *__restrict__ cstate,
-                  float *__restrict__ cdsum, int64_t L, int64_t D, int tiles_per_b,
-                  int64_t chunk_len, int nchunk, int softplus) {
+                  const float *__restrict__ bias, const IO *__restrict__ Bm,
+                  const IO *__restrict__ Cm, float *__restrict__ last_state, float *__restrict__ cstate,
+                  float *__restrict__ cdsum, int *__restrict__ sched, int64_t L, int64_t D,
+                  int tiles_per_b, int n_tiles, int64_t chunk_len, int nchunk, int softplus) {
     constexpr int K = N / S;
-    constexpr int T = kTileT;
-    constexpr int J = T / K;  // prep / epilogue elements per thread per tile
-    static_assert(T % K == 0, "tile must split evenly over the waves");
+    constexpr int J = T / K;                   // prep / epilogue elements per thread per tile
+    constexpr int V = VEC ? (J < 8 ? J : 8) : 1;  // consecutive channels per thread access
+    constexpr int P = J / V;                   // accesses per thread per tile
+    constexpr int GPR = kChanTile / V;         // threads per token row
+    constexpr int RPP = 64 * K / GPR;          // token rows per access round
+    constexpr bool READOUT = MODE != kSummary;
+    static_assert(T % K == 0 && J % V == 0 && RPP * P == T, "tile must split evenly over the threads");
+    using VIO = vec<V, IO>;
+    constexpr int W = VEC ? V * (int)sizeof(IO) / 4 : 1;
     __shared__ f32x2_t s_dk[T][kChanTile];
-    __shared__ float s_yp[MODE == kFull ? K : 1][T][kChanTile];
+    __shared__ float s_yp[READOUT ? K : 1][T][kChanTile];
+    __shared__ int s_item;
 
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int b = blockIdx.x / tiles_per_b;
-    const int64_t d = (int64_t)(blockIdx.x - b * tiles_per_b) * kChanTile + lane;
-    const bool act = d < D;
-    const int c = blockIdx.y;
-    const int64_t t_begin = (int64_t)c * chunk_len;
-    const int64_t t_end = min(L, t_begin + chunk_len);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // prep / epilogue mapping: access p of this thread covers token row p*RPP + tid/GPR,
+    // channels cq .. cq+V-1 of the tile
+    const int rsub = tid / GPR;
+    const int cq = (tid % GPR) * V;
+    const bool gated = READOUT && z != nullptr;
+    const int64_t n_items = (int64_t)n_tiles * nchunk;
 
-    float a2[S], h[S];
+    // Work items.  The claimed index is broadcast through LDS and read back with
+    // readfirstlane, so that it is a scalar the compiler knows to be uniform: the item loop
+    // and every barrier in it then stay in uniform control flow.
+    auto claim = [&]() -> int64_t {
+        if (tid == 0) s_item = atomicAdd(&sched[0], 1);
+        __syncthreads();
+        const int it = __builtin_amdgcn_readfirstlane(s_item);
+        __syncthreads();
+        return it;
+    };
+    int64_t item = MODE == kChained ? claim() : (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    while (item < n_items) {
+        const int c = (int)(item / n_tiles);
+        const int tile = (int)(item - (int64_t)c * n_tiles);
+        const int b = tile / tiles_per_b;
+        const int64_t d0 = (int64_t)(tile - b * tiles_per_b) * kChanTile;
+        const int64_t d = d0 + lane;            // channel of this lane in the recurrence
+        const bool act = d < D;
+        const int64_t t_begin = (int64_t)c * chunk_len;
+        const int64_t t_end = min(L, t_begin + chunk_len);
+        const int64_t row0 = (int64_t)b * L;
+        const bool qact = d0 + cq < D;          // whole group in or out (D % V == 0 when VEC)
+        const int64_t dq = qact ? d0 + cq : (D - V) / V * V;  // in-bounds channel for loads
+
+        float a2[S], h[S];
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const int n = w * S + s;
-        a2[s] = act ? A[d * N + n] * kLog2e : 0.0f;
-        h[s] = 0.0f;
-        if (MODE == kFull && c > 0 && act) h[s] = cstate[(((int64_t)b * nchunk + c - 1) * D + d) * N + n];
-    }
-    const float Dd = (act && Dv) ? Dv[d] : 0.0f;
-    const float bd = (act && bias) ? bias[d] : 0.0f;
-    float dsum = 0.0f;
-    const int64_t row0 = (int64_t)b * L;
-    const float *__restrict__ bcw = bc + ((int64_t)(b * K + w) * L) * (2 * S);
-
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += T) {
-        const int nt = (int)min((int64_t)T, t_end - t0);
-        float Du[J], g[J];
-        // prep: (delta, delta*u) into LDS; skip and gate factors kept in registers
+        for (int s = 0; s < S; ++s) {
+            a2[s] = act ? A[d * N + w * S + s] * kLog2e : 0.0f;
+            h[s] = 0.0f;
+        }
+        if (MODE == kFull && c > 0 && act) {
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int tt = w + j * K;
-            float dl = 0.0f, kk = 0.0f;
-            Du[j] = 0.0f;
-            g[j] = 1.0f;
-            if (tt < nt && act) {
-                const int64_t idx = (row0 + t0 + tt) * D + d;
-                const float uu = io<IO>::ld(u, idx);
-                const float x = io<IO>::ld(delta, idx) + bd;
-                dl = softplus ? softplus_f32(x) : x;
-                kk = dl * uu;
-                if (MODE == kFull) {
-                    Du[j] = Dd * uu;
-                    if (z) g[j] = silu_f32(io<IO>::ld(z, idx));
+            for (int s = 0; s < S; ++s) h[s] = cstate[(((int64_t)b * nchunk + c - 1) * D + d) * N + w * S + s];
+        }
+        float Dq[V], bq[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            const bool ok = qact && (VEC || d0 + cq + v < D);
+            Dq[v] = (ok && Dv) ? Dv[dq + v] : 0.0f;
+            bq[v] = (ok && bias) ? bias[dq + v] : 0.0f;
+        }
+        float dsum = 0.0f;
+
+        // Raw inputs of one tile.  The next tile's loads are issued before the current
+        // tile's recurrence so that their latency is hidden behind it; indices are clamped
+        // so every load is in bounds.
+        uint32_t ru[P][W], rd[P][W], rz[P][W];
+        auto load_tile = [&](int64_t t0) {
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const int64_t t = min(t0 + (p * RPP + rsub), t_end - 1);
+                const int64_t idx = (row0 + t) * D + dq;
+                if constexpr (VEC) {
+                    VIO::load(u, idx, ru[p]);
+                    VIO::load(delta, idx, rd[p]);
+                    if (gated) VIO::load(z, idx, rz[p]);
+                } else {
+                    ru[p][0] = __float_as_uint(io<IO>::ld(u, idx));
+                    rd[p][0] = __float_as_uint(io<IO>::ld(delta, idx));
+                    rz[p][0] = gated ? __float_as_uint(io<IO>::ld(z, idx)) : 0u;
                 }
             }
-            s_dk[tt][lane] = f32x2_t{dl, kk};
+        };
+        auto raw = [&](const uint32_t (&r)[W], int v) -> float {
+            if constexpr (VEC) return VIO::get(r, v);
+            else return __uint_as_float(r[0]);
+        };
+        load_tile(t_begin);
+        if (MODE == kChained && c > 0) {
+            // wait (with the first tile already in flight) until the previous chunk of this
+            // tile has published its final state
+            if (tid == 0) {
+                unsigned spins = 0;
+                while (__hip_atomic_load(&sched[1 + tile], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < c) {
+                    if (++spins > kSpinLimit) {
+                        __hip_atomic_store(&sched[1 + n_tiles], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+                h[s] = __hip_atomic_load(&cstate[((int64_t)tile * kChanTile + lane) * N + w * S + s],
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        __syncthreads();
-        // recurrence over the tile
-        const float *__restrict__ bct = bcw + t0 * (2 * S);
+
+        for (int64_t t0 = t_begin; t0 < t_end; t0 += T) {
+            const int nt = (int)min((int64_t)T, t_end - t0);
+            float Du[P][V], g[P][V];
+            // prep: (delta, delta*u) into LDS; skip and gate factors kept in registers
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const int tt = p * RPP + rsub;
+                const bool valid = qact && tt < nt;
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    const float uu = raw(ru[p], v);
+                    const float x = raw(rd[p], v) + bq[v];
+                    const float dl = softplus ? softplus_f32(x) : x;
+                    const bool ok = valid && (VEC || d0 + cq + v < D);
+                    s_dk[tt][cq + v] = ok ? f32x2_t{dl, dl * uu} : f32x2_t{0.0f, 0.0f};
+                    if (READOUT) {
+                        Du[p][v] = Dq[v] * uu;
+                        g[p][v] = gated ? silu_f32(raw(rz[p], v)) : 1.0f;
+                    }
+                }
+            }
+            if (t0 + T < t_end) load_tile(t0 + T);
+            __syncthreads();
+            // recurrence over the tile: lane = channel, this wave's S states
 #pragma unroll 4
-        for (int tt = 0; tt < nt; ++tt) {
-            const f32x2_t v = s_dk[tt][lane];
-            float acc = 0.0f;
+            for (int tt = 0; tt < nt; ++tt) {
+                const f32x2_t v = s_dk[tt][lane];
+                const int64_t boff = (row0 + t0 + tt) * N + w * S;
+                float Bs[S], Cs[S];
+                load_slice<S>(Bm, boff, Bs);
+                if (READOUT) load_slice<S>(Cm, boff, Cs);
+                float acc = 0.0f;
 #pragma unroll
-            for (int s = 0; s < S; ++s) {
-                const float e = hw_exp2(v.x * a2[s]);
-                h[s] = fmaf(e, h[s], v.y * bct[tt * (2 * S) + s]);
-                if (MODE == kFull) acc = fmaf(bct[tt * (2 * S) + S + s], h[s], acc);
+                for (int s = 0; s < S; ++s) {
+                    const float e = hw_exp2(v.x * a2[s]);
+                    h[s] = fmaf(e, h[s], v.y * Bs[s]);
+                    if (READOUT) acc = fmaf(Cs[s], h[s], acc);
+                }
+                if (READOUT)
+                    s_yp[w][tt][lane] = acc;
+                else
+                    dsum += v.x;
             }
-            if (MODE == kFull)
-                s_yp[w][tt][lane] = acc;
-            else
-                dsum += v.x;
-        }
-        __syncthreads();
-        if (MODE == kFull) {
-            // epilogue: y = (sum of the K partial readouts + D u) * silu(z)
+            __syncthreads();
+            if (READOUT) {
+                // epilogue: y = (sum of the K partial readouts + D u) * silu(z)
 #pragma unroll
-            for (int j = 0; j < J; ++j) {
-                const int tt = w + j * K;
-                if (tt < nt && act) {
-                    float yv = Du[j];
+                for (int p = 0; p < P; ++p) {
+                    const int tt = p * RPP + rsub;
+                    if (tt < nt && qact) {
+                        float yv[V];
 #pragma unroll
-                    for (int k = 0; k < K; ++k) yv += s_yp[k][tt][lane];
-                    yv *= g[j];
-                    io<IO>::st(y, (row0 + t0 + tt) * D + d, yv);
+                        for (int v = 0; v < V; ++v) {
+                            float a = Du[p][v];
+#pragma unroll
+                            for (int k = 0; k < K; ++k) a += s_yp[k][tt][cq + v];
+                            yv[v] = a * g[p][v];
+                        }
+                        const int64_t idx = (row0 + t0 + tt) * D + d0 + cq;
+                        if constexpr (VEC) {
+                            VIO::store(y, idx, yv);
+                        } else {
+                            io<IO>::st(y, idx, yv[0]);
+                        }
+                    }
                 }
             }
         }
-    }
 
-    if (!act) return;
-    if (MODE == kFull) {
-        if (last_state && c == nchunk - 1) {
+        if (MODE == kSummary) {
+            if (act) {
 #pragma unroll
-            for (int s = 0; s < S; ++s) last_state[((int64_t)b * D + d) * N + w * S + s] = h[s];
+                for (int s = 0; s < S; ++s) cstate[(((int64_t)b * nchunk + c) * D + d) * N + w * S + s] = h[s];
+                if (w == 0) cdsum[((int64_t)b * nchunk + c) * D + d] = dsum;
+            }
+        } else if (c == nchunk - 1) {
+            if (last_state && act) {
+#pragma unroll
+                for (int s = 0; s < S; ++s) last_state[((int64_t)b * D + d) * N + w * S + s] = h[s];
+            }
+        } else if (MODE == kChained) {
+            // publish this chunk's final state to the next chunk of the tile
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+                __hip_atomic_store(&cstate[((int64_t)tile * kChanTile + lane) * N + w * S + s], h[s],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __threadfence();
+            __syncthreads();
+            if (tid == 0) __hip_atomic_store(&sched[1 + tile], c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         }
-    } else {
-#pragma unroll
-        for (int s = 0; s < S; ++s) cstate[(((int64_t)b * nchunk + c) * D + d) * N + w * S + s] = h[s];
-        if (w == 0) cdsum[((int64_t)b * nchunk + c) * D + d] = dsum;
+        if (MODE != kChained) break;
+        item = claim();
     }
 }
 
-// Writes zeros (a scan of zero tokens leaves the zero initial state).
-__global__ void __launch_bounds__(256) fill_zero_kernel(float *__restrict__ p, int64_t n) {
+// Writes zeros (a scan of zero tokens leaves the zero initial state; also clears the
+// scheduling words of the chained mode).
+template <typename TP>
+__global__ void __launch_bounds__(256) fill_zero_kernel(TP *__restrict__ p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) p[i] = 0.0f;
+    if (i < n) p[i] = TP(0);
 }
 
 }  // namespace ssm

@@ -60,11 +60,31 @@ int check_dims(const ssm_dims *dm, bool scan) {
     return SSM_OK;
 }
 
+enum Schedule { kGrid = 0, kChain = 1, kCarry = 2 };
+
 struct Plan {
-    int64_t nchunk = 1;
-    int64_t chunk_len = 0;
+    int schedule = kGrid;
+    int64_t nchunk = 1;      // chunks per sequence (work items per tile)
+    int64_t chunk_len = 0;   // tokens per chunk
     size_t off_cstate = 0, off_cdsum = 0, bytes = 0;
 };
+
+// Workgroups of the scan kernel resident at once on the current device (for the
+// persistent chained schedule): occupancy per CU x CU count, cached per kernel.
+template <typename F>
+int resident_groups(F kernel, int block, int *cache) {
+    if (*cache > 0) return *cache;
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess) return 0;
+    *cache = cus * (per_cu > 0 ? per_cu : 1);
+    return *cache;
+}
+
+constexpr int64_t kChainMinTiles = 256;   // enough channel tiles to fill the GPU in one pass
+constexpr int64_t kChainItemsPerGroup = 8;
+constexpr int64_t kAssumedGroups = 768;   // 3 resident workgroups per CU on 256 CUs
 
 Plan make_plan(const ssm_dims *dm) {
     Plan p;
@@ -73,72 +93,122 @@ Plan make_plan(const ssm_dims *dm) {
     const int64_t tiles = bsz * ((D + ssm::kChanTile - 1) / ssm::kChanTile);
     int64_t clen = L;
     if (dm->chunk_len > 0) {
+        p.schedule = kCarry;
         clen = dm->chunk_len < L ? dm->chunk_len : L;
         if ((L + clen - 1) / clen > kMaxChunks) clen = (L + kMaxChunks - 1) / kMaxChunks;
-    } else if (dm->chunk_len == 0 && tiles < 512) {
+    } else if (dm->chunk_len == 0 && tiles >= kChainMinTiles) {
+        // enough tiles: one pass, chained chunks so that every CU gets the same work
+        p.schedule = kChain;
+        int64_t nck = (kChainItemsPerGroup * kAssumedGroups + tiles - 1) / tiles;
+        const int64_t most = (L + 127) / 128;
+        if (nck > most) nck = most;
+        if (nck < 1) nck = 1;
+        clen = (L + nck - 1) / nck;
+        clen = (clen + 31) / 32 * 32;
+    } else if (dm->chunk_len == 0) {
         // too few channel tiles to fill the GPU: split the tokens too, keeping chunks at
-        // least 8 LDS tiles long so that the extra summary and carry passes stay cheap
+        // least 256 tokens long so that the extra summary and carry passes stay cheap
         const int64_t want = (kTargetGroups + tiles - 1) / tiles;
-        const int64_t most = (L + 8 * ssm::kTileT - 1) / (8 * ssm::kTileT);
+        const int64_t most = (L + 255) / 256;
         int64_t nchunk = want < most ? want : most;
         if (nchunk < 1) nchunk = 1;
         if (nchunk > kMaxChunks) nchunk = kMaxChunks;
         if (nchunk > 1) {
+            p.schedule = kCarry;
             clen = (L + nchunk - 1) / nchunk;
-            clen = (clen + ssm::kTileT - 1) / ssm::kTileT * ssm::kTileT;
+            clen = (clen + 31) / 32 * 32;
         }
     }
     p.chunk_len = clen;
     p.nchunk = (L + clen - 1) / clen;
-    size_t bc = align256((size_t)(bsz * L * 2 * N) * sizeof(float));
-    p.off_cstate = bc;
-    p.off_cdsum = bc;
-    p.bytes = bc;
-    if (p.nchunk > 1) {
+    if (p.schedule == kCarry && p.nchunk == 1) p.schedule = kGrid;
+    if (p.schedule == kCarry) {
         size_t cs = align256((size_t)(bsz * p.nchunk * D * N) * sizeof(float));
         size_t cd = align256((size_t)(bsz * p.nchunk * D) * sizeof(float));
-        p.off_cdsum = bc + cs;
-        p.bytes = bc + cs + cd;
+        p.off_cstate = 0;
+        p.off_cdsum = cs;
+        p.bytes = cs + cd;
+    } else if (p.schedule == kChain) {
+        size_t sc = align256((size_t)(tiles + 2) * sizeof(int));
+        size_t slots = align256((size_t)(tiles * ssm::kChanTile * N) * sizeof(float));
+        p.off_cstate = sc;
+        p.off_cdsum = 0;
+        p.bytes = sc + slots;
     }
     return p;
 }
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Kernel shape per state size: S states per wave (K = N/S waves per workgroup) and T
+// tokens per LDS tile.
+template <int N> struct ScanShape;
+template <> struct ScanShape<1> { static constexpr int S = 1, T = 32; };
+template <> struct ScanShape<2> { static constexpr int S = 2, T = 32; };
+template <> struct ScanShape<4> { static constexpr int S = 4, T = 32; };
+template <> struct ScanShape<8> { static constexpr int S = 4, T = 32; };
+template <> struct ScanShape<16> { static constexpr int S = 4, T = 32; };
+
+template <int N, typename IO, bool VEC>
+void launch_scan_kernels(const IO *u, const IO *dl, const float *A, const IO *B, const IO *C, const float *Dv,
+                         const IO *z, const float *bias, int softplus, IO *y, float *last_state,
+                         const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st) {
+    constexpr int S = ScanShape<N>::S;
+    constexpr int T = ScanShape<N>::T;
+    constexpr int K = N / S;
+    const int64_t bsz = dm->batch, L = dm->seqlen, D = dm->dim;
+    const int tiles_per_b = (int)((D + ssm::kChanTile - 1) / ssm::kChanTile);
+    const int n_tiles = (int)(bsz * tiles_per_b);
+    const dim3 block(64 * K);
+    float *cstate = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_cstate);
+    float *cdsum = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_cdsum);
+    int *sched = reinterpret_cast<int *>(ws);
+    const int64_t cl = p.chunk_len;
+    const int nc = (int)p.nchunk;
+    if (p.schedule == kChain) {
+        auto kern = ssm::scan_chunk_kernel<N, S, T, IO, ssm::kChained, VEC>;
+        static int cache = 0;
+        int groups = resident_groups(kern, 64 * K, &cache);
+        const int64_t items = (int64_t)n_tiles * nc;
+        if (groups <= 0 || groups > items) groups = (int)(items < kAssumedGroups ? items : kAssumedGroups);
+        const int64_t nw = n_tiles + 2;
+        hipLaunchKernelGGL(ssm::fill_zero_kernel<int>, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, st,
+                           sched, nw);
+        hipLaunchKernelGGL(kern, dim3((unsigned)groups), block, 0, st, u, dl, z, y, A, Dv, bias, B, C, last_state,
+                           cstate, (float *)nullptr, sched, L, D, tiles_per_b, n_tiles, cl, nc, softplus);
+        return;
+    }
+    if (p.schedule == kCarry) {
+        hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kSummary, VEC>),
+                           dim3((unsigned)n_tiles, (unsigned)(nc - 1)), block, 0, st, u, dl, (const IO *)nullptr,
+                           (IO *)nullptr, A, (const float *)nullptr, bias, B, C, (float *)nullptr, cstate, cdsum,
+                           (int *)nullptr, L, D, tiles_per_b, n_tiles, cl, nc, softplus);
+        const int col_tiles = (int)((D * N + 63) / 64);
+        hipLaunchKernelGGL((ssm::carry_scan_kernel<N>), dim3((unsigned)(bsz * col_tiles)), dim3(256), 0, st,
+                           cstate, (const float *)cdsum, A, D, nc, col_tiles);
+    }
+    hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kFull, VEC>), dim3((unsigned)n_tiles, (unsigned)nc),
+                       block, 0, st, u, dl, z, y, A, Dv, bias, B, C, last_state, cstate, cdsum, (int *)nullptr, L, D,
+                       tiles_per_b, n_tiles, cl, nc, softplus);
+}
+
 template <int N, typename IO>
 int launch_scan(const void *u, const void *delta, const float *A, const void *B, const void *C,
                 const float *Dv, const void *z, const float *bias, int softplus, void *y,
                 float *last_state, const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st) {
-    constexpr int S = N < 4 ? N : 4;
-    constexpr int K = N / S;
-    const int64_t bsz = dm->batch, L = dm->seqlen, D = dm->dim;
-    const int tiles_per_b = (int)((D + ssm::kChanTile - 1) / ssm::kChanTile);
-    float *bc = reinterpret_cast<float *>(ws);
-    float *cstate = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_cstate);
-    float *cdsum = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_cdsum);
     const IO *u_ = static_cast<const IO *>(u);
     const IO *dl_ = static_cast<const IO *>(delta);
     const IO *z_ = static_cast<const IO *>(z);
+    const IO *B_ = static_cast<const IO *>(B);
+    const IO *C_ = static_cast<const IO *>(C);
     IO *y_ = static_cast<IO *>(y);
-
-    const int64_t nbc = bsz * L * N;
-    hipLaunchKernelGGL((ssm::stage_bc_kernel<N, S, IO>), dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, st,
-                       static_cast<const IO *>(B), static_cast<const IO *>(C), bc, nbc, L);
-    const dim3 block(64 * K);
-    if (p.nchunk > 1) {
-        hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, IO, ssm::kSummary>),
-                           dim3((unsigned)(bsz * tiles_per_b), (unsigned)(p.nchunk - 1)), block, 0, st,
-                           u_, dl_, (const IO *)nullptr, (IO *)nullptr, A, (const float *)nullptr, bias, bc,
-                           (float *)nullptr, cstate, cdsum, L, D, tiles_per_b, p.chunk_len, (int)p.nchunk,
-                           softplus);
-        const int col_tiles = (int)((D * N + 63) / 64);
-        hipLaunchKernelGGL((ssm::carry_scan_kernel<N>), dim3((unsigned)(bsz * col_tiles)), dim3(256), 0, st,
-                           cstate, (const float *)cdsum, A, D, (int)p.nchunk, col_tiles);
-    }
-    hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, IO, ssm::kFull>),
-                       dim3((unsigned)(bsz * tiles_per_b), (unsigned)p.nchunk), block, 0, st,
-                       u_, dl_, z_, y_, A, Dv, bias, bc, last_state, cstate, cdsum, L, D, tiles_per_b,
-                       p.chunk_len, (int)p.nchunk, softplus);
+    // 16-byte prep/epilogue accesses need whole groups of 8 channels and aligned rows
+    const bool vec = dm->dim % 8 == 0 && aligned(u, 16) && aligned(delta, 16) && aligned(y, 16) &&
+                     (!z || aligned(z, 16));
+    if (vec)
+        launch_scan_kernels<N, IO, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, y_, last_state, dm, p, ws, st);
+    else
+        launch_scan_kernels<N, IO, false>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, y_, last_state, dm, p, ws, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -204,7 +274,7 @@ int64_t ssm_scan_plan(const ssm_dims *dims, int64_t *chunk_len_out) {
     Plan p = make_plan(dims);
     if (chunk_len_out) *chunk_len_out = p.chunk_len;
     ok();
-    return p.nchunk;
+    return p.schedule == kCarry ? p.nchunk : 1;
 }
 
 int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
@@ -220,7 +290,7 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
         if (last_state) {
             if (!aligned(last_state, 4)) return fail(SSM_ERR_ALIGN, "last_state not 4-byte aligned");
             const int64_t n = bsz * Dm * N;
-            hipLaunchKernelGGL(ssm::fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+            hipLaunchKernelGGL(ssm::fill_zero_kernel<float>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                                last_state, n);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -235,12 +305,14 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
         (z && !aligned(z, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
         (delta_bias && !aligned(delta_bias, 4)) || (last_state && !aligned(last_state, 4)))
         return fail(SSM_ERR_ALIGN, "a tensor pointer is not aligned to its element size");
+    if (dims->io_dtype == SSM_IO_BF16 && N >= 2 && (!aligned(B, 4) || !aligned(C, 4)))
+        return fail(SSM_ERR_ALIGN, "bf16 B and C must be 4-byte aligned");
     Plan p = make_plan(dims);
-    if (!workspace) return fail(SSM_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", p.bytes);
+    if (p.bytes > 0 && !workspace) return fail(SSM_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", p.bytes);
     if (workspace_bytes < p.bytes)
         return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
                     p.bytes);
-    if (!aligned(workspace, 16)) return fail(SSM_ERR_ALIGN, "workspace not 16-byte aligned");
+    if (p.bytes > 0 && !aligned(workspace, 16)) return fail(SSM_ERR_ALIGN, "workspace not 16-byte aligned");
     if (dims->io_dtype == SSM_IO_BF16)
         return dispatch_scan<uint16_t>(N, u, delta, A, B, C, D, z, delta_bias, softplus_flag != 0, y, last_state,
                                        dims, p, workspace, st);

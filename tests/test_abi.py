@@ -88,9 +88,9 @@ def test_bad_shape(b, kw):
 
 
 def test_workspace_too_small(b):
-    d = _dims(b)
+    d = _dims(b, chunk_len=16)   # 4 chunks per sequence: carry states need workspace
     need = b.lib.ssm_scan_workspace_bytes(ctypes.byref(d))
-    assert need >= 2 * 64 * 2 * 16 * 4
+    assert need >= 2 * 4 * 128 * 16 * 4
     assert _scan(b, d, ws_bytes=need - 1) == -6
     assert _scan(b, d, ws=0) == -6
 
@@ -98,7 +98,8 @@ def test_workspace_too_small(b):
 def test_misaligned_rejected(b):
     assert _scan(b, _dims(b), u=FAKE + 1) == -4
     assert _scan(b, _dims(b, io_dtype=0), y=FAKE + 2) == -4
-    assert _scan(b, _dims(b), ws=FAKE + 8) == -4
+    assert _scan(b, _dims(b, chunk_len=16), ws=FAKE + 8) == -4
+    assert _scan(b, _dims(b), B=FAKE + 2) == -4    # bf16 B/C are read as 32-bit words
 
 
 def test_step_validation(b):
@@ -119,13 +120,17 @@ def test_empty_problems_are_noops(b):
 
 
 def test_plan(b):
-    # the B8 L2048 D5120 layer fills the GPU with channel tiles: one pass
-    assert b.scan_plan(8, 2048, 5120, 16, 1) == (1, 2048)
+    # the B8 L2048 D5120 layer fills the GPU with channel tiles: one pass over every token,
+    # as chained work items of a few hundred tokens
+    n, cl = b.scan_plan(8, 2048, 5120, 16, 1)
+    assert n == 1 and 128 <= cl <= 2048 and cl % 32 == 0
     # the long B1 L131072 D2048 sequence has 32 channel tiles: split into chunks
     n, cl = b.scan_plan(1, 131072, 2048, 16, 1)
     assert n > 8 and cl % 32 == 0 and n * cl >= 131072 and (n - 1) * cl < 131072
     assert b.scan_plan(2, 300, 70, 4, 0, chunk_len=64) == (5, 64)
     assert b.scan_plan(2, 300, 70, 4, 0, chunk_len=-1) == (1, 300)
     assert b.scan_plan(1, 256, 16, 4, 0) == (1, 256)
-    # workspace grows with the chunk carry
+    # a grid-mapped single pass needs no workspace; the chained pass and the chunk carry do
+    assert b.workspace_bytes(8, 2048, 5120, 16, 1, chunk_len=-1) == 0
+    assert b.workspace_bytes(8, 2048, 5120, 16, 1) >= 640 * 64 * 16 * 4
     assert b.workspace_bytes(1, 4096, 64, 16, 1, chunk_len=128) > b.workspace_bytes(1, 4096, 64, 16, 1, chunk_len=-1)

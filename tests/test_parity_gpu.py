@@ -80,6 +80,24 @@ def test_ragged_multi_tile(oracle_mod, io, N, chunk_len):
     check(case, y, ls, y_ref, ls_ref, f"chunk_len={chunk_len}")
 
 
+@pytest.mark.parametrize("shape,io", [((4, 777, 4096), "bf16"), ((5, 600, 3300), "bf16"), ((4, 500, 4096), "f32"),
+                                      ((64, 96, 256), "bf16")])
+def test_chained_schedule(oracle_mod, shape, io):
+    """Enough channel tiles for the persistent chained schedule (chunk_len = 0): the state of
+    each tile is handed from chunk to chunk between workgroups.  Ragged L, ragged D (no
+    16-byte path when D % 8 != 0) and many short sequences; sampled channels."""
+    bsz, L, D = shape
+    case = inputs.scan_case(bsz, L, D, 16, io, gate=True, seed=21)
+    n, cl = ssmscan.scan_plan(bsz, L, D, 16, torch.bfloat16 if io == "bf16" else torch.float32)
+    assert n == 1
+    y, ls = run_gpu(case)
+    sel = _sample_channels(D, 24, 3)
+    y_ref, ls_ref = run_oracle(oracle_mod, case, channels=sel)
+    check(case, y[:, :, sel], ls[:, sel], y_ref, ls_ref, f"chained items of {cl} tokens")
+    y2, ls2 = run_gpu(case)
+    assert np.array_equal(y, y2) and np.array_equal(ls, ls2)
+
+
 @pytest.mark.parametrize("drop", [(), ("D",), ("z",), ("delta_bias",), ("D", "z", "delta_bias")])
 @pytest.mark.parametrize("softplus", [True, False])
 def test_optional_inputs(oracle_mod, drop, softplus):
