@@ -25,7 +25,8 @@
 //    (tile, chunk) items from an atomic counter in chunk-major order and hand the fp32
 //    state of a tile from one chunk to the next through a per-tile slot and a progress
 //    word (release / acquire at device scope).  Every token is still processed exactly
-//    once, but all CUs get equal work whatever the number of tiles.  A workgroup only
+//    once; with more tiles than resident workgroups all CUs get equal work instead of a
+//    partly idle last round of the grid.  A workgroup only
 //    waits for an item claimed before its own, whose workgroup is running, so the chain
 //    always drains; the wait is bounded and, if the bound is ever hit, an error word is
 //    raised instead of hanging.
@@ -43,6 +44,19 @@ enum ScanMode { kFull = 0, kSummary = 1, kChained = 2 };
 //   sched[0] work counter, sched[1 + tile] chunks of the tile completed,
 //   sched[1 + n_tiles] error word (nonzero if a wait hit its bound).
 constexpr unsigned kSpinLimit = 1u << 24;
+
+// s_waitcnt immediate that waits for all LDS and scalar-memory operations (lgkmcnt = 0) and
+// leaves the vector-memory and export counters unconstrained (gfx9 encoding).
+constexpr int kWaitLgkm0 = 0xC07F;
+
+// Element s of a slice of B or C held as raw 32-bit words (bf16 pairs, low half first).
+template <typename IO, int BW>
+__device__ __forceinline__ float word_f32(const uint32_t (&w)[BW], int s) {
+    if constexpr (sizeof(IO) == 2)
+        return __uint_as_float((s & 1) ? (w[s >> 1] & 0xffff0000u) : (w[s >> 1] << 16));
+    else
+        return __uint_as_float(w[s]);
+}
 
 // S consecutive B or C values starting at element `off` (a wave-uniform offset), widened
 // to fp32.  bf16 pairs are read as 32-bit words (the offset is even whenever S is).
@@ -93,6 +107,10 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     static_assert(T % K == 0 && J % V == 0 && RPP * P == T, "tile must split evenly over the threads");
     using VIO = vec<V, IO>;
     constexpr int W = VEC ? V * (int)sizeof(IO) / 4 : 1;
+    // token loop pipelining: groups of G tokens; B / C slices read as BW 32-bit words
+    constexpr bool PIPE = !(sizeof(IO) == 2 && S % 2 == 1) && T % 8 == 0;
+    constexpr int G = 4;
+    constexpr int BW = PIPE ? S * (int)sizeof(IO) / 4 : 1;
     __shared__ f32x2_t s_dk[T][kChanTile];
     __shared__ float s_yp[READOUT ? K : 1][T][kChanTile];
     __shared__ int s_item;
@@ -178,15 +196,18 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
         if (MODE == kChained && c > 0) {
             // wait (with the first tile already in flight) until the previous chunk of this
             // tile has published its final state
+            // (polled with relaxed loads: an acquire on every poll would invalidate the L2
+            // each time; one acquire fence follows the wait)
             if (tid == 0) {
                 unsigned spins = 0;
-                while (__hip_atomic_load(&sched[1 + tile], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < c) {
+                while (__hip_atomic_load(&sched[1 + tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < c) {
                     if (++spins > kSpinLimit) {
                         __hip_atomic_store(&sched[1 + n_tiles], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         break;
                     }
-                    __builtin_amdgcn_s_sleep(2);
+                    __builtin_amdgcn_s_sleep(4);
                 }
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             }
             __syncthreads();
 #pragma unroll
@@ -219,24 +240,80 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
             if (t0 + T < t_end) load_tile(t0 + T);
             __syncthreads();
             // recurrence over the tile: lane = channel, this wave's S states
-#pragma unroll 4
-            for (int tt = 0; tt < nt; ++tt) {
-                const f32x2_t v = s_dk[tt][lane];
-                const int64_t boff = (row0 + t0 + tt) * N + w * S;
-                float Bs[S], Cs[S];
-                load_slice<S>(Bm, boff, Bs);
-                if (READOUT) load_slice<S>(Cm, boff, Cs);
-                float acc = 0.0f;
+            if (PIPE && nt == T) {
+                // A full tile, software-pipelined in groups of G tokens (two register sets,
+                // ping-pong): after the wait for the current group, the LDS (delta, delta*u)
+                // reads and the scalar B / C loads of the next group are issued, then the
+                // current group is computed.  All indices are compile-time constants.
+                f32x2_t va[G], vb[G];
+                uint32_t ba[G][BW], ca[G][BW], bb[G][BW], cb[G][BW];
+                const IO *btile = Bm + (row0 + t0) * N + w * S;
+                const IO *ctile = Cm + (row0 + t0) * N + w * S;
+                auto gload = [&](int g0, f32x2_t (&v)[G], uint32_t (&bw)[G][BW], uint32_t (&cw)[G][BW]) {
 #pragma unroll
-                for (int s = 0; s < S; ++s) {
-                    const float e = hw_exp2(v.x * a2[s]);
-                    h[s] = fmaf(e, h[s], v.y * Bs[s]);
-                    if (READOUT) acc = fmaf(Cs[s], h[s], acc);
+                    for (int i = 0; i < G; ++i) {
+                        // the prefetch after the last group runs past the tile: clamp (unused)
+                        const int tt = g0 + i < T ? g0 + i : T - 1;
+                        v[i] = s_dk[tt][lane];
+                        const uint32_t *bp = reinterpret_cast<const uint32_t *>(btile + tt * N);
+                        const uint32_t *cp = reinterpret_cast<const uint32_t *>(ctile + tt * N);
+#pragma unroll
+                        for (int k = 0; k < BW; ++k) {
+                            bw[i][k] = bp[k];
+                            cw[i][k] = READOUT ? cp[k] : 0u;
+                        }
+                    }
+                };
+                auto gcomp = [&](int g0, const f32x2_t (&v)[G], const uint32_t (&bw)[G][BW],
+                                 const uint32_t (&cw)[G][BW]) {
+#pragma unroll
+                    for (int i = 0; i < G; ++i) {
+                        float acc = 0.0f;
+#pragma unroll
+                        for (int s = 0; s < S; ++s) {
+                            const float e = hw_exp2(v[i].x * a2[s]);
+                            h[s] = fmaf(e, h[s], v[i].y * word_f32<IO>(bw[i], s));
+                            if (READOUT) acc = fmaf(word_f32<IO>(cw[i], s), h[s], acc);
+                        }
+                        if (READOUT)
+                            s_yp[w][g0 + i][lane] = acc;
+                        else
+                            dsum += v[i].x;
+                    }
+                };
+                gload(0, va, ba, ca);
+#pragma unroll
+                for (int g0 = 0; g0 < T; g0 += 2 * G) {
+                    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+                    gload(g0 + G, vb, bb, cb);
+                    __builtin_amdgcn_sched_barrier(0);
+                    gcomp(g0, va, ba, ca);
+                    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+                    gload(g0 + 2 * G, va, ba, ca);
+                    __builtin_amdgcn_sched_barrier(0);
+                    gcomp(g0 + G, vb, bb, cb);
                 }
-                if (READOUT)
-                    s_yp[w][tt][lane] = acc;
-                else
-                    dsum += v.x;
+            } else {
+                // a partial tile (or a slice shape the pipelined loop does not take)
+#pragma unroll 4
+                for (int tt = 0; tt < nt; ++tt) {
+                    const f32x2_t v = s_dk[tt][lane];
+                    const int64_t boff = (row0 + t0 + tt) * N + w * S;
+                    float Bs[S], Cs[S];
+                    load_slice<S>(Bm, boff, Bs);
+                    if (READOUT) load_slice<S>(Cm, boff, Cs);
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int s = 0; s < S; ++s) {
+                        const float e = hw_exp2(v.x * a2[s]);
+                        h[s] = fmaf(e, h[s], v.y * Bs[s]);
+                        if (READOUT) acc = fmaf(Cs[s], h[s], acc);
+                    }
+                    if (READOUT)
+                        s_yp[w][tt][lane] = acc;
+                    else
+                        dsum += v.x;
+                }
             }
             __syncthreads();
             if (READOUT) {

@@ -82,9 +82,12 @@ int resident_groups(F kernel, int block, int *cache) {
     return *cache;
 }
 
-constexpr int64_t kChainMinTiles = 256;   // enough channel tiles to fill the GPU in one pass
-constexpr int64_t kChainItemsPerGroup = 8;
+// The chained schedule pays off when there are more channel tiles than workgroups
+// resident at once (a grid would leave its last round partly idle); with fewer tiles every
+// tile already gets its own resident workgroup and the grid is used.
 constexpr int64_t kAssumedGroups = 768;   // 3 resident workgroups per CU on 256 CUs
+constexpr int64_t kChainMinTiles = kAssumedGroups + 1;
+constexpr int64_t kChainItemsPerGroup = 8;
 
 Plan make_plan(const ssm_dims *dm) {
     Plan p;
@@ -96,7 +99,7 @@ Plan make_plan(const ssm_dims *dm) {
         p.schedule = kCarry;
         clen = dm->chunk_len < L ? dm->chunk_len : L;
         if ((L + clen - 1) / clen > kMaxChunks) clen = (L + kMaxChunks - 1) / kMaxChunks;
-    } else if (dm->chunk_len == 0 && tiles >= kChainMinTiles) {
+    } else if (dm->chunk_len == 0 && tiles >= kChainMinTiles && L >= 256) {
         // enough tiles: one pass, chained chunks so that every CU gets the same work
         p.schedule = kChain;
         int64_t nck = (kChainItemsPerGroup * kAssumedGroups + tiles - 1) / tiles;
@@ -105,7 +108,7 @@ Plan make_plan(const ssm_dims *dm) {
         if (nck < 1) nck = 1;
         clen = (L + nck - 1) / nck;
         clen = (clen + 31) / 32 * 32;
-    } else if (dm->chunk_len == 0) {
+    } else if (dm->chunk_len == 0 && tiles < 512) {
         // too few channel tiles to fill the GPU: split the tokens too, keeping chunks at
         // least 256 tokens long so that the extra summary and carry passes stay cheap
         const int64_t want = (kTargetGroups + tiles - 1) / tiles;

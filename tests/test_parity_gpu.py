@@ -80,12 +80,13 @@ def test_ragged_multi_tile(oracle_mod, io, N, chunk_len):
     check(case, y, ls, y_ref, ls_ref, f"chunk_len={chunk_len}")
 
 
-@pytest.mark.parametrize("shape,io", [((4, 777, 4096), "bf16"), ((5, 600, 3300), "bf16"), ((4, 500, 4096), "f32"),
-                                      ((64, 96, 256), "bf16")])
+@pytest.mark.parametrize("shape,io", [((13, 777, 4096), "bf16"), ((16, 300, 3300), "bf16"), ((13, 260, 4096), "f32"),
+                                      ((50, 300, 1024), "bf16")])
 def test_chained_schedule(oracle_mod, shape, io):
-    """Enough channel tiles for the persistent chained schedule (chunk_len = 0): the state of
-    each tile is handed from chunk to chunk between workgroups.  Ragged L, ragged D (no
-    16-byte path when D % 8 != 0) and many short sequences; sampled channels."""
+    """More channel tiles than resident workgroups, so the persistent chained schedule is
+    used (chunk_len = 0): the state of each tile is handed from chunk to chunk between
+    workgroups.  Ragged L, ragged D (no 16-byte path when D % 8 != 0) and many short
+    sequences; sampled channels."""
     bsz, L, D = shape
     case = inputs.scan_case(bsz, L, D, 16, io, gate=True, seed=21)
     n, cl = ssmscan.scan_plan(bsz, L, D, 16, torch.bfloat16 if io == "bf16" else torch.float32)
