@@ -123,6 +123,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     const int rsub = tid / GPR;
     const int cq = (tid % GPR) * V;
     const bool gated = READOUT && z != nullptr;
+    const IO *__restrict__ zsrc = gated ? z : u;
     const int64_t n_items = (int64_t)n_tiles * nchunk;
 
     // Work items.  The claimed index is broadcast through LDS and read back with
@@ -168,23 +169,26 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
         }
         float dsum = 0.0f;
 
-        // Raw inputs of one tile.  The next tile's loads are issued before the current
-        // tile's recurrence so that their latency is hidden behind it; indices are clamped
-        // so every load is in bounds.
-        uint32_t ru[P][W], rd[P][W], rz[P][W];
-        auto load_tile = [&](int64_t t0) {
+        // Raw inputs of a tile, in two register buffers: the loads of tile i+2 are issued
+        // as soon as tile i has been read out of its buffer, so that two tiles of recurrence
+        // hide their latency; indices are clamped so every load is in bounds.
+        struct Raw { uint32_t u[P][W], d[P][W], z[P][W]; };
+        Raw r0, r1;
+        auto load_tile = [&](int64_t t0, Raw &r) {
 #pragma unroll
             for (int p = 0; p < P; ++p) {
                 const int64_t t = min(t0 + (p * RPP + rsub), t_end - 1);
                 const int64_t idx = (row0 + t) * D + dq;
+                // (z is loaded unconditionally -- from u when there is no gate -- so that the
+                // buffer registers carry no conditional value around the loop)
                 if constexpr (VEC) {
-                    VIO::load(u, idx, ru[p]);
-                    VIO::load(delta, idx, rd[p]);
-                    if (gated) VIO::load(z, idx, rz[p]);
+                    VIO::load(u, idx, r.u[p]);
+                    VIO::load(delta, idx, r.d[p]);
+                    VIO::load(zsrc, idx, r.z[p]);
                 } else {
-                    ru[p][0] = __float_as_uint(io<IO>::ld(u, idx));
-                    rd[p][0] = __float_as_uint(io<IO>::ld(delta, idx));
-                    rz[p][0] = gated ? __float_as_uint(io<IO>::ld(z, idx)) : 0u;
+                    r.u[p][0] = __float_as_uint(io<IO>::ld(u, idx));
+                    r.d[p][0] = __float_as_uint(io<IO>::ld(delta, idx));
+                    r.z[p][0] = __float_as_uint(io<IO>::ld(zsrc, idx));
                 }
             }
         };
@@ -192,7 +196,8 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
             if constexpr (VEC) return VIO::get(r, v);
             else return __uint_as_float(r[0]);
         };
-        load_tile(t_begin);
+        load_tile(t_begin, r0);
+        load_tile(t_begin + T, r1);
         if (MODE == kChained && c > 0) {
             // wait (with the first tile already in flight) until the previous chunk of this
             // tile has published its final state
@@ -216,9 +221,42 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 
-        for (int64_t t0 = t_begin; t0 < t_end; t0 += T) {
-            const int nt = (int)min((int64_t)T, t_end - t0);
-            float Du[P][V], g[P][V];
+        // epilogue of a tile: y = (sum of the K partial readouts + D u) * silu(z), read from
+        // s_yp after the recurrence of that tile
+        // (the skip term is applied as one explicit FMA, D u + partial_0, so that no tile
+        // position is left to the compiler's choice of contraction: results are bitwise the
+        // same wherever a tile falls)
+        struct DG { float u[P][V], g[P][V]; };
+        auto epilogue = [&](int64_t t0, const DG &dg) {
+            if (!READOUT) return;
+            const int nt = (int)max((int64_t)0, min((int64_t)T, t_end - t0));
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const int tt = p * RPP + rsub;
+                if (tt < nt && qact) {
+                    float yv[V];
+#pragma unroll
+                    for (int v = 0; v < V; ++v) {
+                        float a = fmaf(Dq[v], dg.u[p][v], s_yp[0][tt][cq + v]);
+#pragma unroll
+                        for (int k = 1; k < K; ++k) a += s_yp[k][tt][cq + v];
+                        yv[v] = a * dg.g[p][v];
+                    }
+                    const int64_t idx = (row0 + t0 + tt) * D + d0 + cq;
+                    if constexpr (VEC) {
+                        VIO::store(y, idx, yv);
+                    } else {
+                        io<IO>::st(y, idx, yv[0]);
+                    }
+                }
+            }
+        };
+        // One tile: the prep of this tile (from loads issued two tiles ago), the epilogue of
+        // the previous tile (its stores then retire while this tile runs), the prefetch of the
+        // tile after next into the buffer just read, and the recurrence.  A tile past the end
+        // is empty (nt = 0).
+        auto do_tile = [&](int64_t t0, Raw &r, const DG &prev, DG &cur, bool has_prev) {
+            const int nt = (int)max((int64_t)0, min((int64_t)T, t_end - t0));
             // prep: (delta, delta*u) into LDS; skip and gate factors kept in registers
 #pragma unroll
             for (int p = 0; p < P; ++p) {
@@ -226,18 +264,24 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                 const bool valid = qact && tt < nt;
 #pragma unroll
                 for (int v = 0; v < V; ++v) {
-                    const float uu = raw(ru[p], v);
-                    const float x = raw(rd[p], v) + bq[v];
+                    const float uu = raw(r.u[p], v);
+                    const float x = raw(r.d[p], v) + bq[v];
                     const float dl = softplus ? softplus_f32(x) : x;
                     const bool ok = valid && (VEC || d0 + cq + v < D);
                     s_dk[tt][cq + v] = ok ? f32x2_t{dl, dl * uu} : f32x2_t{0.0f, 0.0f};
                     if (READOUT) {
-                        Du[p][v] = Dq[v] * uu;
-                        g[p][v] = gated ? silu_f32(raw(rz[p], v)) : 1.0f;
+                        cur.u[p][v] = uu;
+                        cur.g[p][v] = gated ? silu_f32(raw(r.z[p], v)) : 1.0f;
                     }
                 }
             }
-            if (t0 + T < t_end) load_tile(t0 + T);
+            __builtin_amdgcn_sched_barrier(0);
+            if (has_prev) epilogue(t0 - T, prev);
+            // (issued only after the prep has read the buffer, and unconditionally -- past the
+            // end the clamped loads are merely redundant -- so that the loads land in the same
+            // registers, with no copies and no wait for them at the loop back-edge)
+            __builtin_amdgcn_sched_barrier(0);
+            load_tile(t0 + 2 * T, r);
             __syncthreads();
             // recurrence over the tile: lane = channel, this wave's S states
             if (PIPE && nt == T) {
@@ -316,29 +360,18 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                 }
             }
             __syncthreads();
-            if (READOUT) {
-                // epilogue: y = (sum of the K partial readouts + D u) * silu(z)
-#pragma unroll
-                for (int p = 0; p < P; ++p) {
-                    const int tt = p * RPP + rsub;
-                    if (tt < nt && qact) {
-                        float yv[V];
-#pragma unroll
-                        for (int v = 0; v < V; ++v) {
-                            float a = Du[p][v];
-#pragma unroll
-                            for (int k = 0; k < K; ++k) a += s_yp[k][tt][cq + v];
-                            yv[v] = a * g[p][v];
-                        }
-                        const int64_t idx = (row0 + t0 + tt) * D + d0 + cq;
-                        if constexpr (VEC) {
-                            VIO::store(y, idx, yv);
-                        } else {
-                            io<IO>::st(y, idx, yv[0]);
-                        }
-                    }
-                }
-            }
+        };
+        // tiles in pairs (two input buffers, two skip/gate sets); the second tile of the last
+        // pair may be empty, and its epilogue-of-the-previous-tile still runs
+        DG dg0, dg1;
+        for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * T) {
+            do_tile(t0, r0, dg1, dg0, t0 > t_begin);
+            do_tile(t0 + T, r1, dg0, dg1, true);
+        }
+        {
+            // the last pair's second tile (empty or not) still owes its epilogue
+            const int64_t npair = (t_end - t_begin + 2 * T - 1) / (2 * T);
+            epilogue(t_begin + (2 * npair - 1) * T, dg1);
         }
 
         if (MODE == kSummary) {
