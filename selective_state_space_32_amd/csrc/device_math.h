@@ -41,9 +41,15 @@ template <> struct io<uint16_t> {
     __device__ __forceinline__ static void st(uint16_t *p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
 };
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
 // V consecutive I/O elements moved as raw 32-bit words (W = V * sizeof(IO) / 4 words; bf16
 // pairs share a word, low half first).  Requires V * sizeof(IO) to be 4, 8 or a multiple of
 // 16 bytes and the address to be aligned to min(16, V * sizeof(IO)) bytes.
+// These are the streaming tensors of the scan (u, delta and z read once, y written once), so
+// the accesses are non-temporal: they then do not push out of L2 the B / C rows and the
+// per-channel parameters that every workgroup of a sequence reads again.
 template <int V, typename IO> struct vec {
     static constexpr int W = V * (int)sizeof(IO) / 4;
     static_assert(W >= 1 && (W <= 2 || W % 4 == 0), "unsupported vector width");
@@ -53,14 +59,14 @@ template <int V, typename IO> struct vec {
         if constexpr (W % 4 == 0) {
 #pragma unroll
             for (int i = 0; i < W / 4; ++i) {
-                const uint4 r = reinterpret_cast<const uint4 *>(q)[i];
+                const u32x4_t r = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(q) + i);
                 w[4 * i] = r.x; w[4 * i + 1] = r.y; w[4 * i + 2] = r.z; w[4 * i + 3] = r.w;
             }
         } else if constexpr (W == 2) {
-            const uint2 r = *reinterpret_cast<const uint2 *>(q);
+            const u32x2_t r = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(q));
             w[0] = r.x; w[1] = r.y;
         } else {
-            w[0] = q[0];
+            w[0] = __builtin_nontemporal_load(q);
         }
     }
     __device__ __forceinline__ static float get(const uint32_t (&w)[W], int v) {
@@ -81,12 +87,15 @@ template <int V, typename IO> struct vec {
         uint32_t *q = reinterpret_cast<uint32_t *>(p + idx);
         if constexpr (W % 4 == 0) {
 #pragma unroll
-            for (int i = 0; i < W / 4; ++i)
-                reinterpret_cast<uint4 *>(q)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+            for (int i = 0; i < W / 4; ++i) {
+                const u32x4_t r = {w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+                __builtin_nontemporal_store(r, reinterpret_cast<u32x4_t *>(q) + i);
+            }
         } else if constexpr (W == 2) {
-            *reinterpret_cast<uint2 *>(q) = make_uint2(w[0], w[1]);
+            const u32x2_t r = {w[0], w[1]};
+            __builtin_nontemporal_store(r, reinterpret_cast<u32x2_t *>(q));
         } else {
-            q[0] = w[0];
+            __builtin_nontemporal_store(w[0], q);
         }
     }
 };

@@ -261,14 +261,15 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
 #pragma unroll
             for (int p = 0; p < P; ++p) {
                 const int tt = p * RPP + rsub;
-                const bool valid = qact && tt < nt;
 #pragma unroll
                 for (int v = 0; v < V; ++v) {
                     const float uu = raw(r.u[p], v);
                     const float x = raw(r.d[p], v) + bq[v];
                     const float dl = softplus ? softplus_f32(x) : x;
-                    const bool ok = valid && (VEC || d0 + cq + v < D);
-                    s_dk[tt][cq + v] = ok ? f32x2_t{dl, dl * uu} : f32x2_t{0.0f, 0.0f};
+                    // (written unmasked: rows of tokens past the end are never read by the
+                    // recurrence, and lanes of channels past D hold values loaded from an
+                    // in-bounds channel and are never stored)
+                    s_dk[tt][cq + v] = f32x2_t{dl, dl * uu};
                     if (READOUT) {
                         cur.u[p][v] = uu;
                         cur.g[p][v] = gated ? silu_f32(raw(r.z[p], v)) : 1.0f;
