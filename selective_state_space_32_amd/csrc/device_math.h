@@ -104,11 +104,15 @@ template <int V, typename IO> struct vec {
 // log1p(e): w = 1 + e is rounded; the rounding error r = e - (w - 1) is exact, and
 // log1p(e) = log(w) + r/w.  r/w is taken as r: |r| <= 2^-24 and r only matters when w is
 // close to 1 (for e < 2^-24, w = 1 and the result is e itself).
+// max(x, 0) + f is formed as max(x + f, f), the same value for f >= 0 (for x <= 0 the
+// rounded x + f cannot exceed f), in two instructions: both operands are arithmetic results,
+// so the maximum needs no NaN-quieting step.  A NaN x makes f NaN and the result NaN.
 __device__ __forceinline__ float softplus_f32(float x) {
     const float e = hw_exp2(-fabsf(x) * kLog2e);
     const float w = 1.0f + e;
     const float r = e - (w - 1.0f);
-    return fmaxf(x, 0.0f) + fmaf(hw_log2(w), kLn2, r);
+    const float f = fmaf(hw_log2(w), kLn2, r);
+    return fmaxf(x + f, f);
 }
 
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z).  For z << 0, e^-z = inf and the result is -0.

@@ -182,9 +182,14 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                 // (z is loaded unconditionally -- from u when there is no gate -- so that the
                 // buffer registers carry no conditional value around the loop)
                 if constexpr (VEC) {
+                    // (kept in this order everywhere -- also before the tile loop -- so that
+                    // the waits for them in the loop can count on a fixed issue order)
                     VIO::load(u, idx, r.u[p]);
+                    __builtin_amdgcn_sched_barrier(0);
                     VIO::load(delta, idx, r.d[p]);
+                    __builtin_amdgcn_sched_barrier(0);
                     VIO::load(zsrc, idx, r.z[p]);
+                    __builtin_amdgcn_sched_barrier(0);
                 } else {
                     r.u[p][0] = __float_as_uint(io<IO>::ld(u, idx));
                     r.d[p][0] = __float_as_uint(io<IO>::ld(delta, idx));
@@ -258,6 +263,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
         auto do_tile = [&](int64_t t0, Raw &r, const DG &prev, DG &cur, bool has_prev) {
             const int nt = (int)max((int64_t)0, min((int64_t)T, t_end - t0));
             // prep: (delta, delta*u) into LDS; skip and gate factors kept in registers
+            // (without a gate the factors keep the 1.0 they start with)
 #pragma unroll
             for (int p = 0; p < P; ++p) {
                 const int tt = p * RPP + rsub;
@@ -272,7 +278,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                     s_dk[tt][cq + v] = f32x2_t{dl, dl * uu};
                     if (READOUT) {
                         cur.u[p][v] = uu;
-                        cur.g[p][v] = gated ? silu_f32(raw(r.z[p], v)) : 1.0f;
+                        if (gated) cur.g[p][v] = silu_f32(raw(r.z[p], v));
                     }
                 }
             }
@@ -365,6 +371,10 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
         // tiles in pairs (two input buffers, two skip/gate sets); the second tile of the last
         // pair may be empty, and its epilogue-of-the-previous-tile still runs
         DG dg0, dg1;
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int v = 0; v < V; ++v) dg0.g[p][v] = dg1.g[p][v] = 1.0f;
         for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * T) {
             do_tile(t0, r0, dg1, dg0, t0 > t_begin);
             do_tile(t0 + T, r1, dg0, dg1, true);
