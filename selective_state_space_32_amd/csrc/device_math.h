@@ -43,6 +43,7 @@ template <> struct io<uint16_t> {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // V consecutive I/O elements moved as raw 32-bit words (W = V * sizeof(IO) / 4 words; bf16
 // pairs share a word, low half first).  Requires V * sizeof(IO) to be 4, 8 or a multiple of

@@ -235,11 +235,21 @@ template <int N, typename IO>
 int launch_step(float *state, const void *u, const void *delta, const float *A, const void *B,
                 const void *C, const float *Dv, const void *z, void *y, const ssm_dims *dm, hipStream_t st) {
     constexpr int G = N >= 4 ? N / 4 : 1;
-    const int64_t threads = dm->batch * dm->dim * G;
-    hipLaunchKernelGGL((ssm::step_kernel<N, IO>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
-                       state, static_cast<const IO *>(u), static_cast<const IO *>(delta), A,
-                       static_cast<const IO *>(B), static_cast<const IO *>(C), Dv,
-                       static_cast<const IO *>(z), static_cast<IO *>(y), dm->batch, dm->dim);
+    constexpr int SP = ssm::kStepSeqPerThread;
+    const int64_t threads = (dm->batch + SP - 1) / SP * dm->dim * G;
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    // vector reads of the A, B, C slices of a lane need them aligned to the slice
+    const size_t es = sizeof(IO);
+    const bool vp = N >= 4 && aligned(A, 16) && aligned(B, 4 * es) && aligned(C, 4 * es);
+    const IO *u_ = static_cast<const IO *>(u), *dl_ = static_cast<const IO *>(delta);
+    const IO *B_ = static_cast<const IO *>(B), *C_ = static_cast<const IO *>(C), *z_ = static_cast<const IO *>(z);
+    IO *y_ = static_cast<IO *>(y);
+    if (vp)
+        hipLaunchKernelGGL((ssm::step_kernel<N, IO, true>), grid, dim3(256), 0, st, state, u_, dl_, A, B_, C_, Dv,
+                           z_, y_, dm->batch, dm->dim);
+    else
+        hipLaunchKernelGGL((ssm::step_kernel<N, IO, false>), grid, dim3(256), 0, st, state, u_, dl_, A, B_, C_, Dv,
+                           z_, y_, dm->batch, dm->dim);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

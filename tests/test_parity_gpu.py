@@ -199,6 +199,42 @@ def test_decode_steps_vs_oracle(oracle_mod, c5_case):
     assert es <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("S,D,gate,skip,misalign", [
+    (5, 37, True, True, False),      # odd sequence count (a thread's second sequence past S)
+    (1, 200, False, True, False),    # one sequence, no gate
+    (8, 64, True, False, False),     # no skip term
+    (3, 70, True, True, True),       # B and C not aligned to a lane's slice: element-wise reads
+])
+def test_step_shapes(oracle_mod, io, N, S, D, gate, skip, misalign):
+    """Three consecutive steps of every state size and I/O type against the oracle step."""
+    c = inputs.step_case(S, D, N, 3, io, gate=gate, skip=skip, seed=40 + N)
+    st = torch.from_numpy(c.state0).cuda()
+    A = to_dev(c.A, torch)
+    Dv = to_dev(c.Dskip, torch) if skip else None
+    ref_state = c.state0.astype(np.float64)
+    for k in range(c.steps):
+        u, dl = to_dev(c.u[k], torch), to_dev(c.delta[k], torch)
+        z = to_dev(c.z[k], torch) if gate else None
+        Bk, Ck = to_dev(c.B[k], torch), to_dev(c.C[k], torch)
+        if misalign:
+            # the same values one element into a larger buffer
+            Bb = torch.empty(Bk.numel() + 1, dtype=Bk.dtype, device="cuda")
+            Cb = torch.empty(Ck.numel() + 1, dtype=Ck.dtype, device="cuda")
+            Bb[1:] = Bk.reshape(-1)
+            Cb[1:] = Ck.reshape(-1)
+            Bk, Ck = Bb[1:].view(Bk.shape), Cb[1:].view(Ck.shape)
+        y = ssmscan.step(st, u, dl, A, Bk, Ck, D=Dv, z=z)
+        yr, ref_state = oracle_mod.step(ref_state, c.values("u")[k], c.values("delta")[k], c.A,
+                                        c.values("B")[k], c.values("C")[k], D=c.Dskip if skip else None,
+                                        z=c.values("z")[k] if gate else None)
+        e = y_error(to_host_f64(y), yr, io)
+        assert e <= TOL[io], (k, e)
+    es = raw_error(to_host_f64(st), ref_state)
+    assert es <= TOL[io], es
+
+
 def test_decode_steps_vs_scan(c5_case):
     """64 GPU steps from a zero state equal the GPU scan of the same 64-token sequences (step
     size already activated: softplus off, no bias)."""
