@@ -78,9 +78,8 @@ typedef enum {
  *   chunk_len scan plan: 0 = the library chooses; > 0 = split every sequence into
  *             chunks of this many tokens and combine the chunk states (two-pass chunk
  *             carry); -1 = one pass, one workgroup per 64 channels of a sequence.  With 0
- *             and enough channels the library also runs one pass, but as a persistent
- *             grid that hands each sequence's state between workgroups piece by piece so
- *             that every CU gets the same work.  Results agree up to fp32 rounding
+ *             the library runs one pass when there are enough channel tiles to fill the
+ *             GPU and the chunk carry otherwise.  Results agree up to fp32 rounding
  *             whatever the plan. */
 typedef struct ssm_dims {
     int64_t batch;

@@ -18,18 +18,9 @@
 // Per (token, channel, state) the recurrence costs one multiply (delta*A), one exp2, one
 // multiply (delta*u*B), one FMA (state) and one FMA (readout) -- no more.
 //
-// Scheduling (MODE):
-//  * kFull / kSummary: one workgroup per (tile, chunk) of the grid -- the single pass and
-//    the first and last passes of the chunk carry (see carry_kernel.h).
-//  * kChained: a persistent grid sized to what is resident at once; workgroups claim
-//    (tile, chunk) items from an atomic counter in chunk-major order and hand the fp32
-//    state of a tile from one chunk to the next through a per-tile slot and a progress
-//    word (release / acquire at device scope).  Every token is still processed exactly
-//    once; with more tiles than resident workgroups all CUs get equal work instead of a
-//    partly idle last round of the grid.  A workgroup only
-//    waits for an item claimed before its own, whose workgroup is running, so the chain
-//    always drains; the wait is bounded and, if the bound is ever hit, an error word is
-//    raised instead of hanging.
+// Work items (MODE):
+//  * kFull / kSummary: one workgroup per (tile, chunk) of the grid -- the single pass, and the
+//    first and last passes of the chunk carry (see carry_kernel.h).
 #pragma once
 
 #include "device_math.h"
@@ -38,12 +29,7 @@ namespace ssm {
 
 constexpr int kChanTile = 64;    // channels per workgroup (one per lane)
 
-enum ScanMode { kFull = 0, kSummary = 1, kChained = 2 };
-
-// Scheduling words of the chained mode, at the start of the workspace:
-//   sched[0] work counter, sched[1 + tile] chunks of the tile completed,
-//   sched[1 + n_tiles] error word (nonzero if a wait hit its bound).
-constexpr unsigned kSpinLimit = 1u << 24;
+enum ScanMode { kFull = 0, kSummary = 1 };
 
 // s_waitcnt immediate that waits for all LDS and scalar-memory operations (lgkmcnt = 0) and
 // leaves the vector-memory and export counters unconstrained (gfx9 encoding).
@@ -82,8 +68,6 @@ __device__ __forceinline__ void load_slice(const IO *__restrict__ p, int64_t off
 //             last chunk writes last_state.
 //   kSummary: start from h = 0, no readout; write the chunk's local final state to
 //             cstate[b][c] and the chunk's sum of step sizes to cdsum[b][c].
-//   kChained: as kFull, with the state handed between chunks through cstate[tile] slots
-//             (64 x N floats each) and the scheduling words `sched`.
 //   N: state size; S: states per wave (K = N/S waves); T: tokens per LDS tile.
 //   VEC: the prep and epilogue move V consecutive channels of one token per thread
 //        (one 16-byte access for 8 bf16); needs D % 8 == 0 and 16-byte aligned u, delta,
@@ -95,7 +79,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                   const float *__restrict__ A, const float *__restrict__ Dv,
                   const float *__restrict__ bias, const IO *__restrict__ Bm,
                   const IO *__restrict__ Cm, float *__restrict__ last_state, float *__restrict__ cstate,
-                  float *__restrict__ cdsum, int *__restrict__ sched, int64_t L, int64_t D,
+                  float *__restrict__ cdsum, int64_t L, int64_t D,
                   int tiles_per_b, int n_tiles, int64_t chunk_len, int nchunk, int softplus) {
     constexpr int K = N / S;
     constexpr int J = T / K;                   // prep / epilogue elements per thread per tile
@@ -113,7 +97,6 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     constexpr int BW = PIPE ? S * (int)sizeof(IO) / 4 : 1;
     __shared__ f32x2_t s_dk[T][kChanTile];
     __shared__ float s_yp[READOUT ? K : 1][T][kChanTile];
-    __shared__ int s_item;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -126,293 +109,247 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     const IO *__restrict__ zsrc = gated ? z : u;
     const int64_t n_items = (int64_t)n_tiles * nchunk;
 
-    // Work items.  The claimed index is broadcast through LDS and read back with
-    // readfirstlane, so that it is a scalar the compiler knows to be uniform: the item loop
-    // and every barrier in it then stay in uniform control flow.
-    auto claim = [&]() -> int64_t {
-        if (tid == 0) s_item = atomicAdd(&sched[0], 1);
-        __syncthreads();
-        const int it = __builtin_amdgcn_readfirstlane(s_item);
-        __syncthreads();
-        return it;
+    const int64_t item = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    if (item >= n_items) return;
+    const int c = (int)(item / n_tiles);
+    const int tile = (int)(item - (int64_t)c * n_tiles);
+    const int b = tile / tiles_per_b;
+    const int64_t d0 = (int64_t)(tile - b * tiles_per_b) * kChanTile;
+    const int64_t d = d0 + lane;            // channel of this lane in the recurrence
+    const bool act = d < D;
+    const int64_t t_begin = (int64_t)c * chunk_len;
+    const int64_t t_end = min(L, t_begin + chunk_len);
+    const int64_t row0 = (int64_t)b * L;
+    const bool qact = d0 + cq < D;          // whole group in or out (D % V == 0 when VEC)
+    const int64_t dq = qact ? d0 + cq : (D - V) / V * V;  // in-bounds channel for loads
+
+    float a2[S], h[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        a2[s] = act ? A[d * N + w * S + s] * kLog2e : 0.0f;
+        h[s] = 0.0f;
+    }
+    if (MODE == kFull && c > 0 && act) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) h[s] = cstate[(((int64_t)b * nchunk + c - 1) * D + d) * N + w * S + s];
+    }
+    float Dq[V], bq[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const bool ok = qact && (VEC || d0 + cq + v < D);
+        Dq[v] = (ok && Dv) ? Dv[dq + v] : 0.0f;
+        bq[v] = (ok && bias) ? bias[dq + v] : 0.0f;
+    }
+    float dsum = 0.0f;
+
+    // Raw inputs of a tile, in two register buffers: the loads of tile i+2 are issued
+    // as soon as tile i has been read out of its buffer, so that two tiles of recurrence
+    // hide their latency; indices are clamped so every load is in bounds.
+    struct Raw { uint32_t u[P][W], d[P][W], z[P][W]; };
+    Raw r0, r1;
+    auto load_tile = [&](int64_t t0, Raw &r) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int64_t t = min(t0 + (p * RPP + rsub), t_end - 1);
+            const int64_t idx = (row0 + t) * D + dq;
+            // (z is loaded unconditionally -- from u when there is no gate -- so that the
+            // buffer registers carry no conditional value around the loop)
+            if constexpr (VEC) {
+                // (kept in this order everywhere -- also before the tile loop -- so that
+                // the waits for them in the loop can count on a fixed issue order)
+                VIO::load(u, idx, r.u[p]);
+                __builtin_amdgcn_sched_barrier(0);
+                VIO::load(delta, idx, r.d[p]);
+                __builtin_amdgcn_sched_barrier(0);
+                VIO::load(zsrc, idx, r.z[p]);
+                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                r.u[p][0] = __float_as_uint(io<IO>::ld(u, idx));
+                r.d[p][0] = __float_as_uint(io<IO>::ld(delta, idx));
+                r.z[p][0] = __float_as_uint(io<IO>::ld(zsrc, idx));
+            }
+        }
     };
-    int64_t item = MODE == kChained ? claim() : (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-    while (item < n_items) {
-        const int c = (int)(item / n_tiles);
-        const int tile = (int)(item - (int64_t)c * n_tiles);
-        const int b = tile / tiles_per_b;
-        const int64_t d0 = (int64_t)(tile - b * tiles_per_b) * kChanTile;
-        const int64_t d = d0 + lane;            // channel of this lane in the recurrence
-        const bool act = d < D;
-        const int64_t t_begin = (int64_t)c * chunk_len;
-        const int64_t t_end = min(L, t_begin + chunk_len);
-        const int64_t row0 = (int64_t)b * L;
-        const bool qact = d0 + cq < D;          // whole group in or out (D % V == 0 when VEC)
-        const int64_t dq = qact ? d0 + cq : (D - V) / V * V;  // in-bounds channel for loads
-
-        float a2[S], h[S];
+    auto raw = [&](const uint32_t (&r)[W], int v) -> float {
+        if constexpr (VEC) return VIO::get(r, v);
+        else return __uint_as_float(r[0]);
+    };
+    load_tile(t_begin, r0);
+    load_tile(t_begin + T, r1);
+    // epilogue of a tile: y = (sum of the K partial readouts + D u) * silu(z), read from
+    // s_yp after the recurrence of that tile
+    // (the skip term is applied as one explicit FMA, D u + partial_0, so that no tile
+    // position is left to the compiler's choice of contraction: results are bitwise the
+    // same wherever a tile falls)
+    struct DG { float u[P][V], g[P][V]; };
+    auto epilogue = [&](int64_t t0, const DG &dg) {
+        if (!READOUT) return;
+        const int nt = (int)max((int64_t)0, min((int64_t)T, t_end - t0));
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            a2[s] = act ? A[d * N + w * S + s] * kLog2e : 0.0f;
-            h[s] = 0.0f;
-        }
-        if (MODE == kFull && c > 0 && act) {
-#pragma unroll
-            for (int s = 0; s < S; ++s) h[s] = cstate[(((int64_t)b * nchunk + c - 1) * D + d) * N + w * S + s];
-        }
-        float Dq[V], bq[V];
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-            const bool ok = qact && (VEC || d0 + cq + v < D);
-            Dq[v] = (ok && Dv) ? Dv[dq + v] : 0.0f;
-            bq[v] = (ok && bias) ? bias[dq + v] : 0.0f;
-        }
-        float dsum = 0.0f;
-
-        // Raw inputs of a tile, in two register buffers: the loads of tile i+2 are issued
-        // as soon as tile i has been read out of its buffer, so that two tiles of recurrence
-        // hide their latency; indices are clamped so every load is in bounds.
-        struct Raw { uint32_t u[P][W], d[P][W], z[P][W]; };
-        Raw r0, r1;
-        auto load_tile = [&](int64_t t0, Raw &r) {
-#pragma unroll
-            for (int p = 0; p < P; ++p) {
-                const int64_t t = min(t0 + (p * RPP + rsub), t_end - 1);
-                const int64_t idx = (row0 + t) * D + dq;
-                // (z is loaded unconditionally -- from u when there is no gate -- so that the
-                // buffer registers carry no conditional value around the loop)
-                if constexpr (VEC) {
-                    // (kept in this order everywhere -- also before the tile loop -- so that
-                    // the waits for them in the loop can count on a fixed issue order)
-                    VIO::load(u, idx, r.u[p]);
-                    __builtin_amdgcn_sched_barrier(0);
-                    VIO::load(delta, idx, r.d[p]);
-                    __builtin_amdgcn_sched_barrier(0);
-                    VIO::load(zsrc, idx, r.z[p]);
-                    __builtin_amdgcn_sched_barrier(0);
-                } else {
-                    r.u[p][0] = __float_as_uint(io<IO>::ld(u, idx));
-                    r.d[p][0] = __float_as_uint(io<IO>::ld(delta, idx));
-                    r.z[p][0] = __float_as_uint(io<IO>::ld(zsrc, idx));
-                }
-            }
-        };
-        auto raw = [&](const uint32_t (&r)[W], int v) -> float {
-            if constexpr (VEC) return VIO::get(r, v);
-            else return __uint_as_float(r[0]);
-        };
-        load_tile(t_begin, r0);
-        load_tile(t_begin + T, r1);
-        if (MODE == kChained && c > 0) {
-            // wait (with the first tile already in flight) until the previous chunk of this
-            // tile has published its final state
-            // (polled with relaxed loads: an acquire on every poll would invalidate the L2
-            // each time; one acquire fence follows the wait)
-            if (tid == 0) {
-                unsigned spins = 0;
-                while (__hip_atomic_load(&sched[1 + tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < c) {
-                    if (++spins > kSpinLimit) {
-                        __hip_atomic_store(&sched[1 + n_tiles], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(4);
-                }
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            }
-            __syncthreads();
-#pragma unroll
-            for (int s = 0; s < S; ++s)
-                h[s] = __hip_atomic_load(&cstate[((int64_t)tile * kChanTile + lane) * N + w * S + s],
-                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-
-        // epilogue of a tile: y = (sum of the K partial readouts + D u) * silu(z), read from
-        // s_yp after the recurrence of that tile
-        // (the skip term is applied as one explicit FMA, D u + partial_0, so that no tile
-        // position is left to the compiler's choice of contraction: results are bitwise the
-        // same wherever a tile falls)
-        struct DG { float u[P][V], g[P][V]; };
-        auto epilogue = [&](int64_t t0, const DG &dg) {
-            if (!READOUT) return;
-            const int nt = (int)max((int64_t)0, min((int64_t)T, t_end - t0));
-#pragma unroll
-            for (int p = 0; p < P; ++p) {
-                const int tt = p * RPP + rsub;
-                if (tt < nt && qact) {
-                    float yv[V];
-#pragma unroll
-                    for (int v = 0; v < V; ++v) {
-                        float a = fmaf(Dq[v], dg.u[p][v], s_yp[0][tt][cq + v]);
-#pragma unroll
-                        for (int k = 1; k < K; ++k) a += s_yp[k][tt][cq + v];
-                        yv[v] = a * dg.g[p][v];
-                    }
-                    const int64_t idx = (row0 + t0 + tt) * D + d0 + cq;
-                    if constexpr (VEC) {
-                        VIO::store(y, idx, yv);
-                    } else {
-                        io<IO>::st(y, idx, yv[0]);
-                    }
-                }
-            }
-        };
-        // One tile: the prep of this tile (from loads issued two tiles ago), the epilogue of
-        // the previous tile (its stores then retire while this tile runs), the prefetch of the
-        // tile after next into the buffer just read, and the recurrence.  A tile past the end
-        // is empty (nt = 0).
-        auto do_tile = [&](int64_t t0, Raw &r, const DG &prev, DG &cur, bool has_prev) {
-            const int nt = (int)max((int64_t)0, min((int64_t)T, t_end - t0));
-            // prep: (delta, delta*u) into LDS; skip and gate factors kept in registers
-            // (without a gate the factors keep the 1.0 they start with)
-#pragma unroll
-            for (int p = 0; p < P; ++p) {
-                const int tt = p * RPP + rsub;
+        for (int p = 0; p < P; ++p) {
+            const int tt = p * RPP + rsub;
+            if (tt < nt && qact) {
+                float yv[V];
 #pragma unroll
                 for (int v = 0; v < V; ++v) {
-                    const float uu = raw(r.u[p], v);
-                    const float x = raw(r.d[p], v) + bq[v];
-                    const float dl = softplus ? softplus_f32(x) : x;
-                    // (written unmasked: rows of tokens past the end are never read by the
-                    // recurrence, and lanes of channels past D hold values loaded from an
-                    // in-bounds channel and are never stored)
-                    s_dk[tt][cq + v] = f32x2_t{dl, dl * uu};
-                    if (READOUT) {
-                        cur.u[p][v] = uu;
-                        if (gated) cur.g[p][v] = silu_f32(raw(r.z[p], v));
-                    }
+                    float a = fmaf(Dq[v], dg.u[p][v], s_yp[0][tt][cq + v]);
+#pragma unroll
+                    for (int k = 1; k < K; ++k) a += s_yp[k][tt][cq + v];
+                    yv[v] = a * dg.g[p][v];
+                }
+                const int64_t idx = (row0 + t0 + tt) * D + d0 + cq;
+                if constexpr (VEC) {
+                    VIO::store(y, idx, yv);
+                } else {
+                    io<IO>::st(y, idx, yv[0]);
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);
-            if (has_prev) epilogue(t0 - T, prev);
-            // (issued only after the prep has read the buffer, and unconditionally -- past the
-            // end the clamped loads are merely redundant -- so that the loads land in the same
-            // registers, with no copies and no wait for them at the loop back-edge)
-            __builtin_amdgcn_sched_barrier(0);
-            load_tile(t0 + 2 * T, r);
-            __syncthreads();
-            // recurrence over the tile: lane = channel, this wave's S states
-            if (PIPE && nt == T) {
-                // A full tile, software-pipelined in groups of G tokens (two register sets,
-                // ping-pong): after the wait for the current group, the LDS (delta, delta*u)
-                // reads and the scalar B / C loads of the next group are issued, then the
-                // current group is computed.  All indices are compile-time constants.
-                f32x2_t va[G], vb[G];
-                uint32_t ba[G][BW], ca[G][BW], bb[G][BW], cb[G][BW];
-                const IO *btile = Bm + (row0 + t0) * N + w * S;
-                const IO *ctile = Cm + (row0 + t0) * N + w * S;
-                auto gload = [&](int g0, f32x2_t (&v)[G], uint32_t (&bw)[G][BW], uint32_t (&cw)[G][BW]) {
+        }
+    };
+    // One tile: the prep of this tile (from loads issued two tiles ago), the epilogue of
+    // the previous tile (its stores then retire while this tile runs), the prefetch of the
+    // tile after next into the buffer just read, and the recurrence.  A tile past the end
+    // is empty (nt = 0).
+    auto do_tile = [&](int64_t t0, Raw &r, const DG &prev, DG &cur, bool has_prev) {
+        const int nt = (int)max((int64_t)0, min((int64_t)T, t_end - t0));
+        // prep: (delta, delta*u) into LDS; skip and gate factors kept in registers
+        // (without a gate the factors keep the 1.0 they start with)
 #pragma unroll
-                    for (int i = 0; i < G; ++i) {
-                        // the prefetch after the last group runs past the tile: clamp (unused)
-                        const int tt = g0 + i < T ? g0 + i : T - 1;
-                        v[i] = s_dk[tt][lane];
-                        const uint32_t *bp = reinterpret_cast<const uint32_t *>(btile + tt * N);
-                        const uint32_t *cp = reinterpret_cast<const uint32_t *>(ctile + tt * N);
+        for (int p = 0; p < P; ++p) {
+            const int tt = p * RPP + rsub;
 #pragma unroll
-                        for (int k = 0; k < BW; ++k) {
-                            bw[i][k] = bp[k];
-                            cw[i][k] = READOUT ? cp[k] : 0u;
-                        }
-                    }
-                };
-                auto gcomp = [&](int g0, const f32x2_t (&v)[G], const uint32_t (&bw)[G][BW],
-                                 const uint32_t (&cw)[G][BW]) {
-#pragma unroll
-                    for (int i = 0; i < G; ++i) {
-                        float acc = 0.0f;
-#pragma unroll
-                        for (int s = 0; s < S; ++s) {
-                            const float e = hw_exp2(v[i].x * a2[s]);
-                            h[s] = fmaf(e, h[s], v[i].y * word_f32<IO>(bw[i], s));
-                            if (READOUT) acc = fmaf(word_f32<IO>(cw[i], s), h[s], acc);
-                        }
-                        if (READOUT)
-                            s_yp[w][g0 + i][lane] = acc;
-                        else
-                            dsum += v[i].x;
-                    }
-                };
-                gload(0, va, ba, ca);
-#pragma unroll
-                for (int g0 = 0; g0 < T; g0 += 2 * G) {
-                    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-                    gload(g0 + G, vb, bb, cb);
-                    __builtin_amdgcn_sched_barrier(0);
-                    gcomp(g0, va, ba, ca);
-                    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-                    gload(g0 + 2 * G, va, ba, ca);
-                    __builtin_amdgcn_sched_barrier(0);
-                    gcomp(g0 + G, vb, bb, cb);
+            for (int v = 0; v < V; ++v) {
+                const float uu = raw(r.u[p], v);
+                const float x = raw(r.d[p], v) + bq[v];
+                const float dl = softplus ? softplus_f32(x) : x;
+                // (written unmasked: rows of tokens past the end are never read by the
+                // recurrence, and lanes of channels past D hold values loaded from an
+                // in-bounds channel and are never stored)
+                s_dk[tt][cq + v] = f32x2_t{dl, dl * uu};
+                if (READOUT) {
+                    cur.u[p][v] = uu;
+                    if (gated) cur.g[p][v] = silu_f32(raw(r.z[p], v));
                 }
-            } else {
-                // a partial tile (or a slice shape the pipelined loop does not take)
-#pragma unroll 4
-                for (int tt = 0; tt < nt; ++tt) {
-                    const f32x2_t v = s_dk[tt][lane];
-                    const int64_t boff = (row0 + t0 + tt) * N + w * S;
-                    float Bs[S], Cs[S];
-                    load_slice<S>(Bm, boff, Bs);
-                    if (READOUT) load_slice<S>(Cm, boff, Cs);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (has_prev) epilogue(t0 - T, prev);
+        // (issued only after the prep has read the buffer, and unconditionally -- past the
+        // end the clamped loads are merely redundant -- so that the loads land in the same
+        // registers, with no copies and no wait for them at the loop back-edge)
+        __builtin_amdgcn_sched_barrier(0);
+        load_tile(t0 + 2 * T, r);
+        __syncthreads();
+        // recurrence over the tile: lane = channel, this wave's S states
+        if (PIPE && nt == T) {
+            // A full tile, software-pipelined in groups of G tokens (two register sets,
+            // ping-pong): after the wait for the current group, the LDS (delta, delta*u)
+            // reads and the scalar B / C loads of the next group are issued, then the
+            // current group is computed.  All indices are compile-time constants.
+            f32x2_t va[G], vb[G];
+            uint32_t ba[G][BW], ca[G][BW], bb[G][BW], cb[G][BW];
+            const IO *btile = Bm + (row0 + t0) * N + w * S;
+            const IO *ctile = Cm + (row0 + t0) * N + w * S;
+            auto gload = [&](int g0, f32x2_t (&v)[G], uint32_t (&bw)[G][BW], uint32_t (&cw)[G][BW]) {
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
+                    // the prefetch after the last group runs past the tile: clamp (unused)
+                    const int tt = g0 + i < T ? g0 + i : T - 1;
+                    v[i] = s_dk[tt][lane];
+                    const uint32_t *bp = reinterpret_cast<const uint32_t *>(btile + tt * N);
+                    const uint32_t *cp = reinterpret_cast<const uint32_t *>(ctile + tt * N);
+#pragma unroll
+                    for (int k = 0; k < BW; ++k) {
+                        bw[i][k] = bp[k];
+                        cw[i][k] = READOUT ? cp[k] : 0u;
+                    }
+                }
+            };
+            auto gcomp = [&](int g0, const f32x2_t (&v)[G], const uint32_t (&bw)[G][BW],
+                             const uint32_t (&cw)[G][BW]) {
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
                     float acc = 0.0f;
 #pragma unroll
                     for (int s = 0; s < S; ++s) {
-                        const float e = hw_exp2(v.x * a2[s]);
-                        h[s] = fmaf(e, h[s], v.y * Bs[s]);
-                        if (READOUT) acc = fmaf(Cs[s], h[s], acc);
+                        const float e = hw_exp2(v[i].x * a2[s]);
+                        h[s] = fmaf(e, h[s], v[i].y * word_f32<IO>(bw[i], s));
+                        if (READOUT) acc = fmaf(word_f32<IO>(cw[i], s), h[s], acc);
                     }
                     if (READOUT)
-                        s_yp[w][tt][lane] = acc;
+                        s_yp[w][g0 + i][lane] = acc;
                     else
-                        dsum += v.x;
+                        dsum += v[i].x;
                 }
+            };
+            gload(0, va, ba, ca);
+#pragma unroll
+            for (int g0 = 0; g0 < T; g0 += 2 * G) {
+                __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+                gload(g0 + G, vb, bb, cb);
+                __builtin_amdgcn_sched_barrier(0);
+                gcomp(g0, va, ba, ca);
+                __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+                gload(g0 + 2 * G, va, ba, ca);
+                __builtin_amdgcn_sched_barrier(0);
+                gcomp(g0 + G, vb, bb, cb);
             }
-            __syncthreads();
-        };
-        // tiles in pairs (two input buffers, two skip/gate sets); the second tile of the last
-        // pair may be empty, and its epilogue-of-the-previous-tile still runs
-        DG dg0, dg1;
+        } else {
+            // a partial tile (or a slice shape the pipelined loop does not take)
+#pragma unroll 4
+            for (int tt = 0; tt < nt; ++tt) {
+                const f32x2_t v = s_dk[tt][lane];
+                const int64_t boff = (row0 + t0 + tt) * N + w * S;
+                float Bs[S], Cs[S];
+                load_slice<S>(Bm, boff, Bs);
+                if (READOUT) load_slice<S>(Cm, boff, Cs);
+                float acc = 0.0f;
 #pragma unroll
-        for (int p = 0; p < P; ++p)
+                for (int s = 0; s < S; ++s) {
+                    const float e = hw_exp2(v.x * a2[s]);
+                    h[s] = fmaf(e, h[s], v.y * Bs[s]);
+                    if (READOUT) acc = fmaf(Cs[s], h[s], acc);
+                }
+                if (READOUT)
+                    s_yp[w][tt][lane] = acc;
+                else
+                    dsum += v.x;
+            }
+        }
+        __syncthreads();
+    };
+    // tiles in pairs (two input buffers, two skip/gate sets); the second tile of the last
+    // pair may be empty, and its epilogue-of-the-previous-tile still runs
+    DG dg0, dg1;
 #pragma unroll
-            for (int v = 0; v < V; ++v) dg0.g[p][v] = dg1.g[p][v] = 1.0f;
-        for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * T) {
-            do_tile(t0, r0, dg1, dg0, t0 > t_begin);
-            do_tile(t0 + T, r1, dg0, dg1, true);
-        }
-        {
-            // the last pair's second tile (empty or not) still owes its epilogue
-            const int64_t npair = (t_end - t_begin + 2 * T - 1) / (2 * T);
-            epilogue(t_begin + (2 * npair - 1) * T, dg1);
-        }
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int v = 0; v < V; ++v) dg0.g[p][v] = dg1.g[p][v] = 1.0f;
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * T) {
+        do_tile(t0, r0, dg1, dg0, t0 > t_begin);
+        do_tile(t0 + T, r1, dg0, dg1, true);
+    }
+    {
+        // the last pair's second tile (empty or not) still owes its epilogue
+        const int64_t npair = (t_end - t_begin + 2 * T - 1) / (2 * T);
+        epilogue(t_begin + (2 * npair - 1) * T, dg1);
+    }
 
-        if (MODE == kSummary) {
-            if (act) {
+    if (MODE == kSummary) {
+        if (act) {
 #pragma unroll
-                for (int s = 0; s < S; ++s) cstate[(((int64_t)b * nchunk + c) * D + d) * N + w * S + s] = h[s];
-                if (w == 0) cdsum[((int64_t)b * nchunk + c) * D + d] = dsum;
-            }
-        } else if (c == nchunk - 1) {
-            if (last_state && act) {
-#pragma unroll
-                for (int s = 0; s < S; ++s) last_state[((int64_t)b * D + d) * N + w * S + s] = h[s];
-            }
-        } else if (MODE == kChained) {
-            // publish this chunk's final state to the next chunk of the tile
-#pragma unroll
-            for (int s = 0; s < S; ++s)
-                __hip_atomic_store(&cstate[((int64_t)tile * kChanTile + lane) * N + w * S + s], h[s],
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __threadfence();
-            __syncthreads();
-            if (tid == 0) __hip_atomic_store(&sched[1 + tile], c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            for (int s = 0; s < S; ++s) cstate[(((int64_t)b * nchunk + c) * D + d) * N + w * S + s] = h[s];
+            if (w == 0) cdsum[((int64_t)b * nchunk + c) * D + d] = dsum;
         }
-        if (MODE != kChained) break;
-        item = claim();
+    } else if (c == nchunk - 1) {
+        if (last_state && act) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) last_state[((int64_t)b * D + d) * N + w * S + s] = h[s];
+        }
     }
 }
 
-// Writes zeros (a scan of zero tokens leaves the zero initial state; also clears the
-// scheduling words of the chained mode).
+// Writes zeros (a scan of zero tokens leaves the zero initial state).
 template <typename TP>
 __global__ void __launch_bounds__(256) fill_zero_kernel(TP *__restrict__ p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;

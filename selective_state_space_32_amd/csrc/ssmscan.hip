@@ -1,6 +1,7 @@
 // libssmscan: C ABI, argument validation, planning and kernel launches.
 // The declarations and the contract of every entry point are in include/ssmscan.h.
 #include <hip/hip_runtime.h>
+#include <algorithm>
 
 #include <cstdarg>
 #include <cstdint>
@@ -52,6 +53,8 @@ int check_dims(const ssm_dims *dm, bool scan) {
         return fail(SSM_ERR_UNSUPPORTED_N, "dstate %lld not supported (1, 2, 4, 8 or 16)", (long long)dm->dstate);
     if (dm->dim > kMaxDim || dm->batch > kMaxDim)
         return fail(SSM_ERR_SHAPE, "dim or batch larger than 2^30");
+    if (dm->batch > 0 && dm->dim > (int64_t(1) << 36) / dm->batch)
+        return fail(SSM_ERR_SHAPE, "batch*dim exceeds 2^36 (grid size)");
     const int64_t L = scan ? dm->seqlen : 1;
     if (L > kMaxElems || (dm->batch > 0 && dm->dim > 0 && L > kMaxElems / dm->batch / dm->dim))
         return fail(SSM_ERR_SHAPE, "batch*seqlen*dim exceeds 2^46 elements");
@@ -60,7 +63,7 @@ int check_dims(const ssm_dims *dm, bool scan) {
     return SSM_OK;
 }
 
-enum Schedule { kGrid = 0, kChain = 1, kCarry = 2 };
+enum Schedule { kGrid = 0, kCarry = 1 };
 
 struct Plan {
     int schedule = kGrid;
@@ -69,26 +72,9 @@ struct Plan {
     size_t off_cstate = 0, off_cdsum = 0, bytes = 0;
 };
 
-// Workgroups of the scan kernel resident at once on the current device (for the
-// persistent chained schedule): occupancy per CU x CU count, cached per kernel.
-template <typename F>
-int resident_groups(F kernel, int block, int *cache) {
-    if (*cache > 0) return *cache;
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess) return 0;
-    *cache = cus * (per_cu > 0 ? per_cu : 1);
-    return *cache;
-}
-
-// The chained schedule pays off when there are more channel tiles than workgroups
-// resident at once (a grid would leave its last round partly idle); with fewer tiles every
-// tile already gets its own resident workgroup and the grid is used.
-constexpr int64_t kAssumedGroups = 768;   // 3 resident workgroups per CU on 256 CUs
-constexpr int64_t kChainMinTiles = kAssumedGroups + 1;
-constexpr int64_t kChainItemsPerGroup = 8;
-
+// One workgroup per (sequence, 64-channel tile) fills the GPU once there are about two
+// tiles per CU or more; with fewer tiles the tokens are split into chunks as well (the
+// chunk carry), which costs an extra summary pass over all but the last chunk.
 Plan make_plan(const ssm_dims *dm) {
     Plan p;
     const int64_t bsz = dm->batch, L = dm->seqlen, D = dm->dim, N = dm->dstate;
@@ -99,20 +85,14 @@ Plan make_plan(const ssm_dims *dm) {
         p.schedule = kCarry;
         clen = dm->chunk_len < L ? dm->chunk_len : L;
         if ((L + clen - 1) / clen > kMaxChunks) clen = (L + kMaxChunks - 1) / kMaxChunks;
-    } else if (dm->chunk_len == 0 && tiles >= kChainMinTiles && L >= 256) {
-        // enough tiles: one pass, chained chunks so that every CU gets the same work
-        p.schedule = kChain;
-        int64_t nck = (kChainItemsPerGroup * kAssumedGroups + tiles - 1) / tiles;
+    } else if (dm->chunk_len == 0 && tiles < 512 && L >= 512) {
+        // too few channel tiles to fill the GPU: split the tokens too.  At least one round of
+        // resident workgroups, and chunks of at most 512 tokens so that long sequences give
+        // many items (the grid then balances itself over the CUs); chunks of at least 128
+        // tokens keep the per-item start-up and the carry small.  (Short sequences stay one
+        // pass: three launches would cost more than they save.)
+        const int64_t want = std::max((kTargetGroups + tiles - 1) / tiles, (L + 511) / 512);
         const int64_t most = (L + 127) / 128;
-        if (nck > most) nck = most;
-        if (nck < 1) nck = 1;
-        clen = (L + nck - 1) / nck;
-        clen = (clen + 31) / 32 * 32;
-    } else if (dm->chunk_len == 0 && tiles < 512) {
-        // too few channel tiles to fill the GPU: split the tokens too, keeping chunks at
-        // least 256 tokens long so that the extra summary and carry passes stay cheap
-        const int64_t want = (kTargetGroups + tiles - 1) / tiles;
-        const int64_t most = (L + 255) / 256;
         int64_t nchunk = want < most ? want : most;
         if (nchunk < 1) nchunk = 1;
         if (nchunk > kMaxChunks) nchunk = kMaxChunks;
@@ -131,12 +111,6 @@ Plan make_plan(const ssm_dims *dm) {
         p.off_cstate = 0;
         p.off_cdsum = cs;
         p.bytes = cs + cd;
-    } else if (p.schedule == kChain) {
-        size_t sc = align256((size_t)(tiles + 2) * sizeof(int));
-        size_t slots = align256((size_t)(tiles * ssm::kChanTile * N) * sizeof(float));
-        p.off_cstate = sc;
-        p.off_cdsum = 0;
-        p.bytes = sc + slots;
     }
     return p;
 }
@@ -165,33 +139,19 @@ void launch_scan_kernels(const IO *u, const IO *dl, const float *A, const IO *B,
     const dim3 block(64 * K);
     float *cstate = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_cstate);
     float *cdsum = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_cdsum);
-    int *sched = reinterpret_cast<int *>(ws);
     const int64_t cl = p.chunk_len;
     const int nc = (int)p.nchunk;
-    if (p.schedule == kChain) {
-        auto kern = ssm::scan_chunk_kernel<N, S, T, IO, ssm::kChained, VEC>;
-        static int cache = 0;
-        int groups = resident_groups(kern, 64 * K, &cache);
-        const int64_t items = (int64_t)n_tiles * nc;
-        if (groups <= 0 || groups > items) groups = (int)(items < kAssumedGroups ? items : kAssumedGroups);
-        const int64_t nw = n_tiles + 2;
-        hipLaunchKernelGGL(ssm::fill_zero_kernel<int>, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, st,
-                           sched, nw);
-        hipLaunchKernelGGL(kern, dim3((unsigned)groups), block, 0, st, u, dl, z, y, A, Dv, bias, B, C, last_state,
-                           cstate, (float *)nullptr, sched, L, D, tiles_per_b, n_tiles, cl, nc, softplus);
-        return;
-    }
     if (p.schedule == kCarry) {
         hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kSummary, VEC>),
                            dim3((unsigned)n_tiles, (unsigned)(nc - 1)), block, 0, st, u, dl, (const IO *)nullptr,
                            (IO *)nullptr, A, (const float *)nullptr, bias, B, C, (float *)nullptr, cstate, cdsum,
-                           (int *)nullptr, L, D, tiles_per_b, n_tiles, cl, nc, softplus);
+                           L, D, tiles_per_b, n_tiles, cl, nc, softplus);
         const int col_tiles = (int)((D * N + 63) / 64);
         hipLaunchKernelGGL((ssm::carry_scan_kernel<N>), dim3((unsigned)(bsz * col_tiles)), dim3(256), 0, st,
                            cstate, (const float *)cdsum, A, D, nc, col_tiles);
     }
     hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kFull, VEC>), dim3((unsigned)n_tiles, (unsigned)nc),
-                       block, 0, st, u, dl, z, y, A, Dv, bias, B, C, last_state, cstate, cdsum, (int *)nullptr, L, D,
+                       block, 0, st, u, dl, z, y, A, Dv, bias, B, C, last_state, cstate, cdsum, L, D,
                        tiles_per_b, n_tiles, cl, nc, softplus);
 }
 

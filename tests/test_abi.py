@@ -122,16 +122,18 @@ def test_empty_problems_are_noops(b):
 def test_plan(b):
     # the B8 L2048 D5120 layer has 640 channel tiles, all resident at once: one grid pass
     assert b.scan_plan(8, 2048, 5120, 16, 1) == (1, 2048)
-    # more tiles than resident workgroups: one pass as chained work items
-    n, cl = b.scan_plan(16, 2048, 4096, 16, 1)
-    assert n == 1 and 128 <= cl < 2048 and cl % 32 == 0
-    # the long B1 L131072 D2048 sequence has 32 channel tiles: split into chunks
+    # more tiles than resident workgroups: still one grid pass (several rounds)
+    assert b.scan_plan(16, 2048, 4096, 16, 1) == (1, 2048)
+    # the long B1 L131072 D2048 sequence has 32 channel tiles: chunks of at most 512 tokens
     n, cl = b.scan_plan(1, 131072, 2048, 16, 1)
-    assert n > 8 and cl % 32 == 0 and n * cl >= 131072 and (n - 1) * cl < 131072
+    assert cl <= 512 and cl % 32 == 0 and n * cl >= 131072 and (n - 1) * cl < 131072
+    # B2 L2048 D1536 (48 tiles): one round of 768 work items
+    assert b.scan_plan(2, 2048, 1536, 16, 0) == (16, 128)
     assert b.scan_plan(2, 300, 70, 4, 0, chunk_len=64) == (5, 64)
     assert b.scan_plan(2, 300, 70, 4, 0, chunk_len=-1) == (1, 300)
     assert b.scan_plan(1, 256, 16, 4, 0) == (1, 256)
-    # a grid-mapped single pass needs no workspace; the chained pass and the chunk carry do
+    # a single pass needs no workspace; the chunk carry does
     assert b.workspace_bytes(8, 2048, 5120, 16, 1) == 0
-    assert b.workspace_bytes(16, 2048, 4096, 16, 1) >= 1024 * 64 * 16 * 4
+    assert b.workspace_bytes(16, 2048, 4096, 16, 1) == 0
+    assert b.workspace_bytes(1, 131072, 2048, 16, 1) >= 256 * 2048 * 16 * 4
     assert b.workspace_bytes(1, 4096, 64, 16, 1, chunk_len=128) > b.workspace_bytes(1, 4096, 64, 16, 1, chunk_len=-1)
