@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional, Tuple
+from typing import Callable, Optional, Tuple
 
 import torch
 
@@ -114,18 +114,8 @@ def _stream_handle(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
-             D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
-             delta_bias: Optional[torch.Tensor] = None, softplus: bool = True, *,
-             y: Optional[torch.Tensor] = None, last_state: Optional[torch.Tensor] = None,
-             return_last_state: bool = True, chunk_len: int = 0,
-             workspace: Optional[torch.Tensor] = None, stream=None):
-    """Selective scan forward from a zero state (ssm_scan_fwd).
-
-    u, delta, z: (batch, L, dim); B, C: (batch, L, N), all of one dtype (float32 or bfloat16);
-    A: (dim, N) float32; D, delta_bias: (dim,) float32 or None.
-    Returns (y, last_state) -- last_state (batch, dim, N) float32, or None if not asked for.
-    """
+def _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state, return_last_state, chunk_len,
+               workspace, stream):
     if u.dim() != 3:
         raise ValueError("u must be (batch, L, dim)")
     bsz, L, dim = u.shape
@@ -155,20 +145,50 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
     need = int(lib.ssm_scan_workspace_bytes(ctypes.byref(dims)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    rc = lib.ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-                          int(bool(softplus)), _ptr(y), _ptr(last_state), ctypes.byref(dims), _ptr(workspace),
-                          workspace.numel() * workspace.element_size(), _stream_handle(stream))
-    _check(rc)
+    args = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            int(bool(softplus)), _ptr(y), _ptr(last_state), ctypes.byref(dims), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    # the tensors and the dims struct the pointers refer to, kept alive with the arguments
+    keep = (u, delta, A, B, C, D, z, delta_bias, y, last_state, workspace, dims)
+    return args, keep, y, last_state
+
+
+def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+             D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+             delta_bias: Optional[torch.Tensor] = None, softplus: bool = True, *,
+             y: Optional[torch.Tensor] = None, last_state: Optional[torch.Tensor] = None,
+             return_last_state: bool = True, chunk_len: int = 0,
+             workspace: Optional[torch.Tensor] = None, stream=None):
+    """Selective scan forward from a zero state (ssm_scan_fwd).
+
+    u, delta, z: (batch, L, dim); B, C: (batch, L, N), all of one dtype (float32 or bfloat16);
+    A: (dim, N) float32; D, delta_bias: (dim,) float32 or None.
+    Returns (y, last_state) -- last_state (batch, dim, N) float32, or None if not asked for.
+    """
+    args, _keep, y, last_state = _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
+                                            return_last_state, chunk_len, workspace, stream)
+    _check(lib.ssm_scan_fwd(*args))
     return y, last_state
 
 
-def step(state: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
-         C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None, *,
-         y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """One recurrent step (ssm_step); `state` (S, dim, N) float32 is updated in place.
+def scan_fwd_call(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                  D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                  delta_bias: Optional[torch.Tensor] = None, softplus: bool = True, *,
+                  y: Optional[torch.Tensor] = None, last_state: Optional[torch.Tensor] = None,
+                  return_last_state: bool = True, chunk_len: int = 0,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> Callable[[], None]:
+    """The scan_fwd call checked and marshalled once: returns a function that enqueues the
+    same call again (same tensors, the stream given or current now), for loops that repeat
+    it.  Outputs go to the y / last_state tensors passed in (or allocated here and kept)."""
+    args, keep, _y, _ls = _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
+                                     return_last_state, chunk_len, workspace, stream)
 
-    u, delta, z: (S, dim); B, C: (S, N) of one dtype; delta is the activated step size.
-    Returns y (S, dim)."""
+    def call(_args=args, _keep=keep):
+        _check(lib.ssm_scan_fwd(*_args))
+    return call
+
+
+def _step_args(state, u, delta, A, B, C, D, z, y, stream):
     S, dim, N = state.shape
     dev, io = u.device, u.dtype
     _io_code(io)
@@ -187,7 +207,30 @@ def step(state: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Ten
     else:
         _need(y, "y", (S, dim), io, dev)
     dims = make_dims(S, 1, dim, N, io)
-    rc = lib.ssm_step(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y),
-                      ctypes.byref(dims), _stream_handle(stream))
-    _check(rc)
+    args = (_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y),
+            ctypes.byref(dims), _stream_handle(stream))
+    keep = (state, u, delta, A, B, C, D, z, y, dims)
+    return args, keep, y
+
+
+def step(state: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+         C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None, *,
+         y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One recurrent step (ssm_step); `state` (S, dim, N) float32 is updated in place.
+
+    u, delta, z: (S, dim); B, C: (S, N) of one dtype; delta is the activated step size.
+    Returns y (S, dim)."""
+    args, _keep, y = _step_args(state, u, delta, A, B, C, D, z, y, stream)
+    _check(lib.ssm_step(*args))
     return y
+
+
+def step_call(state: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+              C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None, *,
+              y: Optional[torch.Tensor] = None, stream=None) -> Callable[[], None]:
+    """The step call checked and marshalled once (see scan_fwd_call)."""
+    args, keep, _y = _step_args(state, u, delta, A, B, C, D, z, y, stream)
+
+    def call(_args=args, _keep=keep):
+        _check(lib.ssm_step(*_args))
+    return call

@@ -365,3 +365,56 @@ def test_nan_propagates_only_downstream():
     mask = np.ones_like(y, dtype=bool)
     mask[0, 30:, 5] = False
     assert np.all(np.isfinite(y[mask]))
+
+
+# --- prepared calls and graph capture ----------------------------------------------------
+
+def test_prepared_scan_call_matches_direct():
+    """scan_fwd_call (checked and marshalled once) writes exactly what scan_fwd writes."""
+    case = inputs.scan_case(2, 300, 200, 16, "bf16", gate=True, seed=31)
+    t = case_tensors(case, torch)
+    y0, ls0 = ssmscan.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                               delta_bias=t["delta_bias"], softplus=case.softplus)
+    y1 = torch.full_like(y0, float("nan"))
+    ls1 = torch.full_like(ls0, float("nan"))
+    call = ssmscan.scan_fwd_call(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                 delta_bias=t["delta_bias"], softplus=case.softplus, y=y1, last_state=ls1)
+    for _ in range(2):
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1) and torch.equal(ls0, ls1)
+
+
+def test_step_graph_replays_match_eager():
+    """Steps captured in a HIP graph (as the decode benchmark runs them): every replay, with
+    eager work and synchronisation in between, equals the eager steps bitwise."""
+    c = inputs.step_case(6, 96, 16, 3, "bf16", seed=33)
+    A, Dv = to_dev(c.A, torch), to_dev(c.Dskip, torch)
+    ins = [tuple(to_dev(getattr(c, f)[k], torch) for f in ("u", "delta", "B", "C", "z")) for k in range(c.steps)]
+    st0 = torch.from_numpy(c.state0).cuda()
+    # eager reference
+    st = st0.clone()
+    y = torch.empty((c.S, c.D), dtype=torch.bfloat16, device="cuda")
+    ys = []
+    for (u, dl, Bk, Ck, z) in ins:
+        ssmscan.step(st, u, dl, A, Bk, Ck, D=Dv, z=z, y=y)
+        ys.append(y.clone())
+    ref_state, ref_y = st.clone(), ys[-1]
+    # captured
+    stg = st0.clone()
+    yg = torch.empty_like(y)
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=cap):
+        for (u, dl, Bk, Ck, z) in ins:
+            ssmscan.step(stg, u, dl, A, Bk, Ck, D=Dv, z=z, y=yg)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        stg.copy_(st0)
+        yg.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(stg, ref_state), rep
+        assert torch.equal(yg, ref_y), rep
