@@ -46,6 +46,9 @@ def _load():
         lib.ssm_oracle_scan.argtypes = [I64, I64, I64, I64, P, P, P, P, P, P, P, P, ctypes.c_int,
                                         P, P, ctypes.c_int]
         lib.ssm_oracle_scan.restype = ctypes.c_int
+        lib.ssm_oracle_scan_from.argtypes = [I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, ctypes.c_int,
+                                             P, P, ctypes.c_int]
+        lib.ssm_oracle_scan_from.restype = ctypes.c_int
         lib.ssm_oracle_step.argtypes = [I64, I64, I64, P, P, P, P, P, P, P, P, P, ctypes.c_int]
         lib.ssm_oracle_step.restype = ctypes.c_int
         _lib = lib
@@ -70,8 +73,8 @@ def default_threads() -> int:
 
 
 def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
-         threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
-    """fp64 selective scan from h = 0.
+         threads: Optional[int] = None, h0=None) -> Tuple[np.ndarray, np.ndarray]:
+    """fp64 selective scan from h = 0, or from the state h0 (bsz, Dch, N) if given.
 
     u, delta, z: (bsz, L, Dch); B, C: (bsz, L, N); A: (Dch, N); D, delta_bias: (Dch,).
     Returns (y (bsz, L, Dch), last_state (bsz, Dch, N)), both float64.
@@ -89,9 +92,10 @@ def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = Tr
     delta_bias = _f64(delta_bias, (Dch,))
     y = np.empty((bsz, L, Dch), dtype=np.float64)
     last = np.empty((bsz, Dch, N), dtype=np.float64)
-    rc = _load().ssm_oracle_scan(bsz, L, Dch, N, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C),
-                                 _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)),
-                                 _ptr(y), _ptr(last), int(threads or default_threads()))
+    h0 = _f64(h0, (bsz, Dch, N))
+    rc = _load().ssm_oracle_scan_from(bsz, L, Dch, N, _ptr(h0), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                                      _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)),
+                                      _ptr(y), _ptr(last), int(threads or default_threads()))
     if rc != 0:
         raise ValueError("oracle scan rejected N=%d" % N)
     return y, last
@@ -119,12 +123,13 @@ def step(state, u, delta, A, B, C, D=None, z=None,
     return y, st
 
 
-def scan_case(case, channels=None, threads: Optional[int] = None):
+def scan_case(case, channels=None, threads: Optional[int] = None, h0=None):
     """Run the oracle on a generated ScanCase (from the package's input module).
 
     channels: optional index array of channels d to evaluate (all batches); the oracle
     then runs on those channel columns only -- channels are independent, so each
-    sampled output is exactly the full-problem value.
+    sampled output is exactly the full-problem value.  h0: optional initial state
+    (bsz, Dch, N) of the whole problem.
     Returns (y, last_state) restricted to the sampled channels.
     """
     sel = slice(None) if channels is None else np.asarray(channels)
@@ -135,5 +140,7 @@ def scan_case(case, channels=None, threads: Optional[int] = None):
     A = case.A[sel]
     D = None if case.Dskip is None else case.Dskip[sel]
     bias = None if case.delta_bias is None else case.delta_bias[sel]
+    if h0 is not None:
+        h0 = np.asarray(h0)[:, sel]
     return scan(u, dl, A, case.values("B"), case.values("C"), D=D, z=z, delta_bias=bias,
-                softplus=case.softplus, threads=threads)
+                softplus=case.softplus, threads=threads, h0=h0)

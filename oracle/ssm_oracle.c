@@ -48,25 +48,26 @@ static double oracle_softplus(double x) {
 static double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
 
 /*
- * Scan over one batch of sequences.
+ * Scan over one batch of sequences, continuing from the state h0 (the recurrent form
+ * carries the state from one stretch of tokens to the next: shakilmahmud.com section 3).
  *   u, delta, z, y : [bsz][L][D]      B, C : [bsz][L][N]
  *   A : [D][N]     Dv, delta_bias : [D]   (Dv, z, delta_bias may be NULL)
- *   last_state : [bsz][D][N] or NULL
+ *   h0, last_state : [bsz][D][N] or NULL (h0 NULL: start from zero)
  * Channels (b, d) are independent; they are spread over `nthreads` OpenMP threads,
  * each walking its channel's tokens in order.  Returns 0, or -1 if N is too large.
  */
-int ssm_oracle_scan(int64_t bsz, int64_t L, int64_t D, int64_t N,
-                    const double *u, const double *delta, const double *A,
-                    const double *B, const double *C, const double *Dv,
-                    const double *z, const double *delta_bias, int softplus_flag,
-                    double *y, double *last_state, int nthreads) {
+int ssm_oracle_scan_from(int64_t bsz, int64_t L, int64_t D, int64_t N, const double *h0,
+                         const double *u, const double *delta, const double *A,
+                         const double *B, const double *C, const double *Dv,
+                         const double *z, const double *delta_bias, int softplus_flag,
+                         double *y, double *last_state, int nthreads) {
     if (N > ORACLE_MAX_N || N < 1) return -1;
     int64_t nch = bsz * D;
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
     for (int64_t ch = 0; ch < nch; ++ch) {
         int64_t b = ch / D, d = ch % D;
         double h[ORACLE_MAX_N];
-        for (int64_t n = 0; n < N; ++n) h[n] = 0.0;
+        for (int64_t n = 0; n < N; ++n) h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;
         for (int64_t t = 0; t < L; ++t) {
             int64_t i = (b * L + t) * D + d;       /* (b, t, d) */
             const double *Bt = B + (b * L + t) * N;
@@ -90,6 +91,16 @@ int ssm_oracle_scan(int64_t bsz, int64_t L, int64_t D, int64_t N,
             for (int64_t n = 0; n < N; ++n) last_state[(b * D + d) * N + n] = h[n];
     }
     return 0;
+}
+
+/* The scan from h = 0 (the scan of a whole sequence). */
+int ssm_oracle_scan(int64_t bsz, int64_t L, int64_t D, int64_t N,
+                    const double *u, const double *delta, const double *A,
+                    const double *B, const double *C, const double *Dv,
+                    const double *z, const double *delta_bias, int softplus_flag,
+                    double *y, double *last_state, int nthreads) {
+    return ssm_oracle_scan_from(bsz, L, D, N, NULL, u, delta, A, B, C, Dv, z, delta_bias, softplus_flag,
+                                y, last_state, nthreads);
 }
 
 /*

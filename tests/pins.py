@@ -310,3 +310,66 @@ ALL_CHECKS = [
     check_linearity, check_causality, check_zero_input, check_b_or_c_zero,
     check_chunk_composition, check_softplus_values,
 ]
+
+
+# --- the scan continued from a given state ------------------------------------------------
+# scan_from(u, x, A, B, C, D, z, bias, softplus, h0) -> (y, last_state)
+
+def check_h0_no_input_decay(scan_from, seed=51, L=40, D=3, N=4):
+    """With B = 0 nothing enters the state: it only decays, h_t = exp(A * S_t) h0 with S_t
+    the running sum of step sizes, so y_t = (C_t . h_t + D u_t) silu(z_t) in closed form."""
+    rng = _rng(seed)
+    u = rng.standard_normal((1, L, D))
+    x = 0.5 * rng.standard_normal((1, L, D))
+    bias = rng.uniform(-2.0, 0.0, D)
+    A = -np.exp(rng.normal(0.5, 0.5, (D, N)))
+    B = np.zeros((1, L, N))
+    C = rng.standard_normal((1, L, N))
+    Dv = rng.standard_normal(D)
+    z = rng.standard_normal((1, L, D))
+    h0 = rng.standard_normal((1, D, N))
+    y, h = scan_from(u, x, A, B, C, Dv, z, bias, True, h0)
+    S = np.cumsum(_softplus_np(x[0] + bias), axis=0)            # (L, D)
+    ht = np.exp(A[None] * S[:, :, None]) * h0[0][None]          # (L, D, N)
+    yref = (np.einsum("tn,tdn->td", C[0], ht) + Dv * u[0]) * z[0] / (1.0 + np.exp(-z[0]))
+    assert _rel(y[0], yref) < 1e-12
+    assert _rel(h[0], ht[-1]) < 1e-12
+
+
+def check_h0_composition(scan_from, seed=52, L=70, split=29, D=3, N=4):
+    """Running tokens [0, s) from h0 and then [s, L) from the state reached equals one run
+    over [0, L) from h0 (the state is all the recurrence carries)."""
+    rng = _rng(seed)
+    u = rng.standard_normal((2, L, D))
+    x = 0.6 * rng.standard_normal((2, L, D))
+    A = -np.exp(rng.normal(0.3, 0.5, (D, N)))
+    B = rng.standard_normal((2, L, N))
+    C = rng.standard_normal((2, L, N))
+    Dv = rng.standard_normal(D)
+    z = rng.standard_normal((2, L, D))
+    h0 = rng.standard_normal((2, D, N))
+    y, h = scan_from(u, x, A, B, C, Dv, z, None, True, h0)
+    y1, h1 = scan_from(u[:, :split], x[:, :split], A, B[:, :split], C[:, :split], Dv, z[:, :split], None, True, h0)
+    y2, h2 = scan_from(u[:, split:], x[:, split:], A, B[:, split:], C[:, split:], Dv, z[:, split:], None, True, h1)
+    assert _rel(y, np.concatenate([y1, y2], axis=1)) < 1e-12
+    assert _rel(h, h2) < 1e-12
+
+
+def check_h0_linear_without_input(scan_from, seed=53, L=30, D=2, N=3):
+    """With u = 0 (no input, no skip term) and no gate, y and the final state are linear in
+    the initial state."""
+    rng = _rng(seed)
+    u = np.zeros((1, L, D))
+    x = 0.5 * rng.standard_normal((1, L, D))
+    A = -np.exp(rng.normal(0.0, 0.5, (D, N)))
+    B = rng.standard_normal((1, L, N))
+    C = rng.standard_normal((1, L, N))
+    ha, hb = rng.standard_normal((1, D, N)), rng.standard_normal((1, D, N))
+    ya, la = scan_from(u, x, A, B, C, None, None, None, True, ha)
+    yb, lb = scan_from(u, x, A, B, C, None, None, None, True, hb)
+    yab, lab = scan_from(u, x, A, B, C, None, None, None, True, 2.0 * ha - 3.0 * hb)
+    assert _rel(yab, 2.0 * ya - 3.0 * yb) < 1e-12
+    assert _rel(lab, 2.0 * la - 3.0 * lb) < 1e-12
+
+
+H0_CHECKS = [check_h0_no_input_decay, check_h0_composition, check_h0_linear_without_input]

@@ -34,6 +34,7 @@ MUTANTS = {
                               "double dA = exp(dt * A[d * N + n]);\n                h[n] = h[n];\n                (void)dA;\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];\n            for (int64_t n = 0; n < N; ++n) h[n] = exp(dt * A[d * N + n]) * h[n] + dt * Bt[n] * ut;"),
     "last_state_wrong_index": ("last_state[(b * D + d) * N + n] = h[n];", "last_state[(b * D + d) * N + n] = h[0];"),
     "softplus_wrong_branch": ("if (x > 0.0) return x + log1p(exp(-x));", "if (x > 0.0) return x + log1p(exp(x));"),
+    "ignore_initial_state": ("h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;", "h[n] = 0.0;"),
     "decay_squared": ("h[n] = dA * h[n] + dt * Bt[n] * ut;\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];\n            double yt = acc;\n            if (Dv) yt = yt + Dv[d] * ut;\n            if (z) yt = yt * oracle_silu(z[i]);",
                       "h[n] = dA * dA * h[n] + dt * Bt[n] * ut;\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];\n            double yt = acc;\n            if (Dv) yt = yt + Dv[d] * ut;\n            if (z) yt = yt * oracle_silu(z[i]);"),
 }
@@ -52,6 +53,9 @@ def _build_mutant(tmp_path, name, old, new):
     P, I64 = ctypes.c_void_p, ctypes.c_int64
     lib.ssm_oracle_scan.argtypes = [I64, I64, I64, I64, P, P, P, P, P, P, P, P, ctypes.c_int, P, P, ctypes.c_int]
     lib.ssm_oracle_scan.restype = ctypes.c_int
+    lib.ssm_oracle_scan_from.argtypes = [I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, ctypes.c_int, P, P,
+                                         ctypes.c_int]
+    lib.ssm_oracle_scan_from.restype = ctypes.c_int
 
     def f64(a):
         return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
@@ -68,18 +72,33 @@ def _build_mutant(tmp_path, name, old, new):
         lib.ssm_oracle_scan(bsz, L, Dch, N, ptr(u), ptr(x), ptr(A), ptr(B), ptr(C), ptr(D), ptr(z),
                             ptr(bias), int(bool(softplus)), ptr(y), ptr(h), 1)
         return y, h
-    return scan
+
+    def scan_from(u, x, A, B, C, D, z, bias, softplus, h0):
+        u, x, A, B, C, D, z, bias, h0 = map(f64, (u, x, A, B, C, D, z, bias, h0))
+        bsz, L, Dch = u.shape
+        N = A.shape[1]
+        y = np.empty((bsz, L, Dch))
+        h = np.empty((bsz, Dch, N))
+        lib.ssm_oracle_scan_from(bsz, L, Dch, N, ptr(h0), ptr(u), ptr(x), ptr(A), ptr(B), ptr(C), ptr(D),
+                                 ptr(z), ptr(bias), int(bool(softplus)), ptr(y), ptr(h), 1)
+        return y, h
+    return scan, scan_from
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(tmp_path, name):
     old, new = MUTANTS[name]
-    scan = _build_mutant(tmp_path, name, old, new)
+    scan, scan_from = _build_mutant(tmp_path, name, old, new)
     caught = []
     with np.errstate(all="ignore"):
         for check in pins.ALL_CHECKS:
             try:
                 check(scan)
+            except AssertionError:
+                caught.append(check.__name__)
+        for check in pins.H0_CHECKS:
+            try:
+                check(scan_from)
             except AssertionError:
                 caught.append(check.__name__)
     assert caught, f"mutant {name} passed every pin"

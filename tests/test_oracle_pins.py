@@ -81,3 +81,35 @@ def test_oracle_rejects_bad_n(oracle_mod):
     with pytest.raises(ValueError):
         oracle_mod.scan(np.ones((1, 2, 1)), np.ones((1, 2, 1)), np.ones((1, 300)),
                         np.ones((1, 2, 300)), np.ones((1, 2, 300)))
+
+
+def _scan_from(oracle_mod):
+    def f(u, x, A, B, C, D, z, bias, softplus, h0):
+        return oracle_mod.scan(u, x, A, B, C, D=D, z=z, delta_bias=bias, softplus=softplus, h0=h0)
+    return f
+
+
+@pytest.mark.parametrize("check", pins.H0_CHECKS, ids=lambda c: c.__name__)
+def test_h0_pins(oracle_mod, check):
+    check(_scan_from(oracle_mod))
+
+
+def test_scan_from_state_equals_steps(oracle_mod):
+    """The recurrent form (shakilmahmud.com section 3): L oracle steps from a state equal the
+    oracle scan from that state (step sizes already activated, no bias)."""
+    rng = np.random.default_rng(54)
+    S, L, Dch, N = 2, 12, 3, 4
+    u = rng.standard_normal((S, L, Dch))
+    dt = np.log1p(np.exp(0.5 * rng.standard_normal((S, L, Dch))))
+    A = -np.exp(rng.normal(0.3, 0.5, (Dch, N)))
+    B = rng.standard_normal((S, L, N))
+    C = rng.standard_normal((S, L, N))
+    Dv = rng.standard_normal(Dch)
+    z = rng.standard_normal((S, L, Dch))
+    h0 = rng.standard_normal((S, Dch, N))
+    y, last = oracle_mod.scan(u, dt, A, B, C, D=Dv, z=z, softplus=False, h0=h0)
+    st = h0.copy()
+    for t in range(L):
+        yt, st = oracle_mod.step(st, u[:, t], dt[:, t], A, B[:, t], C[:, t], D=Dv, z=z[:, t])
+        assert np.array_equal(yt, y[:, t])
+    assert np.array_equal(st, last)
