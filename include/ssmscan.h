@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define SSMSCAN_VERSION 1
+#define SSMSCAN_VERSION 2
 
 #if defined(__GNUC__) || defined(__clang__)
 #define SSMSCAN_API __attribute__((visibility("default")))
@@ -98,9 +98,8 @@ SSMSCAN_API size_t ssm_scan_workspace_bytes(const ssm_dims *dims);
 /* The plan ssm_scan_fwd will use.  Returns the number of chunks each sequence is split
  * into for the chunk carry (1 = a single pass: every token's state is computed once) and
  * stores in *chunk_len_out (may be NULL) the tokens per work item: the carry chunk length,
- * or, for a single pass, the length of the pieces a sequence is handed over in between
- * workgroups (the whole sequence when it is not split).  Returns a negative ssm_status for
- * invalid sizes. */
+ * or the whole sequence for a single pass.  Returns a negative ssm_status for invalid
+ * sizes. */
 SSMSCAN_API int64_t ssm_scan_plan(const ssm_dims *dims, int64_t *chunk_len_out);
 
 /* Selective scan forward over a batch of sequences, from a zero state.
@@ -119,6 +118,21 @@ SSMSCAN_API int ssm_scan_fwd(const void *u, const void *delta, const float *A, c
                  const float *D, const void *z, const float *delta_bias, int softplus_flag,
                  void *y, float *last_state, const ssm_dims *dims,
                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* The same scan continued from a given state: h_0 = initial_state instead of zero.  The
+ * recurrent form carries the whole history in the state (shakilmahmud.com section 3;
+ * urworte.de "Methodische Grundlagen"), so scanning a sequence in pieces, each from the
+ * last_state of the previous piece, gives the scan of the whole sequence (up to fp32
+ * rounding); this is how a prompt is prefilled in pieces or a decode state is rebuilt.
+ *   initial_state  : [batch][dim][dstate] fp32, or NULL (= zero: exactly ssm_scan_fwd).
+ *                    It may be the same buffer as last_state (the state advanced in place);
+ *                    it must not overlap any other argument.
+ * All other arguments, the workspace size and the errors are those of ssm_scan_fwd.  With
+ * seqlen 0, last_state receives a copy of the initial state. */
+SSMSCAN_API int ssm_scan_fwd_from(const float *initial_state, const void *u, const void *delta, const float *A,
+                      const void *B, const void *C, const float *D, const void *z, const float *delta_bias,
+                      int softplus_flag, void *y, float *last_state, const ssm_dims *dims, void *workspace,
+                      size_t workspace_bytes, void *stream);
 
 /* One recurrent (inference) step for `batch` independent sequences: the constant-memory
  * recurrent form (shakilmahmud.com section 3; urworte.de "Methodische Grundlagen").

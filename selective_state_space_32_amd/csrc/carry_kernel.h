@@ -6,7 +6,8 @@
 // chunk c of the sequence acts on the state as the pair (P_c, hc_c): P_c[n] = exp(A[n] *
 // sum of the chunk's step sizes) and hc_c = the chunk's final state when started from 0.
 // The state after chunk c is the inclusive prefix H_c = (P_0,hc_0) o ... o (P_c,hc_c)
-// applied to h = 0.  Here one wave64 computes that prefix for 64 chunks at once, lane =
+// applied to the initial state (zero unless one is given).  Here one wave64 computes that
+// prefix for 64 chunks at once, lane =
 // chunk, with a DPP scan: row_shr 1, 2, 4, 8 inside rows of 16 lanes, then row_bcast 15
 // and row_bcast 31 across rows (6 steps).  Lanes with no predecessor at a step combine
 // with the identity (1, 0).  Longer chunk lists are processed 64 at a time, carrying the
@@ -42,13 +43,17 @@ __device__ __forceinline__ void wave_scan_pairs(float &a, float &b) {
 }
 
 // cstate: [bsz][nchunk][D*N] -- in: local final states of chunks 0..nchunk-2;
-//         out: the state after each of those chunks (the carry into the next chunk).
+//         out: the state after each of those chunks (the carry into the next chunk),
+//         starting from h0; slot nchunk-1 receives a copy of h0 (when h0 is given) for
+//         the first chunk of the last pass.
 // cdsum:  [bsz][nchunk][D] sums of step sizes per chunk.
+// h0:     [bsz][D*N] initial state, or null for zero.
 // One workgroup = one sequence x 64 consecutive (d, n) columns; 4 waves x 16 columns.
 template <int N>
 __global__ void __launch_bounds__(256)
 carry_scan_kernel(float *__restrict__ cstate, const float *__restrict__ cdsum,
-                  const float *__restrict__ A, int64_t D, int nchunk, int col_tiles) {
+                  const float *__restrict__ A, const float *__restrict__ h0, int64_t D, int nchunk,
+                  int col_tiles) {
     __shared__ float s_a[64][65];
     __shared__ float s_b[64][65];
     const int64_t DN = D * N;
@@ -63,9 +68,14 @@ carry_scan_kernel(float *__restrict__ cstate, const float *__restrict__ cdsum,
     const int64_t dcol = dn / N;
     const float a2 = ok ? A[dn] * kLog2e : 0.0f;
 
+    // the running state of column w*16+k (the same in every lane), from the initial state
     float carry[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) carry[k] = 0.0f;
+    for (int k = 0; k < 16; ++k) {
+        const int64_t col = dn0 + w * 16 + k;
+        carry[k] = (h0 && col < DN) ? h0[(int64_t)b * DN + col] : 0.0f;
+    }
+    if (h0 && ok) cstate[((int64_t)b * nchunk + nchunk - 1) * DN + dn] = h0[(int64_t)b * DN + dn];
 
     for (int c0 = 0; c0 < nc; c0 += 64) {
 #pragma unroll

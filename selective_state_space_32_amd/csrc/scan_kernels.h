@@ -63,9 +63,12 @@ __device__ __forceinline__ void load_slice(const IO *__restrict__ p, int64_t off
 }
 
 // The scan over (tile, chunk) work items.
-//   kFull:    start from h = 0 (chunk 0) or from the carried state cstate[b][c-1]
-//             (the state after chunk c-1), run the recurrence with readout, write y; the
-//             last chunk writes last_state.
+//   kFull:    start from the state before the chunk -- for chunk 0 the initial state h0
+//             (zero if h0 is null), for a later chunk the carried state cstate[b][c-1] --
+//             run the recurrence with readout, write y; the last chunk writes last_state.
+//             With several chunks the initial state is read from its copy in slot
+//             cstate[b][nchunk-1] (written by the carry pass), never from h0, so h0 may be
+//             the last_state buffer.
 //   kSummary: start from h = 0, no readout; write the chunk's local final state to
 //             cstate[b][c] and the chunk's sum of step sizes to cdsum[b][c].
 //   N: state size; S: states per wave (K = N/S waves); T: tokens per LDS tile.
@@ -78,8 +81,8 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                   const IO *__restrict__ z, IO *__restrict__ y,
                   const float *__restrict__ A, const float *__restrict__ Dv,
                   const float *__restrict__ bias, const IO *__restrict__ Bm,
-                  const IO *__restrict__ Cm, float *__restrict__ last_state, float *__restrict__ cstate,
-                  float *__restrict__ cdsum, int64_t L, int64_t D,
+                  const IO *__restrict__ Cm, const float *__restrict__ h0, float *__restrict__ last_state,
+                  float *__restrict__ cstate, float *__restrict__ cdsum, int64_t L, int64_t D,
                   int tiles_per_b, int n_tiles, int64_t chunk_len, int nchunk, int softplus) {
     constexpr int K = N / S;
     constexpr int J = T / K;                   // prep / epilogue elements per thread per tile
@@ -129,9 +132,18 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
         a2[s] = act ? A[d * N + w * S + s] * kLog2e : 0.0f;
         h[s] = 0.0f;
     }
-    if (MODE == kFull && c > 0 && act) {
+    if (MODE == kFull && act) {
+        // the state before this chunk: carried from chunk c-1, or the initial state (read
+        // from h0 itself in a single pass, from the copy in slot nchunk-1 otherwise)
+        const float *src = nullptr;
+        if (c > 0 || (h0 && nchunk > 1))
+            src = cstate + (((int64_t)b * nchunk + (c + nchunk - 1) % nchunk) * D + d) * N;
+        else if (h0)
+            src = h0 + ((int64_t)b * D + d) * N;
+        if (src) {
 #pragma unroll
-        for (int s = 0; s < S; ++s) h[s] = cstate[(((int64_t)b * nchunk + c - 1) * D + d) * N + w * S + s];
+            for (int s = 0; s < S; ++s) h[s] = src[w * S + s];
+        }
     }
     float Dq[V], bq[V];
 #pragma unroll
@@ -347,6 +359,13 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
             for (int s = 0; s < S; ++s) last_state[((int64_t)b * D + d) * N + w * S + s] = h[s];
         }
     }
+}
+
+// Copies n elements (a scan of zero tokens leaves the initial state as the final one).
+template <typename TP>
+__global__ void __launch_bounds__(256) copy_kernel(TP *__restrict__ dst, const TP *__restrict__ src, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) dst[i] = src[i];
 }
 
 // Writes zeros (a scan of zero tokens leaves the zero initial state).

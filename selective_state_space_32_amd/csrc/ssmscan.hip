@@ -128,7 +128,7 @@ template <> struct ScanShape<16> { static constexpr int S = 4, T = 32; };
 
 template <int N, typename IO, bool VEC>
 void launch_scan_kernels(const IO *u, const IO *dl, const float *A, const IO *B, const IO *C, const float *Dv,
-                         const IO *z, const float *bias, int softplus, IO *y, float *last_state,
+                         const IO *z, const float *bias, int softplus, const float *h0, IO *y, float *last_state,
                          const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st) {
     constexpr int S = ScanShape<N>::S;
     constexpr int T = ScanShape<N>::T;
@@ -144,20 +144,20 @@ void launch_scan_kernels(const IO *u, const IO *dl, const float *A, const IO *B,
     if (p.schedule == kCarry) {
         hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kSummary, VEC>),
                            dim3((unsigned)n_tiles, (unsigned)(nc - 1)), block, 0, st, u, dl, (const IO *)nullptr,
-                           (IO *)nullptr, A, (const float *)nullptr, bias, B, C, (float *)nullptr, cstate, cdsum,
-                           L, D, tiles_per_b, n_tiles, cl, nc, softplus);
+                           (IO *)nullptr, A, (const float *)nullptr, bias, B, C, (const float *)nullptr,
+                           (float *)nullptr, cstate, cdsum, L, D, tiles_per_b, n_tiles, cl, nc, softplus);
         const int col_tiles = (int)((D * N + 63) / 64);
         hipLaunchKernelGGL((ssm::carry_scan_kernel<N>), dim3((unsigned)(bsz * col_tiles)), dim3(256), 0, st,
-                           cstate, (const float *)cdsum, A, D, nc, col_tiles);
+                           cstate, (const float *)cdsum, A, h0, D, nc, col_tiles);
     }
     hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kFull, VEC>), dim3((unsigned)n_tiles, (unsigned)nc),
-                       block, 0, st, u, dl, z, y, A, Dv, bias, B, C, last_state, cstate, cdsum, L, D,
+                       block, 0, st, u, dl, z, y, A, Dv, bias, B, C, h0, last_state, cstate, cdsum, L, D,
                        tiles_per_b, n_tiles, cl, nc, softplus);
 }
 
 template <int N, typename IO>
 int launch_scan(const void *u, const void *delta, const float *A, const void *B, const void *C,
-                const float *Dv, const void *z, const float *bias, int softplus, void *y,
+                const float *Dv, const void *z, const float *bias, int softplus, const float *h0, void *y,
                 float *last_state, const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st) {
     const IO *u_ = static_cast<const IO *>(u);
     const IO *dl_ = static_cast<const IO *>(delta);
@@ -169,9 +169,11 @@ int launch_scan(const void *u, const void *delta, const float *A, const void *B,
     const bool vec = dm->dim % 8 == 0 && aligned(u, 16) && aligned(delta, 16) && aligned(y, 16) &&
                      (!z || aligned(z, 16));
     if (vec)
-        launch_scan_kernels<N, IO, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, y_, last_state, dm, p, ws, st);
+        launch_scan_kernels<N, IO, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state, dm, p, ws,
+                                         st);
     else
-        launch_scan_kernels<N, IO, false>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, y_, last_state, dm, p, ws, st);
+        launch_scan_kernels<N, IO, false>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state, dm, p, ws,
+                                          st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -179,14 +181,14 @@ int launch_scan(const void *u, const void *delta, const float *A, const void *B,
 
 template <typename IO>
 int dispatch_scan(int64_t N, const void *u, const void *delta, const float *A, const void *B,
-                  const void *C, const float *Dv, const void *z, const float *bias, int sp, void *y,
-                  float *ls, const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st) {
+                  const void *C, const float *Dv, const void *z, const float *bias, int sp, const float *h0,
+                  void *y, float *ls, const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st) {
     switch (N) {
-        case 1: return launch_scan<1, IO>(u, delta, A, B, C, Dv, z, bias, sp, y, ls, dm, p, ws, st);
-        case 2: return launch_scan<2, IO>(u, delta, A, B, C, Dv, z, bias, sp, y, ls, dm, p, ws, st);
-        case 4: return launch_scan<4, IO>(u, delta, A, B, C, Dv, z, bias, sp, y, ls, dm, p, ws, st);
-        case 8: return launch_scan<8, IO>(u, delta, A, B, C, Dv, z, bias, sp, y, ls, dm, p, ws, st);
-        case 16: return launch_scan<16, IO>(u, delta, A, B, C, Dv, z, bias, sp, y, ls, dm, p, ws, st);
+        case 1: return launch_scan<1, IO>(u, delta, A, B, C, Dv, z, bias, sp, h0, y, ls, dm, p, ws, st);
+        case 2: return launch_scan<2, IO>(u, delta, A, B, C, Dv, z, bias, sp, h0, y, ls, dm, p, ws, st);
+        case 4: return launch_scan<4, IO>(u, delta, A, B, C, Dv, z, bias, sp, h0, y, ls, dm, p, ws, st);
+        case 8: return launch_scan<8, IO>(u, delta, A, B, C, Dv, z, bias, sp, h0, y, ls, dm, p, ws, st);
+        case 16: return launch_scan<16, IO>(u, delta, A, B, C, Dv, z, bias, sp, h0, y, ls, dm, p, ws, st);
     }
     return fail(SSM_ERR_UNSUPPORTED_N, "dstate %lld not supported", (long long)N);
 }
@@ -230,6 +232,55 @@ int dispatch_step(int64_t N, float *state, const void *u, const void *delta, con
 
 }  // namespace
 
+static int scan_impl(const float *h0, const void *u, const void *delta, const float *A, const void *B,
+                     const void *C, const float *D, const void *z, const float *delta_bias, int softplus_flag,
+                     void *y, float *last_state, const ssm_dims *dims, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    int rc = check_dims(dims, true);
+    if (rc != SSM_OK) return rc;
+    const int64_t bsz = dims->batch, L = dims->seqlen, Dm = dims->dim, N = dims->dstate;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (bsz == 0 || Dm == 0) return ok();
+    if (h0 && !aligned(h0, 4)) return fail(SSM_ERR_ALIGN, "initial_state not 4-byte aligned");
+    if (L == 0) {
+        // no tokens: the final state is the initial one (zero without it)
+        if (last_state && last_state != h0) {
+            if (!aligned(last_state, 4)) return fail(SSM_ERR_ALIGN, "last_state not 4-byte aligned");
+            const int64_t n = bsz * Dm * N;
+            const dim3 grid((unsigned)((n + 255) / 256));
+            if (h0)
+                hipLaunchKernelGGL(ssm::copy_kernel<float>, grid, dim3(256), 0, st, last_state, h0, n);
+            else
+                hipLaunchKernelGGL(ssm::fill_zero_kernel<float>, grid, dim3(256), 0, st, last_state, n);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+        }
+        return ok();
+    }
+    if (!u || !delta || !A || !B || !C || !y)
+        return fail(SSM_ERR_NULL, "required pointer is NULL (u=%p delta=%p A=%p B=%p C=%p y=%p)", u, delta,
+                    (const void *)A, B, C, y);
+    const size_t es = dims->io_dtype == SSM_IO_BF16 ? 2 : 4;
+    if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) || !aligned(y, es) ||
+        (z && !aligned(z, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
+        (delta_bias && !aligned(delta_bias, 4)) || (last_state && !aligned(last_state, 4)))
+        return fail(SSM_ERR_ALIGN, "a tensor pointer is not aligned to its element size");
+    if (dims->io_dtype == SSM_IO_BF16 && N >= 2 && (!aligned(B, 4) || !aligned(C, 4)))
+        return fail(SSM_ERR_ALIGN, "bf16 B and C must be 4-byte aligned");
+    Plan p = make_plan(dims);
+    if (p.bytes > 0 && !workspace) return fail(SSM_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", p.bytes);
+    if (workspace_bytes < p.bytes)
+        return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+                    p.bytes);
+    if (p.bytes > 0 && !aligned(workspace, 16)) return fail(SSM_ERR_ALIGN, "workspace not 16-byte aligned");
+    if (dims->io_dtype == SSM_IO_BF16)
+        return dispatch_scan<uint16_t>(N, u, delta, A, B, C, D, z, delta_bias, softplus_flag != 0, h0, y,
+                                       last_state, dims, p, workspace, st);
+    return dispatch_scan<float>(N, u, delta, A, B, C, D, z, delta_bias, softplus_flag != 0, h0, y, last_state,
+                                dims, p, workspace, st);
+}
+
+
 extern "C" {
 
 int ssm_version(void) { return SSMSCAN_VERSION; }
@@ -254,43 +305,16 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
                  const float *D, const void *z, const float *delta_bias, int softplus_flag,
                  void *y, float *last_state, const ssm_dims *dims,
                  void *workspace, size_t workspace_bytes, void *stream) {
-    int rc = check_dims(dims, true);
-    if (rc != SSM_OK) return rc;
-    const int64_t bsz = dims->batch, L = dims->seqlen, Dm = dims->dim, N = dims->dstate;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (bsz == 0 || Dm == 0) return ok();
-    if (L == 0) {
-        if (last_state) {
-            if (!aligned(last_state, 4)) return fail(SSM_ERR_ALIGN, "last_state not 4-byte aligned");
-            const int64_t n = bsz * Dm * N;
-            hipLaunchKernelGGL(ssm::fill_zero_kernel<float>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                               last_state, n);
-            hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-        }
-        return ok();
-    }
-    if (!u || !delta || !A || !B || !C || !y)
-        return fail(SSM_ERR_NULL, "required pointer is NULL (u=%p delta=%p A=%p B=%p C=%p y=%p)", u, delta,
-                    (const void *)A, B, C, y);
-    const size_t es = dims->io_dtype == SSM_IO_BF16 ? 2 : 4;
-    if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) || !aligned(y, es) ||
-        (z && !aligned(z, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
-        (delta_bias && !aligned(delta_bias, 4)) || (last_state && !aligned(last_state, 4)))
-        return fail(SSM_ERR_ALIGN, "a tensor pointer is not aligned to its element size");
-    if (dims->io_dtype == SSM_IO_BF16 && N >= 2 && (!aligned(B, 4) || !aligned(C, 4)))
-        return fail(SSM_ERR_ALIGN, "bf16 B and C must be 4-byte aligned");
-    Plan p = make_plan(dims);
-    if (p.bytes > 0 && !workspace) return fail(SSM_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", p.bytes);
-    if (workspace_bytes < p.bytes)
-        return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
-                    p.bytes);
-    if (p.bytes > 0 && !aligned(workspace, 16)) return fail(SSM_ERR_ALIGN, "workspace not 16-byte aligned");
-    if (dims->io_dtype == SSM_IO_BF16)
-        return dispatch_scan<uint16_t>(N, u, delta, A, B, C, D, z, delta_bias, softplus_flag != 0, y, last_state,
-                                       dims, p, workspace, st);
-    return dispatch_scan<float>(N, u, delta, A, B, C, D, z, delta_bias, softplus_flag != 0, y, last_state, dims,
-                                p, workspace, st);
+    return scan_impl(nullptr, u, delta, A, B, C, D, z, delta_bias, softplus_flag, y, last_state, dims, workspace,
+                     workspace_bytes, stream);
+}
+
+int ssm_scan_fwd_from(const float *initial_state, const void *u, const void *delta, const float *A,
+                      const void *B, const void *C, const float *D, const void *z, const float *delta_bias,
+                      int softplus_flag, void *y, float *last_state, const ssm_dims *dims, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    return scan_impl(initial_state, u, delta, A, B, C, D, z, delta_bias, softplus_flag, y, last_state, dims,
+                     workspace, workspace_bytes, stream);
 }
 
 int ssm_step(float *state, const void *u, const void *delta, const float *A, const void *B,

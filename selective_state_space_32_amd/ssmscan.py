@@ -49,6 +49,8 @@ def _load() -> ctypes.CDLL:
     lib.ssm_scan_plan.restype = ctypes.c_int64
     lib.ssm_scan_fwd.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int, P, P, D, P, ctypes.c_size_t, P]
     lib.ssm_scan_fwd.restype = ctypes.c_int
+    lib.ssm_scan_fwd_from.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_int, P, P, D, P, ctypes.c_size_t, P]
+    lib.ssm_scan_fwd_from.restype = ctypes.c_int
     lib.ssm_step.argtypes = [P, P, P, P, P, P, P, P, P, D, P]
     lib.ssm_step.restype = ctypes.c_int
     return lib
@@ -115,7 +117,7 @@ def _stream_handle(stream) -> ctypes.c_void_p:
 
 
 def _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state, return_last_state, chunk_len,
-               workspace, stream):
+               workspace, stream, initial_state=None):
     if u.dim() != 3:
         raise ValueError("u must be (batch, L, dim)")
     bsz, L, dim = u.shape
@@ -137,6 +139,8 @@ def _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state, ret
         y = torch.empty((bsz, L, dim), dtype=io, device=dev)
     else:
         _need(y, "y", (bsz, L, dim), io, dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", (bsz, dim, N), torch.float32, dev)
     if last_state is None and return_last_state:
         last_state = torch.empty((bsz, dim, N), dtype=torch.float32, device=dev)
     elif last_state is not None:
@@ -148,8 +152,10 @@ def _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state, ret
     args = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
             int(bool(softplus)), _ptr(y), _ptr(last_state), ctypes.byref(dims), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    if initial_state is not None:
+        args = (_ptr(initial_state),) + args
     # the tensors and the dims struct the pointers refer to, kept alive with the arguments
-    keep = (u, delta, A, B, C, D, z, delta_bias, y, last_state, workspace, dims)
+    keep = (u, delta, A, B, C, D, z, delta_bias, y, last_state, workspace, dims, initial_state)
     return args, keep, y, last_state
 
 
@@ -186,6 +192,21 @@ def scan_fwd_call(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torc
     def call(_args=args, _keep=keep):
         _check(lib.ssm_scan_fwd(*_args))
     return call
+
+
+def scan_fwd_from(initial_state: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
+                  B: torch.Tensor, C: torch.Tensor, D: Optional[torch.Tensor] = None,
+                  z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                  softplus: bool = True, *, y: Optional[torch.Tensor] = None,
+                  last_state: Optional[torch.Tensor] = None, return_last_state: bool = True,
+                  chunk_len: int = 0, workspace: Optional[torch.Tensor] = None, stream=None):
+    """The scan continued from initial_state (batch, dim, N) float32 (ssm_scan_fwd_from).
+    last_state may be initial_state itself (the state advanced in place).  Otherwise as
+    scan_fwd."""
+    args, _keep, y, last_state = _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
+                                            return_last_state, chunk_len, workspace, stream, initial_state)
+    _check(lib.ssm_scan_fwd_from(*args))
+    return y, last_state
 
 
 def _step_args(state, u, delta, A, B, C, D, z, y, stream):

@@ -27,8 +27,8 @@ def b():
 
 def test_header_declares_the_entry_points():
     syms = set(declared_symbols())
-    assert {"ssm_scan_fwd", "ssm_step", "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_last_error",
-            "ssm_version"} <= syms
+    assert {"ssm_scan_fwd", "ssm_scan_fwd_from", "ssm_step", "ssm_scan_workspace_bytes", "ssm_scan_plan",
+            "ssm_last_error", "ssm_version"} <= syms
 
 
 def test_library_exports_every_declared_symbol():
@@ -38,7 +38,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version(b):
-    assert b.lib.ssm_version() == 1
+    import re
+    hdr = open(os.path.join(ROOT, "include", "ssmscan.h")).read()
+    assert b.lib.ssm_version() == int(re.search(r"#define SSMSCAN_VERSION (\d+)", hdr).group(1))
 
 
 def _dims(b, **kw):
@@ -93,6 +95,18 @@ def test_workspace_too_small(b):
     assert need >= 2 * 4 * 128 * 16 * 4
     assert _scan(b, d, ws_bytes=need - 1) == -6
     assert _scan(b, d, ws=0) == -6
+
+
+def test_scan_from_validation(b):
+    # a misaligned initial state is rejected before any launch; the other checks are the scan's
+    P = ctypes.c_void_p
+    d = _dims(b)
+    ws = b.lib.ssm_scan_workspace_bytes(ctypes.byref(d))
+    args = [P(FAKE)] * 5 + [None, None, None, 1, P(FAKE), None, ctypes.byref(d), P(FAKE), ws, None]
+    assert b.lib.ssm_scan_fwd_from(P(FAKE + 2), *args) == -4
+    assert "initial_state" in b.last_error()
+    args[0] = P(0)
+    assert b.lib.ssm_scan_fwd_from(P(FAKE), *args) == -1
 
 
 def test_misaligned_rejected(b):

@@ -418,3 +418,72 @@ def test_step_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(stg, ref_state), rep
         assert torch.equal(yg, ref_y), rep
+
+
+# --- the scan continued from a given state -----------------------------------------------
+
+def _h0(bsz, D, N, seed):
+    return (0.5 * np.random.default_rng(seed).standard_normal((bsz, D, N))).astype(np.float32)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [4, 16])
+@pytest.mark.parametrize("chunk_len,in_place", [(-1, False), (-1, True), (96, False), (96, True), (0, False)])
+def test_scan_from_state(oracle_mod, io, N, chunk_len, in_place):
+    """ssm_scan_fwd_from against the oracle scan from the same state: one pass and the chunk
+    carry, with last_state a separate buffer or the initial-state buffer itself."""
+    Dch = 136 if N == 4 else 128        # element-wise and 16-byte access paths
+    case = inputs.scan_case(2, 700, Dch, N, io, gate=True, seed=60 + N)
+    h0 = _h0(2, Dch, N, 61)
+    t = case_tensors(case, torch)
+    h0_dev = torch.from_numpy(h0).cuda()
+    ls = h0_dev if in_place else None
+    y, ls = ssmscan.scan_fwd_from(h0_dev, t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                  delta_bias=t["delta_bias"], softplus=case.softplus, last_state=ls,
+                                  chunk_len=chunk_len)
+    torch.cuda.synchronize()
+    if in_place:
+        assert ls.data_ptr() == h0_dev.data_ptr()
+    y_ref, ls_ref = oracle_mod.scan_case(case, h0=h0)
+    check(case, to_host_f64(y), to_host_f64(ls), y_ref, ls_ref, f"from state, chunk_len={chunk_len}")
+
+
+def test_scan_in_pieces_equals_whole(oracle_mod):
+    """A sequence scanned in three pieces, each continuing from the previous piece's state
+    (advanced in place), gives the oracle's scan of the whole sequence."""
+    case = inputs.scan_case(3, 1000, 200, 16, "bf16", gate=True, seed=62)
+    t = case_tensors(case, torch)
+    st = torch.zeros((3, 200, 16), dtype=torch.float32, device="cuda")
+    ys = []
+    for a, b_ in ((0, 333), (333, 334), (334, 1000)):
+        sl = {k: (v[:, a:b_].contiguous() if (v is not None and k in ("u", "delta", "B", "C", "z")) else v)
+              for k, v in t.items()}
+        y, _ = ssmscan.scan_fwd_from(st, sl["u"], sl["delta"], sl["A"], sl["B"], sl["C"], D=sl["D"], z=sl["z"],
+                                     delta_bias=sl["delta_bias"], softplus=case.softplus, last_state=st)
+        ys.append(y)
+    torch.cuda.synchronize()
+    y_ref, ls_ref = oracle_mod.scan_case(case)
+    check(case, to_host_f64(torch.cat(ys, dim=1)), to_host_f64(st), y_ref, ls_ref, "three pieces")
+
+
+def test_scan_from_zero_state_is_scan():
+    """A null initial state and a zero one both give ssm_scan_fwd's output bitwise."""
+    case = inputs.scan_case(2, 300, 96, 16, "bf16", gate=True, seed=63)
+    t = case_tensors(case, torch)
+    kw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"], softplus=case.softplus)
+    y0, l0 = ssmscan.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], **kw)
+    zero = torch.zeros((2, 96, 16), dtype=torch.float32, device="cuda")
+    y1, l1 = ssmscan.scan_fwd_from(zero, t["u"], t["delta"], t["A"], t["B"], t["C"], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(l0, l1)
+
+
+def test_scan_from_state_zero_tokens():
+    """With no tokens the final state is the initial one."""
+    h0 = torch.from_numpy(_h0(2, 40, 8, 64)).cuda()
+    u = torch.empty((2, 0, 40), dtype=torch.float32, device="cuda")
+    B = torch.empty((2, 0, 8), dtype=torch.float32, device="cuda")
+    A = -torch.ones((40, 8), dtype=torch.float32, device="cuda")
+    _, ls = ssmscan.scan_fwd_from(h0, u, u, A, B, B)
+    torch.cuda.synchronize()
+    assert torch.equal(ls, h0)
