@@ -49,6 +49,9 @@ def _load():
         lib.ssm_oracle_scan_from.argtypes = [I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, ctypes.c_int,
                                              P, P, ctypes.c_int]
         lib.ssm_oracle_scan_from.restype = ctypes.c_int
+        lib.ssm_oracle_scan_bwd.argtypes = [I64, I64, I64, I64] + [P] * 9 + [ctypes.c_int] + [P] * 11 + \
+            [ctypes.c_int]
+        lib.ssm_oracle_scan_bwd.restype = ctypes.c_int
         lib.ssm_oracle_step.argtypes = [I64, I64, I64, P, P, P, P, P, P, P, P, P, ctypes.c_int]
         lib.ssm_oracle_step.restype = ctypes.c_int
         _lib = lib
@@ -121,6 +124,39 @@ def step(state, u, delta, A, B, C, D=None, z=None,
     if rc != 0:
         raise ValueError("oracle step rejected N=%d" % N)
     return y, st
+
+
+def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus: bool = True, h0=None,
+             dlast=None, threads: Optional[int] = None) -> dict:
+    """fp64 gradients of the scan (from h0, or zero) given dy = dLoss/dy and dlast =
+    dLoss/d(last_state).  Returns a dict with du, ddelta (w.r.t. the delta input), dA, dB,
+    dC, and dD, dz, ddelta_bias, dh0 for the optional inputs that are given."""
+    u = _f64(u)
+    bsz, L, Dch = u.shape
+    A = _f64(A)
+    N = A.shape[1]
+    args = dict(delta=_f64(delta, (bsz, L, Dch)), B=_f64(B, (bsz, L, N)), C=_f64(C, (bsz, L, N)),
+                D=_f64(D, (Dch,)), z=_f64(z, (bsz, L, Dch)), delta_bias=_f64(delta_bias, (Dch,)),
+                h0=_f64(h0, (bsz, Dch, N)), dy=_f64(dy, (bsz, L, Dch)), dlast=_f64(dlast, (bsz, Dch, N)))
+    out = dict(du=np.empty((bsz, L, Dch)), ddelta=np.empty((bsz, L, Dch)), dA=np.empty((Dch, N)),
+               dB=np.empty((bsz, L, N)), dC=np.empty((bsz, L, N)))
+    if D is not None:
+        out["dD"] = np.empty(Dch)
+    if z is not None:
+        out["dz"] = np.empty((bsz, L, Dch))
+    if delta_bias is not None:
+        out["ddelta_bias"] = np.empty(Dch)
+    if h0 is not None:
+        out["dh0"] = np.empty((bsz, Dch, N))
+    rc = _load().ssm_oracle_scan_bwd(
+        bsz, L, Dch, N, _ptr(args["h0"]), _ptr(u), _ptr(args["delta"]), _ptr(A), _ptr(args["B"]), _ptr(args["C"]),
+        _ptr(args["D"]), _ptr(args["z"]), _ptr(args["delta_bias"]), int(bool(softplus)), _ptr(args["dy"]),
+        _ptr(args["dlast"]), _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
+        _ptr(out["dC"]), _ptr(out.get("dD")), _ptr(out.get("dz")), _ptr(out.get("ddelta_bias")),
+        _ptr(out.get("dh0")), int(threads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle backward failed (N=%d)" % N)
+    return out
 
 
 def scan_case(case, channels=None, threads: Optional[int] = None, h0=None):

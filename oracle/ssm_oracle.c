@@ -33,6 +33,8 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #define ORACLE_MAX_N 256
 
@@ -46,6 +48,13 @@ static double oracle_softplus(double x) {
 
 /* silu(z) = z * sigmoid(z) = z / (1 + e^-z). */
 static double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* sigmoid(x) = 1 / (1 + e^-x), written so that e^x is only taken of x <= 0. */
+static double oracle_sigmoid(double x) {
+    if (x >= 0.0) return 1.0 / (1.0 + exp(-x));
+    double e = exp(x);
+    return e / (1.0 + e);
+}
 
 /*
  * Scan over one batch of sequences, continuing from the state h0 (the recurrent form
@@ -135,4 +144,138 @@ int ssm_oracle_step(int64_t S, int64_t D, int64_t N, double *state,
         y[ch] = yt;
     }
     return 0;
+}
+
+/*
+ * Gradients of the scan from h0 (reverse mode of the recurrence, written out): given
+ * dy = dLoss/dy and dlast = dLoss/d(last_state) (NULL = 0), returns the gradients with
+ * respect to every input.  Per channel the forward states h_t are kept, then the tokens
+ * are walked backwards with the adjoint G = dLoss/dh_t carried from token t+1
+ * (G <- dA_t * lambda_t), where lambda_t = C_t dp_t + G is the full gradient w.r.t. h_t and
+ * dp_t = dy_t silu(z_t) the gradient w.r.t. the ungated output:
+ *   du_t     = D dp_t + sum_n lambda_t[n] delta_t B_t[n]
+ *   ddelta_t = (sum_n lambda_t[n] (A[n] dA_t[n] h_{t-1}[n] + B_t[n] u_t)) * softplus'(x_t)
+ *   dA[n]   += lambda_t[n] delta_t dA_t[n] h_{t-1}[n]
+ *   dB_t[n] += lambda_t[n] delta_t u_t,   dC_t[n] += dp_t h_t[n]   (summed over channels)
+ *   dD      += dp_t u_t,  ddelta_bias += ddelta_t,  dz_t = dy_t p_t silu'(z_t)
+ *   dh0      = the adjoint left after token 0
+ * with softplus'(x) = sigmoid(x) and silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z))).
+ * Shapes as ssm_oracle_scan_from; du, ddelta, dz [bsz][L][D]; dA [D][N]; dB, dC
+ * [bsz][L][N]; dD, dbias [D]; dh0 [bsz][D][N].  Every output is overwritten; dz, dD,
+ * dbias, dh0 may be NULL (not wanted).  Channels d are spread over the threads (each
+ * thread owns dA, dD, dbias of its channels); dB and dC are summed over channels from
+ * per-thread buffers.  Returns 0, or -1 if N is too large or memory is short.
+ */
+int ssm_oracle_scan_bwd(int64_t bsz, int64_t L, int64_t D, int64_t N, const double *h0,
+                        const double *u, const double *delta, const double *A,
+                        const double *B, const double *C, const double *Dv,
+                        const double *z, const double *delta_bias, int softplus_flag,
+                        const double *dy, const double *dlast,
+                        double *du, double *ddelta, double *dA, double *dB, double *dC,
+                        double *dD, double *dz, double *dbias, double *dh0, int nthreads) {
+    if (N > ORACLE_MAX_N || N < 1) return -1;
+    const int64_t nbt = bsz * L * N;
+    memset(dB, 0, sizeof(double) * (size_t)nbt);
+    memset(dC, 0, sizeof(double) * (size_t)nbt);
+    int fail = 0;
+#pragma omp parallel num_threads(nthreads)
+    {
+        double *hist = malloc(sizeof(double) * (size_t)((L > 0 ? L : 1) * N));   /* h_t */
+        double *decay = malloc(sizeof(double) * (size_t)((L > 0 ? L : 1) * N));  /* dA_t */
+        double *dt = malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+        double *dBl = calloc((size_t)(nbt > 0 ? nbt : 1), sizeof(double));
+        double *dCl = calloc((size_t)(nbt > 0 ? nbt : 1), sizeof(double));
+        const int have = hist && decay && dt && dBl && dCl;
+#pragma omp for schedule(static)
+        for (int64_t d = 0; d < D; ++d) {
+            if (!have) {
+#pragma omp atomic write
+                fail = 1;
+                continue;
+            }
+            double dD_d = 0.0, dbias_d = 0.0;
+            for (int64_t n = 0; n < N; ++n) dA[d * N + n] = 0.0;
+            for (int64_t b = 0; b < bsz; ++b) {
+                /* forward, keeping every state */
+                double h[ORACLE_MAX_N], hinit[ORACLE_MAX_N], G[ORACLE_MAX_N];
+                for (int64_t n = 0; n < N; ++n) {
+                    hinit[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;
+                    h[n] = hinit[n];
+                }
+                for (int64_t t = 0; t < L; ++t) {
+                    int64_t i = (b * L + t) * D + d;
+                    const double *Bt = B + (b * L + t) * N;
+                    double x = delta[i];
+                    if (delta_bias) x = x + delta_bias[d];
+                    dt[t] = softplus_flag ? oracle_softplus(x) : x;
+                    for (int64_t n = 0; n < N; ++n) {
+                        double a = exp(dt[t] * A[d * N + n]);
+                        h[n] = a * h[n] + dt[t] * Bt[n] * u[i];
+                        decay[t * N + n] = a;
+                        hist[t * N + n] = h[n];
+                    }
+                }
+                /* backward */
+                for (int64_t n = 0; n < N; ++n) G[n] = dlast ? dlast[(b * D + d) * N + n] : 0.0;
+                for (int64_t t = L - 1; t >= 0; --t) {
+                    int64_t i = (b * L + t) * D + d;
+                    const double *Bt = B + (b * L + t) * N;
+                    const double *Ct = C + (b * L + t) * N;
+                    double ut = u[i];
+                    double p = 0.0;
+                    for (int64_t n = 0; n < N; ++n) p = p + Ct[n] * hist[t * N + n];
+                    if (Dv) p = p + Dv[d] * ut;
+                    double g = z ? oracle_silu(z[i]) : 1.0;
+                    double dp = dy[i] * g;
+                    if (dz) {
+                        if (z) {
+                            double sg = oracle_sigmoid(z[i]);
+                            dz[i] = dy[i] * p * (sg * (1.0 + z[i] * (1.0 - sg)));
+                        } else {
+                            dz[i] = 0.0;
+                        }
+                    }
+                    dD_d = dD_d + dp * ut;
+                    double du_t = Dv ? Dv[d] * dp : 0.0;
+                    double dd = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        double lam = Ct[n] * dp + G[n];
+                        double hprev = t > 0 ? hist[(t - 1) * N + n] : hinit[n];
+                        double a = decay[t * N + n];
+                        dCl[(b * L + t) * N + n] += dp * hist[t * N + n];
+                        dBl[(b * L + t) * N + n] += lam * dt[t] * ut;
+                        du_t = du_t + lam * dt[t] * Bt[n];
+                        dd = dd + lam * (A[d * N + n] * a * hprev + Bt[n] * ut);
+                        dA[d * N + n] += lam * dt[t] * a * hprev;
+                        G[n] = a * lam;
+                    }
+                    double x = delta[i];
+                    if (delta_bias) x = x + delta_bias[d];
+                    double dx = softplus_flag ? dd * oracle_sigmoid(x) : dd;
+                    du[i] = du_t;
+                    ddelta[i] = dx;
+                    dbias_d = dbias_d + dx;
+                }
+                if (dh0)
+                    for (int64_t n = 0; n < N; ++n) dh0[(b * D + d) * N + n] = G[n];
+            }
+            if (dD) dD[d] = dD_d;
+            if (dbias) dbias[d] = dbias_d;
+        }
+        if (have) {
+#pragma omp critical
+            {
+                for (int64_t k = 0; k < nbt; ++k) {
+                    dB[k] += dBl[k];
+                    dC[k] += dCl[k];
+                }
+            }
+        }
+        free(hist);
+        free(decay);
+        free(dt);
+        free(dBl);
+        free(dCl);
+    }
+    return fail ? -1 : 0;
 }

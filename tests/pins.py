@@ -373,3 +373,76 @@ def check_h0_linear_without_input(scan_from, seed=53, L=30, D=2, N=3):
 
 
 H0_CHECKS = [check_h0_no_input_decay, check_h0_composition, check_h0_linear_without_input]
+
+
+# --- gradients of the scan ------------------------------------------------------------------
+# scan_from(u, x, A, B, C, D, z, bias, softplus, h0) -> (y, last_state)
+# scan_bwd(u, x, A, B, C, dy, D, z, bias, softplus, h0, dlast) -> dict of gradients
+
+def _bwd_case(seed, full):
+    rng = _rng(seed)
+    b, L, D, N = 2, 14, 3, 4
+    c = dict(u=rng.standard_normal((b, L, D)), x=0.5 * rng.standard_normal((b, L, D)),
+             A=-np.exp(rng.normal(0.0, 0.5, (D, N))), B=rng.standard_normal((b, L, N)),
+             C=rng.standard_normal((b, L, N)), D=None, z=None, bias=None, h0=None, dlast=None,
+             softplus=full)
+    if full:
+        c.update(D=rng.standard_normal(D), z=rng.standard_normal((b, L, D)), bias=rng.uniform(-1.0, 0.0, D),
+                 h0=rng.standard_normal((b, D, N)), dlast=rng.standard_normal((b, D, N)))
+    else:
+        c["x"] = np.abs(c["x"]) + 0.05          # without softplus the step size itself stays positive
+    c["dy"] = rng.standard_normal((b, L, D))
+    return c, rng
+
+
+def _check_bwd_fd(scan_from, scan_bwd, seed, full):
+    """Every gradient against a central difference of the forward (fp64, eps = 1e-6) along a
+    random direction: the loss is sum(dy * y) + sum(dlast * last_state)."""
+    c, rng = _bwd_case(seed, full)
+    g = scan_bwd(c["u"], c["x"], c["A"], c["B"], c["C"], c["dy"], c["D"], c["z"], c["bias"], c["softplus"],
+                 c["h0"], c["dlast"])
+
+    def loss(**kw):
+        a = dict(c)
+        a.update(kw)
+        y, last = scan_from(a["u"], a["x"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["softplus"],
+                            a["h0"])
+        val = np.sum(c["dy"] * y)
+        if c["dlast"] is not None:
+            val += np.sum(c["dlast"] * last)
+        return val
+
+    pairs = [("u", "du"), ("x", "ddelta"), ("A", "dA"), ("B", "dB"), ("C", "dC")]
+    if full:
+        pairs += [("D", "dD"), ("z", "dz"), ("bias", "ddelta_bias"), ("h0", "dh0")]
+    eps = 1e-6
+    for name, gk in pairs:
+        V = rng.standard_normal(np.shape(c[name]))
+        fd = (loss(**{name: c[name] + eps * V}) - loss(**{name: c[name] - eps * V})) / (2 * eps)
+        an = float(np.sum(g[gk] * V))
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (name, fd, an)
+
+
+def check_bwd_fd_all_inputs(scan_from, scan_bwd):
+    _check_bwd_fd(scan_from, scan_bwd, 71, True)
+
+
+def check_bwd_fd_plain(scan_from, scan_bwd):
+    _check_bwd_fd(scan_from, scan_bwd, 72, False)
+
+
+def check_bwd_closed_forms(scan_from, scan_bwd):
+    """dD = sum over batch and tokens of dy silu(z) u (the skip term is linear in D); with
+    C = 0 and no dlast nothing flows back through the state: dB = dA = 0, ddelta = 0 and
+    du = D dy silu(z)."""
+    c, _ = _bwd_case(73, True)
+    c["C"] = np.zeros_like(c["C"])
+    g = scan_bwd(c["u"], c["x"], c["A"], c["B"], c["C"], c["dy"], c["D"], c["z"], c["bias"], True, c["h0"], None)
+    gate = c["z"] / (1.0 + np.exp(-c["z"]))
+    assert _rel(g["dD"], np.sum(c["dy"] * gate * c["u"], axis=(0, 1))) < 1e-13
+    assert np.all(g["dB"] == 0.0) and np.all(g["dA"] == 0.0) and np.all(g["ddelta"] == 0.0)
+    assert np.all(g["dh0"] == 0.0)
+    assert _rel(g["du"], c["D"] * c["dy"] * gate) < 1e-13
+
+
+BWD_CHECKS = [check_bwd_fd_all_inputs, check_bwd_fd_plain, check_bwd_closed_forms]

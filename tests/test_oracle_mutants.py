@@ -35,6 +35,16 @@ MUTANTS = {
     "last_state_wrong_index": ("last_state[(b * D + d) * N + n] = h[n];", "last_state[(b * D + d) * N + n] = h[0];"),
     "softplus_wrong_branch": ("if (x > 0.0) return x + log1p(exp(-x));", "if (x > 0.0) return x + log1p(exp(x));"),
     "ignore_initial_state": ("h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;", "h[n] = 0.0;"),
+    "bwd_adjoint_without_decay": ("G[n] = a * lam;", "G[n] = lam;"),
+    "bwd_drop_input_term_of_ddelta": ("dd = dd + lam * (A[d * N + n] * a * hprev + Bt[n] * ut);",
+                                      "dd = dd + lam * (A[d * N + n] * a * hprev);"),
+    "bwd_current_state_for_previous": ("double hprev = t > 0 ? hist[(t - 1) * N + n] : hinit[n];",
+                                       "double hprev = hist[t * N + n];"),
+    "bwd_no_softplus_derivative": ("double dx = softplus_flag ? dd * oracle_sigmoid(x) : dd;", "double dx = dd;"),
+    "bwd_dC_from_adjoint": ("dCl[(b * L + t) * N + n] += dp * hist[t * N + n];",
+                            "dCl[(b * L + t) * N + n] += lam * hist[t * N + n];"),
+    "bwd_gate_derivative_missing_term": ("dz[i] = dy[i] * p * (sg * (1.0 + z[i] * (1.0 - sg)));",
+                                         "dz[i] = dy[i] * p * sg;"),
     "decay_squared": ("h[n] = dA * h[n] + dt * Bt[n] * ut;\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];\n            double yt = acc;\n            if (Dv) yt = yt + Dv[d] * ut;\n            if (z) yt = yt * oracle_silu(z[i]);",
                       "h[n] = dA * dA * h[n] + dt * Bt[n] * ut;\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];\n            double yt = acc;\n            if (Dv) yt = yt + Dv[d] * ut;\n            if (z) yt = yt * oracle_silu(z[i]);"),
 }
@@ -56,6 +66,8 @@ def _build_mutant(tmp_path, name, old, new):
     lib.ssm_oracle_scan_from.argtypes = [I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, ctypes.c_int, P, P,
                                          ctypes.c_int]
     lib.ssm_oracle_scan_from.restype = ctypes.c_int
+    lib.ssm_oracle_scan_bwd.argtypes = [I64, I64, I64, I64] + [P] * 9 + [ctypes.c_int] + [P] * 11 + [ctypes.c_int]
+    lib.ssm_oracle_scan_bwd.restype = ctypes.c_int
 
     def f64(a):
         return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
@@ -82,13 +94,25 @@ def _build_mutant(tmp_path, name, old, new):
         lib.ssm_oracle_scan_from(bsz, L, Dch, N, ptr(h0), ptr(u), ptr(x), ptr(A), ptr(B), ptr(C), ptr(D),
                                  ptr(z), ptr(bias), int(bool(softplus)), ptr(y), ptr(h), 1)
         return y, h
-    return scan, scan_from
+    def scan_bwd(u, x, A, B, C, dy, D, z, bias, softplus, h0, dlast):
+        u, x, A, B, C, dy, D, z, bias, h0, dlast = map(f64, (u, x, A, B, C, dy, D, z, bias, h0, dlast))
+        bsz, L, Dch = u.shape
+        N = A.shape[1]
+        out = dict(du=np.empty((bsz, L, Dch)), ddelta=np.empty((bsz, L, Dch)), dA=np.empty((Dch, N)),
+                   dB=np.empty((bsz, L, N)), dC=np.empty((bsz, L, N)), dD=np.empty(Dch),
+                   dz=np.empty((bsz, L, Dch)), ddelta_bias=np.empty(Dch), dh0=np.empty((bsz, Dch, N)))
+        lib.ssm_oracle_scan_bwd(bsz, L, Dch, N, ptr(h0), ptr(u), ptr(x), ptr(A), ptr(B), ptr(C), ptr(D), ptr(z),
+                                ptr(bias), int(bool(softplus)), ptr(dy), ptr(dlast), ptr(out["du"]),
+                                ptr(out["ddelta"]), ptr(out["dA"]), ptr(out["dB"]), ptr(out["dC"]), ptr(out["dD"]),
+                                ptr(out["dz"]), ptr(out["ddelta_bias"]), ptr(out["dh0"]), 1)
+        return out
+    return scan, scan_from, scan_bwd
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(tmp_path, name):
     old, new = MUTANTS[name]
-    scan, scan_from = _build_mutant(tmp_path, name, old, new)
+    scan, scan_from, scan_bwd = _build_mutant(tmp_path, name, old, new)
     caught = []
     with np.errstate(all="ignore"):
         for check in pins.ALL_CHECKS:
@@ -99,6 +123,11 @@ def test_planted_mistake_is_caught(tmp_path, name):
         for check in pins.H0_CHECKS:
             try:
                 check(scan_from)
+            except AssertionError:
+                caught.append(check.__name__)
+        for check in pins.BWD_CHECKS:
+            try:
+                check(scan_from, scan_bwd)
             except AssertionError:
                 caught.append(check.__name__)
     assert caught, f"mutant {name} passed every pin"

@@ -113,3 +113,15 @@ def test_scan_from_state_equals_steps(oracle_mod):
         yt, st = oracle_mod.step(st, u[:, t], dt[:, t], A, B[:, t], C[:, t], D=Dv, z=z[:, t])
         assert np.array_equal(yt, y[:, t])
     assert np.array_equal(st, last)
+
+
+def _scan_bwd(oracle_mod):
+    def f(u, x, A, B, C, dy, D, z, bias, softplus, h0, dlast):
+        return oracle_mod.scan_bwd(u, x, A, B, C, dy, D=D, z=z, delta_bias=bias, softplus=softplus, h0=h0,
+                                   dlast=dlast)
+    return f
+
+
+@pytest.mark.parametrize("check", pins.BWD_CHECKS, ids=lambda c: c.__name__)
+def test_bwd_pins(oracle_mod, check):
+    check(_scan_from(oracle_mod), _scan_bwd(oracle_mod))
