@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define SSMSCAN_VERSION 2
+#define SSMSCAN_VERSION 3
 
 #if defined(__GNUC__) || defined(__clang__)
 #define SSMSCAN_API __attribute__((visibility("default")))
@@ -133,6 +133,37 @@ SSMSCAN_API int ssm_scan_fwd_from(const float *initial_state, const void *u, con
                       const void *B, const void *C, const float *D, const void *z, const float *delta_bias,
                       int softplus_flag, void *y, float *last_state, const ssm_dims *dims, void *workspace,
                       size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace ssm_scan_bwd needs: the checkpointed states, one per 16
+ * tokens (batch * ceil(seqlen / 16) * dim * dstate fp32, 256-byte aligned).  Returns 0 for
+ * an invalid or empty problem. */
+SSMSCAN_API size_t ssm_scan_bwd_workspace_bytes(const ssm_dims *dims);
+
+/* Gradients of ssm_scan_fwd_from (and so of ssm_scan_fwd, initial_state NULL) with respect
+ * to every input, given dy = dLoss/dy and dlast_state = dLoss/d(last_state): the backward
+ * pass, recomputing the states from checkpoints instead of storing them
+ * (azimuth.plus/paper/mamba, hardware-aware algorithm section).
+ *   inputs          : exactly those of the forward call (same shapes, dtypes, NULLs)
+ *   dy              : [batch][seqlen][dim] (io_dtype)
+ *   dlast_state     : [batch][dim][dstate] fp32, or NULL (= 0)
+ *   du, ddelta      : [batch][seqlen][dim] (io_dtype) outputs; ddelta is the gradient with
+ *                     respect to the delta input (through delta_bias and softplus)
+ *   dz              : [batch][seqlen][dim] (io_dtype) output, required when z is given
+ *   dA              : [dim][dstate] fp32 output
+ *   dB, dC          : [batch][seqlen][dstate] fp32 outputs (summed over channels)
+ *   dD, ddelta_bias : [dim] fp32 outputs, or NULL (not wanted)
+ *   dinitial_state  : [batch][dim][dstate] fp32 output, or NULL (not wanted)
+ *   workspace       : at least ssm_scan_bwd_workspace_bytes(dims) bytes, 16-byte aligned
+ * dims->chunk_len is ignored.  dA, dB, dC, dD and ddelta_bias are sums over many
+ * workgroups, accumulated with atomic adds after the library has zeroed them: their last
+ * bits may differ from run to run.  Outputs must not overlap inputs or each other.
+ * Returns SSM_OK or a negative ssm_status (validation before any launch). */
+SSMSCAN_API int ssm_scan_bwd(const float *initial_state, const void *u, const void *delta, const float *A,
+                 const void *B, const void *C, const float *D, const void *z, const float *delta_bias,
+                 int softplus_flag, const void *dy, const float *dlast_state, void *du, void *ddelta,
+                 float *dA, float *dB, float *dC, float *dD, void *dz, float *ddelta_bias,
+                 float *dinitial_state, const ssm_dims *dims, void *workspace, size_t workspace_bytes,
+                 void *stream);
 
 /* One recurrent (inference) step for `batch` independent sequences: the constant-memory
  * recurrent form (shakilmahmud.com section 3; urworte.de "Methodische Grundlagen").

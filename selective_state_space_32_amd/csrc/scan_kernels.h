@@ -29,7 +29,10 @@ namespace ssm {
 
 constexpr int kChanTile = 64;    // channels per workgroup (one per lane)
 
-enum ScanMode { kFull = 0, kSummary = 1 };
+enum ScanMode { kFull = 0, kSummary = 1, kCheckpoint = 2 };
+
+// kCheckpoint stores the state before every kCkptEvery-th token (for the backward pass).
+constexpr int kCkptEvery = 16;
 
 // s_waitcnt immediate that waits for all LDS and scalar-memory operations (lgkmcnt = 0) and
 // leaves the vector-memory and export counters unconstrained (gfx9 encoding).
@@ -71,6 +74,9 @@ __device__ __forceinline__ void load_slice(const IO *__restrict__ p, int64_t off
 //             the last_state buffer.
 //   kSummary: start from h = 0, no readout; write the chunk's local final state to
 //             cstate[b][c] and the chunk's sum of step sizes to cdsum[b][c].
+//   kCheckpoint: one pass from h0 without readout, storing the state before every
+//             kCkptEvery-th token to cstate[b][t / kCkptEvery] (the backward pass's
+//             recomputation points).
 //   N: state size; S: states per wave (K = N/S waves); T: tokens per LDS tile.
 //   VEC: the prep and epilogue move V consecutive channels of one token per thread
 //        (one 16-byte access for 8 bf16); needs D % 8 == 0 and 16-byte aligned u, delta,
@@ -90,7 +96,8 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     constexpr int P = J / V;                   // accesses per thread per tile
     constexpr int GPR = kChanTile / V;         // threads per token row
     constexpr int RPP = 64 * K / GPR;          // token rows per access round
-    constexpr bool READOUT = MODE != kSummary;
+    constexpr bool READOUT = MODE == kFull;
+    static_assert(MODE != kCheckpoint || T % kCkptEvery == 0, "checkpoints fall on tile halves");
     static_assert(T % K == 0 && J % V == 0 && RPP * P == T, "tile must split evenly over the threads");
     using VIO = vec<V, IO>;
     constexpr int W = VEC ? V * (int)sizeof(IO) / 4 : 1;
@@ -132,7 +139,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
         a2[s] = act ? A[d * N + w * S + s] * kLog2e : 0.0f;
         h[s] = 0.0f;
     }
-    if (MODE == kFull && act) {
+    if ((MODE == kFull || MODE == kCheckpoint) && act) {
         // the state before this chunk: carried from chunk c-1, or the initial state (read
         // from h0 itself in a single pass, from the copy in slot nchunk-1 otherwise)
         const float *src = nullptr;
@@ -188,6 +195,16 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     };
     load_tile(t_begin, r0);
     load_tile(t_begin + T, r1);
+    // kCheckpoint: the state before token t (t a multiple of kCkptEvery) into
+    // cstate[b][t / kCkptEvery][d][:]
+    const int64_t n_ckpt = (L + kCkptEvery - 1) / kCkptEvery;
+    auto checkpoint = [&](int64_t t) {
+        if (MODE == kCheckpoint && act && t < t_end) {
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+                cstate[(((int64_t)b * n_ckpt + t / kCkptEvery) * D + d) * N + w * S + s] = h[s];
+        }
+    };
     // epilogue of a tile: y = (sum of the K partial readouts + D u) * silu(z), read from
     // s_yp after the recurrence of that tile
     // (the skip term is applied as one explicit FMA, D u + partial_0, so that no tile
@@ -253,6 +270,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
         load_tile(t0 + 2 * T, r);
         __syncthreads();
         // recurrence over the tile: lane = channel, this wave's S states
+        checkpoint(t0);
         if (PIPE && nt == T) {
             // A full tile, software-pipelined in groups of G tokens (two register sets,
             // ping-pong): after the wait for the current group, the LDS (delta, delta*u)
@@ -290,7 +308,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                     }
                     if (READOUT)
                         s_yp[w][g0 + i][lane] = acc;
-                    else
+                    else if (MODE == kSummary)
                         dsum += v[i].x;
                 }
             };
@@ -300,6 +318,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                 __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
                 gload(g0 + G, vb, bb, cb);
                 __builtin_amdgcn_sched_barrier(0);
+                if (g0 > 0 && g0 % kCkptEvery == 0) checkpoint(t0 + g0);
                 gcomp(g0, va, ba, ca);
                 __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
                 gload(g0 + 2 * G, va, ba, ca);
@@ -310,6 +329,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
             // a partial tile (or a slice shape the pipelined loop does not take)
 #pragma unroll 4
             for (int tt = 0; tt < nt; ++tt) {
+                if (tt > 0 && tt % kCkptEvery == 0) checkpoint(t0 + tt);
                 const f32x2_t v = s_dk[tt][lane];
                 const int64_t boff = (row0 + t0 + tt) * N + w * S;
                 float Bs[S], Cs[S];
@@ -324,7 +344,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                 }
                 if (READOUT)
                     s_yp[w][tt][lane] = acc;
-                else
+                else if (MODE == kSummary)
                     dsum += v.x;
             }
         }

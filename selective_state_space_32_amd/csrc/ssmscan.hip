@@ -12,6 +12,7 @@
 #include "carry_kernel.h"
 #include "scan_kernels.h"
 #include "step_kernel.h"
+#include "bwd_kernel.h"
 
 namespace {
 
@@ -230,6 +231,88 @@ int dispatch_step(int64_t N, float *state, const void *u, const void *delta, con
     return fail(SSM_ERR_UNSUPPORTED_N, "dstate %lld not supported", (long long)N);
 }
 
+// ---- backward ----------------------------------------------------------------------------
+
+size_t bwd_workspace_bytes(const ssm_dims *dm) {
+    const int64_t n_ckpt = (dm->seqlen + ssm::kCkptEvery - 1) / ssm::kCkptEvery;
+    return align256((size_t)(dm->batch * n_ckpt * dm->dim * dm->dstate) * sizeof(float));
+}
+
+template <typename TP>
+void fill_zero(TP *p, int64_t n, hipStream_t st) {
+    if (p && n > 0)
+        hipLaunchKernelGGL(ssm::fill_zero_kernel<TP>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
+}
+
+struct BwdArgs {
+    const float *h0;
+    const void *u, *delta;
+    const float *A;
+    const void *B, *C;
+    const float *D;
+    const void *z;
+    const float *bias;
+    int softplus;
+    const void *dy;
+    const float *dlast;
+    void *du, *ddelta;
+    float *dA, *dB, *dC, *dD;
+    void *dz;
+    float *dbias, *dh0;
+};
+
+template <int N, typename IO>
+int launch_bwd(const BwdArgs &a, const ssm_dims *dm, void *ws, hipStream_t st) {
+    constexpr int S = ScanShape<N>::S, T = ScanShape<N>::T, K = N / S;
+    constexpr int KB = ssm::BwdShape<N>::K;
+    const int64_t bsz = dm->batch, L = dm->seqlen, D = dm->dim;
+    const int tiles_per_b = (int)((D + ssm::kChanTile - 1) / ssm::kChanTile);
+    const int n_tiles = (int)(bsz * tiles_per_b);
+    const IO *u = static_cast<const IO *>(a.u), *dl = static_cast<const IO *>(a.delta);
+    const IO *B = static_cast<const IO *>(a.B), *C = static_cast<const IO *>(a.C);
+    const IO *z = static_cast<const IO *>(a.z), *dy = static_cast<const IO *>(a.dy);
+    IO *du = static_cast<IO *>(a.du), *ddl = static_cast<IO *>(a.ddelta), *dz = static_cast<IO *>(a.dz);
+    float *ckpt = static_cast<float *>(ws);
+    // forward in checkpoint mode: the state before every kCkptEvery-th token
+    const bool vf = D % 8 == 0 && aligned(u, 16) && aligned(dl, 16);
+    if (vf)
+        hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kCheckpoint, true>), dim3((unsigned)n_tiles, 1),
+                           dim3(64 * K), 0, st, u, dl, (const IO *)nullptr, (IO *)nullptr, a.A, (const float *)nullptr,
+                           a.bias, B, C, a.h0, (float *)nullptr, ckpt, (float *)nullptr, L, D, tiles_per_b, n_tiles, L,
+                           1, a.softplus);
+    else
+        hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kCheckpoint, false>), dim3((unsigned)n_tiles, 1),
+                           dim3(64 * K), 0, st, u, dl, (const IO *)nullptr, (IO *)nullptr, a.A, (const float *)nullptr,
+                           a.bias, B, C, a.h0, (float *)nullptr, ckpt, (float *)nullptr, L, D, tiles_per_b, n_tiles, L,
+                           1, a.softplus);
+    // the reverse walk; 16-byte (or 8-byte) element access when every (token, channel) tensor allows it
+    const bool vb = D % 8 == 0 && aligned(u, 16) && aligned(dl, 16) && aligned(dy, 16) && aligned(du, 16) &&
+                    aligned(ddl, 16) && (!z || (aligned(z, 16) && aligned(dz, 16)));
+    if (vb)
+        hipLaunchKernelGGL((ssm::scan_bwd_kernel<N, IO, true>), dim3((unsigned)n_tiles), dim3(64 * KB), 0, st, u, dl,
+                           z, dy, a.A, a.D, a.bias, B, C, ckpt, a.dlast, du, ddl, dz, a.dA, a.dB, a.dC, a.dD, a.dbias,
+                           a.dh0, L, D, tiles_per_b, a.softplus);
+    else
+        hipLaunchKernelGGL((ssm::scan_bwd_kernel<N, IO, false>), dim3((unsigned)n_tiles), dim3(64 * KB), 0, st, u, dl,
+                           z, dy, a.A, a.D, a.bias, B, C, ckpt, a.dlast, du, ddl, dz, a.dA, a.dB, a.dC, a.dD, a.dbias,
+                           a.dh0, L, D, tiles_per_b, a.softplus);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+template <typename IO>
+int dispatch_bwd(int64_t N, const BwdArgs &a, const ssm_dims *dm, void *ws, hipStream_t st) {
+    switch (N) {
+        case 1: return launch_bwd<1, IO>(a, dm, ws, st);
+        case 2: return launch_bwd<2, IO>(a, dm, ws, st);
+        case 4: return launch_bwd<4, IO>(a, dm, ws, st);
+        case 8: return launch_bwd<8, IO>(a, dm, ws, st);
+        case 16: return launch_bwd<16, IO>(a, dm, ws, st);
+    }
+    return fail(SSM_ERR_UNSUPPORTED_N, "dstate %lld not supported", (long long)N);
+}
+
 }  // namespace
 
 static int scan_impl(const float *h0, const void *u, const void *delta, const float *A, const void *B,
@@ -334,6 +417,68 @@ int ssm_step(float *state, const void *u, const void *delta, const float *A, con
     if (dims->io_dtype == SSM_IO_BF16)
         return dispatch_step<uint16_t>(N, state, u, delta, A, B, C, D, z, y, dims, st);
     return dispatch_step<float>(N, state, u, delta, A, B, C, D, z, y, dims, st);
+}
+
+size_t ssm_scan_bwd_workspace_bytes(const ssm_dims *dims) {
+    if (check_dims(dims, true) != SSM_OK) return 0;
+    return bwd_workspace_bytes(dims);
+}
+
+int ssm_scan_bwd(const float *initial_state, const void *u, const void *delta, const float *A, const void *B,
+                 const void *C, const float *D, const void *z, const float *delta_bias, int softplus_flag,
+                 const void *dy, const float *dlast_state, void *du, void *ddelta, float *dA, float *dB,
+                 float *dC, float *dD, void *dz, float *ddelta_bias, float *dinitial_state, const ssm_dims *dims,
+                 void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = check_dims(dims, true);
+    if (rc != SSM_OK) return rc;
+    const int64_t bsz = dims->batch, L = dims->seqlen, Dm = dims->dim, N = dims->dstate;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!A || !dA || (bsz > 0 && L > 0 && Dm > 0 && (!u || !delta || !B || !C || !dy || !du || !ddelta || !dB || !dC)))
+        return fail(SSM_ERR_NULL, "required pointer is NULL");
+    if (z && !dz) return fail(SSM_ERR_NULL, "z is given but dz is NULL");
+    const size_t es = dims->io_dtype == SSM_IO_BF16 ? 2 : 4;
+    if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) || !aligned(dy, es) ||
+        !aligned(du, es) || !aligned(ddelta, es) || (z && (!aligned(z, es) || !aligned(dz, es))) ||
+        !aligned(A, 4) || !aligned(dA, 4) || !aligned(dB, 4) || !aligned(dC, 4) || (D && !aligned(D, 4)) ||
+        (dD && !aligned(dD, 4)) || (delta_bias && !aligned(delta_bias, 4)) ||
+        (ddelta_bias && !aligned(ddelta_bias, 4)) || (initial_state && !aligned(initial_state, 4)) ||
+        (dlast_state && !aligned(dlast_state, 4)) || (dinitial_state && !aligned(dinitial_state, 4)))
+        return fail(SSM_ERR_ALIGN, "a tensor pointer is not aligned to its element size");
+    if (dims->io_dtype == SSM_IO_BF16 && N >= 2 && (!aligned(B, 4) || !aligned(C, 4)))
+        return fail(SSM_ERR_ALIGN, "bf16 B and C must be 4-byte aligned");
+    const size_t need = bwd_workspace_bytes(dims);
+    if (bsz > 0 && L > 0 && Dm > 0) {
+        if (!workspace) return fail(SSM_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+        if (workspace_bytes < need)
+            return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+                        need);
+        if (!aligned(workspace, 16)) return fail(SSM_ERR_ALIGN, "workspace not 16-byte aligned");
+    }
+    // the summed gradients are accumulated atomically: start them from zero
+    fill_zero(dA, Dm * N, st);
+    fill_zero(dB, bsz * L * N, st);
+    fill_zero(dC, bsz * L * N, st);
+    fill_zero(dD, Dm, st);
+    fill_zero(ddelta_bias, Dm, st);
+    if (bsz == 0 || Dm == 0) return ok();
+    if (L == 0) {
+        // no tokens: the state's gradient passes straight through
+        if (dinitial_state) {
+            const int64_t n = bsz * Dm * N;
+            if (dlast_state)
+                hipLaunchKernelGGL(ssm::copy_kernel<float>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                                   dinitial_state, dlast_state, n);
+            else
+                fill_zero(dinitial_state, n, st);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+        return ok();
+    }
+    BwdArgs a{initial_state, u, delta, A, B, C, D, z, delta_bias, softplus_flag != 0, dy, dlast_state, du, ddelta,
+              dA, dB, dC, dD, dz, ddelta_bias, dinitial_state};
+    if (dims->io_dtype == SSM_IO_BF16) return dispatch_bwd<uint16_t>(N, a, dims, workspace, st);
+    return dispatch_bwd<float>(N, a, dims, workspace, st);
 }
 
 }  // extern "C"

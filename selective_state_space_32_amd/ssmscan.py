@@ -51,6 +51,10 @@ def _load() -> ctypes.CDLL:
     lib.ssm_scan_fwd.restype = ctypes.c_int
     lib.ssm_scan_fwd_from.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_int, P, P, D, P, ctypes.c_size_t, P]
     lib.ssm_scan_fwd_from.restype = ctypes.c_int
+    lib.ssm_scan_bwd_workspace_bytes.argtypes = [D]
+    lib.ssm_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssm_scan_bwd.argtypes = [P] * 9 + [ctypes.c_int] + [P] * 11 + [D, P, ctypes.c_size_t, P]
+    lib.ssm_scan_bwd.restype = ctypes.c_int
     lib.ssm_step.argtypes = [P, P, P, P, P, P, P, P, P, D, P]
     lib.ssm_step.restype = ctypes.c_int
     return lib
@@ -207,6 +211,57 @@ def scan_fwd_from(initial_state: torch.Tensor, u: torch.Tensor, delta: torch.Ten
                                             return_last_state, chunk_len, workspace, stream, initial_state)
     _check(lib.ssm_scan_fwd_from(*args))
     return y, last_state
+
+
+def scan_bwd(dy: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+             C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+             delta_bias: Optional[torch.Tensor] = None, softplus: bool = True, *,
+             initial_state: Optional[torch.Tensor] = None, dlast_state: Optional[torch.Tensor] = None,
+             want_initial_state_grad: bool = False, workspace: Optional[torch.Tensor] = None,
+             stream=None) -> dict:
+    """Gradients of the scan (ssm_scan_bwd) given dy (batch, L, dim) and optionally
+    dlast_state (batch, dim, N).  The forward inputs are passed as to scan_fwd / scan_fwd_from.
+    Returns a dict: du, ddelta, dz (if z), dA, dB, dC (float32), dD (if D), ddelta_bias
+    (if delta_bias), dinitial_state (if asked for)."""
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, L, dim)")
+    bsz, L, dim = u.shape
+    N = A.shape[-1]
+    dev, io = u.device, u.dtype
+    _io_code(io)
+    for t, name, shape, dt in ((u, "u", (bsz, L, dim), io), (delta, "delta", (bsz, L, dim), io),
+                               (A, "A", (dim, N), torch.float32), (B, "B", (bsz, L, N), io),
+                               (C, "C", (bsz, L, N), io), (dy, "dy", (bsz, L, dim), io)):
+        _need(t, name, shape, dt, dev)
+    for t, name, shape, dt in ((D, "D", (dim,), torch.float32), (z, "z", (bsz, L, dim), io),
+                               (delta_bias, "delta_bias", (dim,), torch.float32),
+                               (initial_state, "initial_state", (bsz, dim, N), torch.float32),
+                               (dlast_state, "dlast_state", (bsz, dim, N), torch.float32)):
+        if t is not None:
+            _need(t, name, shape, dt, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(du=torch.empty((bsz, L, dim), dtype=io, device=dev), ddelta=torch.empty((bsz, L, dim), dtype=io, device=dev),
+             dA=torch.empty((dim, N), **f32), dB=torch.empty((bsz, L, N), **f32), dC=torch.empty((bsz, L, N), **f32))
+    if z is not None:
+        g["dz"] = torch.empty((bsz, L, dim), dtype=io, device=dev)
+    if D is not None:
+        g["dD"] = torch.empty((dim,), **f32)
+    if delta_bias is not None:
+        g["ddelta_bias"] = torch.empty((dim,), **f32)
+    if want_initial_state_grad:
+        g["dinitial_state"] = torch.empty((bsz, dim, N), **f32)
+    dims = make_dims(bsz, L, dim, N, io)
+    need = int(lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(dims)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = lib.ssm_scan_bwd(_ptr(initial_state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                          _ptr(delta_bias), int(bool(softplus)), _ptr(dy), _ptr(dlast_state), _ptr(g["du"]),
+                          _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dD")),
+                          _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")), _ptr(g.get("dinitial_state")),
+                          ctypes.byref(dims), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                          _stream_handle(stream))
+    _check(rc)
+    return g
 
 
 def _step_args(state, u, delta, A, B, C, D, z, y, stream):

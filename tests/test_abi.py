@@ -27,8 +27,8 @@ def b():
 
 def test_header_declares_the_entry_points():
     syms = set(declared_symbols())
-    assert {"ssm_scan_fwd", "ssm_scan_fwd_from", "ssm_step", "ssm_scan_workspace_bytes", "ssm_scan_plan",
-            "ssm_last_error", "ssm_version"} <= syms
+    assert {"ssm_scan_fwd", "ssm_scan_fwd_from", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes", "ssm_step",
+            "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_last_error", "ssm_version"} <= syms
 
 
 def test_library_exports_every_declared_symbol():
@@ -107,6 +107,30 @@ def test_scan_from_validation(b):
     assert "initial_state" in b.last_error()
     args[0] = P(0)
     assert b.lib.ssm_scan_fwd_from(P(FAKE), *args) == -1
+
+
+def _bwd(b, dims, ws_bytes=None, **kw):
+    P = ctypes.c_void_p
+    names = ["h0", "u", "delta", "A", "B", "C", "D", "z", "bias", "softplus", "dy", "dlast", "du", "ddelta", "dA",
+             "dB", "dC", "dD", "dz", "dbias", "dh0"]
+    vals = dict(h0=None, u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, softplus=1, dy=FAKE,
+                dlast=None, du=FAKE, ddelta=FAKE, dA=FAKE, dB=FAKE, dC=FAKE, dD=None, dz=None, dbias=None, dh0=None)
+    vals.update(kw)
+    args = [vals[k] if k == "softplus" else (P(vals[k]) if vals[k] else None) for k in names]
+    if ws_bytes is None:
+        ws_bytes = b.lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(dims))
+    return b.lib.ssm_scan_bwd(*args, ctypes.byref(dims), P(FAKE), ws_bytes, None)
+
+
+def test_bwd_validation(b):
+    # every rejection happens before any launch (the pointers are never dereferenced)
+    d = _dims(b)
+    assert b.lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(d)) >= 2 * 4 * 128 * 16 * 4
+    assert _bwd(b, d, dy=0) == -1
+    assert _bwd(b, d, z=FAKE) == -1 and "dz" in b.last_error()
+    assert _bwd(b, d, du=FAKE + 1) == -4
+    assert _bwd(b, d, dh0=FAKE + 2) == -4
+    assert _bwd(b, d, ws_bytes=16) == -6
 
 
 def test_misaligned_rejected(b):
