@@ -41,7 +41,13 @@ WORKLOADS = {
     "c3": "selective scan B8 L2048 D5120 N16, bf16 I/O, fp32 state, SiLU(z) gate, D skip, last_state",
     "c4": "selective scan B1 L131072 D2048 N16, bf16 I/O, fp32 state, last_state",
     "c5": "recurrent step S256 D5120 N16, bf16 I/O, fp32 state in place",
+    "c3_bwd": "selective scan backward B8 L2048 D5120 N16, bf16 I/O, fp32 state, SiLU(z) gate, D skip",
 }
+# VALU issue slots per (token, channel, state) of the backward: the recomputed step (delta*A,
+# exp2 = 2, (delta u)*B, state FMA, readout FMA for the gate gradient) and the adjoint step
+# (lambda FMA, delta*A and exp2 = 3 for the decay, decay * h_{t-1}, lambda*delta, dA FMA,
+# A*(decay h) + B*u = 2, d delta FMA, du FMA, the dB and dC terms, the carried adjoint).
+SLOTS_PER_ELEMENT_BWD = 20
 METRIC = "selective-scan HBM GB/s (% of peak) + channel-tokens/s, B8 L2048 D5120 N16 bf16"
 
 
@@ -61,6 +67,12 @@ def step_alg_bytes(S, D, N, io_bytes, gate, skip):
     """state read + write, u, delta, (z), y per (sequence, channel), B, C per sequence, A, D."""
     return S * D * (2 * N * 4 + io_bytes * (3 + (1 if gate else 0))) + 2 * S * N * io_bytes + D * N * 4 + \
         (D * 4 if skip else 0)
+
+
+def scan_bwd_alg_bytes(bsz, L, D, N, io_bytes):
+    """Bytes the backward must move: u, delta, z, dy read and du, ddelta, dz written per
+    element; B, C read and dB, dC (fp32) written per token; A, dA, D, dD, bias, dbias."""
+    return (bsz * L * D * io_bytes * 7 + bsz * L * N * (2 * io_bytes + 2 * 4) + D * N * 4 * 2 + D * 4 * 4)
 
 
 def kernel_source_digest() -> str:
@@ -111,6 +123,36 @@ def cpu_baseline_scan(case, alg_bytes_full, target_s=30.0):
                       f"(fp64 oracle, OpenMP over channels)"}
 
 
+def cpu_baseline_bwd(case, alg_bytes_full, target_s=20.0):
+    """The fp64 oracle's backward on a channel sample of the workload (per-channel work is
+    independent; the cross-channel dB / dC sums then cover the sample only)."""
+    from oracle import oracle
+    oracle.build(force=False)
+    threads = min(16, oracle.default_threads())
+    rng = np.random.default_rng(12)
+    dyv = rng.standard_normal((case.bsz, case.L, 16))
+
+    def run(sel):
+        zv = case.values("z")
+        oracle.scan_bwd(case.values("u")[:, :, sel], case.values("delta")[:, :, sel], case.A[sel], case.values("B"),
+                        case.values("C"), np.resize(dyv, (case.bsz, case.L, len(sel))), D=case.Dskip[sel],
+                        z=None if zv is None else zv[:, :, sel], delta_bias=case.delta_bias[sel],
+                        softplus=case.softplus, threads=threads)
+    probe = np.arange(16)
+    t = time.perf_counter()
+    run(probe)
+    per_ch = (time.perf_counter() - t) / len(probe)
+    k = int(min(case.D, max(16, target_s / max(per_ch, 1e-9))))
+    sel = np.linspace(0, case.D - 1, k).astype(np.int64)
+    t = time.perf_counter()
+    run(sel)
+    dt = time.perf_counter() - t
+    return {"value": round(alg_bytes_full * len(sel) / case.D / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{len(sel)} of {case.D} channels x all {case.bsz} sequences x {case.L} tokens "
+                      f"(fp64 oracle backward, OpenMP over channels)"}
+
+
 def cpu_baseline_step(case, alg_bytes_step, target_s=20.0):
     from oracle import oracle
     oracle.build(force=False)
@@ -159,7 +201,7 @@ def main():
 
     dev = "cuda"
     wl = args.workload
-    case = inputs.config_case(wl)
+    case = inputs.config_case("c3" if wl == "c3_bwd" else wl)
     io_bytes = 2 if case.io == "bf16" else 4
 
     def td(a):
@@ -187,6 +229,22 @@ def main():
         def one(i):
             calls[i % case.steps]()
         plan = "one step kernel per call"
+    elif wl == "c3_bwd":
+        t = {k: td(getattr(case, f)) for k, f in (("u", "u"), ("delta", "delta"), ("A", "A"), ("B", "B"),
+                                                   ("C", "C"), ("D", "Dskip"), ("z", "z"), ("bias", "delta_bias"))}
+        bsz, L, D, N = case.bsz, case.L, case.D, case.N
+        dy = td(inputs.bf16_bits(np.random.default_rng(13).standard_normal((bsz, L, D), dtype=np.float32)))
+        ws = torch.empty(max(1, ssmscan.bwd_workspace_bytes(bsz, L, D, N, dy.dtype)), dtype=torch.uint8, device=dev)
+        grads = ssmscan.scan_bwd(dy, t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                 delta_bias=t["bias"], softplus=case.softplus, workspace=ws)
+        alg = scan_bwd_alg_bytes(bsz, L, D, N, io_bytes)
+        chtok = bsz * L * D
+        elements = chtok * N
+
+        def one(i):
+            ssmscan.scan_bwd(dy, t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                             delta_bias=t["bias"], softplus=case.softplus, workspace=ws, out=grads)
+        plan = "checkpoint pass (state every 16 tokens) + backward kernel"
     else:
         t = {k: td(getattr(case, f)) for k, f in (("u", "u"), ("delta", "delta"), ("A", "A"), ("B", "B"),
                                                    ("C", "C"), ("D", "Dskip"), ("z", "z"), ("bias", "delta_bias"))}
@@ -249,7 +307,8 @@ def main():
     step_s = wall / args.steps
     gbps = alg / step_s / 1e9          # whole-job throughput over the timed region
     kern_gbps = alg / kern_s / 1e9     # the kernel's own rate (event-timed launches)
-    lane_ops = elements * SLOTS_PER_ELEMENT / kern_s / 1e12
+    slots = SLOTS_PER_ELEMENT_BWD if wl == "c3_bwd" else SLOTS_PER_ELEMENT
+    lane_ops = elements * slots / kern_s / 1e12
     traffic = counter_traffic(wl)
     if wl == "c5":
         roof = {"bound": "hbm", "achieved": round(kern_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -258,12 +317,13 @@ def main():
         roof = {"bound": "alu", "achieved": round(lane_ops, 3), "peak": round(VALU_PEAK_TLANEOPS, 3),
                 "unit": "T fp32 VALU lane-ops/s", "frac": round(lane_ops / VALU_PEAK_TLANEOPS, 4),
                 "traffic": traffic,
-                "work": f"{SLOTS_PER_ELEMENT} VALU issue slots per (token, channel, state) x {elements} per launch"}
+                "work": f"{slots} VALU issue slots per (token, channel, state) x {elements} per launch"}
 
     cpu = None
     if not args.no_cpu:
         try:
-            cpu = cpu_baseline_step(case, alg) if wl == "c5" else cpu_baseline_scan(case, alg)
+            cpu = (cpu_baseline_step(case, alg) if wl == "c5" else cpu_baseline_bwd(case, alg) if wl == "c3_bwd"
+                   else cpu_baseline_scan(case, alg))
         except Exception as e:  # the GPU figures stand without it
             cpu = {"error": repr(e)}
 

@@ -90,6 +90,11 @@ def workspace_bytes(batch: int, seqlen: int, dim: int, dstate: int, io_dtype, ch
     return int(lib.ssm_scan_workspace_bytes(ctypes.byref(d)))
 
 
+def bwd_workspace_bytes(batch: int, seqlen: int, dim: int, dstate: int, io_dtype) -> int:
+    d = make_dims(batch, seqlen, dim, dstate, io_dtype)
+    return int(lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(d)))
+
+
 def scan_plan(batch: int, seqlen: int, dim: int, dstate: int, io_dtype, chunk_len: int = 0) -> Tuple[int, int]:
     """(number of chunks per sequence, chunk length) the library will use."""
     d = make_dims(batch, seqlen, dim, dstate, io_dtype, chunk_len)
@@ -218,11 +223,12 @@ def scan_bwd(dy: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Te
              delta_bias: Optional[torch.Tensor] = None, softplus: bool = True, *,
              initial_state: Optional[torch.Tensor] = None, dlast_state: Optional[torch.Tensor] = None,
              want_initial_state_grad: bool = False, workspace: Optional[torch.Tensor] = None,
-             stream=None) -> dict:
+             out: Optional[dict] = None, stream=None) -> dict:
     """Gradients of the scan (ssm_scan_bwd) given dy (batch, L, dim) and optionally
     dlast_state (batch, dim, N).  The forward inputs are passed as to scan_fwd / scan_fwd_from.
     Returns a dict: du, ddelta, dz (if z), dA, dB, dC (float32), dD (if D), ddelta_bias
-    (if delta_bias), dinitial_state (if asked for)."""
+    (if delta_bias), dinitial_state (if asked for).  `out`: such a dict from an earlier call
+    with the same shapes, whose tensors are written again instead of new ones."""
     if u.dim() != 3:
         raise ValueError("u must be (batch, L, dim)")
     bsz, L, dim = u.shape
@@ -239,17 +245,11 @@ def scan_bwd(dy: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Te
                                (dlast_state, "dlast_state", (bsz, dim, N), torch.float32)):
         if t is not None:
             _need(t, name, shape, dt, dev)
-    f32 = dict(dtype=torch.float32, device=dev)
-    g = dict(du=torch.empty((bsz, L, dim), dtype=io, device=dev), ddelta=torch.empty((bsz, L, dim), dtype=io, device=dev),
-             dA=torch.empty((dim, N), **f32), dB=torch.empty((bsz, L, N), **f32), dC=torch.empty((bsz, L, N), **f32))
-    if z is not None:
-        g["dz"] = torch.empty((bsz, L, dim), dtype=io, device=dev)
-    if D is not None:
-        g["dD"] = torch.empty((dim,), **f32)
-    if delta_bias is not None:
-        g["ddelta_bias"] = torch.empty((dim,), **f32)
-    if want_initial_state_grad:
-        g["dinitial_state"] = torch.empty((bsz, dim, N), **f32)
+    if out is not None:
+        g = out
+    else:
+        g = _bwd_outputs(bsz, L, dim, N, io, dev, z is not None, D is not None, delta_bias is not None,
+                         want_initial_state_grad)
     dims = make_dims(bsz, L, dim, N, io)
     need = int(lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(dims)))
     if workspace is None:
@@ -261,6 +261,21 @@ def scan_bwd(dy: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Te
                           ctypes.byref(dims), _ptr(workspace), workspace.numel() * workspace.element_size(),
                           _stream_handle(stream))
     _check(rc)
+    return g
+
+
+def _bwd_outputs(bsz, L, dim, N, io, dev, gate, skip, bias, want_h0):
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(du=torch.empty((bsz, L, dim), dtype=io, device=dev), ddelta=torch.empty((bsz, L, dim), dtype=io, device=dev),
+             dA=torch.empty((dim, N), **f32), dB=torch.empty((bsz, L, N), **f32), dC=torch.empty((bsz, L, N), **f32))
+    if gate:
+        g["dz"] = torch.empty((bsz, L, dim), dtype=io, device=dev)
+    if skip:
+        g["dD"] = torch.empty((dim,), **f32)
+    if bias:
+        g["ddelta_bias"] = torch.empty((dim,), **f32)
+    if want_h0:
+        g["dinitial_state"] = torch.empty((bsz, dim, N), **f32)
     return g
 
 
