@@ -244,7 +244,7 @@ def main():
         def one(i):
             ssmscan.scan_bwd(dy, t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
                              delta_bias=t["bias"], softplus=case.softplus, workspace=ws, out=grads)
-        plan = "checkpoint pass (state every 16 tokens) + backward kernel"
+        plan = "checkpoint pass (state every 8 tokens) + backward kernel"
     else:
         t = {k: td(getattr(case, f)) for k, f in (("u", "u"), ("delta", "delta"), ("A", "A"), ("B", "B"),
                                                    ("C", "C"), ("D", "Dskip"), ("z", "z"), ("bias", "delta_bias"))}

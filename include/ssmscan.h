@@ -134,8 +134,8 @@ SSMSCAN_API int ssm_scan_fwd_from(const float *initial_state, const void *u, con
                       int softplus_flag, void *y, float *last_state, const ssm_dims *dims, void *workspace,
                       size_t workspace_bytes, void *stream);
 
-/* Bytes of device workspace ssm_scan_bwd needs: the checkpointed states, one per 16
- * tokens (batch * ceil(seqlen / 16) * dim * dstate fp32, 256-byte aligned).  Returns 0 for
+/* Bytes of device workspace ssm_scan_bwd needs: the checkpointed states, one per 8
+ * tokens (batch * ceil(seqlen / 8) * dim * dstate fp32, 256-byte aligned).  Returns 0 for
  * an invalid or empty problem. */
 SSMSCAN_API size_t ssm_scan_bwd_workspace_bytes(const ssm_dims *dims);
 

@@ -17,7 +17,8 @@
 // channel (as in the forward kernel).  A forward pass in checkpoint mode first stores the
 // state before every kBwdTile-th token.  This kernel then walks the tiles of kBwdTile
 // tokens from the last to the first; per tile it
-//   1. prepares (delta, delta*u, u, dp) per (token, channel) in LDS (all threads),
+//   1. prepares (delta, delta*u, u, dp) per (token, channel) and the tile's B and C rows
+//      (fp32) in LDS (all threads),
 //   2. recomputes the tile's states from its checkpoint into registers (the wave's S states
 //      x kBwdTile tokens) and the partial readouts p,
 //   3. walks the tile backwards, accumulating dA in registers, writing per-wave partial du
@@ -90,6 +91,7 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
     __shared__ float s_du[K][T][kChanTile];        // partial du, per wave
     __shared__ float s_dd[K][T][kChanTile];        // partial d delta, per wave
     __shared__ float s_red[K][NV][64];             // per-wave transposition for dB / dC
+    __shared__ float s_bc[T][2][N];                // the tile's B and C rows, widened to fp32
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -169,6 +171,12 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
                 ksg[p][v] = softplus ? sigmoid_f32(x) : 1.0f;
             }
         }
+        // the tile's B and C rows (shared by every channel) into LDS as fp32
+        for (int i = tid; i < T * 2 * N; i += 64 * K) {
+            const int tt = i / (2 * N), which = (i / N) % 2, n = i % N;
+            const int64_t o = (row0 + t0 + min(tt, nt - 1)) * N + n;
+            s_bc[tt][which][n] = io<IO>::ld(which ? Cm : Bm, o);
+        }
         __syncthreads();
 
         // 2. recompute the tile's states from its checkpoint
@@ -185,8 +193,11 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
                 if (tt < nt) {
                     const f32x4_t v = s_in[tt][lane];
                     float Bs[S], Cs[S];
-                    load_slice<S>(Bm, (row0 + t0 + tt) * N + w * S, Bs);
-                    load_slice<S>(Cm, (row0 + t0 + tt) * N + w * S, Cs);
+#pragma unroll
+                    for (int s = 0; s < S; ++s) {
+                        Bs[s] = s_bc[tt][0][w * S + s];
+                        Cs[s] = s_bc[tt][1][w * S + s];
+                    }
                     float acc = 0.0f;
 #pragma unroll
                     for (int s = 0; s < S; ++s) {
@@ -205,8 +216,11 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
             if (tt < nt) {
                 const f32x4_t v = s_in[tt][lane];   // (delta, delta*u, u, dp)
                 float Bs[S], Cs[S];
-                load_slice<S>(Bm, (row0 + t0 + tt) * N + w * S, Bs);
-                load_slice<S>(Cm, (row0 + t0 + tt) * N + w * S, Cs);
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    Bs[s] = s_bc[tt][0][w * S + s];
+                    Cs[s] = s_bc[tt][1][w * S + s];
+                }
                 float du_p = 0.0f, dd_p = 0.0f, rv[NV];
 #pragma unroll
                 for (int s = 0; s < S; ++s) {

@@ -32,7 +32,7 @@ constexpr int kChanTile = 64;    // channels per workgroup (one per lane)
 enum ScanMode { kFull = 0, kSummary = 1, kCheckpoint = 2 };
 
 // kCheckpoint stores the state before every kCkptEvery-th token (for the backward pass).
-constexpr int kCkptEvery = 16;
+constexpr int kCkptEvery = 8;
 
 // s_waitcnt immediate that waits for all LDS and scalar-memory operations (lgkmcnt = 0) and
 // leaves the vector-memory and export counters unconstrained (gfx9 encoding).

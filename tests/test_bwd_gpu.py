@@ -84,7 +84,7 @@ def check_grads(case, got, ref, label=""):
 @pytest.mark.parametrize("D", [70, 128])   # element-wise and vector access
 def test_bwd_small(oracle_mod, io, N, D):
     """Every gradient, all optional inputs present, ragged length (not a multiple of the
-    16-token tile or the 32-token forward tile)."""
+    8-token tile or the 32-token forward tile)."""
     case = inputs.scan_case(2, 100, D, N, io, gate=True, seed=80 + N)
     got, ref = run_both(oracle_mod, case, seed=81)
     check_grads(case, got, ref, f"D={D}")
@@ -104,7 +104,7 @@ def test_bwd_optional_inputs(oracle_mod, variant):
 
 
 def test_bwd_many_tiles(oracle_mod):
-    """B2 L2048 D256 N16 bf16 with gate: 128 tiles of 16 tokens, 8 channel tiles; every
+    """B2 L2048 D256 N16 bf16 with gate: 256 tiles of 8 tokens, 8 channel tiles; every
     gradient over the whole problem."""
     case = inputs.scan_case(2, 2048, 256, 16, "bf16", gate=True, seed=84)
     got, ref = run_both(oracle_mod, case, seed=85)
