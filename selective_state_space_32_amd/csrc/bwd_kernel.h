@@ -19,11 +19,12 @@
 // tokens from the last to the first; per tile it
 //   1. prepares (delta, delta*u, u, dp) per (token, channel) and the tile's B and C rows
 //      (fp32) in LDS (all threads),
-//   2. recomputes the tile's states from its checkpoint into registers (the wave's S states
-//      x kBwdTile tokens) and the partial readouts p,
+//   2. recomputes the tile's states and exp(delta A) from its checkpoint into registers
+//      (the wave's S states x kBwdTile tokens) and the partial readouts p,
 //   3. walks the tile backwards, accumulating dA in registers, writing per-wave partial du
 //      and d delta to LDS, and summing the dB / dC contributions of the tile's 64 channels
-//      through a wave-private LDS transposition, added to global memory atomically,
+//      through a wave-private LDS transposition, added to global memory atomically (the
+//      transposition of one token overlaps the arithmetic of the next),
 //   4. finishes du, d delta, dz and the dD / d delta_bias sums per element (all threads).
 // dA, dB, dC, dD and d delta_bias are sums over workgroups and are accumulated with atomic
 // adds into buffers the host has zeroed; their summation order is not fixed.
@@ -56,15 +57,20 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
-// Orders this wave's LDS accesses around an exchange between its lanes: the compiler may
-// not move memory accesses across it, and it waits until earlier LDS operations are done.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    asm volatile("" ::: "memory");
+// Orders this wave's LDS accesses around an exchange between its lanes.  A wavefront's
+// own LDS operations are performed in the order it issues them, so no wait is needed:
+// the fences only keep the compiler from moving memory accesses across this point.
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Register budget: with 4 waves per workgroup three workgroups share a CU (LDS allows it),
+// which needs at most 168 VGPRs per lane.
 template <int N, typename IO, bool VEC>
 __global__ void __launch_bounds__(64 * BwdShape<N>::K)
+__attribute__((amdgpu_waves_per_eu(BwdShape<N>::K == 4 ? 3 : 1)))
 scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO *__restrict__ z,
                 const IO *__restrict__ dy, const float *__restrict__ A, const float *__restrict__ Dv,
                 const float *__restrict__ bias, const IO *__restrict__ Bm, const IO *__restrict__ Cm,
@@ -86,12 +92,17 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
     using VIO = vec<V, IO>;
     constexpr int W = VEC ? V * (int)sizeof(IO) / 4 : 1;
 
-    __shared__ f32x4_t s_in[T][kChanTile];         // (delta, delta*u, u, dp) per (token, channel)
+    __shared__ f32x2_t s_dk[T][kChanTile];         // (delta, delta*u) per (token, channel)
+    __shared__ f32x2_t s_ud[T][kChanTile];         // (u, dp)
     __shared__ float s_p[K][T][kChanTile];         // partial readouts, per wave
     __shared__ float s_du[K][T][kChanTile];        // partial du, per wave
     __shared__ float s_dd[K][T][kChanTile];        // partial d delta, per wave
-    __shared__ float s_red[K][NV][64];             // per-wave transposition for dB / dC
+    // per-wave transposition for dB / dC (2 buffers); rows padded by 4 words so that the 8
+    // lanes reading the same offsets of different rows fall in different banks
+    __shared__ float s_red[K][2][NV][64 + 4];
     __shared__ float s_bc[T][2][N];                // the tile's B and C rows, widened to fp32
+    __shared__ float s_dbc[T][2][N];               // the tile's dB / dC sums over its 64 channels
+    static_assert(T * 2 * N <= 64 * K, "one B / C element per thread");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -109,11 +120,10 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
     const bool gated = z != nullptr;
     const int64_t n_ckpt = (L + kCkptEvery - 1) / kCkptEvery;
 
-    float a2[S], Aw[S], G[S], dA_acc[S];
+    float a2[S], G[S], dA_acc[S];   // a2 = A log2(e)
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        Aw[s] = act ? A[d * N + w * S + s] : 0.0f;
-        a2[s] = Aw[s] * kLog2e;
+        a2[s] = act ? A[d * N + w * S + s] * kLog2e : 0.0f;
         G[s] = (act && dlast) ? dlast[((int64_t)b * D + d) * N + w * S + s] : 0.0f;
         dA_acc[s] = 0.0f;
     }
@@ -126,15 +136,18 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
         dD_acc[v] = 0.0f;
         db_acc[v] = 0.0f;
     }
-    auto ld = [&](const IO *p, int64_t idx, float (&out)[V]) {
-        if constexpr (VEC) {
-            uint32_t wd[W];
-            VIO::load(p, idx, wd);
-#pragma unroll
-            for (int v = 0; v < V; ++v) out[v] = VIO::get(wd, v);
-        } else {
-            out[0] = io<IO>::ld(p, idx);
-        }
+    // The next tile's inputs are fetched into registers as raw I/O words while the current
+    // tile is processed, and widened to fp32 only when they are used.
+    struct Raw { uint32_t w[W]; };
+    auto fetch_raw = [&](const IO *p, int64_t idx, Raw &r) {
+        if constexpr (VEC) VIO::load(p, idx, r.w);
+        else if constexpr (sizeof(IO) == 2) r.w[0] = p[idx];
+        else r.w[0] = __float_as_uint(p[idx]);
+    };
+    auto widen = [&](const Raw &r, int v) -> float {
+        if constexpr (VEC) return VIO::get(r.w, v);
+        else if constexpr (sizeof(IO) == 2) return bf16_to_f32((uint16_t)r.w[0]);
+        else return __uint_as_float(r.w[0]);
     };
     auto st = [&](IO *p, int64_t idx, const float (&val)[V]) {
         if constexpr (VEC) VIO::store(p, idx, val);
@@ -142,122 +155,143 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
     };
 
     const int n_tiles = (int)((L + T - 1) / T);
+    const int rk = lane / LPV, rgrp = lane % LPV;   // the dB / dC entry this lane sums
+    Raw ru[P], rx[P], ry[P], rz[P];
+    uint32_t rbc = 0;
+    float hn[S];
+    auto fetch = [&](int jj) {   // tile jj's inputs, its B / C rows and its checkpoint
+        const int64_t tb = (int64_t)jj * T;
+        const int ntj = (int)min((int64_t)T, L - tb);
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int64_t idx = (row0 + tb + min(p * RPP + rsub, ntj - 1)) * D + dq;   // clamped in bounds
+            fetch_raw(u, idx, ru[p]);
+            fetch_raw(delta, idx, rx[p]);
+            fetch_raw(dy, idx, ry[p]);
+            if (gated) fetch_raw(z, idx, rz[p]);
+        }
+        if (tid < T * 2 * N) {
+            const int tt = tid / (2 * N), which = (tid / N) % 2, n = tid % N;
+            const IO *src = which ? Cm : Bm;
+            const int64_t o = (row0 + tb + min(tt, ntj - 1)) * N + n;
+            if constexpr (sizeof(IO) == 2) rbc = src[o];
+            else rbc = __float_as_uint(src[o]);
+        }
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+            hn[s] = act ? ckpt[(((int64_t)b * n_ckpt + jj) * D + d) * N + w * S + s] : 0.0f;
+    };
+    fetch(n_tiles - 1);
     for (int j = n_tiles - 1; j >= 0; --j) {
         const int64_t t0 = (int64_t)j * T;
         const int nt = (int)min((int64_t)T, L - t0);
 
-        // 1. per-element preparation; the values the epilogue needs stay in registers
-        float ku[P][V], kdp[P][V], kdy[P][V], kz[P][V], ksg[P][V];
+        // 1. per-element preparation; the values the epilogue needs stay in registers.
+        // Tokens past the end and channels past D get zeros: a step with delta = 0,
+        // delta*u = 0 and dp = 0 leaves the state and the adjoint unchanged and contributes
+        // nothing to any sum, so the tile is processed whole.
+        float kdy[P][V], kz[P][V], ksg[P][V];   // u and dp are read back from LDS
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             const int tt = p * RPP + rsub;
-            const int64_t idx = (row0 + t0 + min(tt, nt - 1)) * D + dq;   // clamped in bounds
-            float uu[V], xx[V], yy[V], zz[V];
-            ld(u, idx, uu);
-            ld(delta, idx, xx);
-            ld(dy, idx, yy);
-            if (gated) ld(z, idx, zz);
 #pragma unroll
             for (int v = 0; v < V; ++v) {
-                const float x = xx[v] + bq[v];
-                const float dl = softplus ? softplus_f32(x) : x;
-                const float g = gated ? silu_f32(zz[v]) : 1.0f;
-                const float dp = yy[v] * g;
-                s_in[tt][cq + v] = f32x4_t{dl, dl * uu[v], uu[v], dp};
-                ku[p][v] = uu[v];
-                kdp[p][v] = dp;
-                kdy[p][v] = yy[v];
-                kz[p][v] = gated ? zz[v] : 0.0f;
+                const float uu = widen(ru[p], v), yy = widen(ry[p], v);
+                const float zz = gated ? widen(rz[p], v) : 0.0f;
+                const bool live = tt < nt && qact && (VEC || d0 + cq + v < D);
+                const float x = widen(rx[p], v) + bq[v];
+                const float dl = live ? (softplus ? softplus_f32(x) : x) : 0.0f;
+                const float g = gated ? silu_f32(zz) : 1.0f;
+                const float dp = live ? yy * g : 0.0f;
+                s_dk[tt][cq + v] = f32x2_t{dl, dl * uu};
+                s_ud[tt][cq + v] = f32x2_t{uu, dp};
+                kdy[p][v] = yy;
+                kz[p][v] = zz;
                 ksg[p][v] = softplus ? sigmoid_f32(x) : 1.0f;
             }
         }
         // the tile's B and C rows (shared by every channel) into LDS as fp32
-        for (int i = tid; i < T * 2 * N; i += 64 * K) {
-            const int tt = i / (2 * N), which = (i / N) % 2, n = i % N;
-            const int64_t o = (row0 + t0 + min(tt, nt - 1)) * N + n;
-            s_bc[tt][which][n] = io<IO>::ld(which ? Cm : Bm, o);
+        if (tid < T * 2 * N) {
+            const float bcv = sizeof(IO) == 2 ? bf16_to_f32((uint16_t)rbc) : __uint_as_float(rbc);
+            s_bc[tid / (2 * N)][(tid / N) % 2][tid % N] = bcv;
         }
+        float hs[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) hs[s] = hn[s];
+        if (j > 0) fetch(j - 1);
         __syncthreads();
 
-        // 2. recompute the tile's states from its checkpoint
-        float hs[S], hist[T][S];
-#pragma unroll
-        for (int s = 0; s < S; ++s)
-            hs[s] = act ? ckpt[(((int64_t)b * n_ckpt + j) * D + d) * N + w * S + s] : 0.0f;
+        // 2. recompute the tile's states from its checkpoint, keeping h_t and exp(delta_t A)
+        float hist[T][S], ex[T][S];
         {
             float h[S];
 #pragma unroll
             for (int s = 0; s < S; ++s) h[s] = hs[s];
 #pragma unroll
             for (int tt = 0; tt < T; ++tt) {
-                if (tt < nt) {
-                    const f32x4_t v = s_in[tt][lane];
-                    float Bs[S], Cs[S];
+                const f32x2_t v = s_dk[tt][lane];
+                float acc = 0.0f;
 #pragma unroll
-                    for (int s = 0; s < S; ++s) {
-                        Bs[s] = s_bc[tt][0][w * S + s];
-                        Cs[s] = s_bc[tt][1][w * S + s];
-                    }
-                    float acc = 0.0f;
-#pragma unroll
-                    for (int s = 0; s < S; ++s) {
-                        h[s] = fmaf(hw_exp2(v.x * a2[s]), h[s], v.y * Bs[s]);
-                        hist[tt][s] = h[s];
-                        acc = fmaf(Cs[s], h[s], acc);
-                    }
-                    s_p[w][tt][lane] = acc;
+                for (int s = 0; s < S; ++s) {
+                    ex[tt][s] = hw_exp2(v.x * a2[s]);
+                    h[s] = fmaf(ex[tt][s], h[s], v.y * s_bc[tt][0][w * S + s]);
+                    hist[tt][s] = h[s];
+                    acc = fmaf(s_bc[tt][1][w * S + s], h[s], acc);
                 }
+                s_p[w][tt][lane] = acc;
             }
         }
 
-        // 3. walk the tile backwards
+        // 3. walk the tile backwards.  With lambda = C dp + G and r = exp(delta A) lambda
+        // h_{t-1} (= the new G times h_{t-1}):
+        //   dA += delta r,   d delta = sum_n A r + u q,   du = delta q,   q = sum_n lambda B,
+        //   dB = lambda delta u,   dC = dp h_t.
+        // The dB / dC sums over the wave's 64 channels go through LDS; each token's sums are
+        // read back while the next (earlier) token is computed and finished after it.
+        float pr[NV];
+        auto finish = [&](int tt) {   // complete the channel sums of token tt, add them out
+            float part = pr[0];
+#pragma unroll
+            for (int i = 1; i < NV; ++i) part += pr[i];
+            part = group_sum<LPV>(part);
+            if (rgrp == LPV - 1) s_dbc[tt][rk < S ? 0 : 1][w * S + rk % S] = part;
+        };
 #pragma unroll
         for (int tt = T - 1; tt >= 0; --tt) {
-            if (tt < nt) {
-                const f32x4_t v = s_in[tt][lane];   // (delta, delta*u, u, dp)
-                float Bs[S], Cs[S];
+            const f32x2_t dk = s_dk[tt][lane];   // (delta, delta*u)
+            const f32x2_t ud = s_ud[tt][lane];   // (u, dp)
+            float q = 0.0f, ddA = 0.0f, rv[NV];   // ddA = sum_n A r / ln 2
 #pragma unroll
-                for (int s = 0; s < S; ++s) {
-                    Bs[s] = s_bc[tt][0][w * S + s];
-                    Cs[s] = s_bc[tt][1][w * S + s];
-                }
-                float du_p = 0.0f, dd_p = 0.0f, rv[NV];
-#pragma unroll
-                for (int s = 0; s < S; ++s) {
-                    const float lam = fmaf(Cs[s], v.w, G[s]);
-                    const float hprev = tt > 0 ? hist[tt > 0 ? tt - 1 : 0][s] : hs[s];
-                    const float e = hw_exp2(v.x * a2[s]);
-                    const float ah = e * hprev;
-                    const float lamd = lam * v.x;
-                    dA_acc[s] = fmaf(lamd, ah, dA_acc[s]);
-                    dd_p = fmaf(lam, fmaf(Aw[s], ah, Bs[s] * v.z), dd_p);
-                    du_p = fmaf(lamd, Bs[s], du_p);
-                    rv[s] = act ? lamd * v.z : 0.0f;            // dB contribution
-                    rv[S + s] = act ? v.w * hist[tt][s] : 0.0f;  // dC contribution
-                    G[s] = e * lam;
-                }
-                s_du[w][tt][lane] = du_p;
-                s_dd[w][tt][lane] = dd_p;
-                // sum rv over the 64 channels: transpose through LDS, each lane adds NV
-                // entries of one value, then LPV lanes combine with DPP
-#pragma unroll
-                for (int k = 0; k < NV; ++k) s_red[w][k][lane] = rv[k];
-                wave_lds_sync();
-                const int k = lane / LPV, grp = lane % LPV;
-                float part = 0.0f;
-#pragma unroll
-                for (int i = 0; i < NV; ++i) part += s_red[w][k][grp * NV + i];
-                wave_lds_sync();
-                part = group_sum<LPV>(part);
-                if (grp == LPV - 1) {
-                    const int64_t o = (row0 + t0 + tt) * N + w * S + (k % S);
-                    unsafeAtomicAdd(k < S ? dB + o : dC + o, part);
-                }
+            for (int s = 0; s < S; ++s) {
+                const float lam = fmaf(s_bc[tt][1][w * S + s], ud.y, G[s]);
+                G[s] = ex[tt][s] * lam;
+                const float r = G[s] * (tt > 0 ? hist[tt > 0 ? tt - 1 : 0][s] : hs[s]);
+                dA_acc[s] = fmaf(dk.x, r, dA_acc[s]);
+                ddA = fmaf(a2[s], r, ddA);
+                q = fmaf(lam, s_bc[tt][0][w * S + s], q);
+                rv[s] = lam * dk.y;                  // dB contribution
+                rv[S + s] = ud.y * hist[tt][s];      // dC contribution
             }
+            s_du[w][tt][lane] = dk.x * q;
+            s_dd[w][tt][lane] = fmaf(ud.x, q, ddA * kLn2);
+            if (tt < T - 1) finish(tt + 1);
+            // transpose: lane l writes its NV values; lane rgrp*NV+i of value rk is read back
+#pragma unroll
+            for (int k = 0; k < NV; ++k) s_red[w][tt & 1][k][lane] = rv[k];
+            wave_lds_fence();
+#pragma unroll
+            for (int i = 0; i < NV; ++i) pr[i] = s_red[w][tt & 1][rk][rgrp * NV + i];
+            wave_lds_fence();
         }
+        finish(0);
         __syncthreads();
 
-        // 4. finish the per-element gradients
+        // 4. add the tile's dB / dC sums out (one element per thread), finish the
+        // per-element gradients
+        if (tid < T * 2 * N) {
+            const int tt = tid / (2 * N), which = (tid / N) % 2, n = tid % N;
+            if (tt < nt) unsafeAtomicAdd((which ? dC : dB) + (row0 + t0 + tt) * N + n, s_dbc[tt][which][n]);
+        }
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             const int tt = p * RPP + rsub;
@@ -266,8 +300,9 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
 #pragma unroll
                 for (int v = 0; v < V; ++v) {
                     const int c = cq + v;
-                    float pp = fmaf(Dq[v], ku[p][v], s_p[0][tt][c]);
-                    float gu = fmaf(Dq[v], kdp[p][v], s_du[0][tt][c]);
+                    const f32x2_t ud = s_ud[tt][c];   // (u, dp)
+                    float pp = fmaf(Dq[v], ud.x, s_p[0][tt][c]);
+                    float gu = fmaf(Dq[v], ud.y, s_du[0][tt][c]);
                     float gd = s_dd[0][tt][c];
 #pragma unroll
                     for (int kk = 1; kk < K; ++kk) {
@@ -284,7 +319,7 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
                     }
                     const bool ok = VEC || d0 + c < D;
                     if (ok) {
-                        dD_acc[v] = fmaf(kdp[p][v], ku[p][v], dD_acc[v]);
+                        dD_acc[v] = fmaf(ud.y, ud.x, dD_acc[v]);
                         db_acc[v] += gx;
                     }
                 }
