@@ -97,9 +97,9 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
     __shared__ float s_p[K][T][kChanTile];         // partial readouts, per wave
     __shared__ float s_du[K][T][kChanTile];        // partial du, per wave
     __shared__ float s_dd[K][T][kChanTile];        // partial d delta, per wave
-    // per-wave transposition for dB / dC (2 buffers); rows padded by 4 words so that the 8
-    // lanes reading the same offsets of different rows fall in different banks
-    __shared__ float s_red[K][2][NV][64 + 4];
+    // per-wave transposition for dB / dC.  Lane (rk, rgrp) sums row rk at columns rgrp +
+    // LPV i; rows are 72 words apart, so each group of 32 lanes reads 32 distinct banks.
+    __shared__ float s_red[K][NV][64 + 8];
     __shared__ float s_bc[T][2][N];                // the tile's B and C rows, widened to fp32
     __shared__ float s_dbc[T][2][N];               // the tile's dB / dC sums over its 64 channels
     static_assert(T * 2 * N <= 64 * K, "one B / C element per thread");
@@ -186,28 +186,35 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
         const int64_t t0 = (int64_t)j * T;
         const int nt = (int)min((int64_t)T, L - t0);
 
-        // 1. per-element preparation; the values the epilogue needs stay in registers.
-        // Tokens past the end and channels past D get zeros: a step with delta = 0,
-        // delta*u = 0 and dp = 0 leaves the state and the adjoint unchanged and contributes
-        // nothing to any sum, so the tile is processed whole.
-        float kdy[P][V], kz[P][V], ksg[P][V];   // u and dp are read back from LDS
+        // 1. per-element preparation.  Tokens past the end and channels past D get zeros: a
+        // step with delta = 0, delta*u = 0 and dp = 0 leaves the state and the adjoint
+        // unchanged and contributes nothing to any sum, so the tile is processed whole.
+        // Kept in registers for the epilogue: kgz = dy silu'(z) (so dz = kgz p) and
+        // ksg = softplus'(x); u and dp are read back from LDS.
+        float kgz[P][V], ksg[P][V];
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             const int tt = p * RPP + rsub;
 #pragma unroll
             for (int v = 0; v < V; ++v) {
                 const float uu = widen(ru[p], v), yy = widen(ry[p], v);
-                const float zz = gated ? widen(rz[p], v) : 0.0f;
                 const bool live = tt < nt && qact && (VEC || d0 + cq + v < D);
                 const float x = widen(rx[p], v) + bq[v];
-                const float dl = live ? (softplus ? softplus_f32(x) : x) : 0.0f;
-                const float g = gated ? silu_f32(zz) : 1.0f;
+                float sg = 1.0f;
+                const float sp = softplus ? softplus_f32(x, sg) : x;
+                const float dl = live ? sp : 0.0f;
+                float g = 1.0f, gz = 0.0f;
+                if (gated) {   // silu(z) = z sigmoid(z), silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z)))
+                    const float zz = widen(rz[p], v);
+                    const float sz = sigmoid_f32(zz);
+                    g = zz * sz;
+                    gz = yy * (sz * fmaf(zz, 1.0f - sz, 1.0f));
+                }
                 const float dp = live ? yy * g : 0.0f;
                 s_dk[tt][cq + v] = f32x2_t{dl, dl * uu};
                 s_ud[tt][cq + v] = f32x2_t{uu, dp};
-                kdy[p][v] = yy;
-                kz[p][v] = zz;
-                ksg[p][v] = softplus ? sigmoid_f32(x) : 1.0f;
+                kgz[p][v] = gz;
+                ksg[p][v] = sg;
             }
         }
         // the tile's B and C rows (shared by every channel) into LDS as fp32
@@ -246,43 +253,54 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
         // h_{t-1} (= the new G times h_{t-1}):
         //   dA += delta r,   d delta = sum_n A r + u q,   du = delta q,   q = sum_n lambda B,
         //   dB = lambda delta u,   dC = dp h_t.
-        // The dB / dC sums over the wave's 64 channels go through LDS; each token's sums are
-        // read back while the next (earlier) token is computed and finished after it.
-        float pr[NV];
-        auto finish = [&](int tt) {   // complete the channel sums of token tt, add them out
-            float part = pr[0];
+        // The dB / dC sums over the wave's 64 channels go through LDS: a token's values are
+        // transposed at the start of the next (earlier) token's step, after that token's
+        // inputs are requested, and summed at its end.
+        float pr[NV], rvp[NV];
+        auto transpose = [&]() {   // rvp -> pr: lane (rk, rgrp) gets row rk at columns rgrp + LPV i
 #pragma unroll
-            for (int i = 1; i < NV; ++i) part += pr[i];
-            part = group_sum<LPV>(part);
+            for (int k = 0; k < NV; ++k) s_red[w][k][lane] = rvp[k];
+            wave_lds_fence();
+#pragma unroll
+            for (int i = 0; i < NV; ++i) pr[i] = s_red[w][rk][rgrp + LPV * i];
+            wave_lds_fence();
+        };
+        auto finish = [&](int tt) {   // complete the channel sums of token tt
+#pragma unroll
+            for (int m = 1; m < NV; m *= 2)
+#pragma unroll
+                for (int i = 0; i + m < NV; i += 2 * m) pr[i] += pr[i + m];
+            const float part = group_sum<LPV>(pr[0]);
             if (rgrp == LPV - 1) s_dbc[tt][rk < S ? 0 : 1][w * S + rk % S] = part;
         };
 #pragma unroll
         for (int tt = T - 1; tt >= 0; --tt) {
             const f32x2_t dk = s_dk[tt][lane];   // (delta, delta*u)
             const f32x2_t ud = s_ud[tt][lane];   // (u, dp)
-            float q = 0.0f, ddA = 0.0f, rv[NV];   // ddA = sum_n A r / ln 2
+            float Bs[S], Cs[S];
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                const float lam = fmaf(s_bc[tt][1][w * S + s], ud.y, G[s]);
+                Bs[s] = s_bc[tt][0][w * S + s];
+                Cs[s] = s_bc[tt][1][w * S + s];
+            }
+            if (tt < T - 1) transpose();
+            float q = 0.0f, ddA = 0.0f;   // ddA = sum_n A r / ln 2
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const float lam = fmaf(Cs[s], ud.y, G[s]);
                 G[s] = ex[tt][s] * lam;
                 const float r = G[s] * (tt > 0 ? hist[tt > 0 ? tt - 1 : 0][s] : hs[s]);
                 dA_acc[s] = fmaf(dk.x, r, dA_acc[s]);
                 ddA = fmaf(a2[s], r, ddA);
-                q = fmaf(lam, s_bc[tt][0][w * S + s], q);
-                rv[s] = lam * dk.y;                  // dB contribution
-                rv[S + s] = ud.y * hist[tt][s];      // dC contribution
+                q = fmaf(lam, Bs[s], q);
+                rvp[s] = lam * dk.y;                 // dB contribution
+                rvp[S + s] = ud.y * hist[tt][s];     // dC contribution
             }
             s_du[w][tt][lane] = dk.x * q;
             s_dd[w][tt][lane] = fmaf(ud.x, q, ddA * kLn2);
             if (tt < T - 1) finish(tt + 1);
-            // transpose: lane l writes its NV values; lane rgrp*NV+i of value rk is read back
-#pragma unroll
-            for (int k = 0; k < NV; ++k) s_red[w][tt & 1][k][lane] = rv[k];
-            wave_lds_fence();
-#pragma unroll
-            for (int i = 0; i < NV; ++i) pr[i] = s_red[w][tt & 1][rk][rgrp * NV + i];
-            wave_lds_fence();
         }
+        transpose();
         finish(0);
         __syncthreads();
 
@@ -313,10 +331,7 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
                     const float gx = gd * ksg[p][v];
                     o_du[v] = gu;
                     o_dd[v] = gx;
-                    if (gated) {
-                        const float sz = sigmoid_f32(kz[p][v]);
-                        o_dz[v] = kdy[p][v] * pp * (sz * fmaf(kz[p][v], 1.0f - sz, 1.0f));
-                    }
+                    if (gated) o_dz[v] = pp * kgz[p][v];
                     const bool ok = VEC || d0 + c < D;
                     if (ok) {
                         dD_acc[v] = fmaf(ud.y, ud.x, dD_acc[v]);

@@ -108,12 +108,19 @@ template <int V, typename IO> struct vec {
 // max(x, 0) + f is formed as max(x + f, f), the same value for f >= 0 (for x <= 0 the
 // rounded x + f cannot exceed f), in two instructions: both operands are arithmetic results,
 // so the maximum needs no NaN-quieting step.  A NaN x makes f NaN and the result NaN.
-__device__ __forceinline__ float softplus_f32(float x) {
+// The derivative sigmoid(x) = e^x / (1 + e^x) comes from the same e: 1 / w for x >= 0 and
+// e / w for x < 0.
+__device__ __forceinline__ float softplus_f32(float x, float &sig) {
     const float e = hw_exp2(-fabsf(x) * kLog2e);
     const float w = 1.0f + e;
     const float r = e - (w - 1.0f);
     const float f = fmaf(hw_log2(w), kLn2, r);
+    sig = (x >= 0.0f ? 1.0f : e) * hw_rcp(w);
     return fmaxf(x + f, f);
+}
+__device__ __forceinline__ float softplus_f32(float x) {
+    float sig;
+    return softplus_f32(x, sig);
 }
 
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z).  For z << 0, e^-z = inf and the result is -0.
