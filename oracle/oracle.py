@@ -76,8 +76,9 @@ def default_threads() -> int:
 
 
 def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
-         threads: Optional[int] = None, h0=None) -> Tuple[np.ndarray, np.ndarray]:
+         threads: Optional[int] = None, h0=None, exact_zoh: bool = False) -> Tuple[np.ndarray, np.ndarray]:
     """fp64 selective scan from h = 0, or from the state h0 (bsz, Dch, N) if given.
+    exact_zoh: input term (exp(delta A) - 1) / A * B * u instead of delta * B * u.
 
     u, delta, z: (bsz, L, Dch); B, C: (bsz, L, N); A: (Dch, N); D, delta_bias: (Dch,).
     Returns (y (bsz, L, Dch), last_state (bsz, Dch, N)), both float64.
@@ -97,7 +98,8 @@ def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = Tr
     last = np.empty((bsz, Dch, N), dtype=np.float64)
     h0 = _f64(h0, (bsz, Dch, N))
     rc = _load().ssm_oracle_scan_from(bsz, L, Dch, N, _ptr(h0), _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
-                                      _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), int(bool(softplus)),
+                                      _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                      int(bool(softplus)) | (2 if exact_zoh else 0),
                                       _ptr(y), _ptr(last), int(threads or default_threads()))
     if rc != 0:
         raise ValueError("oracle scan rejected N=%d" % N)
@@ -159,13 +161,13 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus: b
     return out
 
 
-def scan_case(case, channels=None, threads: Optional[int] = None, h0=None):
+def scan_case(case, channels=None, threads: Optional[int] = None, h0=None, exact_zoh: bool = False):
     """Run the oracle on a generated ScanCase (from the package's input module).
 
     channels: optional index array of channels d to evaluate (all batches); the oracle
     then runs on those channel columns only -- channels are independent, so each
     sampled output is exactly the full-problem value.  h0: optional initial state
-    (bsz, Dch, N) of the whole problem.
+    (bsz, Dch, N) of the whole problem.  exact_zoh: the exact zero-order-hold input term.
     Returns (y, last_state) restricted to the sampled channels.
     """
     sel = slice(None) if channels is None else np.asarray(channels)
@@ -179,4 +181,4 @@ def scan_case(case, channels=None, threads: Optional[int] = None, h0=None):
     if h0 is not None:
         h0 = np.asarray(h0)[:, sel]
     return scan(u, dl, A, case.values("B"), case.values("C"), D=D, z=z, delta_bias=bias,
-                softplus=case.softplus, threads=threads, h0=h0)
+                softplus=case.softplus, threads=threads, h0=h0, exact_zoh=exact_zoh)

@@ -11,7 +11,9 @@
  *  - discretisation: ZOH for the state matrix, dA = exp(delta * A), exact for a diagonal A
  *      (yapayzekasozluk.tr "Temel Matematiksel Cerceve" names ZOH / A_bar, B_bar);
  *    the input term is taken in its simplified form delta * B_t * u_t (the pages give no
- *    B_bar formula)
+ *    B_bar formula); with the exact-ZOH flag it is B_bar = (exp(delta A) - 1) / A * B, the
+ *    zero-order hold of the same diagonal system (delta * B in the limit A = 0), under
+ *    which Theorem 1's gated recurrence holds exactly (azimuth.plus/paper/mamba, Theorem 1)
  *  - selection: B_t, C_t and delta_t vary per token, delta_t = softplus(linear(x_t)),
  *    A stays fixed (azimuth.plus/paper/mamba, "selection" section, the three bullets and
  *    the remark that A alone stays fixed)
@@ -47,6 +49,14 @@ static double oracle_softplus(double x) {
 }
 
 /* silu(z) = z * sigmoid(z) = z / (1 + e^-z). */
+/* Bits of `flags`: the step size is softplus(delta + bias); the input term uses the
+ * exact zero-order-hold B_bar. */
+#define ORACLE_SOFTPLUS 1
+#define ORACLE_EXACT_ZOH 2
+
+/* B_bar / B for one state under exact ZOH: (exp(dt a) - 1) / a, and dt when a = 0. */
+static double oracle_zoh_coef(double dt, double a) { return a != 0.0 ? expm1(dt * a) / a : dt; }
+
 static double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
 
 /* sigmoid(x) = 1 / (1 + e^-x), written so that e^x is only taken of x <= 0. */
@@ -62,15 +72,18 @@ static double oracle_sigmoid(double x) {
  *   u, delta, z, y : [bsz][L][D]      B, C : [bsz][L][N]
  *   A : [D][N]     Dv, delta_bias : [D]   (Dv, z, delta_bias may be NULL)
  *   h0, last_state : [bsz][D][N] or NULL (h0 NULL: start from zero)
+ *   flags: ORACLE_SOFTPLUS | ORACLE_EXACT_ZOH
  * Channels (b, d) are independent; they are spread over `nthreads` OpenMP threads,
  * each walking its channel's tokens in order.  Returns 0, or -1 if N is too large.
  */
 int ssm_oracle_scan_from(int64_t bsz, int64_t L, int64_t D, int64_t N, const double *h0,
                          const double *u, const double *delta, const double *A,
                          const double *B, const double *C, const double *Dv,
-                         const double *z, const double *delta_bias, int softplus_flag,
+                         const double *z, const double *delta_bias, int flags,
                          double *y, double *last_state, int nthreads) {
     if (N > ORACLE_MAX_N || N < 1) return -1;
+    const int softplus_flag = flags & ORACLE_SOFTPLUS;
+    const int zoh = flags & ORACLE_EXACT_ZOH;
     int64_t nch = bsz * D;
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
     for (int64_t ch = 0; ch < nch; ++ch) {
@@ -85,9 +98,16 @@ int ssm_oracle_scan_from(int64_t bsz, int64_t L, int64_t D, int64_t N, const dou
             if (delta_bias) x = x + delta_bias[d];
             double dt = softplus_flag ? oracle_softplus(x) : x;
             double ut = u[i];
-            for (int64_t n = 0; n < N; ++n) {
-                double dA = exp(dt * A[d * N + n]);
-                h[n] = dA * h[n] + dt * Bt[n] * ut;
+            if (zoh) {
+                for (int64_t n = 0; n < N; ++n) {
+                    double a = A[d * N + n];
+                    h[n] = exp(dt * a) * h[n] + oracle_zoh_coef(dt, a) * Bt[n] * ut;
+                }
+            } else {
+                for (int64_t n = 0; n < N; ++n) {
+                    double dA = exp(dt * A[d * N + n]);
+                    h[n] = dA * h[n] + dt * Bt[n] * ut;
+                }
             }
             double acc = 0.0;
             for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];
@@ -106,9 +126,9 @@ int ssm_oracle_scan_from(int64_t bsz, int64_t L, int64_t D, int64_t N, const dou
 int ssm_oracle_scan(int64_t bsz, int64_t L, int64_t D, int64_t N,
                     const double *u, const double *delta, const double *A,
                     const double *B, const double *C, const double *Dv,
-                    const double *z, const double *delta_bias, int softplus_flag,
+                    const double *z, const double *delta_bias, int flags,
                     double *y, double *last_state, int nthreads) {
-    return ssm_oracle_scan_from(bsz, L, D, N, NULL, u, delta, A, B, C, Dv, z, delta_bias, softplus_flag,
+    return ssm_oracle_scan_from(bsz, L, D, N, NULL, u, delta, A, B, C, Dv, z, delta_bias, flags,
                                 y, last_state, nthreads);
 }
 
@@ -160,7 +180,8 @@ int ssm_oracle_step(int64_t S, int64_t D, int64_t N, double *state,
  *   dD      += dp_t u_t,  ddelta_bias += ddelta_t,  dz_t = dy_t p_t silu'(z_t)
  *   dh0      = the adjoint left after token 0
  * with softplus'(x) = sigmoid(x) and silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z))).
- * Shapes as ssm_oracle_scan_from; du, ddelta, dz [bsz][L][D]; dA [D][N]; dB, dC
+ * Shapes and flags as ssm_oracle_scan_from (the exact-ZOH input term is not covered:
+ * returns -2); du, ddelta, dz [bsz][L][D]; dA [D][N]; dB, dC
  * [bsz][L][N]; dD, dbias [D]; dh0 [bsz][D][N].  Every output is overwritten; dz, dD,
  * dbias, dh0 may be NULL (not wanted).  Channels d are spread over the threads (each
  * thread owns dA, dD, dbias of its channels); dB and dC are summed over channels from
@@ -169,11 +190,13 @@ int ssm_oracle_step(int64_t S, int64_t D, int64_t N, double *state,
 int ssm_oracle_scan_bwd(int64_t bsz, int64_t L, int64_t D, int64_t N, const double *h0,
                         const double *u, const double *delta, const double *A,
                         const double *B, const double *C, const double *Dv,
-                        const double *z, const double *delta_bias, int softplus_flag,
+                        const double *z, const double *delta_bias, int flags,
                         const double *dy, const double *dlast,
                         double *du, double *ddelta, double *dA, double *dB, double *dC,
                         double *dD, double *dz, double *dbias, double *dh0, int nthreads) {
     if (N > ORACLE_MAX_N || N < 1) return -1;
+    if (flags & ORACLE_EXACT_ZOH) return -2;   /* gradients of the simplified input term only */
+    const int softplus_flag = flags & ORACLE_SOFTPLUS;
     const int64_t nbt = bsz * L * N;
     memset(dB, 0, sizeof(double) * (size_t)nbt);
     memset(dC, 0, sizeof(double) * (size_t)nbt);

@@ -375,6 +375,99 @@ def check_h0_linear_without_input(scan_from, seed=53, L=30, D=2, N=3):
 H0_CHECKS = [check_h0_no_input_decay, check_h0_composition, check_h0_linear_without_input]
 
 
+# --- the exact zero-order-hold input term ----------------------------------------------------
+# scan_zoh(u, x, A, B, C, D, z, bias, softplus) -> (y, last_state), the scan with
+# B_bar = (exp(delta A) - 1) / A * B (delta * B where A = 0) in place of delta * B.
+
+def check_zoh_theorem1(scan_zoh, seed=61, L=200, D=4):
+    """Theorem 1 (azimuth.plus/paper/mamba) exactly: with N = 1, A = -1, B = C = 1 and
+    delta = softplus(x), the zero-order hold gives h_t = (1 - g_t) h_{t-1} + g_t u_t with
+    g_t = sigmoid(x_t), the gated recurrence, evaluated here directly."""
+    rng = _rng(seed)
+    x = 2.0 * rng.standard_normal((1, L, D))
+    u = rng.standard_normal((1, L, D))
+    A = -np.ones((D, 1))
+    B = np.ones((1, L, 1))
+    C = np.ones((1, L, 1))
+    y, last = scan_zoh(u, x, A, B, C, None, None, None, True)
+    g = expit(x)
+    want = np.zeros((1, L, D))
+    h = np.zeros(D)
+    for t in range(L):
+        h = (1.0 - g[0, t]) * h + g[0, t] * u[0, t]
+        want[0, t] = h
+    assert _rel(y, want) < 1e-13, _rel(y, want)
+    assert _rel(last[:, :, 0], want[:, -1]) < 1e-13
+
+
+def check_zoh_continuous_solution(scan_zoh, seed=62, L=60, D=3, N=5):
+    """Zero-order hold is exact for an input held constant: with u and B constant in time
+    and any positive step sizes, the state after t steps is the solution of
+    h' = A h + B u from h(0) = 0 at time S_t = sum of the step sizes,
+    h_t[n] = (exp(A[n] S_t) - 1) / A[n] * B[n] * u (yapayzekasozluk.tr "Temel Matematiksel
+    Cerceve": the continuous model that the discretisation samples).  A includes small
+    magnitudes, where exp(A S) - 1 must not lose its digits."""
+    rng = _rng(seed)
+    dt = rng.uniform(1e-4, 0.3, (1, L, D))
+    A = -np.exp(rng.normal(0.0, 1.5, (D, N)))
+    A[0, 0] = -1e-7
+    A[1, 2] = -3e-4
+    Bv = rng.standard_normal(N)
+    uv = rng.standard_normal(D)
+    u = np.broadcast_to(uv, (1, L, D)).copy()
+    B = np.broadcast_to(Bv, (1, L, N)).copy()
+    C = rng.standard_normal((1, L, N))
+    y, last = scan_zoh(u, dt, A, B, C, None, None, None, False)
+    S = np.cumsum(dt[0], axis=0)                                      # (L, D)
+    h = np.expm1(A[None] * S[:, :, None]) / A[None] * Bv[None, None] * uv[None, :, None]   # (L, D, N)
+    want = np.einsum("tdn,tn->td", h, C[0])[None]
+    assert _rel(y, want) < 1e-12, _rel(y, want)
+    assert _rel(last[0], h[-1]) < 1e-12
+
+
+def check_zoh_lti_bruteforce(scan_zoh, seed=63, L=120, D=4, N=3):
+    """With delta, B and C constant the exact-ZOH scan is the convolution
+    y_t = sum_k K_k u_{t-k} + D u_t with K_k = sum_n C_n exp(delta A_n)^k B_bar_n and
+    B_bar_n = (exp(delta A_n) - 1) / A_n * B_n (shakilmahmud.com section 3's convolutional
+    form), summed here term by term."""
+    rng = _rng(seed)
+    dtv = rng.uniform(0.01, 0.5, D)
+    A = -np.exp(rng.normal(0.5, 0.7, (D, N)))
+    Bv = rng.standard_normal(N)
+    Cv = rng.standard_normal(N)
+    Dv = rng.standard_normal(D)
+    u = rng.standard_normal((1, L, D))
+    dt = np.broadcast_to(dtv, (1, L, D)).copy()
+    y, _ = scan_zoh(u, dt, A, np.broadcast_to(Bv, (1, L, N)).copy(), np.broadcast_to(Cv, (1, L, N)).copy(),
+                    Dv, None, None, False)
+    want = np.zeros((1, L, D))
+    for d in range(D):
+        a = np.exp(dtv[d] * A[d])
+        bbar = np.expm1(dtv[d] * A[d]) / A[d] * Bv
+        K = np.array([np.sum(Cv * a ** k * bbar) for k in range(L)])
+        for t in range(L):
+            want[0, t, d] = np.sum(K[:t + 1][::-1] * u[0, :t + 1, d]) + Dv[d] * u[0, t, d]
+    assert _rel(y, want) < 1e-12, _rel(y, want)
+
+
+def check_zoh_zero_A(scan_zoh, seed=64, L=50, D=2, N=3):
+    """Where A = 0 nothing decays and B_bar = delta B (the limit of (exp(delta A) - 1) / A):
+    the state is the running sum of delta_t B_t u_t, evaluated here with a cumulative sum."""
+    rng = _rng(seed)
+    dt = rng.uniform(0.01, 1.0, (1, L, D))
+    u = rng.standard_normal((1, L, D))
+    B = rng.standard_normal((1, L, N))
+    C = rng.standard_normal((1, L, N))
+    A = np.zeros((D, N))
+    y, last = scan_zoh(u, dt, A, B, C, None, None, None, False)
+    h = np.cumsum(dt[0, :, :, None] * u[0, :, :, None] * B[0, :, None, :], axis=0)   # (L, D, N)
+    assert _rel(y[0], np.einsum("tdn,tn->td", h, C[0])) < 1e-12
+    assert _rel(last[0], h[-1]) < 1e-12
+
+
+ZOH_CHECKS = [check_zoh_theorem1, check_zoh_continuous_solution, check_zoh_lti_bruteforce, check_zoh_zero_A]
+
+
 # --- gradients of the scan ------------------------------------------------------------------
 # scan_from(u, x, A, B, C, D, z, bias, softplus, h0) -> (y, last_state)
 # scan_bwd(u, x, A, B, C, dy, D, z, bias, softplus, h0, dlast) -> dict of gradients

@@ -16,22 +16,21 @@ SRC = os.path.join(ROOT, "oracle", "ssm_oracle.c")
 
 MUTANTS = {
     "drop_skip_term": ("if (Dv) yt = yt + Dv[d] * ut;", "if (Dv) yt = yt;"),
-    "wrong_sign_of_A": ("double dA = exp(dt * A[d * N + n]);\n                h[n]",
-                        "double dA = exp(-dt * A[d * N + n]);\n                h[n]"),
-    "reversed_state_index_of_A": ("double dA = exp(dt * A[d * N + n]);\n                h[n]",
-                                  "double dA = exp(dt * A[d * N + (N - 1 - n)]);\n                h[n]"),
+    "wrong_sign_of_A": ("double dA = exp(dt * A[d * N + n]);\n                    h[n]",
+                        "double dA = exp(-dt * A[d * N + n]);\n                    h[n]"),
+    "reversed_state_index_of_A": ("double dA = exp(dt * A[d * N + n]);\n                    h[n]",
+                                  "double dA = exp(dt * A[d * N + (N - 1 - n)]);\n                    h[n]"),
     "swap_B_and_C": ("const double *Bt = B + (b * L + t) * N;\n            const double *Ct = C + (b * L + t) * N;",
                      "const double *Bt = C + (b * L + t) * N;\n            const double *Ct = B + (b * L + t) * N;"),
     "drop_delta_bias": ("if (delta_bias) x = x + delta_bias[d];", "if (delta_bias) x = x;"),
     "no_softplus": ("double dt = softplus_flag ? oracle_softplus(x) : x;", "double dt = x;"),
     "drop_gate": ("if (z) yt = yt * oracle_silu(z[i]);", "if (z) yt = yt;"),
     "sigmoid_not_silu": ("return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
-    "previous_token_input": ("h[n] = dA * h[n] + dt * Bt[n] * ut;\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];\n            double yt = acc;\n            if (Dv) yt = yt + Dv[d] * ut;\n            if (z) yt = yt * oracle_silu(z[i]);",
-                             "h[n] = dA * h[n] + dt * Bt[n] * u[t > 0 ? i - D : i];\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];\n            double yt = acc;\n            if (Dv) yt = yt + Dv[d] * ut;\n            if (z) yt = yt * oracle_silu(z[i]);"),
-    "drop_delta_in_input_term": ("h[n] = dA * h[n] + dt * Bt[n] * ut;\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];\n            double yt = acc;\n            if (Dv) yt = yt + Dv[d] * ut;\n            if (z) yt = yt * oracle_silu(z[i]);",
-                                 "h[n] = dA * h[n] + Bt[n] * ut;\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];\n            double yt = acc;\n            if (Dv) yt = yt + Dv[d] * ut;\n            if (z) yt = yt * oracle_silu(z[i]);"),
-    "readout_before_update": ("double dA = exp(dt * A[d * N + n]);\n                h[n] = dA * h[n] + dt * Bt[n] * ut;\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];",
-                              "double dA = exp(dt * A[d * N + n]);\n                h[n] = h[n];\n                (void)dA;\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];\n            for (int64_t n = 0; n < N; ++n) h[n] = exp(dt * A[d * N + n]) * h[n] + dt * Bt[n] * ut;"),
+    "previous_token_input": ("h[n] = dA * h[n] + dt * Bt[n] * ut;",
+                             "h[n] = dA * h[n] + dt * Bt[n] * u[t > 0 ? i - D : i];"),
+    "drop_delta_in_input_term": ("h[n] = dA * h[n] + dt * Bt[n] * ut;", "h[n] = dA * h[n] + Bt[n] * ut;"),
+    "readout_before_update": ("h[n] = dA * h[n] + dt * Bt[n] * ut;\n                }\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];",
+                              "(void)dA;\n                }\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];\n            if (!zoh) for (int64_t n = 0; n < N; ++n) h[n] = exp(dt * A[d * N + n]) * h[n] + dt * Bt[n] * ut;"),
     "last_state_wrong_index": ("last_state[(b * D + d) * N + n] = h[n];", "last_state[(b * D + d) * N + n] = h[0];"),
     "softplus_wrong_branch": ("if (x > 0.0) return x + log1p(exp(-x));", "if (x > 0.0) return x + log1p(exp(x));"),
     "ignore_initial_state": ("h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;", "h[n] = 0.0;"),
@@ -45,8 +44,12 @@ MUTANTS = {
                             "dCl[(b * L + t) * N + n] += lam * hist[t * N + n];"),
     "bwd_gate_derivative_missing_term": ("dz[i] = dy[i] * p * (sg * (1.0 + z[i] * (1.0 - sg)));",
                                          "dz[i] = dy[i] * p * sg;"),
-    "decay_squared": ("h[n] = dA * h[n] + dt * Bt[n] * ut;\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];\n            double yt = acc;\n            if (Dv) yt = yt + Dv[d] * ut;\n            if (z) yt = yt * oracle_silu(z[i]);",
-                      "h[n] = dA * dA * h[n] + dt * Bt[n] * ut;\n            }\n            double acc = 0.0;\n            for (int64_t n = 0; n < N; ++n) acc = acc + Ct[n] * h[n];\n            double yt = acc;\n            if (Dv) yt = yt + Dv[d] * ut;\n            if (z) yt = yt * oracle_silu(z[i]);"),
+    "zoh_simplified_coefficient": ("return a != 0.0 ? expm1(dt * a) / a : dt;", "return dt;"),
+    "zoh_exp_for_expm1": ("return a != 0.0 ? expm1(dt * a) / a : dt;", "return a != 0.0 ? exp(dt * a) / a : dt;"),
+    "zoh_wrong_limit": ("return a != 0.0 ? expm1(dt * a) / a : dt;", "return a != 0.0 ? expm1(dt * a) / a : 0.0;"),
+    "zoh_decay_from_coefficient": ("h[n] = exp(dt * a) * h[n] + oracle_zoh_coef(dt, a) * Bt[n] * ut;",
+                                   "h[n] = exp(-dt * a) * h[n] + oracle_zoh_coef(dt, a) * Bt[n] * ut;"),
+    "decay_squared": ("h[n] = dA * h[n] + dt * Bt[n] * ut;", "h[n] = dA * dA * h[n] + dt * Bt[n] * ut;"),
 }
 
 
@@ -94,6 +97,16 @@ def _build_mutant(tmp_path, name, old, new):
         lib.ssm_oracle_scan_from(bsz, L, Dch, N, ptr(h0), ptr(u), ptr(x), ptr(A), ptr(B), ptr(C), ptr(D),
                                  ptr(z), ptr(bias), int(bool(softplus)), ptr(y), ptr(h), 1)
         return y, h
+    def scan_zoh(u, x, A, B, C, D, z, bias, softplus):
+        u, x, A, B, C, D, z, bias = map(f64, (u, x, A, B, C, D, z, bias))
+        bsz, L, Dch = u.shape
+        N = A.shape[1]
+        y = np.empty((bsz, L, Dch))
+        h = np.empty((bsz, Dch, N))
+        lib.ssm_oracle_scan(bsz, L, Dch, N, ptr(u), ptr(x), ptr(A), ptr(B), ptr(C), ptr(D), ptr(z),
+                            ptr(bias), int(bool(softplus)) | 2, ptr(y), ptr(h), 1)
+        return y, h
+
     def scan_bwd(u, x, A, B, C, dy, D, z, bias, softplus, h0, dlast):
         u, x, A, B, C, dy, D, z, bias, h0, dlast = map(f64, (u, x, A, B, C, dy, D, z, bias, h0, dlast))
         bsz, L, Dch = u.shape
@@ -106,13 +119,13 @@ def _build_mutant(tmp_path, name, old, new):
                                 ptr(out["ddelta"]), ptr(out["dA"]), ptr(out["dB"]), ptr(out["dC"]), ptr(out["dD"]),
                                 ptr(out["dz"]), ptr(out["ddelta_bias"]), ptr(out["dh0"]), 1)
         return out
-    return scan, scan_from, scan_bwd
+    return scan, scan_from, scan_bwd, scan_zoh
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(tmp_path, name):
     old, new = MUTANTS[name]
-    scan, scan_from, scan_bwd = _build_mutant(tmp_path, name, old, new)
+    scan, scan_from, scan_bwd, scan_zoh = _build_mutant(tmp_path, name, old, new)
     caught = []
     with np.errstate(all="ignore"):
         for check in pins.ALL_CHECKS:
@@ -123,6 +136,11 @@ def test_planted_mistake_is_caught(tmp_path, name):
         for check in pins.H0_CHECKS:
             try:
                 check(scan_from)
+            except AssertionError:
+                caught.append(check.__name__)
+        for check in pins.ZOH_CHECKS:
+            try:
+                check(scan_zoh)
             except AssertionError:
                 caught.append(check.__name__)
         for check in pins.BWD_CHECKS:

@@ -16,6 +16,24 @@ def test_oracle_pin(oracle_mod, check):
     check(_scan(oracle_mod))
 
 
+def _scan_zoh(oracle_mod):
+    def f(u, x, A, B, C, D, z, bias, softplus):
+        return oracle_mod.scan(u, x, A, B, C, D=D, z=z, delta_bias=bias, softplus=softplus, threads=2,
+                               exact_zoh=True)
+    return f
+
+
+@pytest.mark.parametrize("check", pins.ZOH_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_zoh_pin(oracle_mod, check):
+    check(_scan_zoh(oracle_mod))
+
+
+def test_oracle_bwd_rejects_zoh(oracle_mod):
+    """The oracle's gradients cover the simplified input term only."""
+    lib = oracle_mod._load()
+    assert lib.ssm_oracle_scan_bwd(1, 1, 1, 1, *([None] * 9), 3, *([None] * 11), 1) == -2
+
+
 def test_step_repeated_equals_scan(oracle_mod):
     """Recurrent form == scan form (urworte.de "Methodische Grundlagen"; shakilmahmud.com
     section 3): L single-token steps from a zero state reproduce the scan bitwise when the
