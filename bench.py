@@ -42,7 +42,12 @@ WORKLOADS = {
     "c4": "selective scan B1 L131072 D2048 N16, bf16 I/O, fp32 state, last_state",
     "c5": "recurrent step S256 D5120 N16, bf16 I/O, fp32 state in place",
     "c3_bwd": "selective scan backward B8 L2048 D5120 N16, bf16 I/O, fp32 state, SiLU(z) gate, D skip",
+    "c3_zoh": "selective scan with the exact zero-order-hold input term B8 L2048 D5120 N16, bf16 I/O, "
+              "fp32 state, SiLU(z) gate, D skip, last_state",
 }
+# The exact zero-order-hold input term adds, per (token, channel, state), one evaluation of
+# (exp(delta A) - 1) / A counted as a transcendental (2 slots) and its multiply (1 slot).
+SLOTS_PER_ELEMENT_ZOH = SLOTS_PER_ELEMENT + 3
 # VALU issue slots per (token, channel, state) of the backward: the recomputed step (delta*A,
 # exp2 = 2, (delta u)*B, state FMA, readout FMA for the gate gradient) and the adjoint step
 # (lambda FMA, delta*A and exp2 = 3 for the decay, decay * h_{t-1}, lambda*delta, dA FMA,
@@ -97,7 +102,7 @@ def counter_traffic(workload: str):
     return c.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline_scan(case, alg_bytes_full, target_s=30.0):
+def cpu_baseline_scan(case, alg_bytes_full, target_s=30.0, exact_zoh=False):
     """Time the fp64 oracle on a channel sample of the workload on the host cores."""
     from oracle import oracle
     oracle.build(force=False)
@@ -105,14 +110,14 @@ def cpu_baseline_scan(case, alg_bytes_full, target_s=30.0):
     D = case.D
     probe = np.arange(0, D, max(1, D // 16))[:16]
     t = time.perf_counter()
-    oracle.scan_case(case, channels=probe, threads=threads)
+    oracle.scan_case(case, channels=probe, threads=threads, exact_zoh=exact_zoh)
     dt = time.perf_counter() - t
     per_ch = dt / len(probe)
     k = int(min(D, max(len(probe), target_s / max(per_ch, 1e-9))))
     sel = np.linspace(0, D - 1, k).astype(np.int64)
     sel = np.unique(sel)
     t = time.perf_counter()
-    oracle.scan_case(case, channels=sel, threads=threads)
+    oracle.scan_case(case, channels=sel, threads=threads, exact_zoh=exact_zoh)
     dt = time.perf_counter() - t
     frac = len(sel) / D
     gbps = alg_bytes_full * frac / dt / 1e9
@@ -201,7 +206,7 @@ def main():
 
     dev = "cuda"
     wl = args.workload
-    case = inputs.config_case("c3" if wl == "c3_bwd" else wl)
+    case = inputs.config_case("c3" if wl in ("c3_bwd", "c3_zoh") else wl)
     io_bytes = 2 if case.io == "bf16" else 4
 
     def td(a):
@@ -260,11 +265,14 @@ def main():
         elements = chtok * N
 
         call = ssmscan.scan_fwd_call(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
-                                     delta_bias=t["bias"], softplus=case.softplus, y=y, last_state=ls, workspace=ws)
+                                     delta_bias=t["bias"], softplus=case.softplus, y=y, last_state=ls, workspace=ws,
+                                     exact_zoh=wl == "c3_zoh")
 
         def one(i):
             call()
         plan = "single pass" if nchunk == 1 else f"{nchunk} chunks of {clen} tokens (summary + carry + scan)"
+        if wl == "c3_zoh":
+            plan += ", exact zero-order-hold input term"
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
@@ -307,7 +315,7 @@ def main():
     step_s = wall / args.steps
     gbps = alg / step_s / 1e9          # whole-job throughput over the timed region
     kern_gbps = alg / kern_s / 1e9     # the kernel's own rate (event-timed launches)
-    slots = SLOTS_PER_ELEMENT_BWD if wl == "c3_bwd" else SLOTS_PER_ELEMENT
+    slots = {"c3_bwd": SLOTS_PER_ELEMENT_BWD, "c3_zoh": SLOTS_PER_ELEMENT_ZOH}.get(wl, SLOTS_PER_ELEMENT)
     lane_ops = elements * slots / kern_s / 1e12
     traffic = counter_traffic(wl)
     if wl == "c5":
@@ -323,7 +331,7 @@ def main():
     if not args.no_cpu:
         try:
             cpu = (cpu_baseline_step(case, alg) if wl == "c5" else cpu_baseline_bwd(case, alg) if wl == "c3_bwd"
-                   else cpu_baseline_scan(case, alg))
+                   else cpu_baseline_scan(case, alg, exact_zoh=wl == "c3_zoh"))
         except Exception as e:  # the GPU figures stand without it
             cpu = {"error": repr(e)}
 

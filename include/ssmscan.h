@@ -3,13 +3,17 @@
  * recurrent step on AMD MI355X (gfx950).
  *
  * What is computed (per channel d of sequence b, state index n):
- *   step size       dt_t   = softplus(delta_t + delta_bias[d])   if softplus_flag
+ *   step size       dt_t   = softplus(delta_t + delta_bias[d])   with SSM_SCAN_SOFTPLUS
  *                          = delta_t + delta_bias[d]             otherwise
  *     (azimuth.plus/paper/mamba, "selection" section: delta_t = softplus(Linear(x_t)))
  *   discretisation  dA     = exp(dt_t * A[d,n])     (ZOH of a diagonal A;
  *                                                    yapayzekasozluk.tr, "Temel Matematiksel Cerceve")
  *                   input  = dt_t * B_t[n] * u_t    (simplified input matrix; the pages give no formula)
- *   recurrence      h_t[n] = dA * h_{t-1}[n] + dt_t * B_t[n] * u_t
+ *                   or, with SSM_SCAN_EXACT_ZOH, the zero-order hold of the same diagonal
+ *                   system, (exp(dt_t A[d,n]) - 1) / A[d,n] * B_t[n] * u_t (dt_t B_t[n] u_t
+ *                   where A = 0), under which Theorem 1 of azimuth.plus/paper/mamba (the
+ *                   gated recurrence) holds exactly
+ *   recurrence      h_t[n] = dA * h_{t-1}[n] + input
  *     (azimuth.plus/paper/mamba, hardware-aware algorithm section, parallel-scan bullet)
  *   readout         y_t    = (sum_n C_t[n] h_t[n] + D[d] u_t) * silu(z_t)
  *     (y = C h + D x: yapayzekasozluk.tr, same section; the SiLU gate branch multiplies
@@ -45,7 +49,11 @@
 extern "C" {
 #endif
 
-#define SSMSCAN_VERSION 3
+#define SSMSCAN_VERSION 4
+
+/* Bits of the `flags` argument of the scan entry points. */
+#define SSM_SCAN_SOFTPLUS 1     /* step size = softplus(delta + delta_bias) */
+#define SSM_SCAN_EXACT_ZOH 2    /* exact zero-order-hold input term (forward only) */
 
 #if defined(__GNUC__) || defined(__clang__)
 #define SSMSCAN_API __attribute__((visibility("default")))
@@ -66,7 +74,8 @@ typedef enum {
     SSM_ERR_ALIGN = -4,           /* a pointer is not aligned to its element size */
     SSM_ERR_UNSUPPORTED_N = -5,   /* dstate is not 1, 2, 4, 8 or 16 */
     SSM_ERR_WORKSPACE = -6,       /* workspace missing or smaller than required */
-    SSM_ERR_HIP = -7              /* the HIP runtime refused a launch */
+    SSM_ERR_HIP = -7,             /* the HIP runtime refused a launch */
+    SSM_ERR_FLAGS = -8            /* unknown flag bits, or a flag the entry point does not take */
 } ssm_status;
 
 /* Problem sizes.
@@ -107,7 +116,9 @@ SSMSCAN_API int64_t ssm_scan_plan(const ssm_dims *dims, int64_t *chunk_len_out);
  *   B, C           : [batch][seqlen][dstate] (io_dtype)
  *   A              : [dim][dstate] fp32
  *   D, delta_bias  : [dim] fp32, each may be NULL (= 0)
- *   softplus_flag  : nonzero = apply softplus to delta + delta_bias
+ *   flags          : SSM_SCAN_SOFTPLUS (apply softplus to delta + delta_bias) and/or
+ *                    SSM_SCAN_EXACT_ZOH (exact zero-order-hold input term); other bits are
+ *                    rejected with SSM_ERR_FLAGS
  *   y              : output, written completely
  *   last_state     : [batch][dim][dstate] fp32 output h_L, may be NULL
  *   workspace      : device memory of at least ssm_scan_workspace_bytes(dims) bytes, 16-byte
@@ -115,7 +126,7 @@ SSMSCAN_API int64_t ssm_scan_plan(const ssm_dims *dims, int64_t *chunk_len_out);
  *                    may be NULL when that size is 0
  * Returns SSM_OK or a negative ssm_status. */
 SSMSCAN_API int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
-                 const float *D, const void *z, const float *delta_bias, int softplus_flag,
+                 const float *D, const void *z, const float *delta_bias, int flags,
                  void *y, float *last_state, const ssm_dims *dims,
                  void *workspace, size_t workspace_bytes, void *stream);
 
@@ -131,7 +142,7 @@ SSMSCAN_API int ssm_scan_fwd(const void *u, const void *delta, const float *A, c
  * seqlen 0, last_state receives a copy of the initial state. */
 SSMSCAN_API int ssm_scan_fwd_from(const float *initial_state, const void *u, const void *delta, const float *A,
                       const void *B, const void *C, const float *D, const void *z, const float *delta_bias,
-                      int softplus_flag, void *y, float *last_state, const ssm_dims *dims, void *workspace,
+                      int flags, void *y, float *last_state, const ssm_dims *dims, void *workspace,
                       size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace ssm_scan_bwd needs: the checkpointed states, one per 8
@@ -143,7 +154,9 @@ SSMSCAN_API size_t ssm_scan_bwd_workspace_bytes(const ssm_dims *dims);
  * to every input, given dy = dLoss/dy and dlast_state = dLoss/d(last_state): the backward
  * pass, recomputing the states from checkpoints instead of storing them
  * (azimuth.plus/paper/mamba, hardware-aware algorithm section).
- *   inputs          : exactly those of the forward call (same shapes, dtypes, NULLs)
+ *   inputs          : exactly those of the forward call (same shapes, dtypes, NULLs);
+ *                     flags may hold SSM_SCAN_SOFTPLUS only (the gradients of the exact-ZOH
+ *                     input term are not provided: SSM_ERR_FLAGS)
  *   dy              : [batch][seqlen][dim] (io_dtype)
  *   dlast_state     : [batch][dim][dstate] fp32, or NULL (= 0)
  *   du, ddelta      : [batch][seqlen][dim] (io_dtype) outputs; ddelta is the gradient with
@@ -160,7 +173,7 @@ SSMSCAN_API size_t ssm_scan_bwd_workspace_bytes(const ssm_dims *dims);
  * Returns SSM_OK or a negative ssm_status (validation before any launch). */
 SSMSCAN_API int ssm_scan_bwd(const float *initial_state, const void *u, const void *delta, const float *A,
                  const void *B, const void *C, const float *D, const void *z, const float *delta_bias,
-                 int softplus_flag, const void *dy, const float *dlast_state, void *du, void *ddelta,
+                 int flags, const void *dy, const float *dlast_state, void *du, void *ddelta,
                  float *dA, float *dB, float *dC, float *dD, void *dz, float *ddelta_bias,
                  float *dinitial_state, const ssm_dims *dims, void *workspace, size_t workspace_bytes,
                  void *stream);
@@ -173,7 +186,7 @@ SSMSCAN_API int ssm_scan_bwd(const float *initial_state, const void *u, const vo
  *   B, C           : [batch][dstate] (io_dtype)
  *   A              : [dim][dstate] fp32;  D : [dim] fp32 or NULL
  * Repeating it over a sequence from a zero state reproduces ssm_scan_fwd with
- * softplus_flag = 0 and no delta_bias.  Returns SSM_OK or a negative ssm_status. */
+ * flags = 0 and no delta_bias.  Returns SSM_OK or a negative ssm_status. */
 SSMSCAN_API int ssm_step(float *state, const void *u, const void *delta, const float *A, const void *B,
              const void *C, const float *D, const void *z, void *y, const ssm_dims *dims,
              void *stream);

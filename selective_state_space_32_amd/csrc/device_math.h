@@ -123,6 +123,23 @@ __device__ __forceinline__ float softplus_f32(float x) {
     return softplus_f32(x, sig);
 }
 
+// Exact zero-order hold of the input term: B_bar = (exp(delta A) - 1) / A * B =
+// delta * phi(delta A) * B with phi(x) = (e^x - 1) / x.  zoh_factor(y, e) returns
+// ln(2) phi(x) = (e - 1) / y for y = x log2(e) and e = exp2(y) (both already formed for the
+// decay), so the input term is (delta u log2(e)) * B * zoh_factor.  For |x| < 1/4 it is the
+// Taylor series of ln(2) phi(y ln 2) = sum_k ln(2)^(k+1) y^k / (k+1)!, cut after y^5
+// (relative truncation below 6e-8); there e - 1 would lose up to 2^-24 / |x| of its value
+// to the rounding of e.  Elsewhere |e - 1| >= 0.22 and (e - 1) / y is accurate to ~1e-6.
+__device__ __forceinline__ float zoh_factor(float y, float e) {
+    float p = fmaf(y, 1.5403530393381606e-4f, 1.3333558146428441e-3f);
+    p = fmaf(y, p, 9.618129107628477e-3f);
+    p = fmaf(y, p, 5.5504108664821576e-2f);
+    p = fmaf(y, p, 2.402265069591007e-1f);
+    p = fmaf(y, p, 6.931471805599453e-1f);
+    const float q = (e - 1.0f) * hw_rcp(y);
+    return fabsf(y) < 0.25f * kLog2e ? p : q;
+}
+
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z).  For z << 0, e^-z = inf and the result is -0.
 __device__ __forceinline__ float silu_f32(float z) {
     float e = hw_exp2(-z * kLog2e);

@@ -81,7 +81,9 @@ __device__ __forceinline__ void load_slice(const IO *__restrict__ p, int64_t off
 //   VEC: the prep and epilogue move V consecutive channels of one token per thread
 //        (one 16-byte access for 8 bf16); needs D % 8 == 0 and 16-byte aligned u, delta,
 //        z, y.  Otherwise one element per access.
-template <int N, int S, int T, typename IO, int MODE, bool VEC>
+//   ZOH: the input term is the exact zero-order hold (exp(delta A) - 1) / A * B * u
+//        instead of delta * B * u (the decay is the same).
+template <int N, int S, int T, typename IO, int MODE, bool VEC, bool ZOH = false>
 __global__ void __launch_bounds__(64 * (N / S))
 scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                   const IO *__restrict__ z, IO *__restrict__ y,
@@ -241,7 +243,8 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     // is empty (nt = 0).
     auto do_tile = [&](int64_t t0, Raw &r, const DG &prev, DG &cur, bool has_prev) {
         const int nt = (int)max((int64_t)0, min((int64_t)T, t_end - t0));
-        // prep: (delta, delta*u) into LDS; skip and gate factors kept in registers
+        // prep: (delta, delta*u) into LDS (delta*u*log2(e) for the zero-order hold); skip
+        // and gate factors kept in registers
         // (without a gate the factors keep the 1.0 they start with)
 #pragma unroll
         for (int p = 0; p < P; ++p) {
@@ -254,7 +257,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                 // (written unmasked: rows of tokens past the end are never read by the
                 // recurrence, and lanes of channels past D hold values loaded from an
                 // in-bounds channel and are never stored)
-                s_dk[tt][cq + v] = f32x2_t{dl, dl * uu};
+                s_dk[tt][cq + v] = f32x2_t{dl, ZOH ? dl * uu * kLog2e : dl * uu};
                 if (READOUT) {
                     cur.u[p][v] = uu;
                     if (gated) cur.g[p][v] = silu_f32(raw(r.z[p], v));
@@ -302,8 +305,11 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                     float acc = 0.0f;
 #pragma unroll
                     for (int s = 0; s < S; ++s) {
-                        const float e = hw_exp2(v[i].x * a2[s]);
-                        h[s] = fmaf(e, h[s], v[i].y * word_f32<IO>(bw[i], s));
+                        const float ya = v[i].x * a2[s];
+                        const float e = hw_exp2(ya);
+                        float bu = v[i].y * word_f32<IO>(bw[i], s);
+                        if constexpr (ZOH) bu *= zoh_factor(ya, e);
+                        h[s] = fmaf(e, h[s], bu);
                         if (READOUT) acc = fmaf(word_f32<IO>(cw[i], s), h[s], acc);
                     }
                     if (READOUT)
@@ -338,8 +344,11 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                 float acc = 0.0f;
 #pragma unroll
                 for (int s = 0; s < S; ++s) {
-                    const float e = hw_exp2(v.x * a2[s]);
-                    h[s] = fmaf(e, h[s], v.y * Bs[s]);
+                    const float ya = v.x * a2[s];
+                    const float e = hw_exp2(ya);
+                    float bu = v.y * Bs[s];
+                    if constexpr (ZOH) bu *= zoh_factor(ya, e);
+                    h[s] = fmaf(e, h[s], bu);
                     if (READOUT) acc = fmaf(Cs[s], h[s], acc);
                 }
                 if (READOUT)

@@ -127,7 +127,7 @@ template <> struct ScanShape<4> { static constexpr int S = 4, T = 32; };
 template <> struct ScanShape<8> { static constexpr int S = 4, T = 32; };
 template <> struct ScanShape<16> { static constexpr int S = 4, T = 32; };
 
-template <int N, typename IO, bool VEC>
+template <int N, typename IO, bool VEC, bool ZOH>
 void launch_scan_kernels(const IO *u, const IO *dl, const float *A, const IO *B, const IO *C, const float *Dv,
                          const IO *z, const float *bias, int softplus, const float *h0, IO *y, float *last_state,
                          const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st) {
@@ -143,7 +143,7 @@ void launch_scan_kernels(const IO *u, const IO *dl, const float *A, const IO *B,
     const int64_t cl = p.chunk_len;
     const int nc = (int)p.nchunk;
     if (p.schedule == kCarry) {
-        hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kSummary, VEC>),
+        hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kSummary, VEC, ZOH>),
                            dim3((unsigned)n_tiles, (unsigned)(nc - 1)), block, 0, st, u, dl, (const IO *)nullptr,
                            (IO *)nullptr, A, (const float *)nullptr, bias, B, C, (const float *)nullptr,
                            (float *)nullptr, cstate, cdsum, L, D, tiles_per_b, n_tiles, cl, nc, softplus);
@@ -151,15 +151,17 @@ void launch_scan_kernels(const IO *u, const IO *dl, const float *A, const IO *B,
         hipLaunchKernelGGL((ssm::carry_scan_kernel<N>), dim3((unsigned)(bsz * col_tiles)), dim3(256), 0, st,
                            cstate, (const float *)cdsum, A, h0, D, nc, col_tiles);
     }
-    hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kFull, VEC>), dim3((unsigned)n_tiles, (unsigned)nc),
+    hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kFull, VEC, ZOH>), dim3((unsigned)n_tiles, (unsigned)nc),
                        block, 0, st, u, dl, z, y, A, Dv, bias, B, C, h0, last_state, cstate, cdsum, L, D,
                        tiles_per_b, n_tiles, cl, nc, softplus);
 }
 
 template <int N, typename IO>
 int launch_scan(const void *u, const void *delta, const float *A, const void *B, const void *C,
-                const float *Dv, const void *z, const float *bias, int softplus, const float *h0, void *y,
+                const float *Dv, const void *z, const float *bias, int flags, const float *h0, void *y,
                 float *last_state, const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st) {
+    const int softplus = (flags & SSM_SCAN_SOFTPLUS) != 0;
+    const bool zoh = (flags & SSM_SCAN_EXACT_ZOH) != 0;
     const IO *u_ = static_cast<const IO *>(u);
     const IO *dl_ = static_cast<const IO *>(delta);
     const IO *z_ = static_cast<const IO *>(z);
@@ -169,12 +171,18 @@ int launch_scan(const void *u, const void *delta, const float *A, const void *B,
     // 16-byte prep/epilogue accesses need whole groups of 8 channels and aligned rows
     const bool vec = dm->dim % 8 == 0 && aligned(u, 16) && aligned(delta, 16) && aligned(y, 16) &&
                      (!z || aligned(z, 16));
-    if (vec)
-        launch_scan_kernels<N, IO, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state, dm, p, ws,
-                                         st);
+    if (vec && zoh)
+        launch_scan_kernels<N, IO, true, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state, dm, p,
+                                               ws, st);
+    else if (vec)
+        launch_scan_kernels<N, IO, true, false>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state, dm,
+                                                p, ws, st);
+    else if (zoh)
+        launch_scan_kernels<N, IO, false, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state, dm,
+                                                p, ws, st);
     else
-        launch_scan_kernels<N, IO, false>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state, dm, p, ws,
-                                          st);
+        launch_scan_kernels<N, IO, false, false>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state, dm,
+                                                 p, ws, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -182,14 +190,14 @@ int launch_scan(const void *u, const void *delta, const float *A, const void *B,
 
 template <typename IO>
 int dispatch_scan(int64_t N, const void *u, const void *delta, const float *A, const void *B,
-                  const void *C, const float *Dv, const void *z, const float *bias, int sp, const float *h0,
+                  const void *C, const float *Dv, const void *z, const float *bias, int flags, const float *h0,
                   void *y, float *ls, const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st) {
     switch (N) {
-        case 1: return launch_scan<1, IO>(u, delta, A, B, C, Dv, z, bias, sp, h0, y, ls, dm, p, ws, st);
-        case 2: return launch_scan<2, IO>(u, delta, A, B, C, Dv, z, bias, sp, h0, y, ls, dm, p, ws, st);
-        case 4: return launch_scan<4, IO>(u, delta, A, B, C, Dv, z, bias, sp, h0, y, ls, dm, p, ws, st);
-        case 8: return launch_scan<8, IO>(u, delta, A, B, C, Dv, z, bias, sp, h0, y, ls, dm, p, ws, st);
-        case 16: return launch_scan<16, IO>(u, delta, A, B, C, Dv, z, bias, sp, h0, y, ls, dm, p, ws, st);
+        case 1: return launch_scan<1, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st);
+        case 2: return launch_scan<2, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st);
+        case 4: return launch_scan<4, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st);
+        case 8: return launch_scan<8, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st);
+        case 16: return launch_scan<16, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st);
     }
     return fail(SSM_ERR_UNSUPPORTED_N, "dstate %lld not supported", (long long)N);
 }
@@ -316,11 +324,12 @@ int dispatch_bwd(int64_t N, const BwdArgs &a, const ssm_dims *dm, void *ws, hipS
 }  // namespace
 
 static int scan_impl(const float *h0, const void *u, const void *delta, const float *A, const void *B,
-                     const void *C, const float *D, const void *z, const float *delta_bias, int softplus_flag,
+                     const void *C, const float *D, const void *z, const float *delta_bias, int flags,
                      void *y, float *last_state, const ssm_dims *dims, void *workspace, size_t workspace_bytes,
                      void *stream) {
     int rc = check_dims(dims, true);
     if (rc != SSM_OK) return rc;
+    if (flags & ~(SSM_SCAN_SOFTPLUS | SSM_SCAN_EXACT_ZOH)) return fail(SSM_ERR_FLAGS, "unknown flag bits 0x%x", flags);
     const int64_t bsz = dims->batch, L = dims->seqlen, Dm = dims->dim, N = dims->dstate;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (bsz == 0 || Dm == 0) return ok();
@@ -357,10 +366,10 @@ static int scan_impl(const float *h0, const void *u, const void *delta, const fl
                     p.bytes);
     if (p.bytes > 0 && !aligned(workspace, 16)) return fail(SSM_ERR_ALIGN, "workspace not 16-byte aligned");
     if (dims->io_dtype == SSM_IO_BF16)
-        return dispatch_scan<uint16_t>(N, u, delta, A, B, C, D, z, delta_bias, softplus_flag != 0, h0, y,
-                                       last_state, dims, p, workspace, st);
-    return dispatch_scan<float>(N, u, delta, A, B, C, D, z, delta_bias, softplus_flag != 0, h0, y, last_state,
-                                dims, p, workspace, st);
+        return dispatch_scan<uint16_t>(N, u, delta, A, B, C, D, z, delta_bias, flags, h0, y, last_state, dims, p,
+                                       workspace, st);
+    return dispatch_scan<float>(N, u, delta, A, B, C, D, z, delta_bias, flags, h0, y, last_state, dims, p,
+                                workspace, st);
 }
 
 
@@ -385,18 +394,18 @@ int64_t ssm_scan_plan(const ssm_dims *dims, int64_t *chunk_len_out) {
 }
 
 int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
-                 const float *D, const void *z, const float *delta_bias, int softplus_flag,
+                 const float *D, const void *z, const float *delta_bias, int flags,
                  void *y, float *last_state, const ssm_dims *dims,
                  void *workspace, size_t workspace_bytes, void *stream) {
-    return scan_impl(nullptr, u, delta, A, B, C, D, z, delta_bias, softplus_flag, y, last_state, dims, workspace,
+    return scan_impl(nullptr, u, delta, A, B, C, D, z, delta_bias, flags, y, last_state, dims, workspace,
                      workspace_bytes, stream);
 }
 
 int ssm_scan_fwd_from(const float *initial_state, const void *u, const void *delta, const float *A,
                       const void *B, const void *C, const float *D, const void *z, const float *delta_bias,
-                      int softplus_flag, void *y, float *last_state, const ssm_dims *dims, void *workspace,
+                      int flags, void *y, float *last_state, const ssm_dims *dims, void *workspace,
                       size_t workspace_bytes, void *stream) {
-    return scan_impl(initial_state, u, delta, A, B, C, D, z, delta_bias, softplus_flag, y, last_state, dims,
+    return scan_impl(initial_state, u, delta, A, B, C, D, z, delta_bias, flags, y, last_state, dims,
                      workspace, workspace_bytes, stream);
 }
 
@@ -425,12 +434,15 @@ size_t ssm_scan_bwd_workspace_bytes(const ssm_dims *dims) {
 }
 
 int ssm_scan_bwd(const float *initial_state, const void *u, const void *delta, const float *A, const void *B,
-                 const void *C, const float *D, const void *z, const float *delta_bias, int softplus_flag,
+                 const void *C, const float *D, const void *z, const float *delta_bias, int flags,
                  const void *dy, const float *dlast_state, void *du, void *ddelta, float *dA, float *dB,
                  float *dC, float *dD, void *dz, float *ddelta_bias, float *dinitial_state, const ssm_dims *dims,
                  void *workspace, size_t workspace_bytes, void *stream) {
     int rc = check_dims(dims, true);
     if (rc != SSM_OK) return rc;
+    if (flags & ~SSM_SCAN_SOFTPLUS)
+        return fail(SSM_ERR_FLAGS, "flags 0x%x: the backward pass takes the softplus flag only (no exact ZOH)",
+                    flags);
     const int64_t bsz = dims->batch, L = dims->seqlen, Dm = dims->dim, N = dims->dstate;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (!A || !dA || (bsz > 0 && L > 0 && Dm > 0 && (!u || !delta || !B || !C || !dy || !du || !ddelta || !dB || !dC)))
@@ -475,7 +487,7 @@ int ssm_scan_bwd(const float *initial_state, const void *u, const void *delta, c
         if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
         return ok();
     }
-    BwdArgs a{initial_state, u, delta, A, B, C, D, z, delta_bias, softplus_flag != 0, dy, dlast_state, du, ddelta,
+    BwdArgs a{initial_state, u, delta, A, B, C, D, z, delta_bias, (flags & SSM_SCAN_SOFTPLUS) != 0, dy, dlast_state, du, ddelta,
               dA, dB, dC, dD, dz, ddelta_bias, dinitial_state};
     if (dims->io_dtype == SSM_IO_BF16) return dispatch_bwd<uint16_t>(N, a, dims, workspace, st);
     return dispatch_bwd<float>(N, a, dims, workspace, st);

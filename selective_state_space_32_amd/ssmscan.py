@@ -20,7 +20,7 @@ SSM_IO_F32 = 0
 SSM_IO_BF16 = 1
 
 STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL", -2: "SSM_ERR_SHAPE", -3: "SSM_ERR_DTYPE", -4: "SSM_ERR_ALIGN",
-          -5: "SSM_ERR_UNSUPPORTED_N", -6: "SSM_ERR_WORKSPACE", -7: "SSM_ERR_HIP"}
+          -5: "SSM_ERR_UNSUPPORTED_N", -6: "SSM_ERR_WORKSPACE", -7: "SSM_ERR_HIP", -8: "SSM_ERR_FLAGS"}
 
 
 class ssm_dims(ctypes.Structure):
@@ -125,8 +125,12 @@ def _stream_handle(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+SCAN_SOFTPLUS = 1      # flag bits of the scan entry points (include/ssmscan.h)
+SCAN_EXACT_ZOH = 2
+
+
 def _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state, return_last_state, chunk_len,
-               workspace, stream, initial_state=None):
+               workspace, stream, initial_state=None, exact_zoh=False):
     if u.dim() != 3:
         raise ValueError("u must be (batch, L, dim)")
     bsz, L, dim = u.shape
@@ -159,7 +163,8 @@ def _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state, ret
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     args = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-            int(bool(softplus)), _ptr(y), _ptr(last_state), ctypes.byref(dims), _ptr(workspace),
+            (SCAN_SOFTPLUS if softplus else 0) | (SCAN_EXACT_ZOH if exact_zoh else 0), _ptr(y),
+            _ptr(last_state), ctypes.byref(dims), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream_handle(stream))
     if initial_state is not None:
         args = (_ptr(initial_state),) + args
@@ -173,15 +178,17 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
              delta_bias: Optional[torch.Tensor] = None, softplus: bool = True, *,
              y: Optional[torch.Tensor] = None, last_state: Optional[torch.Tensor] = None,
              return_last_state: bool = True, chunk_len: int = 0,
-             workspace: Optional[torch.Tensor] = None, stream=None):
+             workspace: Optional[torch.Tensor] = None, stream=None, exact_zoh: bool = False):
     """Selective scan forward from a zero state (ssm_scan_fwd).
 
     u, delta, z: (batch, L, dim); B, C: (batch, L, N), all of one dtype (float32 or bfloat16);
-    A: (dim, N) float32; D, delta_bias: (dim,) float32 or None.
+    A: (dim, N) float32; D, delta_bias: (dim,) float32 or None.  exact_zoh: the exact
+    zero-order-hold input term (exp(delta A) - 1) / A * B * u instead of delta * B * u.
     Returns (y, last_state) -- last_state (batch, dim, N) float32, or None if not asked for.
     """
     args, _keep, y, last_state = _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
-                                            return_last_state, chunk_len, workspace, stream)
+                                            return_last_state, chunk_len, workspace, stream,
+                                            exact_zoh=exact_zoh)
     _check(lib.ssm_scan_fwd(*args))
     return y, last_state
 
@@ -191,12 +198,13 @@ def scan_fwd_call(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torc
                   delta_bias: Optional[torch.Tensor] = None, softplus: bool = True, *,
                   y: Optional[torch.Tensor] = None, last_state: Optional[torch.Tensor] = None,
                   return_last_state: bool = True, chunk_len: int = 0,
-                  workspace: Optional[torch.Tensor] = None, stream=None) -> Callable[[], None]:
+                  workspace: Optional[torch.Tensor] = None, stream=None,
+                  exact_zoh: bool = False) -> Callable[[], None]:
     """The scan_fwd call checked and marshalled once: returns a function that enqueues the
     same call again (same tensors, the stream given or current now), for loops that repeat
     it.  Outputs go to the y / last_state tensors passed in (or allocated here and kept)."""
     args, keep, _y, _ls = _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
-                                     return_last_state, chunk_len, workspace, stream)
+                                     return_last_state, chunk_len, workspace, stream, exact_zoh=exact_zoh)
 
     def call(_args=args, _keep=keep):
         _check(lib.ssm_scan_fwd(*_args))
@@ -208,12 +216,14 @@ def scan_fwd_from(initial_state: torch.Tensor, u: torch.Tensor, delta: torch.Ten
                   z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
                   softplus: bool = True, *, y: Optional[torch.Tensor] = None,
                   last_state: Optional[torch.Tensor] = None, return_last_state: bool = True,
-                  chunk_len: int = 0, workspace: Optional[torch.Tensor] = None, stream=None):
+                  chunk_len: int = 0, workspace: Optional[torch.Tensor] = None, stream=None,
+                  exact_zoh: bool = False):
     """The scan continued from initial_state (batch, dim, N) float32 (ssm_scan_fwd_from).
     last_state may be initial_state itself (the state advanced in place).  Otherwise as
     scan_fwd."""
     args, _keep, y, last_state = _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
-                                            return_last_state, chunk_len, workspace, stream, initial_state)
+                                            return_last_state, chunk_len, workspace, stream, initial_state,
+                                            exact_zoh=exact_zoh)
     _check(lib.ssm_scan_fwd_from(*args))
     return y, last_state
 

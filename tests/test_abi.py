@@ -133,6 +133,19 @@ def test_bwd_validation(b):
     assert _bwd(b, d, ws_bytes=16) == -6
 
 
+def test_flags_validated(b):
+    # unknown flag bits are rejected by the scan; the backward takes the softplus bit only
+    P = ctypes.c_void_p
+    d = _dims(b)
+    ws = b.lib.ssm_scan_workspace_bytes(ctypes.byref(d))
+    for flags in (4, 8, 1 << 20, -1):
+        rc = b.lib.ssm_scan_fwd(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None, None, flags, P(FAKE), None,
+                                ctypes.byref(d), P(FAKE), ws, None)
+        assert rc == -8 and "flag" in b.last_error()
+    assert _bwd(b, d, softplus=3) == -8 and "ZOH" in b.last_error()
+    assert _bwd(b, d, softplus=2) == -8
+
+
 def test_misaligned_rejected(b):
     assert _scan(b, _dims(b), u=FAKE + 1) == -4
     assert _scan(b, _dims(b, io_dtype=0), y=FAKE + 2) == -4
