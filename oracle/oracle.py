@@ -54,6 +54,8 @@ def _load():
         lib.ssm_oracle_scan_bwd.restype = ctypes.c_int
         lib.ssm_oracle_step.argtypes = [I64, I64, I64, P, P, P, P, P, P, P, P, P, ctypes.c_int]
         lib.ssm_oracle_step.restype = ctypes.c_int
+        lib.ssm_oracle_conv1d.argtypes = [I64, I64, I64, I64, P, P, P, P, ctypes.c_int, P, P]
+        lib.ssm_oracle_conv1d.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -182,3 +184,26 @@ def scan_case(case, channels=None, threads: Optional[int] = None, h0=None, exact
         h0 = np.asarray(h0)[:, sel]
     return scan(u, dl, A, case.values("B"), case.values("C"), D=D, z=z, delta_bias=bias,
                 softplus=case.softplus, threads=threads, h0=h0, exact_zoh=exact_zoh)
+
+
+def conv1d(x, w, bias=None, state=None, silu: bool = True) -> Tuple[np.ndarray, np.ndarray]:
+    """fp64 causal depthwise convolution over time, then SiLU (if silu).
+
+    x: (bsz, L, Dch); w: (Dch, width), tap k multiplying x[t - (width-1) + k]; bias: (Dch,);
+    state: (bsz, width-1, Dch), the inputs before token 0 (None = zeros).
+    Returns (out (bsz, L, Dch), state_out (bsz, width-1, Dch)), both float64.
+    """
+    x = _f64(x)
+    bsz, L, Dch = x.shape
+    w = _f64(w)
+    width = w.shape[1]
+    w = _f64(w, (Dch, width))
+    bias = _f64(bias, (Dch,))
+    state = _f64(state, (bsz, width - 1, Dch))
+    out = np.empty((bsz, L, Dch), dtype=np.float64)
+    st = np.empty((bsz, width - 1, Dch), dtype=np.float64)
+    rc = _load().ssm_oracle_conv1d(bsz, L, Dch, width, _ptr(x), _ptr(w), _ptr(bias), _ptr(state), int(bool(silu)),
+                                   _ptr(out), _ptr(st))
+    if rc != 0:
+        raise ValueError("oracle conv1d rejected width=%d" % width)
+    return out, st

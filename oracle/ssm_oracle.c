@@ -23,6 +23,8 @@
  *      (azimuth.plus/paper/mamba, block architecture section)
  *  - the recurrent (inference) form: constant memory, one state update per token
  *      (shakilmahmud.com section 3; urworte.de "Methodische Grundlagen")
+ *  - the short causal convolution and SiLU that produce the scan's input in the block's
+ *      main branch (azimuth.plus/paper/mamba, block architecture section)
  *
  * Readings where the pages are silent: the scan starts from h = 0; the step size is
  * softplus(delta_in + delta_bias) when the flag is set, else delta_in + delta_bias;
@@ -301,4 +303,43 @@ int ssm_oracle_scan_bwd(int64_t bsz, int64_t L, int64_t D, int64_t N, const doub
         free(dCl);
     }
     return fail ? -1 : 0;
+}
+
+/*
+ * The causal depthwise convolution of the block's main branch, then optionally SiLU:
+ * the input of the selective scan comes from a short 1-D convolution over time (kernel
+ * size 4) followed by SiLU (azimuth.plus/paper/mamba, block architecture section).
+ * Depthwise: every channel has its own filter of `width` taps; causal: token t sees only
+ * tokens t-width+1 .. t, with the inputs before token 0 taken from `state` (zeros if NULL).
+ *   x, out       : [bsz][L][D]
+ *   w            : [D][width], tap k multiplying x[t - (width-1) + k]
+ *   bias         : [D] or NULL (= 0)
+ *   state        : [bsz][width-1][D], the width-1 inputs before token 0, oldest first, or NULL
+ *   silu         : nonzero = out = silu(pre-activation)
+ *   state_out    : [bsz][width-1][D], the last width-1 inputs of (state, x), or NULL
+ * Returns 0, or -1 for a width outside 1..16 or a failed allocation.
+ */
+int ssm_oracle_conv1d(int64_t bsz, int64_t L, int64_t D, int64_t width, const double *x,
+                      const double *w, const double *bias, const double *state, int silu,
+                      double *out, double *state_out) {
+    if (width < 1 || width > 16) return -1;
+    const int64_t H = width - 1;           /* history rows before token 0 */
+    double *hist = malloc(sizeof(double) * (size_t)(H + L > 0 ? H + L : 1));
+    if (!hist) return -1;
+    for (int64_t b = 0; b < bsz; ++b) {
+        for (int64_t d = 0; d < D; ++d) {
+            /* the channel's inputs in time order: the state rows, then x */
+            for (int64_t r = 0; r < H; ++r) hist[r] = state ? state[(b * H + r) * D + d] : 0.0;
+            for (int64_t t = 0; t < L; ++t) hist[H + t] = x[(b * L + t) * D + d];
+            for (int64_t t = 0; t < L; ++t) {
+                double acc = bias ? bias[d] : 0.0;
+                for (int64_t k = 0; k < width; ++k) acc = acc + w[d * width + k] * hist[t + k];
+                out[(b * L + t) * D + d] = silu ? oracle_silu(acc) : acc;
+            }
+            if (state_out)
+                for (int64_t r = 0; r < H; ++r) state_out[(b * H + r) * D + d] = hist[L + r];
+        }
+    }
+    free(hist);
+    return 0;
 }

@@ -468,6 +468,86 @@ def check_zoh_zero_A(scan_zoh, seed=64, L=50, D=2, N=3):
 ZOH_CHECKS = [check_zoh_theorem1, check_zoh_continuous_solution, check_zoh_lti_bruteforce, check_zoh_zero_A]
 
 
+# --- the causal depthwise convolution and SiLU of the block's main branch ---------------------
+# conv(x, w, bias, state, silu) -> (out, state_out)
+# (azimuth.plus/paper/mamba, block architecture section: a short 1-D convolution of kernel
+# size 4, then SiLU, produce the scan's input)
+
+def _conv_case(seed, bsz=2, L=37, D=5, width=4):
+    rng = _rng(seed)
+    return (rng.standard_normal((bsz, L, D)), rng.standard_normal((D, width)), rng.standard_normal(D), rng)
+
+
+def check_conv_numpy_convolve(conv, seed=81):
+    """Without SiLU and from a zero history, each channel is numpy's full convolution of
+    its inputs with its reversed filter, cut to the first L outputs, plus the bias."""
+    for width in (1, 2, 3, 4):
+        x, w, bias, _ = _conv_case(seed + width, width=width)
+        out, _ = conv(x, w, bias, None, False)
+        want = np.empty_like(x)
+        for b in range(x.shape[0]):
+            for d in range(x.shape[2]):
+                want[b, :, d] = np.convolve(x[b, :, d], w[d, ::-1])[:x.shape[1]] + bias[d]
+        assert _rel(out, want) < 1e-14, (width, _rel(out, want))
+
+
+def check_conv_impulse(conv, seed=82, L=20, D=3, width=4):
+    """A unit impulse at token t0 gives the filter back, newest tap first: out[t0 + j] =
+    bias + w[width - 1 - j] for j < width, and the bias alone elsewhere (causal)."""
+    rng = _rng(seed)
+    w = rng.standard_normal((D, width))
+    bias = rng.standard_normal(D)
+    t0 = 7
+    x = np.zeros((1, L, D))
+    x[0, t0] = 1.0
+    out, _ = conv(x, w, bias, None, False)
+    for t in range(L):
+        j = t - t0
+        want = bias + (w[:, width - 1 - j] if 0 <= j < width else 0.0)
+        assert np.all(out[0, t] == want), (t, out[0, t], want)
+
+
+def check_conv_silu(conv, seed=83):
+    """With SiLU the output is v * sigmoid(v) of the pre-activation (scipy's expit)."""
+    x, w, bias, _ = _conv_case(seed)
+    pre, _ = conv(x, w, bias, None, False)
+    out, _ = conv(x, w, bias, None, True)
+    assert _rel(out, pre * expit(pre)) < 1e-14
+
+
+def check_conv_continuation(conv, seed=84):
+    """Running the inputs in two pieces, the second from the first's state, is bitwise the
+    run over the whole; the state is the last width-1 inputs (oldest first), also when a
+    piece is shorter than the history."""
+    for width in (2, 4):
+        x, w, bias, rng = _conv_case(seed + width, L=41, width=width)
+        st0 = rng.standard_normal((x.shape[0], width - 1, x.shape[2]))
+        whole, st_whole = conv(x, w, bias, st0, True)
+        for cut in (1, 2, 17, 40):
+            a, sa = conv(x[:, :cut], w, bias, st0, True)
+            bb, sb = conv(x[:, cut:], w, bias, sa, True)
+            assert np.array_equal(np.concatenate([a, bb], axis=1), whole), (width, cut)
+            assert np.array_equal(sb, st_whole)
+        assert np.array_equal(st_whole, x[:, -(width - 1):])
+        hist = np.concatenate([st0, x[:, :1]], axis=1)
+        _, s1 = conv(x[:, :1], w, bias, st0, True)
+        assert np.array_equal(s1, hist[:, -(width - 1):])
+
+
+def check_conv_state_is_history(conv, seed=85):
+    """A state equals inputs before token 0: the run from a state gives the tail of the run
+    over (state rows, x) from a zero history."""
+    x, w, bias, rng = _conv_case(seed, L=30)
+    st0 = rng.standard_normal((x.shape[0], 3, x.shape[2]))
+    out, _ = conv(x, w, bias, st0, False)
+    full, _ = conv(np.concatenate([st0, x], axis=1), w, bias, None, False)
+    assert _rel(out, full[:, 3:]) < 1e-15
+
+
+CONV_CHECKS = [check_conv_numpy_convolve, check_conv_impulse, check_conv_silu, check_conv_continuation,
+               check_conv_state_is_history]
+
+
 # --- gradients of the scan ------------------------------------------------------------------
 # scan_from(u, x, A, B, C, D, z, bias, softplus, h0) -> (y, last_state)
 # scan_bwd(u, x, A, B, C, dy, D, z, bias, softplus, h0, dlast) -> dict of gradients

@@ -49,6 +49,16 @@ MUTANTS = {
     "zoh_wrong_limit": ("return a != 0.0 ? expm1(dt * a) / a : dt;", "return a != 0.0 ? expm1(dt * a) / a : 0.0;"),
     "zoh_decay_from_coefficient": ("h[n] = exp(dt * a) * h[n] + oracle_zoh_coef(dt, a) * Bt[n] * ut;",
                                    "h[n] = exp(-dt * a) * h[n] + oracle_zoh_coef(dt, a) * Bt[n] * ut;"),
+    "conv_reversed_taps": ("acc = acc + w[d * width + k] * hist[t + k];",
+                           "acc = acc + w[d * width + (width - 1 - k)] * hist[t + k];"),
+    "conv_window_one_late": ("acc = acc + w[d * width + k] * hist[t + k];",
+                             "acc = acc + w[d * width + k] * hist[t + k > 0 ? t + k - 1 : 0];"),
+    "conv_drop_bias": ("double acc = bias ? bias[d] : 0.0;", "double acc = 0.0;"),
+    "conv_drop_silu": ("out[(b * L + t) * D + d] = silu ? oracle_silu(acc) : acc;",
+                       "out[(b * L + t) * D + d] = acc;"),
+    "conv_ignore_state": ("hist[r] = state ? state[(b * H + r) * D + d] : 0.0;", "hist[r] = 0.0;"),
+    "conv_state_out_oldest_rows": ("state_out[(b * H + r) * D + d] = hist[L + r];",
+                                   "state_out[(b * H + r) * D + d] = hist[r];"),
     "decay_squared": ("h[n] = dA * h[n] + dt * Bt[n] * ut;", "h[n] = dA * dA * h[n] + dt * Bt[n] * ut;"),
 }
 
@@ -71,6 +81,8 @@ def _build_mutant(tmp_path, name, old, new):
     lib.ssm_oracle_scan_from.restype = ctypes.c_int
     lib.ssm_oracle_scan_bwd.argtypes = [I64, I64, I64, I64] + [P] * 9 + [ctypes.c_int] + [P] * 11 + [ctypes.c_int]
     lib.ssm_oracle_scan_bwd.restype = ctypes.c_int
+    lib.ssm_oracle_conv1d.argtypes = [I64, I64, I64, I64, P, P, P, P, ctypes.c_int, P, P]
+    lib.ssm_oracle_conv1d.restype = ctypes.c_int
 
     def f64(a):
         return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
@@ -119,13 +131,22 @@ def _build_mutant(tmp_path, name, old, new):
                                 ptr(out["ddelta"]), ptr(out["dA"]), ptr(out["dB"]), ptr(out["dC"]), ptr(out["dD"]),
                                 ptr(out["dz"]), ptr(out["ddelta_bias"]), ptr(out["dh0"]), 1)
         return out
-    return scan, scan_from, scan_bwd, scan_zoh
+    def conv(x, w, bias, state, silu):
+        x, w, bias, state = map(f64, (x, w, bias, state))
+        bsz, L, Dch = x.shape
+        width = w.shape[1]
+        out = np.empty((bsz, L, Dch))
+        st = np.empty((bsz, width - 1, Dch))
+        lib.ssm_oracle_conv1d(bsz, L, Dch, width, ptr(x), ptr(w), ptr(bias), ptr(state), int(bool(silu)), ptr(out),
+                              ptr(st))
+        return out, st
+    return scan, scan_from, scan_bwd, scan_zoh, conv
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(tmp_path, name):
     old, new = MUTANTS[name]
-    scan, scan_from, scan_bwd, scan_zoh = _build_mutant(tmp_path, name, old, new)
+    scan, scan_from, scan_bwd, scan_zoh, conv = _build_mutant(tmp_path, name, old, new)
     caught = []
     with np.errstate(all="ignore"):
         for check in pins.ALL_CHECKS:
@@ -141,6 +162,11 @@ def test_planted_mistake_is_caught(tmp_path, name):
         for check in pins.ZOH_CHECKS:
             try:
                 check(scan_zoh)
+            except AssertionError:
+                caught.append(check.__name__)
+        for check in pins.CONV_CHECKS:
+            try:
+                check(conv)
             except AssertionError:
                 caught.append(check.__name__)
         for check in pins.BWD_CHECKS:

@@ -28,6 +28,17 @@ def test_oracle_zoh_pin(oracle_mod, check):
     check(_scan_zoh(oracle_mod))
 
 
+def _conv(oracle_mod):
+    def f(x, w, bias, state, silu):
+        return oracle_mod.conv1d(x, w, bias=bias, state=state, silu=silu)
+    return f
+
+
+@pytest.mark.parametrize("check", pins.CONV_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_conv_pin(oracle_mod, check):
+    check(_conv(oracle_mod))
+
+
 def test_oracle_bwd_rejects_zoh(oracle_mod):
     """The oracle's gradients cover the simplified input term only."""
     lib = oracle_mod._load()
