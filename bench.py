@@ -44,6 +44,7 @@ WORKLOADS = {
     "c3_bwd": "selective scan backward B8 L2048 D5120 N16, bf16 I/O, fp32 state, SiLU(z) gate, D skip",
     "c3_zoh": "selective scan with the exact zero-order-hold input term B8 L2048 D5120 N16, bf16 I/O, "
               "fp32 state, SiLU(z) gate, D skip, last_state",
+    "c3_conv": "causal depthwise conv1d (width 4) + SiLU B8 L2048 D5120, bf16 I/O, conv state out",
 }
 # The exact zero-order-hold input term adds, per (token, channel, state), one evaluation of
 # (exp(delta A) - 1) / A counted as a transcendental (2 slots) and its multiply (1 slot).
@@ -158,6 +159,34 @@ def cpu_baseline_bwd(case, alg_bytes_full, target_s=20.0):
                       f"(fp64 oracle backward, OpenMP over channels)"}
 
 
+def conv_alg_bytes(bsz, L, D, width, io_bytes):
+    """x read and out written per element, the state rows written, w and bias read."""
+    return bsz * L * D * io_bytes * 2 + bsz * (width - 1) * D * io_bytes + D * (width + 1) * 4
+
+
+def cpu_baseline_conv(case, alg_bytes_full, target_s=20.0):
+    """The fp64 oracle's convolution on a channel sample of the workload (channels are
+    independent; single-threaded)."""
+    from oracle import oracle
+    oracle.build(force=False)
+
+    def run(sel):
+        oracle.conv1d(case.values("x")[:, :, sel], case.w[sel], bias=case.bias[sel],
+                      state=None if case.state is None else case.values("state")[:, :, sel], silu=True)
+    probe = np.arange(64)
+    t = time.perf_counter()
+    run(probe)
+    per_ch = (time.perf_counter() - t) / len(probe)
+    k = int(min(case.D, max(64, target_s / max(per_ch, 1e-9))))
+    sel = np.unique(np.linspace(0, case.D - 1, k).astype(np.int64))
+    t = time.perf_counter()
+    run(sel)
+    dt = time.perf_counter() - t
+    return {"value": round(alg_bytes_full * len(sel) / case.D / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{len(sel)} of {case.D} channels x all {case.bsz} sequences x {case.L} tokens (fp64 oracle)"}
+
+
 def cpu_baseline_step(case, alg_bytes_step, target_s=20.0):
     from oracle import oracle
     oracle.build(force=False)
@@ -206,7 +235,10 @@ def main():
 
     dev = "cuda"
     wl = args.workload
-    case = inputs.config_case("c3" if wl in ("c3_bwd", "c3_zoh") else wl)
+    if wl == "c3_conv":
+        case = inputs.conv_case(8, 2048, 5120, 4, "bf16", state=True, seed=185, name="c3_conv")
+    else:
+        case = inputs.config_case("c3" if wl in ("c3_bwd", "c3_zoh") else wl)
     io_bytes = 2 if case.io == "bf16" else 4
 
     def td(a):
@@ -234,6 +266,20 @@ def main():
         def one(i):
             calls[i % case.steps]()
         plan = "one step kernel per call"
+    elif wl == "c3_conv":
+        bsz, L, D, width = case.bsz, case.L, case.D, case.width
+        x, st_in = td(case.x), td(case.state)
+        out = torch.empty_like(x)
+        st_out = torch.empty_like(st_in)
+        alg = conv_alg_bytes(bsz, L, D, width, io_bytes)
+        chtok = bsz * L * D
+        elements = chtok
+        td_w, td_b = td(case.w), td(case.bias)
+        call = ssmscan.conv1d_call(x, td_w, td_b, st_in, silu=True, out=out, state_out=st_out)
+
+        def one(i):
+            call()
+        plan = "one kernel, runs of 16 tokens x 8 channels per thread"
     elif wl == "c3_bwd":
         t = {k: td(getattr(case, f)) for k, f in (("u", "u"), ("delta", "delta"), ("A", "A"), ("B", "B"),
                                                    ("C", "C"), ("D", "Dskip"), ("z", "z"), ("bias", "delta_bias"))}
@@ -278,17 +324,21 @@ def main():
     for i in range(args.warmup):
         one(i)
     torch.cuda.synchronize()
-    if wl == "c5":
-        # A decode step is a ~35 us kernel, shorter than the host's cost per call: the K timed
-        # steps are captured once as a HIP graph (the library allocates and synchronises
-        # nothing, so its launches capture as they are) and replayed as one submission.
+    if wl in ("c5", "c3_conv"):
+        # A decode step (~35 us) or the convolution (~65 us) is short next to the host's cost
+        # per call: the K timed steps are captured once as a HIP graph (the library allocates
+        # and synchronises nothing, so its launches capture as they are) and replayed as one
+        # submission.
         graph = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
         cap.wait_stream(stream)
         with torch.cuda.graph(graph, stream=cap):
             for i in range(args.steps):
-                u, dl, Bk, Ck, z = ins[i % case.steps]
-                ssmscan.step(st, u, dl, A, Bk, Ck, D=Dv, z=z, y=y)
+                if wl == "c5":
+                    u, dl, Bk, Ck, z = ins[i % case.steps]
+                    ssmscan.step(st, u, dl, A, Bk, Ck, D=Dv, z=z, y=y)
+                else:
+                    ssmscan.conv1d(x, td_w, td_b, st_in, silu=True, out=out, state_out=st_out, stream=cap)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
@@ -318,7 +368,7 @@ def main():
     slots = {"c3_bwd": SLOTS_PER_ELEMENT_BWD, "c3_zoh": SLOTS_PER_ELEMENT_ZOH}.get(wl, SLOTS_PER_ELEMENT)
     lane_ops = elements * slots / kern_s / 1e12
     traffic = counter_traffic(wl)
-    if wl == "c5":
+    if wl in ("c5", "c3_conv"):
         roof = {"bound": "hbm", "achieved": round(kern_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(kern_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
     else:
@@ -331,6 +381,7 @@ def main():
     if not args.no_cpu:
         try:
             cpu = (cpu_baseline_step(case, alg) if wl == "c5" else cpu_baseline_bwd(case, alg) if wl == "c3_bwd"
+                   else cpu_baseline_conv(case, alg) if wl == "c3_conv"
                    else cpu_baseline_scan(case, alg, exact_zoh=wl == "c3_zoh"))
         except Exception as e:  # the GPU figures stand without it
             cpu = {"error": repr(e)}

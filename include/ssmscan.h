@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SSMSCAN_VERSION 4
+#define SSMSCAN_VERSION 5
 
 /* Bits of the `flags` argument of the scan entry points. */
 #define SSM_SCAN_SOFTPLUS 1     /* step size = softplus(delta + delta_bias) */
@@ -177,6 +177,31 @@ SSMSCAN_API int ssm_scan_bwd(const float *initial_state, const void *u, const vo
                  float *dA, float *dB, float *dC, float *dD, void *dz, float *ddelta_bias,
                  float *dinitial_state, const ssm_dims *dims, void *workspace, size_t workspace_bytes,
                  void *stream);
+
+/* Bits of the `flags` argument of ssm_conv1d_fwd. */
+#define SSM_CONV_SILU 1         /* apply SiLU to the convolution's output */
+
+/* The causal depthwise convolution over time that feeds the scan in the block's main
+ * branch, with SiLU: a short 1-D convolution of kernel size 4, then SiLU, before the
+ * selective SSM (azimuth.plus/paper/mamba, block architecture section).
+ *   out[b,t,d] = silu(bias[d] + sum_{k < width} w[d,k] * x[b, t - (width-1) + k, d])
+ * (without SSM_CONV_SILU the pre-activation itself).
+ *   x, out       : [batch][seqlen][dim] (io_dtype)
+ *   w            : [dim][width] fp32; width 1 to 4 (the pages' kernel size is 4)
+ *   bias         : [dim] fp32, or NULL (= 0)
+ *   state_in     : [batch][width-1][dim] (io_dtype), the width-1 inputs before token 0,
+ *                  oldest first, or NULL (= zeros: the start of a sequence)
+ *   state_out    : [batch][width-1][dim] (io_dtype), receives the last width-1 inputs of
+ *                  (state_in, x) -- the state that continues the sequence -- or NULL.  It may
+ *                  be the state_in buffer (advanced in place; then one thread per channel group
+ *                  walks the whole sequence, so use it for short calls such as a decode step);
+ *                  it must not overlap any other argument.
+ * dims->dstate and dims->chunk_len are ignored.  With seqlen 0, state_out receives state_in
+ * (zeros without it).  Running a sequence in pieces, each from the previous piece's
+ * state_out, gives the run over the whole sequence bitwise.  Unknown flag bits return
+ * SSM_ERR_FLAGS; a width outside 1..4 returns SSM_ERR_SHAPE. */
+SSMSCAN_API int ssm_conv1d_fwd(const void *x, const float *w, const float *bias, int width, const void *state_in,
+                   int flags, void *out, void *state_out, const ssm_dims *dims, void *stream);
 
 /* One recurrent (inference) step for `batch` independent sequences: the constant-memory
  * recurrent form (shakilmahmud.com section 3; urworte.de "Methodische Grundlagen").

@@ -13,6 +13,7 @@
 #include "scan_kernels.h"
 #include "step_kernel.h"
 #include "bwd_kernel.h"
+#include "conv_kernel.h"
 
 namespace {
 
@@ -321,6 +322,54 @@ int dispatch_bwd(int64_t N, const BwdArgs &a, const ssm_dims *dm, void *ws, hipS
     return fail(SSM_ERR_UNSUPPORTED_N, "dstate %lld not supported", (long long)N);
 }
 
+// --- the causal depthwise convolution of the block's main branch ---------------------------
+
+template <typename IO, int W, bool VEC, bool SILU>
+void launch_conv_w(const IO *x, const float *w, const float *bias, const IO *st_in, IO *out, IO *st_out,
+                   const ssm_dims *dm, hipStream_t st) {
+    constexpr int V = VEC ? ssm::kConvVec : 1;
+    const int64_t bsz = dm->batch, L = dm->seqlen, D = dm->dim;
+    // a state updated in place is read and written by the same thread: one run per sequence
+    const bool in_place = st_out && st_out == st_in && W > 1;
+    const int64_t R = in_place ? L : ssm::kConvRun;
+    const int64_t runs = (L + R - 1) / R;
+    const int64_t groups = D / V;
+    const int64_t pairs = bsz * runs;
+    const dim3 grid((unsigned)((groups + 255) / 256), (unsigned)std::min<int64_t>(pairs, 65535));
+    hipLaunchKernelGGL((ssm::conv1d_kernel<IO, W, V, VEC, SILU>), grid, dim3(256), 0, st, x, w, bias, st_in, out,
+                       st_out, L, D, groups, runs, pairs, (int)R);
+}
+
+template <typename IO, bool VEC, bool SILU>
+void launch_conv_v(int width, const IO *x, const float *w, const float *bias, const IO *st_in, IO *out,
+                   IO *st_out, const ssm_dims *dm, hipStream_t st) {
+    switch (width) {
+        case 1: launch_conv_w<IO, 1, VEC, SILU>(x, w, bias, st_in, out, st_out, dm, st); break;
+        case 2: launch_conv_w<IO, 2, VEC, SILU>(x, w, bias, st_in, out, st_out, dm, st); break;
+        case 3: launch_conv_w<IO, 3, VEC, SILU>(x, w, bias, st_in, out, st_out, dm, st); break;
+        default: launch_conv_w<IO, 4, VEC, SILU>(x, w, bias, st_in, out, st_out, dm, st); break;
+    }
+}
+
+template <typename IO>
+int launch_conv(int width, bool silu, const void *x, const float *w, const float *bias, const void *st_in,
+                void *out, void *st_out, const ssm_dims *dm, hipStream_t st) {
+    const IO *x_ = static_cast<const IO *>(x);
+    const IO *si = static_cast<const IO *>(st_in);
+    IO *o = static_cast<IO *>(out);
+    IO *so = static_cast<IO *>(st_out);
+    const size_t va = ssm::kConvVec * sizeof(IO);   // bytes of one vector access
+    const bool vec = dm->dim % ssm::kConvVec == 0 && aligned(x, va) && aligned(out, va) &&
+                     (!st_in || aligned(st_in, va)) && (!st_out || aligned(st_out, va));
+    if (vec && silu) launch_conv_v<IO, true, true>(width, x_, w, bias, si, o, so, dm, st);
+    else if (vec) launch_conv_v<IO, true, false>(width, x_, w, bias, si, o, so, dm, st);
+    else if (silu) launch_conv_v<IO, false, true>(width, x_, w, bias, si, o, so, dm, st);
+    else launch_conv_v<IO, false, false>(width, x_, w, bias, si, o, so, dm, st);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // namespace
 
 static int scan_impl(const float *h0, const void *u, const void *delta, const float *A, const void *B,
@@ -491,6 +540,55 @@ int ssm_scan_bwd(const float *initial_state, const void *u, const void *delta, c
               dA, dB, dC, dD, dz, ddelta_bias, dinitial_state};
     if (dims->io_dtype == SSM_IO_BF16) return dispatch_bwd<uint16_t>(N, a, dims, workspace, st);
     return dispatch_bwd<float>(N, a, dims, workspace, st);
+}
+
+int ssm_conv1d_fwd(const void *x, const float *w, const float *bias, int width, const void *state_in, int flags,
+                   void *out, void *state_out, const ssm_dims *dims, void *stream) {
+    if (!dims) return fail(SSM_ERR_NULL, "dims is NULL");
+    ssm_dims d = *dims;   // dstate and chunk_len do not apply
+    d.dstate = 1;
+    d.chunk_len = 0;
+    int rc = check_dims(&d, true);
+    if (rc != SSM_OK) return rc;
+    if (width < 1 || width > 4) return fail(SSM_ERR_SHAPE, "conv width %d not supported (1 to 4)", width);
+    if (flags & ~SSM_CONV_SILU) return fail(SSM_ERR_FLAGS, "unknown flag bits 0x%x", flags);
+    const int64_t bsz = d.batch, L = d.seqlen, Dm = d.dim, H = width - 1;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const size_t es = d.io_dtype == SSM_IO_BF16 ? 2 : 4;
+    if (!aligned(x, es) || !aligned(out, es) || !aligned(state_in, es) || !aligned(state_out, es) ||
+        !aligned(w, 4) || !aligned(bias, 4))
+        return fail(SSM_ERR_ALIGN, "a tensor pointer is not aligned to its element size");
+    if (bsz == 0 || Dm == 0) return ok();
+    if (!w) return fail(SSM_ERR_NULL, "w is NULL");
+    if (L == 0) {
+        // no tokens: the state passes through (zero without one)
+        if (state_out && state_out != state_in && H > 0) {
+            const int64_t n = bsz * H * Dm;
+            const dim3 grid((unsigned)((n + 255) / 256));
+            if (es == 2) {
+                if (state_in)
+                    hipLaunchKernelGGL(ssm::copy_kernel<uint16_t>, grid, dim3(256), 0, st,
+                                       static_cast<uint16_t *>(state_out), static_cast<const uint16_t *>(state_in), n);
+                else
+                    hipLaunchKernelGGL(ssm::fill_zero_kernel<uint16_t>, grid, dim3(256), 0, st,
+                                       static_cast<uint16_t *>(state_out), n);
+            } else {
+                if (state_in)
+                    hipLaunchKernelGGL(ssm::copy_kernel<float>, grid, dim3(256), 0, st, static_cast<float *>(state_out),
+                                       static_cast<const float *>(state_in), n);
+                else
+                    hipLaunchKernelGGL(ssm::fill_zero_kernel<float>, grid, dim3(256), 0, st,
+                                       static_cast<float *>(state_out), n);
+            }
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+        }
+        return ok();
+    }
+    if (!x || !out) return fail(SSM_ERR_NULL, "x or out is NULL");
+    const bool silu = (flags & SSM_CONV_SILU) != 0;
+    if (es == 2) return launch_conv<uint16_t>(width, silu, x, w, bias, state_in, out, state_out, &d, st);
+    return launch_conv<float>(width, silu, x, w, bias, state_in, out, state_out, &d, st);
 }
 
 }  // extern "C"

@@ -24,7 +24,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "bf16_bits", "bf16_to_f32", "ScanCase", "StepCase", "scan_case", "step_case",
+    "bf16_bits", "bf16_to_f32", "ScanCase", "StepCase", "ConvCase", "scan_case", "step_case", "conv_case",
     "config_case", "CONFIGS",
 ]
 
@@ -197,6 +197,43 @@ def step_case(S: int, D: int, N: int, steps: int, io: str = "bf16", *, gate: boo
                     steps=steps, state0=state0, u=_io(u, io), delta=_io(delta, io), A=A,
                     B=_io(Bm, io), C=_io(Cm, io), Dskip=Dskip,
                     z=None if z is None else _io(z, io), seed=seed)
+
+
+@dataclasses.dataclass
+class ConvCase:
+    """Inputs of one causal depthwise convolution call.  x: [bsz][L][D] (io); w: [D][width]
+    fp32; bias: [D] fp32; state: [bsz][width-1][D] (io) or None."""
+    name: str
+    io: str
+    bsz: int
+    L: int
+    D: int
+    width: int
+    x: np.ndarray
+    w: np.ndarray
+    bias: Optional[np.ndarray]
+    state: Optional[np.ndarray]
+    seed: int
+
+    def values(self, field: str) -> Optional[np.ndarray]:
+        a = getattr(self, field)
+        if a is None:
+            return None
+        return bf16_to_f32(a) if a.dtype == np.uint16 else a
+
+
+def conv_case(bsz: int, L: int, D: int, width: int = 4, io: str = "bf16", *, bias: bool = True,
+              state: bool = False, seed: int = 0, name: str = "conv") -> ConvCase:
+    """Draw order w, bias, x, state.  w and bias ~ U(-1/sqrt(width), 1/sqrt(width)) (the
+    default uniform initialisation of a depthwise convolution, fan-in = width); x ~ N(0, 1)
+    (the projected block input); state ~ N(0, 1) rows of earlier inputs."""
+    rng = np.random.default_rng(seed)
+    lim = 1.0 / np.sqrt(width)
+    w = rng.uniform(-lim, lim, (D, width)).astype(np.float32)
+    b = rng.uniform(-lim, lim, D).astype(np.float32) if bias else None
+    x = _io(rng.standard_normal((bsz, L, D), dtype=np.float32), io)
+    st = _io(rng.standard_normal((bsz, width - 1, D), dtype=np.float32), io) if state else None
+    return ConvCase(name, io, bsz, L, D, width, x, w, b, st, seed)
 
 
 # The five measured workloads (plus the LTI variant of the tiny one).

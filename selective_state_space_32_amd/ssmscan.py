@@ -57,6 +57,8 @@ def _load() -> ctypes.CDLL:
     lib.ssm_scan_bwd.restype = ctypes.c_int
     lib.ssm_step.argtypes = [P, P, P, P, P, P, P, P, P, D, P]
     lib.ssm_step.restype = ctypes.c_int
+    lib.ssm_conv1d_fwd.argtypes = [P, P, P, ctypes.c_int, P, ctypes.c_int, P, P, D, P]
+    lib.ssm_conv1d_fwd.restype = ctypes.c_int
     return lib
 
 
@@ -334,4 +336,62 @@ def step_call(state: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torc
 
     def call(_args=args, _keep=keep):
         _check(lib.ssm_step(*_args))
+    return call
+
+
+CONV_SILU = 1   # flag bit of ssm_conv1d_fwd (include/ssmscan.h)
+
+
+def _conv_args(x, w, bias, state, silu, out, state_out, return_state, stream):
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, L, dim)")
+    bsz, L, dim = x.shape
+    if w.dim() != 2 or w.shape[0] != dim:
+        raise ValueError("w must be (dim, width)")
+    width = int(w.shape[1])
+    dev, io = x.device, x.dtype
+    _io_code(io)
+    _need(w, "w", (dim, width), torch.float32, dev)
+    if bias is not None:
+        _need(bias, "bias", (dim,), torch.float32, dev)
+    if state is not None:
+        _need(state, "state", (bsz, width - 1, dim), io, dev)
+    if out is None:
+        out = torch.empty((bsz, L, dim), dtype=io, device=dev)
+    else:
+        _need(out, "out", (bsz, L, dim), io, dev)
+    if state_out is None and return_state:
+        state_out = torch.empty((bsz, width - 1, dim), dtype=io, device=dev)
+    elif state_out is not None:
+        _need(state_out, "state_out", (bsz, width - 1, dim), io, dev)
+    dims = make_dims(bsz, L, dim, 1, io)
+    args = (_ptr(x), _ptr(w), _ptr(bias), width, _ptr(state), CONV_SILU if silu else 0, _ptr(out), _ptr(state_out),
+            ctypes.byref(dims), _stream_handle(stream))
+    keep = (x, w, bias, state, out, state_out, dims)
+    return args, keep, out, state_out
+
+
+def conv1d(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None,
+           state: Optional[torch.Tensor] = None, silu: bool = True, *, out: Optional[torch.Tensor] = None,
+           state_out: Optional[torch.Tensor] = None, return_state: bool = True, stream=None):
+    """Causal depthwise convolution over time, then SiLU (ssm_conv1d_fwd).
+
+    x: (batch, L, dim) float32 or bfloat16; w: (dim, width) float32, width 1..4; bias: (dim,)
+    float32; state: (batch, width-1, dim) of x's dtype, the inputs before token 0 (None = zeros).
+    Returns (out (batch, L, dim), state_out (batch, width-1, dim) or None); state_out may be
+    `state` itself (advanced in place)."""
+    args, _keep, out, state_out = _conv_args(x, w, bias, state, silu, out, state_out, return_state, stream)
+    _check(lib.ssm_conv1d_fwd(*args))
+    return out, state_out
+
+
+def conv1d_call(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                state: Optional[torch.Tensor] = None, silu: bool = True, *, out: Optional[torch.Tensor] = None,
+                state_out: Optional[torch.Tensor] = None, return_state: bool = True,
+                stream=None) -> Callable[[], None]:
+    """The conv1d call checked and marshalled once (see scan_fwd_call)."""
+    args, keep, _o, _s = _conv_args(x, w, bias, state, silu, out, state_out, return_state, stream)
+
+    def call(_args=args, _keep=keep):
+        _check(lib.ssm_conv1d_fwd(*_args))
     return call

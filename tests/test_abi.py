@@ -28,6 +28,7 @@ def b():
 def test_header_declares_the_entry_points():
     syms = set(declared_symbols())
     assert {"ssm_scan_fwd", "ssm_scan_fwd_from", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes", "ssm_step",
+            "ssm_conv1d_fwd",
             "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_last_error", "ssm_version"} <= syms
 
 
@@ -144,6 +145,22 @@ def test_flags_validated(b):
         assert rc == -8 and "flag" in b.last_error()
     assert _bwd(b, d, softplus=3) == -8 and "ZOH" in b.last_error()
     assert _bwd(b, d, softplus=2) == -8
+
+
+def test_conv_validation(b):
+    # every rejection happens before any launch
+    P = ctypes.c_void_p
+    d = _dims(b, dstate=3)           # dstate does not apply to the convolution
+
+    def conv(width=4, flags=1, x=FAKE, out=FAKE, w=FAKE, si=None, so=None, dims=d):
+        return b.lib.ssm_conv1d_fwd(P(x), P(w), None, width, P(si) if si else None, flags, P(out),
+                                    P(so) if so else None, ctypes.byref(dims), None)
+    assert conv(width=0) == -2 and conv(width=5) == -2
+    assert conv(flags=2) == -8
+    assert conv(x=FAKE + 1) == -4
+    assert conv(w=0) == -1
+    assert conv(out=0) == -1
+    assert conv(dims=_dims(b, io_dtype=5)) == -3
 
 
 def test_misaligned_rejected(b):
