@@ -45,7 +45,12 @@ WORKLOADS = {
     "c3_zoh": "selective scan with the exact zero-order-hold input term B8 L2048 D5120 N16, bf16 I/O, "
               "fp32 state, SiLU(z) gate, D skip, last_state",
     "c3_conv": "causal depthwise conv1d (width 4) + SiLU B8 L2048 D5120, bf16 I/O, conv state out",
+    "c3_block": "conv1d (width 4) + SiLU fused into the selective scan B8 L2048 D5120 N16, bf16 I/O, fp32 state, "
+                "SiLU(z) gate, D skip, last_state",
 }
+# The fused convolution adds, per (token, channel), 4 FMAs and SiLU (multiply, exp2 at half
+# rate, add, reciprocal at half rate): 10 issue slots.
+SLOTS_PER_CHTOK_CONV = 10
 # The exact zero-order-hold input term adds, per (token, channel, state), one evaluation of
 # (exp(delta A) - 1) / A counted as a transcendental (2 slots) and its multiply (1 slot).
 SLOTS_PER_ELEMENT_ZOH = SLOTS_PER_ELEMENT + 3
@@ -187,6 +192,32 @@ def cpu_baseline_conv(case, alg_bytes_full, target_s=20.0):
             "sample": f"{len(sel)} of {case.D} channels x all {case.bsz} sequences x {case.L} tokens (fp64 oracle)"}
 
 
+def cpu_baseline_block(case, cc, alg_bytes_full, target_s=20.0):
+    """The fp64 oracle's convolution followed by its scan, on a channel sample."""
+    from oracle import oracle
+    oracle.build(force=False)
+    threads = min(16, oracle.default_threads())
+
+    def run(sel):
+        u, _ = oracle.conv1d(cc.values("x")[:, :, sel], cc.w[sel], bias=cc.bias[sel], silu=True)
+        oracle.scan(u, case.values("delta")[:, :, sel], case.A[sel], case.values("B"), case.values("C"),
+                    D=case.Dskip[sel], z=case.values("z")[:, :, sel], delta_bias=case.delta_bias[sel],
+                    softplus=case.softplus, threads=threads)
+    probe = np.arange(16)
+    t = time.perf_counter()
+    run(probe)
+    per_ch = (time.perf_counter() - t) / len(probe)
+    k = int(min(case.D, max(16, target_s / max(per_ch, 1e-9))))
+    sel = np.unique(np.linspace(0, case.D - 1, k).astype(np.int64))
+    t = time.perf_counter()
+    run(sel)
+    dt = time.perf_counter() - t
+    return {"value": round(alg_bytes_full * len(sel) / case.D / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{len(sel)} of {case.D} channels x all {case.bsz} sequences x {case.L} tokens "
+                      f"(fp64 oracle convolution, then scan)"}
+
+
 def cpu_baseline_step(case, alg_bytes_step, target_s=20.0):
     from oracle import oracle
     oracle.build(force=False)
@@ -238,7 +269,7 @@ def main():
     if wl == "c3_conv":
         case = inputs.conv_case(8, 2048, 5120, 4, "bf16", state=True, seed=185, name="c3_conv")
     else:
-        case = inputs.config_case("c3" if wl in ("c3_bwd", "c3_zoh") else wl)
+        case = inputs.config_case("c3" if wl in ("c3_bwd", "c3_zoh", "c3_block") else wl)
     io_bytes = 2 if case.io == "bf16" else 4
 
     def td(a):
@@ -310,15 +341,25 @@ def main():
         chtok = bsz * L * D
         elements = chtok * N
 
-        call = ssmscan.scan_fwd_call(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
-                                     delta_bias=t["bias"], softplus=case.softplus, y=y, last_state=ls, workspace=ws,
-                                     exact_zoh=wl == "c3_zoh")
+        if wl == "c3_block":
+            # the block's projected input x in place of u, width-4 convolution weights
+            cc = inputs.conv_case(bsz, L, D, 4, case.io, seed=4, name="c3_block")
+            call = ssmscan.scan_fwd_conv_call(td(cc.x), td(cc.w), td(cc.bias), t["delta"], t["A"], t["B"], t["C"],
+                                              D=t["D"], z=t["z"], delta_bias=t["bias"], softplus=case.softplus, y=y,
+                                              last_state=ls, workspace=ws)
+            alg += D * 5 * 4   # the convolution's taps and bias
+        else:
+            call = ssmscan.scan_fwd_call(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                         delta_bias=t["bias"], softplus=case.softplus, y=y, last_state=ls,
+                                         workspace=ws, exact_zoh=wl == "c3_zoh")
 
         def one(i):
             call()
         plan = "single pass" if nchunk == 1 else f"{nchunk} chunks of {clen} tokens (summary + carry + scan)"
         if wl == "c3_zoh":
             plan += ", exact zero-order-hold input term"
+        if wl == "c3_block":
+            plan += ", convolution + SiLU in the scan's preparation"
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
@@ -366,7 +407,8 @@ def main():
     gbps = alg / step_s / 1e9          # whole-job throughput over the timed region
     kern_gbps = alg / kern_s / 1e9     # the kernel's own rate (event-timed launches)
     slots = {"c3_bwd": SLOTS_PER_ELEMENT_BWD, "c3_zoh": SLOTS_PER_ELEMENT_ZOH}.get(wl, SLOTS_PER_ELEMENT)
-    lane_ops = elements * slots / kern_s / 1e12
+    work_ops = elements * slots + (chtok * SLOTS_PER_CHTOK_CONV if wl == "c3_block" else 0)
+    lane_ops = work_ops / kern_s / 1e12
     traffic = counter_traffic(wl)
     if wl in ("c5", "c3_conv"):
         roof = {"bound": "hbm", "achieved": round(kern_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -375,13 +417,16 @@ def main():
         roof = {"bound": "alu", "achieved": round(lane_ops, 3), "peak": round(VALU_PEAK_TLANEOPS, 3),
                 "unit": "T fp32 VALU lane-ops/s", "frac": round(lane_ops / VALU_PEAK_TLANEOPS, 4),
                 "traffic": traffic,
-                "work": f"{slots} VALU issue slots per (token, channel, state) x {elements} per launch"}
+                "work": f"{slots} VALU issue slots per (token, channel, state) x {elements} per launch"
+                        + (f" + {SLOTS_PER_CHTOK_CONV} per (token, channel) x {chtok} for the convolution"
+                           if wl == "c3_block" else "")}
 
     cpu = None
     if not args.no_cpu:
         try:
             cpu = (cpu_baseline_step(case, alg) if wl == "c5" else cpu_baseline_bwd(case, alg) if wl == "c3_bwd"
                    else cpu_baseline_conv(case, alg) if wl == "c3_conv"
+                   else cpu_baseline_block(case, cc, alg) if wl == "c3_block"
                    else cpu_baseline_scan(case, alg, exact_zoh=wl == "c3_zoh"))
         except Exception as e:  # the GPU figures stand without it
             cpu = {"error": repr(e)}

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SSMSCAN_VERSION 5
+#define SSMSCAN_VERSION 6
 
 /* Bits of the `flags` argument of the scan entry points. */
 #define SSM_SCAN_SOFTPLUS 1     /* step size = softplus(delta + delta_bias) */
@@ -202,6 +202,24 @@ SSMSCAN_API int ssm_scan_bwd(const float *initial_state, const void *u, const vo
  * SSM_ERR_FLAGS; a width outside 1..4 returns SSM_ERR_SHAPE. */
 SSMSCAN_API int ssm_conv1d_fwd(const void *x, const float *w, const float *bias, int width, const void *state_in,
                    int flags, void *out, void *state_out, const ssm_dims *dims, void *stream);
+
+/* The causal convolution + SiLU fused into the scan: the block's main branch from its
+ * projected input x to y in one pass (azimuth.plus/paper/mamba, block architecture section:
+ * 1-D convolution of kernel size 4, SiLU, selective SSM, times the SiLU gate).  Computes
+ *   u = silu(conv_b + conv of x with conv_w)   (as ssm_conv1d_fwd, from a zero history)
+ * inside the scan kernel and scans it exactly as ssm_scan_fwd would scan u, without
+ * storing u unless u_out is given.  u stays fp32 inside (the two-call path rounds it to
+ * io_dtype in between).
+ *   x              : [batch][seqlen][dim] (io_dtype), the block's projected input
+ *   conv_w, conv_b : [dim][4], [dim] fp32 (conv_b may be NULL);  conv_width must be 4
+ *   u_out          : [batch][seqlen][dim] (io_dtype) receives u (for the backward pass), or NULL
+ *   flags          : SSM_SCAN_SOFTPLUS only (the exact ZOH is not available here: SSM_ERR_FLAGS)
+ * Every other argument, the workspace and the errors are those of ssm_scan_fwd. */
+SSMSCAN_API int ssm_scan_fwd_conv(const void *x, const float *conv_w, const float *conv_b, int conv_width,
+                      const void *delta, const float *A, const void *B, const void *C, const float *D,
+                      const void *z, const float *delta_bias, int flags, void *y, float *last_state,
+                      void *u_out, const ssm_dims *dims, void *workspace, size_t workspace_bytes,
+                      void *stream);
 
 /* One recurrent (inference) step for `batch` independent sequences: the constant-memory
  * recurrent form (shakilmahmud.com section 3; urworte.de "Methodische Grundlagen").

@@ -83,7 +83,15 @@ __device__ __forceinline__ void load_slice(const IO *__restrict__ p, int64_t off
 //        z, y.  Otherwise one element per access.
 //   ZOH: the input term is the exact zero-order hold (exp(delta A) - 1) / A * B * u
 //        instead of delta * B * u (the decay is the same).
-template <int N, int S, int T, typename IO, int MODE, bool VEC, bool ZOH = false>
+//   CW:  0, or the width of a causal depthwise convolution + SiLU that produces the scan's
+//        input in the kernel: `u` then holds the block's projected input x, and
+//        u_t = silu(cb + sum_k cw[k] x_{t-CW+1+k}) (azimuth.plus/paper/mamba, block
+//        architecture section), from a zero history before token 0; u_out (if not null)
+//        receives it.  The x rows of a tile go into an LDS ring of T + CW - 1 rows (the
+//        tile and the CW - 1 rows before it), filled one tile ahead from the prefetched
+//        registers; a conv phase with lane = channel (each wave takes the rows its own
+//        threads prepare, its CW taps in registers) writes u where the prep reads it.
+template <int N, int S, int T, typename IO, int MODE, bool VEC, bool ZOH = false, int CW = 0>
 __global__ void __launch_bounds__(64 * (N / S))
 scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                   const IO *__restrict__ z, IO *__restrict__ y,
@@ -91,7 +99,9 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                   const float *__restrict__ bias, const IO *__restrict__ Bm,
                   const IO *__restrict__ Cm, const float *__restrict__ h0, float *__restrict__ last_state,
                   float *__restrict__ cstate, float *__restrict__ cdsum, int64_t L, int64_t D,
-                  int tiles_per_b, int n_tiles, int64_t chunk_len, int nchunk, int softplus) {
+                  int tiles_per_b, int n_tiles, int64_t chunk_len, int nchunk, int softplus,
+                  const float *__restrict__ conv_w = nullptr, const float *__restrict__ conv_b = nullptr,
+                  IO *__restrict__ u_out = nullptr) {
     constexpr int K = N / S;
     constexpr int J = T / K;                   // prep / epilogue elements per thread per tile
     constexpr int V = VEC ? (J < 8 ? J : 8) : 1;  // consecutive channels per thread access
@@ -109,6 +119,8 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     constexpr int BW = PIPE ? S * (int)sizeof(IO) / 4 : 1;
     __shared__ f32x2_t s_dk[T][kChanTile];
     __shared__ float s_yp[READOUT ? K : 1][T][kChanTile];
+    constexpr int RS = CW > 0 ? T + CW - 1 : 1;   // rows of the x ring
+    __shared__ IO s_x[RS][kChanTile];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -116,6 +128,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     // prep / epilogue mapping: access p of this thread covers token row p*RPP + tid/GPR,
     // channels cq .. cq+V-1 of the tile
     const int rsub = tid / GPR;
+    auto row_of = [&](int p) -> int { return p * RPP + rsub; };   // token row of access p
     const int cq = (tid % GPR) * V;
     const bool gated = READOUT && z != nullptr;
     const IO *__restrict__ zsrc = gated ? z : u;
@@ -161,17 +174,26 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
         Dq[v] = (ok && Dv) ? Dv[dq + v] : 0.0f;
         bq[v] = (ok && bias) ? bias[dq + v] : 0.0f;
     }
+    // the convolution's taps and bias for this lane's channel (an in-bounds one for lanes
+    // past D, whose values are never stored)
+    float cwl[CW > 0 ? CW : 1], cbl = 0.0f;
+    if constexpr (CW > 0) {
+        const int64_t dc = act ? d : D - 1;
+#pragma unroll
+        for (int k = 0; k < CW; ++k) cwl[k] = conv_w[dc * CW + k];
+        cbl = conv_b ? conv_b[dc] : 0.0f;
+    }
     float dsum = 0.0f;
 
     // Raw inputs of a tile, in two register buffers: the loads of tile i+2 are issued
     // as soon as tile i has been read out of its buffer, so that two tiles of recurrence
     // hide their latency; indices are clamped so every load is in bounds.
-    struct Raw { uint32_t u[P][W], d[P][W], z[P][W]; };
+    struct Raw { uint32_t u[P][W], d[P][W], z[P][W]; };   // (u holds x with the convolution)
     Raw r0, r1;
     auto load_tile = [&](int64_t t0, Raw &r) {
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-            const int64_t t = min(t0 + (p * RPP + rsub), t_end - 1);
+            const int64_t t = min(t0 + row_of(p), t_end - 1);
             const int64_t idx = (row0 + t) * D + dq;
             // (z is loaded unconditionally -- from u when there is no gate -- so that the
             // buffer registers carry no conditional value around the loop)
@@ -197,6 +219,92 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     };
     load_tile(t_begin, r0);
     load_tile(t_begin + T, r1);
+    // The x ring (convolution only): token t of the chunk lives in row
+    // (t - t_begin + CW - 1) mod RS.  The base rb of a tile is (its first token - t_begin)
+    // mod RS, carried from tile to tile (rb_cur below), so token t0 + tt (tt >= 1 - CW)
+    // is in row ring_row(rb, tt).
+    auto ring_row = [&](int rb, int tt) -> int {
+        const int x = rb + tt + (CW - 1);
+        return x >= RS ? x - RS : x;
+    };
+    auto ring_next = [&](int rb) -> int { return rb + T >= RS ? rb + T - RS : rb + T; };
+    int rb_cur = 0;   // ring base of the tile being processed
+    // x rows of the tile with ring base rb from a raw buffer into the ring (rows past the
+    // end hold clamped copies, never used)
+    auto ring_fill = [&](int rb, const Raw &r) {
+        if constexpr (CW > 0) {
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                IO *dst = &s_x[ring_row(rb, row_of(p))][cq];
+                if constexpr (VEC) {
+#pragma unroll
+                    for (int i = 0; i < W; ++i) reinterpret_cast<uint32_t *>(dst)[i] = r.u[p][i];
+                } else if constexpr (sizeof(IO) == 2) {
+                    dst[0] = (IO)(__float_as_uint(raw(r.u[p], 0)) >> 16);
+                } else {
+                    dst[0] = raw(r.u[p], 0);
+                }
+            }
+        }
+    };
+    // the conv phase of the tile at t0: lane = channel; wave w computes u for exactly the
+    // rows its own threads prepare (rows p*RPP + w*V .. + V-1 of each access round p), so
+    // the prep needs only this wave's LDS writes to be done.  u goes to s_dk[tt][lane].x
+    // for the prep (and to u_out).
+    auto conv_phase = [&](int64_t t0, int rb, int nt) {
+        if constexpr (CW > 0) {
+            auto xr = [&](int tt) -> float {
+                const IO v = s_x[ring_row(rb, tt)][lane];
+                if constexpr (sizeof(IO) == 2) return bf16_to_f32(v);
+                else return v;
+            };
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const int tb = p * RPP + w * V;
+                float xw[CW];
+#pragma unroll
+                for (int k = 0; k < CW - 1; ++k) xw[k] = xr(tb - (CW - 1) + k);
+#pragma unroll
+                for (int i = 0; i < V; ++i) {
+                    xw[CW - 1] = xr(tb + i);
+                    float acc = cbl;
+#pragma unroll
+                    for (int k = 0; k < CW; ++k) acc = fmaf(cwl[k], xw[k], acc);
+                    const float uu = silu_f32(acc);
+                    s_dk[tb + i][lane] = f32x2_t{uu, uu};
+#pragma unroll
+                    for (int k = 0; k + 1 < CW; ++k) xw[k] = xw[k + 1];
+                }
+            }
+            if (u_out && act) {   // the convolution's output, for the backward pass
+                IO *dst = u_out + (row0 + t0) * D + d;
+#pragma unroll
+                for (int p = 0; p < P; ++p) {
+                    const int tb = p * RPP + w * V;
+#pragma unroll
+                    for (int i = 0; i < V; ++i)
+                        if (tb + i < nt) io<IO>::st(dst, (int64_t)(tb + i) * D, s_dk[tb + i][lane].x);
+                }
+            }
+            // this wave's LDS writes are performed before its later reads (a wavefront's LDS
+            // operations complete in order); keep the compiler from moving them
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+    };
+    if constexpr (CW > 0) {
+        // the CW - 1 rows before the chunk (zero before token 0), and the first tile
+        for (int i = tid; i < (CW - 1) * kChanTile; i += 64 * K) {
+            const int j = i / kChanTile, c = i % kChanTile;
+            const int64_t t = t_begin - (CW - 1) + j;
+            IO v = IO(0);
+            if (t >= 0 && d0 + c < D) v = u[(row0 + t) * D + d0 + c];
+            s_x[j][c] = v;   // ring rows 0 .. CW-2 hold the tokens before the chunk
+        }
+        ring_fill(0, r0);
+        __syncthreads();
+    }
     // kCheckpoint: the state before token t (t a multiple of kCkptEvery) into
     // cstate[b][t / kCkptEvery][d][:]
     const int64_t n_ckpt = (L + kCkptEvery - 1) / kCkptEvery;
@@ -218,7 +326,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
         const int nt = (int)max((int64_t)0, min((int64_t)T, t_end - t0));
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-            const int tt = p * RPP + rsub;
+            const int tt = row_of(p);
             if (tt < nt && qact) {
                 float yv[V];
 #pragma unroll
@@ -241,17 +349,19 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     // the previous tile (its stores then retire while this tile runs), the prefetch of the
     // tile after next into the buffer just read, and the recurrence.  A tile past the end
     // is empty (nt = 0).
-    auto do_tile = [&](int64_t t0, Raw &r, const DG &prev, DG &cur, bool has_prev) {
+    auto do_tile = [&](int64_t t0, Raw &r, const Raw &rn, const DG &prev, DG &cur, bool has_prev) {
         const int nt = (int)max((int64_t)0, min((int64_t)T, t_end - t0));
+        conv_phase(t0, rb_cur, nt);
         // prep: (delta, delta*u) into LDS (delta*u*log2(e) for the zero-order hold); skip
         // and gate factors kept in registers
         // (without a gate the factors keep the 1.0 they start with)
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-            const int tt = p * RPP + rsub;
+            const int tt = row_of(p);
 #pragma unroll
             for (int v = 0; v < V; ++v) {
-                const float uu = raw(r.u[p], v);
+                // (with the convolution, u comes from the conv phase through s_dk)
+                const float uu = CW > 0 ? s_dk[tt][cq + v].x : raw(r.u[p], v);
                 const float x = raw(r.d[p], v) + bq[v];
                 const float dl = softplus ? softplus_f32(x) : x;
                 // (written unmasked: rows of tokens past the end are never read by the
@@ -272,6 +382,10 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
         __builtin_amdgcn_sched_barrier(0);
         load_tile(t0 + 2 * T, r);
         __syncthreads();
+        if constexpr (CW > 0) {
+            rb_cur = ring_next(rb_cur);
+            ring_fill(rb_cur, rn);   // the next tile's x rows (the ring rows this tile read are free)
+        }
         // recurrence over the tile: lane = channel, this wave's S states
         checkpoint(t0);
         if (PIPE && nt == T) {
@@ -367,8 +481,8 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
 #pragma unroll
         for (int v = 0; v < V; ++v) dg0.g[p][v] = dg1.g[p][v] = 1.0f;
     for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * T) {
-        do_tile(t0, r0, dg1, dg0, t0 > t_begin);
-        do_tile(t0 + T, r1, dg0, dg1, true);
+        do_tile(t0, r0, r1, dg1, dg0, t0 > t_begin);
+        do_tile(t0 + T, r1, r0, dg0, dg1, true);
     }
     {
         // the last pair's second tile (empty or not) still owes its epilogue

@@ -128,10 +128,18 @@ template <> struct ScanShape<4> { static constexpr int S = 4, T = 32; };
 template <> struct ScanShape<8> { static constexpr int S = 4, T = 32; };
 template <> struct ScanShape<16> { static constexpr int S = 4, T = 32; };
 
-template <int N, typename IO, bool VEC, bool ZOH>
+// The fused causal convolution of the scan's input (conv entry point only).
+struct ConvArgs {
+    const float *w;
+    const float *b;
+    void *u_out;
+};
+
+template <int N, typename IO, bool VEC, bool ZOH, int CW = 0>
 void launch_scan_kernels(const IO *u, const IO *dl, const float *A, const IO *B, const IO *C, const float *Dv,
                          const IO *z, const float *bias, int softplus, const float *h0, IO *y, float *last_state,
-                         const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st) {
+                         const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st,
+                         const ConvArgs &cv = ConvArgs{nullptr, nullptr, nullptr}) {
     constexpr int S = ScanShape<N>::S;
     constexpr int T = ScanShape<N>::T;
     constexpr int K = N / S;
@@ -144,23 +152,26 @@ void launch_scan_kernels(const IO *u, const IO *dl, const float *A, const IO *B,
     const int64_t cl = p.chunk_len;
     const int nc = (int)p.nchunk;
     if (p.schedule == kCarry) {
-        hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kSummary, VEC, ZOH>),
+        hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kSummary, VEC, ZOH, CW>),
                            dim3((unsigned)n_tiles, (unsigned)(nc - 1)), block, 0, st, u, dl, (const IO *)nullptr,
                            (IO *)nullptr, A, (const float *)nullptr, bias, B, C, (const float *)nullptr,
-                           (float *)nullptr, cstate, cdsum, L, D, tiles_per_b, n_tiles, cl, nc, softplus);
+                           (float *)nullptr, cstate, cdsum, L, D, tiles_per_b, n_tiles, cl, nc, softplus, cv.w, cv.b,
+                           (IO *)nullptr);
         const int col_tiles = (int)((D * N + 63) / 64);
         hipLaunchKernelGGL((ssm::carry_scan_kernel<N>), dim3((unsigned)(bsz * col_tiles)), dim3(256), 0, st,
                            cstate, (const float *)cdsum, A, h0, D, nc, col_tiles);
     }
-    hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kFull, VEC, ZOH>), dim3((unsigned)n_tiles, (unsigned)nc),
-                       block, 0, st, u, dl, z, y, A, Dv, bias, B, C, h0, last_state, cstate, cdsum, L, D,
-                       tiles_per_b, n_tiles, cl, nc, softplus);
+    hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kFull, VEC, ZOH, CW>),
+                       dim3((unsigned)n_tiles, (unsigned)nc), block, 0, st, u, dl, z, y, A, Dv, bias, B, C, h0,
+                       last_state, cstate, cdsum, L, D, tiles_per_b, n_tiles, cl, nc, softplus, cv.w, cv.b,
+                       static_cast<IO *>(cv.u_out));
 }
 
 template <int N, typename IO>
 int launch_scan(const void *u, const void *delta, const float *A, const void *B, const void *C,
                 const float *Dv, const void *z, const float *bias, int flags, const float *h0, void *y,
-                float *last_state, const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st) {
+                float *last_state, const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st,
+                const ConvArgs *cv) {
     const int softplus = (flags & SSM_SCAN_SOFTPLUS) != 0;
     const bool zoh = (flags & SSM_SCAN_EXACT_ZOH) != 0;
     const IO *u_ = static_cast<const IO *>(u);
@@ -172,6 +183,18 @@ int launch_scan(const void *u, const void *delta, const float *A, const void *B,
     // 16-byte prep/epilogue accesses need whole groups of 8 channels and aligned rows
     const bool vec = dm->dim % 8 == 0 && aligned(u, 16) && aligned(delta, 16) && aligned(y, 16) &&
                      (!z || aligned(z, 16));
+    if (cv) {
+        // the fused convolution (width 4; no exact ZOH, checked by the caller)
+        if (vec)
+            launch_scan_kernels<N, IO, true, false, 4>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state,
+                                                       dm, p, ws, st, *cv);
+        else
+            launch_scan_kernels<N, IO, false, false, 4>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_,
+                                                        last_state, dm, p, ws, st, *cv);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+        return ok();
+    }
     if (vec && zoh)
         launch_scan_kernels<N, IO, true, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state, dm, p,
                                                ws, st);
@@ -192,13 +215,14 @@ int launch_scan(const void *u, const void *delta, const float *A, const void *B,
 template <typename IO>
 int dispatch_scan(int64_t N, const void *u, const void *delta, const float *A, const void *B,
                   const void *C, const float *Dv, const void *z, const float *bias, int flags, const float *h0,
-                  void *y, float *ls, const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st) {
+                  void *y, float *ls, const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st,
+                  const ConvArgs *cv) {
     switch (N) {
-        case 1: return launch_scan<1, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st);
-        case 2: return launch_scan<2, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st);
-        case 4: return launch_scan<4, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st);
-        case 8: return launch_scan<8, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st);
-        case 16: return launch_scan<16, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st);
+        case 1: return launch_scan<1, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv);
+        case 2: return launch_scan<2, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv);
+        case 4: return launch_scan<4, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv);
+        case 8: return launch_scan<8, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv);
+        case 16: return launch_scan<16, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv);
     }
     return fail(SSM_ERR_UNSUPPORTED_N, "dstate %lld not supported", (long long)N);
 }
@@ -375,7 +399,7 @@ int launch_conv(int width, bool silu, const void *x, const float *w, const float
 static int scan_impl(const float *h0, const void *u, const void *delta, const float *A, const void *B,
                      const void *C, const float *D, const void *z, const float *delta_bias, int flags,
                      void *y, float *last_state, const ssm_dims *dims, void *workspace, size_t workspace_bytes,
-                     void *stream) {
+                     void *stream, const ConvArgs *cv = nullptr) {
     int rc = check_dims(dims, true);
     if (rc != SSM_OK) return rc;
     if (flags & ~(SSM_SCAN_SOFTPLUS | SSM_SCAN_EXACT_ZOH)) return fail(SSM_ERR_FLAGS, "unknown flag bits 0x%x", flags);
@@ -408,6 +432,13 @@ static int scan_impl(const float *h0, const void *u, const void *delta, const fl
         return fail(SSM_ERR_ALIGN, "a tensor pointer is not aligned to its element size");
     if (dims->io_dtype == SSM_IO_BF16 && N >= 2 && (!aligned(B, 4) || !aligned(C, 4)))
         return fail(SSM_ERR_ALIGN, "bf16 B and C must be 4-byte aligned");
+    if (cv) {
+        if (!aligned(cv->u_out, es)) return fail(SSM_ERR_ALIGN, "u_out not aligned to its element size");
+        if (!cv->w) return fail(SSM_ERR_NULL, "conv_w is NULL");
+        if (!aligned(cv->w, 4) || !aligned(cv->b, 4)) return fail(SSM_ERR_ALIGN, "conv_w / conv_b not 4-byte aligned");
+        if (flags & SSM_SCAN_EXACT_ZOH)
+            return fail(SSM_ERR_FLAGS, "the exact zero-order hold is not available with the fused convolution");
+    }
     Plan p = make_plan(dims);
     if (p.bytes > 0 && !workspace) return fail(SSM_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", p.bytes);
     if (workspace_bytes < p.bytes)
@@ -416,9 +447,9 @@ static int scan_impl(const float *h0, const void *u, const void *delta, const fl
     if (p.bytes > 0 && !aligned(workspace, 16)) return fail(SSM_ERR_ALIGN, "workspace not 16-byte aligned");
     if (dims->io_dtype == SSM_IO_BF16)
         return dispatch_scan<uint16_t>(N, u, delta, A, B, C, D, z, delta_bias, flags, h0, y, last_state, dims, p,
-                                       workspace, st);
+                                       workspace, st, cv);
     return dispatch_scan<float>(N, u, delta, A, B, C, D, z, delta_bias, flags, h0, y, last_state, dims, p,
-                                workspace, st);
+                                workspace, st, cv);
 }
 
 
@@ -456,6 +487,18 @@ int ssm_scan_fwd_from(const float *initial_state, const void *u, const void *del
                       size_t workspace_bytes, void *stream) {
     return scan_impl(initial_state, u, delta, A, B, C, D, z, delta_bias, flags, y, last_state, dims,
                      workspace, workspace_bytes, stream);
+}
+
+int ssm_scan_fwd_conv(const void *x, const float *conv_w, const float *conv_b, int conv_width, const void *delta,
+                      const float *A, const void *B, const void *C, const float *D, const void *z,
+                      const float *delta_bias, int flags, void *y, float *last_state, void *u_out,
+                      const ssm_dims *dims, void *workspace, size_t workspace_bytes, void *stream) {
+    if (conv_width != 4)
+        return fail(SSM_ERR_SHAPE, "the fused convolution has width 4 (got %d); use ssm_conv1d_fwd + ssm_scan_fwd",
+                    conv_width);
+    const ConvArgs cv{conv_w, conv_b, u_out};
+    return scan_impl(nullptr, x, delta, A, B, C, D, z, delta_bias, flags, y, last_state, dims, workspace,
+                     workspace_bytes, stream, &cv);
 }
 
 int ssm_step(float *state, const void *u, const void *delta, const float *A, const void *B,

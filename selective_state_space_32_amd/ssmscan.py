@@ -59,6 +59,9 @@ def _load() -> ctypes.CDLL:
     lib.ssm_step.restype = ctypes.c_int
     lib.ssm_conv1d_fwd.argtypes = [P, P, P, ctypes.c_int, P, ctypes.c_int, P, P, D, P]
     lib.ssm_conv1d_fwd.restype = ctypes.c_int
+    lib.ssm_scan_fwd_conv.argtypes = [P, P, P, ctypes.c_int, P, P, P, P, P, P, P, ctypes.c_int, P, P, P, D, P,
+                                      ctypes.c_size_t, P]
+    lib.ssm_scan_fwd_conv.restype = ctypes.c_int
     return lib
 
 
@@ -394,4 +397,49 @@ def conv1d_call(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] =
 
     def call(_args=args, _keep=keep):
         _check(lib.ssm_conv1d_fwd(*_args))
+    return call
+
+
+def _scan_conv_args(x, conv_w, conv_b, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
+                    return_last_state, u_out, chunk_len, workspace, stream):
+    if conv_w.dim() != 2 or conv_w.shape[0] != x.shape[-1]:
+        raise ValueError("conv_w must be (dim, width)")
+    bsz, L, dim = x.shape
+    _need(conv_w, "conv_w", (dim, conv_w.shape[1]), torch.float32, x.device)
+    if conv_b is not None:
+        _need(conv_b, "conv_b", (dim,), torch.float32, x.device)
+    if u_out is not None:
+        _need(u_out, "u_out", (bsz, L, dim), x.dtype, x.device)
+    args, keep, y, last_state = _scan_args(x, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
+                                           return_last_state, chunk_len, workspace, stream)
+    # ssm_scan_fwd's arguments with x in place of u, the convolution's before delta, u_out after last_state
+    args = (args[0], _ptr(conv_w), _ptr(conv_b), int(conv_w.shape[1])) + args[1:11] + (_ptr(u_out),) + args[11:]
+    return args, keep + (conv_w, conv_b, u_out), y, last_state
+
+
+def scan_fwd_conv(x: torch.Tensor, conv_w: torch.Tensor, conv_b: Optional[torch.Tensor], delta: torch.Tensor,
+                  A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, D: Optional[torch.Tensor] = None,
+                  z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                  softplus: bool = True, *, y: Optional[torch.Tensor] = None,
+                  last_state: Optional[torch.Tensor] = None, return_last_state: bool = True,
+                  u_out: Optional[torch.Tensor] = None, chunk_len: int = 0,
+                  workspace: Optional[torch.Tensor] = None, stream=None):
+    """Causal convolution (width 4) + SiLU fused into the scan (ssm_scan_fwd_conv): x is the
+    block's projected input, conv_w (dim, 4), conv_b (dim,) float32; u_out (optional) receives
+    the convolution's output.  Otherwise as scan_fwd.  Returns (y, last_state)."""
+    args, _keep, y, last_state = _scan_conv_args(x, conv_w, conv_b, delta, A, B, C, D, z, delta_bias, softplus, y,
+                                                 last_state, return_last_state, u_out, chunk_len, workspace, stream)
+    _check(lib.ssm_scan_fwd_conv(*args))
+    return y, last_state
+
+
+def scan_fwd_conv_call(x, conv_w, conv_b, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, *,
+                       y=None, last_state=None, return_last_state=True, u_out=None, chunk_len=0, workspace=None,
+                       stream=None) -> Callable[[], None]:
+    """The scan_fwd_conv call checked and marshalled once (see scan_fwd_call)."""
+    args, keep, _y, _ls = _scan_conv_args(x, conv_w, conv_b, delta, A, B, C, D, z, delta_bias, softplus, y,
+                                          last_state, return_last_state, u_out, chunk_len, workspace, stream)
+
+    def call(_args=args, _keep=keep):
+        _check(lib.ssm_scan_fwd_conv(*_args))
     return call

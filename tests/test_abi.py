@@ -28,7 +28,7 @@ def b():
 def test_header_declares_the_entry_points():
     syms = set(declared_symbols())
     assert {"ssm_scan_fwd", "ssm_scan_fwd_from", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes", "ssm_step",
-            "ssm_conv1d_fwd",
+            "ssm_conv1d_fwd", "ssm_scan_fwd_conv",
             "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_last_error", "ssm_version"} <= syms
 
 
@@ -161,6 +161,20 @@ def test_conv_validation(b):
     assert conv(w=0) == -1
     assert conv(out=0) == -1
     assert conv(dims=_dims(b, io_dtype=5)) == -3
+
+
+def test_conv_scan_validation(b):
+    P = ctypes.c_void_p
+    d = _dims(b)
+    ws = b.lib.ssm_scan_workspace_bytes(ctypes.byref(d))
+
+    def call(width=4, flags=1, x=FAKE, w=FAKE, dims=d):
+        return b.lib.ssm_scan_fwd_conv(P(x), P(w), None, width, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None, None,
+                                       flags, P(FAKE), None, None, ctypes.byref(dims), P(FAKE), ws, None)
+    assert call(width=3) == -2
+    assert call(flags=3) == -8
+    assert call(w=0) == -1
+    assert call(x=FAKE + 1) == -4          # a bf16 x must be 2-byte aligned
 
 
 def test_misaligned_rejected(b):
