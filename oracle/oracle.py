@@ -56,6 +56,8 @@ def _load():
         lib.ssm_oracle_step.restype = ctypes.c_int
         lib.ssm_oracle_conv1d.argtypes = [I64, I64, I64, I64, P, P, P, P, ctypes.c_int, P, P]
         lib.ssm_oracle_conv1d.restype = ctypes.c_int
+        lib.ssm_oracle_ssd.argtypes = [I64] * 6 + [P] * 9 + [ctypes.c_int, P, P, ctypes.c_int]
+        lib.ssm_oracle_ssd.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -207,3 +209,30 @@ def conv1d(x, w, bias=None, state=None, silu: bool = True) -> Tuple[np.ndarray, 
     if rc != 0:
         raise ValueError("oracle conv1d rejected width=%d" % width)
     return out, st
+
+
+def ssd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus: bool = True, h0=None,
+        threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """fp64 Mamba-2 SSD layer.  x, z: (bsz, L, H, P); dt: (bsz, L, H); A, D, dt_bias: (H,);
+    B, C: (bsz, L, G, N); h0: (bsz, H, P, N).  Returns (y (bsz, L, H, P), last_state
+    (bsz, H, P, N)), float64."""
+    x = _f64(x)
+    bsz, L, H, P = x.shape
+    B = _f64(B)
+    G, N = B.shape[2], B.shape[3]
+    B = _f64(B, (bsz, L, G, N))
+    C = _f64(C, (bsz, L, G, N))
+    dt = _f64(dt, (bsz, L, H))
+    A = _f64(A, (H,))
+    D = _f64(D, (H,))
+    z = _f64(z, (bsz, L, H, P))
+    dt_bias = _f64(dt_bias, (H,))
+    h0 = _f64(h0, (bsz, H, P, N))
+    y = np.empty((bsz, L, H, P), dtype=np.float64)
+    last = np.empty((bsz, H, P, N), dtype=np.float64)
+    rc = _load().ssm_oracle_ssd(bsz, L, H, P, G, N, _ptr(h0), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                _ptr(z), _ptr(dt_bias), int(bool(softplus)), _ptr(y), _ptr(last),
+                                int(threads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle ssd rejected N=%d G=%d H=%d" % (N, G, H))
+    return y, last

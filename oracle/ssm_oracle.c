@@ -25,6 +25,8 @@
  *      (shakilmahmud.com section 3; urworte.de "Methodische Grundlagen")
  *  - the short causal convolution and SiLU that produce the scan's input in the block's
  *      main branch (azimuth.plus/paper/mamba, block architecture section)
+ *  - Mamba-2's state space dual layer: a scalar state matrix per head, whose sequence map
+ *      is a 1-semiseparable matrix (mugbit.ir, Mamba-2 / structured state space duality)
  *
  * Readings where the pages are silent: the scan starts from h = 0; the step size is
  * softplus(delta_in + delta_bias) when the flag is set, else delta_in + delta_bias;
@@ -341,5 +343,55 @@ int ssm_oracle_conv1d(int64_t bsz, int64_t L, int64_t D, int64_t width, const do
         }
     }
     free(hist);
+    return 0;
+}
+
+/*
+ * The state space dual layer (SSD) of Mamba-2 (mugbit.ir, the Mamba-2 / structured state
+ * space duality section): the selective scan with a scalar state matrix per head, so that
+ * the sequence map is a 1-semiseparable matrix.  Per head h (P channels, group g = h / (H/G)
+ * of the B / C projections) the state is a P x N matrix:
+ *   dt_t      = softplus(dt_in[t,h] + dt_bias[h]) with the softplus flag, else dt_in + dt_bias
+ *   S_t[p,n]  = exp(dt_t A[h]) S_{t-1}[p,n] + dt_t x_t[p] B_t[g,n]
+ *   y_t[p]    = (sum_n C_t[g,n] S_t[p,n] + D[h] x_t[p]) * silu(z_t[p])      (z optional)
+ *   x, z, y    : [bsz][L][H][P]     dt_in : [bsz][L][H]     A, dt_bias, D : [H]
+ *   B, C       : [bsz][L][G][N]     h0, last_state : [bsz][H][P][N] (h0 NULL = zero)
+ * Channels (b, h, p) are independent; spread over `nthreads` threads.  Returns 0, or -1 for
+ * N too large or H not a multiple of G.
+ */
+int ssm_oracle_ssd(int64_t bsz, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                   const double *h0, const double *x, const double *dt_in, const double *A,
+                   const double *B, const double *C, const double *Dv, const double *z,
+                   const double *dt_bias, int flags, double *y, double *last_state, int nthreads) {
+    if (N > ORACLE_MAX_N || N < 1 || G < 1 || H % G != 0) return -1;
+    const int softplus_flag = flags & ORACLE_SOFTPLUS;
+    const int64_t hpg = H / G;
+    int64_t nch = bsz * H * P;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t ch = 0; ch < nch; ++ch) {
+        int64_t b = ch / (H * P), h = (ch / P) % H, p = ch % P, g = h / hpg;
+        double s[ORACLE_MAX_N];
+        for (int64_t n = 0; n < N; ++n) s[n] = h0 ? h0[((b * H + h) * P + p) * N + n] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            double v = dt_in[(b * L + t) * H + h];
+            if (dt_bias) v = v + dt_bias[h];
+            double dt = softplus_flag ? oracle_softplus(v) : v;
+            double dA = exp(dt * A[h]);
+            int64_t i = ((b * L + t) * H + h) * P + p;   /* (b, t, h, p) */
+            const double *Bt = B + ((b * L + t) * G + g) * N;
+            const double *Ct = C + ((b * L + t) * G + g) * N;
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                s[n] = dA * s[n] + dt * x[i] * Bt[n];
+                acc = acc + Ct[n] * s[n];
+            }
+            double yt = acc;
+            if (Dv) yt = yt + Dv[h] * x[i];
+            if (z) yt = yt * oracle_silu(z[i]);
+            y[i] = yt;
+        }
+        if (last_state)
+            for (int64_t n = 0; n < N; ++n) last_state[((b * H + h) * P + p) * N + n] = s[n];
+    }
     return 0;
 }

@@ -548,6 +548,103 @@ CONV_CHECKS = [check_conv_numpy_convolve, check_conv_impulse, check_conv_silu, c
                check_conv_state_is_history]
 
 
+# --- Mamba-2's state space dual layer (SSD) -------------------------------------------------
+# ssd(x, dt, A, B, C, D, z, dt_bias, softplus, h0) -> (y, last_state)
+# x, z: (b, L, H, P); dt: (b, L, H); A, D, dt_bias: (H,); B, C: (b, L, G, N); h0: (b, H, P, N)
+
+def _ssd_case(seed, b=2, L=29, H=4, P=3, G=2, N=5, full=True):
+    rng = _rng(seed)
+    c = dict(x=rng.standard_normal((b, L, H, P)), dt=0.5 * rng.standard_normal((b, L, H)),
+             A=-np.exp(rng.normal(0.0, 0.7, H)), B=rng.standard_normal((b, L, G, N)),
+             C=rng.standard_normal((b, L, G, N)), D=None, z=None, dt_bias=None, h0=None)
+    if full:
+        c.update(D=rng.standard_normal(H), z=rng.standard_normal((b, L, H, P)), dt_bias=rng.uniform(-1.5, 0.0, H),
+                 h0=rng.standard_normal((b, H, P, N)))
+    return c
+
+
+def _run_ssd(ssd, c, softplus=True):
+    return ssd(c["x"], c["dt"], c["A"], c["B"], c["C"], c["D"], c["z"], c["dt_bias"], softplus, c["h0"])
+
+
+def check_ssd_is_broadcast_scan(ssd, scan_from, seed=91):
+    """A head is the selective scan of its P channels with the head's A in every state, the
+    head's step size on every channel and its group's B and C (mugbit.ir: Mamba-2 keeps the
+    SSM and makes the state matrix a scalar per head); run through the pinned scan oracle."""
+    c = _ssd_case(seed)
+    y, last = _run_ssd(ssd, c)
+    b, L, H, P = c["x"].shape
+    G, N = c["B"].shape[2], c["B"].shape[3]
+    hpg = H // G
+    for g in range(G):
+        hs = list(range(g * hpg, (g + 1) * hpg))
+        u = c["x"][:, :, hs, :].reshape(b, L, hpg * P)
+        delta = np.repeat(c["dt"][:, :, hs], P, axis=2)
+        A = np.repeat(c["A"][hs], P)[:, None] * np.ones((1, N))
+        Dv = np.repeat(c["D"][hs], P)
+        z = c["z"][:, :, hs, :].reshape(b, L, hpg * P)
+        bias = np.repeat(c["dt_bias"][hs], P)
+        h0 = c["h0"][:, hs].reshape(b, hpg * P, N)
+        ys, ls = scan_from(u, delta, A, c["B"][:, :, g], c["C"][:, :, g], Dv, z, bias, True, h0)
+        assert _rel(y[:, :, hs, :].reshape(b, L, hpg * P), ys) < 1e-13, g
+        assert _rel(last[:, hs].reshape(b, hpg * P, N), ls) < 1e-13, g
+
+
+def check_ssd_semiseparable(ssd, seed=92):
+    """The dual form: the layer is y = M (dt x) + D x with the 1-semiseparable matrix
+    M[t, s] = (C_t . B_s) exp(A (S_t - S_s)) for s <= t, 0 above the diagonal, S the running
+    sum of step sizes (mugbit.ir, structured state space duality), built here as an L x L
+    matrix per head and applied with numpy."""
+    c = _ssd_case(seed)
+    c["h0"] = None
+    c["z"] = None
+    y, _ = _run_ssd(ssd, c, softplus=True)
+    b, L, H, P = c["x"].shape
+    hpg = H // c["B"].shape[2]
+    want = np.zeros_like(y)
+    for bb in range(b):
+        for h in range(H):
+            g = h // hpg
+            dt = _softplus_np(c["dt"][bb, :, h] + c["dt_bias"][h])
+            S = np.cumsum(dt)
+            M = (c["C"][bb, :, g] @ c["B"][bb, :, g].T) * np.tril(np.exp(c["A"][h] * (S[:, None] - S[None, :])))
+            want[bb, :, h] = M @ (dt[:, None] * c["x"][bb, :, h]) + c["D"][h] * c["x"][bb, :, h]
+    assert _rel(y, want) < 1e-12, _rel(y, want)
+
+
+def check_ssd_composition(ssd, seed=93, split=11):
+    """Two pieces, the second from the first's state, are bitwise the run over the whole."""
+    c = _ssd_case(seed)
+    y, last = _run_ssd(ssd, c)
+    c1 = dict(c, x=c["x"][:, :split], dt=c["dt"][:, :split], B=c["B"][:, :split], C=c["C"][:, :split],
+              z=c["z"][:, :split])
+    y1, l1 = _run_ssd(ssd, c1)
+    c2 = dict(c, x=c["x"][:, split:], dt=c["dt"][:, split:], B=c["B"][:, split:], C=c["C"][:, split:],
+              z=c["z"][:, split:], h0=l1)
+    y2, l2 = _run_ssd(ssd, c2)
+    assert np.array_equal(np.concatenate([y1, y2], axis=1), y) and np.array_equal(l2, last)
+
+
+def check_ssd_free_decay(ssd, seed=94):
+    """With no input the state only decays: S_L = exp(A sum dt) h0 and
+    y_t = (C_t . (exp(A S_t) h0[p, :])) silu(z_t) in closed form."""
+    c = _ssd_case(seed)
+    c["x"] = np.zeros_like(c["x"])
+    y, last = _run_ssd(ssd, c, softplus=True)
+    dt = _softplus_np(c["dt"] + c["dt_bias"][None, None, :])             # (b, L, H)
+    S = np.cumsum(dt, axis=1)
+    decay = np.exp(c["A"][None, None, :] * S)                              # (b, L, H)
+    hpg = c["x"].shape[2] // c["B"].shape[2]
+    Cg = np.repeat(c["C"], hpg, axis=2)                                    # (b, L, H, N)
+    want = decay[..., None] * np.einsum("blhn,bhpn->blhp", Cg, c["h0"]) * (c["z"] * expit(c["z"]))
+    assert _rel(y, want) < 1e-12
+    assert _rel(last, decay[:, -1][:, :, None, None] * c["h0"]) < 1e-13
+
+
+SSD_CHECKS = [check_ssd_semiseparable, check_ssd_composition, check_ssd_free_decay]
+SSD_SCAN_CHECKS = [check_ssd_is_broadcast_scan]
+
+
 # --- gradients of the scan ------------------------------------------------------------------
 # scan_from(u, x, A, B, C, D, z, bias, softplus, h0) -> (y, last_state)
 # scan_bwd(u, x, A, B, C, dy, D, z, bias, softplus, h0, dlast) -> dict of gradients

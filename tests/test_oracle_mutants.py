@@ -59,6 +59,10 @@ MUTANTS = {
     "conv_ignore_state": ("hist[r] = state ? state[(b * H + r) * D + d] : 0.0;", "hist[r] = 0.0;"),
     "conv_state_out_oldest_rows": ("state_out[(b * H + r) * D + d] = hist[L + r];",
                                    "state_out[(b * H + r) * D + d] = hist[r];"),
+    "ssd_group_index": ("g = h / hpg;", "g = h % G;"),
+    "ssd_drop_dt_in_input": ("s[n] = dA * s[n] + dt * x[i] * Bt[n];", "s[n] = dA * s[n] + x[i] * Bt[n];"),
+    "ssd_decay_without_dt": ("double dA = exp(dt * A[h]);", "double dA = exp(A[h]);"),
+    "ssd_readout_with_B": ("acc = acc + Ct[n] * s[n];", "acc = acc + Bt[n] * s[n];"),
     "decay_squared": ("h[n] = dA * h[n] + dt * Bt[n] * ut;", "h[n] = dA * dA * h[n] + dt * Bt[n] * ut;"),
 }
 
@@ -83,6 +87,8 @@ def _build_mutant(tmp_path, name, old, new):
     lib.ssm_oracle_scan_bwd.restype = ctypes.c_int
     lib.ssm_oracle_conv1d.argtypes = [I64, I64, I64, I64, P, P, P, P, ctypes.c_int, P, P]
     lib.ssm_oracle_conv1d.restype = ctypes.c_int
+    lib.ssm_oracle_ssd.argtypes = [I64] * 6 + [P] * 9 + [ctypes.c_int, P, P, ctypes.c_int]
+    lib.ssm_oracle_ssd.restype = ctypes.c_int
 
     def f64(a):
         return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
@@ -140,13 +146,22 @@ def _build_mutant(tmp_path, name, old, new):
         lib.ssm_oracle_conv1d(bsz, L, Dch, width, ptr(x), ptr(w), ptr(bias), ptr(state), int(bool(silu)), ptr(out),
                               ptr(st))
         return out, st
-    return scan, scan_from, scan_bwd, scan_zoh, conv
+    def ssd(x, dt, A, B, C, D, z, dt_bias, softplus, h0):
+        x, dt, A, B, C, D, z, dt_bias, h0 = map(f64, (x, dt, A, B, C, D, z, dt_bias, h0))
+        bsz, L, H, Pd = x.shape
+        G, N = B.shape[2], B.shape[3]
+        y = np.empty((bsz, L, H, Pd))
+        last = np.empty((bsz, H, Pd, N))
+        lib.ssm_oracle_ssd(bsz, L, H, Pd, G, N, ptr(h0), ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), ptr(z),
+                           ptr(dt_bias), int(bool(softplus)), ptr(y), ptr(last), 1)
+        return y, last
+    return scan, scan_from, scan_bwd, scan_zoh, conv, ssd
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(tmp_path, name):
     old, new = MUTANTS[name]
-    scan, scan_from, scan_bwd, scan_zoh, conv = _build_mutant(tmp_path, name, old, new)
+    scan, scan_from, scan_bwd, scan_zoh, conv, ssd = _build_mutant(tmp_path, name, old, new)
     caught = []
     with np.errstate(all="ignore"):
         for check in pins.ALL_CHECKS:
@@ -167,6 +182,16 @@ def test_planted_mistake_is_caught(tmp_path, name):
         for check in pins.CONV_CHECKS:
             try:
                 check(conv)
+            except AssertionError:
+                caught.append(check.__name__)
+        for check in pins.SSD_CHECKS:
+            try:
+                check(ssd)
+            except AssertionError:
+                caught.append(check.__name__)
+        for check in pins.SSD_SCAN_CHECKS:
+            try:
+                check(ssd, scan_from)
             except AssertionError:
                 caught.append(check.__name__)
         for check in pins.BWD_CHECKS:

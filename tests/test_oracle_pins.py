@@ -39,6 +39,28 @@ def test_oracle_conv_pin(oracle_mod, check):
     check(_conv(oracle_mod))
 
 
+def _ssd(oracle_mod):
+    def f(x, dt, A, B, C, D, z, dt_bias, softplus, h0):
+        return oracle_mod.ssd(x, dt, A, B, C, D=D, z=z, dt_bias=dt_bias, softplus=softplus, h0=h0, threads=2)
+    return f
+
+
+def _scan_from(oracle_mod):
+    def f(u, x, A, B, C, D, z, bias, softplus, h0):
+        return oracle_mod.scan(u, x, A, B, C, D=D, z=z, delta_bias=bias, softplus=softplus, threads=2, h0=h0)
+    return f
+
+
+@pytest.mark.parametrize("check", pins.SSD_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_ssd_pin(oracle_mod, check):
+    check(_ssd(oracle_mod))
+
+
+@pytest.mark.parametrize("check", pins.SSD_SCAN_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_ssd_scan_pin(oracle_mod, check):
+    check(_ssd(oracle_mod), _scan_from(oracle_mod))
+
+
 def test_oracle_bwd_rejects_zoh(oracle_mod):
     """The oracle's gradients cover the simplified input term only."""
     lib = oracle_mod._load()
