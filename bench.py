@@ -48,6 +48,39 @@ WORKLOADS = {
     "c3_block": "conv1d (width 4) + SiLU fused into the selective scan B8 L2048 D5120 N16, bf16 I/O, fp32 state, "
                 "SiLU(z) gate, D skip, last_state",
 }
+WORKLOADS["ssd"] = ("Mamba-2 SSD layer B8 L2048 H80 P64 N64 G1 (model width 5120), bf16 I/O, fp32 state, "
+                    "SiLU(z) gate, D skip, last_state")
+
+
+def ssd_alg_bytes(bsz, L, H, P, G, N):
+    """x, z read and y written (bf16); dt (bf16) per head; B, C (bf16) per group; A, D,
+    dt_bias; the final state (fp32)."""
+    return bsz * L * H * P * 2 * 3 + bsz * L * H * 2 + bsz * L * G * N * 2 * 2 + H * 12 + bsz * H * P * N * 4
+
+
+def cpu_baseline_ssd(c, alg_bytes_full, target_s=20.0):
+    """The fp64 oracle's SSD layer on a sample of heads (heads are independent)."""
+    from oracle import oracle
+    oracle.build(force=False)
+    threads = min(16, oracle.default_threads())
+
+    def run(sel):
+        oracle.ssd(c.values("x")[:, :, sel], c.values("dt")[:, :, sel], c.A[sel], c.values("B"), c.values("C"),
+                   D=c.Dskip[sel], z=c.values("z")[:, :, sel], dt_bias=c.dt_bias[sel], softplus=True,
+                   threads=threads)
+    t = time.perf_counter()
+    run(np.array([0]))
+    per_h = time.perf_counter() - t
+    k = int(min(c.H, max(1, target_s / max(per_h, 1e-9))))
+    sel = np.unique(np.linspace(0, c.H - 1, k).astype(np.int64))
+    t = time.perf_counter()
+    run(sel)
+    dt = time.perf_counter() - t
+    return {"value": round(alg_bytes_full * len(sel) / c.H / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{len(sel)} of {c.H} heads x all {c.bsz} sequences x {c.L} tokens (fp64 oracle)"}
+
+
 # The fused convolution adds, per (token, channel), 4 FMAs and SiLU (multiply, exp2 at half
 # rate, add, reciprocal at half rate): 10 issue slots.
 SLOTS_PER_CHTOK_CONV = 10
@@ -268,9 +301,11 @@ def main():
     wl = args.workload
     if wl == "c3_conv":
         case = inputs.conv_case(8, 2048, 5120, 4, "bf16", state=True, seed=185, name="c3_conv")
+    elif wl == "ssd":
+        case = inputs.ssd_case(8, 2048, 80, 64, 1, 64, seed=230, name="ssd")
     else:
         case = inputs.config_case("c3" if wl in ("c3_bwd", "c3_zoh", "c3_block") else wl)
-    io_bytes = 2 if case.io == "bf16" else 4
+    io_bytes = 2 if getattr(case, "io", "bf16") == "bf16" else 4
 
     def td(a):
         if a is None:
@@ -297,6 +332,19 @@ def main():
         def one(i):
             calls[i % case.steps]()
         plan = "one step kernel per call"
+    elif wl == "ssd":
+        c = case
+        sx, sdt, sB, sC, sz = (td(a) for a in (c.x, c.dt, c.B, c.C, c.z))
+        sA, sD, sbias = td(c.A), td(c.Dskip), td(c.dt_bias)
+        ys = torch.empty_like(sx)
+        lss = torch.empty((c.bsz, c.H, c.P, c.N), dtype=torch.float32, device=dev)
+        alg = ssd_alg_bytes(c.bsz, c.L, c.H, c.P, c.G, c.N)
+        chtok = c.bsz * c.L * c.H * c.P
+        elements = chtok * c.N
+
+        def one(i):
+            ssmscan.ssd_fwd(sx, sdt, sA, sB, sC, D=sD, z=sz, dt_bias=sbias, y=ys, last_state=lss)
+        plan = "one workgroup per (sequence, head), chunks of 64 tokens, four 64x64x64 bf16 MFMA products per chunk"
     elif wl == "c3_conv":
         bsz, L, D, width = case.bsz, case.L, case.D, case.width
         x, st_in = td(case.x), td(case.state)
@@ -410,7 +458,7 @@ def main():
     work_ops = elements * slots + (chtok * SLOTS_PER_CHTOK_CONV if wl == "c3_block" else 0)
     lane_ops = work_ops / kern_s / 1e12
     traffic = counter_traffic(wl)
-    if wl in ("c5", "c3_conv"):
+    if wl in ("c5", "c3_conv", "ssd"):
         roof = {"bound": "hbm", "achieved": round(kern_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(kern_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
     else:
@@ -426,6 +474,7 @@ def main():
         try:
             cpu = (cpu_baseline_step(case, alg) if wl == "c5" else cpu_baseline_bwd(case, alg) if wl == "c3_bwd"
                    else cpu_baseline_conv(case, alg) if wl == "c3_conv"
+                   else cpu_baseline_ssd(case, alg) if wl == "ssd"
                    else cpu_baseline_block(case, cc, alg) if wl == "c3_block"
                    else cpu_baseline_scan(case, alg, exact_zoh=wl == "c3_zoh"))
         except Exception as e:  # the GPU figures stand without it
@@ -444,7 +493,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": WORKLOADS[wl], "io_dtype": case.io, "plan": plan,
+        "config": {"workload": WORKLOADS[wl], "io_dtype": getattr(case, "io", "bf16"), "plan": plan,
                    "channel_tokens_per_step": chtok, "alg_bytes_per_step": alg},
         "hbm_pct_of_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "channel_tokens_per_s": round(chtok / step_s, 1),

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SSMSCAN_VERSION 6
+#define SSMSCAN_VERSION 7
 
 /* Bits of the `flags` argument of the scan entry points. */
 #define SSM_SCAN_SOFTPLUS 1     /* step size = softplus(delta + delta_bias) */
@@ -220,6 +220,37 @@ SSMSCAN_API int ssm_scan_fwd_conv(const void *x, const float *conv_w, const floa
                       const void *z, const float *delta_bias, int flags, void *y, float *last_state,
                       void *u_out, const ssm_dims *dims, void *workspace, size_t workspace_bytes,
                       void *stream);
+
+/* Sizes of Mamba-2's state space dual layer (ssm_ssd_fwd). */
+typedef struct {
+    int64_t batch;     /* sequences */
+    int64_t seqlen;    /* tokens per sequence */
+    int64_t nheads;    /* heads H */
+    int64_t headdim;   /* channels per head P (64) */
+    int64_t ngroups;   /* groups G of the B / C projections; H % G == 0 */
+    int64_t dstate;    /* states N (64) */
+    int32_t io_dtype;  /* SSM_IO_BF16 */
+    int32_t reserved;  /* 0 */
+} ssm_ssd_dims;
+
+/* Mamba-2's state space dual layer (SSD): the selective scan with a scalar state matrix
+ * per head, computed in its chunked matrix form on the matrix cores (the sequence map is a
+ * 1-semiseparable matrix: mugbit.ir, Mamba-2 / structured state space duality).  Per head h
+ * (channels h*P .. h*P+P-1, group g = h / (H/G)):
+ *   dt_t     = softplus(dt[t,h] + dt_bias[h])  (SSM_SCAN_SOFTPLUS), else dt + dt_bias
+ *   S_t      = exp(dt_t A[h]) S_{t-1} + dt_t x_t B_t[g]^T      (P x N state, from zero)
+ *   y_t      = (S_t C_t[g] + D[h] x_t) * silu(z_t)              (z optional)
+ *   x, z, y    : [batch][seqlen][nheads][headdim] bf16
+ *   dt         : [batch][seqlen][nheads] bf16
+ *   A, D, dt_bias : [nheads] fp32 (D and dt_bias may be NULL)
+ *   B, C       : [batch][seqlen][ngroups][dstate] bf16
+ *   last_state : [batch][nheads][headdim][dstate] fp32 output, or NULL
+ * Supported: io_dtype SSM_IO_BF16, headdim 64, dstate 64 (SSM_ERR_DTYPE / SSM_ERR_SHAPE
+ * otherwise); x, z, y, B, C 16-byte aligned.  Products take bf16 operands with fp32
+ * accumulation; the state is carried in fp32.  Returns SSM_OK or a negative ssm_status. */
+SSMSCAN_API int ssm_ssd_fwd(const void *x, const void *dt, const float *A, const void *B, const void *C,
+                const float *D, const void *z, const float *dt_bias, int flags, void *y, float *last_state,
+                const ssm_ssd_dims *dims, void *stream);
 
 /* One recurrent (inference) step for `batch` independent sequences: the constant-memory
  * recurrent form (shakilmahmud.com section 3; urworte.de "Methodische Grundlagen").

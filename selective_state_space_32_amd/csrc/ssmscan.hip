@@ -14,6 +14,7 @@
 #include "step_kernel.h"
 #include "bwd_kernel.h"
 #include "conv_kernel.h"
+#include "ssd_kernel.h"
 
 namespace {
 
@@ -632,6 +633,47 @@ int ssm_conv1d_fwd(const void *x, const float *w, const float *bias, int width, 
     const bool silu = (flags & SSM_CONV_SILU) != 0;
     if (es == 2) return launch_conv<uint16_t>(width, silu, x, w, bias, state_in, out, state_out, &d, st);
     return launch_conv<float>(width, silu, x, w, bias, state_in, out, state_out, &d, st);
+}
+
+int ssm_ssd_fwd(const void *x, const void *dt, const float *A, const void *B, const void *C, const float *D,
+                const void *z, const float *dt_bias, int flags, void *y, float *last_state, const ssm_ssd_dims *dims,
+                void *stream) {
+    if (!dims) return fail(SSM_ERR_NULL, "dims is NULL");
+    const int64_t bsz = dims->batch, L = dims->seqlen, H = dims->nheads, P = dims->headdim, G = dims->ngroups,
+                  N = dims->dstate;
+    if (bsz < 0 || L < 0 || H < 0 || P < 0 || G < 1 || N < 0)
+        return fail(SSM_ERR_SHAPE, "negative size or ngroups < 1");
+    if (dims->io_dtype != SSM_IO_BF16) return fail(SSM_ERR_DTYPE, "the SSD layer takes bf16 I/O only");
+    if (P != ssm::kSsdP || N != ssm::kSsdN)
+        return fail(SSM_ERR_SHAPE, "headdim %lld and dstate %lld: the SSD kernel supports 64 and 64", (long long)P,
+                    (long long)N);
+    if (H % G != 0) return fail(SSM_ERR_SHAPE, "nheads %lld is not a multiple of ngroups %lld", (long long)H,
+                                (long long)G);
+    if (H > kMaxDim || bsz > kMaxDim || (bsz > 0 && H > (int64_t(1) << 31) / bsz))
+        return fail(SSM_ERR_SHAPE, "batch*nheads exceeds 2^31 (grid size)");
+    if (bsz > 0 && H > 0 && L > kMaxElems / bsz / H / P) return fail(SSM_ERR_SHAPE, "too many elements");
+    if (flags & ~SSM_SCAN_SOFTPLUS) return fail(SSM_ERR_FLAGS, "flags 0x%x: the SSD layer takes the softplus flag only",
+                                                flags);
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) || !aligned(z, 16) ||
+        !aligned(dt, 2) || !aligned(A, 4) || !aligned(D, 4) || !aligned(dt_bias, 4) || !aligned(last_state, 4))
+        return fail(SSM_ERR_ALIGN, "x, z, y, B, C must be 16-byte aligned and the others aligned to their element size");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (bsz == 0 || H == 0) return ok();
+    if (!A || (L > 0 && (!x || !dt || !B || !C || !y))) return fail(SSM_ERR_NULL, "required pointer is NULL");
+    if (L == 0) {
+        if (last_state) fill_zero(last_state, bsz * H * P * N, st);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+        return ok();
+    }
+    hipLaunchKernelGGL(ssm::ssd_chunk_kernel, dim3((unsigned)(bsz * H)), dim3(256), 0, st,
+                       static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(dt), A,
+                       static_cast<const uint16_t *>(B), static_cast<const uint16_t *>(C), D,
+                       static_cast<const uint16_t *>(z), dt_bias, static_cast<uint16_t *>(y), last_state, L, (int)H,
+                       (int)G, (flags & SSM_SCAN_SOFTPLUS) ? 1 : 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
 }
 
 }  // extern "C"

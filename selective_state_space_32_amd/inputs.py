@@ -24,7 +24,8 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "bf16_bits", "bf16_to_f32", "ScanCase", "StepCase", "ConvCase", "scan_case", "step_case", "conv_case",
+    "bf16_bits", "bf16_to_f32", "ScanCase", "StepCase", "ConvCase", "SsdCase", "scan_case", "step_case",
+    "conv_case", "ssd_case",
     "config_case", "CONFIGS",
 ]
 
@@ -234,6 +235,52 @@ def conv_case(bsz: int, L: int, D: int, width: int = 4, io: str = "bf16", *, bia
     x = _io(rng.standard_normal((bsz, L, D), dtype=np.float32), io)
     st = _io(rng.standard_normal((bsz, width - 1, D), dtype=np.float32), io) if state else None
     return ConvCase(name, io, bsz, L, D, width, x, w, b, st, seed)
+
+
+@dataclasses.dataclass
+class SsdCase:
+    """Inputs of one SSD layer call.  x, z: [bsz][L][H][P] bf16 bits; dt: [bsz][L][H] bf16 bits;
+    B, C: [bsz][L][G][N] bf16 bits; A, D, dt_bias: [H] fp32."""
+    name: str
+    bsz: int
+    L: int
+    H: int
+    P: int
+    G: int
+    N: int
+    x: np.ndarray
+    dt: np.ndarray
+    A: np.ndarray
+    B: np.ndarray
+    C: np.ndarray
+    Dskip: Optional[np.ndarray]
+    z: Optional[np.ndarray]
+    dt_bias: Optional[np.ndarray]
+    softplus: bool
+    seed: int
+
+    def values(self, field: str) -> Optional[np.ndarray]:
+        a = getattr(self, field)
+        if a is None:
+            return None
+        return bf16_to_f32(a) if a.dtype == np.uint16 else a
+
+
+def ssd_case(bsz: int, L: int, H: int, P: int = 64, G: int = 1, N: int = 64, *, gate: bool = True,
+             skip: bool = True, seed: int = 0, name: str = "ssd") -> SsdCase:
+    """Draw order A, D, dt_bias, x, dt, B, C, z.  A = -exp(U[log 1, log 16]) per head; dt_bias =
+    log(expm1(U[1e-3, 0.1])) (step sizes between 1e-3 and 0.1 at dt = 0); dt ~ 0.5 N(0, 1);
+    x, B, C, z ~ N(0, 1); D ~ N(0, 1).  bf16 tensors are the RNE rounding of fp32 draws."""
+    rng = np.random.default_rng(seed)
+    A = (-np.exp(rng.uniform(0.0, np.log(16.0), H))).astype(np.float32)
+    Dskip = rng.standard_normal(H).astype(np.float32) if skip else None
+    dt_bias = np.log(np.expm1(rng.uniform(1e-3, 0.1, H))).astype(np.float32)
+    x = bf16_bits(rng.standard_normal((bsz, L, H, P), dtype=np.float32))
+    dt = bf16_bits((0.5 * rng.standard_normal((bsz, L, H))).astype(np.float32))
+    B = bf16_bits(rng.standard_normal((bsz, L, G, N), dtype=np.float32))
+    C = bf16_bits(rng.standard_normal((bsz, L, G, N), dtype=np.float32))
+    z = bf16_bits(rng.standard_normal((bsz, L, H, P), dtype=np.float32)) if gate else None
+    return SsdCase(name, bsz, L, H, P, G, N, x, dt, A, B, C, Dskip, z, dt_bias, True, seed)
 
 
 # The five measured workloads (plus the LTI variant of the tiny one).

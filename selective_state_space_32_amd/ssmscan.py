@@ -28,6 +28,12 @@ class ssm_dims(ctypes.Structure):
                 ("dstate", ctypes.c_int64), ("io_dtype", ctypes.c_int32), ("chunk_len", ctypes.c_int32)]
 
 
+class ssm_ssd_dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("ngroups", ctypes.c_int64), ("dstate", ctypes.c_int64),
+                ("io_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 class SSMError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"{STATUS.get(code, code)}: {msg}")
@@ -62,6 +68,8 @@ def _load() -> ctypes.CDLL:
     lib.ssm_scan_fwd_conv.argtypes = [P, P, P, ctypes.c_int, P, P, P, P, P, P, P, ctypes.c_int, P, P, P, D, P,
                                       ctypes.c_size_t, P]
     lib.ssm_scan_fwd_conv.restype = ctypes.c_int
+    lib.ssm_ssd_fwd.argtypes = [P] * 8 + [ctypes.c_int, P, P, ctypes.POINTER(ssm_ssd_dims), P]
+    lib.ssm_ssd_fwd.restype = ctypes.c_int
     return lib
 
 
@@ -443,3 +451,36 @@ def scan_fwd_conv_call(x, conv_w, conv_b, delta, A, B, C, D=None, z=None, delta_
     def call(_args=args, _keep=keep):
         _check(lib.ssm_scan_fwd_conv(*_args))
     return call
+
+
+def ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+            D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+            dt_bias: Optional[torch.Tensor] = None, softplus: bool = True, *, y: Optional[torch.Tensor] = None,
+            last_state: Optional[torch.Tensor] = None, return_last_state: bool = True, stream=None):
+    """Mamba-2's SSD layer (ssm_ssd_fwd).  x, z: (batch, L, H, P) bfloat16; dt: (batch, L, H)
+    bfloat16; A, D, dt_bias: (H,) float32; B, C: (batch, L, G, N) bfloat16.
+    Returns (y (batch, L, H, P), last_state (batch, H, P, N) float32 or None)."""
+    bsz, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    bf = torch.bfloat16
+    _need(x, "x", (bsz, L, H, P), bf, dev)
+    _need(dt, "dt", (bsz, L, H), bf, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _need(B, "B", (bsz, L, G, N), bf, dev)
+    _need(C, "C", (bsz, L, G, N), bf, dev)
+    if D is not None:
+        _need(D, "D", (H,), torch.float32, dev)
+    if z is not None:
+        _need(z, "z", (bsz, L, H, P), bf, dev)
+    if dt_bias is not None:
+        _need(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    if y is None:
+        y = torch.empty((bsz, L, H, P), dtype=bf, device=dev)
+    if last_state is None and return_last_state:
+        last_state = torch.empty((bsz, H, P, N), dtype=torch.float32, device=dev)
+    dims = ssm_ssd_dims(bsz, L, H, P, G, N, SSM_IO_BF16, 0)
+    _check(lib.ssm_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+                           1 if softplus else 0, _ptr(y), _ptr(last_state), ctypes.byref(dims),
+                           _stream_handle(stream)))
+    return y, last_state

@@ -28,7 +28,7 @@ def b():
 def test_header_declares_the_entry_points():
     syms = set(declared_symbols())
     assert {"ssm_scan_fwd", "ssm_scan_fwd_from", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes", "ssm_step",
-            "ssm_conv1d_fwd", "ssm_scan_fwd_conv",
+            "ssm_conv1d_fwd", "ssm_scan_fwd_conv", "ssm_ssd_fwd",
             "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_last_error", "ssm_version"} <= syms
 
 
@@ -175,6 +175,20 @@ def test_conv_scan_validation(b):
     assert call(flags=3) == -8
     assert call(w=0) == -1
     assert call(x=FAKE + 1) == -4          # a bf16 x must be 2-byte aligned
+
+
+def test_ssd_validation(b):
+    P = ctypes.c_void_p
+
+    def call(x=FAKE, io=1, hd=64, ds=64, H=8, G=2, flags=1):
+        d = b.ssm_ssd_dims(2, 100, H, hd, G, ds, io, 0)
+        return b.lib.ssm_ssd_fwd(P(x), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None, None, flags, P(FAKE), None,
+                                 ctypes.byref(d), None)
+    assert call(io=0) == -3
+    assert call(hd=32) == -2 and call(ds=128) == -2
+    assert call(G=3) == -2
+    assert call(flags=3) == -8
+    assert call(x=FAKE + 2) == -4
 
 
 def test_misaligned_rejected(b):
