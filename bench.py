@@ -290,7 +290,7 @@ def main():
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": max(1, args.steps)}))
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the scan shards "
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); the scan shards "
               "with no communication across sequences and channels, so run one process per GPU.", file=sys.stderr)
         sys.exit(2)
 

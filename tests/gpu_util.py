@@ -1,5 +1,5 @@
 """Helpers for the GPU parity tests: moving generated cases to the device and the
-tolerance metrics the outputs are judged by."""
+tolerance metrics the outputs are checked with."""
 from __future__ import annotations
 
 import numpy as np

@@ -1,6 +1,6 @@
 """Parity of the HIP path (through the C ABI) with the fp64 oracle on the same seeded inputs.
 
-Tolerances (north-star): max error <= 1e-4 rms(y) for fp32 I/O and <= 3e-3 rms(y) for
+Tolerances: max error <= 1e-4 rms(y) for fp32 I/O and <= 3e-3 rms(y) for
 bf16 I/O, the bf16 error measured before the kernel's own final rounding to bf16 (see
 gpu_util.y_error); last_state within the same factor of rms(last_state).
 """
