@@ -245,8 +245,8 @@ typedef struct {
  *   A, D, dt_bias : [nheads] fp32 (D and dt_bias may be NULL)
  *   B, C       : [batch][seqlen][ngroups][dstate] bf16
  *   last_state : [batch][nheads][headdim][dstate] fp32 output, or NULL
- * Supported: io_dtype SSM_IO_BF16, headdim 64, dstate 64 (SSM_ERR_DTYPE / SSM_ERR_SHAPE
- * otherwise); x, z, y, B, C 16-byte aligned.  Products take bf16 operands with fp32
+ * Supported: io_dtype SSM_IO_BF16, headdim 64, dstate 64, nheads*headdim <= 2^24
+ * (SSM_ERR_DTYPE / SSM_ERR_SHAPE otherwise); x, z, y, B, C 16-byte aligned.  Products take bf16 operands with fp32
  * accumulation; the state is carried in fp32.  Returns SSM_OK or a negative ssm_status. */
 SSMSCAN_API int ssm_ssd_fwd(const void *x, const void *dt, const float *A, const void *B, const void *C,
                 const float *D, const void *z, const float *dt_bias, int flags, void *y, float *last_state,

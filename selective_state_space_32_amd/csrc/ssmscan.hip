@@ -652,6 +652,8 @@ int ssm_ssd_fwd(const void *x, const void *dt, const float *A, const void *B, co
     if (H > kMaxDim || bsz > kMaxDim || (bsz > 0 && H > (int64_t(1) << 31) / bsz))
         return fail(SSM_ERR_SHAPE, "batch*nheads exceeds 2^31 (grid size)");
     if (bsz > 0 && H > 0 && L > kMaxElems / bsz / H / P) return fail(SSM_ERR_SHAPE, "too many elements");
+    if (H * P > (int64_t(1) << 24))   // a chunk's rows are addressed with 32-bit offsets
+        return fail(SSM_ERR_SHAPE, "nheads*headdim %lld exceeds 2^24", (long long)(H * P));
     if (flags & ~SSM_SCAN_SOFTPLUS) return fail(SSM_ERR_FLAGS, "flags 0x%x: the SSD layer takes the softplus flag only",
                                                 flags);
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) || !aligned(z, 16) ||

@@ -187,6 +187,7 @@ def test_ssd_validation(b):
     assert call(io=0) == -3
     assert call(hd=32) == -2 and call(ds=128) == -2
     assert call(G=3) == -2
+    assert call(H=(1 << 18) + 1, G=1) == -2   # nheads*headdim above 2^24
     assert call(flags=3) == -8
     assert call(x=FAKE + 2) == -4
 
