@@ -13,7 +13,11 @@
 // row access of a wave is one contiguous span.  The W-1 inputs before the run are loaded
 // first (from x, or the state before token 0); the run's rows then come kConvBatch at a
 // time into two register buffers, the next batch requested before the current one is
-// used, and the sliding window of the last W-1 inputs stays in registers.  The run that
+// used, and the sliding window of the last W-1 inputs stays in registers.  Every load is
+// issued unconditionally (rows clamped into the run; inputs before token 0 without a state
+// are loaded from row 0 and replaced by zeros): a conditional load leaves the compiler a
+// merge of old and new register values, and the copies it makes there wait for the loads at
+// once.  The run that
 // ends the sequence writes the final window as the state that continues it.  Bound: HBM
 // (x read and out written once; the W-1 halo rows of a run are the previous run's last
 // rows, read again).
@@ -53,16 +57,6 @@ conv1d_kernel(const IO *__restrict__ x, const float *__restrict__ w, const float
         const int64_t run = pr - b * runs;
         const int64_t t0 = run * R;
         const int64_t t1 = min(L, t0 + R);
-        auto load_row = [&](const IO *p, int64_t row, float (&v)[V]) {   // V channels of one row
-            if constexpr (VEC) {
-                uint32_t raw[WD];
-                VIO::load(p, row * D + d0, raw);
-#pragma unroll
-                for (int i = 0; i < V; ++i) v[i] = VIO::get(raw, i);
-            } else {
-                v[0] = io<IO>::ld(p, row * D + d0);
-            }
-        };
         // a row kept as raw I/O words until it is used (half the registers for bf16)
         auto load_raw = [&](const IO *p, int64_t row, uint32_t (&r)[WD]) {
             if constexpr (VEC && WD == 2) {   // a plain (cached) load: the halo rows are read twice
@@ -86,24 +80,26 @@ conv1d_kernel(const IO *__restrict__ x, const float *__restrict__ w, const float
             else io<IO>::st(p, row * D + d0, v[0]);
         };
 
-        // the window: the H inputs before token t0, oldest first
+        // the window: the H inputs before token t0, oldest first (all loads issued, then used)
         float win[H > 0 ? H : 1][V];
+        {
+            uint32_t wr[H > 0 ? H : 1][WD];
 #pragma unroll
-        for (int j = 0; j < H; ++j) {
-            const int64_t t = t0 - H + j;
-            if (t >= 0) {
-                load_row(x, b * L + t, win[j]);
-            } else if (st_in) {
-                load_row(st_in, b * H + (t + H), win[j]);
-            } else {
+            for (int j = 0; j < H; ++j) {
+                const int64_t t = t0 - H + j;
+                const bool from_x = t >= 0 || !st_in;   // (one load instruction either way)
+                load_raw(from_x ? x : st_in, from_x ? b * L + max(t, (int64_t)0) : b * H + (t + H), wr[j]);
+            }
 #pragma unroll
-                for (int i = 0; i < V; ++i) win[j][i] = 0.0f;
+            for (int j = 0; j < H; ++j) {
+                const bool zero = t0 - H + j < 0 && !st_in;
+#pragma unroll
+                for (int i = 0; i < V; ++i) win[j][i] = zero ? 0.0f : widen(wr[j], i);
             }
         }
         // the run in batches of kConvBatch rows, two register buffers: the next batch's rows are
-        // requested before the current batch is used (rows past the run are not loaded)
+        // requested before the current batch is used (rows past the run: the run's last row again)
         auto load_batch = [&](int64_t tb, uint32_t (&buf)[kConvBatch][WD]) {
-            if (tb >= t1) return;
 #pragma unroll
             for (int r = 0; r < kConvBatch; ++r) load_raw(x, b * L + min(tb + r, t1 - 1), buf[r]);
         };
