@@ -11,8 +11,9 @@
 //   H      <- exp(c_{Q-1}) H + Bw^T X,  Bw[s,n] = B[s,n] exp(c_{Q-1} - c_s) dt_s
 //   y      = (Y + D x) * silu(z)
 // Each product is 64 x 64 x 64 here (Q = P = N = 64): one workgroup per (sequence, head),
-// four waves, each owning one 32 x 32 quadrant of every product, computed with
-// v_mfma_f32_32x32x16_bf16 (bf16 operands, fp32 accumulation).  The products are taken
+// eight waves, each owning a 16-row band and two 16 x 16 blocks of every product, computed
+// with v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32 accumulation; each operand fetched once
+// per step for both blocks and both high / low parts).  The products are taken
 // transposed (G^T = B C^T, Y^T = X^T M^T, and the state as H[n][p]), so that the four
 // consecutive accumulator rows a lane holds are four consecutive elements of the operand
 // tile they are written to (one 8-byte LDS write) and each lane's output column is one
@@ -35,6 +36,7 @@ namespace ssm {
 constexpr int kSsdQ = 64;          // tokens per chunk
 constexpr int kSsdP = 64;          // channels per head
 constexpr int kSsdN = 64;          // states
+constexpr int kSsdThreads = 512;   // eight waves per (sequence, head)
 // Operand tiles are 64 x 64 bf16, element (row, k) at sw(row, k): rows of 72 (144 bytes:
 // 16-byte aligned, and 16-byte reads of eight consecutive rows fall in distinct banks), or,
 // for the C tile, swz(row, k): unpadded rows whose 16-byte unit k / 8 is stored at unit
@@ -51,28 +53,7 @@ __device__ __forceinline__ int zsw8(int t, int u) { return t * 64 + ((u ^ (t & 1
 __device__ __forceinline__ int zsw16(int t, int v) { return t * 64 + ((v ^ ((t & 15) >> 1)) << 3); }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-// One 32 x 32 block of A B over a contraction of 16 * KS: A rows from tile `a` starting at
-// row a0, B columns from tile `b` ([col][k]) starting at row b0 (multiples of 8; ZA / ZB:
-// the tile is swizzled); the lane fetches its 8 consecutive k of row / column (lane % 32) at
-// offset 8 * (lane / 32) of each 16-wide step.
-template <int KS, bool ZA = false, bool ZB = false>
-__device__ __forceinline__ f32x16_t mma_block(const __bf16 *a, int a0, const __bf16 *b, int b0, int lane,
-                                              f32x16_t acc) {
-    const int r = lane & 31, ko = (lane >> 5) * 8;
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(a + tix<ZA>(a0 + r, 16 * k + ko));
-        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(b + tix<ZB>(b0 + r, 16 * k + ko));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
-    }
-    return acc;
-}
-
-// Row (within the 32 x 32 block) of accumulator element e of this lane; the column is lane % 32.
-__device__ __forceinline__ int acc_row(int e, int lane) { return (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3); }
 
 // Inclusive sum over the 64 lanes of a wave (DPP: row_shr 1, 2, 4, 8, row_bcast 15, 31).
 __device__ __forceinline__ float wave_incl_sum(float v) {
@@ -85,9 +66,76 @@ __device__ __forceinline__ float wave_incl_sum(float v) {
     return v;
 }
 
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+
+// Operand and accumulator layout of v_mfma_f32_16x16x32_bf16: a lane fetches the 8
+// consecutive k at offset 8 (lane / 16) of each 32-wide step, for A row / B column
+// lane % 16; accumulator element e of a lane is row 4 (lane / 16) + e, column lane % 16.
+// Two 16 x 16 blocks side by side (B columns from rows b0 and b1 of tile `b`) over a
+// contraction of 32 * KS, each operand fetched once per step:
+//   mma16_hl_a: A = ah + al (high and low parts, rows a0): acc_i += (ah + al) B_i
+//   mma16_hl_b: B = bh + bl (high and low parts): acc_i += A (bh_i + bl_i)
+//   mma16_x2  : acc_i += A B_i where enabled
+template <int KS, bool ZB>
+__device__ __forceinline__ void mma16_hl_a(const __bf16 *ah, const __bf16 *al, int a0, const __bf16 *b, int b0, int b1,
+                                           int lane, f32x4v_t &acc0, f32x4v_t &acc1) {
+    const int r = lane & 15, ko = (lane >> 4) * 8;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        const int kk = 32 * k + ko;
+        const bf16x8_t hv = *reinterpret_cast<const bf16x8_t *>(ah + sw(a0 + r, kk));
+        const bf16x8_t lv = *reinterpret_cast<const bf16x8_t *>(al + sw(a0 + r, kk));
+        const bf16x8_t b0v = *reinterpret_cast<const bf16x8_t *>(b + tix<ZB>(b0 + r, kk));
+        const bf16x8_t b1v = *reinterpret_cast<const bf16x8_t *>(b + tix<ZB>(b1 + r, kk));
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, b0v, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, b1v, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lv, b0v, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lv, b1v, acc1, 0, 0, 0);
+    }
+}
+// (bh padded, bl swizzled)
+template <int KS>
+__device__ __forceinline__ void mma16_hl_b(const __bf16 *a, int a0, const __bf16 *bh, const __bf16 *bl, int b0, int b1,
+                                           int lane, f32x4v_t &acc0, f32x4v_t &acc1) {
+    const int r = lane & 15, ko = (lane >> 4) * 8;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        const int kk = 32 * k + ko;
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(a + sw(a0 + r, kk));
+        const bf16x8_t h0 = *reinterpret_cast<const bf16x8_t *>(bh + sw(b0 + r, kk));
+        const bf16x8_t h1 = *reinterpret_cast<const bf16x8_t *>(bh + sw(b1 + r, kk));
+        const bf16x8_t l0 = *reinterpret_cast<const bf16x8_t *>(bl + swz(b0 + r, kk));
+        const bf16x8_t l1 = *reinterpret_cast<const bf16x8_t *>(bl + swz(b1 + r, kk));
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, h0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, h1, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, l0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, l1, acc1, 0, 0, 0);
+    }
+}
+template <int KS, bool ZB>
+__device__ __forceinline__ void mma16_x2(const __bf16 *a, int a0, const __bf16 *b, int b0, int b1, bool en0, bool en1,
+                                         int lane, f32x4v_t &acc0, f32x4v_t &acc1) {
+    const int r = lane & 15, ko = (lane >> 4) * 8;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        const int kk = 32 * k + ko;
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(a + sw(a0 + r, kk));
+        if (en0) {
+            const bf16x8_t b0v = *reinterpret_cast<const bf16x8_t *>(b + tix<ZB>(b0 + r, kk));
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b0v, acc0, 0, 0, 0);
+        }
+        if (en1) {
+            const bf16x8_t b1v = *reinterpret_cast<const bf16x8_t *>(b + tix<ZB>(b1 + r, kk));
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b1v, acc1, 0, 0, 0);
+        }
+    }
+}
+
 // x, z, y: [bsz][L][H][P] bf16;  dt: [bsz][L][H] bf16;  A, Dv, dt_bias: [H] fp32;
 // B, C: [bsz][L][G][N] bf16;  last_state: [bsz][H][P][N] fp32 (or null).
 //
+// Eight waves; wave w owns, in every product, the 16-row band qi = w / 2 and the two 16 x 16
+// blocks j = 2 (w % 2) + bb (bb = 0, 1) of columns.
 // Tiles and their phases within a chunk (barriers 1-4):
 //   tC : C [t][n] (swizzled)          -> (2) M low part [t][s]
 //   tB : B [s][n]                     -> (2) M high part [t][s]
@@ -98,13 +146,14 @@ __device__ __forceinline__ float wave_incl_sum(float v) {
 // Between 1 and 2: Y3^T = H^T C^T and G^T = B C^T; between 2 and 3: M and Bw written; between
 // 3 and 4: the state update, Y^T = X^T M^T and the output; after 4: the new H^T, y out to
 // HBM, and the next chunk's C, B, X^T, z.
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+// (at most 128 registers: two workgroups of eight waves per CU)
+__global__ void __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(4)))
 ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt, const float *__restrict__ A,
                  const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm, const float *__restrict__ Dv,
                  const uint16_t *__restrict__ z, const float *__restrict__ dt_bias, uint16_t *__restrict__ y,
                  float *__restrict__ last_state, int64_t L, int H, int G, int softplus) {
     constexpr int Q = kSsdQ, P = kSsdP, N = kSsdN, LD = kSsdLd;
-    static_assert(Q == 64 && P == 64 && N == 64, "one 32 x 32 quadrant per wave of four");
+    static_assert(Q == 64 && P == 64 && N == 64, "a 16-row band and two 16 x 16 blocks per wave of eight");
     constexpr bool ZC = true;                         // tC is swizzled
     __shared__ __attribute__((aligned(16))) __bf16 tC[Q * 64];
     __shared__ __attribute__((aligned(16))) __bf16 tB[Q * LD];
@@ -112,19 +161,20 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
     __shared__ __attribute__((aligned(16))) __bf16 tH1[P * LD];
     __shared__ __attribute__((aligned(16))) __bf16 tH2[P * LD];
     __shared__ __attribute__((aligned(16))) __bf16 tZ[Q * 64];
-    // per-token values, four tokens per row padding of tX (tokens 4r..4r+3 in row r): c_t (in
-    // log2 units) and f_s = exp2(c_r - c_s) dt_s with r the first token of s's half-chunk
-    // (dt_s = 0 for tokens past the end)
+    // per-token values (formed by wave 0), four tokens per row padding of tX (tokens 4r..4r+3
+    // in row r): c_t (in log2 units), f_s = exp2(c_r - c_s) dt_s with r the first token of s's
+    // half-chunk, and the Bw weight w_s = exp2(c_last - c_s) dt_s (dt_s = 0 past the end)
     float *const s_pad = reinterpret_cast<float *>(tX + 64);   // row r at s_pad + r * LD / 2
     auto s_c4 = [&](int t) -> float * { return s_pad + (t >> 2) * (LD / 2) + (t & 3); };
     auto s_f4 = [&](int t) -> float * { return s_pad + (16 + (t >> 2)) * (LD / 2) + (t & 3); };
+    auto s_w4 = [&](int t) -> float * { return s_pad + (32 + (t >> 2)) * (LD / 2) + (t & 3); };
     typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int qi = w >> 1, qj = w & 1;                // this wave's quadrant: rows 32 qi, columns 32 qj
-    const int col = 32 * qj + (lane & 31);            // the lane's accumulator column
-    const int rq = (lane >> 5) * 4;                   // its rows: 32 qi + 8 gq + rq + (0..3), gq < 4
+    const int qi = w >> 1, qj = w & 1;                // row band 16 qi; column blocks 2 qj, 2 qj + 1
+    const int c16 = lane & 15;                        // the lane's column within a block
+    const int rq = (lane >> 4) * 4;                   // its rows: 16 qi + rq + (0..3)
     const int bh = blockIdx.x;
     const int b = bh / H, h = bh - b * H;
     const int g = h / (H / G);
@@ -139,30 +189,25 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
     const uint16_t *Bg = Bm + (int64_t)b * L * brow + (int64_t)g * N;
     const uint16_t *Cg = Cm + (int64_t)b * L * brow + (int64_t)g * N;
 
-    // staging maps: C and z rows coalesced (token tid / 8 + 32 i, 8 elements at 8 (tid % 8));
-    // X and B by token = lane (8 channels / states at group w + 4 i), so that the transposed
-    // LDS writes of one instruction fall in distinct banks.  Addresses: the chunk's base
-    // (uniform) plus a 32-bit offset per lane (64 rows of H P elements fit 32 bits).  z is read
-    // and y written once: streaming (non-temporal) accesses; x and B rows are read by eight
-    // instructions in 16-byte pieces and stay cached.
-    struct Raw { u32x4_t c[2], xv[2], bv[2], zv[2]; uint32_t dt; };
+    // staging maps: C and z rows coalesced (token tid / 8, 8 elements at 8 (tid % 8)); X and B
+    // by token = lane (8 channels / states at group w), so that the transposed LDS writes of
+    // one instruction fall in distinct banks.  Addresses: the chunk's base (uniform) plus a
+    // 32-bit offset per lane (64 rows of H P elements fit 32 bits).  z is read and y written
+    // once: streaming (non-temporal) accesses; x and B rows are read by eight waves in 16-byte
+    // pieces and stay cached.
+    struct Raw { u32x4_t c, xv, bv, zv; uint32_t dt; };
     const uint32_t xr32 = (uint32_t)xrow, br32 = (uint32_t)brow;
+    const int tr = tid / 8, tu = tid % 8;             // the thread's row and 16-byte unit (C, z, y)
     auto fetch = [&](int64_t t0, Raw &r) {
         const uint32_t lim = (uint32_t)min((int64_t)(Q - 1), L - 1 - t0);   // last token present
-        const uint16_t *xc = xh + t0 * xrow, *bc = Bg + t0 * brow, *cc = Cg + t0 * brow;
-        const uint32_t ts = min((uint32_t)lane, lim);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint32_t tc = min((uint32_t)(tid / 8 + 32 * i), lim);
-            r.c[i] = *reinterpret_cast<const u32x4_t *>(cc + (tc * br32 + (uint32_t)(tid % 8) * 8));
-            if (zh)
-                r.zv[i] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4_t *>(zh + t0 * xrow + (tc * xr32 + (uint32_t)(tid % 8) * 8)));
-            const uint32_t grp = (uint32_t)(w + 4 * i);
-            r.xv[i] = *reinterpret_cast<const u32x4_t *>(xc + (ts * xr32 + grp * 8));
-            r.bv[i] = *reinterpret_cast<const u32x4_t *>(bc + (ts * br32 + grp * 8));
-        }
-        r.dt = dt[((int64_t)b * L + t0) * H + h + ts * (uint32_t)H];
+        const uint32_t ts = min((uint32_t)lane, lim), tc = min((uint32_t)tr, lim);
+        r.c = *reinterpret_cast<const u32x4_t *>(Cg + t0 * brow + (tc * br32 + (uint32_t)tu * 8));
+        if (zh)
+            r.zv = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4_t *>(zh + t0 * xrow + (tc * xr32 + (uint32_t)tu * 8)));
+        r.xv = *reinterpret_cast<const u32x4_t *>(xh + t0 * xrow + (ts * xr32 + (uint32_t)w * 8));
+        r.bv = *reinterpret_cast<const u32x4_t *>(Bg + t0 * brow + (ts * br32 + (uint32_t)w * 8));
+        r.dt = dt[((int64_t)b * L + t0) * H + h + (w == 0 ? ts : 0u) * (uint32_t)H];   // (used by wave 0)
     };
     auto lo16 = [](uint32_t v) { return __builtin_bit_cast(__bf16, (uint16_t)(v & 0xffffu)); };
     auto hi16 = [](uint32_t v) { return __builtin_bit_cast(__bf16, (uint16_t)(v >> 16)); };
@@ -171,7 +216,7 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
         lo = (__bf16)(v - (float)hi);
     };
 
-    f32x16_t S = {};                                   // this wave's 32 x 32 block of H [n][p], fp32
+    f32x4v_t S[2] = {};                                // the state H [n][p]: rows n 16 qi.., columns p 16 j..
     Raw r;
     fetch(0, r);
     const int64_t nchunks = (L + Q - 1) / Q;
@@ -180,114 +225,105 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
         const int nt = (int)min((int64_t)Q, L - t0);
         // --- stage C, z, B (natural) and X^T (transposed); the step sizes and their running
         //     sum, token = lane, in every wave
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int tr = tid / 8 + 32 * i;
-            *reinterpret_cast<u32x4_t *>(&tC[tix<ZC>(tr, (tid % 8) * 8)]) = r.c[i];
-            if (zh) {
-                const u32x4_t zv = (tr & 1) ? u32x4_t{r.zv[i].z, r.zv[i].w, r.zv[i].x, r.zv[i].y} : r.zv[i];
-                *reinterpret_cast<u32x4_t *>(&tZ[zsw16(tr, tid % 8)]) = zv;
-            }
-            const int grp = w + 4 * i;
-            *reinterpret_cast<u32x4_t *>(&tB[sw(lane, grp * 8)]) = r.bv[i];
-            const uint32_t xw[4] = {r.xv[i].x, r.xv[i].y, r.xv[i].z, r.xv[i].w};
+        *reinterpret_cast<u32x4_t *>(&tC[swz(tr, tu * 8)]) = r.c;
+        if (zh) {
+            const u32x4_t zv = (tr & 1) ? u32x4_t{r.zv.z, r.zv.w, r.zv.x, r.zv.y} : r.zv;
+            *reinterpret_cast<u32x4_t *>(&tZ[zsw16(tr, tu)]) = zv;
+        }
+        *reinterpret_cast<u32x4_t *>(&tB[sw(lane, w * 8)]) = r.bv;
+        {
+            const uint32_t xw[4] = {r.xv.x, r.xv.y, r.xv.z, r.xv.w};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                tX[sw(grp * 8 + 2 * k, lane)] = lo16(xw[k]);
-                tX[sw(grp * 8 + 2 * k + 1, lane)] = hi16(xw[k]);
+                tX[sw(w * 8 + 2 * k, lane)] = lo16(xw[k]);
+                tX[sw(w * 8 + 2 * k + 1, lane)] = hi16(xw[k]);
             }
         }
-        const float v = bf16_to_f32((uint16_t)r.dt) + bias_h;
-        const float dl = lane < nt ? (softplus ? softplus_f32(v) : v) : 0.0f;   // padded tokens: identity steps
-        const float cl = a2 * wave_incl_sum(dl);
-        const float ctot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cl), 63));
-        const float c32 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cl), 32));
-        const float cref = qi ? c32 : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cl), 0));
-        if (w == 0) {
+        if (w == 0) {   // the step sizes and their running sum, token = lane
+            const float v = bf16_to_f32((uint16_t)r.dt) + bias_h;
+            const float dl = lane < nt ? (softplus ? softplus_f32(v) : v) : 0.0f;   // padded tokens: identity steps
+            const float cl = a2 * wave_incl_sum(dl);
+            const float ctot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cl), 63));
             const float c0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cl), 0));
+            const float c32 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cl), 32));
             *s_c4(lane) = cl;
             *s_f4(lane) = hw_exp2((lane < 32 ? c0 : c32) - cl) * dl;
+            *s_w4(lane) = hw_exp2(ctot - cl) * dl;
         }
-        const float wsl = hw_exp2(ctot - cl) * dl;    // Bw weight of token lane
-        const u32x4_t bcur[2] = {r.bv[0], r.bv[1]};
+        const u32x4_t bcur = r.bv;
         fetch(min(t0 + Q, (nchunks - 1) * Q), r);   // (the last chunk fetches itself again, unused)
         __syncthreads();                                // (1)
+        const float ctot = *s_c4(Q - 1);                // c_last
+        const float cref = *s_c4(qi >= 2 ? 32 : 0);     // c at the first token of this band's half-chunk
+        const float wsl = *s_w4(lane);                  // Bw weight of token lane
         // --- Y3^T = H^T C^T (the state entering the chunk) and G^T = B C^T
-        f32x16_t Y = {};
-        if (c > 0) {
-            Y = mma_block<N / 16, false, ZC>(tH1, 32 * qi, tC, 32 * qj, lane, Y);
-            Y = mma_block<N / 16, false, ZC>(tH2, 32 * qi, tC, 32 * qj, lane, Y);
-        }
-        f32x16_t Gt = {};
-        if (qi <= qj) Gt = mma_block<N / 16, false, ZC>(tB, 32 * qi, tC, 32 * qj, lane, Gt);   // zero for s > t
+        f32x4v_t Y[2] = {}, Gt[2] = {};
+        const int j0 = 2 * qj, j1 = 2 * qj + 1;         // this wave's column blocks
+        if (c > 0) mma16_hl_a<N / 32, ZC>(tH1, tH2, 16 * qi, tC, 16 * j0, 16 * j1, lane, Y[0], Y[1]);
+        if (qi <= j1)   // zero for s > t
+            mma16_x2<N / 32, ZC>(tB, 16 * qi, tC, 16 * j0, 16 * j1, qi <= j0, true, lane, Gt[0], Gt[1]);
         __syncthreads();                                // (2)
         // --- M [t][s] = G^T[s][t] exp2(c_t - c_s) dt_s (s <= t) + D (s = t): rows s of this
-        //     wave's quadrant, column t; four consecutive s per 8-byte write.  The decay is
-        //     exp2(c_t - c_r) f_s with r = 32 qi <= s <= t: both factors are at most 1 (times
-        //     dt_s), as c does not increase along the chunk (a <= 0, dt >= 0).
-        if (qi <= qj) {
-            const float et = hw_exp2(*s_c4(col) - cref);
+        //     wave's band, column t; four consecutive s per 8-byte write.  The decay is
+        //     exp2(c_t - c_r) f_s with r the first token of s's half-chunk (r <= s <= t): both
+        //     factors are at most 1 (times dt_s), as c does not increase along the chunk
+        //     (a <= 0, dt >= 0).  Blocks above the diagonal are written as zeros (some are read).
+        {
+            const int s0 = 16 * qi + rq;
+            const f32x4_t fs = *reinterpret_cast<const f32x4_t *>(s_f4(s0));
+            const float fsv[4] = {fs.x, fs.y, fs.z, fs.w};
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int s0 = 32 * qi + 8 * gq + rq;
-                const f32x4_t fs = *reinterpret_cast<const f32x4_t *>(s_f4(s0));
-                const float fsv[4] = {fs.x, fs.y, fs.z, fs.w};
-                bf16x4_t mh, ml;
+            for (int bb = 0; bb < 2; ++bb) {
+                const int j = 2 * qj + bb, t = 16 * j + c16;
+                bf16x4_t mh = {}, ml = {};
+                if (qi <= j) {
+                    const float et = hw_exp2(*s_c4(t) - cref);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float m = Gt[4 * gq + j] * et * fsv[j];
-                    if (qi == qj) {
-                        m = s0 + j <= col ? m : 0.0f;
-                        if (s0 + j == col) m += d_h;
+                    for (int e = 0; e < 4; ++e) {
+                        float m = Gt[bb][e] * et * fsv[e];
+                        if (qi == j) {
+                            m = s0 + e <= t ? m : 0.0f;
+                            if (s0 + e == t) m += d_h;
+                        }
+                        __bf16 hi, lo;
+                        split(m, hi, lo);
+                        mh[e] = hi;
+                        ml[e] = lo;
                     }
-                    __bf16 hi, lo;
-                    split(m, hi, lo);
-                    mh[j] = hi;
-                    ml[j] = lo;
                 }
-                *reinterpret_cast<bf16x4_t *>(&tB[sw(col, s0)]) = mh;
-                *reinterpret_cast<bf16x4_t *>(&tC[tix<ZC>(col, s0)]) = ml;
+                *reinterpret_cast<bf16x4_t *>(&tB[sw(t, s0)]) = mh;
+                *reinterpret_cast<bf16x4_t *>(&tC[swz(t, s0)]) = ml;
             }
         }
         // --- Bw^T [n][s] = B[s][n] exp2(c_last - c_s) dt_s, token s = lane
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int grp = w + 4 * i;
-            const uint32_t bw[4] = {bcur[i].x, bcur[i].y, bcur[i].z, bcur[i].w};
+        {
+            const uint32_t bw[4] = {bcur.x, bcur.y, bcur.z, bcur.w};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int o = sw(grp * 8 + 2 * k, lane);
+                const int o = sw(w * 8 + 2 * k, lane);
                 split(bf16_to_f32((uint16_t)(bw[k] & 0xffffu)) * wsl, tH1[o], tH2[o]);
                 split(bf16_to_f32((uint16_t)(bw[k] >> 16)) * wsl, tH1[o + LD], tH2[o + LD]);
             }
         }
         __syncthreads();                                // (3)
-        // --- H [n][p] <- exp2(c_last) H + Bw^T X   (rows n = 32 qi.., columns p = 32 qj..)
-        {
-            const float dec = hw_exp2(ctot);
+        // --- H [n][p] <- exp2(c_last) H + Bw^T X   (rows n 16 qi.., columns p 16 j..)
+        const float dec = hw_exp2(ctot);
+        S[0] *= dec;
+        S[1] *= dec;
+        mma16_hl_a<Q / 32, false>(tH1, tH2, 16 * qi, tX, 16 * j0, 16 * j1, lane, S[0], S[1]);
+        // --- Y^T = X^T M^T + exp2(c_t) Y3^T   (rows p 16 qi.., columns t 16 j..), then
+        //     y = Y * silu(z): token t, channels 16 qi + rq .. +3, into the z slot
+        Y[0] *= hw_exp2(*s_c4(16 * j0 + c16));
+        Y[1] *= hw_exp2(*s_c4(16 * j1 + c16));
+        if (qj == 0)   // M is zero for s > t: s < 32 suffices for t < 32
+            mma16_hl_b<1>(tX, 16 * qi, tB, tC, 16 * j0, 16 * j1, lane, Y[0], Y[1]);
+        else
+            mma16_hl_b<2>(tX, 16 * qi, tB, tC, 16 * j0, 16 * j1, lane, Y[0], Y[1]);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) S[e] *= dec;
-            S = mma_block<Q / 16>(tH1, 32 * qi, tX, 32 * qj, lane, S);
-            S = mma_block<Q / 16>(tH2, 32 * qi, tX, 32 * qj, lane, S);
-        }
-        // --- Y^T = X^T M^T + exp2(c_t) Y3^T   (rows p = 32 qi.., columns t = 32 qj..)
-        {
-            const float et = hw_exp2(*s_c4(col));
-#pragma unroll
-            for (int e = 0; e < 16; ++e) Y[e] *= et;
-            if (qj == 0) {   // M is zero for s > t
-                Y = mma_block<2>(tX, 32 * qi, tB, 0, lane, Y);
-                Y = mma_block<2, false, ZC>(tX, 32 * qi, tC, 0, lane, Y);
-            } else {
-                Y = mma_block<Q / 16>(tX, 32 * qi, tB, 32, lane, Y);
-                Y = mma_block<Q / 16, false, ZC>(tX, 32 * qi, tC, 32, lane, Y);
-            }
-        }
-        // --- y = Y * silu(z), token col, channels 32 qi + 8 gq + rq .. +3: into the z slot
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            const int o8 = zsw8(col, 8 * qi + 2 * gq + (rq >> 2));
-            float o[4] = {Y[4 * gq], Y[4 * gq + 1], Y[4 * gq + 2], Y[4 * gq + 3]};
+        for (int bb = 0; bb < 2; ++bb) {
+            const int j = 2 * qj + bb, t = 16 * j + c16;
+            const int o8 = zsw8(t, 4 * qi + (lane >> 4));
+            float o[4] = {Y[bb][0], Y[bb][1], Y[bb][2], Y[bb][3]};
             if (zh) {
                 const u32x2_t zv = *reinterpret_cast<const u32x2_t *>(&tZ[o8]);
                 o[0] *= silu_f32(bf16_to_f32((uint16_t)(zv.x & 0xffffu)));
@@ -299,36 +335,36 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
             *reinterpret_cast<bf16x4_t *>(&tZ[o8]) = ov;
         }
         __syncthreads();                                // (4)
-        // --- y rows out (16 bytes per thread, the slots this thread fills with the next z)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int tr = tid / 8 + 32 * i;
-            if (tr < nt) {
-                const u32x4_t yv = *reinterpret_cast<const u32x4_t *>(&tZ[zsw16(tr, tid % 8)]);
-                __builtin_nontemporal_store((tr & 1) ? u32x4_t{yv.z, yv.w, yv.x, yv.y} : yv,
-                    reinterpret_cast<u32x4_t *>(yh + t0 * xrow + (uint32_t)tr * xr32 + (uint32_t)(tid % 8) * 8));
-            }
+        // --- y rows out (16 bytes per thread, the slot this thread fills with the next z)
+        if (tr < nt) {
+            const u32x4_t yv = *reinterpret_cast<const u32x4_t *>(&tZ[zsw16(tr, tu)]);
+            __builtin_nontemporal_store((tr & 1) ? u32x4_t{yv.z, yv.w, yv.x, yv.y} : yv,
+                reinterpret_cast<u32x4_t *>(yh + t0 * xrow + (uint32_t)tr * xr32 + (uint32_t)tu * 8));
         }
         // --- H^T [p][n] <- H (high and low parts): column p, four consecutive n per write
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            const int n0 = 32 * qi + 8 * gq + rq;
+        for (int bb = 0; bb < 2; ++bb) {
+            const int p = 16 * (2 * qj + bb) + c16, n0 = 16 * qi + rq;
             bf16x4_t hh, hl;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int e = 0; e < 4; ++e) {
                 __bf16 hi, lo;
-                split(S[4 * gq + j], hi, lo);
-                hh[j] = hi;
-                hl[j] = lo;
+                split(S[bb][e], hi, lo);
+                hh[e] = hi;
+                hl[e] = lo;
             }
-            *reinterpret_cast<bf16x4_t *>(&tH1[sw(col, n0)]) = hh;
-            *reinterpret_cast<bf16x4_t *>(&tH2[sw(col, n0)]) = hl;
+            *reinterpret_cast<bf16x4_t *>(&tH1[sw(p, n0)]) = hh;
+            *reinterpret_cast<bf16x4_t *>(&tH2[sw(p, n0)]) = hl;
         }
     }
     if (last_state) {
-        float *ls = last_state + ((int64_t)b * H + h) * P * N + (int64_t)col * N;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) ls[32 * qi + acc_row(e, lane)] = S[e];
+        for (int bb = 0; bb < 2; ++bb) {
+            const int p = 16 * (2 * qj + bb) + c16;
+            float *ls = last_state + (((int64_t)b * H + h) * P + p) * N + 16 * qi + rq;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ls[e] = S[bb][e];
+        }
     }
 }
 

@@ -668,7 +668,7 @@ int ssm_ssd_fwd(const void *x, const void *dt, const float *A, const void *B, co
         if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
         return ok();
     }
-    hipLaunchKernelGGL(ssm::ssd_chunk_kernel, dim3((unsigned)(bsz * H)), dim3(256), 0, st,
+    hipLaunchKernelGGL(ssm::ssd_chunk_kernel, dim3((unsigned)(bsz * H)), dim3(ssm::kSsdThreads), 0, st,
                        static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(dt), A,
                        static_cast<const uint16_t *>(B), static_cast<const uint16_t *>(C), D,
                        static_cast<const uint16_t *>(z), dt_bias, static_cast<uint16_t *>(y), last_state, L, (int)H,
