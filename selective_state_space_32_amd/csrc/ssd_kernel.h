@@ -20,8 +20,10 @@
 // token.  D x is folded into M as D on its diagonal.  x, B and C are bf16 inputs, exact as
 // operands; the operands formed here (M, Bw and the state's copy) are split into a bf16 high
 // part and a bf16 low part (v - hi), each multiplied, so that they keep about 16 bits of
-// their fp32 value.  Operands are staged in LDS with the contraction index contiguous (X and
-// B transposed while staging), so each operand fetch is one 16-byte LDS read per lane.  The
+// their fp32 value.  Every input row is loaded coalesced and staged by token; C, B, the M
+// tiles and the state's copy have the contraction index contiguous (one 16-byte LDS read per
+// operand fetch), X and Bw are stored by token and fetched with gfx950's transposing LDS
+// read (two 8-byte reads per operand).  The
 // state stays in fp32 accumulators across chunks.  The next chunk's inputs are fetched into
 // registers while the current chunk is computed (unconditionally -- the last chunk fetches
 // itself again -- so that the loads land in the loop's own registers and are waited for only
@@ -66,8 +68,6 @@ __device__ __forceinline__ float wave_incl_sum(float v) {
     return v;
 }
 
-typedef float f32x4v_t __attribute__((ext_vector_type(4)));
-
 // Operand and accumulator layout of v_mfma_f32_16x16x32_bf16: a lane fetches the 8
 // consecutive k at offset 8 (lane / 16) of each 32-wide step, for A row / B column
 // lane % 16; accumulator element e of a lane is row 4 (lane / 16) + e, column lane % 16.
@@ -78,7 +78,7 @@ typedef float f32x4v_t __attribute__((ext_vector_type(4)));
 //   mma16_x2  : acc_i += A B_i where enabled
 template <int KS, bool ZB>
 __device__ __forceinline__ void mma16_hl_a(const __bf16 *ah, const __bf16 *al, int a0, const __bf16 *b, int b0, int b1,
-                                           int lane, f32x4v_t &acc0, f32x4v_t &acc1) {
+                                           int lane, f32x4_t &acc0, f32x4_t &acc1) {
     const int r = lane & 15, ko = (lane >> 4) * 8;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
@@ -93,15 +93,45 @@ __device__ __forceinline__ void mma16_hl_a(const __bf16 *ah, const __bf16 *al, i
         acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lv, b1v, acc1, 0, 0, 0);
     }
 }
-// (bh padded, bl swizzled)
+// Operand fetch from a padded tile stored [k][m] (rows k): the 8 consecutive k from
+// k0 + 8 (lane / 16) of m = m0 + lane % 16, by two transposing LDS reads.  Within a group of
+// 16 lanes the read returns to lane j, slot q, slot j % 4 of lane 4 q + j / 4's 8-byte
+// address; so lane i addresses the 4 elements m0 + 4 (i % 4) .. +3 of row k + i / 4, and
+// lane j receives rows k .. k+3 of column m0 + j.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8_t ld_tr(const __bf16 *t, int k0, int m0, int lane) {
+    const int i = lane & 15, kb = k0 + 8 * (lane >> 4) + (i >> 2), m = m0 + 4 * (i & 3);
+    typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+    const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(t + sw(kb, m)));
+    const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(t + sw(kb + 4, m)));
+    const i16x4_t lo = v0, hi = v1;
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// mma16_hl_a with both operands stored [k][m] (A: ah / al [k][row], B: b [k][col])
+template <int KS>
+__device__ __forceinline__ void mma16_hl_a_tr(const __bf16 *ah, const __bf16 *al, int a0, const __bf16 *b, int b0,
+                                              int b1, int lane, f32x4_t &acc0, f32x4_t &acc1) {
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        const bf16x8_t hv = ld_tr(ah, 32 * k, a0, lane);
+        const bf16x8_t lv = ld_tr(al, 32 * k, a0, lane);
+        const bf16x8_t b0v = ld_tr(b, 32 * k, b0, lane);
+        const bf16x8_t b1v = ld_tr(b, 32 * k, b1, lane);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, b0v, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, b1v, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lv, b0v, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lv, b1v, acc1, 0, 0, 0);
+    }
+}
+// (A stored [k][row]; bh padded, bl swizzled)
 template <int KS>
 __device__ __forceinline__ void mma16_hl_b(const __bf16 *a, int a0, const __bf16 *bh, const __bf16 *bl, int b0, int b1,
-                                           int lane, f32x4v_t &acc0, f32x4v_t &acc1) {
+                                           int lane, f32x4_t &acc0, f32x4_t &acc1) {
     const int r = lane & 15, ko = (lane >> 4) * 8;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
         const int kk = 32 * k + ko;
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(a + sw(a0 + r, kk));
+        const bf16x8_t av = ld_tr(a, 32 * k, a0, lane);   // A stored [k][row]
         const bf16x8_t h0 = *reinterpret_cast<const bf16x8_t *>(bh + sw(b0 + r, kk));
         const bf16x8_t h1 = *reinterpret_cast<const bf16x8_t *>(bh + sw(b1 + r, kk));
         const bf16x8_t l0 = *reinterpret_cast<const bf16x8_t *>(bl + swz(b0 + r, kk));
@@ -114,7 +144,7 @@ __device__ __forceinline__ void mma16_hl_b(const __bf16 *a, int a0, const __bf16
 }
 template <int KS, bool ZB>
 __device__ __forceinline__ void mma16_x2(const __bf16 *a, int a0, const __bf16 *b, int b0, int b1, bool en0, bool en1,
-                                         int lane, f32x4v_t &acc0, f32x4v_t &acc1) {
+                                         int lane, f32x4_t &acc0, f32x4_t &acc1) {
     const int r = lane & 15, ko = (lane >> 4) * 8;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
@@ -139,8 +169,8 @@ __device__ __forceinline__ void mma16_x2(const __bf16 *a, int a0, const __bf16 *
 // Tiles and their phases within a chunk (barriers 1-4):
 //   tC : C [t][n] (swizzled)          -> (2) M low part [t][s]
 //   tB : B [s][n]                     -> (2) M high part [t][s]
-//   tX : X^T [p][s]; its row padding holds per-token values
-//   tH1: the state's copy H^T [p][n], high part  -> (2) Bw^T [n][s] high part -> (4) H^T high
+//   tX : X [s][p]; its row padding holds per-token values
+//   tH1: the state's copy H^T [p][n], high part  -> (2) Bw [s][n] high part -> (4) H^T high
 //   tH2: the same, low parts
 //   tZ : z [t][p]                     -> (3) y, in place
 // Between 1 and 2: Y3^T = H^T C^T and G^T = B C^T; between 2 and 3: M and Bw written; between
@@ -189,13 +219,11 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
     const uint16_t *Bg = Bm + (int64_t)b * L * brow + (int64_t)g * N;
     const uint16_t *Cg = Cm + (int64_t)b * L * brow + (int64_t)g * N;
 
-    // staging maps: C and z rows coalesced (token tid / 8, 8 elements at 8 (tid % 8)); X and B
-    // by token = lane (8 channels / states at group w), so that the transposed LDS writes of
-    // one instruction fall in distinct banks.  Addresses: the chunk's base (uniform) plus a
-    // 32-bit offset per lane (64 rows of H P elements fit 32 bits).  z is read and y written
-    // once: streaming (non-temporal) accesses; x and B rows are read by eight waves in 16-byte
-    // pieces and stay cached.
-    struct Raw { u32x4_t c, xv, bv, zv; uint32_t dt; };
+    // staging map: every row coalesced (token tid / 8, 8 elements at 8 (tid % 8)); X and Bw
+    // are stored by token and read transposed where they are operands.  Addresses: the
+    // chunk's base (uniform) plus a 32-bit offset per lane (64 rows of H P elements fit 32
+    // bits).  z is read and y written once: streaming (non-temporal) accesses.
+    struct Raw { u32x4_t c, xv, bv, zv; uint32_t dt; };   // (rows of token tr)
     const uint32_t xr32 = (uint32_t)xrow, br32 = (uint32_t)brow;
     const int tr = tid / 8, tu = tid % 8;             // the thread's row and 16-byte unit (C, z, y)
     auto fetch = [&](int64_t t0, Raw &r) {
@@ -205,40 +233,30 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
         if (zh)
             r.zv = __builtin_nontemporal_load(
                 reinterpret_cast<const u32x4_t *>(zh + t0 * xrow + (tc * xr32 + (uint32_t)tu * 8)));
-        r.xv = *reinterpret_cast<const u32x4_t *>(xh + t0 * xrow + (ts * xr32 + (uint32_t)w * 8));
-        r.bv = *reinterpret_cast<const u32x4_t *>(Bg + t0 * brow + (ts * br32 + (uint32_t)w * 8));
+        r.xv = *reinterpret_cast<const u32x4_t *>(xh + t0 * xrow + (tc * xr32 + (uint32_t)tu * 8));
+        r.bv = *reinterpret_cast<const u32x4_t *>(Bg + t0 * brow + (tc * br32 + (uint32_t)tu * 8));
         r.dt = dt[((int64_t)b * L + t0) * H + h + (w == 0 ? ts : 0u) * (uint32_t)H];   // (used by wave 0)
     };
-    auto lo16 = [](uint32_t v) { return __builtin_bit_cast(__bf16, (uint16_t)(v & 0xffffu)); };
-    auto hi16 = [](uint32_t v) { return __builtin_bit_cast(__bf16, (uint16_t)(v >> 16)); };
     auto split = [](float v, __bf16 &hi, __bf16 &lo) {
         hi = (__bf16)v;
         lo = (__bf16)(v - (float)hi);
     };
 
-    f32x4v_t S[2] = {};                                // the state H [n][p]: rows n 16 qi.., columns p 16 j..
+    f32x4_t S[2] = {};                                // the state H [n][p]: rows n 16 qi.., columns p 16 j..
     Raw r;
     fetch(0, r);
     const int64_t nchunks = (L + Q - 1) / Q;
     for (int64_t c = 0; c < nchunks; ++c) {
         const int64_t t0 = c * Q;
         const int nt = (int)min((int64_t)Q, L - t0);
-        // --- stage C, z, B (natural) and X^T (transposed); the step sizes and their running
-        //     sum, token = lane, in every wave
+        // --- stage C, z, B and X (rows by token); wave 0: the step sizes and their running sum
         *reinterpret_cast<u32x4_t *>(&tC[swz(tr, tu * 8)]) = r.c;
         if (zh) {
             const u32x4_t zv = (tr & 1) ? u32x4_t{r.zv.z, r.zv.w, r.zv.x, r.zv.y} : r.zv;
             *reinterpret_cast<u32x4_t *>(&tZ[zsw16(tr, tu)]) = zv;
         }
-        *reinterpret_cast<u32x4_t *>(&tB[sw(lane, w * 8)]) = r.bv;
-        {
-            const uint32_t xw[4] = {r.xv.x, r.xv.y, r.xv.z, r.xv.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                tX[sw(w * 8 + 2 * k, lane)] = lo16(xw[k]);
-                tX[sw(w * 8 + 2 * k + 1, lane)] = hi16(xw[k]);
-            }
-        }
+        *reinterpret_cast<u32x4_t *>(&tB[sw(tr, tu * 8)]) = r.bv;
+        *reinterpret_cast<u32x4_t *>(&tX[sw(tr, tu * 8)]) = r.xv;
         if (w == 0) {   // the step sizes and their running sum, token = lane
             const float v = bf16_to_f32((uint16_t)r.dt) + bias_h;
             const float dl = lane < nt ? (softplus ? softplus_f32(v) : v) : 0.0f;   // padded tokens: identity steps
@@ -255,9 +273,9 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
         __syncthreads();                                // (1)
         const float ctot = *s_c4(Q - 1);                // c_last
         const float cref = *s_c4(qi >= 2 ? 32 : 0);     // c at the first token of this band's half-chunk
-        const float wsl = *s_w4(lane);                  // Bw weight of token lane
+        const float wsl = *s_w4(tr);                    // Bw weight of token tr
         // --- Y3^T = H^T C^T (the state entering the chunk) and G^T = B C^T
-        f32x4v_t Y[2] = {}, Gt[2] = {};
+        f32x4_t Y[2] = {}, Gt[2] = {};
         const int j0 = 2 * qj, j1 = 2 * qj + 1;         // this wave's column blocks
         if (c > 0) mma16_hl_a<N / 32, ZC>(tH1, tH2, 16 * qi, tC, 16 * j0, 16 * j1, lane, Y[0], Y[1]);
         if (qi <= j1)   // zero for s > t
@@ -295,22 +313,27 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
                 *reinterpret_cast<bf16x4_t *>(&tC[swz(t, s0)]) = ml;
             }
         }
-        // --- Bw^T [n][s] = B[s][n] exp2(c_last - c_s) dt_s, token s = lane
+        // --- Bw [s][n] = B[s][n] exp2(c_last - c_s) dt_s: token tr, states 8 tu .. +7
         {
             const uint32_t bw[4] = {bcur.x, bcur.y, bcur.z, bcur.w};
+            bf16x8_t bh, bl;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int o = sw(w * 8 + 2 * k, lane);
-                split(bf16_to_f32((uint16_t)(bw[k] & 0xffffu)) * wsl, tH1[o], tH2[o]);
-                split(bf16_to_f32((uint16_t)(bw[k] >> 16)) * wsl, tH1[o + LD], tH2[o + LD]);
+                __bf16 h0, l0, h1, l1;
+                split(bf16_to_f32((uint16_t)(bw[k] & 0xffffu)) * wsl, h0, l0);
+                split(bf16_to_f32((uint16_t)(bw[k] >> 16)) * wsl, h1, l1);
+                bh[2 * k] = h0; bh[2 * k + 1] = h1;
+                bl[2 * k] = l0; bl[2 * k + 1] = l1;
             }
+            *reinterpret_cast<bf16x8_t *>(&tH1[sw(tr, tu * 8)]) = bh;
+            *reinterpret_cast<bf16x8_t *>(&tH2[sw(tr, tu * 8)]) = bl;
         }
         __syncthreads();                                // (3)
         // --- H [n][p] <- exp2(c_last) H + Bw^T X   (rows n 16 qi.., columns p 16 j..)
         const float dec = hw_exp2(ctot);
         S[0] *= dec;
         S[1] *= dec;
-        mma16_hl_a<Q / 32, false>(tH1, tH2, 16 * qi, tX, 16 * j0, 16 * j1, lane, S[0], S[1]);
+        mma16_hl_a_tr<Q / 32>(tH1, tH2, 16 * qi, tX, 16 * j0, 16 * j1, lane, S[0], S[1]);
         // --- Y^T = X^T M^T + exp2(c_t) Y3^T   (rows p 16 qi.., columns t 16 j..), then
         //     y = Y * silu(z): token t, channels 16 qi + rq .. +3, into the z slot
         Y[0] *= hw_exp2(*s_c4(16 * j0 + c16));
