@@ -11,9 +11,9 @@
 //   H      <- exp(c_{Q-1}) H + Bw^T X,  Bw[s,n] = B[s,n] exp(c_{Q-1} - c_s) dt_s
 //   y      = (Y + D x) * silu(z)
 // Each product is 64 x 64 x 64 here (Q = P = N = 64): one workgroup per (sequence, head),
-// eight waves, each owning a 16-row band and two 16 x 16 blocks of every product, computed
+// four waves, each owning a 16-row band (all four 16 x 16 blocks) of every product, computed
 // with v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32 accumulation; each operand fetched once
-// per step for both blocks and both high / low parts).  The products are taken
+// per step for all four blocks and both high / low parts).  The products are taken
 // transposed (G^T = B C^T, Y^T = X^T M^T, and the state as H[n][p]), so that the four
 // consecutive accumulator rows a lane holds are four consecutive elements of the operand
 // tile they are written to (one 8-byte LDS write) and each lane's output column is one
@@ -28,7 +28,8 @@
 // registers while the current chunk is computed (unconditionally -- the last chunk fetches
 // itself again -- so that the loads land in the loop's own registers and are waited for only
 // when the next chunk is staged).  Five operand tiles and a z / y tile (52 KB of LDS) serve
-// every phase of a chunk.
+// every phase of a chunk; with at most 168 registers three workgroups fit on a CU, so the
+// whole grid of a layer with up to 768 (sequence, head) pairs is resident at once.
 #pragma once
 
 #include "device_math.h"
@@ -38,7 +39,7 @@ namespace ssm {
 constexpr int kSsdQ = 64;          // tokens per chunk
 constexpr int kSsdP = 64;          // channels per head
 constexpr int kSsdN = 64;          // states
-constexpr int kSsdThreads = 512;   // eight waves per (sequence, head)
+constexpr int kSsdThreads = 256;   // four waves per (sequence, head)
 // Operand tiles are 64 x 64 bf16, element (row, k) at sw(row, k): rows of 72 (144 bytes:
 // 16-byte aligned, and 16-byte reads of eight consecutive rows fall in distinct banks), or,
 // for the C tile, swz(row, k): unpadded rows whose 16-byte unit k / 8 is stored at unit
@@ -71,26 +72,26 @@ __device__ __forceinline__ float wave_incl_sum(float v) {
 // Operand and accumulator layout of v_mfma_f32_16x16x32_bf16: a lane fetches the 8
 // consecutive k at offset 8 (lane / 16) of each 32-wide step, for A row / B column
 // lane % 16; accumulator element e of a lane is row 4 (lane / 16) + e, column lane % 16.
-// Two 16 x 16 blocks side by side (B columns from rows b0 and b1 of tile `b`) over a
+// NB 16 x 16 blocks side by side (B columns from rows bs, bs + 16, ... of tile `b`) over a
 // contraction of 32 * KS, each operand fetched once per step:
 //   mma16_hl_a: A = ah + al (high and low parts, rows a0): acc_i += (ah + al) B_i
 //   mma16_hl_b: B = bh + bl (high and low parts): acc_i += A (bh_i + bl_i)
-//   mma16_x2  : acc_i += A B_i where enabled
-template <int KS, bool ZB>
-__device__ __forceinline__ void mma16_hl_a(const __bf16 *ah, const __bf16 *al, int a0, const __bf16 *b, int b0, int b1,
-                                           int lane, f32x4_t &acc0, f32x4_t &acc1) {
+//   mma16_xn  : acc_i += A B_i where enabled
+template <int KS, int NB, bool ZB>
+__device__ __forceinline__ void mma16_hl_a(const __bf16 *ah, const __bf16 *al, int a0, const __bf16 *b, int bs,
+                                           int lane, f32x4_t (&acc)[NB]) {
     const int r = lane & 15, ko = (lane >> 4) * 8;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
         const int kk = 32 * k + ko;
         const bf16x8_t hv = *reinterpret_cast<const bf16x8_t *>(ah + sw(a0 + r, kk));
         const bf16x8_t lv = *reinterpret_cast<const bf16x8_t *>(al + sw(a0 + r, kk));
-        const bf16x8_t b0v = *reinterpret_cast<const bf16x8_t *>(b + tix<ZB>(b0 + r, kk));
-        const bf16x8_t b1v = *reinterpret_cast<const bf16x8_t *>(b + tix<ZB>(b1 + r, kk));
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, b0v, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, b1v, acc1, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lv, b0v, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lv, b1v, acc1, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(b + tix<ZB>(bs + 16 * i + r, kk));
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, bv, acc[i], 0, 0, 0);
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lv, bv, acc[i], 0, 0, 0);
+        }
     }
 }
 // Operand fetch from a padded tile stored [k][m] (rows k): the 8 consecutive k from
@@ -104,59 +105,56 @@ __device__ __forceinline__ bf16x8_t ld_tr(const __bf16 *t, int k0, int m0, int l
     typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
     const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(t + sw(kb, m)));
     const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(t + sw(kb + 4, m)));
-    const i16x4_t lo = v0, hi = v1;
-    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 // mma16_hl_a with both operands stored [k][m] (A: ah / al [k][row], B: b [k][col])
-template <int KS>
-__device__ __forceinline__ void mma16_hl_a_tr(const __bf16 *ah, const __bf16 *al, int a0, const __bf16 *b, int b0,
-                                              int b1, int lane, f32x4_t &acc0, f32x4_t &acc1) {
+template <int KS, int NB>
+__device__ __forceinline__ void mma16_hl_a_tr(const __bf16 *ah, const __bf16 *al, int a0, const __bf16 *b, int bs,
+                                              int lane, f32x4_t (&acc)[NB]) {
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
         const bf16x8_t hv = ld_tr(ah, 32 * k, a0, lane);
         const bf16x8_t lv = ld_tr(al, 32 * k, a0, lane);
-        const bf16x8_t b0v = ld_tr(b, 32 * k, b0, lane);
-        const bf16x8_t b1v = ld_tr(b, 32 * k, b1, lane);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, b0v, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, b1v, acc1, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lv, b0v, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lv, b1v, acc1, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const bf16x8_t bv = ld_tr(b, 32 * k, bs + 16 * i, lane);
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, bv, acc[i], 0, 0, 0);
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lv, bv, acc[i], 0, 0, 0);
+        }
     }
 }
 // (A stored [k][row]; bh padded, bl swizzled)
-template <int KS>
-__device__ __forceinline__ void mma16_hl_b(const __bf16 *a, int a0, const __bf16 *bh, const __bf16 *bl, int b0, int b1,
-                                           int lane, f32x4_t &acc0, f32x4_t &acc1) {
+template <int KS, int NB>
+__device__ __forceinline__ void mma16_hl_b(const __bf16 *a, int a0, const __bf16 *bh, const __bf16 *bl, int bs,
+                                           int lane, f32x4_t *acc) {
     const int r = lane & 15, ko = (lane >> 4) * 8;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
         const int kk = 32 * k + ko;
-        const bf16x8_t av = ld_tr(a, 32 * k, a0, lane);   // A stored [k][row]
-        const bf16x8_t h0 = *reinterpret_cast<const bf16x8_t *>(bh + sw(b0 + r, kk));
-        const bf16x8_t h1 = *reinterpret_cast<const bf16x8_t *>(bh + sw(b1 + r, kk));
-        const bf16x8_t l0 = *reinterpret_cast<const bf16x8_t *>(bl + swz(b0 + r, kk));
-        const bf16x8_t l1 = *reinterpret_cast<const bf16x8_t *>(bl + swz(b1 + r, kk));
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, h0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, h1, acc1, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, l0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, l1, acc1, 0, 0, 0);
+        const bf16x8_t av = ld_tr(a, 32 * k, a0, lane);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const bf16x8_t hv = *reinterpret_cast<const bf16x8_t *>(bh + sw(bs + 16 * i + r, kk));
+            const bf16x8_t lv = *reinterpret_cast<const bf16x8_t *>(bl + swz(bs + 16 * i + r, kk));
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hv, acc[i], 0, 0, 0);
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, lv, acc[i], 0, 0, 0);
+        }
     }
 }
-template <int KS, bool ZB>
-__device__ __forceinline__ void mma16_x2(const __bf16 *a, int a0, const __bf16 *b, int b0, int b1, bool en0, bool en1,
-                                         int lane, f32x4_t &acc0, f32x4_t &acc1) {
+template <int KS, int NB, bool ZB>
+__device__ __forceinline__ void mma16_xn(const __bf16 *a, int a0, const __bf16 *b, int bs, int first, int lane,
+                                         f32x4_t (&acc)[NB]) {   // blocks i >= first only
     const int r = lane & 15, ko = (lane >> 4) * 8;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
         const int kk = 32 * k + ko;
         const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(a + sw(a0 + r, kk));
-        if (en0) {
-            const bf16x8_t b0v = *reinterpret_cast<const bf16x8_t *>(b + tix<ZB>(b0 + r, kk));
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b0v, acc0, 0, 0, 0);
-        }
-        if (en1) {
-            const bf16x8_t b1v = *reinterpret_cast<const bf16x8_t *>(b + tix<ZB>(b1 + r, kk));
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b1v, acc1, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            if (i >= first) {
+                const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(b + tix<ZB>(bs + 16 * i + r, kk));
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[i], 0, 0, 0);
+            }
         }
     }
 }
@@ -164,26 +162,23 @@ __device__ __forceinline__ void mma16_x2(const __bf16 *a, int a0, const __bf16 *
 // x, z, y: [bsz][L][H][P] bf16;  dt: [bsz][L][H] bf16;  A, Dv, dt_bias: [H] fp32;
 // B, C: [bsz][L][G][N] bf16;  last_state: [bsz][H][P][N] fp32 (or null).
 //
-// Eight waves; wave w owns, in every product, the 16-row band qi = w / 2 and the two 16 x 16
-// blocks j = 2 (w % 2) + bb (bb = 0, 1) of columns.
+// Four waves; wave w owns, in every product, the 16-row band w and the four 16 x 16 column
+// blocks j = 0..3.
 // Tiles and their phases within a chunk (barriers 1-4):
 //   tC : C [t][n] (swizzled)          -> (2) M low part [t][s]
 //   tB : B [s][n]                     -> (2) M high part [t][s]
-//   tX : X [s][p]; its row padding holds per-token values
+//   tX : X [s][p]
 //   tH1: the state's copy H^T [p][n], high part  -> (2) Bw [s][n] high part -> (4) H^T high
 //   tH2: the same, low parts
 //   tZ : z [t][p]                     -> (3) y, in place
-// Between 1 and 2: Y3^T = H^T C^T and G^T = B C^T; between 2 and 3: M and Bw written; between
-// 3 and 4: the state update, Y^T = X^T M^T and the output; after 4: the new H^T, y out to
-// HBM, and the next chunk's C, B, X^T, z.
-// (at most 128 registers: two workgroups of eight waves per CU)
-__global__ void __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(4)))
+// (at most 168 registers: three workgroups of four waves per CU)
+__global__ void __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(3)))
 ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt, const float *__restrict__ A,
                  const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm, const float *__restrict__ Dv,
                  const uint16_t *__restrict__ z, const float *__restrict__ dt_bias, uint16_t *__restrict__ y,
                  float *__restrict__ last_state, int64_t L, int H, int G, int softplus) {
     constexpr int Q = kSsdQ, P = kSsdP, N = kSsdN, LD = kSsdLd;
-    static_assert(Q == 64 && P == 64 && N == 64, "a 16-row band and two 16 x 16 blocks per wave of eight");
+    static_assert(Q == 64 && P == 64 && N == 64, "a 16-row band and four 16 x 16 blocks per wave of four");
     constexpr bool ZC = true;                         // tC is swizzled
     __shared__ __attribute__((aligned(16))) __bf16 tC[Q * 64];
     __shared__ __attribute__((aligned(16))) __bf16 tB[Q * LD];
@@ -202,7 +197,7 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int qi = w >> 1, qj = w & 1;                // row band 16 qi; column blocks 2 qj, 2 qj + 1
+    const int qi = w;                                 // row band 16 qi; column blocks 0..3
     const int c16 = lane & 15;                        // the lane's column within a block
     const int rq = (lane >> 4) * 4;                   // its rows: 16 qi + rq + (0..3)
     const int bh = blockIdx.x;
@@ -219,22 +214,26 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
     const uint16_t *Bg = Bm + (int64_t)b * L * brow + (int64_t)g * N;
     const uint16_t *Cg = Cm + (int64_t)b * L * brow + (int64_t)g * N;
 
-    // staging map: every row coalesced (token tid / 8, 8 elements at 8 (tid % 8)); X and Bw
-    // are stored by token and read transposed where they are operands.  Addresses: the
+    // staging map: every row coalesced (tokens tid / 8 + 32 i, 8 elements at 8 (tid % 8)); X
+    // and Bw are stored by token and read transposed where they are operands.  Addresses: the
     // chunk's base (uniform) plus a 32-bit offset per lane (64 rows of H P elements fit 32
     // bits).  z is read and y written once: streaming (non-temporal) accesses.
-    struct Raw { u32x4_t c, xv, bv, zv; uint32_t dt; };   // (rows of token tr)
+    struct Raw { u32x4_t c[2], xv[2], bv[2], zv[2]; uint32_t dt; };   // rows tr0 + 32 i
     const uint32_t xr32 = (uint32_t)xrow, br32 = (uint32_t)brow;
-    const int tr = tid / 8, tu = tid % 8;             // the thread's row and 16-byte unit (C, z, y)
+    const int tr0 = tid / 8, tu = tid % 8;
     auto fetch = [&](int64_t t0, Raw &r) {
         const uint32_t lim = (uint32_t)min((int64_t)(Q - 1), L - 1 - t0);   // last token present
-        const uint32_t ts = min((uint32_t)lane, lim), tc = min((uint32_t)tr, lim);
-        r.c = *reinterpret_cast<const u32x4_t *>(Cg + t0 * brow + (tc * br32 + (uint32_t)tu * 8));
-        if (zh)
-            r.zv = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4_t *>(zh + t0 * xrow + (tc * xr32 + (uint32_t)tu * 8)));
-        r.xv = *reinterpret_cast<const u32x4_t *>(xh + t0 * xrow + (tc * xr32 + (uint32_t)tu * 8));
-        r.bv = *reinterpret_cast<const u32x4_t *>(Bg + t0 * brow + (tc * br32 + (uint32_t)tu * 8));
+        const uint32_t ts = min((uint32_t)lane, lim);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t tc = min((uint32_t)(tr0 + 32 * i), lim);
+            r.c[i] = *reinterpret_cast<const u32x4_t *>(Cg + t0 * brow + (tc * br32 + (uint32_t)tu * 8));
+            if (zh)
+                r.zv[i] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4_t *>(zh + t0 * xrow + (tc * xr32 + (uint32_t)tu * 8)));
+            r.xv[i] = *reinterpret_cast<const u32x4_t *>(xh + t0 * xrow + (tc * xr32 + (uint32_t)tu * 8));
+            r.bv[i] = *reinterpret_cast<const u32x4_t *>(Bg + t0 * brow + (tc * br32 + (uint32_t)tu * 8));
+        }
         r.dt = dt[((int64_t)b * L + t0) * H + h + (w == 0 ? ts : 0u) * (uint32_t)H];   // (used by wave 0)
     };
     auto split = [](float v, __bf16 &hi, __bf16 &lo) {
@@ -242,7 +241,7 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
         lo = (__bf16)(v - (float)hi);
     };
 
-    f32x4_t S[2] = {};                                // the state H [n][p]: rows n 16 qi.., columns p 16 j..
+    f32x4_t S[4] = {};                                 // the state H [n][p]: rows n 16 qi.., columns p 16 j..
     Raw r;
     fetch(0, r);
     const int64_t nchunks = (L + Q - 1) / Q;
@@ -250,14 +249,18 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
         const int64_t t0 = c * Q;
         const int nt = (int)min((int64_t)Q, L - t0);
         // --- stage C, z, B and X (rows by token); wave 0: the step sizes and their running sum
-        *reinterpret_cast<u32x4_t *>(&tC[swz(tr, tu * 8)]) = r.c;
-        if (zh) {
-            const u32x4_t zv = (tr & 1) ? u32x4_t{r.zv.z, r.zv.w, r.zv.x, r.zv.y} : r.zv;
-            *reinterpret_cast<u32x4_t *>(&tZ[zsw16(tr, tu)]) = zv;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int tr = tr0 + 32 * i;
+            *reinterpret_cast<u32x4_t *>(&tC[swz(tr, tu * 8)]) = r.c[i];
+            if (zh) {
+                const u32x4_t zv = (tr & 1) ? u32x4_t{r.zv[i].z, r.zv[i].w, r.zv[i].x, r.zv[i].y} : r.zv[i];
+                *reinterpret_cast<u32x4_t *>(&tZ[zsw16(tr, tu)]) = zv;
+            }
+            *reinterpret_cast<u32x4_t *>(&tB[sw(tr, tu * 8)]) = r.bv[i];
+            *reinterpret_cast<u32x4_t *>(&tX[sw(tr, tu * 8)]) = r.xv[i];
         }
-        *reinterpret_cast<u32x4_t *>(&tB[sw(tr, tu * 8)]) = r.bv;
-        *reinterpret_cast<u32x4_t *>(&tX[sw(tr, tu * 8)]) = r.xv;
-        if (w == 0) {   // the step sizes and their running sum, token = lane
+        if (w == 0) {   // token = lane
             const float v = bf16_to_f32((uint16_t)r.dt) + bias_h;
             const float dl = lane < nt ? (softplus ? softplus_f32(v) : v) : 0.0f;   // padded tokens: identity steps
             const float cl = a2 * wave_incl_sum(dl);
@@ -268,18 +271,15 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
             *s_f4(lane) = hw_exp2((lane < 32 ? c0 : c32) - cl) * dl;
             *s_w4(lane) = hw_exp2(ctot - cl) * dl;
         }
-        const u32x4_t bcur = r.bv;
+        const u32x4_t bcur[2] = {r.bv[0], r.bv[1]};
         fetch(min(t0 + Q, (nchunks - 1) * Q), r);   // (the last chunk fetches itself again, unused)
         __syncthreads();                                // (1)
         const float ctot = *s_c4(Q - 1);                // c_last
         const float cref = *s_c4(qi >= 2 ? 32 : 0);     // c at the first token of this band's half-chunk
-        const float wsl = *s_w4(tr);                    // Bw weight of token tr
         // --- Y3^T = H^T C^T (the state entering the chunk) and G^T = B C^T
-        f32x4_t Y[2] = {}, Gt[2] = {};
-        const int j0 = 2 * qj, j1 = 2 * qj + 1;         // this wave's column blocks
-        if (c > 0) mma16_hl_a<N / 32, ZC>(tH1, tH2, 16 * qi, tC, 16 * j0, 16 * j1, lane, Y[0], Y[1]);
-        if (qi <= j1)   // zero for s > t
-            mma16_x2<N / 32, ZC>(tB, 16 * qi, tC, 16 * j0, 16 * j1, qi <= j0, true, lane, Gt[0], Gt[1]);
+        f32x4_t Y[4] = {}, Gt[4] = {};
+        if (c > 0) mma16_hl_a<N / 32, 4, ZC>(tH1, tH2, 16 * qi, tC, 0, lane, Y);
+        mma16_xn<N / 32, 4, ZC>(tB, 16 * qi, tC, 0, qi, lane, Gt);   // blocks j >= qi (zero for s > t)
         __syncthreads();                                // (2)
         // --- M [t][s] = G^T[s][t] exp2(c_t - c_s) dt_s (s <= t) + D (s = t): rows s of this
         //     wave's band, column t; four consecutive s per 8-byte write.  The decay is
@@ -291,14 +291,14 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
             const f32x4_t fs = *reinterpret_cast<const f32x4_t *>(s_f4(s0));
             const float fsv[4] = {fs.x, fs.y, fs.z, fs.w};
 #pragma unroll
-            for (int bb = 0; bb < 2; ++bb) {
-                const int j = 2 * qj + bb, t = 16 * j + c16;
+            for (int j = 0; j < 4; ++j) {
+                const int t = 16 * j + c16;
                 bf16x4_t mh = {}, ml = {};
                 if (qi <= j) {
                     const float et = hw_exp2(*s_c4(t) - cref);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        float m = Gt[bb][e] * et * fsv[e];
+                        float m = Gt[j][e] * et * fsv[e];
                         if (qi == j) {
                             m = s0 + e <= t ? m : 0.0f;
                             if (s0 + e == t) m += d_h;
@@ -313,40 +313,41 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
                 *reinterpret_cast<bf16x4_t *>(&tC[swz(t, s0)]) = ml;
             }
         }
-        // --- Bw [s][n] = B[s][n] exp2(c_last - c_s) dt_s: token tr, states 8 tu .. +7
-        {
-            const uint32_t bw[4] = {bcur.x, bcur.y, bcur.z, bcur.w};
-            bf16x8_t bh, bl;
+        // --- Bw [s][n] = B[s][n] exp2(c_last - c_s) dt_s: tokens tr, states 8 tu .. +7
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int tr = tr0 + 32 * i;
+            const float wsl = *s_w4(tr);
+            const uint32_t bw[4] = {bcur[i].x, bcur[i].y, bcur[i].z, bcur[i].w};
+            bf16x8_t bhv, blv;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 __bf16 h0, l0, h1, l1;
                 split(bf16_to_f32((uint16_t)(bw[k] & 0xffffu)) * wsl, h0, l0);
                 split(bf16_to_f32((uint16_t)(bw[k] >> 16)) * wsl, h1, l1);
-                bh[2 * k] = h0; bh[2 * k + 1] = h1;
-                bl[2 * k] = l0; bl[2 * k + 1] = l1;
+                bhv[2 * k] = h0; bhv[2 * k + 1] = h1;
+                blv[2 * k] = l0; blv[2 * k + 1] = l1;
             }
-            *reinterpret_cast<bf16x8_t *>(&tH1[sw(tr, tu * 8)]) = bh;
-            *reinterpret_cast<bf16x8_t *>(&tH2[sw(tr, tu * 8)]) = bl;
+            *reinterpret_cast<bf16x8_t *>(&tH1[sw(tr, tu * 8)]) = bhv;
+            *reinterpret_cast<bf16x8_t *>(&tH2[sw(tr, tu * 8)]) = blv;
         }
         __syncthreads();                                // (3)
         // --- H [n][p] <- exp2(c_last) H + Bw^T X   (rows n 16 qi.., columns p 16 j..)
         const float dec = hw_exp2(ctot);
-        S[0] *= dec;
-        S[1] *= dec;
-        mma16_hl_a_tr<Q / 32>(tH1, tH2, 16 * qi, tX, 16 * j0, 16 * j1, lane, S[0], S[1]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S[j] *= dec;
+        mma16_hl_a_tr<Q / 32, 4>(tH1, tH2, 16 * qi, tX, 0, lane, S);
         // --- Y^T = X^T M^T + exp2(c_t) Y3^T   (rows p 16 qi.., columns t 16 j..), then
         //     y = Y * silu(z): token t, channels 16 qi + rq .. +3, into the z slot
-        Y[0] *= hw_exp2(*s_c4(16 * j0 + c16));
-        Y[1] *= hw_exp2(*s_c4(16 * j1 + c16));
-        if (qj == 0)   // M is zero for s > t: s < 32 suffices for t < 32
-            mma16_hl_b<1>(tX, 16 * qi, tB, tC, 16 * j0, 16 * j1, lane, Y[0], Y[1]);
-        else
-            mma16_hl_b<2>(tX, 16 * qi, tB, tC, 16 * j0, 16 * j1, lane, Y[0], Y[1]);
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            const int j = 2 * qj + bb, t = 16 * j + c16;
+        for (int j = 0; j < 4; ++j) Y[j] *= hw_exp2(*s_c4(16 * j + c16));
+        mma16_hl_b<1, 2>(tX, 16 * qi, tB, tC, 0, lane, Y);        // t < 32: s < 32 suffices
+        mma16_hl_b<2, 2>(tX, 16 * qi, tB, tC, 32, lane, Y + 2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = 16 * j + c16;
             const int o8 = zsw8(t, 4 * qi + (lane >> 4));
-            float o[4] = {Y[bb][0], Y[bb][1], Y[bb][2], Y[bb][3]};
+            float o[4] = {Y[j][0], Y[j][1], Y[j][2], Y[j][3]};
             if (zh) {
                 const u32x2_t zv = *reinterpret_cast<const u32x2_t *>(&tZ[o8]);
                 o[0] *= silu_f32(bf16_to_f32((uint16_t)(zv.x & 0xffffu)));
@@ -358,21 +359,25 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
             *reinterpret_cast<bf16x4_t *>(&tZ[o8]) = ov;
         }
         __syncthreads();                                // (4)
-        // --- y rows out (16 bytes per thread, the slot this thread fills with the next z)
-        if (tr < nt) {
-            const u32x4_t yv = *reinterpret_cast<const u32x4_t *>(&tZ[zsw16(tr, tu)]);
-            __builtin_nontemporal_store((tr & 1) ? u32x4_t{yv.z, yv.w, yv.x, yv.y} : yv,
-                reinterpret_cast<u32x4_t *>(yh + t0 * xrow + (uint32_t)tr * xr32 + (uint32_t)tu * 8));
+        // --- y rows out (16 bytes per thread and row, the slots this thread fills with the next z)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int tr = tr0 + 32 * i;
+            if (tr < nt) {
+                const u32x4_t yv = *reinterpret_cast<const u32x4_t *>(&tZ[zsw16(tr, tu)]);
+                __builtin_nontemporal_store((tr & 1) ? u32x4_t{yv.z, yv.w, yv.x, yv.y} : yv,
+                    reinterpret_cast<u32x4_t *>(yh + t0 * xrow + (uint32_t)tr * xr32 + (uint32_t)tu * 8));
+            }
         }
         // --- H^T [p][n] <- H (high and low parts): column p, four consecutive n per write
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            const int p = 16 * (2 * qj + bb) + c16, n0 = 16 * qi + rq;
+        for (int j = 0; j < 4; ++j) {
+            const int p = 16 * j + c16, n0 = 16 * qi + rq;
             bf16x4_t hh, hl;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 __bf16 hi, lo;
-                split(S[bb][e], hi, lo);
+                split(S[j][e], hi, lo);
                 hh[e] = hi;
                 hl[e] = lo;
             }
@@ -382,11 +387,11 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
     }
     if (last_state) {
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            const int p = 16 * (2 * qj + bb) + c16;
+        for (int j = 0; j < 4; ++j) {
+            const int p = 16 * j + c16;
             float *ls = last_state + (((int64_t)b * H + h) * P + p) * N + 16 * qi + rq;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ls[e] = S[bb][e];
+            for (int e = 0; e < 4; ++e) ls[e] = S[j][e];
         }
     }
 }
