@@ -117,14 +117,25 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     constexpr bool PIPE = !(sizeof(IO) == 2 && S % 2 == 1) && T % 8 == 0;
     constexpr int G = 4;
     constexpr int BW = PIPE ? S * (int)sizeof(IO) / 4 : 1;
-    __shared__ f32x2_t s_dk[T][kChanTile];
-    __shared__ float s_yp[READOUT ? K : 1][T][kChanTile];
+    // (delta, delta*u) of token tt, channel c at s_dk[tt][sdk(c)]: the 16-byte channel pairs of
+    // a row are XOR-permuted by (c / 8) % 8, so that the prep's pair writes (eight threads of a
+    // row, 8 channels apart) fall in distinct banks while a row read by lane = channel stays
+    // one contiguous span
+    __shared__ __attribute__((aligned(16))) f32x2_t s_dk[T][kChanTile];
+    // per-wave partial readouts, channel c at s_yp[k][tt][syp(c)]: 16-byte units XOR-permuted
+    // by (c / 32) % 2, so that the epilogue's 16-byte reads (eight threads of a row, 32 bytes
+    // apart) fall in distinct banks
+    __shared__ __attribute__((aligned(16))) float s_yp[READOUT ? K : 1][T][kChanTile];
     constexpr int RS = CW > 0 ? T + CW - 1 : 1;   // rows of the x ring
     __shared__ IO s_x[RS][kChanTile];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    auto sdk = [](int c) { return c ^ (((c >> 3) & 7) << 1); };
+    auto syp = [](int c) { return c ^ (((c >> 5) & 1) << 2); };
+    const int sl = sdk(lane);                  // this lane's channel slot in s_dk
+    const int yl = syp(lane);                  // ... in s_yp
     // prep / epilogue mapping: access p of this thread covers token row p*RPP + tid/GPR,
     // channels cq .. cq+V-1 of the tile
     const int rsub = tid / GPR;
@@ -249,7 +260,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     };
     // the conv phase of the tile at t0: lane = channel; wave w computes u for exactly the
     // rows its own threads prepare (rows p*RPP + w*V .. + V-1 of each access round p), so
-    // the prep needs only this wave's LDS writes to be done.  u goes to s_dk[tt][lane].x
+    // the prep needs only this wave's LDS writes to be done.  u goes to s_dk[tt][sdk(lane)].x
     // for the prep (and to u_out).
     auto conv_phase = [&](int64_t t0, int rb, int nt) {
         if constexpr (CW > 0) {
@@ -271,7 +282,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
 #pragma unroll
                     for (int k = 0; k < CW; ++k) acc = fmaf(cwl[k], xw[k], acc);
                     const float uu = silu_f32(acc);
-                    s_dk[tb + i][lane] = f32x2_t{uu, uu};
+                    s_dk[tb + i][sl] = f32x2_t{uu, uu};
 #pragma unroll
                     for (int k = 0; k + 1 < CW; ++k) xw[k] = xw[k + 1];
                 }
@@ -283,7 +294,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                     const int tb = p * RPP + w * V;
 #pragma unroll
                     for (int i = 0; i < V; ++i)
-                        if (tb + i < nt) io<IO>::st(dst, (int64_t)(tb + i) * D, s_dk[tb + i][lane].x);
+                        if (tb + i < nt) io<IO>::st(dst, (int64_t)(tb + i) * D, s_dk[tb + i][sl].x);
                 }
             }
             // this wave's LDS writes are performed before its later reads (a wavefront's LDS
@@ -328,12 +339,26 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
         for (int p = 0; p < P; ++p) {
             const int tt = row_of(p);
             if (tt < nt && qact) {
+                float part[K][V];   // the K partials of the thread's V channels (4-float units when V % 4 == 0)
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    if constexpr (V % 4 == 0) {
+#pragma unroll
+                        for (int v = 0; v < V; v += 4) {
+                            const f32x4_t q = *reinterpret_cast<const f32x4_t *>(&s_yp[k][tt][syp(cq + v)]);
+                            part[k][v] = q.x; part[k][v + 1] = q.y; part[k][v + 2] = q.z; part[k][v + 3] = q.w;
+                        }
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < V; ++v) part[k][v] = s_yp[k][tt][syp(cq + v)];
+                    }
+                }
                 float yv[V];
 #pragma unroll
                 for (int v = 0; v < V; ++v) {
-                    float a = fmaf(Dq[v], dg.u[p][v], s_yp[0][tt][cq + v]);
+                    float a = fmaf(Dq[v], dg.u[p][v], part[0][v]);
 #pragma unroll
-                    for (int k = 1; k < K; ++k) a += s_yp[k][tt][cq + v];
+                    for (int k = 1; k < K; ++k) a += part[k][v];
                     yv[v] = a * dg.g[p][v];
                 }
                 const int64_t idx = (row0 + t0 + tt) * D + d0 + cq;
@@ -358,20 +383,30 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             const int tt = row_of(p);
+            f32x2_t dk[V];
 #pragma unroll
             for (int v = 0; v < V; ++v) {
                 // (with the convolution, u comes from the conv phase through s_dk)
-                const float uu = CW > 0 ? s_dk[tt][cq + v].x : raw(r.u[p], v);
+                const float uu = CW > 0 ? s_dk[tt][sdk(cq + v)].x : raw(r.u[p], v);
                 const float x = raw(r.d[p], v) + bq[v];
                 const float dl = softplus ? softplus_f32(x) : x;
-                // (written unmasked: rows of tokens past the end are never read by the
-                // recurrence, and lanes of channels past D hold values loaded from an
-                // in-bounds channel and are never stored)
-                s_dk[tt][cq + v] = f32x2_t{dl, ZOH ? dl * uu * kLog2e : dl * uu};
+                dk[v] = f32x2_t{dl, ZOH ? dl * uu * kLog2e : dl * uu};
                 if (READOUT) {
                     cur.u[p][v] = uu;
                     if (gated) cur.g[p][v] = silu_f32(raw(r.z[p], v));
                 }
+            }
+            // (written unmasked: rows of tokens past the end are never read by the
+            // recurrence, and lanes of channels past D hold values loaded from an in-bounds
+            // channel and are never stored); two channels per 16-byte write when V is even
+            if constexpr (V % 2 == 0) {
+#pragma unroll
+                for (int v = 0; v < V; v += 2)
+                    *reinterpret_cast<f32x4_t *>(&s_dk[tt][sdk(cq + v)]) =
+                        f32x4_t{dk[v].x, dk[v].y, dk[v + 1].x, dk[v + 1].y};
+            } else {
+#pragma unroll
+                for (int v = 0; v < V; ++v) s_dk[tt][sdk(cq + v)] = dk[v];
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -402,7 +437,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                 for (int i = 0; i < G; ++i) {
                     // the prefetch after the last group runs past the tile: clamp (unused)
                     const int tt = g0 + i < T ? g0 + i : T - 1;
-                    v[i] = s_dk[tt][lane];
+                    v[i] = s_dk[tt][sl];
                     const uint32_t *bp = reinterpret_cast<const uint32_t *>(btile + tt * N);
                     const uint32_t *cp = reinterpret_cast<const uint32_t *>(ctile + tt * N);
 #pragma unroll
@@ -427,7 +462,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                         if (READOUT) acc = fmaf(word_f32<IO>(cw[i], s), h[s], acc);
                     }
                     if (READOUT)
-                        s_yp[w][g0 + i][lane] = acc;
+                        s_yp[w][g0 + i][yl] = acc;
                     else if (MODE == kSummary)
                         dsum += v[i].x;
                 }
@@ -450,7 +485,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
 #pragma unroll 4
             for (int tt = 0; tt < nt; ++tt) {
                 if (tt > 0 && tt % kCkptEvery == 0) checkpoint(t0 + tt);
-                const f32x2_t v = s_dk[tt][lane];
+                const f32x2_t v = s_dk[tt][sl];
                 const int64_t boff = (row0 + t0 + tt) * N + w * S;
                 float Bs[S], Cs[S];
                 load_slice<S>(Bm, boff, Bs);
@@ -466,7 +501,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                     if (READOUT) acc = fmaf(Cs[s], h[s], acc);
                 }
                 if (READOUT)
-                    s_yp[w][tt][lane] = acc;
+                    s_yp[w][tt][yl] = acc;
                 else if (MODE == kSummary)
                     dsum += v.x;
             }
