@@ -69,6 +69,22 @@ def test_ssd_layer_size_sampled(oracle_mod):
     check(c, y[:, :, heads], ls[:, heads], y_ref, ls_ref, "layer, 4 heads")
 
 
+def test_ssd_grid_beyond_one_round(oracle_mod):
+    """1024 (sequence, head) workgroups -- more than the GPU holds at once -- with four groups of
+    B / C and a ragged last chunk; the oracle on sampled heads, each with its own group."""
+    c = inputs.ssd_case(4, 130, 256, G=4, seed=232)
+    y, ls = run_gpu(c)
+    H, G = 256, 4
+    for h in (0, 63, 64, 200, 255):
+        g = h // (H // G)
+        xv, dtv, zv = c.values("x")[:, :, [h]], c.values("dt")[:, :, [h]], c.values("z")
+        y_ref, ls_ref = oracle_mod.ssd(xv, dtv, c.A[[h]], c.values("B")[:, :, [g]], c.values("C")[:, :, [g]],
+                                       D=None if c.Dskip is None else c.Dskip[[h]],
+                                       z=None if zv is None else zv[:, :, [h]],
+                                       dt_bias=None if c.dt_bias is None else c.dt_bias[[h]], softplus=c.softplus)
+        check(c, y[:, :, [h]], ls[:, [h]], y_ref, ls_ref, f"1024 workgroups, head {h} (group {g})")
+
+
 def test_ssd_deterministic():
     c = inputs.ssd_case(2, 700, 8, G=2, seed=231)
     y1, l1 = run_gpu(c)
