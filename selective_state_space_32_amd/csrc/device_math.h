@@ -123,21 +123,18 @@ __device__ __forceinline__ float softplus_f32(float x) {
     return softplus_f32(x, sig);
 }
 
-// Exact zero-order hold of the input term: B_bar = (exp(delta A) - 1) / A * B =
-// delta * phi(delta A) * B with phi(x) = (e^x - 1) / x.  zoh_factor(y, e) returns
-// ln(2) phi(x) = (e - 1) / y for y = x log2(e) and e = exp2(y) (both already formed for the
-// decay), so the input term is (delta u log2(e)) * B * zoh_factor.  For |x| < 1/4 it is the
-// Taylor series of ln(2) phi(y ln 2) = sum_k ln(2)^(k+1) y^k / (k+1)!, cut after y^5
-// (relative truncation below 6e-8); there e - 1 would lose up to 2^-24 / |x| of its value
-// to the rounding of e.  Elsewhere |e - 1| >= 0.22 and (e - 1) / y is accurate to ~1e-6.
-__device__ __forceinline__ float zoh_factor(float y, float e) {
-    float p = fmaf(y, 1.5403530393381606e-4f, 1.3333558146428441e-3f);
-    p = fmaf(y, p, 9.618129107628477e-3f);
-    p = fmaf(y, p, 5.5504108664821576e-2f);
-    p = fmaf(y, p, 2.402265069591007e-1f);
-    p = fmaf(y, p, 6.931471805599453e-1f);
-    const float q = (e - 1.0f) * hw_rcp(y);
-    return fabsf(y) < 0.25f * kLog2e ? p : q;
+// Exact zero-order hold of the input term: B_bar u = (exp(delta A) - 1) / A * B * u =
+// delta * phi(delta A) * B * u with phi(x) = (e^x - 1) / x.  zoh_weight returns the factor m
+// with B_bar u = m * u * B, from y = x log2(e) and e = exp2(y) (both already formed for the
+// decay), delta and 1 / A: (e - 1) / A where |x| >= 1/32, else delta (1 + x/2 + x^2/6).  Below
+// the threshold the dropped terms are under x^3/24 < 1.3e-6 of phi; above it e - 1 loses at
+// most 2^-24 / |x| <= 1.9e-6 of its value to the rounding of e.  (For A = 0, x = 0 selects
+// the series, so 1 / A never reaches the result.)
+__device__ __forceinline__ float zoh_weight(float y, float e, float delta, float inv_a) {
+    const float t = fmaf(y, kLn2 * kLn2 * (1.0f / 6.0f), kLn2 * 0.5f);   // (1/2 + x/6) with x = y ln 2, over ln 2
+    const float p = fmaf(delta * y, t, delta);                            // delta (1 + x/2 + x^2/6)
+    const float q = (e - 1.0f) * inv_a;
+    return fabsf(y) < (1.0f / 32.0f) * kLog2e ? p : q;
 }
 
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z).  For z << 0, e^-z = inf and the result is -0.

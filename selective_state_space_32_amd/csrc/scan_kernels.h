@@ -159,10 +159,12 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     const bool qact = d0 + cq < D;          // whole group in or out (D % V == 0 when VEC)
     const int64_t dq = qact ? d0 + cq : (D - V) / V * V;  // in-bounds channel for loads
 
-    float a2[S], h[S];
+    float a2[S], h[S], inv_a[ZOH ? S : 1];   // (1 / A for the zero-order hold)
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        a2[s] = act ? A[d * N + w * S + s] * kLog2e : 0.0f;
+        const float a = act ? A[d * N + w * S + s] : 0.0f;
+        a2[s] = a * kLog2e;
+        if constexpr (ZOH) inv_a[s] = act ? 1.0f / a : 0.0f;
         h[s] = 0.0f;
     }
     if ((MODE == kFull || MODE == kCheckpoint) && act) {
@@ -390,7 +392,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                 const float uu = CW > 0 ? s_dk[tt][sdk(cq + v)].x : raw(r.u[p], v);
                 const float x = raw(r.d[p], v) + bq[v];
                 const float dl = softplus ? softplus_f32(x) : x;
-                dk[v] = f32x2_t{dl, ZOH ? dl * uu * kLog2e : dl * uu};
+                dk[v] = f32x2_t{dl, ZOH ? uu : dl * uu};
                 if (READOUT) {
                     cur.u[p][v] = uu;
                     if (gated) cur.g[p][v] = silu_f32(raw(r.z[p], v));
@@ -457,7 +459,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                         const float ya = v[i].x * a2[s];
                         const float e = hw_exp2(ya);
                         float bu = v[i].y * word_f32<IO>(bw[i], s);
-                        if constexpr (ZOH) bu *= zoh_factor(ya, e);
+                        if constexpr (ZOH) bu *= zoh_weight(ya, e, v[i].x, inv_a[s]);
                         h[s] = fmaf(e, h[s], bu);
                         if (READOUT) acc = fmaf(word_f32<IO>(cw[i], s), h[s], acc);
                     }
@@ -496,7 +498,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                     const float ya = v.x * a2[s];
                     const float e = hw_exp2(ya);
                     float bu = v.y * Bs[s];
-                    if constexpr (ZOH) bu *= zoh_factor(ya, e);
+                    if constexpr (ZOH) bu *= zoh_weight(ya, e, v.x, inv_a[s]);
                     h[s] = fmaf(e, h[s], bu);
                     if (READOUT) acc = fmaf(Cs[s], h[s], acc);
                 }
