@@ -42,6 +42,8 @@ WORKLOADS = {
     "c4": "selective scan B1 L131072 D2048 N16, bf16 I/O, fp32 state, last_state",
     "c5": "recurrent step S256 D5120 N16, bf16 I/O, fp32 state in place",
     "c3_bwd": "selective scan backward B8 L2048 D5120 N16, bf16 I/O, fp32 state, SiLU(z) gate, D skip",
+    "c3_train": "selective scan training step (forward with the backward's checkpoints + backward) B8 L2048 "
+                "D5120 N16, bf16 I/O, fp32 state, SiLU(z) gate, D skip, last_state",
     "c3_zoh": "selective scan with the exact zero-order-hold input term B8 L2048 D5120 N16, bf16 I/O, "
               "fp32 state, SiLU(z) gate, D skip, last_state",
     "c3_conv": "causal depthwise conv1d (width 4) + SiLU B8 L2048 D5120, bf16 I/O, conv state out",
@@ -167,9 +169,10 @@ def cpu_baseline_scan(case, alg_bytes_full, target_s=30.0, exact_zoh=False):
                       f"(fp64 oracle, OpenMP over channels)"}
 
 
-def cpu_baseline_bwd(case, alg_bytes_full, target_s=20.0):
-    """The fp64 oracle's backward on a channel sample of the workload (per-channel work is
-    independent; the cross-channel dB / dC sums then cover the sample only)."""
+def cpu_baseline_bwd(case, alg_bytes_full, target_s=20.0, with_forward=False):
+    """The fp64 oracle's backward (after its forward, with_forward) on a channel sample of the
+    workload (per-channel work is independent; the cross-channel dB / dC sums then cover the
+    sample only)."""
     from oracle import oracle
     oracle.build(force=False)
     threads = min(16, oracle.default_threads())
@@ -178,6 +181,8 @@ def cpu_baseline_bwd(case, alg_bytes_full, target_s=20.0):
 
     def run(sel):
         zv = case.values("z")
+        if with_forward:
+            oracle.scan_case(case, channels=sel, threads=threads)
         oracle.scan_bwd(case.values("u")[:, :, sel], case.values("delta")[:, :, sel], case.A[sel], case.values("B"),
                         case.values("C"), np.resize(dyv, (case.bsz, case.L, len(sel))), D=case.Dskip[sel],
                         z=None if zv is None else zv[:, :, sel], delta_bias=case.delta_bias[sel],
@@ -194,7 +199,7 @@ def cpu_baseline_bwd(case, alg_bytes_full, target_s=20.0):
     return {"value": round(alg_bytes_full * len(sel) / case.D / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"{len(sel)} of {case.D} channels x all {case.bsz} sequences x {case.L} tokens "
-                      f"(fp64 oracle backward, OpenMP over channels)"}
+                      f"(fp64 oracle {'forward + ' if with_forward else ''}backward, OpenMP over channels)"}
 
 
 def conv_alg_bytes(bsz, L, D, width, io_bytes):
@@ -304,7 +309,7 @@ def main():
     elif wl == "ssd":
         case = inputs.ssd_case(8, 2048, 80, 64, 1, 64, seed=230, name="ssd")
     else:
-        case = inputs.config_case("c3" if wl in ("c3_bwd", "c3_zoh", "c3_block") else wl)
+        case = inputs.config_case("c3" if wl in ("c3_bwd", "c3_train", "c3_zoh", "c3_block") else wl)
     io_bytes = 2 if getattr(case, "io", "bf16") == "bf16" else 4
 
     def td(a):
@@ -375,6 +380,31 @@ def main():
             ssmscan.scan_bwd(dy, t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
                              delta_bias=t["bias"], softplus=case.softplus, workspace=ws, out=grads)
         plan = "checkpoint pass (state every 8 tokens) + backward kernel"
+    elif wl == "c3_train":
+        t = {k: td(getattr(case, f)) for k, f in (("u", "u"), ("delta", "delta"), ("A", "A"), ("B", "B"),
+                                                   ("C", "C"), ("D", "Dskip"), ("z", "z"), ("bias", "delta_bias"))}
+        bsz, L, D, N = case.bsz, case.L, case.D, case.N
+        dy = td(inputs.bf16_bits(np.random.default_rng(13).standard_normal((bsz, L, D), dtype=np.float32)))
+        y = torch.empty((bsz, L, D), dtype=dy.dtype, device=dev)
+        ls = torch.empty((bsz, D, N), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, ssmscan.bwd_workspace_bytes(bsz, L, D, N, dy.dtype) +
+                             ssmscan.workspace_bytes(bsz, L, D, N, dy.dtype)), dtype=torch.uint8, device=dev)
+        fwd = ssmscan.scan_fwd_call(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                    delta_bias=t["bias"], softplus=case.softplus, y=y, last_state=ls, workspace=ws,
+                                    save_checkpoints=True)
+        fwd()
+        grads = ssmscan.scan_bwd(dy, t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                 delta_bias=t["bias"], softplus=case.softplus, checkpoints=ws)
+        alg = scan_alg_bytes(bsz, L, D, N, io_bytes, True, True, True, True) + scan_bwd_alg_bytes(bsz, L, D, N,
+                                                                                                 io_bytes)
+        chtok = bsz * L * D
+        elements = chtok * N
+
+        def one(i):
+            fwd()
+            ssmscan.scan_bwd(dy, t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                             delta_bias=t["bias"], softplus=case.softplus, checkpoints=ws, out=grads)
+        plan = "forward storing the backward's checkpoints (state every 8 tokens) + backward kernel from them"
     else:
         t = {k: td(getattr(case, f)) for k, f in (("u", "u"), ("delta", "delta"), ("A", "A"), ("B", "B"),
                                                    ("C", "C"), ("D", "Dskip"), ("z", "z"), ("bias", "delta_bias"))}
@@ -454,7 +484,8 @@ def main():
     step_s = wall / args.steps
     gbps = alg / step_s / 1e9          # whole-job throughput over the timed region
     kern_gbps = alg / kern_s / 1e9     # the kernel's own rate (event-timed launches)
-    slots = {"c3_bwd": SLOTS_PER_ELEMENT_BWD, "c3_zoh": SLOTS_PER_ELEMENT_ZOH}.get(wl, SLOTS_PER_ELEMENT)
+    slots = {"c3_bwd": SLOTS_PER_ELEMENT_BWD, "c3_zoh": SLOTS_PER_ELEMENT_ZOH,
+             "c3_train": SLOTS_PER_ELEMENT + SLOTS_PER_ELEMENT_BWD}.get(wl, SLOTS_PER_ELEMENT)
     work_ops = elements * slots + (chtok * SLOTS_PER_CHTOK_CONV if wl == "c3_block" else 0)
     lane_ops = work_ops / kern_s / 1e12
     traffic = counter_traffic(wl)
@@ -473,6 +504,7 @@ def main():
     if not args.no_cpu:
         try:
             cpu = (cpu_baseline_step(case, alg) if wl == "c5" else cpu_baseline_bwd(case, alg) if wl == "c3_bwd"
+                   else cpu_baseline_bwd(case, alg, with_forward=True) if wl == "c3_train"
                    else cpu_baseline_conv(case, alg) if wl == "c3_conv"
                    else cpu_baseline_ssd(case, alg) if wl == "ssd"
                    else cpu_baseline_block(case, cc, alg) if wl == "c3_block"

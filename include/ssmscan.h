@@ -49,11 +49,13 @@
 extern "C" {
 #endif
 
-#define SSMSCAN_VERSION 7
+#define SSMSCAN_VERSION 8
 
 /* Bits of the `flags` argument of the scan entry points. */
 #define SSM_SCAN_SOFTPLUS 1     /* step size = softplus(delta + delta_bias) */
 #define SSM_SCAN_EXACT_ZOH 2    /* exact zero-order-hold input term (forward only) */
+#define SSM_SCAN_CHECKPOINTS 4  /* forward: also store the backward pass's checkpoints in the
+                                   workspace; backward: the workspace already holds them */
 
 #if defined(__GNUC__) || defined(__clang__)
 #define SSMSCAN_API __attribute__((visibility("default")))
@@ -116,14 +118,20 @@ SSMSCAN_API int64_t ssm_scan_plan(const ssm_dims *dims, int64_t *chunk_len_out);
  *   B, C           : [batch][seqlen][dstate] (io_dtype)
  *   A              : [dim][dstate] fp32
  *   D, delta_bias  : [dim] fp32, each may be NULL (= 0)
- *   flags          : SSM_SCAN_SOFTPLUS (apply softplus to delta + delta_bias) and/or
- *                    SSM_SCAN_EXACT_ZOH (exact zero-order-hold input term); other bits are
- *                    rejected with SSM_ERR_FLAGS
+ *   flags          : SSM_SCAN_SOFTPLUS (apply softplus to delta + delta_bias), and
+ *                    SSM_SCAN_EXACT_ZOH (exact zero-order-hold input term) or
+ *                    SSM_SCAN_CHECKPOINTS (see workspace); other bits and the pair
+ *                    ZOH + CHECKPOINTS are rejected with SSM_ERR_FLAGS
  *   y              : output, written completely
  *   last_state     : [batch][dim][dstate] fp32 output h_L, may be NULL
  *   workspace      : device memory of at least ssm_scan_workspace_bytes(dims) bytes, 16-byte
  *                    aligned (contents on entry do not matter; scratch for this call);
- *                    may be NULL when that size is 0
+ *                    may be NULL when that size is 0.  With SSM_SCAN_CHECKPOINTS (a training
+ *                    forward) it must hold ssm_scan_bwd_workspace_bytes(dims) +
+ *                    ssm_scan_workspace_bytes(dims) bytes, and the call leaves in its first
+ *                    ssm_scan_bwd_workspace_bytes(dims) bytes the states ssm_scan_bwd would
+ *                    otherwise recompute in a pass of its own: pass the same workspace and
+ *                    flag to ssm_scan_bwd
  * Returns SSM_OK or a negative ssm_status. */
 SSMSCAN_API int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
                  const float *D, const void *z, const float *delta_bias, int flags,
@@ -155,8 +163,8 @@ SSMSCAN_API size_t ssm_scan_bwd_workspace_bytes(const ssm_dims *dims);
  * pass, recomputing the states from checkpoints instead of storing them
  * (azimuth.plus/paper/mamba, hardware-aware algorithm section).
  *   inputs          : exactly those of the forward call (same shapes, dtypes, NULLs);
- *                     flags may hold SSM_SCAN_SOFTPLUS only (the gradients of the exact-ZOH
- *                     input term are not provided: SSM_ERR_FLAGS)
+ *                     flags may hold SSM_SCAN_SOFTPLUS and SSM_SCAN_CHECKPOINTS (the
+ *                     gradients of the exact-ZOH input term are not provided: SSM_ERR_FLAGS)
  *   dy              : [batch][seqlen][dim] (io_dtype)
  *   dlast_state     : [batch][dim][dstate] fp32, or NULL (= 0)
  *   du, ddelta      : [batch][seqlen][dim] (io_dtype) outputs; ddelta is the gradient with
@@ -166,7 +174,10 @@ SSMSCAN_API size_t ssm_scan_bwd_workspace_bytes(const ssm_dims *dims);
  *   dB, dC          : [batch][seqlen][dstate] fp32 outputs (summed over channels)
  *   dD, ddelta_bias : [dim] fp32 outputs, or NULL (not wanted)
  *   dinitial_state  : [batch][dim][dstate] fp32 output, or NULL (not wanted)
- *   workspace       : at least ssm_scan_bwd_workspace_bytes(dims) bytes, 16-byte aligned
+ *   workspace       : at least ssm_scan_bwd_workspace_bytes(dims) bytes, 16-byte aligned;
+ *                     with SSM_SCAN_CHECKPOINTS it must hold the checkpoints a forward call
+ *                     with that flag stored there (same inputs, initial state and dims;
+ *                     not checked), and the checkpoint pass is skipped
  * dims->chunk_len is ignored.  dA, dB, dC, dD and ddelta_bias are sums over many
  * workgroups, accumulated with atomic adds after the library has zeroed them: their last
  * bits may differ from run to run.  Outputs must not overlap inputs or each other.

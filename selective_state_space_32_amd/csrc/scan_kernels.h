@@ -77,6 +77,8 @@ __device__ __forceinline__ void load_slice(const IO *__restrict__ p, int64_t off
 //   kCheckpoint: one pass from h0 without readout, storing the state before every
 //             kCkptEvery-th token to cstate[b][t / kCkptEvery] (the backward pass's
 //             recomputation points).
+//   CK (kFull only): the same checkpoints, to ckpt_out, from the forward itself (a
+//             training forward; the backward then skips its kCheckpoint pass).
 //   N: state size; S: states per wave (K = N/S waves); T: tokens per LDS tile.
 //   VEC: the prep and epilogue move V consecutive channels of one token per thread
 //        (one 16-byte access for 8 bf16); needs D % 8 == 0 and 16-byte aligned u, delta,
@@ -91,7 +93,7 @@ __device__ __forceinline__ void load_slice(const IO *__restrict__ p, int64_t off
 //        tile and the CW - 1 rows before it), filled one tile ahead from the prefetched
 //        registers; a conv phase with lane = channel (each wave takes the rows its own
 //        threads prepare, its CW taps in registers) writes u where the prep reads it.
-template <int N, int S, int T, typename IO, int MODE, bool VEC, bool ZOH = false, int CW = 0>
+template <int N, int S, int T, typename IO, int MODE, bool VEC, bool ZOH = false, int CW = 0, bool CK = false>
 __global__ void __launch_bounds__(64 * (N / S))
 scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                   const IO *__restrict__ z, IO *__restrict__ y,
@@ -101,7 +103,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                   float *__restrict__ cstate, float *__restrict__ cdsum, int64_t L, int64_t D,
                   int tiles_per_b, int n_tiles, int64_t chunk_len, int nchunk, int softplus,
                   const float *__restrict__ conv_w = nullptr, const float *__restrict__ conv_b = nullptr,
-                  IO *__restrict__ u_out = nullptr) {
+                  IO *__restrict__ u_out = nullptr, float *__restrict__ ckpt_out = nullptr) {
     constexpr int K = N / S;
     constexpr int J = T / K;                   // prep / epilogue elements per thread per tile
     constexpr int V = VEC ? (J < 8 ? J : 8) : 1;  // consecutive channels per thread access
@@ -318,14 +320,15 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
         ring_fill(0, r0);
         __syncthreads();
     }
-    // kCheckpoint: the state before token t (t a multiple of kCkptEvery) into
-    // cstate[b][t / kCkptEvery][d][:]
+    // kCheckpoint (and kFull with CK, the training forward): the state before token t (t a
+    // multiple of kCkptEvery) into cstate (ckpt_out)[b][t / kCkptEvery][d][:]
     const int64_t n_ckpt = (L + kCkptEvery - 1) / kCkptEvery;
     auto checkpoint = [&](int64_t t) {
-        if (MODE == kCheckpoint && act && t < t_end) {
+        if ((MODE == kCheckpoint || (MODE == kFull && CK)) && act && t < t_end) {
+            float *dst = (MODE == kCheckpoint ? cstate : ckpt_out) +
+                         (((int64_t)b * n_ckpt + t / kCkptEvery) * D + d) * N + w * S;
 #pragma unroll
-            for (int s = 0; s < S; ++s)
-                cstate[(((int64_t)b * n_ckpt + t / kCkptEvery) * D + d) * N + w * S + s] = h[s];
+            for (int s = 0; s < S; ++s) dst[s] = h[s];
         }
     };
     // epilogue of a tile: y = (sum of the K partial readouts + D u) * silu(z), read from

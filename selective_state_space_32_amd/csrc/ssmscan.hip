@@ -136,11 +136,12 @@ struct ConvArgs {
     void *u_out;
 };
 
-template <int N, typename IO, bool VEC, bool ZOH, int CW = 0>
+// (CK: the full pass also stores the backward pass's checkpoints to ckpt)
+template <int N, typename IO, bool VEC, bool ZOH, int CW = 0, bool CK = false>
 void launch_scan_kernels(const IO *u, const IO *dl, const float *A, const IO *B, const IO *C, const float *Dv,
                          const IO *z, const float *bias, int softplus, const float *h0, IO *y, float *last_state,
                          const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st,
-                         const ConvArgs &cv = ConvArgs{nullptr, nullptr, nullptr}) {
+                         const ConvArgs &cv = ConvArgs{nullptr, nullptr, nullptr}, float *ckpt = nullptr) {
     constexpr int S = ScanShape<N>::S;
     constexpr int T = ScanShape<N>::T;
     constexpr int K = N / S;
@@ -162,17 +163,17 @@ void launch_scan_kernels(const IO *u, const IO *dl, const float *A, const IO *B,
         hipLaunchKernelGGL((ssm::carry_scan_kernel<N>), dim3((unsigned)(bsz * col_tiles)), dim3(256), 0, st,
                            cstate, (const float *)cdsum, A, h0, D, nc, col_tiles);
     }
-    hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kFull, VEC, ZOH, CW>),
+    hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kFull, VEC, ZOH, CW, CK>),
                        dim3((unsigned)n_tiles, (unsigned)nc), block, 0, st, u, dl, z, y, A, Dv, bias, B, C, h0,
                        last_state, cstate, cdsum, L, D, tiles_per_b, n_tiles, cl, nc, softplus, cv.w, cv.b,
-                       static_cast<IO *>(cv.u_out));
+                       static_cast<IO *>(cv.u_out), ckpt);
 }
 
 template <int N, typename IO>
 int launch_scan(const void *u, const void *delta, const float *A, const void *B, const void *C,
                 const float *Dv, const void *z, const float *bias, int flags, const float *h0, void *y,
                 float *last_state, const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st,
-                const ConvArgs *cv) {
+                const ConvArgs *cv, float *ckpt) {
     const int softplus = (flags & SSM_SCAN_SOFTPLUS) != 0;
     const bool zoh = (flags & SSM_SCAN_EXACT_ZOH) != 0;
     const IO *u_ = static_cast<const IO *>(u);
@@ -196,7 +197,16 @@ int launch_scan(const void *u, const void *delta, const float *A, const void *B,
         if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
         return ok();
     }
-    if (vec && zoh)
+    if (ckpt) {
+        // the training forward: the backward pass's checkpoints too (no exact ZOH, checked by the caller)
+        const ConvArgs none{nullptr, nullptr, nullptr};
+        if (vec)
+            launch_scan_kernels<N, IO, true, false, 0, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_,
+                                                             last_state, dm, p, ws, st, none, ckpt);
+        else
+            launch_scan_kernels<N, IO, false, false, 0, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_,
+                                                              last_state, dm, p, ws, st, none, ckpt);
+    } else if (vec && zoh)
         launch_scan_kernels<N, IO, true, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state, dm, p,
                                                ws, st);
     else if (vec)
@@ -217,13 +227,13 @@ template <typename IO>
 int dispatch_scan(int64_t N, const void *u, const void *delta, const float *A, const void *B,
                   const void *C, const float *Dv, const void *z, const float *bias, int flags, const float *h0,
                   void *y, float *ls, const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st,
-                  const ConvArgs *cv) {
+                  const ConvArgs *cv, float *ckpt) {
     switch (N) {
-        case 1: return launch_scan<1, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv);
-        case 2: return launch_scan<2, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv);
-        case 4: return launch_scan<4, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv);
-        case 8: return launch_scan<8, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv);
-        case 16: return launch_scan<16, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv);
+        case 1: return launch_scan<1, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv, ckpt);
+        case 2: return launch_scan<2, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv, ckpt);
+        case 4: return launch_scan<4, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv, ckpt);
+        case 8: return launch_scan<8, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv, ckpt);
+        case 16: return launch_scan<16, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv, ckpt);
     }
     return fail(SSM_ERR_UNSUPPORTED_N, "dstate %lld not supported", (long long)N);
 }
@@ -293,6 +303,7 @@ struct BwdArgs {
     float *dA, *dB, *dC, *dD;
     void *dz;
     float *dbias, *dh0;
+    bool ckpt_given;   // the workspace already holds the checkpoints (written by the training forward)
 };
 
 template <int N, typename IO>
@@ -307,18 +318,21 @@ int launch_bwd(const BwdArgs &a, const ssm_dims *dm, void *ws, hipStream_t st) {
     const IO *z = static_cast<const IO *>(a.z), *dy = static_cast<const IO *>(a.dy);
     IO *du = static_cast<IO *>(a.du), *ddl = static_cast<IO *>(a.ddelta), *dz = static_cast<IO *>(a.dz);
     float *ckpt = static_cast<float *>(ws);
-    // forward in checkpoint mode: the state before every kCkptEvery-th token
+    // forward in checkpoint mode: the state before every kCkptEvery-th token (unless the
+    // training forward has stored them already)
     const bool vf = D % 8 == 0 && aligned(u, 16) && aligned(dl, 16);
-    if (vf)
-        hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kCheckpoint, true>), dim3((unsigned)n_tiles, 1),
-                           dim3(64 * K), 0, st, u, dl, (const IO *)nullptr, (IO *)nullptr, a.A, (const float *)nullptr,
-                           a.bias, B, C, a.h0, (float *)nullptr, ckpt, (float *)nullptr, L, D, tiles_per_b, n_tiles, L,
-                           1, a.softplus);
-    else
-        hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kCheckpoint, false>), dim3((unsigned)n_tiles, 1),
-                           dim3(64 * K), 0, st, u, dl, (const IO *)nullptr, (IO *)nullptr, a.A, (const float *)nullptr,
-                           a.bias, B, C, a.h0, (float *)nullptr, ckpt, (float *)nullptr, L, D, tiles_per_b, n_tiles, L,
-                           1, a.softplus);
+    if (!a.ckpt_given) {
+        if (vf)
+            hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kCheckpoint, true>), dim3((unsigned)n_tiles, 1),
+                               dim3(64 * K), 0, st, u, dl, (const IO *)nullptr, (IO *)nullptr, a.A,
+                               (const float *)nullptr, a.bias, B, C, a.h0, (float *)nullptr, ckpt, (float *)nullptr, L,
+                               D, tiles_per_b, n_tiles, L, 1, a.softplus);
+        else
+            hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kCheckpoint, false>),
+                               dim3((unsigned)n_tiles, 1), dim3(64 * K), 0, st, u, dl, (const IO *)nullptr,
+                               (IO *)nullptr, a.A, (const float *)nullptr, a.bias, B, C, a.h0, (float *)nullptr, ckpt,
+                               (float *)nullptr, L, D, tiles_per_b, n_tiles, L, 1, a.softplus);
+    }
     // the reverse walk; 16-byte (or 8-byte) element access when every (token, channel) tensor allows it
     const bool vb = D % 8 == 0 && aligned(u, 16) && aligned(dl, 16) && aligned(dy, 16) && aligned(du, 16) &&
                     aligned(ddl, 16) && (!z || (aligned(z, 16) && aligned(dz, 16)));
@@ -403,7 +417,12 @@ static int scan_impl(const float *h0, const void *u, const void *delta, const fl
                      void *stream, const ConvArgs *cv = nullptr) {
     int rc = check_dims(dims, true);
     if (rc != SSM_OK) return rc;
-    if (flags & ~(SSM_SCAN_SOFTPLUS | SSM_SCAN_EXACT_ZOH)) return fail(SSM_ERR_FLAGS, "unknown flag bits 0x%x", flags);
+    if (flags & ~(SSM_SCAN_SOFTPLUS | SSM_SCAN_EXACT_ZOH | SSM_SCAN_CHECKPOINTS))
+        return fail(SSM_ERR_FLAGS, "unknown flag bits 0x%x", flags);
+    const bool want_ckpt = (flags & SSM_SCAN_CHECKPOINTS) != 0;
+    if (want_ckpt && (flags & SSM_SCAN_EXACT_ZOH))
+        return fail(SSM_ERR_FLAGS, "checkpoints for the backward pass are not available with the exact ZOH");
+    if (want_ckpt && cv) return fail(SSM_ERR_FLAGS, "checkpoints are not available with the fused convolution");
     const int64_t bsz = dims->batch, L = dims->seqlen, Dm = dims->dim, N = dims->dstate;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (bsz == 0 || Dm == 0) return ok();
@@ -441,16 +460,20 @@ static int scan_impl(const float *h0, const void *u, const void *delta, const fl
             return fail(SSM_ERR_FLAGS, "the exact zero-order hold is not available with the fused convolution");
     }
     Plan p = make_plan(dims);
-    if (p.bytes > 0 && !workspace) return fail(SSM_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", p.bytes);
-    if (workspace_bytes < p.bytes)
+    // with checkpoints the workspace holds them first (the backward pass's layout), then the plan's carry area
+    const size_t ck_bytes = want_ckpt ? bwd_workspace_bytes(dims) : 0, need = ck_bytes + p.bytes;
+    if (need > 0 && !workspace) return fail(SSM_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes < need)
         return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
-                    p.bytes);
-    if (p.bytes > 0 && !aligned(workspace, 16)) return fail(SSM_ERR_ALIGN, "workspace not 16-byte aligned");
+                    need);
+    if (need > 0 && !aligned(workspace, 16)) return fail(SSM_ERR_ALIGN, "workspace not 16-byte aligned");
+    float *ckpt = want_ckpt ? static_cast<float *>(workspace) : nullptr;
+    void *carry_ws = p.bytes > 0 ? static_cast<void *>(static_cast<char *>(workspace) + ck_bytes) : workspace;
     if (dims->io_dtype == SSM_IO_BF16)
         return dispatch_scan<uint16_t>(N, u, delta, A, B, C, D, z, delta_bias, flags, h0, y, last_state, dims, p,
-                                       workspace, st, cv);
+                                       carry_ws, st, cv, ckpt);
     return dispatch_scan<float>(N, u, delta, A, B, C, D, z, delta_bias, flags, h0, y, last_state, dims, p,
-                                workspace, st, cv);
+                                carry_ws, st, cv, ckpt);
 }
 
 
@@ -533,9 +556,9 @@ int ssm_scan_bwd(const float *initial_state, const void *u, const void *delta, c
                  void *workspace, size_t workspace_bytes, void *stream) {
     int rc = check_dims(dims, true);
     if (rc != SSM_OK) return rc;
-    if (flags & ~SSM_SCAN_SOFTPLUS)
-        return fail(SSM_ERR_FLAGS, "flags 0x%x: the backward pass takes the softplus flag only (no exact ZOH)",
-                    flags);
+    if (flags & ~(SSM_SCAN_SOFTPLUS | SSM_SCAN_CHECKPOINTS))
+        return fail(SSM_ERR_FLAGS,
+                    "flags 0x%x: the backward pass takes the softplus and checkpoints flags only (no exact ZOH)", flags);
     const int64_t bsz = dims->batch, L = dims->seqlen, Dm = dims->dim, N = dims->dstate;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (!A || !dA || (bsz > 0 && L > 0 && Dm > 0 && (!u || !delta || !B || !C || !dy || !du || !ddelta || !dB || !dC)))
@@ -581,7 +604,7 @@ int ssm_scan_bwd(const float *initial_state, const void *u, const void *delta, c
         return ok();
     }
     BwdArgs a{initial_state, u, delta, A, B, C, D, z, delta_bias, (flags & SSM_SCAN_SOFTPLUS) != 0, dy, dlast_state, du, ddelta,
-              dA, dB, dC, dD, dz, ddelta_bias, dinitial_state};
+              dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, (flags & SSM_SCAN_CHECKPOINTS) != 0};
     if (dims->io_dtype == SSM_IO_BF16) return dispatch_bwd<uint16_t>(N, a, dims, workspace, st);
     return dispatch_bwd<float>(N, a, dims, workspace, st);
 }

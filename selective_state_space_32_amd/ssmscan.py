@@ -140,10 +140,11 @@ def _stream_handle(stream) -> ctypes.c_void_p:
 
 SCAN_SOFTPLUS = 1      # flag bits of the scan entry points (include/ssmscan.h)
 SCAN_EXACT_ZOH = 2
+SCAN_CHECKPOINTS = 4
 
 
 def _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state, return_last_state, chunk_len,
-               workspace, stream, initial_state=None, exact_zoh=False):
+               workspace, stream, initial_state=None, exact_zoh=False, save_checkpoints=False):
     if u.dim() != 3:
         raise ValueError("u must be (batch, L, dim)")
     bsz, L, dim = u.shape
@@ -173,17 +174,20 @@ def _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state, ret
         _need(last_state, "last_state", (bsz, dim, N), torch.float32, dev)
     dims = make_dims(bsz, L, dim, N, io, chunk_len)
     need = int(lib.ssm_scan_workspace_bytes(ctypes.byref(dims)))
+    if save_checkpoints:   # the backward pass's checkpoints first, then the plan's carry area
+        need += int(lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(dims)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     args = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-            (SCAN_SOFTPLUS if softplus else 0) | (SCAN_EXACT_ZOH if exact_zoh else 0), _ptr(y),
+            (SCAN_SOFTPLUS if softplus else 0) | (SCAN_EXACT_ZOH if exact_zoh else 0) |
+            (SCAN_CHECKPOINTS if save_checkpoints else 0), _ptr(y),
             _ptr(last_state), ctypes.byref(dims), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream_handle(stream))
     if initial_state is not None:
         args = (_ptr(initial_state),) + args
     # the tensors and the dims struct the pointers refer to, kept alive with the arguments
     keep = (u, delta, A, B, C, D, z, delta_bias, y, last_state, workspace, dims, initial_state)
-    return args, keep, y, last_state
+    return args, keep, y, last_state, workspace
 
 
 def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
@@ -191,19 +195,23 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
              delta_bias: Optional[torch.Tensor] = None, softplus: bool = True, *,
              y: Optional[torch.Tensor] = None, last_state: Optional[torch.Tensor] = None,
              return_last_state: bool = True, chunk_len: int = 0,
-             workspace: Optional[torch.Tensor] = None, stream=None, exact_zoh: bool = False):
+             workspace: Optional[torch.Tensor] = None, stream=None, exact_zoh: bool = False,
+             save_checkpoints: bool = False):
     """Selective scan forward from a zero state (ssm_scan_fwd).
 
     u, delta, z: (batch, L, dim); B, C: (batch, L, N), all of one dtype (float32 or bfloat16);
     A: (dim, N) float32; D, delta_bias: (dim,) float32 or None.  exact_zoh: the exact
     zero-order-hold input term (exp(delta A) - 1) / A * B * u instead of delta * B * u.
     Returns (y, last_state) -- last_state (batch, dim, N) float32, or None if not asked for.
+    save_checkpoints (a training forward): also store the states the backward pass needs in
+    the workspace and return (y, last_state, workspace); pass that workspace to scan_bwd as
+    `checkpoints` to skip its recompute pass.
     """
-    args, _keep, y, last_state = _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
-                                            return_last_state, chunk_len, workspace, stream,
-                                            exact_zoh=exact_zoh)
+    args, _keep, y, last_state, ws = _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
+                                                return_last_state, chunk_len, workspace, stream,
+                                                exact_zoh=exact_zoh, save_checkpoints=save_checkpoints)
     _check(lib.ssm_scan_fwd(*args))
-    return y, last_state
+    return (y, last_state, ws) if save_checkpoints else (y, last_state)
 
 
 def scan_fwd_call(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
@@ -212,12 +220,16 @@ def scan_fwd_call(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torc
                   y: Optional[torch.Tensor] = None, last_state: Optional[torch.Tensor] = None,
                   return_last_state: bool = True, chunk_len: int = 0,
                   workspace: Optional[torch.Tensor] = None, stream=None,
-                  exact_zoh: bool = False) -> Callable[[], None]:
+                  exact_zoh: bool = False, save_checkpoints: bool = False) -> Callable[[], None]:
     """The scan_fwd call checked and marshalled once: returns a function that enqueues the
     same call again (same tensors, the stream given or current now), for loops that repeat
-    it.  Outputs go to the y / last_state tensors passed in (or allocated here and kept)."""
-    args, keep, _y, _ls = _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
-                                     return_last_state, chunk_len, workspace, stream, exact_zoh=exact_zoh)
+    it.  Outputs go to the y / last_state tensors passed in (or allocated here and kept);
+    with save_checkpoints, the checkpoints go to `workspace` (which must then be given)."""
+    if save_checkpoints and workspace is None:
+        raise ValueError("save_checkpoints needs the workspace that scan_bwd will read")
+    args, keep, _y, _ls, _ws = _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
+                                          return_last_state, chunk_len, workspace, stream, exact_zoh=exact_zoh,
+                                          save_checkpoints=save_checkpoints)
 
     def call(_args=args, _keep=keep):
         _check(lib.ssm_scan_fwd(*_args))
@@ -230,15 +242,15 @@ def scan_fwd_from(initial_state: torch.Tensor, u: torch.Tensor, delta: torch.Ten
                   softplus: bool = True, *, y: Optional[torch.Tensor] = None,
                   last_state: Optional[torch.Tensor] = None, return_last_state: bool = True,
                   chunk_len: int = 0, workspace: Optional[torch.Tensor] = None, stream=None,
-                  exact_zoh: bool = False):
+                  exact_zoh: bool = False, save_checkpoints: bool = False):
     """The scan continued from initial_state (batch, dim, N) float32 (ssm_scan_fwd_from).
     last_state may be initial_state itself (the state advanced in place).  Otherwise as
     scan_fwd."""
-    args, _keep, y, last_state = _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
-                                            return_last_state, chunk_len, workspace, stream, initial_state,
-                                            exact_zoh=exact_zoh)
+    args, _keep, y, last_state, ws = _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
+                                                return_last_state, chunk_len, workspace, stream, initial_state,
+                                                exact_zoh=exact_zoh, save_checkpoints=save_checkpoints)
     _check(lib.ssm_scan_fwd_from(*args))
-    return y, last_state
+    return (y, last_state, ws) if save_checkpoints else (y, last_state)
 
 
 def scan_bwd(dy: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
@@ -246,12 +258,18 @@ def scan_bwd(dy: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Te
              delta_bias: Optional[torch.Tensor] = None, softplus: bool = True, *,
              initial_state: Optional[torch.Tensor] = None, dlast_state: Optional[torch.Tensor] = None,
              want_initial_state_grad: bool = False, workspace: Optional[torch.Tensor] = None,
-             out: Optional[dict] = None, stream=None) -> dict:
+             out: Optional[dict] = None, stream=None, checkpoints: Optional[torch.Tensor] = None) -> dict:
     """Gradients of the scan (ssm_scan_bwd) given dy (batch, L, dim) and optionally
     dlast_state (batch, dim, N).  The forward inputs are passed as to scan_fwd / scan_fwd_from.
     Returns a dict: du, ddelta, dz (if z), dA, dB, dC (float32), dD (if D), ddelta_bias
     (if delta_bias), dinitial_state (if asked for).  `out`: such a dict from an earlier call
-    with the same shapes, whose tensors are written again instead of new ones."""
+    with the same shapes, whose tensors are written again instead of new ones.
+    `checkpoints`: the workspace a scan_fwd(..., save_checkpoints=True) call on the same
+    inputs returned; its checkpoints are used instead of a recompute pass."""
+    if checkpoints is not None:
+        if workspace is not None:
+            raise ValueError("give either workspace or checkpoints")
+        workspace = checkpoints
     if u.dim() != 3:
         raise ValueError("u must be (batch, L, dim)")
     bsz, L, dim = u.shape
@@ -278,7 +296,8 @@ def scan_bwd(dy: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Te
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     rc = lib.ssm_scan_bwd(_ptr(initial_state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                          _ptr(delta_bias), int(bool(softplus)), _ptr(dy), _ptr(dlast_state), _ptr(g["du"]),
+                          _ptr(delta_bias), int(bool(softplus)) | (SCAN_CHECKPOINTS if checkpoints is not None else 0),
+                          _ptr(dy), _ptr(dlast_state), _ptr(g["du"]),
                           _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dD")),
                           _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")), _ptr(g.get("dinitial_state")),
                           ctypes.byref(dims), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -418,8 +437,8 @@ def _scan_conv_args(x, conv_w, conv_b, delta, A, B, C, D, z, delta_bias, softplu
         _need(conv_b, "conv_b", (dim,), torch.float32, x.device)
     if u_out is not None:
         _need(u_out, "u_out", (bsz, L, dim), x.dtype, x.device)
-    args, keep, y, last_state = _scan_args(x, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
-                                           return_last_state, chunk_len, workspace, stream)
+    args, keep, y, last_state, _ws = _scan_args(x, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
+                                                return_last_state, chunk_len, workspace, stream)
     # ssm_scan_fwd's arguments with x in place of u, the convolution's before delta, u_out after last_state
     args = (args[0], _ptr(conv_w), _ptr(conv_b), int(conv_w.shape[1])) + args[1:11] + (_ptr(u_out),) + args[11:]
     return args, keep + (conv_w, conv_b, u_out), y, last_state

@@ -139,12 +139,19 @@ def test_flags_validated(b):
     P = ctypes.c_void_p
     d = _dims(b)
     ws = b.lib.ssm_scan_workspace_bytes(ctypes.byref(d))
-    for flags in (4, 8, 1 << 20, -1):
-        rc = b.lib.ssm_scan_fwd(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None, None, flags, P(FAKE), None,
-                                ctypes.byref(d), P(FAKE), ws, None)
-        assert rc == -8 and "flag" in b.last_error()
+    def fwd(flags, ws_bytes=ws):
+        return b.lib.ssm_scan_fwd(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None, None, flags, P(FAKE),
+                                  None, ctypes.byref(d), P(FAKE), ws_bytes, None)
+    for flags in (8, 1 << 20, -1):
+        assert fwd(flags) == -8 and "flag" in b.last_error()
+    # checkpoints for the backward: not with the exact ZOH, and the workspace must hold them
+    assert fwd(1 | 2 | 4) == -8 and "ZOH" in b.last_error()
+    assert fwd(1 | 4) == -6
+    ckpt = b.lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(d))
+    assert fwd(1 | 4, ckpt + ws - 16) == -6
     assert _bwd(b, d, softplus=3) == -8 and "ZOH" in b.last_error()
     assert _bwd(b, d, softplus=2) == -8
+    assert _bwd(b, d, softplus=1 | 8) == -8
 
 
 def test_conv_validation(b):
@@ -173,6 +180,7 @@ def test_conv_scan_validation(b):
                                        flags, P(FAKE), None, None, ctypes.byref(dims), P(FAKE), ws, None)
     assert call(width=3) == -2
     assert call(flags=3) == -8
+    assert call(flags=1 | 4) == -8 and "convolution" in b.last_error()
     assert call(w=0) == -1
     assert call(x=FAKE + 1) == -4          # a bf16 x must be 2-byte aligned
 

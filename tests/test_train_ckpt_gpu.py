@@ -1,0 +1,96 @@
+"""The training forward: ssm_scan_fwd(_from) with SSM_SCAN_CHECKPOINTS stores in its workspace
+the states the backward pass needs, and ssm_scan_bwd with the same flag reads them there
+instead of recomputing them in a pass of its own (both through the C ABI).
+
+- The forward's own outputs do not change: y and last_state bitwise equal to the plain call.
+- With a single-pass plan the stored states are the recompute pass's arithmetic exactly, so
+  the per-element gradients (du, ddelta, dz) are bitwise those of the plain backward; the
+  summed ones (atomic adds, last bits free) within 1e-6 of their rms.
+- With a chunked plan the states at chunk starts come from the carry and differ by rounding:
+  the fp32 gradients within 1e-5 of their rms of the plain backward, the bf16 ones within
+  1e-3 (a changed state can flip an output's rounding), and every gradient within the
+  parity tolerance of the fp64 oracle.
+"""
+import numpy as np
+import pytest
+
+from selective_state_space_32_amd import inputs
+from gpu_util import TOL, case_tensors, raw_error, to_dev, to_host_f64, y_error
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from selective_state_space_32_amd import ssmscan  # noqa: E402
+
+IO_OUT = ("du", "ddelta", "dz")
+
+
+def _run(case, seed, chunk_len, with_state):
+    rng = np.random.default_rng(seed)
+    bsz, L, D, N = case.bsz, case.L, case.D, case.N
+    dy_f = rng.standard_normal((bsz, L, D), dtype=np.float32)
+    dy = to_dev(inputs.bf16_bits(dy_f) if case.io == "bf16" else dy_f, torch)
+    t = case_tensors(case, torch)
+    h0 = torch.from_numpy((0.5 * rng.standard_normal((bsz, D, N))).astype(np.float32)).cuda() if with_state else None
+    dlast = torch.from_numpy(rng.standard_normal((bsz, D, N)).astype(np.float32)).cuda() if with_state else None
+    common = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"], softplus=case.softplus, chunk_len=chunk_len)
+    args = (t["u"], t["delta"], t["A"], t["B"], t["C"])
+    if with_state:
+        y0, ls0 = ssmscan.scan_fwd_from(h0, *args, **common)
+        y1, ls1, ws = ssmscan.scan_fwd_from(h0, *args, save_checkpoints=True, **common)
+    else:
+        y0, ls0 = ssmscan.scan_fwd(*args, **common)
+        y1, ls1, ws = ssmscan.scan_fwd(*args, save_checkpoints=True, **common)
+    bwd = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"], softplus=case.softplus, initial_state=h0,
+               dlast_state=dlast, want_initial_state_grad=with_state)
+    g0 = ssmscan.scan_bwd(dy, *args, **bwd)
+    g1 = ssmscan.scan_bwd(dy, *args, checkpoints=ws, **bwd)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(ls0, ls1), "the forward's outputs changed with checkpoints"
+    return ({k: to_host_f64(v) for k, v in g0.items()}, {k: to_host_f64(v) for k, v in g1.items()},
+            to_host_f64(dy))
+
+
+CASES = [
+    # (label, case, chunk_len, initial state)
+    ("bf16 gated, one pass", dict(bsz=2, L=300, D=128, N=16, io="bf16", gate=True), -1, False),
+    ("f32 from a state, one pass", dict(bsz=1, L=257, D=64, N=16, io="f32"), -1, True),
+    ("f32 N4, one pass", dict(bsz=2, L=100, D=72, N=4, io="f32"), -1, False),
+    ("bf16 gated from a state, chunks of 64", dict(bsz=2, L=300, D=128, N=16, io="bf16", gate=True), 64, True),
+]
+
+
+@pytest.mark.parametrize("label,spec,chunk_len,with_state", CASES, ids=[c[0] for c in CASES])
+def test_backward_from_forward_checkpoints(oracle_mod, label, spec, chunk_len, with_state):
+    case = inputs.scan_case(seed=300 + spec["L"], name=label, **spec)
+    g0, g1, dy = _run(case, 310 + spec["D"], chunk_len, with_state)
+    assert sorted(g0) == sorted(g1)
+    one_pass = chunk_len < 0
+    for k in g0:
+        e = raw_error(g1[k], g0[k])
+        print(f"[{label}] {k}: vs the plain backward err/rms {e:.3e}", flush=True)
+        assert np.all(np.isfinite(g1[k])), k
+        if one_pass and k in IO_OUT:
+            assert np.array_equal(g0[k], g1[k]), (label, k)
+        elif one_pass:
+            assert e <= 1e-6, (label, k, e)
+        else:
+            assert e <= (1e-3 if k in IO_OUT and case.io == "bf16" else 1e-5), (label, k, e)
+    if not one_pass:   # the chunked plan's gradients against the fp64 oracle as well
+        zv = case.values("z")
+        rng = np.random.default_rng(310 + spec["D"])
+        rng.standard_normal((case.bsz, case.L, case.D), dtype=np.float32)
+        h0 = (0.5 * rng.standard_normal((case.bsz, case.D, case.N))).astype(np.float32) if with_state else None
+        dlast = rng.standard_normal((case.bsz, case.D, case.N)).astype(np.float32) if with_state else None
+        ref = oracle_mod.scan_bwd(case.values("u"), case.values("delta"), case.A, case.values("B"), case.values("C"),
+                                  dy, D=case.Dskip, z=zv, delta_bias=case.delta_bias, softplus=case.softplus,
+                                  h0=h0, dlast=dlast)
+        names = {"dh0": "dinitial_state"}
+        for k, r in ref.items():
+            kg = names.get(k, k)
+            e = y_error(g1[kg], r, case.io) if kg in IO_OUT else raw_error(g1[kg], r)
+            print(f"[{label}] {kg}: vs the oracle err/rms {e:.3e} (tol {TOL[case.io]})", flush=True)
+            assert e <= TOL[case.io], (label, kg, e)
