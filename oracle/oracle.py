@@ -56,6 +56,8 @@ def _load():
         lib.ssm_oracle_step.restype = ctypes.c_int
         lib.ssm_oracle_conv1d.argtypes = [I64, I64, I64, I64, P, P, P, P, ctypes.c_int, P, P]
         lib.ssm_oracle_conv1d.restype = ctypes.c_int
+        lib.ssm_oracle_conv1d_bwd.argtypes = [I64, I64, I64, I64, P, P, P, P, ctypes.c_int, P, P, P, P, P]
+        lib.ssm_oracle_conv1d_bwd.restype = ctypes.c_int
         lib.ssm_oracle_ssd.argtypes = [I64] * 6 + [P] * 9 + [ctypes.c_int, P, P, ctypes.c_int]
         lib.ssm_oracle_ssd.restype = ctypes.c_int
         _lib = lib
@@ -209,6 +211,34 @@ def conv1d(x, w, bias=None, state=None, silu: bool = True) -> Tuple[np.ndarray, 
     if rc != 0:
         raise ValueError("oracle conv1d rejected width=%d" % width)
     return out, st
+
+
+def conv1d_bwd(x, w, dout, bias=None, state=None, silu: bool = True) -> dict:
+    """fp64 gradients of conv1d given dout = dLoss/dout (state_out carries none).
+
+    Returns a dict with dx (bsz, L, Dch), dw (Dch, width), and dbias (Dch,) and dstate
+    (bsz, width-1, Dch) when bias / state are given (dstate: the gradient with respect to
+    the inputs before token 0, also when they are the implicit zeros -- pass a zero state).
+    """
+    x = _f64(x)
+    bsz, L, Dch = x.shape
+    w = _f64(w)
+    width = w.shape[1]
+    w = _f64(w, (Dch, width))
+    bias = _f64(bias, (Dch,))
+    state = _f64(state, (bsz, width - 1, Dch))
+    dout = _f64(dout, (bsz, L, Dch))
+    out = dict(dx=np.empty((bsz, L, Dch)), dw=np.empty((Dch, width)))
+    if bias is not None:
+        out["dbias"] = np.empty(Dch)
+    if state is not None:
+        out["dstate"] = np.empty((bsz, width - 1, Dch))
+    rc = _load().ssm_oracle_conv1d_bwd(bsz, L, Dch, width, _ptr(x), _ptr(w), _ptr(bias), _ptr(state),
+                                       int(bool(silu)), _ptr(dout), _ptr(out["dx"]), _ptr(out["dw"]),
+                                       _ptr(out.get("dbias")), _ptr(out.get("dstate")))
+    if rc != 0:
+        raise ValueError("oracle conv1d_bwd rejected width=%d" % width)
+    return out
 
 
 def ssd(x, dt, A, B, C, D=None, z=None, dt_bias=None, softplus: bool = True, h0=None,

@@ -347,6 +347,77 @@ int ssm_oracle_conv1d(int64_t bsz, int64_t L, int64_t D, int64_t width, const do
 }
 
 /*
+ * Gradients of ssm_oracle_conv1d given dout = dLoss/dout.  The pages give the forward only
+ * (a short causal convolution over time, then SiLU: azimuth.plus/paper/mamba, block
+ * architecture section); its backward is the chain rule through that definition, written
+ * out per channel with the same history array as the forward:
+ *   pre[t]   = bias + sum_k w[k] hist[t+k]            (hist = the state rows, then x)
+ *   g[t]     = dout[t] * silu'(pre[t])  with silu'(p) = s (1 + p (1 - s)), s = sigmoid(p);
+ *              g[t] = dout[t] without SiLU
+ *   dhist[j] = sum over (t, k) with t + k = j of w[k] g[t]
+ *   dx[t]    = dhist[H + t],   dstate[r] = dhist[r]   (H = width - 1)
+ *   dw[k]    = sum over sequences and tokens of g[t] hist[t+k],   dbias = sum of g[t]
+ *   dx           : [bsz][L][D]            dw : [D][width]
+ *   dbias        : [D] or NULL            dstate : [bsz][width-1][D] or NULL
+ * (the final-window output state_out is taken to carry no gradient).  Returns 0, or -1 for
+ * a width outside 1..16 or a failed allocation.
+ */
+int ssm_oracle_conv1d_bwd(int64_t bsz, int64_t L, int64_t D, int64_t width, const double *x,
+                          const double *w, const double *bias, const double *state, int silu,
+                          const double *dout, double *dx, double *dw, double *dbias, double *dstate) {
+    if (width < 1 || width > 16) return -1;
+    const int64_t H = width - 1;
+    const int64_t n = H + L > 0 ? H + L : 1;
+    double *hist = malloc(sizeof(double) * (size_t)n);
+    double *dhist = malloc(sizeof(double) * (size_t)n);
+    double *g = malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    if (!hist || !dhist || !g) {
+        free(hist);
+        free(dhist);
+        free(g);
+        return -1;
+    }
+    for (int64_t d = 0; d < D; ++d) {
+        for (int64_t k = 0; k < width; ++k) dw[d * width + k] = 0.0;
+        if (dbias) dbias[d] = 0.0;
+    }
+    for (int64_t b = 0; b < bsz; ++b) {
+        for (int64_t d = 0; d < D; ++d) {
+            for (int64_t r = 0; r < H; ++r) hist[r] = state ? state[(b * H + r) * D + d] : 0.0;
+            for (int64_t t = 0; t < L; ++t) hist[H + t] = x[(b * L + t) * D + d];
+            /* dLoss/dpre at every token */
+            for (int64_t t = 0; t < L; ++t) {
+                double pre = bias ? bias[d] : 0.0;
+                for (int64_t k = 0; k < width; ++k) pre = pre + w[d * width + k] * hist[t + k];
+                const double go = dout[(b * L + t) * D + d];
+                if (silu) {
+                    const double s = oracle_sigmoid(pre);
+                    g[t] = go * (s * (1.0 + pre * (1.0 - s)));
+                } else {
+                    g[t] = go;
+                }
+            }
+            /* through the taps: to the inputs, the filter and the bias */
+            for (int64_t j = 0; j < H + L; ++j) dhist[j] = 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                for (int64_t k = 0; k < width; ++k) {
+                    dhist[t + k] = dhist[t + k] + w[d * width + k] * g[t];
+                    dw[d * width + k] = dw[d * width + k] + g[t] * hist[t + k];
+                }
+                if (dbias) dbias[d] = dbias[d] + g[t];
+            }
+            for (int64_t t = 0; t < L; ++t) dx[(b * L + t) * D + d] = dhist[H + t];
+            if (dstate)
+                for (int64_t r = 0; r < H; ++r) dstate[(b * H + r) * D + d] = dhist[r];
+        }
+    }
+    free(hist);
+    free(dhist);
+    free(g);
+    return 0;
+}
+
+/*
  * The state space dual layer (SSD) of Mamba-2 (mugbit.ir, the Mamba-2 / structured state
  * space duality section): the selective scan with a scalar state matrix per head, so that
  * the sequence map is a 1-semiseparable matrix.  Per head h (P channels, group g = h / (H/G)

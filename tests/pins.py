@@ -548,6 +548,91 @@ CONV_CHECKS = [check_conv_numpy_convolve, check_conv_impulse, check_conv_silu, c
                check_conv_state_is_history]
 
 
+# --- gradients of the convolution -----------------------------------------------------------
+# conv_bwd(x, w, dout, bias, state, silu) -> dict dx, dw (+ dbias, dstate when given)
+
+def _check_conv_bwd_fd(conv, conv_bwd, seed, width, silu, L=11):
+    """Every gradient against a central difference of the forward (fp64, eps = 1e-6) along a
+    random direction; the loss is sum(dout * out)."""
+    x, w, bias, rng = _conv_case(seed, L=L, D=3, width=width)
+    state = rng.standard_normal((x.shape[0], width - 1, x.shape[2]))
+    dout = rng.standard_normal(x.shape)
+    g = conv_bwd(x, w, dout, bias, state, silu)
+    c = dict(x=x, w=w, bias=bias, state=state)
+
+    def loss(**kw):
+        a = dict(c)
+        a.update(kw)
+        out, _ = conv(a["x"], a["w"], a["bias"], a["state"], silu)
+        return float(np.sum(dout * out))
+
+    eps = 1e-6
+    for name, gk in (("x", "dx"), ("w", "dw"), ("bias", "dbias"), ("state", "dstate")):
+        if width == 1 and name == "state":
+            continue
+        V = rng.standard_normal(np.shape(c[name]))
+        fd = (loss(**{name: c[name] + eps * V}) - loss(**{name: c[name] - eps * V})) / (2 * eps)
+        an = float(np.sum(g[gk] * V))
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (width, silu, name, fd, an)
+
+
+def check_conv_bwd_fd_silu(conv, conv_bwd):
+    for width in (2, 4):
+        _check_conv_bwd_fd(conv, conv_bwd, 86 + width, width, True)
+
+
+def check_conv_bwd_fd_linear(conv, conv_bwd):
+    for width in (1, 3):
+        _check_conv_bwd_fd(conv, conv_bwd, 90 + width, width, False, L=2)
+
+
+def check_conv_bwd_adjoint(conv, conv_bwd, seed=95):
+    """Without SiLU and bias the convolution is linear in (state, x) and in w separately, so
+    the backward is its transpose exactly: sum(dout * out) = sum(dx * x) + sum(dstate * state)
+    = sum(dw * w); and dbias = the sum of dout over sequences and tokens (pre = out)."""
+    x, w, bias, rng = _conv_case(seed, L=23, D=4, width=4)
+    state = rng.standard_normal((x.shape[0], 3, x.shape[2]))
+    dout = rng.standard_normal(x.shape)
+    out, _ = conv(x, w, None, state, False)
+    g = conv_bwd(x, w, dout, bias, state, False)
+    lhs = float(np.sum(dout * out))
+    assert abs(float(np.sum(g["dx"] * x) + np.sum(g["dstate"] * state)) - lhs) <= 1e-12 * max(1.0, abs(lhs))
+    assert abs(float(np.sum(g["dw"] * w)) - lhs) <= 1e-12 * max(1.0, abs(lhs))
+    assert _rel(g["dbias"], np.sum(dout, axis=(0, 1))) < 1e-14
+
+
+def check_conv_bwd_width1(conv, conv_bwd, seed=96):
+    """Width 1 is a per-element map out = silu(w x + b): dx = dout silu'(p) w,
+    dw = sum dout silu'(p) x, dbias = sum dout silu'(p), with silu'(p) = s + p s (1 - s),
+    s = expit(p) (scipy)."""
+    x, w, bias, rng = _conv_case(seed, L=17, D=4, width=1)
+    dout = rng.standard_normal(x.shape)
+    p = w[:, 0] * x + bias
+    s = expit(p)
+    gp = dout * (s + p * s * (1.0 - s))
+    g = conv_bwd(x, w, dout, bias, None, True)
+    assert _rel(g["dx"], gp * w[:, 0]) < 1e-13
+    assert _rel(g["dw"][:, 0], np.sum(gp * x, axis=(0, 1))) < 1e-13
+    assert _rel(g["dbias"], np.sum(gp, axis=(0, 1))) < 1e-13
+
+
+def check_conv_bwd_causal(conv, conv_bwd, seed=97, t0=9):
+    """Causality seen from the backward: a loss on out[t0] alone reaches only the inputs
+    t0 - width + 1 .. t0 (dx is zero after t0 and before t0 - width + 1), with the filter
+    taps in order: dx[t0 - (width-1) + k] = w[k] g[t0]."""
+    x, w, bias, rng = _conv_case(seed, L=20, D=3, width=4)
+    dout = np.zeros_like(x)
+    dout[:, t0] = rng.standard_normal((x.shape[0], x.shape[2]))
+    g = conv_bwd(x, w, dout, bias, None, False)
+    assert np.all(g["dx"][:, t0 + 1:] == 0.0) and np.all(g["dx"][:, : t0 - 3] == 0.0)
+    for k in range(4):
+        assert _rel(g["dx"][:, t0 - 3 + k], w[:, k] * dout[:, t0]) < 1e-15
+
+
+CONV_BWD_CHECKS = [check_conv_bwd_fd_silu, check_conv_bwd_fd_linear, check_conv_bwd_adjoint,
+                   check_conv_bwd_width1, check_conv_bwd_causal]
+
+
 # --- Mamba-2's state space dual layer (SSD) -------------------------------------------------
 # ssd(x, dt, A, B, C, D, z, dt_bias, softplus, h0) -> (y, last_state)
 # x, z: (b, L, H, P); dt: (b, L, H); A, D, dt_bias: (H,); B, C: (b, L, G, N); h0: (b, H, P, N)

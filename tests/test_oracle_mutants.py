@@ -57,6 +57,15 @@ MUTANTS = {
     "conv_drop_silu": ("out[(b * L + t) * D + d] = silu ? oracle_silu(acc) : acc;",
                        "out[(b * L + t) * D + d] = acc;"),
     "conv_ignore_state": ("hist[r] = state ? state[(b * H + r) * D + d] : 0.0;", "hist[r] = 0.0;"),
+    "conv_bwd_no_silu_derivative": ("g[t] = go * (s * (1.0 + pre * (1.0 - s)));", "g[t] = go * s;"),
+    "conv_bwd_reversed_taps_dx": ("dhist[t + k] = dhist[t + k] + w[d * width + k] * g[t];",
+                                  "dhist[t + k] = dhist[t + k] + w[d * width + (width - 1 - k)] * g[t];"),
+    "conv_bwd_dw_input_one_late": ("dw[d * width + k] = dw[d * width + k] + g[t] * hist[t + k];",
+                                   "dw[d * width + k] = dw[d * width + k] + g[t] * hist[t + k > 0 ? t + k - 1 : 0];"),
+    "conv_bwd_dstate_newest_rows": ("dstate[(b * H + r) * D + d] = dhist[r];",
+                                    "dstate[(b * H + r) * D + d] = dhist[r + 1];"),
+    "conv_bwd_dbias_from_dout": ("if (dbias) dbias[d] = dbias[d] + g[t];",
+                                 "if (dbias) dbias[d] = dbias[d] + dout[(b * L + t) * D + d];"),
     "conv_state_out_oldest_rows": ("state_out[(b * H + r) * D + d] = hist[L + r];",
                                    "state_out[(b * H + r) * D + d] = hist[r];"),
     "ssd_group_index": ("g = h / hpg;", "g = h % G;"),
@@ -87,6 +96,8 @@ def _build_mutant(tmp_path, name, old, new):
     lib.ssm_oracle_scan_bwd.restype = ctypes.c_int
     lib.ssm_oracle_conv1d.argtypes = [I64, I64, I64, I64, P, P, P, P, ctypes.c_int, P, P]
     lib.ssm_oracle_conv1d.restype = ctypes.c_int
+    lib.ssm_oracle_conv1d_bwd.argtypes = [I64, I64, I64, I64, P, P, P, P, ctypes.c_int, P, P, P, P, P]
+    lib.ssm_oracle_conv1d_bwd.restype = ctypes.c_int
     lib.ssm_oracle_ssd.argtypes = [I64] * 6 + [P] * 9 + [ctypes.c_int, P, P, ctypes.c_int]
     lib.ssm_oracle_ssd.restype = ctypes.c_int
 
@@ -146,6 +157,15 @@ def _build_mutant(tmp_path, name, old, new):
         lib.ssm_oracle_conv1d(bsz, L, Dch, width, ptr(x), ptr(w), ptr(bias), ptr(state), int(bool(silu)), ptr(out),
                               ptr(st))
         return out, st
+    def conv_bwd(x, w, dout, bias, state, silu):
+        x, w, dout, bias, state = map(f64, (x, w, dout, bias, state))
+        bsz, L, Dch = x.shape
+        width = w.shape[1]
+        out = dict(dx=np.empty((bsz, L, Dch)), dw=np.empty((Dch, width)), dbias=np.empty(Dch),
+                   dstate=np.empty((bsz, width - 1, Dch)))
+        lib.ssm_oracle_conv1d_bwd(bsz, L, Dch, width, ptr(x), ptr(w), ptr(bias), ptr(state), int(bool(silu)),
+                                  ptr(dout), ptr(out["dx"]), ptr(out["dw"]), ptr(out["dbias"]), ptr(out["dstate"]))
+        return out
     def ssd(x, dt, A, B, C, D, z, dt_bias, softplus, h0):
         x, dt, A, B, C, D, z, dt_bias, h0 = map(f64, (x, dt, A, B, C, D, z, dt_bias, h0))
         bsz, L, H, Pd = x.shape
@@ -155,13 +175,13 @@ def _build_mutant(tmp_path, name, old, new):
         lib.ssm_oracle_ssd(bsz, L, H, Pd, G, N, ptr(h0), ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), ptr(z),
                            ptr(dt_bias), int(bool(softplus)), ptr(y), ptr(last), 1)
         return y, last
-    return scan, scan_from, scan_bwd, scan_zoh, conv, ssd
+    return scan, scan_from, scan_bwd, scan_zoh, conv, conv_bwd, ssd
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(tmp_path, name):
     old, new = MUTANTS[name]
-    scan, scan_from, scan_bwd, scan_zoh, conv, ssd = _build_mutant(tmp_path, name, old, new)
+    scan, scan_from, scan_bwd, scan_zoh, conv, conv_bwd, ssd = _build_mutant(tmp_path, name, old, new)
     caught = []
     with np.errstate(all="ignore"):
         for check in pins.ALL_CHECKS:
@@ -182,6 +202,11 @@ def test_planted_mistake_is_caught(tmp_path, name):
         for check in pins.CONV_CHECKS:
             try:
                 check(conv)
+            except AssertionError:
+                caught.append(check.__name__)
+        for check in pins.CONV_BWD_CHECKS:
+            try:
+                check(conv, conv_bwd)
             except AssertionError:
                 caught.append(check.__name__)
         for check in pins.SSD_CHECKS:

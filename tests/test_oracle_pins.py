@@ -39,6 +39,17 @@ def test_oracle_conv_pin(oracle_mod, check):
     check(_conv(oracle_mod))
 
 
+def _conv_bwd(oracle_mod):
+    def f(x, w, dout, bias, state, silu):
+        return oracle_mod.conv1d_bwd(x, w, dout, bias=bias, state=state, silu=silu)
+    return f
+
+
+@pytest.mark.parametrize("check", pins.CONV_BWD_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_conv_bwd_pin(oracle_mod, check):
+    check(_conv(oracle_mod), _conv_bwd(oracle_mod))
+
+
 def _ssd(oracle_mod):
     def f(x, dt, A, B, C, D, z, dt_bias, softplus, h0):
         return oracle_mod.ssd(x, dt, A, B, C, D=D, z=z, dt_bias=dt_bias, softplus=softplus, h0=h0, threads=2)
