@@ -47,6 +47,8 @@ WORKLOADS = {
     "c3_zoh": "selective scan with the exact zero-order-hold input term B8 L2048 D5120 N16, bf16 I/O, "
               "fp32 state, SiLU(z) gate, D skip, last_state",
     "c3_conv": "causal depthwise conv1d (width 4) + SiLU B8 L2048 D5120, bf16 I/O, conv state out",
+    "c3_conv_bwd": "causal depthwise conv1d (width 4) + SiLU backward (dx, dw, dbias, dstate) B8 L2048 D5120, "
+                   "bf16 I/O",
     "c3_block": "conv1d (width 4) + SiLU fused into the selective scan B8 L2048 D5120 N16, bf16 I/O, fp32 state, "
                 "SiLU(z) gate, D skip, last_state",
 }
@@ -207,6 +209,42 @@ def conv_alg_bytes(bsz, L, D, width, io_bytes):
     return bsz * L * D * io_bytes * 2 + bsz * (width - 1) * D * io_bytes + D * (width + 1) * 4
 
 
+def conv_bwd_alg_bytes(bsz, L, D, width, io_bytes):
+    """x and dout read and dx written per element, the state rows read and their gradient
+    written, w and bias read, dw and dbias written."""
+    return bsz * L * D * io_bytes * 3 + bsz * (width - 1) * D * io_bytes * 2 + D * (width + 1) * 4 * 2
+
+
+def cpu_baseline_conv_bwd(case, dout, alg_bytes_full, target_s=20.0):
+    """The fp64 oracle's convolution backward on a channel sample of the workload (channels
+    are independent; single-threaded)."""
+    from oracle import oracle
+    oracle.build(force=False)
+    g = inputs_bf16_f64(dout)
+
+    def run(sel):
+        oracle.conv1d_bwd(case.values("x")[:, :, sel], case.w[sel], g[:, :, sel], bias=case.bias[sel],
+                          state=case.values("state")[:, :, sel], silu=True)
+    probe = np.arange(32)
+    t = time.perf_counter()
+    run(probe)
+    per_ch = (time.perf_counter() - t) / len(probe)
+    k = int(min(case.D, max(32, target_s / max(per_ch, 1e-9))))
+    sel = np.unique(np.linspace(0, case.D - 1, k).astype(np.int64))
+    t = time.perf_counter()
+    run(sel)
+    dt = time.perf_counter() - t
+    return {"value": round(alg_bytes_full * len(sel) / case.D / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{len(sel)} of {case.D} channels x all {case.bsz} sequences x {case.L} tokens "
+                      f"(fp64 oracle backward)"}
+
+
+def inputs_bf16_f64(bits):
+    from selective_state_space_32_amd import inputs
+    return inputs.bf16_to_f32(bits).astype(np.float64)
+
+
 def cpu_baseline_conv(case, alg_bytes_full, target_s=20.0):
     """The fp64 oracle's convolution on a channel sample of the workload (channels are
     independent; single-threaded)."""
@@ -304,8 +342,8 @@ def main():
 
     dev = "cuda"
     wl = args.workload
-    if wl == "c3_conv":
-        case = inputs.conv_case(8, 2048, 5120, 4, "bf16", state=True, seed=185, name="c3_conv")
+    if wl in ("c3_conv", "c3_conv_bwd"):
+        case = inputs.conv_case(8, 2048, 5120, 4, "bf16", state=True, seed=185, name=wl)
     elif wl == "ssd":
         case = inputs.ssd_case(8, 2048, 80, 64, 1, 64, seed=230, name="ssd")
     else:
@@ -364,6 +402,22 @@ def main():
         def one(i):
             call()
         plan = "one kernel, runs of 16 tokens x 8 channels per thread"
+    elif wl == "c3_conv_bwd":
+        bsz, L, D, width = case.bsz, case.L, case.D, case.width
+        x, st_in = td(case.x), td(case.state)
+        dout_bits = inputs.bf16_bits(np.random.default_rng(186).standard_normal((bsz, L, D), dtype=np.float32))
+        dout = td(dout_bits)
+        alg = conv_bwd_alg_bytes(bsz, L, D, width, io_bytes)
+        chtok = bsz * L * D
+        elements = chtok
+        td_w, td_b = td(case.w), td(case.bias)
+        dx = torch.empty_like(x)
+        call, _grads = ssmscan.conv1d_bwd_call(dout, x, td_w, td_b, st_in, silu=True, dx=dx)
+
+        def one(i):
+            call()
+        plan = ("zero fills of dw and dbias, then one kernel: runs of 64 tokens x 4 channels per thread, "
+                "4 runs per workgroup, dw / dbias reduced in LDS and added atomically")
     elif wl == "c3_bwd":
         t = {k: td(getattr(case, f)) for k, f in (("u", "u"), ("delta", "delta"), ("A", "A"), ("B", "B"),
                                                    ("C", "C"), ("D", "Dskip"), ("z", "z"), ("bias", "delta_bias"))}
@@ -443,7 +497,7 @@ def main():
     for i in range(args.warmup):
         one(i)
     torch.cuda.synchronize()
-    if wl in ("c5", "c3_conv"):
+    if wl in ("c5", "c3_conv", "c3_conv_bwd"):
         # A decode step (~35 us) or the convolution (~65 us) is short next to the host's cost
         # per call: the K timed steps are captured once as a HIP graph (the library allocates
         # and synchronises nothing, so its launches capture as they are) and replayed as one
@@ -456,6 +510,8 @@ def main():
                 if wl == "c5":
                     u, dl, Bk, Ck, z = ins[i % case.steps]
                     ssmscan.step(st, u, dl, A, Bk, Ck, D=Dv, z=z, y=y)
+                elif wl == "c3_conv_bwd":
+                    ssmscan.conv1d_bwd(dout, x, td_w, td_b, st_in, silu=True, dx=dx, stream=cap)
                 else:
                     ssmscan.conv1d(x, td_w, td_b, st_in, silu=True, out=out, state_out=st_out, stream=cap)
         torch.cuda.synchronize()
@@ -489,7 +545,7 @@ def main():
     work_ops = elements * slots + (chtok * SLOTS_PER_CHTOK_CONV if wl == "c3_block" else 0)
     lane_ops = work_ops / kern_s / 1e12
     traffic = counter_traffic(wl)
-    if wl in ("c5", "c3_conv", "ssd"):
+    if wl in ("c5", "c3_conv", "c3_conv_bwd", "ssd"):
         roof = {"bound": "hbm", "achieved": round(kern_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(kern_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
     else:
@@ -506,6 +562,7 @@ def main():
             cpu = (cpu_baseline_step(case, alg) if wl == "c5" else cpu_baseline_bwd(case, alg) if wl == "c3_bwd"
                    else cpu_baseline_bwd(case, alg, with_forward=True) if wl == "c3_train"
                    else cpu_baseline_conv(case, alg) if wl == "c3_conv"
+                   else cpu_baseline_conv_bwd(case, dout_bits, alg) if wl == "c3_conv_bwd"
                    else cpu_baseline_ssd(case, alg) if wl == "ssd"
                    else cpu_baseline_block(case, cc, alg) if wl == "c3_block"
                    else cpu_baseline_scan(case, alg, exact_zoh=wl == "c3_zoh"))

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SSMSCAN_VERSION 8
+#define SSMSCAN_VERSION 9
 
 /* Bits of the `flags` argument of the scan entry points. */
 #define SSM_SCAN_SOFTPLUS 1     /* step size = softplus(delta + delta_bias) */
@@ -213,6 +213,29 @@ SSMSCAN_API int ssm_scan_bwd(const float *initial_state, const void *u, const vo
  * SSM_ERR_FLAGS; a width outside 1..4 returns SSM_ERR_SHAPE. */
 SSMSCAN_API int ssm_conv1d_fwd(const void *x, const float *w, const float *bias, int width, const void *state_in,
                    int flags, void *out, void *state_out, const ssm_dims *dims, void *stream);
+
+/* Gradients of ssm_conv1d_fwd given dout = dLoss/dout: the backward pass of the block's
+ * convolution + SiLU (azimuth.plus/paper/mamba, block architecture section, for the forward;
+ * the backward is its exact derivative).  With g[t] = dout[t] * silu'(pre[t]) (dout[t]
+ * without SSM_CONV_SILU) and H = width - 1:
+ *   dx[b,t,d]      = sum_k w[d,k] * g[b, t + H - k, d]      (g = 0 past the sequence's end)
+ *   dw[d,k]        = sum over b, t of g[b,t,d] * x[b, t - H + k, d]
+ *   dbias[d]       = sum over b, t of g[b,t,d]
+ *   dstate_in[b,r,d] = sum_{k <= r} w[d,k] * g[b, r - k, d]   (the inputs before token 0)
+ *   x, w, bias, width, state_in, flags : exactly those of the forward call
+ *   dout, dx     : [batch][seqlen][dim] (io_dtype)
+ *   dw           : [dim][width] fp32 output (required)
+ *   dbias        : [dim] fp32 output, or NULL (not wanted)
+ *   dstate_in    : [batch][width-1][dim] (io_dtype) output, or NULL (not wanted); given also
+ *                  when state_in is NULL (then the gradient with respect to the zero history)
+ * The forward's state_out is taken to carry no gradient.  dw and dbias are sums over
+ * workgroups, accumulated with atomic adds after the library has zeroed them: their last
+ * bits may differ from run to run.  Outputs must not overlap inputs or each other.
+ * dims->dstate and dims->chunk_len are ignored; seqlen is at most 2^30.  Unknown flag bits
+ * return SSM_ERR_FLAGS; a width outside 1..4 returns SSM_ERR_SHAPE. */
+SSMSCAN_API int ssm_conv1d_bwd(const void *x, const float *w, const float *bias, int width, const void *state_in,
+                   int flags, const void *dout, void *dx, float *dw, float *dbias, void *dstate_in,
+                   const ssm_dims *dims, void *stream);
 
 /* The causal convolution + SiLU fused into the scan: the block's main branch from its
  * projected input x to y in one pass (azimuth.plus/paper/mamba, block architecture section:

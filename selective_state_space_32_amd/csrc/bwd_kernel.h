@@ -41,8 +41,6 @@ template <int N> struct BwdShape {
     static constexpr int K = N / S;           // waves per workgroup
 };
 
-__device__ __forceinline__ float sigmoid_f32(float x) { return hw_rcp(1.0f + hw_exp2(-x * kLog2e)); }
-
 // Inclusive sum over groups of LPV consecutive lanes (LPV = 8, 16 or 32); the last lane of
 // each group ends with the group total.
 template <int LPV>

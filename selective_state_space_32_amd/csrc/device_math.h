@@ -137,6 +137,9 @@ __device__ __forceinline__ float zoh_weight(float y, float e, float delta, float
     return fabsf(y) < (1.0f / 32.0f) * kLog2e ? p : q;
 }
 
+// sigmoid(x) = 1 / (1 + e^-x) (0 for x << 0, where e^-x = inf).
+__device__ __forceinline__ float sigmoid_f32(float x) { return hw_rcp(1.0f + hw_exp2(-x * kLog2e)); }
+
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z).  For z << 0, e^-z = inf and the result is -0.
 __device__ __forceinline__ float silu_f32(float z) {
     float e = hw_exp2(-z * kLog2e);

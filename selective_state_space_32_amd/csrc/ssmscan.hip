@@ -409,6 +409,55 @@ int launch_conv(int width, bool silu, const void *x, const float *w, const float
     return ok();
 }
 
+template <typename IO, int W, bool VEC, bool SILU>
+void launch_conv_bwd_w(const IO *x, const float *w, const float *bias, const IO *st_in, const IO *dout, IO *dx,
+                       float *dw, float *dbias, IO *dst, const ssm_dims *dm, hipStream_t st) {
+    constexpr int V = VEC ? ssm::kConvBwdVec : 1;
+    const int64_t bsz = dm->batch, L = dm->seqlen, D = dm->dim;
+    const int64_t R = ssm::kConvBwdRun;
+    const int64_t runs = (L + R - 1) / R;
+    const int64_t groups = D / V;
+    const int64_t pairs = bsz * runs;
+    const int64_t quads = (pairs + ssm::kConvBwdWaves - 1) / ssm::kConvBwdWaves;
+    const dim3 grid((unsigned)((groups + 63) / 64), (unsigned)std::min<int64_t>(quads, 65535));
+    const dim3 block(64 * ssm::kConvBwdWaves);
+    if (groups % 64 == 0)
+        hipLaunchKernelGGL((ssm::conv1d_bwd_kernel<IO, W, V, VEC, SILU, true>), grid, block, 0, st, x, w, bias, st_in,
+                           dout, dx, dw, dbias, dst, (int)L, D, groups, (int)runs, pairs);
+    else
+        hipLaunchKernelGGL((ssm::conv1d_bwd_kernel<IO, W, V, VEC, SILU, false>), grid, block, 0, st, x, w, bias,
+                           st_in, dout, dx, dw, dbias, dst, (int)L, D, groups, (int)runs, pairs);
+}
+
+template <typename IO, bool VEC, bool SILU>
+void launch_conv_bwd_v(int width, const IO *x, const float *w, const float *bias, const IO *st_in, const IO *dout,
+                       IO *dx, float *dw, float *dbias, IO *dst, const ssm_dims *dm, hipStream_t st) {
+    switch (width) {
+        case 1: launch_conv_bwd_w<IO, 1, VEC, SILU>(x, w, bias, st_in, dout, dx, dw, dbias, dst, dm, st); break;
+        case 2: launch_conv_bwd_w<IO, 2, VEC, SILU>(x, w, bias, st_in, dout, dx, dw, dbias, dst, dm, st); break;
+        case 3: launch_conv_bwd_w<IO, 3, VEC, SILU>(x, w, bias, st_in, dout, dx, dw, dbias, dst, dm, st); break;
+        default: launch_conv_bwd_w<IO, 4, VEC, SILU>(x, w, bias, st_in, dout, dx, dw, dbias, dst, dm, st); break;
+    }
+}
+
+template <typename IO>
+void launch_conv_bwd(int width, bool silu, const void *x, const float *w, const float *bias, const void *st_in,
+                     const void *dout, void *dx, float *dw, float *dbias, void *dst, const ssm_dims *dm,
+                     hipStream_t st) {
+    const IO *x_ = static_cast<const IO *>(x);
+    const IO *si = static_cast<const IO *>(st_in);
+    const IO *go = static_cast<const IO *>(dout);
+    IO *gx = static_cast<IO *>(dx);
+    IO *gs = static_cast<IO *>(dst);
+    const size_t va = ssm::kConvBwdVec * sizeof(IO);
+    const bool vec = dm->dim % ssm::kConvBwdVec == 0 && aligned(x, va) && aligned(dout, va) && aligned(dx, va) &&
+                     (!st_in || aligned(st_in, va)) && (!dst || aligned(dst, va));
+    if (vec && silu) launch_conv_bwd_v<IO, true, true>(width, x_, w, bias, si, go, gx, dw, dbias, gs, dm, st);
+    else if (vec) launch_conv_bwd_v<IO, true, false>(width, x_, w, bias, si, go, gx, dw, dbias, gs, dm, st);
+    else if (silu) launch_conv_bwd_v<IO, false, true>(width, x_, w, bias, si, go, gx, dw, dbias, gs, dm, st);
+    else launch_conv_bwd_v<IO, false, false>(width, x_, w, bias, si, go, gx, dw, dbias, gs, dm, st);
+}
+
 }  // namespace
 
 static int scan_impl(const float *h0, const void *u, const void *delta, const float *A, const void *B,
@@ -656,6 +705,48 @@ int ssm_conv1d_fwd(const void *x, const float *w, const float *bias, int width, 
     const bool silu = (flags & SSM_CONV_SILU) != 0;
     if (es == 2) return launch_conv<uint16_t>(width, silu, x, w, bias, state_in, out, state_out, &d, st);
     return launch_conv<float>(width, silu, x, w, bias, state_in, out, state_out, &d, st);
+}
+
+int ssm_conv1d_bwd(const void *x, const float *w, const float *bias, int width, const void *state_in, int flags,
+                   const void *dout, void *dx, float *dw, float *dbias, void *dstate_in, const ssm_dims *dims,
+                   void *stream) {
+    if (!dims) return fail(SSM_ERR_NULL, "dims is NULL");
+    ssm_dims d = *dims;   // dstate and chunk_len do not apply
+    d.dstate = 1;
+    d.chunk_len = 0;
+    int rc = check_dims(&d, true);
+    if (rc != SSM_OK) return rc;
+    if (width < 1 || width > 4) return fail(SSM_ERR_SHAPE, "conv width %d not supported (1 to 4)", width);
+    if (flags & ~SSM_CONV_SILU) return fail(SSM_ERR_FLAGS, "unknown flag bits 0x%x", flags);
+    const int64_t bsz = d.batch, L = d.seqlen, Dm = d.dim, H = width - 1;
+    if (L > (int64_t(1) << 30)) return fail(SSM_ERR_SHAPE, "seqlen %lld exceeds 2^30", (long long)L);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const size_t es = d.io_dtype == SSM_IO_BF16 ? 2 : 4;
+    if (!aligned(x, es) || !aligned(dout, es) || !aligned(dx, es) || !aligned(state_in, es) ||
+        !aligned(dstate_in, es) || !aligned(w, 4) || !aligned(bias, 4) || !aligned(dw, 4) || !aligned(dbias, 4))
+        return fail(SSM_ERR_ALIGN, "a tensor pointer is not aligned to its element size");
+    if (Dm == 0) return ok();
+    if (!w || !dw) return fail(SSM_ERR_NULL, "w or dw is NULL");
+    if (bsz > 0 && L > 0 && (!x || !dout || !dx)) return fail(SSM_ERR_NULL, "x, dout or dx is NULL");
+    // the sums start from zero (and stay zero without tokens)
+    fill_zero(dw, Dm * width, st);
+    fill_zero(dbias, Dm, st);
+    if (bsz > 0 && L == 0 && dstate_in && H > 0) {   // no output depends on the state
+        if (es == 2) fill_zero(static_cast<uint16_t *>(dstate_in), bsz * H * Dm, st);
+        else fill_zero(static_cast<float *>(dstate_in), bsz * H * Dm, st);
+    }
+    if (bsz > 0 && L > 0) {
+        const bool silu = (flags & SSM_CONV_SILU) != 0;
+        if (es == 2)
+            launch_conv_bwd<uint16_t>(width, silu, x, w, bias, state_in, dout, dx, dw, dbias, H > 0 ? dstate_in : nullptr,
+                                      &d, st);
+        else
+            launch_conv_bwd<float>(width, silu, x, w, bias, state_in, dout, dx, dw, dbias, H > 0 ? dstate_in : nullptr,
+                                   &d, st);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
 }
 
 int ssm_ssd_fwd(const void *x, const void *dt, const float *A, const void *B, const void *C, const float *D,

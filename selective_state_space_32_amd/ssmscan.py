@@ -65,6 +65,8 @@ def _load() -> ctypes.CDLL:
     lib.ssm_step.restype = ctypes.c_int
     lib.ssm_conv1d_fwd.argtypes = [P, P, P, ctypes.c_int, P, ctypes.c_int, P, P, D, P]
     lib.ssm_conv1d_fwd.restype = ctypes.c_int
+    lib.ssm_conv1d_bwd.argtypes = [P, P, P, ctypes.c_int, P, ctypes.c_int, P, P, P, P, P, D, P]
+    lib.ssm_conv1d_bwd.restype = ctypes.c_int
     lib.ssm_scan_fwd_conv.argtypes = [P, P, P, ctypes.c_int, P, P, P, P, P, P, P, ctypes.c_int, P, P, P, D, P,
                                       ctypes.c_size_t, P]
     lib.ssm_scan_fwd_conv.restype = ctypes.c_int
@@ -425,6 +427,67 @@ def conv1d_call(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] =
     def call(_args=args, _keep=keep):
         _check(lib.ssm_conv1d_fwd(*_args))
     return call
+
+
+def _conv_bwd_args(dout, x, w, bias, state, silu, want_state_grad, dx, stream):
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, L, dim)")
+    bsz, L, dim = x.shape
+    if w.dim() != 2 or w.shape[0] != dim:
+        raise ValueError("w must be (dim, width)")
+    width = int(w.shape[1])
+    dev, io = x.device, x.dtype
+    _io_code(io)
+    _need(w, "w", (dim, width), torch.float32, dev)
+    _need(dout, "dout", (bsz, L, dim), io, dev)
+    if bias is not None:
+        _need(bias, "bias", (dim,), torch.float32, dev)
+    if state is not None:
+        _need(state, "state", (bsz, width - 1, dim), io, dev)
+    if dx is None:
+        dx = torch.empty((bsz, L, dim), dtype=io, device=dev)
+    else:
+        _need(dx, "dx", (bsz, L, dim), io, dev)
+    g = dict(dx=dx, dw=torch.empty((dim, width), dtype=torch.float32, device=dev))
+    if bias is not None:
+        g["dbias"] = torch.empty((dim,), dtype=torch.float32, device=dev)
+    if want_state_grad:
+        g["dstate"] = torch.empty((bsz, width - 1, dim), dtype=io, device=dev)
+    dims = make_dims(bsz, L, dim, 1, io)
+    args = (_ptr(x), _ptr(w), _ptr(bias), width, _ptr(state), CONV_SILU if silu else 0, _ptr(dout), _ptr(dx),
+            _ptr(g["dw"]), _ptr(g.get("dbias")), _ptr(g.get("dstate")), ctypes.byref(dims), _stream_handle(stream))
+    keep = (x, w, bias, state, dout, g, dims)
+    return args, keep, g
+
+
+def conv1d_bwd(dout: torch.Tensor, x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None,
+               state: Optional[torch.Tensor] = None, silu: bool = True, *, want_state_grad: Optional[bool] = None,
+               dx: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Gradients of conv1d (ssm_conv1d_bwd) given dout = dLoss/dout.
+
+    The inputs are those of the forward call.  Returns a dict with dx (batch, L, dim) of x's
+    dtype, dw (dim, width) float32, dbias (dim,) float32 when bias is given, and dstate
+    (batch, width-1, dim) of x's dtype when want_state_grad (default: when state is given)."""
+    if want_state_grad is None:
+        want_state_grad = state is not None
+    args, _keep, g = _conv_bwd_args(dout, x, w, bias, state, silu, want_state_grad, dx, stream)
+    _check(lib.ssm_conv1d_bwd(*args))
+    return g
+
+
+def conv1d_bwd_call(dout: torch.Tensor, x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                    state: Optional[torch.Tensor] = None, silu: bool = True, *,
+                    want_state_grad: Optional[bool] = None, dx: Optional[torch.Tensor] = None,
+                    stream=None) -> Tuple[Callable[[], None], dict]:
+    """The conv1d_bwd call checked and marshalled once (see scan_fwd_call); returns the call
+    and the dict of gradient tensors it writes."""
+    if want_state_grad is None:
+        want_state_grad = state is not None
+    args, keep, g = _conv_bwd_args(dout, x, w, bias, state, silu, want_state_grad, dx, stream)
+
+    def call(_args=args, _keep=keep):
+        _check(lib.ssm_conv1d_bwd(*_args))
+    return call, g
 
 
 def _scan_conv_args(x, conv_w, conv_b, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,

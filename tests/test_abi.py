@@ -28,7 +28,7 @@ def b():
 def test_header_declares_the_entry_points():
     syms = set(declared_symbols())
     assert {"ssm_scan_fwd", "ssm_scan_fwd_from", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes", "ssm_step",
-            "ssm_conv1d_fwd", "ssm_scan_fwd_conv", "ssm_ssd_fwd",
+            "ssm_conv1d_fwd", "ssm_conv1d_bwd", "ssm_scan_fwd_conv", "ssm_ssd_fwd",
             "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_last_error", "ssm_version"} <= syms
 
 
@@ -168,6 +168,23 @@ def test_conv_validation(b):
     assert conv(w=0) == -1
     assert conv(out=0) == -1
     assert conv(dims=_dims(b, io_dtype=5)) == -3
+
+
+def test_conv_bwd_validation(b):
+    P = ctypes.c_void_p
+    d = _dims(b, dstate=3)
+
+    def call(width=4, flags=1, x=FAKE, dout=FAKE, dx=FAKE, w=FAKE, dw=FAKE, dims=d):
+        return b.lib.ssm_conv1d_bwd(P(x), P(w), None, width, None, flags, P(dout), P(dx), P(dw), None, None,
+                                    ctypes.byref(dims) if dims is not None else None, None)
+    assert call(dims=None) == -1
+    assert call(width=0) == -2 and call(width=5) == -2
+    assert call(flags=2) == -8
+    assert call(x=FAKE + 1) == -4 and call(dx=FAKE + 1) == -4 and call(dw=FAKE + 2) == -4
+    assert call(w=0) == -1 and call(dw=0) == -1
+    assert call(x=0) == -1 and call(dout=0) == -1 and call(dx=0) == -1
+    assert call(dims=_dims(b, io_dtype=5)) == -3
+    assert call(dims=_dims(b, seqlen=-1)) == -2
 
 
 def test_conv_scan_validation(b):
