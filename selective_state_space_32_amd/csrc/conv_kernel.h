@@ -172,6 +172,14 @@ constexpr int kConvBwdRun = 64;    // tokens per run (a multiple of 2 * kConvBat
 constexpr int kConvBwdWaves = 4;   // runs per workgroup, one per wave
 constexpr int kConvBwdVec = 2;     // channels per thread (4-byte bf16 / 8-byte fp32 accesses)
 
+// Zeros two arrays in one launch (the sums the backward adds into).
+__global__ void __launch_bounds__(256) fill_zero2_kernel(float *__restrict__ p, int64_t n, float *__restrict__ q,
+                                                         int64_t m) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+    else if (q && i < n + m) q[i - n] = 0.0f;
+}
+
 template <typename IO, int W, int V, bool VEC, bool SILU, bool EXACT>
 __global__ void __launch_bounds__(64 * kConvBwdWaves)
 conv1d_bwd_kernel(const IO *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
@@ -204,29 +212,41 @@ conv1d_bwd_kernel(const IO *__restrict__ x, const float *__restrict__ w, const f
         bv[i] = bias ? bias[d0 + i] : 0.0f;
         sb[i] = 0.0f;
     }
+    // A row is addressed as a workgroup-uniform base plus the lane's 32-bit byte offset, which
+    // the load and store instructions take as they are (no per-lane 64-bit address arithmetic).
+    const uint32_t lofs = (uint32_t)(d0 * (int64_t)sizeof(IO));
+    static_assert(!VEC || WD <= 2, "a thread's row access is one 4- or 8-byte word");
     auto load_raw = [&](const IO *p, int64_t row, uint32_t (&r)[WD]) {
-        if constexpr (VEC && WD == 1) {   // plain (cached) loads: halo rows are read again
-            r[0] = *reinterpret_cast<const uint32_t *>(p + row * D + d0);
-        } else if constexpr (VEC && WD == 2) {
-            const u32x2_t v = *reinterpret_cast<const u32x2_t *>(p + row * D + d0);
+        // plain (cached) loads: halo rows are read again
+        const char *a = reinterpret_cast<const char *>(p + row * D) + lofs;
+        if constexpr (VEC && WD == 2) {
+            const u32x2_t v = *reinterpret_cast<const u32x2_t *>(a);
             r[0] = v.x;
             r[1] = v.y;
-        } else if constexpr (VEC && WD == 4) {
-            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(p + row * D + d0);
-            r[0] = v.x; r[1] = v.y; r[2] = v.z; r[3] = v.w;
-        } else if constexpr (VEC) VIO::load(p, row * D + d0, r);
-        else if constexpr (sizeof(IO) == 2) r[0] = p[row * D + d0];
-        else r[0] = __float_as_uint(p[row * D + d0]);
+        } else if constexpr (VEC || sizeof(IO) == 4) {
+            r[0] = *reinterpret_cast<const uint32_t *>(a);
+        } else {
+            r[0] = *reinterpret_cast<const uint16_t *>(a);
+        }
     };
     auto widen = [&](const uint32_t (&r)[WD], int i) -> float {
         if constexpr (VEC) return VIO::get(r, i);
         else if constexpr (sizeof(IO) == 2) return bf16_to_f32((uint16_t)r[0]);
         else return __uint_as_float(r[0]);
     };
-    auto store_row = [&](IO *p, int64_t row, const float (&v)[V]) {
+    auto store_row = [&](IO *p, int64_t row, const float (&v)[V]) {   // streaming (non-temporal) stores
         if (!act) return;
-        if constexpr (VEC) VIO::store(p, row * D + d0, v);   // streaming (non-temporal) stores
-        else io<IO>::st(p, row * D + d0, v[0]);
+        char *a = reinterpret_cast<char *>(p + row * D) + lofs;
+        if constexpr (sizeof(IO) == 2 && V == 2) {
+            __builtin_nontemporal_store(f32x2_to_bf16x2(v[0], v[1]), reinterpret_cast<uint32_t *>(a));
+        } else if constexpr (sizeof(IO) == 4 && V == 2) {
+            const u32x2_t w2 = {__float_as_uint(v[0]), __float_as_uint(v[1])};
+            __builtin_nontemporal_store(w2, reinterpret_cast<u32x2_t *>(a));
+        } else if constexpr (sizeof(IO) == 2) {
+            __builtin_nontemporal_store(f32_to_bf16(v[0]), reinterpret_cast<uint16_t *>(a));
+        } else {
+            __builtin_nontemporal_store(__float_as_uint(v[0]), reinterpret_cast<uint32_t *>(a));
+        }
     };
 
     for (int64_t q = (int64_t)blockIdx.y * kConvBwdWaves + slot; q < pairs;

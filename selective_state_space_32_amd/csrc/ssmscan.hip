@@ -729,8 +729,11 @@ int ssm_conv1d_bwd(const void *x, const float *w, const float *bias, int width, 
     if (!w || !dw) return fail(SSM_ERR_NULL, "w or dw is NULL");
     if (bsz > 0 && L > 0 && (!x || !dout || !dx)) return fail(SSM_ERR_NULL, "x, dout or dx is NULL");
     // the sums start from zero (and stay zero without tokens)
-    fill_zero(dw, Dm * width, st);
-    fill_zero(dbias, Dm, st);
+    {
+        const int64_t n = Dm * width + (dbias ? Dm : 0);
+        hipLaunchKernelGGL(ssm::fill_zero2_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dw,
+                           Dm * width, dbias, dbias ? Dm : int64_t(0));
+    }
     if (bsz > 0 && L == 0 && dstate_in && H > 0) {   // no output depends on the state
         if (es == 2) fill_zero(static_cast<uint16_t *>(dstate_in), bsz * H * Dm, st);
         else fill_zero(static_cast<float *>(dstate_in), bsz * H * Dm, st);
