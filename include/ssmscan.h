@@ -247,7 +247,11 @@ SSMSCAN_API int ssm_conv1d_bwd(const void *x, const float *w, const float *bias,
  *   x              : [batch][seqlen][dim] (io_dtype), the block's projected input
  *   conv_w, conv_b : [dim][4], [dim] fp32 (conv_b may be NULL);  conv_width must be 4
  *   u_out          : [batch][seqlen][dim] (io_dtype) receives u (for the backward pass), or NULL
- *   flags          : SSM_SCAN_SOFTPLUS only (the exact ZOH is not available here: SSM_ERR_FLAGS)
+ *   flags          : SSM_SCAN_SOFTPLUS and SSM_SCAN_CHECKPOINTS (the exact ZOH is not available
+ *                    here: SSM_ERR_FLAGS).  With SSM_SCAN_CHECKPOINTS the backward's
+ *                    checkpoints are stored as by ssm_scan_fwd, for ssm_scan_bwd called with
+ *                    u = u_out; u is then scanned as rounded to io_dtype (the values u_out
+ *                    holds), as the two-call path ssm_conv1d_fwd + ssm_scan_fwd does.
  * Every other argument, the workspace and the errors are those of ssm_scan_fwd. */
 SSMSCAN_API int ssm_scan_fwd_conv(const void *x, const float *conv_w, const float *conv_b, int conv_width,
                       const void *delta, const float *A, const void *B, const void *C, const float *D,

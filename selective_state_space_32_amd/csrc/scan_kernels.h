@@ -285,7 +285,11 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                     float acc = cbl;
 #pragma unroll
                     for (int k = 0; k < CW; ++k) acc = fmaf(cwl[k], xw[k], acc);
-                    const float uu = silu_f32(acc);
+                    float uu = silu_f32(acc);
+                    // the training forward scans u as the backward will read it back from
+                    // u_out (rounded to the I/O type), so that its checkpoints are that
+                    // input's states
+                    if constexpr (CK && sizeof(IO) == 2) uu = bf16_to_f32(f32_to_bf16(uu));
                     s_dk[tb + i][sl] = f32x2_t{uu, uu};
 #pragma unroll
                     for (int k = 0; k + 1 < CW; ++k) xw[k] = xw[k + 1];

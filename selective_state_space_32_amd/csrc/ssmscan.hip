@@ -186,8 +186,15 @@ int launch_scan(const void *u, const void *delta, const float *A, const void *B,
     const bool vec = dm->dim % 8 == 0 && aligned(u, 16) && aligned(delta, 16) && aligned(y, 16) &&
                      (!z || aligned(z, 16));
     if (cv) {
-        // the fused convolution (width 4; no exact ZOH, checked by the caller)
-        if (vec)
+        // the fused convolution (width 4; no exact ZOH, checked by the caller), with or without
+        // the backward pass's checkpoints
+        if (vec && ckpt)
+            launch_scan_kernels<N, IO, true, false, 4, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_,
+                                                             last_state, dm, p, ws, st, *cv, ckpt);
+        else if (ckpt)
+            launch_scan_kernels<N, IO, false, false, 4, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_,
+                                                              last_state, dm, p, ws, st, *cv, ckpt);
+        else if (vec)
             launch_scan_kernels<N, IO, true, false, 4>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state,
                                                        dm, p, ws, st, *cv);
         else
@@ -471,7 +478,6 @@ static int scan_impl(const float *h0, const void *u, const void *delta, const fl
     const bool want_ckpt = (flags & SSM_SCAN_CHECKPOINTS) != 0;
     if (want_ckpt && (flags & SSM_SCAN_EXACT_ZOH))
         return fail(SSM_ERR_FLAGS, "checkpoints for the backward pass are not available with the exact ZOH");
-    if (want_ckpt && cv) return fail(SSM_ERR_FLAGS, "checkpoints are not available with the fused convolution");
     const int64_t bsz = dims->batch, L = dims->seqlen, Dm = dims->dim, N = dims->dstate;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (bsz == 0 || Dm == 0) return ok();

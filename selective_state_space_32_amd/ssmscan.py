@@ -491,7 +491,7 @@ def conv1d_bwd_call(dout: torch.Tensor, x: torch.Tensor, w: torch.Tensor, bias: 
 
 
 def _scan_conv_args(x, conv_w, conv_b, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
-                    return_last_state, u_out, chunk_len, workspace, stream):
+                    return_last_state, u_out, chunk_len, workspace, stream, save_checkpoints=False):
     if conv_w.dim() != 2 or conv_w.shape[0] != x.shape[-1]:
         raise ValueError("conv_w must be (dim, width)")
     bsz, L, dim = x.shape
@@ -500,11 +500,12 @@ def _scan_conv_args(x, conv_w, conv_b, delta, A, B, C, D, z, delta_bias, softplu
         _need(conv_b, "conv_b", (dim,), torch.float32, x.device)
     if u_out is not None:
         _need(u_out, "u_out", (bsz, L, dim), x.dtype, x.device)
-    args, keep, y, last_state, _ws = _scan_args(x, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
-                                                return_last_state, chunk_len, workspace, stream)
+    args, keep, y, last_state, ws = _scan_args(x, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
+                                               return_last_state, chunk_len, workspace, stream,
+                                               save_checkpoints=save_checkpoints)
     # ssm_scan_fwd's arguments with x in place of u, the convolution's before delta, u_out after last_state
     args = (args[0], _ptr(conv_w), _ptr(conv_b), int(conv_w.shape[1])) + args[1:11] + (_ptr(u_out),) + args[11:]
-    return args, keep + (conv_w, conv_b, u_out), y, last_state
+    return args, keep + (conv_w, conv_b, u_out), y, last_state, ws
 
 
 def scan_fwd_conv(x: torch.Tensor, conv_w: torch.Tensor, conv_b: Optional[torch.Tensor], delta: torch.Tensor,
@@ -513,22 +514,25 @@ def scan_fwd_conv(x: torch.Tensor, conv_w: torch.Tensor, conv_b: Optional[torch.
                   softplus: bool = True, *, y: Optional[torch.Tensor] = None,
                   last_state: Optional[torch.Tensor] = None, return_last_state: bool = True,
                   u_out: Optional[torch.Tensor] = None, chunk_len: int = 0,
-                  workspace: Optional[torch.Tensor] = None, stream=None):
+                  workspace: Optional[torch.Tensor] = None, stream=None, save_checkpoints: bool = False):
     """Causal convolution (width 4) + SiLU fused into the scan (ssm_scan_fwd_conv): x is the
     block's projected input, conv_w (dim, 4), conv_b (dim,) float32; u_out (optional) receives
-    the convolution's output.  Otherwise as scan_fwd.  Returns (y, last_state)."""
-    args, _keep, y, last_state = _scan_conv_args(x, conv_w, conv_b, delta, A, B, C, D, z, delta_bias, softplus, y,
-                                                 last_state, return_last_state, u_out, chunk_len, workspace, stream)
+    the convolution's output.  Otherwise as scan_fwd (save_checkpoints: also the backward's
+    checkpoints, for scan_bwd with u = u_out).  Returns (y, last_state), or
+    (y, last_state, workspace) with save_checkpoints."""
+    args, _keep, y, last_state, ws = _scan_conv_args(x, conv_w, conv_b, delta, A, B, C, D, z, delta_bias, softplus,
+                                                     y, last_state, return_last_state, u_out, chunk_len, workspace,
+                                                     stream, save_checkpoints=save_checkpoints)
     _check(lib.ssm_scan_fwd_conv(*args))
-    return y, last_state
+    return (y, last_state, ws) if save_checkpoints else (y, last_state)
 
 
 def scan_fwd_conv_call(x, conv_w, conv_b, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, *,
                        y=None, last_state=None, return_last_state=True, u_out=None, chunk_len=0, workspace=None,
                        stream=None) -> Callable[[], None]:
     """The scan_fwd_conv call checked and marshalled once (see scan_fwd_call)."""
-    args, keep, _y, _ls = _scan_conv_args(x, conv_w, conv_b, delta, A, B, C, D, z, delta_bias, softplus, y,
-                                          last_state, return_last_state, u_out, chunk_len, workspace, stream)
+    args, keep, _y, _ls, _ws = _scan_conv_args(x, conv_w, conv_b, delta, A, B, C, D, z, delta_bias, softplus, y,
+                                               last_state, return_last_state, u_out, chunk_len, workspace, stream)
 
     def call(_args=args, _keep=keep):
         _check(lib.ssm_scan_fwd_conv(*_args))

@@ -94,3 +94,64 @@ def test_backward_from_forward_checkpoints(oracle_mod, label, spec, chunk_len, w
             e = y_error(g1[kg], r, case.io) if kg in IO_OUT else raw_error(g1[kg], r)
             print(f"[{label}] {kg}: vs the oracle err/rms {e:.3e} (tol {TOL[case.io]})", flush=True)
             assert e <= TOL[case.io], (label, kg, e)
+
+
+def test_fused_conv_forward_checkpoints(oracle_mod):
+    """The fused convolution's training forward: ssm_scan_fwd_conv with SSM_SCAN_CHECKPOINTS
+    scans u rounded to bf16 (what u_out holds), so its u_out equals the plain call's bitwise,
+    its y and last_state match the oracle's scan of that stored u, and
+    the backward from its checkpoints with u = u_out gives the plain backward's per-element
+    gradients bitwise (one pass: the same states) and its sums within 1e-6; through the
+    convolution's backward, the block's input side matches the oracle."""
+    case = inputs.scan_case(bsz=2, L=200, D=128, N=16, io="bf16", gate=True, seed=331, name="fused")
+    cc = inputs.conv_case(2, 200, 128, 4, "bf16", state=False, seed=332)
+    t = case_tensors(case, torch)
+    x = to_dev(cc.x, torch)
+    w = torch.from_numpy(cc.w).cuda()
+    cb = torch.from_numpy(cc.bias).cuda()
+    args = (t["delta"], t["A"], t["B"], t["C"])
+    kw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"], softplus=case.softplus)
+    u0, u1 = torch.empty_like(x), torch.empty_like(x)
+    # one pass (chunk_len -1), as the backward's own checkpoint pass walks
+    y0, ls0 = ssmscan.scan_fwd_conv(x, w, cb, *args, u_out=u0, chunk_len=-1, **kw)
+    y1, ls1, ws = ssmscan.scan_fwd_conv(x, w, cb, *args, u_out=u1, save_checkpoints=True, chunk_len=-1, **kw)
+    rng = np.random.default_rng(333)
+    dy_f = rng.standard_normal((case.bsz, case.L, case.D), dtype=np.float32)
+    dy = to_dev(inputs.bf16_bits(dy_f), torch)
+    g0 = ssmscan.scan_bwd(dy, u0, *args, **kw)
+    g1 = ssmscan.scan_bwd(dy, u1, *args, checkpoints=ws, **kw)
+    gc = ssmscan.conv1d_bwd(g1["du"], x, w, cb)
+    torch.cuda.synchronize()
+    assert torch.equal(u0, u1)
+    # y of the training forward is the scan of the bf16 u it stored (not of the fp32 u, which
+    # differs by that rounding: up to 8 % of rms(y) here, where |y| reaches 35 times its rms)
+    yref, lref = oracle_mod.scan(to_host_f64(u1), case.values("delta"), case.A, case.values("B"), case.values("C"),
+                                 D=case.Dskip, z=case.values("z"), delta_bias=case.delta_bias, softplus=case.softplus)
+    e = y_error(to_host_f64(y1), yref, "bf16")
+    print(f"[fused ckpt] y vs the oracle on the stored u err/rms {e:.3e}", flush=True)
+    assert e <= TOL["bf16"] and raw_error(to_host_f64(ls1), lref) <= TOL["bf16"]
+    for k in g0:
+        a, r = to_host_f64(g1[k]), to_host_f64(g0[k])
+        e = raw_error(a, r)
+        print(f"[fused ckpt] {k}: vs the plain backward err/rms {e:.3e}", flush=True)
+        assert np.all(np.isfinite(a)), k
+        if k in IO_OUT:
+            assert np.array_equal(a, r), k
+        else:
+            assert e <= 1e-6, (k, e)
+    # the block's input side against the oracle: the scan's backward at u = u_out, then the
+    # convolution's backward of the du it gives
+    uh = to_host_f64(u1)
+    ref = oracle_mod.scan_bwd(uh, case.values("delta"), case.A, case.values("B"), case.values("C"),
+                              to_host_f64(dy), D=case.Dskip, z=case.values("z"), delta_bias=case.delta_bias,
+                              softplus=case.softplus)
+    e = y_error(to_host_f64(g1["du"]), ref["du"], "bf16")
+    print(f"[fused ckpt] du vs the oracle err/rms {e:.3e}", flush=True)
+    assert e <= TOL["bf16"]
+    rc = oracle_mod.conv1d_bwd(cc.values("x"), cc.w, to_host_f64(g1["du"]), bias=cc.bias, silu=True)
+    for k in ("dx", "dw", "dbias"):
+        a = to_host_f64(gc[k])
+        e = y_error(a, rc[k], "bf16") if k == "dx" else raw_error(a, rc[k])
+        print(f"[fused ckpt] conv {k} vs the oracle err/rms {e:.3e}", flush=True)
+        assert e <= TOL["bf16"], (k, e)
+
