@@ -49,6 +49,9 @@ WORKLOADS = {
     "c3_conv": "causal depthwise conv1d (width 4) + SiLU B8 L2048 D5120, bf16 I/O, conv state out",
     "c3_conv_bwd": "causal depthwise conv1d (width 4) + SiLU backward (dx, dw, dbias, dstate) B8 L2048 D5120, "
                    "bf16 I/O",
+    "c3_block_train": "block training step: conv1d (width 4) + SiLU fused into the selective scan storing the "
+                      "backward's checkpoints and u, then the scan's backward and the convolution's backward, "
+                      "B8 L2048 D5120 N16, bf16 I/O, fp32 state, SiLU(z) gate, D skip, last_state",
     "c3_block": "conv1d (width 4) + SiLU fused into the selective scan B8 L2048 D5120 N16, bf16 I/O, fp32 state, "
                 "SiLU(z) gate, D skip, last_state",
 }
@@ -294,6 +297,38 @@ def cpu_baseline_block(case, cc, alg_bytes_full, target_s=20.0):
                       f"(fp64 oracle convolution, then scan)"}
 
 
+def cpu_baseline_block_train(case, cc, alg_bytes_full, target_s=20.0):
+    """The fp64 oracle's block training step on a channel sample: convolution, scan, the
+    scan's backward, the convolution's backward."""
+    from oracle import oracle
+    oracle.build(force=False)
+    threads = min(16, oracle.default_threads())
+    rng = np.random.default_rng(13)
+    dyv = rng.standard_normal((case.bsz, case.L, 16))
+
+    def run(sel):
+        u, _ = oracle.conv1d(cc.values("x")[:, :, sel], cc.w[sel], bias=cc.bias[sel], silu=True)
+        zs = case.values("z")[:, :, sel]
+        args = (u, case.values("delta")[:, :, sel], case.A[sel], case.values("B"), case.values("C"))
+        kw = dict(D=case.Dskip[sel], z=zs, delta_bias=case.delta_bias[sel], softplus=case.softplus)
+        oracle.scan(*args, threads=threads, **kw)
+        g = oracle.scan_bwd(*args, np.resize(dyv, (case.bsz, case.L, len(sel))), threads=threads, **kw)
+        oracle.conv1d_bwd(cc.values("x")[:, :, sel], cc.w[sel], g["du"], bias=cc.bias[sel], silu=True)
+    probe = np.arange(16)
+    t = time.perf_counter()
+    run(probe)
+    per_ch = (time.perf_counter() - t) / len(probe)
+    k = int(min(case.D, max(16, target_s / max(per_ch, 1e-9))))
+    sel = np.unique(np.linspace(0, case.D - 1, k).astype(np.int64))
+    t = time.perf_counter()
+    run(sel)
+    dt = time.perf_counter() - t
+    return {"value": round(alg_bytes_full * len(sel) / case.D / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{len(sel)} of {case.D} channels x all {case.bsz} sequences x {case.L} tokens "
+                      f"(fp64 oracle convolution, scan, scan backward, convolution backward)"}
+
+
 def cpu_baseline_step(case, alg_bytes_step, target_s=20.0):
     from oracle import oracle
     oracle.build(force=False)
@@ -347,7 +382,8 @@ def main():
     elif wl == "ssd":
         case = inputs.ssd_case(8, 2048, 80, 64, 1, 64, seed=230, name="ssd")
     else:
-        case = inputs.config_case("c3" if wl in ("c3_bwd", "c3_train", "c3_zoh", "c3_block") else wl)
+        case = inputs.config_case("c3" if wl in ("c3_bwd", "c3_train", "c3_zoh", "c3_block", "c3_block_train")
+                                  else wl)
     io_bytes = 2 if getattr(case, "io", "bf16") == "bf16" else 4
 
     def td(a):
@@ -459,6 +495,36 @@ def main():
             ssmscan.scan_bwd(dy, t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
                              delta_bias=t["bias"], softplus=case.softplus, checkpoints=ws, out=grads)
         plan = "forward storing the backward's checkpoints (state every 8 tokens) + backward kernel from them"
+    elif wl == "c3_block_train":
+        t = {k: td(getattr(case, f)) for k, f in (("delta", "delta"), ("A", "A"), ("B", "B"), ("C", "C"),
+                                                   ("D", "Dskip"), ("z", "z"), ("bias", "delta_bias"))}
+        bsz, L, D, N = case.bsz, case.L, case.D, case.N
+        cc = inputs.conv_case(bsz, L, D, 4, case.io, seed=4, name="c3_block_train")
+        x, cw, cb = td(cc.x), td(cc.w), td(cc.bias)
+        dy = td(inputs.bf16_bits(np.random.default_rng(13).standard_normal((bsz, L, D), dtype=np.float32)))
+        y = torch.empty((bsz, L, D), dtype=dy.dtype, device=dev)
+        u = torch.empty_like(y)
+        ls = torch.empty((bsz, D, N), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, ssmscan.bwd_workspace_bytes(bsz, L, D, N, dy.dtype) +
+                             ssmscan.workspace_bytes(bsz, L, D, N, dy.dtype)), dtype=torch.uint8, device=dev)
+        kw = dict(D=t["D"], z=t["z"], delta_bias=t["bias"], softplus=case.softplus)
+        fwd = ssmscan.scan_fwd_conv_call(x, cw, cb, t["delta"], t["A"], t["B"], t["C"], y=y, last_state=ls,
+                                         u_out=u, workspace=ws, save_checkpoints=True, **kw)
+        fwd()
+        grads = ssmscan.scan_bwd(dy, u, t["delta"], t["A"], t["B"], t["C"], checkpoints=ws, **kw)
+        dx = torch.empty_like(x)
+        cbwd, _cgrads = ssmscan.conv1d_bwd_call(grads["du"], x, cw, cb, silu=True, dx=dx)
+        alg = (scan_alg_bytes(bsz, L, D, N, io_bytes, True, True, True, True) + D * 5 * 4 + bsz * L * D * io_bytes
+               + scan_bwd_alg_bytes(bsz, L, D, N, io_bytes) + conv_bwd_alg_bytes(bsz, L, D, 4, io_bytes))
+        chtok = bsz * L * D
+        elements = chtok * N
+
+        def one(i):
+            fwd()
+            ssmscan.scan_bwd(dy, u, t["delta"], t["A"], t["B"], t["C"], checkpoints=ws, out=grads, **kw)
+            cbwd()
+        plan = ("fused convolution + scan storing u and the backward's checkpoints, scan backward from them, "
+                "convolution backward")
     else:
         t = {k: td(getattr(case, f)) for k, f in (("u", "u"), ("delta", "delta"), ("A", "A"), ("B", "B"),
                                                    ("C", "C"), ("D", "Dskip"), ("z", "z"), ("bias", "delta_bias"))}
@@ -541,8 +607,9 @@ def main():
     gbps = alg / step_s / 1e9          # whole-job throughput over the timed region
     kern_gbps = alg / kern_s / 1e9     # the kernel's own rate (event-timed launches)
     slots = {"c3_bwd": SLOTS_PER_ELEMENT_BWD, "c3_zoh": SLOTS_PER_ELEMENT_ZOH,
-             "c3_train": SLOTS_PER_ELEMENT + SLOTS_PER_ELEMENT_BWD}.get(wl, SLOTS_PER_ELEMENT)
-    work_ops = elements * slots + (chtok * SLOTS_PER_CHTOK_CONV if wl == "c3_block" else 0)
+             "c3_train": SLOTS_PER_ELEMENT + SLOTS_PER_ELEMENT_BWD,
+             "c3_block_train": SLOTS_PER_ELEMENT + SLOTS_PER_ELEMENT_BWD}.get(wl, SLOTS_PER_ELEMENT)
+    work_ops = elements * slots + (chtok * SLOTS_PER_CHTOK_CONV if wl in ("c3_block", "c3_block_train") else 0)
     lane_ops = work_ops / kern_s / 1e12
     traffic = counter_traffic(wl)
     if wl in ("c5", "c3_conv", "c3_conv_bwd", "ssd"):
@@ -554,7 +621,9 @@ def main():
                 "traffic": traffic,
                 "work": f"{slots} VALU issue slots per (token, channel, state) x {elements} per launch"
                         + (f" + {SLOTS_PER_CHTOK_CONV} per (token, channel) x {chtok} for the convolution"
-                           if wl == "c3_block" else "")}
+                           if wl in ("c3_block", "c3_block_train") else "")
+                        + (" (the convolution's backward, bound by HBM, is not counted)" if wl == "c3_block_train"
+                           else "")}
 
     cpu = None
     if not args.no_cpu:
@@ -565,6 +634,7 @@ def main():
                    else cpu_baseline_conv_bwd(case, dout_bits, alg) if wl == "c3_conv_bwd"
                    else cpu_baseline_ssd(case, alg) if wl == "ssd"
                    else cpu_baseline_block(case, cc, alg) if wl == "c3_block"
+                   else cpu_baseline_block_train(case, cc, alg) if wl == "c3_block_train"
                    else cpu_baseline_scan(case, alg, exact_zoh=wl == "c3_zoh"))
         except Exception as e:  # the GPU figures stand without it
             cpu = {"error": repr(e)}

@@ -529,10 +529,14 @@ def scan_fwd_conv(x: torch.Tensor, conv_w: torch.Tensor, conv_b: Optional[torch.
 
 def scan_fwd_conv_call(x, conv_w, conv_b, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, *,
                        y=None, last_state=None, return_last_state=True, u_out=None, chunk_len=0, workspace=None,
-                       stream=None) -> Callable[[], None]:
-    """The scan_fwd_conv call checked and marshalled once (see scan_fwd_call)."""
+                       stream=None, save_checkpoints=False) -> Callable[[], None]:
+    """The scan_fwd_conv call checked and marshalled once (see scan_fwd_call); with
+    save_checkpoints the checkpoints go to `workspace` (which must then be given)."""
+    if save_checkpoints and workspace is None:
+        raise ValueError("save_checkpoints needs the workspace that scan_bwd will read")
     args, keep, _y, _ls, _ws = _scan_conv_args(x, conv_w, conv_b, delta, A, B, C, D, z, delta_bias, softplus, y,
-                                               last_state, return_last_state, u_out, chunk_len, workspace, stream)
+                                               last_state, return_last_state, u_out, chunk_len, workspace, stream,
+                                               save_checkpoints=save_checkpoints)
 
     def call(_args=args, _keep=keep):
         _check(lib.ssm_scan_fwd_conv(*_args))
