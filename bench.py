@@ -35,6 +35,8 @@ VALU_PEAK_TLANEOPS = 256 * 64 * 2.4e9 / 1e12
 # Unavoidable VALU issue slots per (token, channel, state): the multiplies delta*A and
 # (delta u)*B, the state FMA and the readout FMA at one slot each, and exp2 at half rate.
 SLOTS_PER_ELEMENT = 6
+# state buffers the decode-step benchmark rotates over (4 x 84 MB > the 256 MB MALL)
+ROTATE_STEP = 4
 
 WORKLOADS = {
     "c2": "selective scan B2 L2048 D1536 N16, fp32 I/O, fp32 state",
@@ -59,6 +61,27 @@ WORKLOADS["ssd"] = ("Mamba-2 SSD layer B8 L2048 H80 P64 N64 G1 (model width 5120
                     "SiLU(z) gate, D skip, last_state")
 
 
+def host_threads() -> int:
+    """Threads the CPU baseline may use: the cores this process is allowed to run on,
+    capped by OMP_NUM_THREADS when that is set (the host's CPU share)."""
+    n = max(1, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count() or 1)
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return n
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def ssd_alg_bytes(bsz, L, H, P, G, N):
     """x, z read and y written (bf16); dt (bf16) per head; B, C (bf16) per group; A, D,
     dt_bias; the final state (fp32)."""
@@ -69,7 +92,7 @@ def cpu_baseline_ssd(c, alg_bytes_full, target_s=20.0):
     """The fp64 oracle's SSD layer on a sample of heads (heads are independent)."""
     from oracle import oracle
     oracle.build(force=False)
-    threads = min(16, oracle.default_threads())
+    threads = host_threads()
 
     def run(sel):
         oracle.ssd(c.values("x")[:, :, sel], c.values("dt")[:, :, sel], c.A[sel], c.values("B"), c.values("C"),
@@ -148,30 +171,38 @@ def counter_traffic(workload: str):
     return c.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline_scan(case, alg_bytes_full, target_s=30.0, exact_zoh=False):
-    """Time the fp64 oracle on a channel sample of the workload on the host cores."""
+def cpu_baseline_scan(case, alg_bytes_full, target_s=12.0, target_1core_s=8.0, exact_zoh=False):
+    """Time the fp64 oracle on channel samples of the workload: on all the host cores this
+    process may use (OpenMP over channels), and on one core.  Channels are independent, so
+    each rate is scaled to the whole workload by the sampled fraction."""
     from oracle import oracle
     oracle.build(force=False)
-    threads = min(16, oracle.default_threads())
+    threads = host_threads()
     D = case.D
-    probe = np.arange(0, D, max(1, D // 16))[:16]
-    t = time.perf_counter()
-    oracle.scan_case(case, channels=probe, threads=threads, exact_zoh=exact_zoh)
-    dt = time.perf_counter() - t
-    per_ch = dt / len(probe)
-    k = int(min(D, max(len(probe), target_s / max(per_ch, 1e-9))))
-    sel = np.linspace(0, D - 1, k).astype(np.int64)
-    sel = np.unique(sel)
-    t = time.perf_counter()
-    oracle.scan_case(case, channels=sel, threads=threads, exact_zoh=exact_zoh)
-    dt = time.perf_counter() - t
-    frac = len(sel) / D
-    gbps = alg_bytes_full * frac / dt / 1e9
-    chtok = case.bsz * case.L * len(sel) / dt
-    return {"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "channel_tokens_per_s": round(chtok, 1), "seconds": round(dt, 2),
+
+    def timed(threads_, budget):
+        probe = np.arange(0, D, max(1, D // 16))[:16]
+        t = time.perf_counter()
+        oracle.scan_case(case, channels=probe, threads=threads_, exact_zoh=exact_zoh)
+        per_ch = (time.perf_counter() - t) / len(probe)
+        k = int(min(D, max(len(probe), budget / max(per_ch, 1e-9))))
+        sel = np.unique(np.linspace(0, D - 1, k).astype(np.int64))
+        t = time.perf_counter()
+        oracle.scan_case(case, channels=sel, threads=threads_, exact_zoh=exact_zoh)
+        return sel, time.perf_counter() - t
+
+    sel, dt = timed(threads, target_s)
+    sel1, dt1 = timed(1, target_1core_s)
+    frac, frac1 = len(sel) / D, len(sel1) / D
+    return {"value": round(alg_bytes_full * frac / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "channel_tokens_per_s": round(case.bsz * case.L * len(sel) / dt, 1), "seconds": round(dt, 2),
             "sample": f"{len(sel)} of {D} channels x all {case.bsz} sequences x {case.L} tokens "
-                      f"(fp64 oracle, OpenMP over channels)"}
+                      f"(fp64 oracle, OpenMP over channels, {threads} threads)",
+            "single_core": {"value": round(alg_bytes_full * frac1 / dt1 / 1e9, 5), "unit": "GB/s", "cores": 1,
+                            "channel_tokens_per_s": round(case.bsz * case.L * len(sel1) / dt1, 1),
+                            "seconds": round(dt1, 2),
+                            "sample": f"{len(sel1)} of {D} channels x all {case.bsz} sequences x {case.L} tokens"},
+            "cpu_model": host_cpu_model()}
 
 
 def cpu_baseline_bwd(case, alg_bytes_full, target_s=20.0, with_forward=False):
@@ -180,7 +211,7 @@ def cpu_baseline_bwd(case, alg_bytes_full, target_s=20.0, with_forward=False):
     sample only)."""
     from oracle import oracle
     oracle.build(force=False)
-    threads = min(16, oracle.default_threads())
+    threads = host_threads()
     rng = np.random.default_rng(12)
     dyv = rng.standard_normal((case.bsz, case.L, 16))
 
@@ -275,7 +306,7 @@ def cpu_baseline_block(case, cc, alg_bytes_full, target_s=20.0):
     """The fp64 oracle's convolution followed by its scan, on a channel sample."""
     from oracle import oracle
     oracle.build(force=False)
-    threads = min(16, oracle.default_threads())
+    threads = host_threads()
 
     def run(sel):
         u, _ = oracle.conv1d(cc.values("x")[:, :, sel], cc.w[sel], bias=cc.bias[sel], silu=True)
@@ -302,7 +333,7 @@ def cpu_baseline_block_train(case, cc, alg_bytes_full, target_s=20.0):
     scan's backward, the convolution's backward."""
     from oracle import oracle
     oracle.build(force=False)
-    threads = min(16, oracle.default_threads())
+    threads = host_threads()
     rng = np.random.default_rng(13)
     dyv = rng.standard_normal((case.bsz, case.L, 16))
 
@@ -332,7 +363,7 @@ def cpu_baseline_block_train(case, cc, alg_bytes_full, target_s=20.0):
 def cpu_baseline_step(case, alg_bytes_step, target_s=20.0):
     from oracle import oracle
     oracle.build(force=False)
-    threads = min(16, oracle.default_threads())
+    threads = host_threads()
     st = case.state0.astype(np.float64)
     done = 0
     t = time.perf_counter()
@@ -398,6 +429,9 @@ def main():
         S, D, N = case.S, case.D, case.N
         A, Dv = td(case.A), td(case.Dskip)
         st = td(case.state0).clone()
+        # R state buffers of 84 MB each, more than the 256 MB MALL together: steps that rotate
+        # over them read each state cold from HBM; steps on one buffer find it in the MALL
+        rot_states = [st] + [td(case.state0).clone() for _ in range(ROTATE_STEP - 1)]
         ins = [(td(case.u[k]), td(case.delta[k]), td(case.B[k]), td(case.C[k]), td(case.z[k]))
                for k in range(case.steps)]
         y = torch.empty((S, D), dtype=torch.bfloat16, device=dev)
@@ -429,6 +463,9 @@ def main():
         x, st_in = td(case.x), td(case.state)
         out = torch.empty_like(x)
         st_out = torch.empty_like(st_in)
+        # a second input / output set (168 MB each): steps alternating over the two sets read
+        # x cold from HBM (336 MB of other traffic between two reads of one x)
+        rot_conv = [(x, out), (x.clone(), torch.empty_like(x))]
         alg = conv_alg_bytes(bsz, L, D, width, io_bytes)
         chtok = bsz * L * D
         elements = chtok
@@ -449,6 +486,7 @@ def main():
         td_w, td_b = td(case.w), td(case.bias)
         dx = torch.empty_like(x)
         call, _grads = ssmscan.conv1d_bwd_call(dout, x, td_w, td_b, st_in, silu=True, dx=dx)
+        rot_conv = [(x, dout, dx), (x.clone(), dout.clone(), torch.empty_like(dx))]
 
         def one(i):
             call()
@@ -553,7 +591,15 @@ def main():
 
         def one(i):
             call()
-        plan = "single pass" if nchunk == 1 else f"{nchunk} chunks of {clen} tokens (summary + carry + scan)"
+        pinfo = ssmscan.plan_info(bsz, L, D, N, dtype)
+        if pinfo["split_tiles"] > 0:
+            plan = (f"one pass, split schedule on {pinfo['cu_count']} CUs: {pinfo['workgroups'] - 2 * pinfo['split_tiles']}"
+                    f" whole tiles + {pinfo['split_tiles']} tiles as two token halves (from token "
+                    f"{pinfo['split_at']}), {pinfo['workgroups']} workgroups")
+        elif nchunk == 1:
+            plan = "single pass"
+        else:
+            plan = f"{nchunk} chunks of {clen} tokens (summary + carry + scan)"
         if wl == "c3_zoh":
             plan += ", exact zero-order-hold input term"
         if wl == "c3_block":
@@ -563,33 +609,51 @@ def main():
     for i in range(args.warmup):
         one(i)
     torch.cuda.synchronize()
+    resident = None
     if wl in ("c5", "c3_conv", "c3_conv_bwd"):
         # A decode step (~35 us) or the convolution (~65 us) is short next to the host's cost
         # per call: the K timed steps are captured once as a HIP graph (the library allocates
         # and synchronises nothing, so its launches capture as they are) and replayed as one
-        # submission.
-        graph = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        cap.wait_stream(stream)
-        with torch.cuda.graph(graph, stream=cap):
-            for i in range(args.steps):
-                if wl == "c5":
-                    u, dl, Bk, Ck, z = ins[i % case.steps]
-                    ssmscan.step(st, u, dl, A, Bk, Ck, D=Dv, z=z, y=y)
-                elif wl == "c3_conv_bwd":
-                    ssmscan.conv1d_bwd(dout, x, td_w, td_b, st_in, silu=True, dx=dx, stream=cap)
-                else:
-                    ssmscan.conv1d(x, td_w, td_b, st_in, silu=True, out=out, state_out=st_out, stream=cap)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record(stream)
-        graph.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        per = np.full(args.steps, e0.elapsed_time(e1) * 1e-3 / args.steps)  # seconds per step
-        plan += "; the timed steps replayed as one HIP graph"
+        # submission.  Two graphs: the steps on one buffer set (whose data the 256 MB MALL
+        # partly keeps between steps) and the steps rotating over buffer sets larger than the
+        # MALL together (every step reads its inputs from HBM); the rotating one is `value`.
+        def step_on(i, rot, cap):
+            if wl == "c5":
+                u, dl, Bk, Ck, z = ins[i % case.steps]
+                ssmscan.step(rot_states[i % ROTATE_STEP] if rot else st, u, dl, A, Bk, Ck, D=Dv, z=z, y=y)
+            elif wl == "c3_conv_bwd":
+                xx, dd, gx = rot_conv[i % 2] if rot else (x, dout, dx)
+                ssmscan.conv1d_bwd(dd, xx, td_w, td_b, st_in, silu=True, dx=gx, stream=cap)
+            else:
+                xx, oo = rot_conv[i % 2] if rot else (x, out)
+                ssmscan.conv1d(xx, td_w, td_b, st_in, silu=True, out=oo, state_out=st_out, stream=cap)
+
+        def graph_run(rot):
+            graph = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(stream)
+            with torch.cuda.graph(graph, stream=cap):
+                for i in range(args.steps):
+                    step_on(i, rot, cap)
+            torch.cuda.synchronize()
+            graph.replay()   # one untimed replay
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return time.perf_counter() - t0, e0.elapsed_time(e1) * 1e-3 / args.steps
+
+        _, res_s = graph_run(False)
+        wall, rot_s = graph_run(True)
+        per = np.full(args.steps, rot_s)  # seconds per step
+        resident = {"kernel_us_mean": round(res_s * 1e6, 3), "kernel_gbps": round(alg / res_s / 1e9, 2),
+                    "note": "the same K steps on one buffer set: part of the data stays in the 256 MB MALL "
+                            "between steps, so this rate is not an HBM rate"}
+        plan += (f"; the timed steps replayed as one HIP graph, rotating over "
+                 f"{ROTATE_STEP if wl == 'c5' else 2} buffer sets larger than the MALL together")
     else:
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
         t0 = time.perf_counter()
@@ -619,6 +683,8 @@ def main():
         roof = {"bound": "alu", "achieved": round(lane_ops, 3), "peak": round(VALU_PEAK_TLANEOPS, 3),
                 "unit": "T fp32 VALU lane-ops/s", "frac": round(lane_ops / VALU_PEAK_TLANEOPS, 4),
                 "traffic": traffic,
+                "hbm": {"achieved": round(kern_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(kern_gbps / HBM_PEAK_GBPS, 4)},
                 "work": f"{slots} VALU issue slots per (token, channel, state) x {elements} per launch"
                         + (f" + {SLOTS_PER_CHTOK_CONV} per (token, channel) x {chtok} for the convolution"
                            if wl in ("c3_block", "c3_block_train") else "")
@@ -652,7 +718,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": WORKLOADS[wl], "io_dtype": getattr(case, "io", "bf16"), "plan": plan,
+        "config": {"workload": WORKLOADS[wl], "io_dtype": getattr(case, "io", "bf16"), "state_dtype": "f32",
+                   "plan": plan,
                    "channel_tokens_per_step": chtok, "alg_bytes_per_step": alg},
         "hbm_pct_of_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "channel_tokens_per_s": round(chtok / step_s, 1),
@@ -661,6 +728,7 @@ def main():
         "kernel_us_p10_p50_p90": [round(float(np.percentile(per, q)) * 1e6, 3) for q in (10, 50, 90)],
         "roofline": roof,
         "cpu_baseline": cpu,
+        **({"mall_resident": resident} if resident else {}),
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SSMSCAN_VERSION 9
+#define SSMSCAN_VERSION 10
 
 /* Bits of the `flags` argument of the scan entry points. */
 #define SSM_SCAN_SOFTPLUS 1     /* step size = softplus(delta + delta_bias) */
@@ -90,8 +90,9 @@ typedef enum {
  *             chunks of this many tokens and combine the chunk states (two-pass chunk
  *             carry); -1 = one pass, one workgroup per 64 channels of a sequence.  With 0
  *             the library runs one pass when there are enough channel tiles to fill the
- *             GPU and the chunk carry otherwise.  Results agree up to fp32 rounding
- *             whatever the plan. */
+ *             GPU (with dstate 16 and 2 to 2.5 tiles per CU, the split schedule of
+ *             ssm_scan_plan_info: bitwise the one pass's results) and the chunk carry
+ *             otherwise.  Results agree up to fp32 rounding whatever the plan. */
 typedef struct ssm_dims {
     int64_t batch;
     int64_t seqlen;
@@ -101,9 +102,10 @@ typedef struct ssm_dims {
     int32_t chunk_len;
 } ssm_dims;
 
-/* Bytes of device workspace ssm_scan_fwd needs for these sizes and plan (256-byte
- * aligned regions): the per-chunk carry states of a chunked plan, 0 for a single pass.
- * Returns 0 for an invalid or empty problem. */
+/* Bytes of device workspace ssm_scan_fwd needs for these sizes and plan on the current device
+ * (256-byte aligned regions): the per-chunk carry states of a chunked plan, the handed-over
+ * states and flags of the split schedule (see ssm_scan_plan_info), 0 for a plain single
+ * pass.  Returns 0 for an invalid or empty problem. */
 SSMSCAN_API size_t ssm_scan_workspace_bytes(const ssm_dims *dims);
 
 /* The plan ssm_scan_fwd will use.  Returns the number of chunks each sequence is split
@@ -112,6 +114,26 @@ SSMSCAN_API size_t ssm_scan_workspace_bytes(const ssm_dims *dims);
  * or the whole sequence for a single pass.  Returns a negative ssm_status for invalid
  * sizes. */
 SSMSCAN_API int64_t ssm_scan_plan(const ssm_dims *dims, int64_t *chunk_len_out);
+
+/* The schedule the scan takes on a device with cu_count compute units (cu_count <= 0: the
+ * current device; 256 when no device is visible).  The library plans from the device's CU
+ * count: one workgroup of four waves per (sequence, 64-channel tile) in one pass; the chunk
+ * carry when there are fewer than 2 tiles per CU and sequences of 512 tokens or more; and, for
+ * dstate 16 with 2 to 2.5 tiles per CU, the split schedule: split_tiles of the tiles are run
+ * as two token halves (the second from the state the first hands over through the workspace,
+ * starting at token split_at), so that every CU gets the same number of tokens.  The results
+ * are bitwise those of the one-pass schedule (dims->chunk_len = -1).  Fills *out; returns
+ * SSM_OK or a negative ssm_status. */
+typedef struct ssm_plan_info {
+    int32_t cu_count;       /* the CU count the plan was made for */
+    int64_t nchunk;         /* carry chunks per sequence (1: no carry) */
+    int64_t chunk_len;      /* tokens per carry chunk (seqlen without the carry) */
+    int64_t split_tiles;    /* tiles run as two token halves (0: not the split schedule) */
+    int64_t split_at;       /* first token of the second halves */
+    int64_t workgroups;     /* workgroups of the scan's main launch */
+    size_t workspace_bytes; /* = ssm_scan_workspace_bytes on that device */
+} ssm_plan_info;
+SSMSCAN_API int ssm_scan_plan_info(const ssm_dims *dims, int cu_count, ssm_plan_info *out);
 
 /* Selective scan forward over a batch of sequences, from a zero state.
  *   u, delta, z, y : [batch][seqlen][dim]   (io_dtype; z may be NULL = no gate)
@@ -125,13 +147,16 @@ SSMSCAN_API int64_t ssm_scan_plan(const ssm_dims *dims, int64_t *chunk_len_out);
  *   y              : output, written completely
  *   last_state     : [batch][dim][dstate] fp32 output h_L, may be NULL
  *   workspace      : device memory of at least ssm_scan_workspace_bytes(dims) bytes, 16-byte
- *                    aligned (contents on entry do not matter; scratch for this call);
- *                    may be NULL when that size is 0.  With SSM_SCAN_CHECKPOINTS (a training
+ *                    aligned (contents on entry do not matter; scratch for this call: the
+ *                    carry's chunk states, or the split schedule's handed-over states and
+ *                    flags); may be NULL when that size is 0.  With SSM_SCAN_CHECKPOINTS (a training
  *                    forward) it must hold ssm_scan_bwd_workspace_bytes(dims) +
  *                    ssm_scan_workspace_bytes(dims) bytes, and the call leaves in its first
  *                    ssm_scan_bwd_workspace_bytes(dims) bytes the states ssm_scan_bwd would
  *                    otherwise recompute in a pass of its own: pass the same workspace and
- *                    flag to ssm_scan_bwd
+ *                    flag to ssm_scan_bwd.  The checkpoints are the states before every 8th
+ *                    token, so with this flag a chunked plan's chunk length (dims->chunk_len
+ *                    > 0, or the library's choice) is rounded up to a multiple of 8
  * Returns SSM_OK or a negative ssm_status. */
 SSMSCAN_API int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
                  const float *D, const void *z, const float *delta_bias, int flags,

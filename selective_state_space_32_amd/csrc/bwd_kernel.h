@@ -199,7 +199,8 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
                 const bool live = tt < nt && qact && (VEC || d0 + cq + v < D);
                 const float x = widen(rx[p], v) + bq[v];
                 float sg = 1.0f;
-                const float sp = softplus ? softplus_f32(x, sg) : x;
+                // (the forward's step size: the short softplus for bf16 I/O)
+                const float sp = softplus ? (sizeof(IO) == 2 ? softplus_short_f32(x, sg) : softplus_f32(x, sg)) : x;
                 const float dl = live ? sp : 0.0f;
                 float g = 1.0f, gz = 0.0f;
                 if (gated) {   // silu(z) = z sigmoid(z), silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z)))

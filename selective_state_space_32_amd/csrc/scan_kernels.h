@@ -31,6 +31,15 @@ constexpr int kChanTile = 64;    // channels per workgroup (one per lane)
 
 enum ScanMode { kFull = 0, kSummary = 1, kCheckpoint = 2 };
 
+// Roles of a workgroup under the split schedule (kFull only): a whole tile, the first part of a
+// tile (tokens [0, l_mid), handing its final state over), or the rest of that tile (tokens
+// [l_mid, L), starting from the handed-over state).
+enum SplitRole { kWhole = 0, kFirstPart = 1, kSecondPart = 2 };
+
+// The second part's wait for its hand-over is bounded (wait_ticks of the 100 MHz constant clock,
+// s_memrealtime; the host passes 20 ms by default): a first part takes a few hundred
+// microseconds, and the bound only guarantees progress when the first part cannot run.
+
 // kCheckpoint stores the state before every kCkptEvery-th token (for the backward pass).
 constexpr int kCkptEvery = 8;
 
@@ -77,8 +86,26 @@ __device__ __forceinline__ void load_slice(const IO *__restrict__ p, int64_t off
 //   kCheckpoint: one pass from h0 without readout, storing the state before every
 //             kCkptEvery-th token to cstate[b][t / kCkptEvery] (the backward pass's
 //             recomputation points).
-//   CK (kFull only): the same checkpoints, to ckpt_out, from the forward itself (a
-//             training forward; the backward then skips its kCheckpoint pass).
+//   CK (kFull): the same checkpoints, to ckpt_out, from the forward itself (a training
+//             forward; the backward then skips its kCheckpoint pass).  With the convolution
+//             (CW > 0) the training forward scans u rounded to the I/O type, the values the
+//             backward reads back from u_out; kSummary takes CK for that rounding alone, so
+//             that the chunk states it carries are those of the same u.
+//   Split schedule (kFull, n_split > 0): the grid holds n_full + 2 n_split workgroups.  Ids
+//             [0, n_full) take whole tiles 0 .. n_full-1; ids [n_full, n_full + n_split)
+//             take tokens [0, l_mid) of tiles n_full .. n_tiles-1, store their final state in
+//             hand[tile - n_full] and then set hflag[tile - n_full] (release, device scope);
+//             ids [n_full + n_split, n_full + 2 n_split) wait for that flag (acquire), start
+//             from the handed-over state and take tokens [l_mid, L).  The states are those of
+//             the single pass, so the results are bitwise the same.  With 3 workgroups
+//             resident per CU and workgroups dispatched round-robin over the CUs, ids c,
+//             c + C and c + 2C share CU c, so every CU gets two whole tiles and one part (for
+//             n_tiles = 2.5 C): the same work everywhere instead of 3 tiles on half the CUs and
+//             2 on the rest.  First parts run at wave priority 3 and second parts at 2 once
+//             they start, so the hand-over comes early and the parts do not form the tail.
+//             A second part that waits longer than wait_ticks computes the whole tile itself
+//             (same values), so no schedule or placement can hang the kernel.  hflag must be
+//             zero at launch.
 //   N: state size; S: states per wave (K = N/S waves); T: tokens per LDS tile.
 //   VEC: the prep and epilogue move V consecutive channels of one token per thread
 //        (one 16-byte access for 8 bf16); needs D % 8 == 0 and 16-byte aligned u, delta,
@@ -103,7 +130,9 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                   float *__restrict__ cstate, float *__restrict__ cdsum, int64_t L, int64_t D,
                   int tiles_per_b, int n_tiles, int64_t chunk_len, int nchunk, int softplus,
                   const float *__restrict__ conv_w = nullptr, const float *__restrict__ conv_b = nullptr,
-                  IO *__restrict__ u_out = nullptr, float *__restrict__ ckpt_out = nullptr) {
+                  IO *__restrict__ u_out = nullptr, float *__restrict__ ckpt_out = nullptr,
+                  int n_full = 0, int n_split = 0, int64_t l_mid = 0, float *__restrict__ hand = nullptr,
+                  int *__restrict__ hflag = nullptr, unsigned long long wait_ticks = 0) {
     constexpr int K = N / S;
     constexpr int J = T / K;                   // prep / epilogue elements per thread per tile
     constexpr int V = VEC ? (J < 8 ? J : 8) : 1;  // consecutive channels per thread access
@@ -148,15 +177,32 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     const int64_t n_items = (int64_t)n_tiles * nchunk;
 
     const int64_t item = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-    if (item >= n_items) return;
-    const int c = (int)(item / n_tiles);
-    const int tile = (int)(item - (int64_t)c * n_tiles);
+    int role = kWhole, c = 0, tile;
+    if (MODE == kFull && n_split > 0) {
+        const int g = (int)item;
+        if (g >= n_full + 2 * n_split) return;
+        if (g < n_full) {
+            tile = g;
+        } else if (g < n_full + n_split) {
+            tile = g;
+            role = kFirstPart;
+        } else {
+            tile = g - n_split;
+            role = kSecondPart;
+        }
+    } else {
+        if (item >= n_items) return;
+        c = (int)(item / n_tiles);
+        tile = (int)(item - (int64_t)c * n_tiles);
+    }
     const int b = tile / tiles_per_b;
     const int64_t d0 = (int64_t)(tile - b * tiles_per_b) * kChanTile;
     const int64_t d = d0 + lane;            // channel of this lane in the recurrence
     const bool act = d < D;
-    const int64_t t_begin = (int64_t)c * chunk_len;
-    const int64_t t_end = min(L, t_begin + chunk_len);
+    int64_t t_begin = (int64_t)c * chunk_len;
+    int64_t t_end = min(L, t_begin + chunk_len);
+    if (role == kFirstPart) t_end = l_mid;
+    if (role == kSecondPart) t_begin = l_mid;
     const int64_t row0 = (int64_t)b * L;
     const bool qact = d0 + cq < D;          // whole group in or out (D % V == 0 when VEC)
     const int64_t dq = qact ? d0 + cq : (D - V) / V * V;  // in-bounds channel for loads
@@ -169,7 +215,36 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
         if constexpr (ZOH) inv_a[s] = act ? 1.0f / a : 0.0f;
         h[s] = 0.0f;
     }
-    if ((MODE == kFull || MODE == kCheckpoint) && act) {
+    if (role == kFirstPart) __builtin_amdgcn_s_setprio(3);
+    if (role == kSecondPart) {
+        // wait for the first part's state (wave 0 polls; the others wait at the barrier)
+        __shared__ int s_handed;
+        if (tid < 64) {
+            const unsigned long long w0 = __builtin_amdgcn_s_memrealtime();
+            int ok = 0;
+            for (;;) {
+                if (__hip_atomic_load(&hflag[tile - n_full], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+                    ok = 1;
+                    break;
+                }
+                if (__builtin_amdgcn_s_memrealtime() - w0 > wait_ticks) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+            if (tid == 0) s_handed = ok;
+        }
+        __syncthreads();
+        if (s_handed) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        } else {
+            role = kWhole;   // no hand-over: the whole tile from the initial state
+            t_begin = 0;
+        }
+        __builtin_amdgcn_s_setprio(2);
+    }
+    if (role == kSecondPart && act) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) h[s] = hand[((int64_t)(tile - n_full) * kChanTile + lane) * N + w * S + s];
+    } else if ((MODE == kFull || MODE == kCheckpoint) && act) {
         // the state before this chunk: carried from chunk c-1, or the initial state (read
         // from h0 itself in a single pass, from the copy in slot nchunk-1 otherwise)
         const float *src = nullptr;
@@ -398,7 +473,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                 // (with the convolution, u comes from the conv phase through s_dk)
                 const float uu = CW > 0 ? s_dk[tt][sdk(cq + v)].x : raw(r.u[p], v);
                 const float x = raw(r.d[p], v) + bq[v];
-                const float dl = softplus ? softplus_f32(x) : x;
+                const float dl = softplus ? (sizeof(IO) == 2 ? softplus_short_f32(x) : softplus_f32(x)) : x;
                 dk[v] = f32x2_t{dl, ZOH ? uu : dl * uu};
                 if (READOUT) {
                     cur.u[p][v] = uu;
@@ -540,6 +615,15 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
             for (int s = 0; s < S; ++s) cstate[(((int64_t)b * nchunk + c) * D + d) * N + w * S + s] = h[s];
             if (w == 0) cdsum[((int64_t)b * nchunk + c) * D + d] = dsum;
         }
+    } else if (role == kFirstPart) {
+        // hand the state over: stores, release at device scope, then the flag
+        if (act) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) hand[((int64_t)(tile - n_full) * kChanTile + lane) * N + w * S + s] = h[s];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();
+        if (tid == 0) __hip_atomic_store(&hflag[tile - n_full], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else if (c == nchunk - 1) {
         if (last_state && act) {
 #pragma unroll

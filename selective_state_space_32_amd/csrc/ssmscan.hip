@@ -3,9 +3,11 @@
 #include <hip/hip_runtime.h>
 #include <algorithm>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 
 #include "ssmscan.h"
@@ -40,7 +42,44 @@ bool n_supported(int64_t n) { return n == 1 || n == 2 || n == 4 || n == 8 || n =
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 constexpr int64_t kMaxElems = int64_t(1) << 46;
 constexpr int kMaxChunks = 65535;  // grid.y limit
-constexpr int kTargetGroups = 768; // 3 workgroups per CU on a 256-CU MI355X
+// Scan workgroups resident per CU (N = 16: 133-137 VGPRs and 48 KB of LDS per 4-wave group),
+// the basis of the schedules below.
+constexpr int kGroupsPerCU = 3;
+// CU count assumed when no device is visible (plan queries on a host without a GPU): MI355X.
+constexpr int kDefaultCUs = 256;
+
+// How long a second half of the split schedule waits for its hand-over, in ticks of the
+// 100 MHz constant clock: SSMSCAN_HANDOVER_WAIT_US microseconds (default 20000), read at each
+// call.  0 makes every second half compute its whole tile (the time-out path; same results).
+unsigned long long handover_wait_ticks() {
+    const char *e = getenv("SSMSCAN_HANDOVER_WAIT_US");
+    long long us = 20000;
+    if (e && *e) {
+        char *end = nullptr;
+        const long long v = strtoll(e, &end, 10);
+        if (end != e && v >= 0 && v <= 10000000) us = v;
+    }
+    return (unsigned long long)us * 100ull;
+}
+
+// Compute units of the current device, cached per device.
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return kDefaultCUs;
+    }
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        n = kDefaultCUs;
+    }
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -66,35 +105,51 @@ int check_dims(const ssm_dims *dm, bool scan) {
     return SSM_OK;
 }
 
-enum Schedule { kGrid = 0, kCarry = 1 };
+enum Schedule { kGrid = 0, kCarry = 1, kSplit = 2 };
 
 struct Plan {
     int schedule = kGrid;
     int64_t nchunk = 1;      // chunks per sequence (work items per tile)
     int64_t chunk_len = 0;   // tokens per chunk
-    size_t off_cstate = 0, off_cdsum = 0, bytes = 0;
+    int64_t n_full = 0, n_split = 0, l_mid = 0;   // the split schedule
+    size_t off_cstate = 0, off_cdsum = 0, off_hand = 0, off_flags = 0, bytes = 0;
 };
 
 // One workgroup per (sequence, 64-channel tile) fills the GPU once there are about two
 // tiles per CU or more; with fewer tiles the tokens are split into chunks as well (the
 // chunk carry), which costs an extra summary pass over all but the last chunk.
-Plan make_plan(const ssm_dims *dm) {
+// align_ckpt: the call also stores the backward pass's checkpoints (the state before every
+// kCkptEvery-th token); each chunk's first token must then be one of those points, so a
+// carry chunk length is rounded up to a multiple of kCkptEvery (fewer chunks, never more
+// workspace than the plan without the flag).
+// cus: compute units of the device.  allow_split: the split schedule may be used (not when the
+// initial state is the last_state buffer: a second part that found no hand-over would rewrite
+// last_state while its first part may still read the initial state).
+//
+// The split schedule (N = 16, library's choice, 2 C < tiles <= 2.5 C for C CUs): with one
+// workgroup per tile, tiles = 2.5 C puts 3 tiles on half the CUs and 2 on the rest, and the
+// kernel lasts as long as 3.  Splitting 3 C - tiles of the tiles into two token halves (the
+// second started from the first's handed-over state) gives 3 C workgroups, three per CU, and
+// an equal share of tokens to every CU.
+Plan make_plan(const ssm_dims *dm, int cus, bool align_ckpt = false, bool allow_split = true) {
     Plan p;
     const int64_t bsz = dm->batch, L = dm->seqlen, D = dm->dim, N = dm->dstate;
     if (bsz == 0 || L == 0 || D == 0) return p;
+    if (cus <= 0) cus = kDefaultCUs;
     const int64_t tiles = bsz * ((D + ssm::kChanTile - 1) / ssm::kChanTile);
+    const int64_t target_groups = (int64_t)kGroupsPerCU * cus;
     int64_t clen = L;
     if (dm->chunk_len > 0) {
         p.schedule = kCarry;
         clen = dm->chunk_len < L ? dm->chunk_len : L;
         if ((L + clen - 1) / clen > kMaxChunks) clen = (L + kMaxChunks - 1) / kMaxChunks;
-    } else if (dm->chunk_len == 0 && tiles < 512 && L >= 512) {
+    } else if (dm->chunk_len == 0 && tiles < 2 * (int64_t)cus && L >= 512) {
         // too few channel tiles to fill the GPU: split the tokens too.  At least one round of
         // resident workgroups, and chunks of at most 512 tokens so that long sequences give
         // many items (the grid then balances itself over the CUs); chunks of at least 128
         // tokens keep the per-item start-up and the carry small.  (Short sequences stay one
         // pass: three launches would cost more than they save.)
-        const int64_t want = std::max((kTargetGroups + tiles - 1) / tiles, (L + 511) / 512);
+        const int64_t want = std::max((target_groups + tiles - 1) / tiles, (L + 511) / 512);
         const int64_t most = (L + 127) / 128;
         int64_t nchunk = want < most ? want : most;
         if (nchunk < 1) nchunk = 1;
@@ -105,6 +160,10 @@ Plan make_plan(const ssm_dims *dm) {
             clen = (clen + 31) / 32 * 32;
         }
     }
+    if (align_ckpt && p.schedule == kCarry) {
+        clen = (clen + ssm::kCkptEvery - 1) / ssm::kCkptEvery * ssm::kCkptEvery;
+        if (clen > L) clen = L;
+    }
     p.chunk_len = clen;
     p.nchunk = (L + clen - 1) / clen;
     if (p.schedule == kCarry && p.nchunk == 1) p.schedule = kGrid;
@@ -114,6 +173,17 @@ Plan make_plan(const ssm_dims *dm) {
         p.off_cstate = 0;
         p.off_cdsum = cs;
         p.bytes = cs + cd;
+    } else if (dm->chunk_len == 0 && allow_split && N == 16 && tiles > 2 * (int64_t)cus &&
+               2 * tiles <= 5 * (int64_t)cus && L >= 128) {
+        p.schedule = kSplit;
+        p.n_split = target_groups - tiles;
+        p.n_full = tiles - p.n_split;
+        p.l_mid = (L / 2 + 31) / 32 * 32;   // a whole number of 32-token tiles (and of checkpoint spans)
+        const size_t hb = align256((size_t)(p.n_split * ssm::kChanTile * N) * sizeof(float));
+        const size_t fb = align256((size_t)p.n_split * sizeof(int));
+        p.off_hand = 0;
+        p.off_flags = hb;
+        p.bytes = hb + fb;
     }
     return p;
 }
@@ -154,7 +224,9 @@ void launch_scan_kernels(const IO *u, const IO *dl, const float *A, const IO *B,
     const int64_t cl = p.chunk_len;
     const int nc = (int)p.nchunk;
     if (p.schedule == kCarry) {
-        hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kSummary, VEC, ZOH, CW>),
+        // (CK also here: with the fused convolution, the training forward scans u rounded to the
+        // I/O type, so the summary pass must carry the states of that same u)
+        hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kSummary, VEC, ZOH, CW, CK>),
                            dim3((unsigned)n_tiles, (unsigned)(nc - 1)), block, 0, st, u, dl, (const IO *)nullptr,
                            (IO *)nullptr, A, (const float *)nullptr, bias, B, C, (const float *)nullptr,
                            (float *)nullptr, cstate, cdsum, L, D, tiles_per_b, n_tiles, cl, nc, softplus, cv.w, cv.b,
@@ -162,6 +234,19 @@ void launch_scan_kernels(const IO *u, const IO *dl, const float *A, const IO *B,
         const int col_tiles = (int)((D * N + 63) / 64);
         hipLaunchKernelGGL((ssm::carry_scan_kernel<N>), dim3((unsigned)(bsz * col_tiles)), dim3(256), 0, st,
                            cstate, (const float *)cdsum, A, h0, D, nc, col_tiles);
+    }
+    if (p.schedule == kSplit) {
+        // the hand-over flags start at zero (a fill kernel: no memset node if the caller captures a graph)
+        int *flags = reinterpret_cast<int *>(static_cast<char *>(ws) + p.off_flags);
+        float *hand = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_hand);
+        hipLaunchKernelGGL(ssm::fill_zero_kernel<int>, dim3((unsigned)((p.n_split + 255) / 256)), dim3(256), 0, st, flags,
+                           p.n_split);
+        hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kFull, VEC, ZOH, CW, CK>),
+                           dim3((unsigned)(p.n_full + 2 * p.n_split), 1), block, 0, st, u, dl, z, y, A, Dv, bias, B, C,
+                           h0, last_state, cstate, cdsum, L, D, tiles_per_b, n_tiles, cl, nc, softplus, cv.w, cv.b,
+                           static_cast<IO *>(cv.u_out), ckpt, (int)p.n_full, (int)p.n_split, p.l_mid, hand, flags,
+                           handover_wait_ticks());
+        return;
     }
     hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kFull, VEC, ZOH, CW, CK>),
                        dim3((unsigned)n_tiles, (unsigned)nc), block, 0, st, u, dl, z, y, A, Dv, bias, B, C, h0,
@@ -514,7 +599,8 @@ static int scan_impl(const float *h0, const void *u, const void *delta, const fl
         if (flags & SSM_SCAN_EXACT_ZOH)
             return fail(SSM_ERR_FLAGS, "the exact zero-order hold is not available with the fused convolution");
     }
-    Plan p = make_plan(dims);
+    // (the split schedule is not used when the initial state is the last_state buffer)
+    Plan p = make_plan(dims, device_cus(), want_ckpt, !(h0 && h0 == last_state));
     // with checkpoints the workspace holds them first (the backward pass's layout), then the plan's carry area
     const size_t ck_bytes = want_ckpt ? bwd_workspace_bytes(dims) : 0, need = ck_bytes + p.bytes;
     if (need > 0 && !workspace) return fail(SSM_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
@@ -540,16 +626,33 @@ const char *ssm_last_error(void) { return g_err.c_str(); }
 
 size_t ssm_scan_workspace_bytes(const ssm_dims *dims) {
     if (check_dims(dims, true) != SSM_OK) return 0;
-    return make_plan(dims).bytes;
+    return make_plan(dims, device_cus()).bytes;
 }
 
 int64_t ssm_scan_plan(const ssm_dims *dims, int64_t *chunk_len_out) {
     int rc = check_dims(dims, true);
     if (rc != SSM_OK) return rc;
-    Plan p = make_plan(dims);
+    Plan p = make_plan(dims, device_cus());
     if (chunk_len_out) *chunk_len_out = p.chunk_len;
     ok();
     return p.schedule == kCarry ? p.nchunk : 1;
+}
+
+int ssm_scan_plan_info(const ssm_dims *dims, int cu_count, ssm_plan_info *out) {
+    int rc = check_dims(dims, true);
+    if (rc != SSM_OK) return rc;
+    if (!out) return fail(SSM_ERR_NULL, "out is NULL");
+    const int cus = cu_count > 0 ? cu_count : device_cus();
+    Plan p = make_plan(dims, cus);
+    out->cu_count = cus;
+    out->nchunk = p.schedule == kCarry ? p.nchunk : 1;
+    out->chunk_len = p.chunk_len;
+    out->split_tiles = p.n_split;
+    out->split_at = p.l_mid;
+    out->workgroups = p.schedule == kSplit ? p.n_full + 2 * p.n_split
+                      : (int64_t)dims->batch * ((dims->dim + ssm::kChanTile - 1) / ssm::kChanTile) * out->nchunk;
+    out->workspace_bytes = p.bytes;
+    return ok();
 }
 
 int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B, const void *C,

@@ -34,6 +34,12 @@ class ssm_ssd_dims(ctypes.Structure):
                 ("io_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
+class ssm_plan_info(ctypes.Structure):
+    _fields_ = [("cu_count", ctypes.c_int32), ("nchunk", ctypes.c_int64), ("chunk_len", ctypes.c_int64),
+                ("split_tiles", ctypes.c_int64), ("split_at", ctypes.c_int64), ("workgroups", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
 class SSMError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"{STATUS.get(code, code)}: {msg}")
@@ -53,6 +59,8 @@ def _load() -> ctypes.CDLL:
     lib.ssm_scan_workspace_bytes.restype = ctypes.c_size_t
     lib.ssm_scan_plan.argtypes = [D, ctypes.POINTER(ctypes.c_int64)]
     lib.ssm_scan_plan.restype = ctypes.c_int64
+    lib.ssm_scan_plan_info.argtypes = [D, ctypes.c_int, ctypes.POINTER(ssm_plan_info)]
+    lib.ssm_scan_plan_info.restype = ctypes.c_int
     lib.ssm_scan_fwd.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int, P, P, D, P, ctypes.c_size_t, P]
     lib.ssm_scan_fwd.restype = ctypes.c_int
     lib.ssm_scan_fwd_from.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_int, P, P, D, P, ctypes.c_size_t, P]
@@ -118,6 +126,16 @@ def scan_plan(batch: int, seqlen: int, dim: int, dstate: int, io_dtype, chunk_le
     if n < 0:
         raise SSMError(n, last_error())
     return n, int(cl.value)
+
+
+def plan_info(batch: int, seqlen: int, dim: int, dstate: int, io_dtype, chunk_len: int = 0,
+              cu_count: int = 0) -> dict:
+    """The scan's schedule on a device with cu_count CUs (0: the current device), as a dict of
+    the ssm_plan_info fields."""
+    d = make_dims(batch, seqlen, dim, dstate, io_dtype, chunk_len)
+    out = ssm_plan_info()
+    _check(lib.ssm_scan_plan_info(ctypes.byref(d), int(cu_count), ctypes.byref(out)))
+    return {f: getattr(out, f) for f, _ in ssm_plan_info._fields_}
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -54,6 +54,15 @@ def y_error(y_gpu: np.ndarray, y_ref: np.ndarray, io: str) -> float:
     return float(np.max(d)) / r if r > 0 else float(np.max(d))
 
 
+def bf16_pair_error(a: np.ndarray, b: np.ndarray) -> float:
+    """Difference of two bf16 outputs computed from values that agree up to fp32 rounding,
+    beyond the rounding of each to bf16: max(|a - b| - ulp(a)/2 - ulp(b)/2) / rms(b)."""
+    d = np.abs(a - b) - 0.5 * bf16_ulp(a) - 0.5 * bf16_ulp(b)
+    r = rms(b)
+    m = float(np.max(d)) if d.size else 0.0
+    return max(m, 0.0) / r if r > 0 else max(m, 0.0)
+
+
 def raw_error(a: np.ndarray, ref: np.ndarray) -> float:
     r = rms(ref)
     d = float(np.max(np.abs(a - ref))) if a.size else 0.0

@@ -242,7 +242,9 @@ def test_empty_problems_are_noops(b):
 
 
 def test_plan(b):
-    # the B8 L2048 D5120 layer has 640 channel tiles, all resident at once: one grid pass
+    # (with no GPU visible the library plans for 256 CUs)
+    # the B8 L2048 D5120 layer has 640 channel tiles, all resident at once: one pass (the split
+    # schedule, see test_plan_follows_the_cu_count)
     assert b.scan_plan(8, 2048, 5120, 16, 1) == (1, 2048)
     # more tiles than resident workgroups: still one grid pass (several rounds)
     assert b.scan_plan(16, 2048, 4096, 16, 1) == (1, 2048)
@@ -254,8 +256,43 @@ def test_plan(b):
     assert b.scan_plan(2, 300, 70, 4, 0, chunk_len=64) == (5, 64)
     assert b.scan_plan(2, 300, 70, 4, 0, chunk_len=-1) == (1, 300)
     assert b.scan_plan(1, 256, 16, 4, 0) == (1, 256)
-    # a single pass needs no workspace; the chunk carry does
-    assert b.workspace_bytes(8, 2048, 5120, 16, 1) == 0
+    # a plain single pass needs no workspace; the split schedule holds its handed-over states
+    # (128 tiles x 64 channels x 16 states fp32) and flags, the chunk carry its chunk states
+    assert b.workspace_bytes(8, 2048, 5120, 16, 1) == 128 * 64 * 16 * 4 + 512
     assert b.workspace_bytes(16, 2048, 4096, 16, 1) == 0
     assert b.workspace_bytes(1, 131072, 2048, 16, 1) >= 256 * 2048 * 16 * 4
     assert b.workspace_bytes(1, 4096, 64, 16, 1, chunk_len=128) > b.workspace_bytes(1, 4096, 64, 16, 1, chunk_len=-1)
+
+
+def test_plan_follows_the_cu_count(b):
+    """ssm_scan_plan_info for devices of several CU counts (planning is host logic)."""
+    # B8 L2048 D5120 N16 = 640 tiles.  256 CUs: 2.5 tiles per CU; 128 tiles run as two halves,
+    # 512 + 2 x 128 = 768 workgroups = 3 per CU, each CU the work of 2.5 tiles
+    p = b.plan_info(8, 2048, 5120, 16, 1, cu_count=256)
+    assert p["cu_count"] == 256 and p["nchunk"] == 1 and p["chunk_len"] == 2048
+    assert p["split_tiles"] == 128 and p["split_at"] == 1024 and p["workgroups"] == 768
+    assert p["workspace_bytes"] == 128 * 64 * 16 * 4 + 512
+    # 304 CUs (2.1 tiles per CU): 3 x 304 - 640 = 272 tiles split, 912 workgroups
+    p = b.plan_info(8, 2048, 5120, 16, 1, cu_count=304)
+    assert p["split_tiles"] == 272 and p["workgroups"] == 912 and p["nchunk"] == 1
+    # 200 CUs (3.2 tiles per CU): more than 2.5 per CU, a plain pass
+    p = b.plan_info(8, 2048, 5120, 16, 1, cu_count=200)
+    assert p["split_tiles"] == 0 and p["nchunk"] == 1 and p["workgroups"] == 640 and p["workspace_bytes"] == 0
+    # 400 CUs (1.6 tiles per CU, L >= 512): the chunk carry, chunks of 512 tokens
+    p = b.plan_info(8, 2048, 5120, 16, 1, cu_count=400)
+    assert (p["nchunk"], p["chunk_len"], p["split_tiles"]) == (4, 512, 0) and p["workgroups"] == 2560
+    # the small-batch carry follows the CU count too: B2 L2048 D1536 (48 tiles)
+    assert (b.plan_info(2, 2048, 1536, 16, 0, cu_count=256)["nchunk"], b.plan_info(2, 2048, 1536, 16, 0,
+            cu_count=256)["chunk_len"]) == (16, 128)
+    p = b.plan_info(2, 2048, 1536, 16, 0, cu_count=64)
+    assert (p["nchunk"], p["chunk_len"]) == (4, 512)
+    # no split for another state size, a forced one pass, forced chunks or short sequences
+    assert b.plan_info(8, 2048, 5120, 8, 1, cu_count=256)["split_tiles"] == 0
+    assert b.plan_info(8, 2048, 5120, 16, 1, chunk_len=-1, cu_count=256)["split_tiles"] == 0
+    assert b.plan_info(8, 2048, 5120, 16, 1, chunk_len=256, cu_count=256)["split_tiles"] == 0
+    assert b.plan_info(8, 64, 5120, 16, 1, cu_count=256)["split_tiles"] == 0
+    # an odd length: the second halves start on a 32-token boundary
+    p = b.plan_info(8, 1001, 5120, 16, 0, cu_count=256)
+    assert p["split_tiles"] == 128 and p["split_at"] == 512
+    # cu_count <= 0 plans for the current device (256 without one)
+    assert b.plan_info(8, 2048, 5120, 16, 1)["cu_count"] > 0

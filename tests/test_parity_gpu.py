@@ -146,8 +146,10 @@ def c3_case():
 
 def test_layer_scan_bf16_full_size_sampled(oracle_mod, c3_case):
     """B8 L2048 D5120 N16 bf16 with gate and last_state, in the benchmark's launch
-    configuration; outputs of sampled channels (all batches, all tokens) against the oracle."""
+    configuration (on a 256-CU MI355X the split schedule: 512 whole tiles and 128 tiles in two
+    token halves); outputs of sampled channels (all batches, all tokens) against the oracle."""
     case = c3_case
+    print(f"[c3] plan {ssmscan.plan_info(case.bsz, case.L, case.D, case.N, torch.bfloat16)}", flush=True)
     y, ls = run_gpu(case)
     sel = _sample_channels(case.D, 40, 1)
     y_ref, ls_ref = run_oracle(oracle_mod, case, channels=sel)
