@@ -163,6 +163,22 @@ SSMSCAN_API int ssm_scan_fwd(const void *u, const void *delta, const float *A, c
                  void *y, float *last_state, const ssm_dims *dims,
                  void *workspace, size_t workspace_bytes, void *stream);
 
+/* ssm_scan_fwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same scan, arguments and results
+ * (bitwise those of ssm_scan_fwd on the same plan), with no workspace argument.  Its scratch
+ * (the carry's chunk states or the split schedule's handed-over states) is an array of
+ * 64 MiB inside the library's code object, one copy per device, held until the process ends.
+ * The call allocates and frees nothing.
+ *   flags : SSM_SCAN_SOFTPLUS and SSM_SCAN_EXACT_ZOH; SSM_SCAN_CHECKPOINTS is rejected with
+ *           SSM_ERR_FLAGS (the checkpoints must outlive the call: use ssm_scan_fwd)
+ * A plan whose scratch exceeds 64 MiB (ssm_scan_workspace_bytes) returns SSM_ERR_WORKSPACE
+ * before anything is launched.  All calls on one device share its scratch: calls that overlap
+ * in time on one device (different streams or host threads) race and must not be issued;
+ * calls in one stream are ordered and safe.  Returns SSM_OK or a negative ssm_status. */
+SSMSCAN_API int ssm_scan_fwd_noalloc(const void *u, const void *delta, const float *A, const void *B,
+                                     const void *C, const float *D, const void *z, const float *delta_bias,
+                                     int flags, void *y, float *last_state, const ssm_dims *dims, void *stream);
+
 /* The same scan continued from a given state: h_0 = initial_state instead of zero.  The
  * recurrent form carries the whole history in the state (shakilmahmud.com section 3;
  * urworte.de "Methodische Grundlagen"), so scanning a sequence in pieces, each from the

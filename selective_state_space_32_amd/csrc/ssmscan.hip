@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 
 #include "ssmscan.h"
@@ -552,6 +553,39 @@ void launch_conv_bwd(int width, bool silu, const void *x, const float *w, const 
 
 }  // namespace
 
+// ---- scratch for the entry point that allocates nothing ------------------------------------
+
+// Device scratch of ssm_scan_fwd_noalloc: the carry's chunk states or the split schedule's
+// handed-over states, in the code object itself, one copy per device (held until the process
+// ends).  64 MiB covers the chunk carry of B1 L131072 D2048 N16 (35.7 MB).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// The current device's copy of `scratch` (its device address, looked up once per device with
+// that device current).  In host code the name `scratch` is only a host-side stand-in; kernels
+// get this address.  Returns nullptr (message set) if the lookup fails.
+void *scratch_address() {
+    static std::mutex mu;
+    static void *addr[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        fail(SSM_ERR_HIP, "no current device for the library's scratch");
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            fail(SSM_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+            return nullptr;
+        }
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
 static int scan_impl(const float *h0, const void *u, const void *delta, const float *A, const void *B,
                      const void *C, const float *D, const void *z, const float *delta_bias, int flags,
                      void *y, float *last_state, const ssm_dims *dims, void *workspace, size_t workspace_bytes,
@@ -661,6 +695,24 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
                  void *workspace, size_t workspace_bytes, void *stream) {
     return scan_impl(nullptr, u, delta, A, B, C, D, z, delta_bias, flags, y, last_state, dims, workspace,
                      workspace_bytes, stream);
+}
+
+int ssm_scan_fwd_noalloc(const void *u, const void *delta, const float *A, const void *B, const void *C,
+                         const float *D, const void *z, const float *delta_bias, int flags, void *y,
+                         float *last_state, const ssm_dims *dims, void *stream) {
+    int rc = check_dims(dims, true);
+    if (rc != SSM_OK) return rc;
+    if (flags & SSM_SCAN_CHECKPOINTS)
+        return fail(SSM_ERR_FLAGS, "the checkpoints outlive the call: use ssm_scan_fwd with a workspace");
+    const size_t need = make_plan(dims, device_cus()).bytes;
+    if (need > kNoAllocScratchBytes)
+        return fail(SSM_ERR_WORKSPACE,
+                    "this plan needs %zu bytes of scratch, more than the %zu the library holds per device; "
+                    "use ssm_scan_fwd with a workspace", need, kNoAllocScratchBytes);
+    void *ws = nullptr;
+    if (need > 0 && !(ws = scratch_address())) return SSM_ERR_HIP;
+    return scan_impl(nullptr, u, delta, A, B, C, D, z, delta_bias, flags, y, last_state, dims, ws,
+                     need > 0 ? kNoAllocScratchBytes : 0, stream);
 }
 
 int ssm_scan_fwd_from(const float *initial_state, const void *u, const void *delta, const float *A,

@@ -63,6 +63,8 @@ def _load() -> ctypes.CDLL:
     lib.ssm_scan_plan_info.restype = ctypes.c_int
     lib.ssm_scan_fwd.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int, P, P, D, P, ctypes.c_size_t, P]
     lib.ssm_scan_fwd.restype = ctypes.c_int
+    lib.ssm_scan_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int, P, P, D, P]
+    lib.ssm_scan_fwd_noalloc.restype = ctypes.c_int
     lib.ssm_scan_fwd_from.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_int, P, P, D, P, ctypes.c_size_t, P]
     lib.ssm_scan_fwd_from.restype = ctypes.c_int
     lib.ssm_scan_bwd_workspace_bytes.argtypes = [D]
@@ -232,6 +234,40 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
                                                 exact_zoh=exact_zoh, save_checkpoints=save_checkpoints)
     _check(lib.ssm_scan_fwd(*args))
     return (y, last_state, ws) if save_checkpoints else (y, last_state)
+
+
+def scan_fwd_noalloc(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                     D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                     delta_bias: Optional[torch.Tensor] = None, softplus: bool = True, *,
+                     y: torch.Tensor, last_state: Optional[torch.Tensor] = None, chunk_len: int = 0,
+                     stream=None, exact_zoh: bool = False):
+    """ssm_scan_fwd_noalloc: the scan of scan_fwd with the library's own device scratch.  Nothing
+    is allocated here or in the library: y (and last_state, if wanted) are given by the caller.
+    Returns (y, last_state)."""
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, L, dim)")
+    bsz, L, dim = u.shape
+    N = A.shape[-1]
+    dev, io = u.device, u.dtype
+    _io_code(io)
+    for t, name, shape, dt in ((u, "u", (bsz, L, dim), io), (delta, "delta", (bsz, L, dim), io),
+                               (A, "A", (dim, N), torch.float32), (B, "B", (bsz, L, N), io),
+                               (C, "C", (bsz, L, N), io), (y, "y", (bsz, L, dim), io)):
+        _need(t, name, shape, dt, dev)
+    if D is not None:
+        _need(D, "D", (dim,), torch.float32, dev)
+    if z is not None:
+        _need(z, "z", (bsz, L, dim), io, dev)
+    if delta_bias is not None:
+        _need(delta_bias, "delta_bias", (dim,), torch.float32, dev)
+    if last_state is not None:
+        _need(last_state, "last_state", (bsz, dim, N), torch.float32, dev)
+    dims = make_dims(bsz, L, dim, N, io, chunk_len)
+    _check(lib.ssm_scan_fwd_noalloc(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                    _ptr(delta_bias),
+                                    (SCAN_SOFTPLUS if softplus else 0) | (SCAN_EXACT_ZOH if exact_zoh else 0),
+                                    _ptr(y), _ptr(last_state), ctypes.byref(dims), _stream_handle(stream)))
+    return y, last_state
 
 
 def scan_fwd_call(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,

@@ -296,3 +296,19 @@ def test_plan_follows_the_cu_count(b):
     assert p["split_tiles"] == 128 and p["split_at"] == 512
     # cu_count <= 0 plans for the current device (256 without one)
     assert b.plan_info(8, 2048, 5120, 16, 1)["cu_count"] > 0
+
+
+def test_noalloc_validation(b):
+    """ssm_scan_fwd_noalloc refuses the checkpoints flag and plans needing more scratch than the
+    library holds (64 MiB) before anything is launched."""
+    P = ctypes.c_void_p
+
+    def call(dims, flags=1):
+        return b.lib.ssm_scan_fwd_noalloc(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None, None, flags,
+                                          P(FAKE), None, ctypes.byref(dims), None)
+    assert call(_dims(b), flags=1 | 4) == -8               # SSM_ERR_FLAGS
+    big = _dims(b, batch=1, seqlen=1 << 20, dim=4096, chunk_len=256)   # 4096 chunks x 4096 x 16 states
+    assert b.lib.ssm_scan_workspace_bytes(ctypes.byref(big)) > 64 << 20
+    assert call(big) == -6                                  # SSM_ERR_WORKSPACE
+    assert "64" in b.last_error() or "67108864" in b.last_error()
+    assert call(_dims(b, dstate=3)) == -5
