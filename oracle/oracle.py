@@ -17,16 +17,28 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssm_oracle.c")
-_LIBPATH = os.path.join(_HERE, "liboracle.so")
+# SSM_ORACLE_LIBRARY may name another build of the same source (the sanitized one, see build)
+_SANITIZED = os.environ.get("SSM_ORACLE_LIBRARY", "")
+_LIBPATH = _SANITIZED or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
            "-std=c11", "-Wall", "-Wextra"]
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
 
 
-def build(force: bool = True) -> str:
-    """Compile ssm_oracle.c into liboracle.so with gcc (fp64, no FMA contraction)."""
+def build(force: bool = True, sanitize: bool = False, out: str = "") -> str:
+    """Compile ssm_oracle.c into liboracle.so with gcc (fp64, no FMA contraction).  sanitize:
+    an AddressSanitizer + UBSan build at `out` instead (run Python with gcc's libasan
+    preloaded, ASAN_OPTIONS=detect_leaks=0 and SSM_ORACLE_LIBRARY=<out>)."""
     global _lib
+    if sanitize:
+        out = out or os.path.join(os.path.dirname(_HERE), "_build", "liboracle_asan.so")
+        os.makedirs(os.path.dirname(out), exist_ok=True)
+        subprocess.run(["gcc", *_CFLAGS, *_SAN_FLAGS, _SRC, "-o", out, "-lm"], check=True)
+        return out
+    if _SANITIZED:   # a sanitized build named by the environment is used as it is
+        return _LIBPATH
     if force or not os.path.exists(_LIBPATH):
         tmp = _LIBPATH + ".tmp%d" % os.getpid()
         subprocess.run(["gcc", *_CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
@@ -38,7 +50,7 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIBPATH) or os.path.getmtime(_LIBPATH) < os.path.getmtime(_SRC):
+        if not _SANITIZED and (not os.path.exists(_LIBPATH) or os.path.getmtime(_LIBPATH) < os.path.getmtime(_SRC)):
             build()
         lib = ctypes.CDLL(_LIBPATH)
         P = ctypes.c_void_p

@@ -14,7 +14,8 @@ from typing import Callable, Optional, Tuple
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIBPATH = os.path.join(_PKG, "libssmscan.so")
+# SSMSCAN_LIBRARY may name another build of the same library (the sanitized host build)
+LIBPATH = os.environ.get("SSMSCAN_LIBRARY") or os.path.join(_PKG, "libssmscan.so")
 
 SSM_IO_F32 = 0
 SSM_IO_BF16 = 1

@@ -9,7 +9,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ssmscan.h")
-LIB = os.path.join(ROOT, "selective_state_space_32_amd", "libssmscan.so")
+LIB = os.environ.get("SSMSCAN_LIBRARY") or os.path.join(ROOT, "selective_state_space_32_amd", "libssmscan.so")
 
 
 def declared_symbols():
