@@ -147,10 +147,11 @@ def step(state, u, delta, A, B, C, D=None, z=None,
 
 
 def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus: bool = True, h0=None,
-             dlast=None, threads: Optional[int] = None) -> dict:
-    """fp64 gradients of the scan (from h0, or zero) given dy = dLoss/dy and dlast =
-    dLoss/d(last_state).  Returns a dict with du, ddelta (w.r.t. the delta input), dA, dB,
-    dC, and dD, dz, ddelta_bias, dh0 for the optional inputs that are given."""
+             dlast=None, threads: Optional[int] = None, exact_zoh: bool = False) -> dict:
+    """fp64 gradients of the scan (from h0, or zero; with the exact-ZOH input term if asked)
+    given dy = dLoss/dy and dlast = dLoss/d(last_state).  Returns a dict with du, ddelta
+    (w.r.t. the delta input), dA, dB, dC, and dD, dz, ddelta_bias, dh0 for the optional
+    inputs that are given."""
     u = _f64(u)
     bsz, L, Dch = u.shape
     A = _f64(A)
@@ -170,7 +171,8 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus: b
         out["dh0"] = np.empty((bsz, Dch, N))
     rc = _load().ssm_oracle_scan_bwd(
         bsz, L, Dch, N, _ptr(args["h0"]), _ptr(u), _ptr(args["delta"]), _ptr(A), _ptr(args["B"]), _ptr(args["C"]),
-        _ptr(args["D"]), _ptr(args["z"]), _ptr(args["delta_bias"]), int(bool(softplus)), _ptr(args["dy"]),
+        _ptr(args["D"]), _ptr(args["z"]), _ptr(args["delta_bias"]), int(bool(softplus)) | (2 if exact_zoh else 0),
+        _ptr(args["dy"]),
         _ptr(args["dlast"]), _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
         _ptr(out["dC"]), _ptr(out.get("dD")), _ptr(out.get("dz")), _ptr(out.get("ddelta_bias")),
         _ptr(out.get("dh0")), int(threads or default_threads()))

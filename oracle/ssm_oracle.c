@@ -61,6 +61,17 @@ static double oracle_softplus(double x) {
 /* B_bar / B for one state under exact ZOH: (exp(dt a) - 1) / a, and dt when a = 0. */
 static double oracle_zoh_coef(double dt, double a) { return a != 0.0 ? expm1(dt * a) / a : dt; }
 
+/* d/da of the exact-ZOH coefficient (exp(dt a) - 1) / a: (dt exp(dt a) - (exp(dt a) - 1) / a) / a,
+ * which tends to dt^2 / 2 at a = 0.  Where |dt a| < 1e-3 the closed form loses digits to
+ * cancellation, and the power series of the same function is used instead:
+ * dt^2 (1/2 + x/3 + x^2/8 + x^3/30 + x^4/144), x = dt a (term k: (k+1) x^k / (k+2)!). */
+static double oracle_zoh_coef_da(double dt, double a) {
+    double x = dt * a;
+    if (fabs(x) < 1e-3)
+        return dt * dt * (0.5 + x * (1.0 / 3.0 + x * (1.0 / 8.0 + x * (1.0 / 30.0 + x / 144.0))));
+    return (dt * exp(x) - expm1(x) / a) / a;
+}
+
 static double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
 
 /* sigmoid(x) = 1 / (1 + e^-x), written so that e^x is only taken of x <= 0. */
@@ -177,15 +188,16 @@ int ssm_oracle_step(int64_t S, int64_t D, int64_t N, double *state,
  * are walked backwards with the adjoint G = dLoss/dh_t carried from token t+1
  * (G <- dA_t * lambda_t), where lambda_t = C_t dp_t + G is the full gradient w.r.t. h_t and
  * dp_t = dy_t silu(z_t) the gradient w.r.t. the ungated output:
- *   du_t     = D dp_t + sum_n lambda_t[n] delta_t B_t[n]
- *   ddelta_t = (sum_n lambda_t[n] (A[n] dA_t[n] h_{t-1}[n] + B_t[n] u_t)) * softplus'(x_t)
- *   dA[n]   += lambda_t[n] delta_t dA_t[n] h_{t-1}[n]
- *   dB_t[n] += lambda_t[n] delta_t u_t,   dC_t[n] += dp_t h_t[n]   (summed over channels)
+ *   du_t     = D dp_t + sum_n lambda_t[n] m_t[n] B_t[n]
+ *   ddelta_t = (sum_n lambda_t[n] (A[n] dA_t[n] h_{t-1}[n] + m'_t[n] B_t[n] u_t)) * softplus'(x_t)
+ *   dA[n]   += lambda_t[n] (delta_t dA_t[n] h_{t-1}[n] + dm_t[n]/dA[n] B_t[n] u_t)
+ *   dB_t[n] += lambda_t[n] m_t[n] u_t,   dC_t[n] += dp_t h_t[n]   (summed over channels)
  *   dD      += dp_t u_t,  ddelta_bias += ddelta_t,  dz_t = dy_t p_t silu'(z_t)
  *   dh0      = the adjoint left after token 0
- * with softplus'(x) = sigmoid(x) and silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z))).
- * Shapes and flags as ssm_oracle_scan_from (the exact-ZOH input term is not covered:
- * returns -2); du, ddelta, dz [bsz][L][D]; dA [D][N]; dB, dC
+ * with softplus'(x) = sigmoid(x) and silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z))).  m is
+ * the input term's coefficient: delta itself (m' = 1, dm/dA = 0), or under the exact ZOH
+ * (exp(delta A) - 1) / A (m' = exp(delta A) = dA_t, dm/dA = oracle_zoh_coef_da).
+ * Shapes and flags as ssm_oracle_scan_from; du, ddelta, dz [bsz][L][D]; dA [D][N]; dB, dC
  * [bsz][L][N]; dD, dbias [D]; dh0 [bsz][D][N].  Every output is overwritten; dz, dD,
  * dbias, dh0 may be NULL (not wanted).  Channels d are spread over the threads (each
  * thread owns dA, dD, dbias of its channels); dB and dC are summed over channels from
@@ -199,8 +211,8 @@ int ssm_oracle_scan_bwd(int64_t bsz, int64_t L, int64_t D, int64_t N, const doub
                         double *du, double *ddelta, double *dA, double *dB, double *dC,
                         double *dD, double *dz, double *dbias, double *dh0, int nthreads) {
     if (N > ORACLE_MAX_N || N < 1) return -1;
-    if (flags & ORACLE_EXACT_ZOH) return -2;   /* gradients of the simplified input term only */
     const int softplus_flag = flags & ORACLE_SOFTPLUS;
+    const int zoh = flags & ORACLE_EXACT_ZOH;
     const int64_t nbt = bsz * L * N;
     memset(dB, 0, sizeof(double) * (size_t)nbt);
     memset(dC, 0, sizeof(double) * (size_t)nbt);
@@ -209,10 +221,11 @@ int ssm_oracle_scan_bwd(int64_t bsz, int64_t L, int64_t D, int64_t N, const doub
     {
         double *hist = malloc(sizeof(double) * (size_t)((L > 0 ? L : 1) * N));   /* h_t */
         double *decay = malloc(sizeof(double) * (size_t)((L > 0 ? L : 1) * N));  /* dA_t */
+        double *coef = malloc(sizeof(double) * (size_t)((L > 0 ? L : 1) * N));   /* m_t */
         double *dt = malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
         double *dBl = calloc((size_t)(nbt > 0 ? nbt : 1), sizeof(double));
         double *dCl = calloc((size_t)(nbt > 0 ? nbt : 1), sizeof(double));
-        const int have = hist && decay && dt && dBl && dCl;
+        const int have = hist && decay && coef && dt && dBl && dCl;
 #pragma omp for schedule(static)
         for (int64_t d = 0; d < D; ++d) {
             if (!have) {
@@ -237,8 +250,10 @@ int ssm_oracle_scan_bwd(int64_t bsz, int64_t L, int64_t D, int64_t N, const doub
                     dt[t] = softplus_flag ? oracle_softplus(x) : x;
                     for (int64_t n = 0; n < N; ++n) {
                         double a = exp(dt[t] * A[d * N + n]);
-                        h[n] = a * h[n] + dt[t] * Bt[n] * u[i];
+                        double m = zoh ? oracle_zoh_coef(dt[t], A[d * N + n]) : dt[t];
+                        h[n] = a * h[n] + m * Bt[n] * u[i];
                         decay[t * N + n] = a;
+                        coef[t * N + n] = m;
                         hist[t * N + n] = h[n];
                     }
                 }
@@ -269,11 +284,14 @@ int ssm_oracle_scan_bwd(int64_t bsz, int64_t L, int64_t D, int64_t N, const doub
                         double lam = Ct[n] * dp + G[n];
                         double hprev = t > 0 ? hist[(t - 1) * N + n] : hinit[n];
                         double a = decay[t * N + n];
+                        double m = coef[t * N + n];
+                        double dm_ddt = zoh ? a : 1.0;   /* d m / d delta */
                         dCl[(b * L + t) * N + n] += dp * hist[t * N + n];
-                        dBl[(b * L + t) * N + n] += lam * dt[t] * ut;
-                        du_t = du_t + lam * dt[t] * Bt[n];
-                        dd = dd + lam * (A[d * N + n] * a * hprev + Bt[n] * ut);
+                        dBl[(b * L + t) * N + n] += lam * m * ut;
+                        du_t = du_t + lam * m * Bt[n];
+                        dd = dd + lam * (A[d * N + n] * a * hprev + dm_ddt * Bt[n] * ut);
                         dA[d * N + n] += lam * dt[t] * a * hprev;
+                        if (zoh) dA[d * N + n] += lam * oracle_zoh_coef_da(dt[t], A[d * N + n]) * Bt[n] * ut;
                         G[n] = a * lam;
                     }
                     double x = delta[i];
@@ -300,6 +318,7 @@ int ssm_oracle_scan_bwd(int64_t bsz, int64_t L, int64_t D, int64_t N, const doub
         }
         free(hist);
         free(decay);
+        free(coef);
         free(dt);
         free(dBl);
         free(dCl);

@@ -801,3 +801,65 @@ def check_bwd_closed_forms(scan_from, scan_bwd):
 
 
 BWD_CHECKS = [check_bwd_fd_all_inputs, check_bwd_fd_plain, check_bwd_closed_forms]
+
+
+# --- gradients under the exact zero-order hold ------------------------------------------------
+# scan_from_zoh / scan_bwd_zoh: as scan_from / scan_bwd with the input term
+# (exp(delta A) - 1) / A * B * u (azimuth.plus/paper/mamba, Theorem 1's exact discretisation).
+
+def check_bwd_zoh_fd_all_inputs(scan_from_zoh, scan_bwd_zoh):
+    """Every gradient against central differences of the ZOH forward (A ~ -1: the closed form
+    of d coefficient / dA)."""
+    _check_bwd_fd(scan_from_zoh, scan_bwd_zoh, 74, True)
+
+
+def check_bwd_zoh_fd_plain(scan_from_zoh, scan_bwd_zoh):
+    _check_bwd_fd(scan_from_zoh, scan_bwd_zoh, 75, False)
+
+
+def check_bwd_zoh_fd_small_A(scan_from_zoh, scan_bwd_zoh, seed=76):
+    """Entries of A exactly 0, of size 1e-5 and of size 1e-3 (|delta A| from 1e-6 to a few
+    1e-3: both sides of the series branch of d coefficient / dA), against central differences
+    of the forward (whose coefficient is expm1 based there); the step along A is 1e-8."""
+    c, rng = _bwd_case(seed, True)
+    A = c["A"].copy()
+    A[:, 0] = 0.0
+    A[:, 1] = A[:, 1] * 1e-5
+    A[:, 2:] = A[:, 2:] * 1e-3
+    c["A"] = A
+    g = scan_bwd_zoh(c["u"], c["x"], c["A"], c["B"], c["C"], c["dy"], c["D"], c["z"], c["bias"], True,
+                     c["h0"], c["dlast"])
+
+    def loss(A_):
+        y, last = scan_from_zoh(c["u"], c["x"], A_, c["B"], c["C"], c["D"], c["z"], c["bias"], True, c["h0"])
+        return np.sum(c["dy"] * y) + np.sum(c["dlast"] * last)
+    eps = 1e-8
+    for n in range(A.shape[1]):
+        V = np.zeros_like(A)
+        V[:, n] = rng.standard_normal(A.shape[0])
+        fd = (loss(A + eps * V) - loss(A - eps * V)) / (2 * eps)
+        an = float(np.sum(g["dA"] * V))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (n, fd, an)
+
+
+def check_bwd_zoh_zero_A(scan_from_zoh, scan_bwd_zoh, scan_bwd, seed=77):
+    """At A = 0 the exact-ZOH coefficient is delta itself and the decay 1, so every gradient
+    equals the simplified form's except dA, which gains d coefficient / dA = delta^2 / 2:
+    dA_zoh - dA = sum over batch and tokens of lambda_t delta_t^2 / 2 B_t u_t, with lambda_t
+    = the full gradient w.r.t. h_t (= sum_{s >= t} C_s dp_s + dlast, no decay at A = 0)."""
+    c, _ = _bwd_case(seed, True)
+    c["A"] = np.zeros_like(c["A"])
+    args = (c["u"], c["x"], c["A"], c["B"], c["C"], c["dy"], c["D"], c["z"], c["bias"], True, c["h0"], c["dlast"])
+    gz, gs = scan_bwd_zoh(*args), scan_bwd(*args)
+    for k in gs:
+        if k != "dA":
+            assert _rel(gz[k], gs[k]) < 1e-12, k
+    dt = _softplus_np(c["x"] + c["bias"])
+    dp = c["dy"] * c["z"] / (1.0 + np.exp(-c["z"]))                       # (b, L, D)
+    cdp = c["C"][:, :, None, :] * dp[:, :, :, None]                        # (b, L, D, N)
+    lam = np.flip(np.cumsum(np.flip(cdp, axis=1), axis=1), axis=1) + c["dlast"][:, None, :, :]
+    extra = np.sum(lam * (0.5 * dt * dt * c["u"])[:, :, :, None] * c["B"][:, :, None, :], axis=(0, 1))
+    assert _rel(gz["dA"] - gs["dA"], extra) < 1e-10
+
+
+BWD_ZOH_CHECKS = [check_bwd_zoh_fd_all_inputs, check_bwd_zoh_fd_plain, check_bwd_zoh_fd_small_A]

@@ -35,8 +35,19 @@ MUTANTS = {
     "softplus_wrong_branch": ("if (x > 0.0) return x + log1p(exp(-x));", "if (x > 0.0) return x + log1p(exp(x));"),
     "ignore_initial_state": ("h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;", "h[n] = 0.0;"),
     "bwd_adjoint_without_decay": ("G[n] = a * lam;", "G[n] = lam;"),
-    "bwd_drop_input_term_of_ddelta": ("dd = dd + lam * (A[d * N + n] * a * hprev + Bt[n] * ut);",
+    "bwd_drop_input_term_of_ddelta": ("dd = dd + lam * (A[d * N + n] * a * hprev + dm_ddt * Bt[n] * ut);",
                                       "dd = dd + lam * (A[d * N + n] * a * hprev);"),
+    "bwd_zoh_coefficient_derivative_one": ("double dm_ddt = zoh ? a : 1.0;", "double dm_ddt = 1.0;"),
+    "bwd_zoh_no_coefficient_term_in_dA": (
+        "if (zoh) dA[d * N + n] += lam * oracle_zoh_coef_da(dt[t], A[d * N + n]) * Bt[n] * ut;", ""),
+    "bwd_zoh_dB_with_delta": ("dBl[(b * L + t) * N + n] += lam * m * ut;", "dBl[(b * L + t) * N + n] += lam * dt[t] * ut;"),
+    "bwd_zoh_du_with_delta": ("du_t = du_t + lam * m * Bt[n];", "du_t = du_t + lam * dt[t] * Bt[n];"),
+    "bwd_zoh_coefficient_derivative_sign": ("return (dt * exp(x) - expm1(x) / a) / a;",
+                                            "return (expm1(x) / a - dt * exp(x)) / a;"),
+    "bwd_zoh_series_second_term": ("return dt * dt * (0.5 + x * (1.0 / 3.0 + x * (1.0 / 8.0 + x * (1.0 / 30.0 + x / 144.0))));",
+                                   "return dt * dt * (0.5 + x * (1.0 / 2.0 + x * (1.0 / 8.0 + x * (1.0 / 30.0 + x / 144.0))));"),
+    "bwd_zoh_series_limit": ("return dt * dt * (0.5 + x * (1.0 / 3.0 + x * (1.0 / 8.0 + x * (1.0 / 30.0 + x / 144.0))));",
+                             "return dt * (0.5 + x * (1.0 / 3.0 + x * (1.0 / 8.0 + x * (1.0 / 30.0 + x / 144.0))));"),
     "bwd_current_state_for_previous": ("double hprev = t > 0 ? hist[(t - 1) * N + n] : hinit[n];",
                                        "double hprev = hist[t * N + n];"),
     "bwd_no_softplus_derivative": ("double dx = softplus_flag ? dd * oracle_sigmoid(x) : dd;", "double dx = dd;"),
@@ -126,6 +137,16 @@ def _build_mutant(tmp_path, name, old, new):
         lib.ssm_oracle_scan_from(bsz, L, Dch, N, ptr(h0), ptr(u), ptr(x), ptr(A), ptr(B), ptr(C), ptr(D),
                                  ptr(z), ptr(bias), int(bool(softplus)), ptr(y), ptr(h), 1)
         return y, h
+    def scan_from_zoh(u, x, A, B, C, D, z, bias, softplus, h0):
+        u, x, A, B, C, D, z, bias, h0 = map(f64, (u, x, A, B, C, D, z, bias, h0))
+        bsz, L, Dch = u.shape
+        N = A.shape[1]
+        y = np.empty((bsz, L, Dch))
+        h = np.empty((bsz, Dch, N))
+        lib.ssm_oracle_scan_from(bsz, L, Dch, N, ptr(h0), ptr(u), ptr(x), ptr(A), ptr(B), ptr(C), ptr(D),
+                                 ptr(z), ptr(bias), int(bool(softplus)) | 2, ptr(y), ptr(h), 1)
+        return y, h
+
     def scan_zoh(u, x, A, B, C, D, z, bias, softplus):
         u, x, A, B, C, D, z, bias = map(f64, (u, x, A, B, C, D, z, bias))
         bsz, L, Dch = u.shape
@@ -136,7 +157,7 @@ def _build_mutant(tmp_path, name, old, new):
                             ptr(bias), int(bool(softplus)) | 2, ptr(y), ptr(h), 1)
         return y, h
 
-    def scan_bwd(u, x, A, B, C, dy, D, z, bias, softplus, h0, dlast):
+    def scan_bwd(u, x, A, B, C, dy, D, z, bias, softplus, h0, dlast, zoh=False):
         u, x, A, B, C, dy, D, z, bias, h0, dlast = map(f64, (u, x, A, B, C, dy, D, z, bias, h0, dlast))
         bsz, L, Dch = u.shape
         N = A.shape[1]
@@ -144,7 +165,8 @@ def _build_mutant(tmp_path, name, old, new):
                    dB=np.empty((bsz, L, N)), dC=np.empty((bsz, L, N)), dD=np.empty(Dch),
                    dz=np.empty((bsz, L, Dch)), ddelta_bias=np.empty(Dch), dh0=np.empty((bsz, Dch, N)))
         lib.ssm_oracle_scan_bwd(bsz, L, Dch, N, ptr(h0), ptr(u), ptr(x), ptr(A), ptr(B), ptr(C), ptr(D), ptr(z),
-                                ptr(bias), int(bool(softplus)), ptr(dy), ptr(dlast), ptr(out["du"]),
+                                ptr(bias), int(bool(softplus)) | (2 if zoh else 0), ptr(dy), ptr(dlast),
+                                ptr(out["du"]),
                                 ptr(out["ddelta"]), ptr(out["dA"]), ptr(out["dB"]), ptr(out["dC"]), ptr(out["dD"]),
                                 ptr(out["dz"]), ptr(out["ddelta_bias"]), ptr(out["dh0"]), 1)
         return out
@@ -175,13 +197,16 @@ def _build_mutant(tmp_path, name, old, new):
         lib.ssm_oracle_ssd(bsz, L, H, Pd, G, N, ptr(h0), ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), ptr(z),
                            ptr(dt_bias), int(bool(softplus)), ptr(y), ptr(last), 1)
         return y, last
-    return scan, scan_from, scan_bwd, scan_zoh, conv, conv_bwd, ssd
+    def scan_bwd_zoh(*a):
+        return scan_bwd(*a, zoh=True)
+    return scan, scan_from, scan_bwd, scan_zoh, conv, conv_bwd, ssd, scan_from_zoh, scan_bwd_zoh
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(tmp_path, name):
     old, new = MUTANTS[name]
-    scan, scan_from, scan_bwd, scan_zoh, conv, conv_bwd, ssd = _build_mutant(tmp_path, name, old, new)
+    (scan, scan_from, scan_bwd, scan_zoh, conv, conv_bwd, ssd, scan_from_zoh,
+     scan_bwd_zoh) = _build_mutant(tmp_path, name, old, new)
     caught = []
     with np.errstate(all="ignore"):
         for check in pins.ALL_CHECKS:
@@ -224,4 +249,13 @@ def test_planted_mistake_is_caught(tmp_path, name):
                 check(scan_from, scan_bwd)
             except AssertionError:
                 caught.append(check.__name__)
+        for check in pins.BWD_ZOH_CHECKS:
+            try:
+                check(scan_from_zoh, scan_bwd_zoh)
+            except AssertionError:
+                caught.append(check.__name__)
+        try:
+            pins.check_bwd_zoh_zero_A(scan_from_zoh, scan_bwd_zoh, scan_bwd)
+        except AssertionError:
+            caught.append("check_bwd_zoh_zero_A")
     assert caught, f"mutant {name} passed every pin"

@@ -72,11 +72,6 @@ def test_oracle_ssd_scan_pin(oracle_mod, check):
     check(_ssd(oracle_mod), _scan_from(oracle_mod))
 
 
-def test_oracle_bwd_rejects_zoh(oracle_mod):
-    """The oracle's gradients cover the simplified input term only."""
-    lib = oracle_mod._load()
-    assert lib.ssm_oracle_scan_bwd(1, 1, 1, 1, *([None] * 9), 3, *([None] * 11), 1) == -2
-
 
 def test_step_repeated_equals_scan(oracle_mod):
     """Recurrent form == scan form (urworte.de "Methodische Grundlagen"; shakilmahmud.com
@@ -187,3 +182,26 @@ def _scan_bwd(oracle_mod):
 @pytest.mark.parametrize("check", pins.BWD_CHECKS, ids=lambda c: c.__name__)
 def test_bwd_pins(oracle_mod, check):
     check(_scan_from(oracle_mod), _scan_bwd(oracle_mod))
+
+
+def _scan_from_zoh(oracle_mod):
+    def f(u, x, A, B, C, D, z, bias, softplus, h0):
+        return oracle_mod.scan(u, x, A, B, C, D=D, z=z, delta_bias=bias, softplus=softplus, threads=2, h0=h0,
+                               exact_zoh=True)
+    return f
+
+
+def _scan_bwd_zoh(oracle_mod):
+    def f(u, x, A, B, C, dy, D, z, bias, softplus, h0, dlast):
+        return oracle_mod.scan_bwd(u, x, A, B, C, dy, D=D, z=z, delta_bias=bias, softplus=softplus, h0=h0,
+                                   dlast=dlast, exact_zoh=True)
+    return f
+
+
+@pytest.mark.parametrize("check", pins.BWD_ZOH_CHECKS, ids=lambda c: c.__name__)
+def test_bwd_zoh_pins(oracle_mod, check):
+    check(_scan_from_zoh(oracle_mod), _scan_bwd_zoh(oracle_mod))
+
+
+def test_bwd_zoh_zero_A(oracle_mod):
+    pins.check_bwd_zoh_zero_A(_scan_from_zoh(oracle_mod), _scan_bwd_zoh(oracle_mod), _scan_bwd(oracle_mod))
