@@ -49,11 +49,11 @@
 extern "C" {
 #endif
 
-#define SSMSCAN_VERSION 10
+#define SSMSCAN_VERSION 11
 
 /* Bits of the `flags` argument of the scan entry points. */
 #define SSM_SCAN_SOFTPLUS 1     /* step size = softplus(delta + delta_bias) */
-#define SSM_SCAN_EXACT_ZOH 2    /* exact zero-order-hold input term (forward only) */
+#define SSM_SCAN_EXACT_ZOH 2    /* exact zero-order-hold input term */
 #define SSM_SCAN_CHECKPOINTS 4  /* forward: also store the backward pass's checkpoints in the
                                    workspace; backward: the workspace already holds them */
 
@@ -140,10 +140,10 @@ SSMSCAN_API int ssm_scan_plan_info(const ssm_dims *dims, int cu_count, ssm_plan_
  *   B, C           : [batch][seqlen][dstate] (io_dtype)
  *   A              : [dim][dstate] fp32
  *   D, delta_bias  : [dim] fp32, each may be NULL (= 0)
- *   flags          : SSM_SCAN_SOFTPLUS (apply softplus to delta + delta_bias), and
- *                    SSM_SCAN_EXACT_ZOH (exact zero-order-hold input term) or
- *                    SSM_SCAN_CHECKPOINTS (see workspace); other bits and the pair
- *                    ZOH + CHECKPOINTS are rejected with SSM_ERR_FLAGS
+ *   flags          : SSM_SCAN_SOFTPLUS (apply softplus to delta + delta_bias),
+ *                    SSM_SCAN_EXACT_ZOH (exact zero-order-hold input term) and
+ *                    SSM_SCAN_CHECKPOINTS (see workspace); other bits are rejected with
+ *                    SSM_ERR_FLAGS
  *   y              : output, written completely
  *   last_state     : [batch][dim][dstate] fp32 output h_L, may be NULL
  *   workspace      : device memory of at least ssm_scan_workspace_bytes(dims) bytes, 16-byte
@@ -194,6 +194,24 @@ SSMSCAN_API int ssm_scan_fwd_from(const float *initial_state, const void *u, con
                       int flags, void *y, float *last_state, const ssm_dims *dims, void *workspace,
                       size_t workspace_bytes, void *stream);
 
+/* The scan of a batch of sequences of different lengths, continued from a given state: the
+ * recurrent form runs one token at a time over each sequence's own tokens only
+ * (shakilmahmud.com section 3), so a batch padded to seqlen tokens is scanned sequence by
+ * sequence up to its length, as separate calls of ssm_scan_fwd_from would.
+ *   seq_lens       : [batch] int32 in device memory, 4-byte aligned: sequence b has
+ *                    seq_lens[b] tokens (values outside [0, seqlen] are taken as 0 or
+ *                    seqlen; they are read on the device, so the host never synchronises)
+ *   y              : tokens t < seq_lens[b] are written; later tokens of y are left untouched
+ *                    (no input past a sequence's length is read either)
+ *   last_state     : the state after seq_lens[b] tokens (the initial state for length 0)
+ * All other arguments (dims->seqlen is the padded length), the workspace size, the plans and
+ * the errors are those of ssm_scan_fwd_from; seq_lens NULL returns SSM_ERR_NULL. */
+SSMSCAN_API int ssm_scan_fwd_varlen(const float *initial_state, const int32_t *seq_lens, const void *u,
+                                    const void *delta, const float *A, const void *B, const void *C,
+                                    const float *D, const void *z, const float *delta_bias, int flags, void *y,
+                                    float *last_state, const ssm_dims *dims, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
 /* Bytes of device workspace ssm_scan_bwd needs: the checkpointed states, one per 8
  * tokens (batch * ceil(seqlen / 8) * dim * dstate fp32, 256-byte aligned).  Returns 0 for
  * an invalid or empty problem. */
@@ -204,8 +222,9 @@ SSMSCAN_API size_t ssm_scan_bwd_workspace_bytes(const ssm_dims *dims);
  * pass, recomputing the states from checkpoints instead of storing them
  * (azimuth.plus/paper/mamba, hardware-aware algorithm section).
  *   inputs          : exactly those of the forward call (same shapes, dtypes, NULLs);
- *                     flags may hold SSM_SCAN_SOFTPLUS and SSM_SCAN_CHECKPOINTS (the
- *                     gradients of the exact-ZOH input term are not provided: SSM_ERR_FLAGS)
+ *                     flags may hold SSM_SCAN_SOFTPLUS, SSM_SCAN_EXACT_ZOH (the gradients
+ *                     of the exact zero-order-hold scan; with SSM_SCAN_CHECKPOINTS the
+ *                     forward call must have had it too) and SSM_SCAN_CHECKPOINTS
  *   dy              : [batch][seqlen][dim] (io_dtype)
  *   dlast_state     : [batch][dim][dstate] fp32, or NULL (= 0)
  *   du, ddelta      : [batch][seqlen][dim] (io_dtype) outputs; ddelta is the gradient with

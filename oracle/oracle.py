@@ -124,6 +124,34 @@ def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = Tr
     return y, last
 
 
+def scan_varlen(u, delta, A, B, C, seq_lens, D=None, z=None, delta_bias=None, softplus: bool = True,
+                threads: Optional[int] = None, h0=None, exact_zoh: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """The scan of sequences of different lengths: sequence b over its first seq_lens[b] tokens
+    (clamped to [0, L]) only, each from h0[b] (or zero), exactly as the scan of that sequence
+    alone (the recurrent form, shakilmahmud.com section 3).  Returns (y, last_state): y
+    (bsz, L, Dch) with NaN at the tokens past each length (never computed), last_state the
+    state after each sequence's own length."""
+    u = _f64(u)
+    bsz, L, Dch = u.shape
+    A = _f64(A)
+    N = A.shape[1]
+    y = np.full((bsz, L, Dch), np.nan)
+    last = np.empty((bsz, Dch, N))
+    for b in range(bsz):
+        lb = int(min(max(int(seq_lens[b]), 0), L))
+        hb = None if h0 is None else np.asarray(h0, np.float64)[b:b + 1]
+        if lb == 0:
+            last[b] = 0.0 if hb is None else hb[0]
+            continue
+        sl = (slice(b, b + 1), slice(0, lb))
+        yb, lsb = scan(u[sl], np.asarray(delta)[sl], A, np.asarray(B)[sl], np.asarray(C)[sl], D=D,
+                       z=None if z is None else np.asarray(z)[sl], delta_bias=delta_bias, softplus=softplus,
+                       threads=threads, h0=hb, exact_zoh=exact_zoh)
+        y[b, :lb] = yb[0]
+        last[b] = lsb[0]
+    return y, last
+
+
 def step(state, u, delta, A, B, C, D=None, z=None,
          threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
     """fp64 single-token step.  state: (S, Dch, N); u, delta, z: (S, Dch); B, C: (S, N).

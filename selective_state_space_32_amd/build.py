@@ -13,32 +13,58 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssmscan.so")
-SOURCES = ["ssmscan.hip"]   # includes every header in csrc/
+def sources():
+    """The library's translation units: the C ABI (ssmscan.hip) and the instantiations of the
+    launch templates (inst_*.hip), compiled separately and in parallel."""
+    return sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
     # packed fp32 instructions stay disabled: every fp32 operation is a plain VALU op
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fvisibility=hidden", "-Wall",
 ]
 
 
+def _quiet(stderr: str) -> str:
+    return "\n".join(l for l in (stderr or "").splitlines() if "packed-fp32-ops" not in l and "--hip-link" not in l)
+
+
+def _compile_all(flags, objdir: str, out: str, verbose: bool, jobs: int = 0) -> str:
+    os.makedirs(objdir, exist_ok=True)
+    srcs = sources()
+    objs = [os.path.join(objdir, os.path.splitext(f)[0] + ".o") for f in srcs]
+
+    def one(src_obj):
+        src, obj = src_obj
+        cmd = [HIPCC, *flags, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        return src, r.returncode, _quiet(r.stderr)
+
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = jobs or max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", "0") or 0) or (os.cpu_count() or 1)))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        for src, rc, err in ex.map(one, zip(srcs, objs)):
+            if rc != 0:
+                raise RuntimeError(f"hipcc failed on {src}:\n{err}")
+            if verbose and err.strip():
+                print(err, file=sys.stderr)
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *flags, "-shared", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc link failed:\n" + _quiet(r.stderr))
+    os.replace(tmp, out)
+    return out
+
+
 def build(verbose: bool = False) -> str:
     """Compile the HIP sources into libssmscan.so next to this file (always recompiles)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in (r.stderr or "").splitlines()
-                    if "packed-fp32-ops" not in l and "--hip-link" not in l)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + err)
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    return _compile_all(FLAGS, os.path.join(ROOT, "_build", "obj"), LIB, verbose)
 
 
 def build_sanitized(out: str = "") -> str:
@@ -51,16 +77,9 @@ def build_sanitized(out: str = "") -> str:
         SSMSCAN_LIBRARY=<that path> python -m pytest tests/test_abi.py
     """
     out = out or os.path.join(ROOT, "_build", "libssmscan_asan.so")
-    os.makedirs(os.path.dirname(out), exist_ok=True)
-    cmd = [HIPCC, "-O1", "-g", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
-           "-fno-omit-frame-pointer", "-fvisibility=hidden", "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc (sanitized host build) failed:\n" + r.stderr)
-    return out
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+                                                 "-fsanitize=undefined", "-fno-omit-frame-pointer"]
+    return _compile_all(flags, os.path.join(ROOT, "_build", "obj_asan"), out, verbose=False)
 
 
 def asan_runtime() -> str:

@@ -12,6 +12,10 @@
 //   dB_t[n]   += lambda_t[n] delta_t u_t,   dC_t[n] += dp_t h_t[n]   (over channels)
 //   dD        += dp_t u_t,   d delta_bias += d x_t,   dz_t = dy_t p_t silu'(z_t)
 //   d h0       = the adjoint left after token 0.
+// With the exact zero-order hold (ZOH) the input term's coefficient delta becomes
+// m = (exp(delta A) - 1) / A, so du_t = D dp_t + sum_n lambda m B, dB += lambda m u, the input
+// part of d delta_t is sum_n lambda exp(delta A) B u (d m / d delta = exp(delta A)) and dA gains
+// lambda (d m / dA) B u, with d m / dA from zoh_weight_da.
 //
 // Layout: one workgroup per (sequence, 64-channel tile), K waves of S states, lane =
 // channel (as in the forward kernel).  A forward pass in checkpoint mode first stores the
@@ -66,7 +70,7 @@ __device__ __forceinline__ void wave_lds_fence() {
 
 // Register budget: with 4 waves per workgroup three workgroups share a CU (LDS allows it),
 // which needs at most 168 VGPRs per lane.
-template <int N, typename IO, bool VEC>
+template <int N, typename IO, bool VEC, bool ZOH = false>
 __global__ void __launch_bounds__(64 * BwdShape<N>::K)
 __attribute__((amdgpu_waves_per_eu(BwdShape<N>::K == 4 ? 3 : 1)))
 scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO *__restrict__ z,
@@ -90,7 +94,7 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
     using VIO = vec<V, IO>;
     constexpr int W = VEC ? V * (int)sizeof(IO) / 4 : 1;
 
-    __shared__ f32x2_t s_dk[T][kChanTile];         // (delta, delta*u) per (token, channel)
+    __shared__ f32x2_t s_dk[T][kChanTile];         // (delta, delta*u) per (token, channel); (delta, u) with ZOH
     __shared__ f32x2_t s_ud[T][kChanTile];         // (u, dp)
     __shared__ float s_p[K][T][kChanTile];         // partial readouts, per wave
     __shared__ float s_du[K][T][kChanTile];        // partial du, per wave
@@ -118,10 +122,11 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
     const bool gated = z != nullptr;
     const int64_t n_ckpt = (L + kCkptEvery - 1) / kCkptEvery;
 
-    float a2[S], G[S], dA_acc[S];   // a2 = A log2(e)
+    float a2[S], G[S], dA_acc[S], inv_a[ZOH ? S : 1];   // a2 = A log2(e); 1 / A for the exact ZOH
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         a2[s] = act ? A[d * N + w * S + s] * kLog2e : 0.0f;
+        if constexpr (ZOH) inv_a[s] = act ? 1.0f / A[d * N + w * S + s] : 0.0f;
         G[s] = (act && dlast) ? dlast[((int64_t)b * D + d) * N + w * S + s] : 0.0f;
         dA_acc[s] = 0.0f;
     }
@@ -210,7 +215,7 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
                     gz = yy * (sz * fmaf(zz, 1.0f - sz, 1.0f));
                 }
                 const float dp = live ? yy * g : 0.0f;
-                s_dk[tt][cq + v] = f32x2_t{dl, dl * uu};
+                s_dk[tt][cq + v] = f32x2_t{dl, ZOH ? uu : dl * uu};
                 s_ud[tt][cq + v] = f32x2_t{uu, dp};
                 kgz[p][v] = gz;
                 ksg[p][v] = sg;
@@ -239,8 +244,12 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
                 float acc = 0.0f;
 #pragma unroll
                 for (int s = 0; s < S; ++s) {
-                    ex[tt][s] = hw_exp2(v.x * a2[s]);
-                    h[s] = fmaf(ex[tt][s], h[s], v.y * s_bc[tt][0][w * S + s]);
+                    // (the forward kernel's arithmetic, in its order)
+                    const float ya = v.x * a2[s];
+                    ex[tt][s] = hw_exp2(ya);
+                    float bu = v.y * s_bc[tt][0][w * S + s];
+                    if constexpr (ZOH) bu *= zoh_weight(ya, ex[tt][s], v.x, inv_a[s]);
+                    h[s] = fmaf(ex[tt][s], h[s], bu);
                     hist[tt][s] = h[s];
                     acc = fmaf(s_bc[tt][1][w * S + s], h[s], acc);
                 }
@@ -283,7 +292,7 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
                 Cs[s] = s_bc[tt][1][w * S + s];
             }
             if (tt < T - 1) transpose();
-            float q = 0.0f, ddA = 0.0f;   // ddA = sum_n A r / ln 2
+            float q = 0.0f, qe = 0.0f, ddA = 0.0f;   // ddA = sum_n A r / ln 2
 #pragma unroll
             for (int s = 0; s < S; ++s) {
                 const float lam = fmaf(Cs[s], ud.y, G[s]);
@@ -291,12 +300,24 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
                 const float r = G[s] * (tt > 0 ? hist[tt > 0 ? tt - 1 : 0][s] : hs[s]);
                 dA_acc[s] = fmaf(dk.x, r, dA_acc[s]);
                 ddA = fmaf(a2[s], r, ddA);
-                q = fmaf(lam, Bs[s], q);
-                rvp[s] = lam * dk.y;                 // dB contribution
+                if constexpr (ZOH) {
+                    // m and d m / dA from the recomputed decay (dk.y = u)
+                    const float ya = dk.x * a2[s];
+                    const float m = zoh_weight(ya, ex[tt][s], dk.x, inv_a[s]);
+                    const float mda = zoh_weight_da(ya, ex[tt][s], m, dk.x, inv_a[s]);
+                    const float lm = lam * m;
+                    dA_acc[s] = fmaf(lam * mda, dk.y * Bs[s], dA_acc[s]);
+                    q = fmaf(lm, Bs[s], q);          // du: sum lambda m B
+                    qe = fmaf(G[s], Bs[s], qe);      // d delta: u sum lambda exp(delta A) B
+                    rvp[s] = lm * dk.y;              // dB contribution
+                } else {
+                    q = fmaf(lam, Bs[s], q);
+                    rvp[s] = lam * dk.y;             // dB contribution
+                }
                 rvp[S + s] = ud.y * hist[tt][s];     // dC contribution
             }
-            s_du[w][tt][lane] = dk.x * q;
-            s_dd[w][tt][lane] = fmaf(ud.x, q, ddA * kLn2);
+            s_du[w][tt][lane] = ZOH ? q : dk.x * q;
+            s_dd[w][tt][lane] = fmaf(ud.x, ZOH ? qe : q, ddA * kLn2);
             if (tt < T - 1) finish(tt + 1);
         }
         transpose();

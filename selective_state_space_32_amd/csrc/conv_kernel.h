@@ -173,7 +173,7 @@ constexpr int kConvBwdWaves = 4;   // runs per workgroup, one per wave
 constexpr int kConvBwdVec = 2;     // channels per thread (4-byte bf16 / 8-byte fp32 accesses)
 
 // Zeros two arrays in one launch (the sums the backward adds into).
-__global__ void __launch_bounds__(256) fill_zero2_kernel(float *__restrict__ p, int64_t n, float *__restrict__ q,
+static __global__ void __launch_bounds__(256) fill_zero2_kernel(float *__restrict__ p, int64_t n, float *__restrict__ q,
                                                          int64_t m) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n) p[i] = 0.0f;

@@ -1,0 +1,383 @@
+// libssmscan's kernel launches: the schedule (Plan) and, per operation, the templates that
+// pick a kernel instantiation for the arguments and launch it on the caller's stream.  The
+// templates are instantiated in the inst_*.hip translation units (compiled in parallel) and
+// called from the C ABI in ssmscan.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <algorithm>
+#include <cstdint>
+#include <type_traits>
+
+#include "ssmscan.h"
+#include "carry_kernel.h"
+#include "scan_kernels.h"
+#include "step_kernel.h"
+#include "bwd_kernel.h"
+#include "conv_kernel.h"
+#include "ssd_kernel.h"
+
+namespace ssmlib {
+
+// The status and message of the calling thread's last failure (ssm_last_error); defined in
+// ssmscan.hip.
+int fail(int code, const char *fmt, ...);
+int ok();
+// How long a second half of the split schedule waits for its hand-over (ssmscan.hip).
+unsigned long long handover_wait_ticks();
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+enum Schedule { kGrid = 0, kCarry = 1, kSplit = 2 };
+
+struct Plan {
+    int schedule = kGrid;
+    int64_t nchunk = 1;      // chunks per sequence (work items per tile)
+    int64_t chunk_len = 0;   // tokens per chunk
+    int64_t n_full = 0, n_split = 0, l_mid = 0;   // the split schedule
+    size_t off_cstate = 0, off_cdsum = 0, off_hand = 0, off_flags = 0, bytes = 0;
+};
+
+// One workgroup per (sequence, 64-channel tile) fills the GPU once there are about two
+// tiles per CU or more; with fewer tiles the tokens are split into chunks as well (the
+// chunk carry), which costs an extra summary pass over all but the last chunk.
+// align_ckpt: the call also stores the backward pass's checkpoints (the state before every
+// kCkptEvery-th token); each chunk's first token must then be one of those points, so a
+// carry chunk length is rounded up to a multiple of kCkptEvery (fewer chunks, never more
+// workspace than the plan without the flag).
+// Kernel shape per state size: S states per wave (K = N/S waves per workgroup) and T
+// tokens per LDS tile.
+template <int N> struct ScanShape;
+template <> struct ScanShape<1> { static constexpr int S = 1, T = 32; };
+template <> struct ScanShape<2> { static constexpr int S = 2, T = 32; };
+template <> struct ScanShape<4> { static constexpr int S = 4, T = 32; };
+template <> struct ScanShape<8> { static constexpr int S = 4, T = 32; };
+template <> struct ScanShape<16> { static constexpr int S = 4, T = 32; };
+
+// The fused causal convolution of the scan's input (conv entry point only).
+struct ConvArgs {
+    const float *w;
+    const float *b;
+    void *u_out;
+};
+
+// (CK: the full pass also stores the backward pass's checkpoints to ckpt)
+template <int N, typename IO, bool VEC, bool ZOH, int CW = 0, bool CK = false>
+void launch_scan_kernels(const IO *u, const IO *dl, const float *A, const IO *B, const IO *C, const float *Dv,
+                         const IO *z, const float *bias, int softplus, const float *h0, IO *y, float *last_state,
+                         const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st,
+                         const ConvArgs &cv = ConvArgs{nullptr, nullptr, nullptr}, float *ckpt = nullptr,
+                         const int32_t *seq_lens = nullptr) {
+    constexpr int S = ScanShape<N>::S;
+    constexpr int T = ScanShape<N>::T;
+    constexpr int K = N / S;
+    const int64_t bsz = dm->batch, L = dm->seqlen, D = dm->dim;
+    const int tiles_per_b = (int)((D + ssm::kChanTile - 1) / ssm::kChanTile);
+    const int n_tiles = (int)(bsz * tiles_per_b);
+    const dim3 block(64 * K);
+    float *cstate = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_cstate);
+    float *cdsum = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_cdsum);
+    const int64_t cl = p.chunk_len;
+    const int nc = (int)p.nchunk;
+    if (p.schedule == kCarry) {
+        // (CK also here: with the fused convolution, the training forward scans u rounded to the
+        // I/O type, so the summary pass must carry the states of that same u)
+        hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kSummary, VEC, ZOH, CW, CK>),
+                           dim3((unsigned)n_tiles, (unsigned)(nc - 1)), block, 0, st, u, dl, (const IO *)nullptr,
+                           (IO *)nullptr, A, (const float *)nullptr, bias, B, C, (const float *)nullptr,
+                           (float *)nullptr, cstate, cdsum, L, D, tiles_per_b, n_tiles, cl, nc, softplus, cv.w, cv.b,
+                           (IO *)nullptr, (float *)nullptr, 0, 0, (int64_t)0, (float *)nullptr, (int *)nullptr, 0ull,
+                           seq_lens);
+        const int col_tiles = (int)((D * N + 63) / 64);
+        hipLaunchKernelGGL((ssm::carry_scan_kernel<N>), dim3((unsigned)(bsz * col_tiles)), dim3(256), 0, st,
+                           cstate, (const float *)cdsum, A, h0, D, nc, col_tiles);
+    }
+    if (p.schedule == kSplit) {
+        // the hand-over flags start at zero (a fill kernel: no memset node if the caller captures a graph)
+        int *flags = reinterpret_cast<int *>(static_cast<char *>(ws) + p.off_flags);
+        float *hand = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_hand);
+        hipLaunchKernelGGL(ssm::fill_zero_kernel<int>, dim3((unsigned)((p.n_split + 255) / 256)), dim3(256), 0, st, flags,
+                           p.n_split);
+        hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kFull, VEC, ZOH, CW, CK>),
+                           dim3((unsigned)(p.n_full + 2 * p.n_split), 1), block, 0, st, u, dl, z, y, A, Dv, bias, B, C,
+                           h0, last_state, cstate, cdsum, L, D, tiles_per_b, n_tiles, cl, nc, softplus, cv.w, cv.b,
+                           static_cast<IO *>(cv.u_out), ckpt, (int)p.n_full, (int)p.n_split, p.l_mid, hand, flags,
+                           handover_wait_ticks(), seq_lens);
+        return;
+    }
+    hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kFull, VEC, ZOH, CW, CK>),
+                       dim3((unsigned)n_tiles, (unsigned)nc), block, 0, st, u, dl, z, y, A, Dv, bias, B, C, h0,
+                       last_state, cstate, cdsum, L, D, tiles_per_b, n_tiles, cl, nc, softplus, cv.w, cv.b,
+                       static_cast<IO *>(cv.u_out), ckpt, 0, 0, (int64_t)0, (float *)nullptr, (int *)nullptr, 0ull,
+                       seq_lens);
+}
+
+template <int N, typename IO>
+int launch_scan(const void *u, const void *delta, const float *A, const void *B, const void *C,
+                const float *Dv, const void *z, const float *bias, int flags, const float *h0, void *y,
+                float *last_state, const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st,
+                const ConvArgs *cv, float *ckpt, const int32_t *seq_lens) {
+    const int softplus = (flags & SSM_SCAN_SOFTPLUS) != 0;
+    const bool zoh = (flags & SSM_SCAN_EXACT_ZOH) != 0;
+    const IO *u_ = static_cast<const IO *>(u);
+    const IO *dl_ = static_cast<const IO *>(delta);
+    const IO *z_ = static_cast<const IO *>(z);
+    const IO *B_ = static_cast<const IO *>(B);
+    const IO *C_ = static_cast<const IO *>(C);
+    IO *y_ = static_cast<IO *>(y);
+    // 16-byte prep/epilogue accesses need whole groups of 8 channels and aligned rows
+    const bool vec = dm->dim % 8 == 0 && aligned(u, 16) && aligned(delta, 16) && aligned(y, 16) &&
+                     (!z || aligned(z, 16));
+    if (cv) {
+        // the fused convolution (width 4; no exact ZOH, checked by the caller), with or without
+        // the backward pass's checkpoints
+        if (vec && ckpt)
+            launch_scan_kernels<N, IO, true, false, 4, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_,
+                                                             last_state, dm, p, ws, st, *cv, ckpt, seq_lens);
+        else if (ckpt)
+            launch_scan_kernels<N, IO, false, false, 4, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_,
+                                                              last_state, dm, p, ws, st, *cv, ckpt, seq_lens);
+        else if (vec)
+            launch_scan_kernels<N, IO, true, false, 4>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state,
+                                                       dm, p, ws, st, *cv, nullptr, seq_lens);
+        else
+            launch_scan_kernels<N, IO, false, false, 4>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_,
+                                                        last_state, dm, p, ws, st, *cv, nullptr, seq_lens);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+        return ok();
+    }
+    if (ckpt) {
+        // the training forward: the backward pass's checkpoints too
+        const ConvArgs none{nullptr, nullptr, nullptr};
+        if (vec && zoh)
+            launch_scan_kernels<N, IO, true, true, 0, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_,
+                                                            last_state, dm, p, ws, st, none, ckpt, seq_lens);
+        else if (vec)
+            launch_scan_kernels<N, IO, true, false, 0, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_,
+                                                             last_state, dm, p, ws, st, none, ckpt, seq_lens);
+        else if (zoh)
+            launch_scan_kernels<N, IO, false, true, 0, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_,
+                                                             last_state, dm, p, ws, st, none, ckpt, seq_lens);
+        else
+            launch_scan_kernels<N, IO, false, false, 0, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_,
+                                                              last_state, dm, p, ws, st, none, ckpt, seq_lens);
+    } else if (vec && zoh)
+        launch_scan_kernels<N, IO, true, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state, dm, p,
+                                               ws, st, ConvArgs{nullptr, nullptr, nullptr}, nullptr, seq_lens);
+    else if (vec)
+        launch_scan_kernels<N, IO, true, false>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state, dm,
+                                                p, ws, st, ConvArgs{nullptr, nullptr, nullptr}, nullptr, seq_lens);
+    else if (zoh)
+        launch_scan_kernels<N, IO, false, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state, dm,
+                                                p, ws, st, ConvArgs{nullptr, nullptr, nullptr}, nullptr, seq_lens);
+    else
+        launch_scan_kernels<N, IO, false, false>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state, dm,
+                                                 p, ws, st, ConvArgs{nullptr, nullptr, nullptr}, nullptr, seq_lens);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+template <int N, typename IO>
+int launch_step(float *state, const void *u, const void *delta, const float *A, const void *B,
+                const void *C, const float *Dv, const void *z, void *y, const ssm_dims *dm, hipStream_t st) {
+    constexpr int G = N >= 4 ? N / 4 : 1;
+    constexpr int SP = ssm::kStepSeqPerThread;
+    const int64_t threads = (dm->batch + SP - 1) / SP * dm->dim * G;
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    // vector reads of the A, B, C slices of a lane need them aligned to the slice
+    const size_t es = sizeof(IO);
+    const bool vp = N >= 4 && aligned(A, 16) && aligned(B, 4 * es) && aligned(C, 4 * es);
+    const IO *u_ = static_cast<const IO *>(u), *dl_ = static_cast<const IO *>(delta);
+    const IO *B_ = static_cast<const IO *>(B), *C_ = static_cast<const IO *>(C), *z_ = static_cast<const IO *>(z);
+    IO *y_ = static_cast<IO *>(y);
+    if (vp)
+        hipLaunchKernelGGL((ssm::step_kernel<N, IO, true>), grid, dim3(256), 0, st, state, u_, dl_, A, B_, C_, Dv,
+                           z_, y_, dm->batch, dm->dim);
+    else
+        hipLaunchKernelGGL((ssm::step_kernel<N, IO, false>), grid, dim3(256), 0, st, state, u_, dl_, A, B_, C_, Dv,
+                           z_, y_, dm->batch, dm->dim);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+template <typename TP>
+void fill_zero(TP *p, int64_t n, hipStream_t st) {
+    if (p && n > 0)
+        hipLaunchKernelGGL(ssm::fill_zero_kernel<TP>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
+}
+
+struct BwdArgs {
+    const float *h0;
+    const void *u, *delta;
+    const float *A;
+    const void *B, *C;
+    const float *D;
+    const void *z;
+    const float *bias;
+    int softplus;
+    const void *dy;
+    const float *dlast;
+    void *du, *ddelta;
+    float *dA, *dB, *dC, *dD;
+    void *dz;
+    float *dbias, *dh0;
+    bool ckpt_given;   // the workspace already holds the checkpoints (written by the training forward)
+    bool zoh;          // the exact zero-order-hold input term
+};
+
+template <int N, typename IO>
+int launch_bwd(const BwdArgs &a, const ssm_dims *dm, void *ws, hipStream_t st) {
+    constexpr int S = ScanShape<N>::S, T = ScanShape<N>::T, K = N / S;
+    constexpr int KB = ssm::BwdShape<N>::K;
+    const int64_t bsz = dm->batch, L = dm->seqlen, D = dm->dim;
+    const int tiles_per_b = (int)((D + ssm::kChanTile - 1) / ssm::kChanTile);
+    const int n_tiles = (int)(bsz * tiles_per_b);
+    const IO *u = static_cast<const IO *>(a.u), *dl = static_cast<const IO *>(a.delta);
+    const IO *B = static_cast<const IO *>(a.B), *C = static_cast<const IO *>(a.C);
+    const IO *z = static_cast<const IO *>(a.z), *dy = static_cast<const IO *>(a.dy);
+    IO *du = static_cast<IO *>(a.du), *ddl = static_cast<IO *>(a.ddelta), *dz = static_cast<IO *>(a.dz);
+    float *ckpt = static_cast<float *>(ws);
+    // forward in checkpoint mode: the state before every kCkptEvery-th token (unless the
+    // training forward has stored them already)
+    const bool vf = D % 8 == 0 && aligned(u, 16) && aligned(dl, 16);
+    if (!a.ckpt_given) {
+        auto ckpt_pass = [&](auto vec_c, auto zoh_c) {
+            hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kCheckpoint, decltype(vec_c)::value,
+                                                       decltype(zoh_c)::value>),
+                               dim3((unsigned)n_tiles, 1), dim3(64 * K), 0, st, u, dl, (const IO *)nullptr,
+                               (IO *)nullptr, a.A, (const float *)nullptr, a.bias, B, C, a.h0, (float *)nullptr, ckpt,
+                               (float *)nullptr, L, D, tiles_per_b, n_tiles, L, 1, a.softplus);
+        };
+        using T1 = std::true_type;
+        using F0 = std::false_type;
+        if (vf && a.zoh) ckpt_pass(T1{}, T1{});
+        else if (vf) ckpt_pass(T1{}, F0{});
+        else if (a.zoh) ckpt_pass(F0{}, T1{});
+        else ckpt_pass(F0{}, F0{});
+    }
+    // the reverse walk; 16-byte (or 8-byte) element access when every (token, channel) tensor allows it
+    const bool vb = D % 8 == 0 && aligned(u, 16) && aligned(dl, 16) && aligned(dy, 16) && aligned(du, 16) &&
+                    aligned(ddl, 16) && (!z || (aligned(z, 16) && aligned(dz, 16)));
+    auto walk = [&](auto vec_c, auto zoh_c) {
+        hipLaunchKernelGGL((ssm::scan_bwd_kernel<N, IO, decltype(vec_c)::value, decltype(zoh_c)::value>),
+                           dim3((unsigned)n_tiles), dim3(64 * KB), 0, st, u, dl, z, dy, a.A, a.D, a.bias, B, C, ckpt,
+                           a.dlast, du, ddl, dz, a.dA, a.dB, a.dC, a.dD, a.dbias, a.dh0, L, D, tiles_per_b,
+                           a.softplus);
+    };
+    if (vb && a.zoh) walk(std::true_type{}, std::true_type{});
+    else if (vb) walk(std::true_type{}, std::false_type{});
+    else if (a.zoh) walk(std::false_type{}, std::true_type{});
+    else walk(std::false_type{}, std::false_type{});
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+// --- the causal depthwise convolution of the block's main branch ---------------------------
+
+template <typename IO, int W, bool VEC, bool SILU>
+void launch_conv_w(const IO *x, const float *w, const float *bias, const IO *st_in, IO *out, IO *st_out,
+                   const ssm_dims *dm, hipStream_t st) {
+    constexpr int V = VEC ? ssm::kConvVec : 1;
+    const int64_t bsz = dm->batch, L = dm->seqlen, D = dm->dim;
+    // a state updated in place is read and written by the same thread: one run per sequence
+    const bool in_place = st_out && st_out == st_in && W > 1;
+    const int64_t R = in_place ? L : ssm::kConvRun;
+    const int64_t runs = (L + R - 1) / R;
+    const int64_t groups = D / V;
+    const int64_t pairs = bsz * runs;
+    const dim3 grid((unsigned)((groups + 255) / 256), (unsigned)std::min<int64_t>(pairs, 65535));
+    hipLaunchKernelGGL((ssm::conv1d_kernel<IO, W, V, VEC, SILU>), grid, dim3(256), 0, st, x, w, bias, st_in, out,
+                       st_out, L, D, groups, runs, pairs, (int)R);
+}
+
+template <typename IO, bool VEC, bool SILU>
+void launch_conv_v(int width, const IO *x, const float *w, const float *bias, const IO *st_in, IO *out,
+                   IO *st_out, const ssm_dims *dm, hipStream_t st) {
+    switch (width) {
+        case 1: launch_conv_w<IO, 1, VEC, SILU>(x, w, bias, st_in, out, st_out, dm, st); break;
+        case 2: launch_conv_w<IO, 2, VEC, SILU>(x, w, bias, st_in, out, st_out, dm, st); break;
+        case 3: launch_conv_w<IO, 3, VEC, SILU>(x, w, bias, st_in, out, st_out, dm, st); break;
+        default: launch_conv_w<IO, 4, VEC, SILU>(x, w, bias, st_in, out, st_out, dm, st); break;
+    }
+}
+
+template <typename IO>
+int launch_conv(int width, bool silu, const void *x, const float *w, const float *bias, const void *st_in,
+                void *out, void *st_out, const ssm_dims *dm, hipStream_t st) {
+    const IO *x_ = static_cast<const IO *>(x);
+    const IO *si = static_cast<const IO *>(st_in);
+    IO *o = static_cast<IO *>(out);
+    IO *so = static_cast<IO *>(st_out);
+    const size_t va = ssm::kConvVec * sizeof(IO);   // bytes of one vector access
+    const bool vec = dm->dim % ssm::kConvVec == 0 && aligned(x, va) && aligned(out, va) &&
+                     (!st_in || aligned(st_in, va)) && (!st_out || aligned(st_out, va));
+    if (vec && silu) launch_conv_v<IO, true, true>(width, x_, w, bias, si, o, so, dm, st);
+    else if (vec) launch_conv_v<IO, true, false>(width, x_, w, bias, si, o, so, dm, st);
+    else if (silu) launch_conv_v<IO, false, true>(width, x_, w, bias, si, o, so, dm, st);
+    else launch_conv_v<IO, false, false>(width, x_, w, bias, si, o, so, dm, st);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+template <typename IO, int W, bool VEC, bool SILU>
+void launch_conv_bwd_w(const IO *x, const float *w, const float *bias, const IO *st_in, const IO *dout, IO *dx,
+                       float *dw, float *dbias, IO *dst, const ssm_dims *dm, hipStream_t st) {
+    constexpr int V = VEC ? ssm::kConvBwdVec : 1;
+    const int64_t bsz = dm->batch, L = dm->seqlen, D = dm->dim;
+    const int64_t R = ssm::kConvBwdRun;
+    const int64_t runs = (L + R - 1) / R;
+    const int64_t groups = D / V;
+    const int64_t pairs = bsz * runs;
+    const int64_t quads = (pairs + ssm::kConvBwdWaves - 1) / ssm::kConvBwdWaves;
+    const dim3 grid((unsigned)((groups + 63) / 64), (unsigned)std::min<int64_t>(quads, 65535));
+    const dim3 block(64 * ssm::kConvBwdWaves);
+    if (groups % 64 == 0)
+        hipLaunchKernelGGL((ssm::conv1d_bwd_kernel<IO, W, V, VEC, SILU, true>), grid, block, 0, st, x, w, bias, st_in,
+                           dout, dx, dw, dbias, dst, (int)L, D, groups, (int)runs, pairs);
+    else
+        hipLaunchKernelGGL((ssm::conv1d_bwd_kernel<IO, W, V, VEC, SILU, false>), grid, block, 0, st, x, w, bias,
+                           st_in, dout, dx, dw, dbias, dst, (int)L, D, groups, (int)runs, pairs);
+}
+
+template <typename IO, bool VEC, bool SILU>
+void launch_conv_bwd_v(int width, const IO *x, const float *w, const float *bias, const IO *st_in, const IO *dout,
+                       IO *dx, float *dw, float *dbias, IO *dst, const ssm_dims *dm, hipStream_t st) {
+    switch (width) {
+        case 1: launch_conv_bwd_w<IO, 1, VEC, SILU>(x, w, bias, st_in, dout, dx, dw, dbias, dst, dm, st); break;
+        case 2: launch_conv_bwd_w<IO, 2, VEC, SILU>(x, w, bias, st_in, dout, dx, dw, dbias, dst, dm, st); break;
+        case 3: launch_conv_bwd_w<IO, 3, VEC, SILU>(x, w, bias, st_in, dout, dx, dw, dbias, dst, dm, st); break;
+        default: launch_conv_bwd_w<IO, 4, VEC, SILU>(x, w, bias, st_in, dout, dx, dw, dbias, dst, dm, st); break;
+    }
+}
+
+template <typename IO>
+void launch_conv_bwd(int width, bool silu, const void *x, const float *w, const float *bias, const void *st_in,
+                     const void *dout, void *dx, float *dw, float *dbias, void *dst, const ssm_dims *dm,
+                     hipStream_t st) {
+    const IO *x_ = static_cast<const IO *>(x);
+    const IO *si = static_cast<const IO *>(st_in);
+    const IO *go = static_cast<const IO *>(dout);
+    IO *gx = static_cast<IO *>(dx);
+    IO *gs = static_cast<IO *>(dst);
+    const size_t va = ssm::kConvBwdVec * sizeof(IO);
+    const bool vec = dm->dim % ssm::kConvBwdVec == 0 && aligned(x, va) && aligned(dout, va) && aligned(dx, va) &&
+                     (!st_in || aligned(st_in, va)) && (!dst || aligned(dst, va));
+    if (vec && silu) launch_conv_bwd_v<IO, true, true>(width, x_, w, bias, si, go, gx, dw, dbias, gs, dm, st);
+    else if (vec) launch_conv_bwd_v<IO, true, false>(width, x_, w, bias, si, go, gx, dw, dbias, gs, dm, st);
+    else if (silu) launch_conv_bwd_v<IO, false, true>(width, x_, w, bias, si, go, gx, dw, dbias, gs, dm, st);
+    else launch_conv_bwd_v<IO, false, false>(width, x_, w, bias, si, go, gx, dw, dbias, gs, dm, st);
+}
+
+
+// The SSD layer's launch (inst_misc.hip).
+void launch_ssd(const void *x, const void *dt, const float *A, const void *B, const void *C, const float *D,
+                const void *z, const float *dt_bias, int softplus, void *y, float *last_state, int64_t bsz,
+                int64_t L, int64_t H, int64_t G, hipStream_t st);
+
+}  // namespace ssmlib

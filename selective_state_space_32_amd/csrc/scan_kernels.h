@@ -106,6 +106,9 @@ __device__ __forceinline__ void load_slice(const IO *__restrict__ p, int64_t off
 //             A second part that waits longer than wait_ticks computes the whole tile itself
 //             (same values), so no schedule or placement can hang the kernel.  hflag must be
 //             zero at launch.
+//   seq_lens (nullable): per-sequence token counts; sequence b is scanned over its first
+//             seq_lens[b] tokens (clamped to [0, L]): no later token is read or written, and
+//             its final state is the state after that many tokens.
 //   N: state size; S: states per wave (K = N/S waves); T: tokens per LDS tile.
 //   VEC: the prep and epilogue move V consecutive channels of one token per thread
 //        (one 16-byte access for 8 bf16); needs D % 8 == 0 and 16-byte aligned u, delta,
@@ -132,7 +135,8 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                   const float *__restrict__ conv_w = nullptr, const float *__restrict__ conv_b = nullptr,
                   IO *__restrict__ u_out = nullptr, float *__restrict__ ckpt_out = nullptr,
                   int n_full = 0, int n_split = 0, int64_t l_mid = 0, float *__restrict__ hand = nullptr,
-                  int *__restrict__ hflag = nullptr, unsigned long long wait_ticks = 0) {
+                  int *__restrict__ hflag = nullptr, unsigned long long wait_ticks = 0,
+                  const int32_t *__restrict__ seq_lens = nullptr) {
     constexpr int K = N / S;
     constexpr int J = T / K;                   // prep / epilogue elements per thread per tile
     constexpr int V = VEC ? (J < 8 ? J : 8) : 1;  // consecutive channels per thread access
@@ -203,6 +207,11 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     int64_t t_end = min(L, t_begin + chunk_len);
     if (role == kFirstPart) t_end = l_mid;
     if (role == kSecondPart) t_begin = l_mid;
+    // variable lengths: sequence b has seq_lens[b] tokens (clamped to [0, L]); the item's range
+    // ends there and may be empty (no token read or written; the state passes through)
+    const int64_t len_b = seq_lens ? min((int64_t)max(seq_lens[b], 0), L) : L;
+    t_end = min(t_end, len_b);
+    if (t_begin > t_end) t_begin = t_end;
     const int64_t row0 = (int64_t)b * L;
     const bool qact = d0 + cq < D;          // whole group in or out (D % V == 0 when VEC)
     const int64_t dq = qact ? d0 + cq : (D - V) / V * V;  // in-bounds channel for loads
@@ -283,7 +292,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     auto load_tile = [&](int64_t t0, Raw &r) {
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-            const int64_t t = min(t0 + row_of(p), t_end - 1);
+            const int64_t t = max(min(t0 + row_of(p), t_end - 1), (int64_t)0);
             const int64_t idx = (row0 + t) * D + dq;
             // (z is loaded unconditionally -- from u when there is no gate -- so that the
             // buffer registers carry no conditional value around the loop)
@@ -604,9 +613,10 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
         do_tile(t0 + T, r1, r0, dg0, dg1, true);
     }
     {
-        // the last pair's second tile (empty or not) still owes its epilogue
+        // the last pair's second tile (empty or not) still owes its epilogue (no pair: an
+        // empty range, nothing to write)
         const int64_t npair = (t_end - t_begin + 2 * T - 1) / (2 * T);
-        epilogue(t_begin + (2 * npair - 1) * T, dg1);
+        if (npair > 0) epilogue(t_begin + (2 * npair - 1) * T, dg1);
     }
 
     if (MODE == kSummary) {

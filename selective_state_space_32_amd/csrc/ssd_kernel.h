@@ -172,7 +172,7 @@ __device__ __forceinline__ void mma16_xn(const __bf16 *a, int a0, const __bf16 *
 //   tH2: the same, low parts
 //   tZ : z [t][p]                     -> (3) y, in place
 // (at most 168 registers: three workgroups of four waves per CU)
-__global__ void __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(3)))
+static __global__ void __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(3)))
 ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt, const float *__restrict__ A,
                  const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm, const float *__restrict__ Dv,
                  const uint16_t *__restrict__ z, const float *__restrict__ dt_bias, uint16_t *__restrict__ y,

@@ -11,15 +11,10 @@
 #include <mutex>
 #include <string>
 
-#include "ssmscan.h"
-#include "carry_kernel.h"
-#include "scan_kernels.h"
-#include "step_kernel.h"
-#include "bwd_kernel.h"
-#include "conv_kernel.h"
-#include "ssd_kernel.h"
+#include "launch.h"
 
-namespace {
+namespace ssmlib {
+
 
 thread_local std::string g_err;
 
@@ -38,17 +33,6 @@ int ok() {
     return SSM_OK;
 }
 
-bool n_supported(int64_t n) { return n == 1 || n == 2 || n == 4 || n == 8 || n == 16; }
-
-constexpr int64_t kMaxDim = int64_t(1) << 30;
-constexpr int64_t kMaxElems = int64_t(1) << 46;
-constexpr int kMaxChunks = 65535;  // grid.y limit
-// Scan workgroups resident per CU (N = 16: 133-137 VGPRs and 48 KB of LDS per 4-wave group),
-// the basis of the schedules below.
-constexpr int kGroupsPerCU = 3;
-// CU count assumed when no device is visible (plan queries on a host without a GPU): MI355X.
-constexpr int kDefaultCUs = 256;
-
 // How long a second half of the split schedule waits for its hand-over, in ticks of the
 // 100 MHz constant clock: SSMSCAN_HANDOVER_WAIT_US microseconds (default 20000), read at each
 // call.  0 makes every second half compute its whole tile (the time-out path; same results).
@@ -62,6 +46,51 @@ unsigned long long handover_wait_ticks() {
     }
     return (unsigned long long)us * 100ull;
 }
+
+
+// The launch templates are instantiated in the inst_*.hip translation units.
+#define SSM_EXTERN_N(N, IO) \
+    extern template int launch_scan<N, IO>(const void *, const void *, const float *, const void *, const void *, \
+                                           const float *, const void *, const float *, int, const float *, void *, \
+                                           float *, const ssm_dims *, const Plan &, void *, hipStream_t, \
+                                           const ConvArgs *, float *, const int32_t *); \
+    extern template int launch_step<N, IO>(float *, const void *, const void *, const float *, const void *, \
+                                           const void *, const float *, const void *, void *, const ssm_dims *, \
+                                           hipStream_t); \
+    extern template int launch_bwd<N, IO>(const BwdArgs &, const ssm_dims *, void *, hipStream_t);
+#define SSM_EXTERN_IO(IO) SSM_EXTERN_N(1, IO) SSM_EXTERN_N(2, IO) SSM_EXTERN_N(4, IO) SSM_EXTERN_N(8, IO) \
+    SSM_EXTERN_N(16, IO)
+SSM_EXTERN_IO(float)
+SSM_EXTERN_IO(uint16_t)
+#undef SSM_EXTERN_IO
+#undef SSM_EXTERN_N
+extern template int launch_conv<float>(int, bool, const void *, const float *, const float *, const void *, void *,
+                                       void *, const ssm_dims *, hipStream_t);
+extern template int launch_conv<uint16_t>(int, bool, const void *, const float *, const float *, const void *,
+                                          void *, void *, const ssm_dims *, hipStream_t);
+extern template void launch_conv_bwd<float>(int, bool, const void *, const float *, const float *, const void *,
+                                            const void *, void *, float *, float *, void *, const ssm_dims *,
+                                            hipStream_t);
+extern template void launch_conv_bwd<uint16_t>(int, bool, const void *, const float *, const float *,
+                                               const void *, const void *, void *, float *, float *, void *,
+                                               const ssm_dims *, hipStream_t);
+
+}  // namespace ssmlib
+
+namespace {
+
+using namespace ssmlib;
+
+bool n_supported(int64_t n) { return n == 1 || n == 2 || n == 4 || n == 8 || n == 16; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int64_t kMaxElems = int64_t(1) << 46;
+constexpr int kMaxChunks = 65535;  // grid.y limit
+// Scan workgroups resident per CU (N = 16: 133-137 VGPRs and 48 KB of LDS per 4-wave group),
+// the basis of the schedules below.
+constexpr int kGroupsPerCU = 3;
+// CU count assumed when no device is visible (plan queries on a host without a GPU): MI355X.
+constexpr int kDefaultCUs = 256;
 
 // Compute units of the current device, cached per device.
 int device_cus() {
@@ -106,23 +135,6 @@ int check_dims(const ssm_dims *dm, bool scan) {
     return SSM_OK;
 }
 
-enum Schedule { kGrid = 0, kCarry = 1, kSplit = 2 };
-
-struct Plan {
-    int schedule = kGrid;
-    int64_t nchunk = 1;      // chunks per sequence (work items per tile)
-    int64_t chunk_len = 0;   // tokens per chunk
-    int64_t n_full = 0, n_split = 0, l_mid = 0;   // the split schedule
-    size_t off_cstate = 0, off_cdsum = 0, off_hand = 0, off_flags = 0, bytes = 0;
-};
-
-// One workgroup per (sequence, 64-channel tile) fills the GPU once there are about two
-// tiles per CU or more; with fewer tiles the tokens are split into chunks as well (the
-// chunk carry), which costs an extra summary pass over all but the last chunk.
-// align_ckpt: the call also stores the backward pass's checkpoints (the state before every
-// kCkptEvery-th token); each chunk's first token must then be one of those points, so a
-// carry chunk length is rounded up to a multiple of kCkptEvery (fewer chunks, never more
-// workspace than the plan without the flag).
 // cus: compute units of the device.  allow_split: the split schedule may be used (not when the
 // initial state is the last_state buffer: a second part that found no hand-over would rewrite
 // last_state while its first part may still read the initial state).
@@ -189,170 +201,24 @@ Plan make_plan(const ssm_dims *dm, int cus, bool align_ckpt = false, bool allow_
     return p;
 }
 
-bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Kernel shape per state size: S states per wave (K = N/S waves per workgroup) and T
 // tokens per LDS tile.
-template <int N> struct ScanShape;
-template <> struct ScanShape<1> { static constexpr int S = 1, T = 32; };
-template <> struct ScanShape<2> { static constexpr int S = 2, T = 32; };
-template <> struct ScanShape<4> { static constexpr int S = 4, T = 32; };
-template <> struct ScanShape<8> { static constexpr int S = 4, T = 32; };
-template <> struct ScanShape<16> { static constexpr int S = 4, T = 32; };
-
-// The fused causal convolution of the scan's input (conv entry point only).
-struct ConvArgs {
-    const float *w;
-    const float *b;
-    void *u_out;
-};
-
-// (CK: the full pass also stores the backward pass's checkpoints to ckpt)
-template <int N, typename IO, bool VEC, bool ZOH, int CW = 0, bool CK = false>
-void launch_scan_kernels(const IO *u, const IO *dl, const float *A, const IO *B, const IO *C, const float *Dv,
-                         const IO *z, const float *bias, int softplus, const float *h0, IO *y, float *last_state,
-                         const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st,
-                         const ConvArgs &cv = ConvArgs{nullptr, nullptr, nullptr}, float *ckpt = nullptr) {
-    constexpr int S = ScanShape<N>::S;
-    constexpr int T = ScanShape<N>::T;
-    constexpr int K = N / S;
-    const int64_t bsz = dm->batch, L = dm->seqlen, D = dm->dim;
-    const int tiles_per_b = (int)((D + ssm::kChanTile - 1) / ssm::kChanTile);
-    const int n_tiles = (int)(bsz * tiles_per_b);
-    const dim3 block(64 * K);
-    float *cstate = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_cstate);
-    float *cdsum = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_cdsum);
-    const int64_t cl = p.chunk_len;
-    const int nc = (int)p.nchunk;
-    if (p.schedule == kCarry) {
-        // (CK also here: with the fused convolution, the training forward scans u rounded to the
-        // I/O type, so the summary pass must carry the states of that same u)
-        hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kSummary, VEC, ZOH, CW, CK>),
-                           dim3((unsigned)n_tiles, (unsigned)(nc - 1)), block, 0, st, u, dl, (const IO *)nullptr,
-                           (IO *)nullptr, A, (const float *)nullptr, bias, B, C, (const float *)nullptr,
-                           (float *)nullptr, cstate, cdsum, L, D, tiles_per_b, n_tiles, cl, nc, softplus, cv.w, cv.b,
-                           (IO *)nullptr);
-        const int col_tiles = (int)((D * N + 63) / 64);
-        hipLaunchKernelGGL((ssm::carry_scan_kernel<N>), dim3((unsigned)(bsz * col_tiles)), dim3(256), 0, st,
-                           cstate, (const float *)cdsum, A, h0, D, nc, col_tiles);
-    }
-    if (p.schedule == kSplit) {
-        // the hand-over flags start at zero (a fill kernel: no memset node if the caller captures a graph)
-        int *flags = reinterpret_cast<int *>(static_cast<char *>(ws) + p.off_flags);
-        float *hand = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_hand);
-        hipLaunchKernelGGL(ssm::fill_zero_kernel<int>, dim3((unsigned)((p.n_split + 255) / 256)), dim3(256), 0, st, flags,
-                           p.n_split);
-        hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kFull, VEC, ZOH, CW, CK>),
-                           dim3((unsigned)(p.n_full + 2 * p.n_split), 1), block, 0, st, u, dl, z, y, A, Dv, bias, B, C,
-                           h0, last_state, cstate, cdsum, L, D, tiles_per_b, n_tiles, cl, nc, softplus, cv.w, cv.b,
-                           static_cast<IO *>(cv.u_out), ckpt, (int)p.n_full, (int)p.n_split, p.l_mid, hand, flags,
-                           handover_wait_ticks());
-        return;
-    }
-    hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kFull, VEC, ZOH, CW, CK>),
-                       dim3((unsigned)n_tiles, (unsigned)nc), block, 0, st, u, dl, z, y, A, Dv, bias, B, C, h0,
-                       last_state, cstate, cdsum, L, D, tiles_per_b, n_tiles, cl, nc, softplus, cv.w, cv.b,
-                       static_cast<IO *>(cv.u_out), ckpt);
-}
-
-template <int N, typename IO>
-int launch_scan(const void *u, const void *delta, const float *A, const void *B, const void *C,
-                const float *Dv, const void *z, const float *bias, int flags, const float *h0, void *y,
-                float *last_state, const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st,
-                const ConvArgs *cv, float *ckpt) {
-    const int softplus = (flags & SSM_SCAN_SOFTPLUS) != 0;
-    const bool zoh = (flags & SSM_SCAN_EXACT_ZOH) != 0;
-    const IO *u_ = static_cast<const IO *>(u);
-    const IO *dl_ = static_cast<const IO *>(delta);
-    const IO *z_ = static_cast<const IO *>(z);
-    const IO *B_ = static_cast<const IO *>(B);
-    const IO *C_ = static_cast<const IO *>(C);
-    IO *y_ = static_cast<IO *>(y);
-    // 16-byte prep/epilogue accesses need whole groups of 8 channels and aligned rows
-    const bool vec = dm->dim % 8 == 0 && aligned(u, 16) && aligned(delta, 16) && aligned(y, 16) &&
-                     (!z || aligned(z, 16));
-    if (cv) {
-        // the fused convolution (width 4; no exact ZOH, checked by the caller), with or without
-        // the backward pass's checkpoints
-        if (vec && ckpt)
-            launch_scan_kernels<N, IO, true, false, 4, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_,
-                                                             last_state, dm, p, ws, st, *cv, ckpt);
-        else if (ckpt)
-            launch_scan_kernels<N, IO, false, false, 4, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_,
-                                                              last_state, dm, p, ws, st, *cv, ckpt);
-        else if (vec)
-            launch_scan_kernels<N, IO, true, false, 4>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state,
-                                                       dm, p, ws, st, *cv);
-        else
-            launch_scan_kernels<N, IO, false, false, 4>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_,
-                                                        last_state, dm, p, ws, st, *cv);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-        return ok();
-    }
-    if (ckpt) {
-        // the training forward: the backward pass's checkpoints too (no exact ZOH, checked by the caller)
-        const ConvArgs none{nullptr, nullptr, nullptr};
-        if (vec)
-            launch_scan_kernels<N, IO, true, false, 0, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_,
-                                                             last_state, dm, p, ws, st, none, ckpt);
-        else
-            launch_scan_kernels<N, IO, false, false, 0, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_,
-                                                              last_state, dm, p, ws, st, none, ckpt);
-    } else if (vec && zoh)
-        launch_scan_kernels<N, IO, true, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state, dm, p,
-                                               ws, st);
-    else if (vec)
-        launch_scan_kernels<N, IO, true, false>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state, dm,
-                                                p, ws, st);
-    else if (zoh)
-        launch_scan_kernels<N, IO, false, true>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state, dm,
-                                                p, ws, st);
-    else
-        launch_scan_kernels<N, IO, false, false>(u_, dl_, A, B_, C_, Dv, z_, bias, softplus, h0, y_, last_state, dm,
-                                                 p, ws, st);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-    return ok();
-}
 
 template <typename IO>
 int dispatch_scan(int64_t N, const void *u, const void *delta, const float *A, const void *B,
                   const void *C, const float *Dv, const void *z, const float *bias, int flags, const float *h0,
                   void *y, float *ls, const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st,
-                  const ConvArgs *cv, float *ckpt) {
+                  const ConvArgs *cv, float *ckpt, const int32_t *sl) {
     switch (N) {
-        case 1: return launch_scan<1, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv, ckpt);
-        case 2: return launch_scan<2, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv, ckpt);
-        case 4: return launch_scan<4, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv, ckpt);
-        case 8: return launch_scan<8, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv, ckpt);
-        case 16: return launch_scan<16, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv, ckpt);
+        case 1: return launch_scan<1, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv, ckpt, sl);
+        case 2: return launch_scan<2, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv, ckpt, sl);
+        case 4: return launch_scan<4, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv, ckpt, sl);
+        case 8: return launch_scan<8, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv, ckpt, sl);
+        case 16:
+            return launch_scan<16, IO>(u, delta, A, B, C, Dv, z, bias, flags, h0, y, ls, dm, p, ws, st, cv, ckpt, sl);
     }
     return fail(SSM_ERR_UNSUPPORTED_N, "dstate %lld not supported", (long long)N);
-}
-
-template <int N, typename IO>
-int launch_step(float *state, const void *u, const void *delta, const float *A, const void *B,
-                const void *C, const float *Dv, const void *z, void *y, const ssm_dims *dm, hipStream_t st) {
-    constexpr int G = N >= 4 ? N / 4 : 1;
-    constexpr int SP = ssm::kStepSeqPerThread;
-    const int64_t threads = (dm->batch + SP - 1) / SP * dm->dim * G;
-    const dim3 grid((unsigned)((threads + 255) / 256));
-    // vector reads of the A, B, C slices of a lane need them aligned to the slice
-    const size_t es = sizeof(IO);
-    const bool vp = N >= 4 && aligned(A, 16) && aligned(B, 4 * es) && aligned(C, 4 * es);
-    const IO *u_ = static_cast<const IO *>(u), *dl_ = static_cast<const IO *>(delta);
-    const IO *B_ = static_cast<const IO *>(B), *C_ = static_cast<const IO *>(C), *z_ = static_cast<const IO *>(z);
-    IO *y_ = static_cast<IO *>(y);
-    if (vp)
-        hipLaunchKernelGGL((ssm::step_kernel<N, IO, true>), grid, dim3(256), 0, st, state, u_, dl_, A, B_, C_, Dv,
-                           z_, y_, dm->batch, dm->dim);
-    else
-        hipLaunchKernelGGL((ssm::step_kernel<N, IO, false>), grid, dim3(256), 0, st, state, u_, dl_, A, B_, C_, Dv,
-                           z_, y_, dm->batch, dm->dim);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-    return ok();
 }
 
 template <typename IO>
@@ -368,78 +234,9 @@ int dispatch_step(int64_t N, float *state, const void *u, const void *delta, con
     return fail(SSM_ERR_UNSUPPORTED_N, "dstate %lld not supported", (long long)N);
 }
 
-// ---- backward ----------------------------------------------------------------------------
-
 size_t bwd_workspace_bytes(const ssm_dims *dm) {
     const int64_t n_ckpt = (dm->seqlen + ssm::kCkptEvery - 1) / ssm::kCkptEvery;
     return align256((size_t)(dm->batch * n_ckpt * dm->dim * dm->dstate) * sizeof(float));
-}
-
-template <typename TP>
-void fill_zero(TP *p, int64_t n, hipStream_t st) {
-    if (p && n > 0)
-        hipLaunchKernelGGL(ssm::fill_zero_kernel<TP>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
-}
-
-struct BwdArgs {
-    const float *h0;
-    const void *u, *delta;
-    const float *A;
-    const void *B, *C;
-    const float *D;
-    const void *z;
-    const float *bias;
-    int softplus;
-    const void *dy;
-    const float *dlast;
-    void *du, *ddelta;
-    float *dA, *dB, *dC, *dD;
-    void *dz;
-    float *dbias, *dh0;
-    bool ckpt_given;   // the workspace already holds the checkpoints (written by the training forward)
-};
-
-template <int N, typename IO>
-int launch_bwd(const BwdArgs &a, const ssm_dims *dm, void *ws, hipStream_t st) {
-    constexpr int S = ScanShape<N>::S, T = ScanShape<N>::T, K = N / S;
-    constexpr int KB = ssm::BwdShape<N>::K;
-    const int64_t bsz = dm->batch, L = dm->seqlen, D = dm->dim;
-    const int tiles_per_b = (int)((D + ssm::kChanTile - 1) / ssm::kChanTile);
-    const int n_tiles = (int)(bsz * tiles_per_b);
-    const IO *u = static_cast<const IO *>(a.u), *dl = static_cast<const IO *>(a.delta);
-    const IO *B = static_cast<const IO *>(a.B), *C = static_cast<const IO *>(a.C);
-    const IO *z = static_cast<const IO *>(a.z), *dy = static_cast<const IO *>(a.dy);
-    IO *du = static_cast<IO *>(a.du), *ddl = static_cast<IO *>(a.ddelta), *dz = static_cast<IO *>(a.dz);
-    float *ckpt = static_cast<float *>(ws);
-    // forward in checkpoint mode: the state before every kCkptEvery-th token (unless the
-    // training forward has stored them already)
-    const bool vf = D % 8 == 0 && aligned(u, 16) && aligned(dl, 16);
-    if (!a.ckpt_given) {
-        if (vf)
-            hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kCheckpoint, true>), dim3((unsigned)n_tiles, 1),
-                               dim3(64 * K), 0, st, u, dl, (const IO *)nullptr, (IO *)nullptr, a.A,
-                               (const float *)nullptr, a.bias, B, C, a.h0, (float *)nullptr, ckpt, (float *)nullptr, L,
-                               D, tiles_per_b, n_tiles, L, 1, a.softplus);
-        else
-            hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kCheckpoint, false>),
-                               dim3((unsigned)n_tiles, 1), dim3(64 * K), 0, st, u, dl, (const IO *)nullptr,
-                               (IO *)nullptr, a.A, (const float *)nullptr, a.bias, B, C, a.h0, (float *)nullptr, ckpt,
-                               (float *)nullptr, L, D, tiles_per_b, n_tiles, L, 1, a.softplus);
-    }
-    // the reverse walk; 16-byte (or 8-byte) element access when every (token, channel) tensor allows it
-    const bool vb = D % 8 == 0 && aligned(u, 16) && aligned(dl, 16) && aligned(dy, 16) && aligned(du, 16) &&
-                    aligned(ddl, 16) && (!z || (aligned(z, 16) && aligned(dz, 16)));
-    if (vb)
-        hipLaunchKernelGGL((ssm::scan_bwd_kernel<N, IO, true>), dim3((unsigned)n_tiles), dim3(64 * KB), 0, st, u, dl,
-                           z, dy, a.A, a.D, a.bias, B, C, ckpt, a.dlast, du, ddl, dz, a.dA, a.dB, a.dC, a.dD, a.dbias,
-                           a.dh0, L, D, tiles_per_b, a.softplus);
-    else
-        hipLaunchKernelGGL((ssm::scan_bwd_kernel<N, IO, false>), dim3((unsigned)n_tiles), dim3(64 * KB), 0, st, u, dl,
-                           z, dy, a.A, a.D, a.bias, B, C, ckpt, a.dlast, du, ddl, dz, a.dA, a.dB, a.dC, a.dD, a.dbias,
-                           a.dh0, L, D, tiles_per_b, a.softplus);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-    return ok();
 }
 
 template <typename IO>
@@ -452,103 +249,6 @@ int dispatch_bwd(int64_t N, const BwdArgs &a, const ssm_dims *dm, void *ws, hipS
         case 16: return launch_bwd<16, IO>(a, dm, ws, st);
     }
     return fail(SSM_ERR_UNSUPPORTED_N, "dstate %lld not supported", (long long)N);
-}
-
-// --- the causal depthwise convolution of the block's main branch ---------------------------
-
-template <typename IO, int W, bool VEC, bool SILU>
-void launch_conv_w(const IO *x, const float *w, const float *bias, const IO *st_in, IO *out, IO *st_out,
-                   const ssm_dims *dm, hipStream_t st) {
-    constexpr int V = VEC ? ssm::kConvVec : 1;
-    const int64_t bsz = dm->batch, L = dm->seqlen, D = dm->dim;
-    // a state updated in place is read and written by the same thread: one run per sequence
-    const bool in_place = st_out && st_out == st_in && W > 1;
-    const int64_t R = in_place ? L : ssm::kConvRun;
-    const int64_t runs = (L + R - 1) / R;
-    const int64_t groups = D / V;
-    const int64_t pairs = bsz * runs;
-    const dim3 grid((unsigned)((groups + 255) / 256), (unsigned)std::min<int64_t>(pairs, 65535));
-    hipLaunchKernelGGL((ssm::conv1d_kernel<IO, W, V, VEC, SILU>), grid, dim3(256), 0, st, x, w, bias, st_in, out,
-                       st_out, L, D, groups, runs, pairs, (int)R);
-}
-
-template <typename IO, bool VEC, bool SILU>
-void launch_conv_v(int width, const IO *x, const float *w, const float *bias, const IO *st_in, IO *out,
-                   IO *st_out, const ssm_dims *dm, hipStream_t st) {
-    switch (width) {
-        case 1: launch_conv_w<IO, 1, VEC, SILU>(x, w, bias, st_in, out, st_out, dm, st); break;
-        case 2: launch_conv_w<IO, 2, VEC, SILU>(x, w, bias, st_in, out, st_out, dm, st); break;
-        case 3: launch_conv_w<IO, 3, VEC, SILU>(x, w, bias, st_in, out, st_out, dm, st); break;
-        default: launch_conv_w<IO, 4, VEC, SILU>(x, w, bias, st_in, out, st_out, dm, st); break;
-    }
-}
-
-template <typename IO>
-int launch_conv(int width, bool silu, const void *x, const float *w, const float *bias, const void *st_in,
-                void *out, void *st_out, const ssm_dims *dm, hipStream_t st) {
-    const IO *x_ = static_cast<const IO *>(x);
-    const IO *si = static_cast<const IO *>(st_in);
-    IO *o = static_cast<IO *>(out);
-    IO *so = static_cast<IO *>(st_out);
-    const size_t va = ssm::kConvVec * sizeof(IO);   // bytes of one vector access
-    const bool vec = dm->dim % ssm::kConvVec == 0 && aligned(x, va) && aligned(out, va) &&
-                     (!st_in || aligned(st_in, va)) && (!st_out || aligned(st_out, va));
-    if (vec && silu) launch_conv_v<IO, true, true>(width, x_, w, bias, si, o, so, dm, st);
-    else if (vec) launch_conv_v<IO, true, false>(width, x_, w, bias, si, o, so, dm, st);
-    else if (silu) launch_conv_v<IO, false, true>(width, x_, w, bias, si, o, so, dm, st);
-    else launch_conv_v<IO, false, false>(width, x_, w, bias, si, o, so, dm, st);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-    return ok();
-}
-
-template <typename IO, int W, bool VEC, bool SILU>
-void launch_conv_bwd_w(const IO *x, const float *w, const float *bias, const IO *st_in, const IO *dout, IO *dx,
-                       float *dw, float *dbias, IO *dst, const ssm_dims *dm, hipStream_t st) {
-    constexpr int V = VEC ? ssm::kConvBwdVec : 1;
-    const int64_t bsz = dm->batch, L = dm->seqlen, D = dm->dim;
-    const int64_t R = ssm::kConvBwdRun;
-    const int64_t runs = (L + R - 1) / R;
-    const int64_t groups = D / V;
-    const int64_t pairs = bsz * runs;
-    const int64_t quads = (pairs + ssm::kConvBwdWaves - 1) / ssm::kConvBwdWaves;
-    const dim3 grid((unsigned)((groups + 63) / 64), (unsigned)std::min<int64_t>(quads, 65535));
-    const dim3 block(64 * ssm::kConvBwdWaves);
-    if (groups % 64 == 0)
-        hipLaunchKernelGGL((ssm::conv1d_bwd_kernel<IO, W, V, VEC, SILU, true>), grid, block, 0, st, x, w, bias, st_in,
-                           dout, dx, dw, dbias, dst, (int)L, D, groups, (int)runs, pairs);
-    else
-        hipLaunchKernelGGL((ssm::conv1d_bwd_kernel<IO, W, V, VEC, SILU, false>), grid, block, 0, st, x, w, bias,
-                           st_in, dout, dx, dw, dbias, dst, (int)L, D, groups, (int)runs, pairs);
-}
-
-template <typename IO, bool VEC, bool SILU>
-void launch_conv_bwd_v(int width, const IO *x, const float *w, const float *bias, const IO *st_in, const IO *dout,
-                       IO *dx, float *dw, float *dbias, IO *dst, const ssm_dims *dm, hipStream_t st) {
-    switch (width) {
-        case 1: launch_conv_bwd_w<IO, 1, VEC, SILU>(x, w, bias, st_in, dout, dx, dw, dbias, dst, dm, st); break;
-        case 2: launch_conv_bwd_w<IO, 2, VEC, SILU>(x, w, bias, st_in, dout, dx, dw, dbias, dst, dm, st); break;
-        case 3: launch_conv_bwd_w<IO, 3, VEC, SILU>(x, w, bias, st_in, dout, dx, dw, dbias, dst, dm, st); break;
-        default: launch_conv_bwd_w<IO, 4, VEC, SILU>(x, w, bias, st_in, dout, dx, dw, dbias, dst, dm, st); break;
-    }
-}
-
-template <typename IO>
-void launch_conv_bwd(int width, bool silu, const void *x, const float *w, const float *bias, const void *st_in,
-                     const void *dout, void *dx, float *dw, float *dbias, void *dst, const ssm_dims *dm,
-                     hipStream_t st) {
-    const IO *x_ = static_cast<const IO *>(x);
-    const IO *si = static_cast<const IO *>(st_in);
-    const IO *go = static_cast<const IO *>(dout);
-    IO *gx = static_cast<IO *>(dx);
-    IO *gs = static_cast<IO *>(dst);
-    const size_t va = ssm::kConvBwdVec * sizeof(IO);
-    const bool vec = dm->dim % ssm::kConvBwdVec == 0 && aligned(x, va) && aligned(dout, va) && aligned(dx, va) &&
-                     (!st_in || aligned(st_in, va)) && (!dst || aligned(dst, va));
-    if (vec && silu) launch_conv_bwd_v<IO, true, true>(width, x_, w, bias, si, go, gx, dw, dbias, gs, dm, st);
-    else if (vec) launch_conv_bwd_v<IO, true, false>(width, x_, w, bias, si, go, gx, dw, dbias, gs, dm, st);
-    else if (silu) launch_conv_bwd_v<IO, false, true>(width, x_, w, bias, si, go, gx, dw, dbias, gs, dm, st);
-    else launch_conv_bwd_v<IO, false, false>(width, x_, w, bias, si, go, gx, dw, dbias, gs, dm, st);
 }
 
 }  // namespace
@@ -589,14 +289,12 @@ void *scratch_address() {
 static int scan_impl(const float *h0, const void *u, const void *delta, const float *A, const void *B,
                      const void *C, const float *D, const void *z, const float *delta_bias, int flags,
                      void *y, float *last_state, const ssm_dims *dims, void *workspace, size_t workspace_bytes,
-                     void *stream, const ConvArgs *cv = nullptr) {
+                     void *stream, const ConvArgs *cv = nullptr, const int32_t *seq_lens = nullptr) {
     int rc = check_dims(dims, true);
     if (rc != SSM_OK) return rc;
     if (flags & ~(SSM_SCAN_SOFTPLUS | SSM_SCAN_EXACT_ZOH | SSM_SCAN_CHECKPOINTS))
         return fail(SSM_ERR_FLAGS, "unknown flag bits 0x%x", flags);
     const bool want_ckpt = (flags & SSM_SCAN_CHECKPOINTS) != 0;
-    if (want_ckpt && (flags & SSM_SCAN_EXACT_ZOH))
-        return fail(SSM_ERR_FLAGS, "checkpoints for the backward pass are not available with the exact ZOH");
     const int64_t bsz = dims->batch, L = dims->seqlen, Dm = dims->dim, N = dims->dstate;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (bsz == 0 || Dm == 0) return ok();
@@ -644,11 +342,12 @@ static int scan_impl(const float *h0, const void *u, const void *delta, const fl
     if (need > 0 && !aligned(workspace, 16)) return fail(SSM_ERR_ALIGN, "workspace not 16-byte aligned");
     float *ckpt = want_ckpt ? static_cast<float *>(workspace) : nullptr;
     void *carry_ws = p.bytes > 0 ? static_cast<void *>(static_cast<char *>(workspace) + ck_bytes) : workspace;
+    if (seq_lens && !aligned(seq_lens, 4)) return fail(SSM_ERR_ALIGN, "seq_lens not 4-byte aligned");
     if (dims->io_dtype == SSM_IO_BF16)
         return dispatch_scan<uint16_t>(N, u, delta, A, B, C, D, z, delta_bias, flags, h0, y, last_state, dims, p,
-                                       carry_ws, st, cv, ckpt);
+                                       carry_ws, st, cv, ckpt, seq_lens);
     return dispatch_scan<float>(N, u, delta, A, B, C, D, z, delta_bias, flags, h0, y, last_state, dims, p,
-                                carry_ws, st, cv, ckpt);
+                                carry_ws, st, cv, ckpt, seq_lens);
 }
 
 
@@ -723,6 +422,15 @@ int ssm_scan_fwd_from(const float *initial_state, const void *u, const void *del
                      workspace, workspace_bytes, stream);
 }
 
+int ssm_scan_fwd_varlen(const float *initial_state, const int32_t *seq_lens, const void *u, const void *delta,
+                        const float *A, const void *B, const void *C, const float *D, const void *z,
+                        const float *delta_bias, int flags, void *y, float *last_state, const ssm_dims *dims,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    if (!seq_lens) return fail(SSM_ERR_NULL, "seq_lens is NULL (use ssm_scan_fwd_from for equal lengths)");
+    return scan_impl(initial_state, u, delta, A, B, C, D, z, delta_bias, flags, y, last_state, dims, workspace,
+                     workspace_bytes, stream, nullptr, seq_lens);
+}
+
 int ssm_scan_fwd_conv(const void *x, const float *conv_w, const float *conv_b, int conv_width, const void *delta,
                       const float *A, const void *B, const void *C, const float *D, const void *z,
                       const float *delta_bias, int flags, void *y, float *last_state, void *u_out,
@@ -766,9 +474,8 @@ int ssm_scan_bwd(const float *initial_state, const void *u, const void *delta, c
                  void *workspace, size_t workspace_bytes, void *stream) {
     int rc = check_dims(dims, true);
     if (rc != SSM_OK) return rc;
-    if (flags & ~(SSM_SCAN_SOFTPLUS | SSM_SCAN_CHECKPOINTS))
-        return fail(SSM_ERR_FLAGS,
-                    "flags 0x%x: the backward pass takes the softplus and checkpoints flags only (no exact ZOH)", flags);
+    if (flags & ~(SSM_SCAN_SOFTPLUS | SSM_SCAN_EXACT_ZOH | SSM_SCAN_CHECKPOINTS))
+        return fail(SSM_ERR_FLAGS, "unknown flag bits 0x%x", flags);
     const int64_t bsz = dims->batch, L = dims->seqlen, Dm = dims->dim, N = dims->dstate;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (!A || !dA || (bsz > 0 && L > 0 && Dm > 0 && (!u || !delta || !B || !C || !dy || !du || !ddelta || !dB || !dC)))
@@ -814,7 +521,8 @@ int ssm_scan_bwd(const float *initial_state, const void *u, const void *delta, c
         return ok();
     }
     BwdArgs a{initial_state, u, delta, A, B, C, D, z, delta_bias, (flags & SSM_SCAN_SOFTPLUS) != 0, dy, dlast_state, du, ddelta,
-              dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, (flags & SSM_SCAN_CHECKPOINTS) != 0};
+              dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, (flags & SSM_SCAN_CHECKPOINTS) != 0,
+              (flags & SSM_SCAN_EXACT_ZOH) != 0};
     if (dims->io_dtype == SSM_IO_BF16) return dispatch_bwd<uint16_t>(N, a, dims, workspace, st);
     return dispatch_bwd<float>(N, a, dims, workspace, st);
 }
@@ -946,11 +654,7 @@ int ssm_ssd_fwd(const void *x, const void *dt, const float *A, const void *B, co
         if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
         return ok();
     }
-    hipLaunchKernelGGL(ssm::ssd_chunk_kernel, dim3((unsigned)(bsz * H)), dim3(ssm::kSsdThreads), 0, st,
-                       static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(dt), A,
-                       static_cast<const uint16_t *>(B), static_cast<const uint16_t *>(C), D,
-                       static_cast<const uint16_t *>(z), dt_bias, static_cast<uint16_t *>(y), last_state, L, (int)H,
-                       (int)G, (flags & SSM_SCAN_SOFTPLUS) ? 1 : 0);
+    launch_ssd(x, dt, A, B, C, D, z, dt_bias, (flags & SSM_SCAN_SOFTPLUS) ? 1 : 0, y, last_state, bsz, L, H, G, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

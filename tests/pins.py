@@ -863,3 +863,77 @@ def check_bwd_zoh_zero_A(scan_from_zoh, scan_bwd_zoh, scan_bwd, seed=77):
 
 
 BWD_ZOH_CHECKS = [check_bwd_zoh_fd_all_inputs, check_bwd_zoh_fd_plain, check_bwd_zoh_fd_small_A]
+
+
+
+# --- sequences of different lengths -------------------------------------------------------------
+# scan_varlen(u, x, A, B, C, lens, D, z, bias, softplus, h0) -> (y with NaN past each length,
+# last_state); scan_from as above.
+
+def _varlen_case(seed, bsz=4, L=37, D=3, N=4):
+    rng = _rng(seed)
+    c = dict(u=rng.standard_normal((bsz, L, D)), x=0.5 * rng.standard_normal((bsz, L, D)),
+             A=-np.exp(rng.normal(0.0, 0.5, (D, N))), B=rng.standard_normal((bsz, L, N)),
+             C=rng.standard_normal((bsz, L, N)), D=rng.standard_normal(D), z=rng.standard_normal((bsz, L, D)),
+             bias=rng.uniform(-1.0, 0.0, D), h0=rng.standard_normal((bsz, D, N)))
+    return c, rng
+
+
+def _vl(scan_varlen, c, lens, **kw):
+    a = dict(c)
+    a.update(kw)
+    return scan_varlen(a["u"], a["x"], a["A"], a["B"], a["C"], lens, a["D"], a["z"], a["bias"], True, a["h0"])
+
+
+def check_varlen_full_lengths(scan_from, scan_varlen):
+    """Every length = L: the batch scan itself, bitwise."""
+    c, _ = _varlen_case(101)
+    L = c["u"].shape[1]
+    y, last = _vl(scan_varlen, c, [L] * c["u"].shape[0])
+    y0, last0 = scan_from(c["u"], c["x"], c["A"], c["B"], c["C"], c["D"], c["z"], c["bias"], True, c["h0"])
+    assert np.array_equal(y, y0) and np.array_equal(last, last0)
+
+
+def check_varlen_padding_ignored(scan_from, scan_varlen):
+    """Values past a sequence's length (here huge and NaN) change nothing: they are never read."""
+    c, rng = _varlen_case(102)
+    lens = [0, 1, 20, c["u"].shape[1]]
+    y, last = _vl(scan_varlen, c, lens)
+    d = {k: np.array(c[k], dtype=np.float64) for k in ("u", "x", "B", "C", "z")}
+    for b, lb in enumerate(lens):
+        for k in d:
+            d[k][b, lb:] = np.nan if k in ("u", "B") else 1e30
+    y2, last2 = _vl(scan_varlen, c, lens, **d)
+    assert np.array_equal(y, y2, equal_nan=True) and np.array_equal(last, last2)
+    for b, lb in enumerate(lens):
+        assert np.all(np.isnan(y[b, lb:])) and np.all(np.isfinite(y[b, :lb]))
+
+
+def check_varlen_continuation(scan_from, scan_varlen):
+    """The state after a sequence's length, carried on over its remaining tokens, gives the
+    full sequence's outputs and final state (within fp64 rounding), and its outputs up to the
+    length are the full scan's: the lengths cut the recurrence, nothing else."""
+    c, _ = _varlen_case(103)
+    L = c["u"].shape[1]
+    lens = [3, 17, 30, 36]
+    y, last = _vl(scan_varlen, c, lens)
+    y0, last0 = scan_from(c["u"], c["x"], c["A"], c["B"], c["C"], c["D"], c["z"], c["bias"], True, c["h0"])
+    for b, lb in enumerate(lens):
+        assert _rel(y[b, :lb], y0[b, :lb]) < 1e-14
+        sl = (slice(b, b + 1), slice(lb, L))
+        yr, lr = scan_from(c["u"][sl], c["x"][sl], c["A"], c["B"][sl], c["C"][sl], c["D"], c["z"][sl], c["bias"],
+                           True, last[b:b + 1])
+        assert _rel(yr[0], y0[b, lb:]) < 1e-12 and _rel(lr[0], last0[b]) < 1e-12
+
+
+def check_varlen_zero_length(scan_from, scan_varlen):
+    """Length 0: the final state is the initial one (zero without it), no output."""
+    c, _ = _varlen_case(104)
+    y, last = _vl(scan_varlen, c, [0, 0, 0, 0])
+    assert np.array_equal(last, c["h0"]) and np.all(np.isnan(y))
+    y, last = _vl(scan_varlen, c, [0, 5, 0, 2], h0=None)
+    assert np.all(last[0] == 0.0) and np.all(last[2] == 0.0)
+
+
+VARLEN_CHECKS = [check_varlen_full_lengths, check_varlen_padding_ignored, check_varlen_continuation,
+                 check_varlen_zero_length]

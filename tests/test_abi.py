@@ -135,7 +135,7 @@ def test_bwd_validation(b):
 
 
 def test_flags_validated(b):
-    # unknown flag bits are rejected by the scan; the backward takes the softplus bit only
+    # unknown flag bits are rejected by the scan and by the backward
     P = ctypes.c_void_p
     d = _dims(b)
     ws = b.lib.ssm_scan_workspace_bytes(ctypes.byref(d))
@@ -144,14 +144,15 @@ def test_flags_validated(b):
                                   None, ctypes.byref(d), P(FAKE), ws_bytes, None)
     for flags in (8, 1 << 20, -1):
         assert fwd(flags) == -8 and "flag" in b.last_error()
-    # checkpoints for the backward: not with the exact ZOH, and the workspace must hold them
-    assert fwd(1 | 2 | 4) == -8 and "ZOH" in b.last_error()
+    # checkpoints for the backward (also with the exact ZOH): the workspace must hold them
+    assert fwd(1 | 2 | 4) == -6
     assert fwd(1 | 4) == -6
     ckpt = b.lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(d))
     assert fwd(1 | 4, ckpt + ws - 16) == -6
-    assert _bwd(b, d, softplus=3) == -8 and "ZOH" in b.last_error()
-    assert _bwd(b, d, softplus=2) == -8
-    assert _bwd(b, d, softplus=1 | 8) == -8
+    # the backward takes softplus, the exact ZOH and checkpoints (rejected here for the workspace)
+    assert _bwd(b, d, softplus=3, ws_bytes=16) == -6
+    assert _bwd(b, d, softplus=2 | 4, ws_bytes=16) == -6
+    assert _bwd(b, d, softplus=1 | 8) == -8 and "flag" in b.last_error()
 
 
 def test_conv_validation(b):

@@ -31,7 +31,7 @@ def _values(a, io):
     return inputs.bf16_to_f32(a) if io == "bf16" else a
 
 
-def run_both(oracle_mod, case, seed, with_state=True, channels=None):
+def run_both(oracle_mod, case, seed, with_state=True, channels=None, exact_zoh=False):
     rng = np.random.default_rng(seed)
     bsz, L, D, N = case.bsz, case.L, case.D, case.N
     dy = _io_array(rng.standard_normal((bsz, L, D), dtype=np.float32), case.io)
@@ -44,7 +44,7 @@ def run_both(oracle_mod, case, seed, with_state=True, channels=None):
                          delta_bias=t["delta_bias"], softplus=case.softplus,
                          initial_state=None if h0 is None else torch.from_numpy(h0).cuda(),
                          dlast_state=None if dlast is None else torch.from_numpy(dlast).cuda(),
-                         want_initial_state_grad=with_state)
+                         want_initial_state_grad=with_state, exact_zoh=exact_zoh)
     torch.cuda.synchronize()
     got = {k: to_host_f64(v) for k, v in g.items()}
     sel = slice(None) if channels is None else np.asarray(channels)
@@ -55,7 +55,7 @@ def run_both(oracle_mod, case, seed, with_state=True, channels=None):
                               z=None if zv is None else zv[:, :, sel],
                               delta_bias=None if case.delta_bias is None else case.delta_bias[sel],
                               softplus=case.softplus, h0=None if h0 is None else h0[:, sel],
-                              dlast=None if dlast is None else dlast[:, sel])
+                              dlast=None if dlast is None else dlast[:, sel], exact_zoh=exact_zoh)
     if channels is not None:
         got = {k: (v[:, :, sel] if v.ndim == 3 and k in IO_OUT else
                    v[sel] if k in ("dA", "dD", "ddelta_bias") else
@@ -132,3 +132,61 @@ def test_bwd_zero_length():
     torch.cuda.synchronize()
     assert torch.equal(g["dinitial_state"], dlast)
     assert torch.count_nonzero(g["dA"]) == 0 and torch.count_nonzero(g["dD"]) == 0
+
+
+# --- the exact zero-order hold -------------------------------------------------------------------
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("D", [70, 128])
+def test_bwd_zoh_small(oracle_mod, io, N, D):
+    """Gradients of the exact-ZOH scan (input coefficient (exp(delta A) - 1) / A): every
+    gradient against the oracle's, all optional inputs present, ragged length."""
+    case = inputs.scan_case(2, 100, D, N, io, gate=True, seed=180 + N)
+    got, ref = run_both(oracle_mod, case, seed=181, exact_zoh=True)
+    check_grads(case, got, ref, f"zoh D={D}")
+
+
+def test_bwd_zoh_small_and_zero_A(oracle_mod):
+    """A with entries exactly 0, of size 1e-6 and of size 1e-2 (|delta A| on both sides of the
+    switch between the series and the closed form of d coefficient / dA)."""
+    import dataclasses
+    case = inputs.scan_case(2, 120, 64, 16, "f32", gate=True, seed=182)
+    A = case.A.copy()
+    A[:, 0] = 0.0
+    A[:, 1:6] *= 1e-6
+    A[:, 6:11] *= 1e-2
+    case = dataclasses.replace(case, A=A.astype(np.float32))
+    got, ref = run_both(oracle_mod, case, seed=183, exact_zoh=True)
+    check_grads(case, got, ref, "zoh small A")
+
+
+def test_bwd_zoh_layer_sampled(oracle_mod):
+    """B2 L1024 D512 N16 bf16 with the exact ZOH: sampled channels against the oracle."""
+    case = inputs.scan_case(2, 1024, 512, 16, "bf16", gate=True, seed=184)
+    sel = np.unique(np.array([0, 1, 63, 64, 255, 256, 447, 510, 511]))
+    got, ref = run_both(oracle_mod, case, seed=185, channels=sel, exact_zoh=True)
+    check_grads(case, got, ref, "zoh layer sampled")
+
+
+def test_bwd_zoh_from_training_forward(oracle_mod):
+    """The exact-ZOH training forward (SSM_SCAN_CHECKPOINTS) stores the checkpoints the ZOH
+    backward then reads: y as without checkpoints (bitwise), and the per-element gradients
+    bitwise those of the backward's own recompute."""
+    case = inputs.scan_case(2, 300, 128, 16, "bf16", gate=True, seed=186)
+    t = case_tensors(case, torch)
+    args = (t["u"], t["delta"], t["A"], t["B"], t["C"])
+    kw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"], softplus=True)
+    y0, ls0 = ssmscan.scan_fwd(*args, exact_zoh=True, chunk_len=-1, **kw)
+    y1, ls1, ws = ssmscan.scan_fwd(*args, exact_zoh=True, chunk_len=-1, save_checkpoints=True, **kw)
+    dy = to_dev(inputs.bf16_bits(np.random.default_rng(187).standard_normal((case.bsz, case.L, case.D),
+                                                                             dtype=np.float32)), torch)
+    g0 = ssmscan.scan_bwd(dy, *args, exact_zoh=True, **kw)
+    g1 = ssmscan.scan_bwd(dy, *args, exact_zoh=True, checkpoints=ws, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(ls0, ls1)
+    for k in IO_OUT:
+        assert torch.equal(g0[k], g1[k]), k
+    for k in ("dA", "dB", "dC", "dD", "ddelta_bias"):
+        e = raw_error(to_host_f64(g1[k]), to_host_f64(g0[k]))
+        assert e <= 1e-6, (k, e)

@@ -205,3 +205,15 @@ def test_bwd_zoh_pins(oracle_mod, check):
 
 def test_bwd_zoh_zero_A(oracle_mod):
     pins.check_bwd_zoh_zero_A(_scan_from_zoh(oracle_mod), _scan_bwd_zoh(oracle_mod), _scan_bwd(oracle_mod))
+
+
+def _scan_varlen(oracle_mod):
+    def f(u, x, A, B, C, lens, D, z, bias, softplus, h0):
+        return oracle_mod.scan_varlen(u, x, A, B, C, lens, D=D, z=z, delta_bias=bias, softplus=softplus, threads=2,
+                                      h0=h0)
+    return f
+
+
+@pytest.mark.parametrize("check", pins.VARLEN_CHECKS, ids=lambda c: c.__name__)
+def test_varlen_pins(oracle_mod, check):
+    check(_scan_from(oracle_mod), _scan_varlen(oracle_mod))
