@@ -151,9 +151,9 @@ SSMSCAN_API int ssm_scan_plan_info(const ssm_dims *dims, int cu_count, ssm_plan_
  *                    carry's chunk states, or the split schedule's handed-over states and
  *                    flags); may be NULL when that size is 0.  With SSM_SCAN_CHECKPOINTS (a training
  *                    forward) it must hold ssm_scan_bwd_workspace_bytes(dims) +
- *                    ssm_scan_workspace_bytes(dims) bytes, and the call leaves in its first
- *                    ssm_scan_bwd_workspace_bytes(dims) bytes the states ssm_scan_bwd would
- *                    otherwise recompute in a pass of its own: pass the same workspace and
+ *                    ssm_scan_workspace_bytes(dims) bytes, and the call leaves at its start
+ *                    (batch * ceil(seqlen / 8) * dim * dstate fp32) the states ssm_scan_bwd
+ *                    would otherwise recompute in a pass of its own: pass the same workspace and
  *                    flag to ssm_scan_bwd.  The checkpoints are the states before every 8th
  *                    token, so with this flag a chunked plan's chunk length (dims->chunk_len
  *                    > 0, or the library's choice) is rounded up to a multiple of 8
@@ -213,8 +213,11 @@ SSMSCAN_API int ssm_scan_fwd_varlen(const float *initial_state, const int32_t *s
                                     size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace ssm_scan_bwd needs: the checkpointed states, one per 8
- * tokens (batch * ceil(seqlen / 8) * dim * dstate fp32, 256-byte aligned).  Returns 0 for
- * an invalid or empty problem. */
+ * tokens (batch * ceil(seqlen / 8) * dim * dstate fp32, 256-byte aligned), followed, for
+ * shapes the library runs under the split schedule (see ssm_plan_info), by that schedule's
+ * hand-over scratch (states and flags of the checkpoint pass and of the reverse walk).
+ * Depends on the current device's CU count.
+ * Returns 0 for an invalid or empty problem. */
 SSMSCAN_API size_t ssm_scan_bwd_workspace_bytes(const ssm_dims *dims);
 
 /* Gradients of ssm_scan_fwd_from (and so of ssm_scan_fwd, initial_state NULL) with respect

@@ -27,11 +27,23 @@
 //      (the wave's S states x kBwdTile tokens) and the partial readouts p,
 //   3. walks the tile backwards, accumulating dA in registers, writing per-wave partial du
 //      and d delta to LDS, and summing the dB / dC contributions of the tile's 64 channels
-//      through a wave-private LDS transposition, added to global memory atomically (the
-//      transposition of one token overlaps the arithmetic of the next),
+//      across the wave's lanes in registers (a reduce-scatter over lane exchanges), added to
+//      global memory atomically,
 //   4. finishes du, d delta, dz and the dD / d delta_bias sums per element (all threads).
 // dA, dB, dC, dD and d delta_bias are sums over workgroups and are accumulated with atomic
 // adds into buffers the host has zeroed; their summation order is not fixed.
+//
+// Split schedule (n_split > 0), as in the forward kernel but mirrored in time: the grid holds
+// n_full + 2 n_split workgroups; ids [0, n_full) take whole tiles, ids [n_full, n_full +
+// n_split) take the tokens from j_mid * kBwdTile to the end of tiles n_full .. n_tiles-1 and
+// hand over the adjoint G they reach at that token (hand, then hflag), ids [n_full + n_split,
+// n_full + 2 n_split) wait for it and take tokens [0, j_mid * kBwdTile) of the same tiles.
+// Every CU then holds the same amount of work (two whole tiles and one part at 2.5 tiles per
+// CU).  The per-element gradients are bitwise those of the whole tile.  A second part whose
+// hand-over does not come within wait_ticks forms G itself from the adjoint recurrence
+// alone over the first part's tokens (G <- exp(delta A) (C dp + G), no states needed), so no
+// placement can hang the kernel and no contribution is counted twice.  hflag must be zero at
+// launch.
 #pragma once
 
 #include "scan_kernels.h"
@@ -59,13 +71,44 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
-// Orders this wave's LDS accesses around an exchange between its lanes.  A wavefront's
-// own LDS operations are performed in the order it issues them, so no wait is needed:
-// the fences only keep the compiler from moving memory accesses across this point.
-__device__ __forceinline__ void wave_lds_fence() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// Sums over the wave's 64 lanes of NV values per lane (NV = 2, 4 or 8), as a reduce-scatter
+// in registers: value j ends up summed in the lanes of group j (64 / NV consecutive lanes),
+// whose last lane returns the total.  The halves of the values are exchanged between lanes
+// l and l ^ 32 (v_permlane32_swap: the upper 32 lanes of its first operand trade places with
+// the lower 32 of its second) and added, then between l and l ^ 16 (v_permlane16_swap: odd
+// 16-lane rows of the first operand with even rows of the second), then, for NV = 8, between
+// l and l ^ 8 within each row (DPP row rotation by 8); each step halves the values per lane.
+// The remaining group is summed with group_sum.
+template <int NV>
+__device__ __forceinline__ float lanes_reduce_scatter(const float (&v)[NV], int lane) {
+    static_assert(NV == 2 || NV == 4 || NV == 8, "2, 4 or 8 values");
+    auto add_pair = [](float a, float b, bool rows16) {
+        const auto p = rows16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false)
+                              : __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    };
+    float r[NV / 2];
+#pragma unroll
+    for (int k = 0; k < NV / 2; ++k) r[k] = add_pair(v[k], v[k + NV / 2], false);   // [v_k | v_k+NV/2]
+    if constexpr (NV == 2) {
+        return group_sum<32>(r[0]);
+    } else {
+        float q[NV / 4];
+#pragma unroll
+        for (int k = 0; k < NV / 4; ++k) q[k] = add_pair(r[k], r[k + NV / 4], true);
+        if constexpr (NV == 4) {
+            return group_sum<16>(q[0]);   // row j holds value j
+        } else {
+            // rows hold (v0, v2, v4, v6) in q[0] and (v1, v3, v5, v7) in q[1]: lanes 0-7 of a
+            // row keep q[0], lanes 8-15 keep q[1], each adding the other half's copy
+            const bool lo = (lane & 8) == 0;
+            const float keep = lo ? q[0] : q[1];
+            const float send = lo ? q[1] : q[0];
+            const float t = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), 0x128, 0xf,
+                                                                              0xf, false));   // row_ror:8
+            return group_sum<8>(t);
+        }
+    }
 }
 
 // Register budget: with 4 waves per workgroup three workgroups share a CU (LDS allows it),
@@ -79,7 +122,9 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
                 const float *__restrict__ ckpt, const float *__restrict__ dlast, IO *__restrict__ du,
                 IO *__restrict__ ddelta, IO *__restrict__ dz, float *__restrict__ dA, float *__restrict__ dB,
                 float *__restrict__ dC, float *__restrict__ dD, float *__restrict__ dbias,
-                float *__restrict__ dh0, int64_t L, int64_t D, int tiles_per_b, int softplus) {
+                float *__restrict__ dh0, int64_t L, int64_t D, int tiles_per_b, int softplus, int n_full = 0,
+                int n_split = 0, int j_mid = 0, float *__restrict__ hand = nullptr, int *__restrict__ hflag = nullptr,
+                unsigned long long wait_ticks = 0) {
     constexpr int S = BwdShape<N>::S;
     constexpr int K = BwdShape<N>::K;
     constexpr int T = kBwdTile;
@@ -99,9 +144,6 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
     __shared__ float s_p[K][T][kChanTile];         // partial readouts, per wave
     __shared__ float s_du[K][T][kChanTile];        // partial du, per wave
     __shared__ float s_dd[K][T][kChanTile];        // partial d delta, per wave
-    // per-wave transposition for dB / dC.  Lane (rk, rgrp) sums row rk at columns rgrp +
-    // LPV i; rows are 72 words apart, so each group of 32 lanes reads 32 distinct banks.
-    __shared__ float s_red[K][NV][64 + 8];
     __shared__ float s_bc[T][2][N];                // the tile's B and C rows, widened to fp32
     __shared__ float s_dbc[T][2][N];               // the tile's dB / dC sums over its 64 channels
     static_assert(T * 2 * N <= 64 * K, "one B / C element per thread");
@@ -111,7 +153,15 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rsub = tid / GPR;
     const int cq = (tid % GPR) * V;
-    const int tile = blockIdx.x;
+    int tile = blockIdx.x, role = kWhole;
+    if (n_split > 0 && tile >= n_full) {
+        if (tile < n_full + n_split) {
+            role = kFirstPart;   // the later tokens, first
+        } else {
+            tile -= n_split;
+            role = kSecondPart;  // the earlier tokens, from the handed-over adjoint
+        }
+    }
     const int b = tile / tiles_per_b;
     const int64_t d0 = (int64_t)(tile - b * tiles_per_b) * kChanTile;
     const int64_t d = d0 + lane;
@@ -158,6 +208,8 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
     };
 
     const int n_tiles = (int)((L + T - 1) / T);
+    const int j_first = role == kSecondPart ? j_mid - 1 : n_tiles - 1;   // tiles j_first down to j_last
+    const int j_last = role == kFirstPart ? j_mid : 0;
     const int rk = lane / LPV, rgrp = lane % LPV;   // the dB / dC entry this lane sums
     Raw ru[P], rx[P], ry[P], rz[P];
     uint32_t rbc = 0;
@@ -182,10 +234,59 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
         }
 #pragma unroll
         for (int s = 0; s < S; ++s)
-            hn[s] = act ? ckpt[(((int64_t)b * n_ckpt + jj) * D + d) * N + w * S + s] : 0.0f;
+            hn[s] = act ? ckpt[ckpt_index(b, jj, n_ckpt, w, K, D, d, S, s)] : 0.0f;
     };
-    fetch(n_tiles - 1);
-    for (int j = n_tiles - 1; j >= 0; --j) {
+    if (role == kFirstPart) __builtin_amdgcn_s_setprio(3);
+    if (role == kSecondPart) {
+        // wait for the first part's adjoint (wave 0 polls; the others wait at the barrier)
+        __shared__ int s_handed;
+        if (tid < 64) {
+            const unsigned long long w0 = __builtin_amdgcn_s_memrealtime();
+            int okh = 0;
+            for (;;) {
+                if (__hip_atomic_load(&hflag[tile - n_full], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+                    okh = 1;
+                    break;
+                }
+                if (__builtin_amdgcn_s_memrealtime() - w0 > wait_ticks) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+            if (tid == 0) s_handed = okh;
+        }
+        __syncthreads();
+        if (s_handed) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            if (act) {
+#pragma unroll
+                for (int s = 0; s < S; ++s) G[s] = hand[((int64_t)(tile - n_full) * kChanTile + lane) * N + w * S + s];
+            }
+        } else if (act) {
+            // no hand-over: the adjoint over the first part's tokens, from dlast, with the
+            // arithmetic of the reverse walk below (lambda = C dp + G, G = exp(delta A) lambda)
+            const float bb = bias ? bias[d] : 0.0f;
+            for (int64_t t = L - 1; t >= (int64_t)j_mid * T; --t) {
+                const int64_t e = (row0 + t) * D + d;
+                const float x = io<IO>::ld(delta, e) + bb;
+                float sg;
+                const float dl = softplus ? (sizeof(IO) == 2 ? softplus_short_f32(x, sg) : softplus_f32(x, sg)) : x;
+                const float yy = io<IO>::ld(dy, e);
+                float dp = yy;
+                if (gated) {
+                    const float zz = io<IO>::ld(z, e);
+                    dp = yy * (zz * sigmoid_f32(zz));
+                }
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    const float cc = io<IO>::ld(Cm, (row0 + t) * N + w * S + s);
+                    const float lam = fmaf(cc, dp, G[s]);
+                    G[s] = hw_exp2(dl * a2[s]) * lam;
+                }
+            }
+        }
+        __builtin_amdgcn_s_setprio(2);
+    }
+    fetch(j_first);
+    for (int j = j_first; j >= j_last; --j) {
         const int64_t t0 = (int64_t)j * T;
         const int nt = (int)min((int64_t)T, L - t0);
 
@@ -229,7 +330,7 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
         float hs[S];
 #pragma unroll
         for (int s = 0; s < S; ++s) hs[s] = hn[s];
-        if (j > 0) fetch(j - 1);
+        if (j > j_last) fetch(j - 1);
         __syncthreads();
 
         // 2. recompute the tile's states from its checkpoint, keeping h_t and exp(delta_t A)
@@ -261,26 +362,9 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
         // h_{t-1} (= the new G times h_{t-1}):
         //   dA += delta r,   d delta = sum_n A r + u q,   du = delta q,   q = sum_n lambda B,
         //   dB = lambda delta u,   dC = dp h_t.
-        // The dB / dC sums over the wave's 64 channels go through LDS: a token's values are
-        // transposed at the start of the next (earlier) token's step, after that token's
-        // inputs are requested, and summed at its end.
-        float pr[NV], rvp[NV];
-        auto transpose = [&]() {   // rvp -> pr: lane (rk, rgrp) gets row rk at columns rgrp + LPV i
-#pragma unroll
-            for (int k = 0; k < NV; ++k) s_red[w][k][lane] = rvp[k];
-            wave_lds_fence();
-#pragma unroll
-            for (int i = 0; i < NV; ++i) pr[i] = s_red[w][rk][rgrp + LPV * i];
-            wave_lds_fence();
-        };
-        auto finish = [&](int tt) {   // complete the channel sums of token tt
-#pragma unroll
-            for (int m = 1; m < NV; m *= 2)
-#pragma unroll
-                for (int i = 0; i + m < NV; i += 2 * m) pr[i] += pr[i + m];
-            const float part = group_sum<LPV>(pr[0]);
-            if (rgrp == LPV - 1) s_dbc[tt][rk < S ? 0 : 1][w * S + rk % S] = part;
-        };
+        // The dB / dC sums over the wave's 64 channels are reduced across lanes in registers
+        // (lanes_reduce_scatter); the last lane of group rk writes entry rk to LDS.
+        float rvp[NV];
 #pragma unroll
         for (int tt = T - 1; tt >= 0; --tt) {
             const f32x2_t dk = s_dk[tt][lane];   // (delta, delta*u)
@@ -291,7 +375,6 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
                 Bs[s] = s_bc[tt][0][w * S + s];
                 Cs[s] = s_bc[tt][1][w * S + s];
             }
-            if (tt < T - 1) transpose();
             float q = 0.0f, qe = 0.0f, ddA = 0.0f;   // ddA = sum_n A r / ln 2
 #pragma unroll
             for (int s = 0; s < S; ++s) {
@@ -318,10 +401,9 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
             }
             s_du[w][tt][lane] = ZOH ? q : dk.x * q;
             s_dd[w][tt][lane] = fmaf(ud.x, ZOH ? qe : q, ddA * kLn2);
-            if (tt < T - 1) finish(tt + 1);
+            const float part = lanes_reduce_scatter<NV>(rvp, lane);
+            if (rgrp == LPV - 1) s_dbc[tt][rk < S ? 0 : 1][w * S + rk % S] = part;
         }
-        transpose();
-        finish(0);
         __syncthreads();
 
         // 4. add the tile's dB / dC sums out (one element per thread), finish the
@@ -371,8 +453,17 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             unsafeAtomicAdd(dA + d * N + w * S + s, dA_acc[s]);
-            if (dh0) dh0[((int64_t)b * D + d) * N + w * S + s] = G[s];
+            if (role == kFirstPart)
+                hand[((int64_t)(tile - n_full) * kChanTile + lane) * N + w * S + s] = G[s];
+            else if (dh0)
+                dh0[((int64_t)b * D + d) * N + w * S + s] = G[s];
         }
+    }
+    if (role == kFirstPart) {
+        // hand the adjoint over: stores, release at device scope, then the flag
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();
+        if (tid == 0) __hip_atomic_store(&hflag[tile - n_full], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (qact) {
 #pragma unroll

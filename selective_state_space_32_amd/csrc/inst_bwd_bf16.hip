@@ -3,10 +3,10 @@
 #include "launch.h"
 
 namespace ssmlib {
-template int launch_bwd<1, uint16_t>(const BwdArgs &, const ssm_dims *, void *, hipStream_t);
-template int launch_bwd<2, uint16_t>(const BwdArgs &, const ssm_dims *, void *, hipStream_t);
-template int launch_bwd<4, uint16_t>(const BwdArgs &, const ssm_dims *, void *, hipStream_t);
-template int launch_bwd<8, uint16_t>(const BwdArgs &, const ssm_dims *, void *, hipStream_t);
-template int launch_bwd<16, uint16_t>(const BwdArgs &, const ssm_dims *, void *, hipStream_t);
+template int launch_bwd<1, uint16_t>(const BwdArgs &, const ssm_dims *, const Plan &, size_t, void *, hipStream_t);
+template int launch_bwd<2, uint16_t>(const BwdArgs &, const ssm_dims *, const Plan &, size_t, void *, hipStream_t);
+template int launch_bwd<4, uint16_t>(const BwdArgs &, const ssm_dims *, const Plan &, size_t, void *, hipStream_t);
+template int launch_bwd<8, uint16_t>(const BwdArgs &, const ssm_dims *, const Plan &, size_t, void *, hipStream_t);
+template int launch_bwd<16, uint16_t>(const BwdArgs &, const ssm_dims *, const Plan &, size_t, void *, hipStream_t);
 
 }  // namespace ssmlib

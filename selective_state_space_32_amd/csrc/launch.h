@@ -227,10 +227,30 @@ struct BwdArgs {
     float *dbias, *dh0;
     bool ckpt_given;   // the workspace already holds the checkpoints (written by the training forward)
     bool zoh;          // the exact zero-order-hold input term
+    ssm::FillList zero;   // the accumulators to zero before the walk (the hand-over flags are added)
 };
 
+// Adds a buffer of n 32-bit words to a fill list (skipped when null or empty).
+inline void fill_list_add(ssm::FillList &f, void *p, int64_t n) {
+    if (p && n > 0 && f.count < ssm::kMaxFill) {
+        f.p[f.count] = static_cast<uint32_t *>(p);
+        f.n[f.count] = n;
+        ++f.count;
+    }
+}
+
+inline void launch_fill_list(const ssm::FillList &f, hipStream_t st) {
+    int64_t most = 0;
+    for (int k = 0; k < f.count; ++k) most = f.n[k] > most ? f.n[k] : most;
+    if (most == 0) return;
+    const int64_t blocks = std::min<int64_t>((most + 255) / 256, 2048);
+    hipLaunchKernelGGL(ssm::fill_zero_many_kernel, dim3((unsigned)blocks), dim3(256), 0, st, f);
+}
+
+// sp: the plan of the checkpoint pass (the split schedule, or a one-pass grid); its workspace
+// follows the checkpoints, at ckpt_bytes.
 template <int N, typename IO>
-int launch_bwd(const BwdArgs &a, const ssm_dims *dm, void *ws, hipStream_t st) {
+int launch_bwd(const BwdArgs &a, const ssm_dims *dm, const Plan &sp, size_t ckpt_bytes, void *ws, hipStream_t st) {
     constexpr int S = ScanShape<N>::S, T = ScanShape<N>::T, K = N / S;
     constexpr int KB = ssm::BwdShape<N>::K;
     const int64_t bsz = dm->batch, L = dm->seqlen, D = dm->dim;
@@ -241,16 +261,36 @@ int launch_bwd(const BwdArgs &a, const ssm_dims *dm, void *ws, hipStream_t st) {
     const IO *z = static_cast<const IO *>(a.z), *dy = static_cast<const IO *>(a.dy);
     IO *du = static_cast<IO *>(a.du), *ddl = static_cast<IO *>(a.ddelta), *dz = static_cast<IO *>(a.dz);
     float *ckpt = static_cast<float *>(ws);
+    // the split schedule's hand-over scratch follows the checkpoints: the checkpoint pass and
+    // the reverse walk use its states in turn, each with flags of its own (a second flag array
+    // after the plan's); the flags are cleared with the accumulators, in one launch
+    const bool split = sp.schedule == kSplit;
+    char *spw = static_cast<char *>(ws) + ckpt_bytes;
+    int *flags = split ? reinterpret_cast<int *>(spw + sp.off_flags) : nullptr;
+    int *wflags = split ? reinterpret_cast<int *>(spw + sp.bytes) : nullptr;
+    float *hand = split ? reinterpret_cast<float *>(spw + sp.off_hand) : nullptr;
+    ssm::FillList zl = a.zero;
+    if (split) {
+        fill_list_add(zl, flags, sp.n_split);
+        fill_list_add(zl, wflags, sp.n_split);
+    }
+    launch_fill_list(zl, st);
     // forward in checkpoint mode: the state before every kCkptEvery-th token (unless the
     // training forward has stored them already)
     const bool vf = D % 8 == 0 && aligned(u, 16) && aligned(dl, 16);
     if (!a.ckpt_given) {
+        // (under the split schedule, as the forward: part of the tiles as two token halves, the
+        // second started from the state the first hands over; the checkpoints are the same)
+        const unsigned groups = split ? (unsigned)(sp.n_full + 2 * sp.n_split) : (unsigned)n_tiles;
         auto ckpt_pass = [&](auto vec_c, auto zoh_c) {
             hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kCheckpoint, decltype(vec_c)::value,
                                                        decltype(zoh_c)::value>),
-                               dim3((unsigned)n_tiles, 1), dim3(64 * K), 0, st, u, dl, (const IO *)nullptr,
-                               (IO *)nullptr, a.A, (const float *)nullptr, a.bias, B, C, a.h0, (float *)nullptr, ckpt,
-                               (float *)nullptr, L, D, tiles_per_b, n_tiles, L, 1, a.softplus);
+                               dim3(groups, 1), dim3(64 * K), 0, st, u, dl, (const IO *)nullptr, (IO *)nullptr, a.A,
+                               (const float *)nullptr, a.bias, B, C, a.h0, (float *)nullptr, ckpt, (float *)nullptr,
+                               L, D, tiles_per_b, n_tiles, L, 1, a.softplus, (const float *)nullptr,
+                               (const float *)nullptr, (IO *)nullptr, (float *)nullptr, split ? (int)sp.n_full : 0,
+                               split ? (int)sp.n_split : 0, split ? sp.l_mid : (int64_t)0, hand, flags,
+                               split ? handover_wait_ticks() : 0ull, (const int32_t *)nullptr);
         };
         using T1 = std::true_type;
         using F0 = std::false_type;
@@ -262,11 +302,15 @@ int launch_bwd(const BwdArgs &a, const ssm_dims *dm, void *ws, hipStream_t st) {
     // the reverse walk; 16-byte (or 8-byte) element access when every (token, channel) tensor allows it
     const bool vb = D % 8 == 0 && aligned(u, 16) && aligned(dl, 16) && aligned(dy, 16) && aligned(du, 16) &&
                     aligned(ddl, 16) && (!z || (aligned(z, 16) && aligned(dz, 16)));
+    // (under the split schedule too: the later half of a split tile hands the adjoint over)
+    const unsigned wgroups = split ? (unsigned)(sp.n_full + 2 * sp.n_split) : (unsigned)n_tiles;
     auto walk = [&](auto vec_c, auto zoh_c) {
         hipLaunchKernelGGL((ssm::scan_bwd_kernel<N, IO, decltype(vec_c)::value, decltype(zoh_c)::value>),
-                           dim3((unsigned)n_tiles), dim3(64 * KB), 0, st, u, dl, z, dy, a.A, a.D, a.bias, B, C, ckpt,
-                           a.dlast, du, ddl, dz, a.dA, a.dB, a.dC, a.dD, a.dbias, a.dh0, L, D, tiles_per_b,
-                           a.softplus);
+                           dim3(wgroups), dim3(64 * KB), 0, st, u, dl, z, dy, a.A, a.D, a.bias, B, C, ckpt, a.dlast, du,
+                           ddl, dz, a.dA, a.dB, a.dC, a.dD, a.dbias, a.dh0, L, D, tiles_per_b, a.softplus,
+                           split ? (int)sp.n_full : 0, split ? (int)sp.n_split : 0,
+                           split ? (int)(sp.l_mid / ssm::kBwdTile) : 0, hand, wflags,
+                           split ? handover_wait_ticks() : 0ull);
     };
     if (vb && a.zoh) walk(std::true_type{}, std::true_type{});
     else if (vb) walk(std::true_type{}, std::false_type{});

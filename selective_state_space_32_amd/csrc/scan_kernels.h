@@ -43,6 +43,14 @@ enum SplitRole { kWhole = 0, kFirstPart = 1, kSecondPart = 2 };
 // kCheckpoint stores the state before every kCkptEvery-th token (for the backward pass).
 constexpr int kCkptEvery = 8;
 
+// Index of state s of wave w (states w*S .. w*S+S-1 of channel d) in checkpoint ck of sequence b:
+// the layout is [b][ck][w][d][S], so that the S states of the 64 channels a wave holds are one
+// contiguous span (its store and its load are whole cache lines).
+__device__ __forceinline__ int64_t ckpt_index(int64_t b, int64_t ck, int64_t n_ckpt, int w, int K, int64_t D,
+                                              int64_t d, int S, int s) {
+    return (((b * n_ckpt + ck) * K + w) * D + d) * S + s;
+}
+
 // s_waitcnt immediate that waits for all LDS and scalar-memory operations (lgkmcnt = 0) and
 // leaves the vector-memory and export counters unconstrained (gfx9 encoding).
 constexpr int kWaitLgkm0 = 0xC07F;
@@ -84,8 +92,8 @@ __device__ __forceinline__ void load_slice(const IO *__restrict__ p, int64_t off
 //   kSummary: start from h = 0, no readout; write the chunk's local final state to
 //             cstate[b][c] and the chunk's sum of step sizes to cdsum[b][c].
 //   kCheckpoint: one pass from h0 without readout, storing the state before every
-//             kCkptEvery-th token to cstate[b][t / kCkptEvery] (the backward pass's
-//             recomputation points).
+//             kCkptEvery-th token to cstate at checkpoint t / kCkptEvery (ckpt_index: the
+//             backward pass's recomputation points).
 //   CK (kFull): the same checkpoints, to ckpt_out, from the forward itself (a training
 //             forward; the backward then skips its kCheckpoint pass).  With the convolution
 //             (CW > 0) the training forward scans u rounded to the I/O type, the values the
@@ -182,7 +190,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
 
     const int64_t item = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
     int role = kWhole, c = 0, tile;
-    if (MODE == kFull && n_split > 0) {
+    if ((MODE == kFull || MODE == kCheckpoint) && n_split > 0) {
         const int g = (int)item;
         if (g >= n_full + 2 * n_split) return;
         if (g < n_full) {
@@ -409,12 +417,11 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
         __syncthreads();
     }
     // kCheckpoint (and kFull with CK, the training forward): the state before token t (t a
-    // multiple of kCkptEvery) into cstate (ckpt_out)[b][t / kCkptEvery][d][:]
+    // multiple of kCkptEvery) into cstate (ckpt_out) at checkpoint t / kCkptEvery
     const int64_t n_ckpt = (L + kCkptEvery - 1) / kCkptEvery;
     auto checkpoint = [&](int64_t t) {
         if ((MODE == kCheckpoint || (MODE == kFull && CK)) && act && t < t_end) {
-            float *dst = (MODE == kCheckpoint ? cstate : ckpt_out) +
-                         (((int64_t)b * n_ckpt + t / kCkptEvery) * D + d) * N + w * S;
+            float *dst = (MODE == kCheckpoint ? cstate : ckpt_out) + ckpt_index(b, t / kCkptEvery, n_ckpt, w, K, D, d, S, 0);
 #pragma unroll
             for (int s = 0; s < S; ++s) dst[s] = h[s];
         }
@@ -647,6 +654,20 @@ template <typename TP>
 __global__ void __launch_bounds__(256) copy_kernel(TP *__restrict__ dst, const TP *__restrict__ src, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n) dst[i] = src[i];
+}
+
+// Zeros up to kMaxFill buffers of 32-bit words in one launch (the backward's accumulators and
+// hand-over flags), each by a grid-stride loop.
+constexpr int kMaxFill = 8;
+struct FillList {
+    uint32_t *p[kMaxFill];
+    int64_t n[kMaxFill];
+    int count;
+};
+static __global__ void __launch_bounds__(256) fill_zero_many_kernel(FillList f) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int k = 0; k < f.count; ++k)
+        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < f.n[k]; i += stride) f.p[k][i] = 0u;
 }
 
 // Writes zeros (a scan of zero tokens leaves the zero initial state).

@@ -57,7 +57,7 @@ unsigned long long handover_wait_ticks() {
     extern template int launch_step<N, IO>(float *, const void *, const void *, const float *, const void *, \
                                            const void *, const float *, const void *, void *, const ssm_dims *, \
                                            hipStream_t); \
-    extern template int launch_bwd<N, IO>(const BwdArgs &, const ssm_dims *, void *, hipStream_t);
+    extern template int launch_bwd<N, IO>(const BwdArgs &, const ssm_dims *, const Plan &, size_t, void *, hipStream_t);
 #define SSM_EXTERN_IO(IO) SSM_EXTERN_N(1, IO) SSM_EXTERN_N(2, IO) SSM_EXTERN_N(4, IO) SSM_EXTERN_N(8, IO) \
     SSM_EXTERN_N(16, IO)
 SSM_EXTERN_IO(float)
@@ -234,19 +234,37 @@ int dispatch_step(int64_t N, float *state, const void *u, const void *delta, con
     return fail(SSM_ERR_UNSUPPORTED_N, "dstate %lld not supported", (long long)N);
 }
 
-size_t bwd_workspace_bytes(const ssm_dims *dm) {
+// The backward's checkpoint pass runs under the split schedule where the forward would (its
+// chunk length setting aside); any other plan is the one-pass grid.
+Plan bwd_ckpt_plan(const ssm_dims *dm) {
+    ssm_dims d = *dm;
+    d.chunk_len = 0;
+    Plan p = make_plan(&d, device_cus());
+    return p.schedule == kSplit ? p : Plan{};
+}
+
+size_t ckpt_bytes(const ssm_dims *dm) {
     const int64_t n_ckpt = (dm->seqlen + ssm::kCkptEvery - 1) / ssm::kCkptEvery;
     return align256((size_t)(dm->batch * n_ckpt * dm->dim * dm->dstate) * sizeof(float));
 }
 
+// the checkpoints, then the split schedule's scratch (hand-over states and the checkpoint
+// pass's flags), then the reverse walk's flags
+size_t bwd_workspace_bytes(const ssm_dims *dm) {
+    const Plan p = bwd_ckpt_plan(dm);
+    return ckpt_bytes(dm) + p.bytes + (p.schedule == kSplit ? align256((size_t)p.n_split * sizeof(int)) : 0);
+}
+
 template <typename IO>
 int dispatch_bwd(int64_t N, const BwdArgs &a, const ssm_dims *dm, void *ws, hipStream_t st) {
+    const Plan sp = bwd_ckpt_plan(dm);
+    const size_t cb = ckpt_bytes(dm);
     switch (N) {
-        case 1: return launch_bwd<1, IO>(a, dm, ws, st);
-        case 2: return launch_bwd<2, IO>(a, dm, ws, st);
-        case 4: return launch_bwd<4, IO>(a, dm, ws, st);
-        case 8: return launch_bwd<8, IO>(a, dm, ws, st);
-        case 16: return launch_bwd<16, IO>(a, dm, ws, st);
+        case 1: return launch_bwd<1, IO>(a, dm, sp, cb, ws, st);
+        case 2: return launch_bwd<2, IO>(a, dm, sp, cb, ws, st);
+        case 4: return launch_bwd<4, IO>(a, dm, sp, cb, ws, st);
+        case 8: return launch_bwd<8, IO>(a, dm, sp, cb, ws, st);
+        case 16: return launch_bwd<16, IO>(a, dm, sp, cb, ws, st);
     }
     return fail(SSM_ERR_UNSUPPORTED_N, "dstate %lld not supported", (long long)N);
 }
@@ -499,12 +517,15 @@ int ssm_scan_bwd(const float *initial_state, const void *u, const void *delta, c
                         need);
         if (!aligned(workspace, 16)) return fail(SSM_ERR_ALIGN, "workspace not 16-byte aligned");
     }
-    // the summed gradients are accumulated atomically: start them from zero
-    fill_zero(dA, Dm * N, st);
-    fill_zero(dB, bsz * L * N, st);
-    fill_zero(dC, bsz * L * N, st);
-    fill_zero(dD, Dm, st);
-    fill_zero(ddelta_bias, Dm, st);
+    // the summed gradients are accumulated atomically: they start from zero (one fill launch,
+    // with the split schedule's flags when the walk runs)
+    ssm::FillList zero{};
+    fill_list_add(zero, dA, Dm * N);
+    fill_list_add(zero, dB, bsz * L * N);
+    fill_list_add(zero, dC, bsz * L * N);
+    fill_list_add(zero, dD, Dm);
+    fill_list_add(zero, ddelta_bias, Dm);
+    if (bsz == 0 || Dm == 0 || L == 0) launch_fill_list(zero, st);
     if (bsz == 0 || Dm == 0) return ok();
     if (L == 0) {
         // no tokens: the state's gradient passes straight through
@@ -522,7 +543,7 @@ int ssm_scan_bwd(const float *initial_state, const void *u, const void *delta, c
     }
     BwdArgs a{initial_state, u, delta, A, B, C, D, z, delta_bias, (flags & SSM_SCAN_SOFTPLUS) != 0, dy, dlast_state, du, ddelta,
               dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, (flags & SSM_SCAN_CHECKPOINTS) != 0,
-              (flags & SSM_SCAN_EXACT_ZOH) != 0};
+              (flags & SSM_SCAN_EXACT_ZOH) != 0, zero};
     if (dims->io_dtype == SSM_IO_BF16) return dispatch_bwd<uint16_t>(N, a, dims, workspace, st);
     return dispatch_bwd<float>(N, a, dims, workspace, st);
 }

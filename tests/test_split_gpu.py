@@ -34,6 +34,12 @@ def _case(L, io, gate, seed):
     return inputs.scan_case(8, L, D, 16, io, gate=gate, seed=seed, name=f"split {io} L{L}")
 
 
+def _ckpt_bytes(case):
+    """The checkpoints at the start of a training forward's workspace: the state before every
+    8th token, fp32."""
+    return case.bsz * ((case.L + 7) // 8) * case.D * 16 * 4
+
+
 def _fwd(case, t, chunk_len, **kw):
     y, ls = ssmscan.scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
                              delta_bias=t["delta_bias"], softplus=case.softplus, chunk_len=chunk_len, **kw)
@@ -117,7 +123,7 @@ def test_split_training_forward_checkpoints():
     kw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"], softplus=True)
     y0, ls0, ws0 = ssmscan.scan_fwd(*args, chunk_len=-1, save_checkpoints=True, **kw)
     y1, ls1, ws1 = ssmscan.scan_fwd(*args, chunk_len=0, save_checkpoints=True, **kw)
-    nck = ssmscan.bwd_workspace_bytes(case.bsz, case.L, case.D, 16, torch.bfloat16)
+    nck = _ckpt_bytes(case)
     torch.cuda.synchronize()
     assert torch.equal(y0, y1) and torch.equal(ls0, ls1)
     assert torch.equal(ws0[:nck], ws1[:nck]), "checkpoints differ between the split and the one pass"
@@ -125,9 +131,12 @@ def test_split_training_forward_checkpoints():
                                                                              dtype=np.float32)), torch)
     g0 = ssmscan.scan_bwd(dy, *args, checkpoints=ws0, **kw)
     g1 = ssmscan.scan_bwd(dy, *args, checkpoints=ws1, **kw)
+    # the backward's own checkpoint pass, under the split schedule on this device
+    g2 = ssmscan.scan_bwd(dy, *args, **kw)
     torch.cuda.synchronize()
     for k in ("du", "ddelta", "dz"):
         assert torch.equal(g0[k], g1[k]), k
+        assert torch.equal(g0[k], g2[k]), k + " (checkpoint pass)"
 
 
 @pytest.mark.parametrize("ckpt", [False, True], ids=["forward", "training forward"])
@@ -147,5 +156,34 @@ def test_split_fused_convolution(ckpt):
     torch.cuda.synchronize()
     assert torch.equal(r0[0], r1[0]) and torch.equal(r0[1], r1[1]) and torch.equal(u0, u1)
     if ckpt:
-        nck = ssmscan.bwd_workspace_bytes(case.bsz, case.L, case.D, 16, torch.bfloat16)
+        nck = _ckpt_bytes(case)
         assert torch.equal(r0[2][:nck], r1[2][:nck])
+
+
+@pytest.mark.parametrize("gate", [True, False], ids=["gated", "ungated"])
+def test_split_backward_time_out_path(monkeypatch, gate):
+    """The backward under the split schedule (checkpoint pass and reverse walk) with every
+    second half giving up at once: the checkpoint pass's second halves compute whole tiles,
+    the walk's form the adjoint at the split point themselves.  The per-element gradients and
+    the initial state's gradient are bitwise those with the hand-overs; the sums over
+    workgroups (atomic, in another order) agree to rounding."""
+    case = _case(300, "bf16", gate, seed=570)
+    t = case_tensors(case, torch)
+    args = (t["u"], t["delta"], t["A"], t["B"], t["C"])
+    kw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"], softplus=True)
+    rng = np.random.default_rng(571)
+    dy = to_dev(inputs.bf16_bits(rng.standard_normal((case.bsz, case.L, case.D), dtype=np.float32)), torch)
+    dls = torch.from_numpy(rng.standard_normal((case.bsz, case.D, 16)).astype(np.float32)).cuda()
+    g0 = ssmscan.scan_bwd(dy, *args, dlast_state=dls, want_initial_state_grad=True, **kw)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("SSMSCAN_HANDOVER_WAIT_US", "0")
+    g1 = ssmscan.scan_bwd(dy, *args, dlast_state=dls, want_initial_state_grad=True, **kw)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("SSMSCAN_HANDOVER_WAIT_US")
+    keys = ("du", "ddelta", "dinitial_state") + (("dz",) if gate else ())
+    for k in keys:
+        assert torch.equal(g0[k], g1[k]), k
+    for k in ("dA", "dB", "dC", "dD", "ddelta_bias"):
+        a, b = g0[k].double(), g1[k].double()
+        e = float((a - b).abs().max() / a.abs().max().clamp_min(1e-30))
+        assert e < 1e-5, f"{k}: {e:.3g}"
