@@ -422,8 +422,14 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     auto checkpoint = [&](int64_t t) {
         if ((MODE == kCheckpoint || (MODE == kFull && CK)) && act && t < t_end) {
             float *dst = (MODE == kCheckpoint ? cstate : ckpt_out) + ckpt_index(b, t / kCkptEvery, n_ckpt, w, K, D, d, S, 0);
+            // (non-temporal: the checkpoints are read back only by the backward pass, after
+            // everything else this kernel touches)
+            if constexpr (S == 4) {
+                __builtin_nontemporal_store(f32x4_t{h[0], h[1], h[2], h[3]}, reinterpret_cast<f32x4_t *>(dst));
+            } else {
 #pragma unroll
-            for (int s = 0; s < S; ++s) dst[s] = h[s];
+                for (int s = 0; s < S; ++s) __builtin_nontemporal_store(h[s], dst + s);
+            }
         }
     };
     // epilogue of a tile: y = (sum of the K partial readouts + D u) * silu(z), read from
