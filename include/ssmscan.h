@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SSMSCAN_VERSION 11
+#define SSMSCAN_VERSION 12
 
 /* Bits of the `flags` argument of the scan entry points. */
 #define SSM_SCAN_SOFTPLUS 1     /* step size = softplus(delta + delta_bias) */
@@ -352,6 +352,17 @@ typedef struct {
 SSMSCAN_API int ssm_ssd_fwd(const void *x, const void *dt, const float *A, const void *B, const void *C,
                 const float *D, const void *z, const float *dt_bias, int flags, void *y, float *last_state,
                 const ssm_ssd_dims *dims, void *stream);
+
+/* ssm_ssd_fwd continued from a given state (a prefill in pieces, or a decode state carried into
+ * a new segment): S_{-1} = initial_state instead of zero.
+ *   initial_state : [batch][nheads][headdim][dstate] fp32, or NULL (= zero); it may be the
+ *                   last_state buffer (each element is read before it is overwritten)
+ * Running a sequence in two calls, the second from the first's last_state, equals one call
+ * (bitwise when the first piece's length is a multiple of the 64-token chunk).  With
+ * seqlen = 0, last_state receives initial_state (or zeros).  Everything else as ssm_ssd_fwd. */
+SSMSCAN_API int ssm_ssd_fwd_from(const float *initial_state, const void *x, const void *dt, const float *A,
+                const void *B, const void *C, const float *D, const void *z, const float *dt_bias, int flags,
+                void *y, float *last_state, const ssm_ssd_dims *dims, void *stream);
 
 /* One recurrent (inference) step for `batch` independent sequences: the constant-memory
  * recurrent form (shakilmahmud.com section 3; urworte.de "Methodische Grundlagen").

@@ -160,7 +160,8 @@ __device__ __forceinline__ void mma16_xn(const __bf16 *a, int a0, const __bf16 *
 }
 
 // x, z, y: [bsz][L][H][P] bf16;  dt: [bsz][L][H] bf16;  A, Dv, dt_bias: [H] fp32;
-// B, C: [bsz][L][G][N] bf16;  last_state: [bsz][H][P][N] fp32 (or null).
+// B, C: [bsz][L][G][N] bf16;  h0, last_state: [bsz][H][P][N] fp32 (or null; h0 may be
+// last_state: each thread reads its own state elements before it writes them).
 //
 // Four waves; wave w owns, in every product, the 16-row band w and the four 16 x 16 column
 // blocks j = 0..3.
@@ -176,7 +177,7 @@ static __global__ void __launch_bounds__(kSsdThreads) __attribute__((amdgpu_wave
 ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt, const float *__restrict__ A,
                  const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm, const float *__restrict__ Dv,
                  const uint16_t *__restrict__ z, const float *__restrict__ dt_bias, uint16_t *__restrict__ y,
-                 float *__restrict__ last_state, int64_t L, int H, int G, int softplus) {
+                 float *last_state, int64_t L, int H, int G, int softplus, const float *h0) {
     constexpr int Q = kSsdQ, P = kSsdP, N = kSsdN, LD = kSsdLd;
     static_assert(Q == 64 && P == 64 && N == 64, "a 16-row band and four 16 x 16 blocks per wave of four");
     constexpr bool ZC = true;                         // tC is swizzled
@@ -242,6 +243,35 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
     };
 
     f32x4_t S[4] = {};                                 // the state H [n][p]: rows n 16 qi.., columns p 16 j..
+    // the H^T [p][n] copy (high and low parts) that the next chunk's Y3 product reads:
+    // column p, four consecutive n per write
+    auto state_copy = [&]() {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int p = 16 * j + c16, n0 = 16 * qi + rq;
+            bf16x4_t hh, hl;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                __bf16 hi, lo;
+                split(S[j][e], hi, lo);
+                hh[e] = hi;
+                hl[e] = lo;
+            }
+            *reinterpret_cast<bf16x4_t *>(&tH1[sw(p, n0)]) = hh;
+            *reinterpret_cast<bf16x4_t *>(&tH2[sw(p, n0)]) = hl;
+        }
+    };
+    if (h0) {
+        // the initial state into the accumulators (the layout last_state is written in)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int p = 16 * j + c16;
+            const float *hs = h0 + (((int64_t)b * H + h) * P + p) * N + 16 * qi + rq;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[j][e] = hs[e];
+        }
+        state_copy();   // (read after barrier (1) of the first chunk)
+    }
     Raw r;
     fetch(0, r);
     const int64_t nchunks = (L + Q - 1) / Q;
@@ -278,7 +308,7 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
         const float cref = *s_c4(qi >= 2 ? 32 : 0);     // c at the first token of this band's half-chunk
         // --- Y3^T = H^T C^T (the state entering the chunk) and G^T = B C^T
         f32x4_t Y[4] = {}, Gt[4] = {};
-        if (c > 0) mma16_hl_a<N / 32, 4, ZC>(tH1, tH2, 16 * qi, tC, 0, lane, Y);
+        if (c > 0 || h0) mma16_hl_a<N / 32, 4, ZC>(tH1, tH2, 16 * qi, tC, 0, lane, Y);
         mma16_xn<N / 32, 4, ZC>(tB, 16 * qi, tC, 0, qi, lane, Gt);   // blocks j >= qi (zero for s > t)
         __syncthreads();                                // (2)
         // --- M [t][s] = G^T[s][t] exp2(c_t - c_s) dt_s (s <= t) + D (s = t): rows s of this
@@ -369,21 +399,8 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
                     reinterpret_cast<u32x4_t *>(yh + t0 * xrow + (uint32_t)tr * xr32 + (uint32_t)tu * 8));
             }
         }
-        // --- H^T [p][n] <- H (high and low parts): column p, four consecutive n per write
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int p = 16 * j + c16, n0 = 16 * qi + rq;
-            bf16x4_t hh, hl;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                __bf16 hi, lo;
-                split(S[j][e], hi, lo);
-                hh[e] = hi;
-                hl[e] = lo;
-            }
-            *reinterpret_cast<bf16x4_t *>(&tH1[sw(p, n0)]) = hh;
-            *reinterpret_cast<bf16x4_t *>(&tH2[sw(p, n0)]) = hl;
-        }
+        // --- H^T [p][n] <- H (high and low parts)
+        state_copy();
     }
     if (last_state) {
 #pragma unroll

@@ -645,6 +645,12 @@ int ssm_conv1d_bwd(const void *x, const float *w, const float *bias, int width, 
 int ssm_ssd_fwd(const void *x, const void *dt, const float *A, const void *B, const void *C, const float *D,
                 const void *z, const float *dt_bias, int flags, void *y, float *last_state, const ssm_ssd_dims *dims,
                 void *stream) {
+    return ssm_ssd_fwd_from(nullptr, x, dt, A, B, C, D, z, dt_bias, flags, y, last_state, dims, stream);
+}
+
+int ssm_ssd_fwd_from(const float *initial_state, const void *x, const void *dt, const float *A, const void *B,
+                     const void *C, const float *D, const void *z, const float *dt_bias, int flags, void *y,
+                     float *last_state, const ssm_ssd_dims *dims, void *stream) {
     if (!dims) return fail(SSM_ERR_NULL, "dims is NULL");
     const int64_t bsz = dims->batch, L = dims->seqlen, H = dims->nheads, P = dims->headdim, G = dims->ngroups,
                   N = dims->dstate;
@@ -664,18 +670,26 @@ int ssm_ssd_fwd(const void *x, const void *dt, const float *A, const void *B, co
     if (flags & ~SSM_SCAN_SOFTPLUS) return fail(SSM_ERR_FLAGS, "flags 0x%x: the SSD layer takes the softplus flag only",
                                                 flags);
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) || !aligned(z, 16) ||
-        !aligned(dt, 2) || !aligned(A, 4) || !aligned(D, 4) || !aligned(dt_bias, 4) || !aligned(last_state, 4))
+        !aligned(dt, 2) || !aligned(A, 4) || !aligned(D, 4) || !aligned(dt_bias, 4) || !aligned(last_state, 4) ||
+        !aligned(initial_state, 4))
         return fail(SSM_ERR_ALIGN, "x, z, y, B, C must be 16-byte aligned and the others aligned to their element size");
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (bsz == 0 || H == 0) return ok();
     if (!A || (L > 0 && (!x || !dt || !B || !C || !y))) return fail(SSM_ERR_NULL, "required pointer is NULL");
     if (L == 0) {
-        if (last_state) fill_zero(last_state, bsz * H * P * N, st);
+        // no tokens: the final state is the initial one
+        const int64_t n = bsz * H * P * N;
+        if (last_state && initial_state && initial_state != last_state)
+            hipLaunchKernelGGL(ssm::copy_kernel<float>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, last_state,
+                               initial_state, n);
+        else if (last_state && !initial_state)
+            fill_zero(last_state, n, st);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
         return ok();
     }
-    launch_ssd(x, dt, A, B, C, D, z, dt_bias, (flags & SSM_SCAN_SOFTPLUS) ? 1 : 0, y, last_state, bsz, L, H, G, st);
+    launch_ssd(x, dt, A, B, C, D, z, dt_bias, (flags & SSM_SCAN_SOFTPLUS) ? 1 : 0, y, last_state, bsz, L, H, G, st,
+               initial_state);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

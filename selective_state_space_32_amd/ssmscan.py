@@ -85,6 +85,8 @@ def _load() -> ctypes.CDLL:
     lib.ssm_scan_fwd_conv.restype = ctypes.c_int
     lib.ssm_ssd_fwd.argtypes = [P] * 8 + [ctypes.c_int, P, P, ctypes.POINTER(ssm_ssd_dims), P]
     lib.ssm_ssd_fwd.restype = ctypes.c_int
+    lib.ssm_ssd_fwd_from.argtypes = [P] * 9 + [ctypes.c_int, P, P, ctypes.POINTER(ssm_ssd_dims), P]
+    lib.ssm_ssd_fwd_from.restype = ctypes.c_int
     return lib
 
 
@@ -630,9 +632,11 @@ def scan_fwd_conv_call(x, conv_w, conv_b, delta, A, B, C, D=None, z=None, delta_
 def ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
             D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
             dt_bias: Optional[torch.Tensor] = None, softplus: bool = True, *, y: Optional[torch.Tensor] = None,
-            last_state: Optional[torch.Tensor] = None, return_last_state: bool = True, stream=None):
-    """Mamba-2's SSD layer (ssm_ssd_fwd).  x, z: (batch, L, H, P) bfloat16; dt: (batch, L, H)
-    bfloat16; A, D, dt_bias: (H,) float32; B, C: (batch, L, G, N) bfloat16.
+            last_state: Optional[torch.Tensor] = None, return_last_state: bool = True,
+            initial_state: Optional[torch.Tensor] = None, stream=None):
+    """Mamba-2's SSD layer (ssm_ssd_fwd; ssm_ssd_fwd_from with initial_state).  x, z:
+    (batch, L, H, P) bfloat16; dt: (batch, L, H) bfloat16; A, D, dt_bias: (H,) float32; B, C:
+    (batch, L, G, N) bfloat16; initial_state: (batch, H, P, N) float32 (may be last_state).
     Returns (y (batch, L, H, P), last_state (batch, H, P, N) float32 or None)."""
     bsz, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
@@ -649,12 +653,14 @@ def ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
         _need(z, "z", (bsz, L, H, P), bf, dev)
     if dt_bias is not None:
         _need(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", (bsz, H, P, N), torch.float32, dev)
     if y is None:
         y = torch.empty((bsz, L, H, P), dtype=bf, device=dev)
     if last_state is None and return_last_state:
         last_state = torch.empty((bsz, H, P, N), dtype=torch.float32, device=dev)
     dims = ssm_ssd_dims(bsz, L, H, P, G, N, SSM_IO_BF16, 0)
-    _check(lib.ssm_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
-                           1 if softplus else 0, _ptr(y), _ptr(last_state), ctypes.byref(dims),
-                           _stream_handle(stream)))
+    _check(lib.ssm_ssd_fwd_from(_ptr(initial_state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                _ptr(z), _ptr(dt_bias), 1 if softplus else 0, _ptr(y), _ptr(last_state),
+                                ctypes.byref(dims), _stream_handle(stream)))
     return y, last_state

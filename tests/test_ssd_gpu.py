@@ -17,22 +17,24 @@ if not torch.cuda.is_available():
 from selective_state_space_32_amd import ssmscan  # noqa: E402
 
 
-def run_gpu(c):
+def run_gpu(c, h0=None):
     dev = lambda a: None if a is None else to_dev(a, torch)   # noqa: E731
     f = lambda a: None if a is None else torch.from_numpy(a).cuda()   # noqa: E731
     y, ls = ssmscan.ssd_fwd(dev(c.x), dev(c.dt), f(c.A), dev(c.B), dev(c.C), D=f(c.Dskip), z=dev(c.z),
-                            dt_bias=f(c.dt_bias), softplus=c.softplus)
+                            dt_bias=f(c.dt_bias), softplus=c.softplus,
+                            initial_state=None if h0 is None else torch.from_numpy(h0.astype(np.float32)).cuda())
     torch.cuda.synchronize()
     return to_host_f64(y), to_host_f64(ls)
 
 
-def run_oracle(oracle_mod, c, heads=None):
+def run_oracle(oracle_mod, c, heads=None, h0=None):
     sel = slice(None) if heads is None else np.asarray(heads)
     zv = c.values("z")
     return oracle_mod.ssd(c.values("x")[:, :, sel], c.values("dt")[:, :, sel], c.A[sel], c.values("B"),
                           c.values("C"), D=None if c.Dskip is None else c.Dskip[sel],
                           z=None if zv is None else zv[:, :, sel],
-                          dt_bias=None if c.dt_bias is None else c.dt_bias[sel], softplus=c.softplus)
+                          dt_bias=None if c.dt_bias is None else c.dt_bias[sel], softplus=c.softplus,
+                          h0=None if h0 is None else np.asarray(h0, np.float64)[:, sel])
 
 
 def check(c, y, ls, y_ref, ls_ref, label):
@@ -90,3 +92,50 @@ def test_ssd_deterministic():
     y1, l1 = run_gpu(c)
     y2, l2 = run_gpu(c)
     assert np.array_equal(y1, y2) and np.array_equal(l1, l2)
+
+
+def _h0(c, seed):
+    """An initial state of the size a layer carries: N(0, 0.5), rounded to fp32."""
+    return (0.5 * np.random.default_rng(seed).standard_normal((c.bsz, c.H, c.P, c.N))).astype(np.float32)
+
+
+@pytest.mark.parametrize("L", [1, 64, 200])
+def test_ssd_from_state(oracle_mod, L):
+    """ssm_ssd_fwd_from: the layer continued from a given state, against the oracle from it."""
+    c = inputs.ssd_case(2, L, 4, G=2, seed=240 + L)
+    h0 = _h0(c, 241 + L)
+    y, ls = run_gpu(c, h0)
+    check(c, y, ls, *run_oracle(oracle_mod, c, h0=h0), f"from a state L={L}")
+
+
+def test_ssd_pieces_equal_whole():
+    """A sequence in two calls, the second from the first's last_state: the first piece a whole
+    number of 64-token chunks, so every chunk and every state copy is the same as in one call
+    (bitwise); in place (initial_state = last_state) as well."""
+    c = inputs.ssd_case(2, 320, 3, G=1, seed=250)
+    dev = lambda a: to_dev(a, torch)   # noqa: E731
+    f = lambda a: torch.from_numpy(a).cuda()   # noqa: E731
+    x, dt, B, C, z = dev(c.x), dev(c.dt), dev(c.B), dev(c.C), dev(c.z)
+    kw = dict(D=f(c.Dskip), dt_bias=f(c.dt_bias), softplus=c.softplus)
+    y0, ls0 = ssmscan.ssd_fwd(x, dt, f(c.A), B, C, z=z, **kw)
+    cut = 128
+    part = lambda t, a, b: t[:, a:b].contiguous()   # noqa: E731
+    y1, ls1 = ssmscan.ssd_fwd(part(x, 0, cut), part(dt, 0, cut), f(c.A), part(B, 0, cut), part(C, 0, cut),
+                              z=part(z, 0, cut), **kw)
+    y2, ls2 = ssmscan.ssd_fwd(part(x, cut, c.L), part(dt, cut, c.L), f(c.A), part(B, cut, c.L),
+                              part(C, cut, c.L), z=part(z, cut, c.L), initial_state=ls1, last_state=ls1, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([y1, y2], 1), y0) and torch.equal(ls2, ls0)
+
+
+def test_ssd_from_state_zero_length():
+    """No tokens: last_state is the initial state."""
+    c = inputs.ssd_case(1, 1, 2, G=1, seed=260)
+    h0 = torch.from_numpy(_h0(c, 261)).cuda()
+    e = torch.empty((1, 0, c.H, c.P), dtype=torch.bfloat16, device="cuda")
+    f = lambda a: torch.from_numpy(a).cuda()   # noqa: E731
+    _, ls = ssmscan.ssd_fwd(e, torch.empty((1, 0, c.H), dtype=torch.bfloat16, device="cuda"), f(c.A),
+                            torch.empty((1, 0, 1, c.N), dtype=torch.bfloat16, device="cuda"),
+                            torch.empty((1, 0, 1, c.N), dtype=torch.bfloat16, device="cuda"), initial_state=h0)
+    torch.cuda.synchronize()
+    assert torch.equal(ls, h0)
