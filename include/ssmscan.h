@@ -327,9 +327,9 @@ typedef struct {
     int64_t batch;     /* sequences */
     int64_t seqlen;    /* tokens per sequence */
     int64_t nheads;    /* heads H */
-    int64_t headdim;   /* channels per head P (64) */
+    int64_t headdim;   /* channels per head P (32 or a multiple of 64) */
     int64_t ngroups;   /* groups G of the B / C projections; H % G == 0 */
-    int64_t dstate;    /* states N (64) */
+    int64_t dstate;    /* states N (32 or 64) */
     int32_t io_dtype;  /* SSM_IO_BF16 */
     int32_t reserved;  /* 0 */
 } ssm_ssd_dims;
@@ -346,9 +346,12 @@ typedef struct {
  *   A, D, dt_bias : [nheads] fp32 (D and dt_bias may be NULL)
  *   B, C       : [batch][seqlen][ngroups][dstate] bf16
  *   last_state : [batch][nheads][headdim][dstate] fp32 output, or NULL
- * Supported: io_dtype SSM_IO_BF16, headdim 64, dstate 64, nheads*headdim <= 2^24
- * (SSM_ERR_DTYPE / SSM_ERR_SHAPE otherwise); x, z, y, B, C 16-byte aligned.  Products take bf16 operands with fp32
- * accumulation; the state is carried in fp32.  Returns SSM_OK or a negative ssm_status. */
+ * Supported: io_dtype SSM_IO_BF16; headdim 32 or a multiple of 64 (a head of 64 v channels
+ * runs as v independent 64-channel parts); dstate 32 or 64 (32-wide heads and states are
+ * padded to the 64-wide tiles with zeros, at the cost of 64-wide products);
+ * nheads*headdim <= 2^24 (SSM_ERR_DTYPE / SSM_ERR_SHAPE otherwise); x, z, y, B, C 16-byte
+ * aligned.  Products take bf16 operands with fp32 accumulation; the state is carried in
+ * fp32.  Returns SSM_OK or a negative ssm_status. */
 SSMSCAN_API int ssm_ssd_fwd(const void *x, const void *dt, const float *A, const void *B, const void *C,
                 const float *D, const void *z, const float *dt_bias, int flags, void *y, float *last_state,
                 const ssm_ssd_dims *dims, void *stream);

@@ -25,12 +25,14 @@ template void launch_conv_bwd<uint16_t>(int, bool, const void *, const float *, 
 
 void launch_ssd(const void *x, const void *dt, const float *A, const void *B, const void *C, const float *D,
                 const void *z, const float *dt_bias, int softplus, void *y, float *last_state, int64_t bsz,
-                int64_t L, int64_t H, int64_t G, hipStream_t st, const float *h0) {
-    hipLaunchKernelGGL(ssm::ssd_chunk_kernel, dim3((unsigned)(bsz * H)), dim3(ssm::kSsdThreads), 0, st,
+                int64_t L, int64_t H, int64_t G, hipStream_t st, const float *h0, int64_t P, int64_t N) {
+    const int64_t vh = P > 64 ? P / 64 : 1;   // 64-channel virtual heads per head
+    auto kern = (P < 64 || N < 64) ? ssm::ssd_chunk_kernel<true> : ssm::ssd_chunk_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(bsz * H * vh)), dim3(ssm::kSsdThreads), 0, st,
                        static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(dt), A,
                        static_cast<const uint16_t *>(B), static_cast<const uint16_t *>(C), D,
                        static_cast<const uint16_t *>(z), dt_bias, static_cast<uint16_t *>(y), last_state, L, (int)H,
-                       (int)G, softplus, h0);
+                       (int)G, softplus, h0, (int)P, (int)N);
 }
 
 }  // namespace ssmlib

@@ -37,8 +37,8 @@
 namespace ssm {
 
 constexpr int kSsdQ = 64;          // tokens per chunk
-constexpr int kSsdP = 64;          // channels per head
-constexpr int kSsdN = 64;          // states
+constexpr int kSsdP = 64;          // channels per tile (a head's 64 channels, or fewer padded)
+constexpr int kSsdN = 64;          // states per tile (64, or fewer padded)
 constexpr int kSsdThreads = 256;   // four waves per (sequence, head)
 // Operand tiles are 64 x 64 bf16, element (row, k) at sw(row, k): rows of 72 (144 bytes:
 // 16-byte aligned, and 16-byte reads of eight consecutive rows fall in distinct banks), or,
@@ -159,9 +159,14 @@ __device__ __forceinline__ void mma16_xn(const __bf16 *a, int a0, const __bf16 *
     }
 }
 
-// x, z, y: [bsz][L][H][P] bf16;  dt: [bsz][L][H] bf16;  A, Dv, dt_bias: [H] fp32;
-// B, C: [bsz][L][G][N] bf16;  h0, last_state: [bsz][H][P][N] fp32 (or null; h0 may be
+// x, z, y: [bsz][L][H][hp] bf16;  dt: [bsz][L][H] bf16;  A, Dv, dt_bias: [H] fp32;
+// B, C: [bsz][L][G][ns] bf16;  h0, last_state: [bsz][H][hp][ns] fp32 (or null; h0 may be
 // last_state: each thread reads its own state elements before it writes them).
+// Head and state sizes: the tiles are 64 wide.  A head of hp = 64 v channels is v virtual
+// heads of 64 (its channels are independent given the head's dt, A, B and C), one
+// workgroup each (grid bsz * H * v).  hp = 32 and ns = 32 are padded to 64 with zeros:
+// zero x channels give zero outputs and state columns (not stored), zero B / C states add
+// nothing to C B^T or to the readout and keep zero state rows (not stored).
 //
 // Four waves; wave w owns, in every product, the 16-row band w and the four 16 x 16 column
 // blocks j = 0..3.
@@ -173,11 +178,14 @@ __device__ __forceinline__ void mma16_xn(const __bf16 *a, int a0, const __bf16 *
 //   tH2: the same, low parts
 //   tZ : z [t][p]                     -> (3) y, in place
 // (at most 168 registers: three workgroups of four waves per CU)
-static __global__ void __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(3)))
+// PAD: hp or ns is 32 (the masked loads and stores of padded channels and states).
+template <bool PAD>
+__global__ void __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(3)))
 ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt, const float *__restrict__ A,
                  const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm, const float *__restrict__ Dv,
                  const uint16_t *__restrict__ z, const float *__restrict__ dt_bias, uint16_t *__restrict__ y,
-                 float *last_state, int64_t L, int H, int G, int softplus, const float *h0) {
+                 float *last_state, int64_t L, int H, int G, int softplus, const float *h0, int hp, int ns_in) {
+    const int ns = PAD ? ns_in : 64;   // (without padding the state size is the tile's)
     constexpr int Q = kSsdQ, P = kSsdP, N = kSsdN, LD = kSsdLd;
     static_assert(Q == 64 && P == 64 && N == 64, "a 16-row band and four 16 x 16 blocks per wave of four");
     constexpr bool ZC = true;                         // tC is swizzled
@@ -201,19 +209,29 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
     const int qi = w;                                 // row band 16 qi; column blocks 0..3
     const int c16 = lane & 15;                        // the lane's column within a block
     const int rq = (lane >> 4) * 4;                   // its rows: 16 qi + rq + (0..3)
+    const int vh = hp > 64 ? hp / 64 : 1;            // virtual heads of 64 channels per head
+    const int Hv = H * vh;
     const int bh = blockIdx.x;
-    const int b = bh / H, h = bh - b * H;
+    const int b = bh / Hv, hv = bh - b * Hv;          // hv: the virtual head
+    const int h = hv / vh, p0 = (hv - h * vh) * 64;   // the head and its first channel here
+    const int pw = hp < 64 ? hp : 64;                 // channels present in the 64-wide tile
     const int g = h / (H / G);
     const float a2 = A[h] * kLog2e;                   // decays as exp2(a2 * sum of dt)
     const float bias_h = dt_bias ? dt_bias[h] : 0.0f;
     const float d_h = Dv ? Dv[h] : 0.0f;
-    const int64_t xrow = (int64_t)H * P;              // elements between tokens in x, z, y
-    const int64_t brow = (int64_t)G * N;              // ... in B, C
-    const uint16_t *xh = x + (int64_t)b * L * xrow + (int64_t)h * P;
-    const uint16_t *zh = z ? z + (int64_t)b * L * xrow + (int64_t)h * P : nullptr;
-    uint16_t *yh = y + (int64_t)b * L * xrow + (int64_t)h * P;
-    const uint16_t *Bg = Bm + (int64_t)b * L * brow + (int64_t)g * N;
-    const uint16_t *Cg = Cm + (int64_t)b * L * brow + (int64_t)g * N;
+    // elements between tokens in x, z, y, and this workgroup's first channel (without
+    // padding, virtual head hv's channels start at 64 hv)
+    const int64_t xrow = PAD ? (int64_t)H * hp : (int64_t)Hv * P;
+    const int64_t xoff = PAD ? (int64_t)h * hp + p0 : (int64_t)hv * P;
+    const int64_t brow = (int64_t)G * ns;             // ... in B, C
+    const uint16_t *xh = x + (int64_t)b * L * xrow + xoff;
+    const uint16_t *zh = z ? z + (int64_t)b * L * xrow + xoff : nullptr;
+    uint16_t *yh = y + (int64_t)b * L * xrow + xoff;
+    const uint16_t *Bg = Bm + (int64_t)b * L * brow + (int64_t)g * ns;
+    const uint16_t *Cg = Cm + (int64_t)b * L * brow + (int64_t)g * ns;
+    // state element (channel p, state n) of this workgroup in h0 / last_state
+    const int64_t st0 = (((int64_t)b * H + h) * hp + p0) * ns;
+    auto st_index = [st0, ns](int p, int n) -> int64_t { return st0 + (int64_t)p * ns + n; };
 
     // staging map: every row coalesced (tokens tid / 8 + 32 i, 8 elements at 8 (tid % 8)); X
     // and Bw are stored by token and read transposed where they are operands.  Addresses: the
@@ -222,18 +240,21 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
     struct Raw { u32x4_t c[2], xv[2], bv[2], zv[2]; uint32_t dt; };   // rows tr0 + 32 i
     const uint32_t xr32 = (uint32_t)xrow, br32 = (uint32_t)brow;
     const int tr0 = tid / 8, tu = tid % 8;
+    const bool xin = !PAD || tu * 8 < pw, bin = !PAD || tu * 8 < ns;   // this thread's 8 channels / states exist
+    const u32x4_t zero4 = {0u, 0u, 0u, 0u};
     auto fetch = [&](int64_t t0, Raw &r) {
         const uint32_t lim = (uint32_t)min((int64_t)(Q - 1), L - 1 - t0);   // last token present
         const uint32_t ts = min((uint32_t)lane, lim);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const uint32_t tc = min((uint32_t)(tr0 + 32 * i), lim);
-            r.c[i] = *reinterpret_cast<const u32x4_t *>(Cg + t0 * brow + (tc * br32 + (uint32_t)tu * 8));
+            r.c[i] = bin ? *reinterpret_cast<const u32x4_t *>(Cg + t0 * brow + (tc * br32 + (uint32_t)tu * 8)) : zero4;
             if (zh)
-                r.zv[i] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4_t *>(zh + t0 * xrow + (tc * xr32 + (uint32_t)tu * 8)));
-            r.xv[i] = *reinterpret_cast<const u32x4_t *>(xh + t0 * xrow + (tc * xr32 + (uint32_t)tu * 8));
-            r.bv[i] = *reinterpret_cast<const u32x4_t *>(Bg + t0 * brow + (tc * br32 + (uint32_t)tu * 8));
+                r.zv[i] = xin ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(
+                                    zh + t0 * xrow + (tc * xr32 + (uint32_t)tu * 8)))
+                              : zero4;
+            r.xv[i] = xin ? *reinterpret_cast<const u32x4_t *>(xh + t0 * xrow + (tc * xr32 + (uint32_t)tu * 8)) : zero4;
+            r.bv[i] = bin ? *reinterpret_cast<const u32x4_t *>(Bg + t0 * brow + (tc * br32 + (uint32_t)tu * 8)) : zero4;
         }
         r.dt = dt[((int64_t)b * L + t0) * H + h + (w == 0 ? ts : 0u) * (uint32_t)H];   // (used by wave 0)
     };
@@ -265,10 +286,10 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
         // the initial state into the accumulators (the layout last_state is written in)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int p = 16 * j + c16;
-            const float *hs = h0 + (((int64_t)b * H + h) * P + p) * N + 16 * qi + rq;
+            const int p = 16 * j + c16, n0 = 16 * qi + rq;
+            const float *hs = h0 + st_index(p, n0);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) S[j][e] = hs[e];
+            for (int e = 0; e < 4; ++e) S[j][e] = (!PAD || (p < pw && n0 + e < ns)) ? hs[e] : 0.0f;
         }
         state_copy();   // (read after barrier (1) of the first chunk)
     }
@@ -393,7 +414,7 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int tr = tr0 + 32 * i;
-            if (tr < nt) {
+            if (tr < nt && xin) {
                 const u32x4_t yv = *reinterpret_cast<const u32x4_t *>(&tZ[zsw16(tr, tu)]);
                 __builtin_nontemporal_store((tr & 1) ? u32x4_t{yv.z, yv.w, yv.x, yv.y} : yv,
                     reinterpret_cast<u32x4_t *>(yh + t0 * xrow + (uint32_t)tr * xr32 + (uint32_t)tu * 8));
@@ -405,10 +426,11 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
     if (last_state) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int p = 16 * j + c16;
-            float *ls = last_state + (((int64_t)b * H + h) * P + p) * N + 16 * qi + rq;
+            const int p = 16 * j + c16, n0 = 16 * qi + rq;
+            float *ls = last_state + st_index(p, n0);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ls[e] = S[j][e];
+            for (int e = 0; e < 4; ++e)
+                if (!PAD || (p < pw && n0 + e < ns)) ls[e] = S[j][e];
         }
     }
 }

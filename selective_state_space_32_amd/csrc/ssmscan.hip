@@ -657,13 +657,14 @@ int ssm_ssd_fwd_from(const float *initial_state, const void *x, const void *dt, 
     if (bsz < 0 || L < 0 || H < 0 || P < 0 || G < 1 || N < 0)
         return fail(SSM_ERR_SHAPE, "negative size or ngroups < 1");
     if (dims->io_dtype != SSM_IO_BF16) return fail(SSM_ERR_DTYPE, "the SSD layer takes bf16 I/O only");
-    if (P != ssm::kSsdP || N != ssm::kSsdN)
-        return fail(SSM_ERR_SHAPE, "headdim %lld and dstate %lld: the SSD kernel supports 64 and 64", (long long)P,
-                    (long long)N);
+    if (!(P == 32 || (P >= 64 && P % 64 == 0)) || !(N == 32 || N == 64))
+        return fail(SSM_ERR_SHAPE,
+                    "headdim %lld and dstate %lld: the SSD kernel supports headdim 32 or a multiple of 64 and dstate "
+                    "32 or 64", (long long)P, (long long)N);
     if (H % G != 0) return fail(SSM_ERR_SHAPE, "nheads %lld is not a multiple of ngroups %lld", (long long)H,
                                 (long long)G);
-    if (H > kMaxDim || bsz > kMaxDim || (bsz > 0 && H > (int64_t(1) << 31) / bsz))
-        return fail(SSM_ERR_SHAPE, "batch*nheads exceeds 2^31 (grid size)");
+    if (H > kMaxDim || bsz > kMaxDim || (bsz > 0 && H * (P > 64 ? P / 64 : 1) > (int64_t(1) << 31) / bsz))
+        return fail(SSM_ERR_SHAPE, "batch*nheads*(headdim/64) exceeds 2^31 (grid size)");
     if (bsz > 0 && H > 0 && L > kMaxElems / bsz / H / P) return fail(SSM_ERR_SHAPE, "too many elements");
     if (H * P > (int64_t(1) << 24))   // a chunk's rows are addressed with 32-bit offsets
         return fail(SSM_ERR_SHAPE, "nheads*headdim %lld exceeds 2^24", (long long)(H * P));
@@ -689,7 +690,7 @@ int ssm_ssd_fwd_from(const float *initial_state, const void *x, const void *dt, 
         return ok();
     }
     launch_ssd(x, dt, A, B, C, D, z, dt_bias, (flags & SSM_SCAN_SOFTPLUS) ? 1 : 0, y, last_state, bsz, L, H, G, st,
-               initial_state);
+               initial_state, P, N);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -139,3 +139,15 @@ def test_ssd_from_state_zero_length():
                             torch.empty((1, 0, 1, c.N), dtype=torch.bfloat16, device="cuda"), initial_state=h0)
     torch.cuda.synchronize()
     assert torch.equal(ls, h0)
+
+
+@pytest.mark.parametrize("P,N", [(32, 64), (64, 32), (32, 32), (128, 64), (128, 32), (192, 64)])
+@pytest.mark.parametrize("L", [77, 200])
+def test_ssd_head_and_state_sizes(oracle_mod, P, N, L):
+    """headdim 32 / 128 / 192 and dstate 32: heads of several 64-channel parts, and 32-wide
+    heads or states padded to the 64-wide tiles; two groups, gate, skip, from a state."""
+    c = inputs.ssd_case(2, L, 4, P=P, G=2, N=N, seed=270 + P + N + L)
+    h0 = _h0(c, 271 + P + N)
+    y, ls = run_gpu(c, h0)
+    assert y.shape == (2, L, 4, P) and ls.shape == (2, 4, P, N)
+    check(c, y, ls, *run_oracle(oracle_mod, c, h0=h0), f"P={P} N={N} L={L}")
