@@ -88,11 +88,11 @@ def ssd_alg_bytes(bsz, L, H, P, G, N):
     return bsz * L * H * P * 2 * 3 + bsz * L * H * 2 + bsz * L * G * N * 2 * 2 + H * 12 + bsz * H * P * N * 4
 
 
-def cpu_baseline_ssd(c, alg_bytes_full, target_s=20.0):
+def cpu_baseline_ssd(c, alg_bytes_full, target_s=20.0, threads=None):
     """The fp64 oracle's SSD layer on a sample of heads (heads are independent)."""
     from oracle import oracle
     oracle.build(force=False)
-    threads = host_threads()
+    threads = threads or host_threads()
 
     def run(sel):
         oracle.ssd(c.values("x")[:, :, sel], c.values("dt")[:, :, sel], c.A[sel], c.values("B"), c.values("C"),
@@ -205,13 +205,13 @@ def cpu_baseline_scan(case, alg_bytes_full, target_s=12.0, target_1core_s=8.0, e
             "cpu_model": host_cpu_model()}
 
 
-def cpu_baseline_bwd(case, alg_bytes_full, target_s=20.0, with_forward=False):
+def cpu_baseline_bwd(case, alg_bytes_full, target_s=20.0, with_forward=False, threads=None):
     """The fp64 oracle's backward (after its forward, with_forward) on a channel sample of the
     workload (per-channel work is independent; the cross-channel dB / dC sums then cover the
     sample only)."""
     from oracle import oracle
     oracle.build(force=False)
-    threads = host_threads()
+    threads = threads or host_threads()
     rng = np.random.default_rng(12)
     dyv = rng.standard_normal((case.bsz, case.L, 16))
 
@@ -302,11 +302,11 @@ def cpu_baseline_conv(case, alg_bytes_full, target_s=20.0):
             "sample": f"{len(sel)} of {case.D} channels x all {case.bsz} sequences x {case.L} tokens (fp64 oracle)"}
 
 
-def cpu_baseline_block(case, cc, alg_bytes_full, target_s=20.0):
+def cpu_baseline_block(case, cc, alg_bytes_full, target_s=20.0, threads=None):
     """The fp64 oracle's convolution followed by its scan, on a channel sample."""
     from oracle import oracle
     oracle.build(force=False)
-    threads = host_threads()
+    threads = threads or host_threads()
 
     def run(sel):
         u, _ = oracle.conv1d(cc.values("x")[:, :, sel], cc.w[sel], bias=cc.bias[sel], silu=True)
@@ -328,12 +328,12 @@ def cpu_baseline_block(case, cc, alg_bytes_full, target_s=20.0):
                       f"(fp64 oracle convolution, then scan)"}
 
 
-def cpu_baseline_block_train(case, cc, alg_bytes_full, target_s=20.0):
+def cpu_baseline_block_train(case, cc, alg_bytes_full, target_s=20.0, threads=None):
     """The fp64 oracle's block training step on a channel sample: convolution, scan, the
     scan's backward, the convolution's backward."""
     from oracle import oracle
     oracle.build(force=False)
-    threads = host_threads()
+    threads = threads or host_threads()
     rng = np.random.default_rng(13)
     dyv = rng.standard_normal((case.bsz, case.L, 16))
 
@@ -360,10 +360,10 @@ def cpu_baseline_block_train(case, cc, alg_bytes_full, target_s=20.0):
                       f"(fp64 oracle convolution, scan, scan backward, convolution backward)"}
 
 
-def cpu_baseline_step(case, alg_bytes_step, target_s=20.0):
+def cpu_baseline_step(case, alg_bytes_step, target_s=20.0, threads=None):
     from oracle import oracle
     oracle.build(force=False)
-    threads = host_threads()
+    threads = threads or host_threads()
     st = case.state0.astype(np.float64)
     done = 0
     t = time.perf_counter()
@@ -375,6 +375,16 @@ def cpu_baseline_step(case, alg_bytes_step, target_s=20.0):
     dt = time.perf_counter() - t
     return {"value": round(alg_bytes_step * done / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "seconds": round(dt, 2), "sample": f"{done} of {case.steps} steps over all {case.S} sequences"}
+
+
+def with_one_core(leg, target_s=12.0, target_1core_s=6.0):
+    """A CPU-baseline leg on all the host cores this process may use, then on one core (a
+    shorter sample); the one-core rate and the CPU model go into the result."""
+    r = leg(target_s=target_s)
+    one = leg(target_s=target_1core_s, threads=1)
+    r["single_core"] = {k: one[k] for k in ("value", "unit", "cores", "seconds", "sample") if k in one}
+    r["cpu_model"] = host_cpu_model()
+    return r
 
 
 def main():
@@ -474,7 +484,7 @@ def main():
 
         def one(i):
             call()
-        plan = "one kernel, runs of 16 tokens x 8 channels per thread"
+        plan = "one kernel, runs of 32 tokens x 4 channels per thread"
     elif wl == "c3_conv_bwd":
         bsz, L, D, width = case.bsz, case.L, case.D, case.width
         x, st_in = td(case.x), td(case.state)
@@ -490,8 +500,8 @@ def main():
 
         def one(i):
             call()
-        plan = ("zero fills of dw and dbias, then one kernel: runs of 64 tokens x 4 channels per thread, "
-                "4 runs per workgroup, dw / dbias reduced in LDS and added atomically")
+        plan = ("one fill launch zeroing dw and dbias, then one kernel: a wave walks a run of 64 tokens, "
+                "2 channels per lane, 4 runs per workgroup, dw / dbias reduced in LDS and added atomically")
     elif wl == "c3_bwd":
         t = {k: td(getattr(case, f)) for k, f in (("u", "u"), ("delta", "delta"), ("A", "A"), ("B", "B"),
                                                    ("C", "C"), ("D", "Dskip"), ("z", "z"), ("bias", "delta_bias"))}
@@ -507,7 +517,10 @@ def main():
         def one(i):
             ssmscan.scan_bwd(dy, t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
                              delta_bias=t["bias"], softplus=case.softplus, workspace=ws, out=grads)
-        plan = "checkpoint pass (state every 8 tokens) + backward kernel"
+        pinfo = ssmscan.plan_info(bsz, L, D, N, dy.dtype)
+        plan = ("one fill launch, checkpoint pass (state every 8 tokens) + backward kernel"
+                + (f", both under the split schedule ({pinfo['split_tiles']} of {bsz * ((D + 63) // 64)} tiles as "
+                   f"two token halves, {pinfo['workgroups']} workgroups)" if pinfo["split_tiles"] else ""))
     elif wl == "c3_train":
         t = {k: td(getattr(case, f)) for k, f in (("u", "u"), ("delta", "delta"), ("A", "A"), ("B", "B"),
                                                    ("C", "C"), ("D", "Dskip"), ("z", "z"), ("bias", "delta_bias"))}
@@ -532,7 +545,10 @@ def main():
             fwd()
             ssmscan.scan_bwd(dy, t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
                              delta_bias=t["bias"], softplus=case.softplus, checkpoints=ws, out=grads)
-        plan = "forward storing the backward's checkpoints (state every 8 tokens) + backward kernel from them"
+        pinfo = ssmscan.plan_info(bsz, L, D, N, dy.dtype)
+        plan = ("forward storing the backward's checkpoints (state every 8 tokens) + backward kernel from them"
+                + (f", both under the split schedule ({pinfo['split_tiles']} tiles as two token halves)"
+                   if pinfo["split_tiles"] else ""))
     elif wl == "c3_block_train":
         t = {k: td(getattr(case, f)) for k, f in (("delta", "delta"), ("A", "A"), ("B", "B"), ("C", "C"),
                                                    ("D", "Dskip"), ("z", "z"), ("bias", "delta_bias"))}
@@ -694,14 +710,19 @@ def main():
     cpu = None
     if not args.no_cpu:
         try:
-            cpu = (cpu_baseline_step(case, alg) if wl == "c5" else cpu_baseline_bwd(case, alg) if wl == "c3_bwd"
-                   else cpu_baseline_bwd(case, alg, with_forward=True) if wl == "c3_train"
-                   else cpu_baseline_conv(case, alg) if wl == "c3_conv"
-                   else cpu_baseline_conv_bwd(case, dout_bits, alg) if wl == "c3_conv_bwd"
-                   else cpu_baseline_ssd(case, alg) if wl == "ssd"
-                   else cpu_baseline_block(case, cc, alg) if wl == "c3_block"
-                   else cpu_baseline_block_train(case, cc, alg) if wl == "c3_block_train"
-                   else cpu_baseline_scan(case, alg, exact_zoh=wl == "c3_zoh"))
+            if wl in ("c3_conv", "c3_conv_bwd"):   # (single-threaded oracle: one core already)
+                cpu = (cpu_baseline_conv(case, alg) if wl == "c3_conv" else cpu_baseline_conv_bwd(case, dout_bits, alg))
+                cpu["cpu_model"] = host_cpu_model()
+            elif wl in ("c2", "c3", "c4", "c3_zoh"):
+                cpu = cpu_baseline_scan(case, alg, exact_zoh=wl == "c3_zoh")
+            else:
+                leg = {"c5": lambda **k: cpu_baseline_step(case, alg, **k),
+                       "c3_bwd": lambda **k: cpu_baseline_bwd(case, alg, **k),
+                       "c3_train": lambda **k: cpu_baseline_bwd(case, alg, with_forward=True, **k),
+                       "ssd": lambda **k: cpu_baseline_ssd(case, alg, **k),
+                       "c3_block": lambda **k: cpu_baseline_block(case, cc, alg, **k),
+                       "c3_block_train": lambda **k: cpu_baseline_block_train(case, cc, alg, **k)}[wl]
+                cpu = with_one_core(leg)
         except Exception as e:  # the GPU figures stand without it
             cpu = {"error": repr(e)}
 
