@@ -49,11 +49,14 @@ struct Plan {
 // Kernel shape per state size: S states per wave (K = N/S waves per workgroup) and T
 // tokens per LDS tile.
 template <int N> struct ScanShape;
-template <> struct ScanShape<1> { static constexpr int S = 1, T = 32; };
-template <> struct ScanShape<2> { static constexpr int S = 2, T = 32; };
-template <> struct ScanShape<4> { static constexpr int S = 4, T = 32; };
-template <> struct ScanShape<8> { static constexpr int S = 4, T = 32; };
-template <> struct ScanShape<16> { static constexpr int S = 4, T = 32; };
+// TC: tokens per LDS tile under the chunk carry.  At N = 16 the carry's many short work items
+// run faster with 16-token tiles (B1 L131072 D2048: 1,615 -> 1,499 us; B2 L2048 D1536 fp32:
+// 74 -> 69 us), the one-pass and split grids with 32 (B8 L2048 D5120: 367 against 380 us).
+template <> struct ScanShape<1> { static constexpr int S = 1, T = 32, TC = 32; };
+template <> struct ScanShape<2> { static constexpr int S = 2, T = 32, TC = 32; };
+template <> struct ScanShape<4> { static constexpr int S = 4, T = 32, TC = 32; };
+template <> struct ScanShape<8> { static constexpr int S = 4, T = 32, TC = 32; };
+template <> struct ScanShape<16> { static constexpr int S = 4, T = 32, TC = 16; };
 
 // The fused causal convolution of the scan's input (conv entry point only).
 struct ConvArgs {
@@ -63,14 +66,12 @@ struct ConvArgs {
 };
 
 // (CK: the full pass also stores the backward pass's checkpoints to ckpt)
-template <int N, typename IO, bool VEC, bool ZOH, int CW = 0, bool CK = false>
-void launch_scan_kernels(const IO *u, const IO *dl, const float *A, const IO *B, const IO *C, const float *Dv,
-                         const IO *z, const float *bias, int softplus, const float *h0, IO *y, float *last_state,
-                         const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st,
-                         const ConvArgs &cv = ConvArgs{nullptr, nullptr, nullptr}, float *ckpt = nullptr,
-                         const int32_t *seq_lens = nullptr) {
+template <int N, int T, typename IO, bool VEC, bool ZOH, int CW, bool CK>
+void launch_scan_kernels_t(const IO *u, const IO *dl, const float *A, const IO *B, const IO *C, const float *Dv,
+                           const IO *z, const float *bias, int softplus, const float *h0, IO *y, float *last_state,
+                           const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st, const ConvArgs &cv,
+                           float *ckpt, const int32_t *seq_lens) {
     constexpr int S = ScanShape<N>::S;
-    constexpr int T = ScanShape<N>::T;
     constexpr int K = N / S;
     const int64_t bsz = dm->batch, L = dm->seqlen, D = dm->dim;
     const int tiles_per_b = (int)((D + ssm::kChanTile - 1) / ssm::kChanTile);
@@ -111,6 +112,22 @@ void launch_scan_kernels(const IO *u, const IO *dl, const float *A, const IO *B,
                        last_state, cstate, cdsum, L, D, tiles_per_b, n_tiles, cl, nc, softplus, cv.w, cv.b,
                        static_cast<IO *>(cv.u_out), ckpt, 0, 0, (int64_t)0, (float *)nullptr, (int *)nullptr, 0ull,
                        seq_lens);
+}
+
+// The scan's launches with the plan's tile length (TC under the chunk carry, else T).
+template <int N, typename IO, bool VEC, bool ZOH, int CW = 0, bool CK = false>
+void launch_scan_kernels(const IO *u, const IO *dl, const float *A, const IO *B, const IO *C, const float *Dv,
+                         const IO *z, const float *bias, int softplus, const float *h0, IO *y, float *last_state,
+                         const ssm_dims *dm, const Plan &p, void *ws, hipStream_t st,
+                         const ConvArgs &cv = ConvArgs{nullptr, nullptr, nullptr}, float *ckpt = nullptr,
+                         const int32_t *seq_lens = nullptr) {
+    constexpr int T = ScanShape<N>::T, TC = ScanShape<N>::TC;
+    if (TC != T && p.schedule == kCarry)
+        launch_scan_kernels_t<N, TC, IO, VEC, ZOH, CW, CK>(u, dl, A, B, C, Dv, z, bias, softplus, h0, y, last_state,
+                                                           dm, p, ws, st, cv, ckpt, seq_lens);
+    else
+        launch_scan_kernels_t<N, T, IO, VEC, ZOH, CW, CK>(u, dl, A, B, C, Dv, z, bias, softplus, h0, y, last_state,
+                                                          dm, p, ws, st, cv, ckpt, seq_lens);
 }
 
 template <int N, typename IO>
