@@ -152,6 +152,46 @@ def scan_varlen(u, delta, A, B, C, seq_lens, D=None, z=None, delta_bias=None, so
     return y, last
 
 
+def scan_bwd_varlen(u, delta, A, B, C, dy, seq_lens, D=None, z=None, delta_bias=None, softplus: bool = True,
+                    h0=None, dlast=None, threads: Optional[int] = None, exact_zoh: bool = False) -> dict:
+    """Gradients of scan_varlen: sequence b is the scan of its first seq_lens[b] tokens
+    (clamped to [0, L]) alone, so its gradients are scan_bwd of that prefix, with dlast[b]
+    applied to the state after its own length; the inputs past a length do not reach any
+    output, so their gradients (du, ddelta, dz, dB, dC) are zero.  dA, dD, ddelta_bias are sums
+    over the sequences; dh0 (always returned) is the gradient of each sequence's initial state
+    (dlast[b] itself for a length of 0)."""
+    u = _f64(u)
+    bsz, L, Dch = u.shape
+    A = _f64(A)
+    N = A.shape[1]
+    out = dict(du=np.zeros((bsz, L, Dch)), ddelta=np.zeros((bsz, L, Dch)), dA=np.zeros((Dch, N)),
+               dB=np.zeros((bsz, L, N)), dC=np.zeros((bsz, L, N)), dh0=np.zeros((bsz, Dch, N)))
+    if D is not None:
+        out["dD"] = np.zeros(Dch)
+    if z is not None:
+        out["dz"] = np.zeros((bsz, L, Dch))
+    if delta_bias is not None:
+        out["ddelta_bias"] = np.zeros(Dch)
+    for b in range(bsz):
+        lb = int(min(max(int(seq_lens[b]), 0), L))
+        dl_b = None if dlast is None else np.asarray(dlast, np.float64)[b:b + 1]
+        if lb == 0:
+            if dl_b is not None:
+                out["dh0"][b] = dl_b[0]
+            continue
+        sl = (slice(b, b + 1), slice(0, lb))
+        h0_b = np.zeros((1, Dch, N)) if h0 is None else np.asarray(h0, np.float64)[b:b + 1]
+        g = scan_bwd(u[sl], np.asarray(delta)[sl], A, np.asarray(B)[sl], np.asarray(C)[sl], np.asarray(dy)[sl],
+                     D=D, z=None if z is None else np.asarray(z)[sl], delta_bias=delta_bias, softplus=softplus,
+                     h0=h0_b, dlast=dl_b, threads=threads, exact_zoh=exact_zoh)
+        for k in ("du", "ddelta", "dB", "dC") + (("dz",) if z is not None else ()):
+            out[k][b, :lb] = g[k][0]
+        for k in ("dA",) + (("dD",) if D is not None else ()) + (("ddelta_bias",) if delta_bias is not None else ()):
+            out[k] += g[k]
+        out["dh0"][b] = g["dh0"][0]
+    return out
+
+
 def step(state, u, delta, A, B, C, D=None, z=None,
          threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
     """fp64 single-token step.  state: (S, Dch, N); u, delta, z: (S, Dch); B, C: (S, N).

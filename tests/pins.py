@@ -937,3 +937,74 @@ def check_varlen_zero_length(scan_from, scan_varlen):
 
 VARLEN_CHECKS = [check_varlen_full_lengths, check_varlen_padding_ignored, check_varlen_continuation,
                  check_varlen_zero_length]
+
+
+
+# --- gradients of the variable-length scan ---------------------------------------------------------
+# scan_bwd_varlen(u, x, A, B, C, dy, lens, D, z, bias, softplus, h0, dlast) -> dict of gradients
+
+def _vl_bwd(scan_bwd_varlen, c, dy, lens, dlast, **kw):
+    a = dict(c)
+    a.update(kw)
+    return scan_bwd_varlen(a["u"], a["x"], a["A"], a["B"], a["C"], dy, lens, a["D"], a["z"], a["bias"], True,
+                           a["h0"], dlast)
+
+
+def check_bwd_varlen_fd(scan_varlen, scan_bwd_varlen, seed=121):
+    """Every gradient against central differences of the variable-length forward (a loss on
+    y up to each length and on the state after it), lengths 0, 1, ragged and L."""
+    c, rng = _varlen_case(seed, bsz=4, L=23, D=3, N=4)
+    L = c["u"].shape[1]
+    lens = np.array([0, 1, 14, L])
+    dy = rng.standard_normal(c["u"].shape)
+    dlast = rng.standard_normal(c["h0"].shape)
+    g = _vl_bwd(scan_bwd_varlen, c, dy, lens, dlast)
+
+    def loss(**kw):
+        y, last = _vl(scan_varlen, c, lens, **kw)
+        return np.nansum(dy * np.nan_to_num(y, nan=0.0)) + np.sum(dlast * last)
+    eps = 1e-6
+    for name, key in (("u", "du"), ("x", "ddelta"), ("z", "dz"), ("B", "dB"), ("C", "dC"), ("h0", "dh0"),
+                      ("A", "dA"), ("D", "dD"), ("bias", "ddelta_bias")):
+        V = rng.standard_normal(np.shape(c[name]))
+        fd = (loss(**{name: c[name] + eps * V}) - loss(**{name: c[name] - eps * V})) / (2 * eps)
+        an = float(np.sum(g[key] * V))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+def check_bwd_varlen_full_lengths(scan_bwd, scan_bwd_varlen, seed=122):
+    """All lengths L: the batch backward exactly (same arithmetic per sequence)."""
+    c, rng = _varlen_case(seed)
+    L = c["u"].shape[1]
+    dy = rng.standard_normal(c["u"].shape)
+    dlast = rng.standard_normal(c["h0"].shape)
+    g = _vl_bwd(scan_bwd_varlen, c, dy, [L] * c["u"].shape[0], dlast)
+    g0 = scan_bwd(c["u"], c["x"], c["A"], c["B"], c["C"], dy, c["D"], c["z"], c["bias"], True, c["h0"], dlast)
+    for k in g0:
+        assert _rel(g[k], g0[k]) < 1e-13, k
+
+
+def check_bwd_varlen_padding(scan_bwd, scan_bwd_varlen, seed=123):
+    """Values past each length, in the inputs and in dy, change no gradient; the gradients
+    there are exactly zero."""
+    c, rng = _varlen_case(seed)
+    lens = [0, 1, 20, c["u"].shape[1]]
+    dy = rng.standard_normal(c["u"].shape)
+    dlast = rng.standard_normal(c["h0"].shape)
+    g = _vl_bwd(scan_bwd_varlen, c, dy, lens, dlast)
+    d = {k: np.array(c[k], dtype=np.float64) for k in ("u", "x", "B", "C", "z")}
+    dy2 = dy.copy()
+    for b, lb in enumerate(lens):
+        for k in d:
+            d[k][b, lb:] = 1e30 if k in ("x", "z") else -7.5
+        dy2[b, lb:] = 1e30
+    g2 = _vl_bwd(scan_bwd_varlen, c, dy2, lens, dlast, **d)
+    for k in g:
+        assert np.array_equal(g[k], g2[k]), k
+    for b, lb in enumerate(lens):
+        for k in ("du", "ddelta", "dz", "dB", "dC"):
+            assert np.all(g[k][b, lb:] == 0.0), (k, b)
+    assert np.array_equal(g["dh0"][0], dlast[0])   # length 0: the adjoint passes straight through
+
+
+BWD_VARLEN_CHECKS = [check_bwd_varlen_full_lengths, check_bwd_varlen_padding]

@@ -217,3 +217,19 @@ def _scan_varlen(oracle_mod):
 @pytest.mark.parametrize("check", pins.VARLEN_CHECKS, ids=lambda c: c.__name__)
 def test_varlen_pins(oracle_mod, check):
     check(_scan_from(oracle_mod), _scan_varlen(oracle_mod))
+
+
+def _scan_bwd_varlen(oracle_mod):
+    def f(u, x, A, B, C, dy, lens, D, z, bias, softplus, h0, dlast):
+        return oracle_mod.scan_bwd_varlen(u, x, A, B, C, dy, lens, D=D, z=z, delta_bias=bias, softplus=softplus,
+                                          h0=h0, dlast=dlast, threads=2)
+    return f
+
+
+def test_bwd_varlen_fd(oracle_mod):
+    pins.check_bwd_varlen_fd(_scan_varlen(oracle_mod), _scan_bwd_varlen(oracle_mod))
+
+
+@pytest.mark.parametrize("check", pins.BWD_VARLEN_CHECKS, ids=lambda c: c.__name__)
+def test_bwd_varlen_pins(oracle_mod, check):
+    check(_scan_bwd(oracle_mod), _scan_bwd_varlen(oracle_mod))
