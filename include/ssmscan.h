@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SSMSCAN_VERSION 12
+#define SSMSCAN_VERSION 13
 
 /* Bits of the `flags` argument of the scan entry points. */
 #define SSM_SCAN_SOFTPLUS 1     /* step size = softplus(delta + delta_bias) */
@@ -251,6 +251,24 @@ SSMSCAN_API int ssm_scan_bwd(const float *initial_state, const void *u, const vo
                  float *dA, float *dB, float *dC, float *dD, void *dz, float *ddelta_bias,
                  float *dinitial_state, const ssm_dims *dims, void *workspace, size_t workspace_bytes,
                  void *stream);
+
+/* Gradients of ssm_scan_fwd_varlen (sequences of different lengths in one batch): sequence b's
+ * gradients are those of the scan of its first seq_lens[b] tokens (clamped to [0, L]), with
+ * dlast_state[b] applied to the state after that many tokens (shakilmahmud.com section 3,
+ * recurrent form).
+ *   seq_lens : [batch] int32 device array (4-byte aligned), the lengths the forward used
+ *   du, ddelta, dz : written for every token; zero past each sequence's length (those inputs
+ *                    reach no output), whatever dy holds there
+ *   dB, dC   : zero past each length; dA, dD, ddelta_bias : sums over the real tokens only
+ *   dinitial_state : dlast_state[b] itself for a length of 0
+ * Everything else (flags, checkpoints from a training forward_varlen with
+ * SSM_SCAN_CHECKPOINTS, workspace) as ssm_scan_bwd.  Returns SSM_OK or a negative ssm_status. */
+SSMSCAN_API int ssm_scan_bwd_varlen(const float *initial_state, const int32_t *seq_lens, const void *u,
+                const void *delta, const float *A, const void *B, const void *C, const float *D, const void *z,
+                const float *delta_bias, int flags, const void *dy, const float *dlast_state, void *du,
+                void *ddelta, float *dA, float *dB, float *dC, float *dD, void *dz, float *ddelta_bias,
+                float *dinitial_state, const ssm_dims *dims, void *workspace, size_t workspace_bytes,
+                void *stream);
 
 /* Bits of the `flags` argument of ssm_conv1d_fwd. */
 #define SSM_CONV_SILU 1         /* apply SiLU to the convolution's output */

@@ -44,6 +44,11 @@
 // alone over the first part's tokens (G <- exp(delta A) (C dp + G), no states needed), so no
 // placement can hang the kernel and no contribution is counted twice.  hflag must be zero at
 // launch.
+//
+// seq_lens (nullable): sequence b has seq_lens[b] tokens (clamped to [0, L]); its walk starts
+// at its last token with the adjoint dlast, tokens past it are identity steps like tokens past
+// L (nothing read from them), and du, d delta, dz there are written as zeros (the gradient of
+// inputs that reach no output).
 #pragma once
 
 #include "scan_kernels.h"
@@ -124,7 +129,7 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
                 float *__restrict__ dC, float *__restrict__ dD, float *__restrict__ dbias,
                 float *__restrict__ dh0, int64_t L, int64_t D, int tiles_per_b, int softplus, int n_full = 0,
                 int n_split = 0, int j_mid = 0, float *__restrict__ hand = nullptr, int *__restrict__ hflag = nullptr,
-                unsigned long long wait_ticks = 0) {
+                unsigned long long wait_ticks = 0, const int32_t *__restrict__ seq_lens = nullptr) {
     constexpr int S = BwdShape<N>::S;
     constexpr int K = BwdShape<N>::K;
     constexpr int T = kBwdTile;
@@ -169,6 +174,7 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
     const bool qact = d0 + cq < D;
     const int64_t dq = qact ? d0 + cq : (D - V) / V * V;
     const int64_t row0 = (int64_t)b * L;
+    const int64_t Lb = seq_lens ? min((int64_t)max(seq_lens[b], 0), L) : L;   // this sequence's tokens
     const bool gated = z != nullptr;
     const int64_t n_ckpt = (L + kCkptEvery - 1) / kCkptEvery;
 
@@ -207,8 +213,8 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
         else io<IO>::st(p, idx, val[0]);
     };
 
-    const int n_tiles = (int)((L + T - 1) / T);
-    const int j_first = role == kSecondPart ? j_mid - 1 : n_tiles - 1;   // tiles j_first down to j_last
+    const int n_tiles = (int)((Lb + T - 1) / T);   // (of this sequence)
+    const int j_first = (role == kSecondPart ? min(j_mid, n_tiles) : n_tiles) - 1;   // tiles j_first down to j_last
     const int j_last = role == kFirstPart ? j_mid : 0;
     const int rk = lane / LPV, rgrp = lane % LPV;   // the dB / dC entry this lane sums
     Raw ru[P], rx[P], ry[P], rz[P];
@@ -216,7 +222,7 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
     float hn[S];
     auto fetch = [&](int jj) {   // tile jj's inputs, its B / C rows and its checkpoint
         const int64_t tb = (int64_t)jj * T;
-        const int ntj = (int)min((int64_t)T, L - tb);
+        const int ntj = (int)min((int64_t)T, Lb - tb);
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             const int64_t idx = (row0 + tb + min(p * RPP + rsub, ntj - 1)) * D + dq;   // clamped in bounds
@@ -264,7 +270,7 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
             // no hand-over: the adjoint over the first part's tokens, from dlast, with the
             // arithmetic of the reverse walk below (lambda = C dp + G, G = exp(delta A) lambda)
             const float bb = bias ? bias[d] : 0.0f;
-            for (int64_t t = L - 1; t >= (int64_t)j_mid * T; --t) {
+            for (int64_t t = Lb - 1; t >= (int64_t)j_mid * T; --t) {
                 const int64_t e = (row0 + t) * D + d;
                 const float x = io<IO>::ld(delta, e) + bb;
                 float sg;
@@ -285,10 +291,10 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
         }
         __builtin_amdgcn_s_setprio(2);
     }
-    fetch(j_first);
+    if (j_first >= j_last) fetch(j_first);
     for (int j = j_first; j >= j_last; --j) {
         const int64_t t0 = (int64_t)j * T;
-        const int nt = (int)min((int64_t)T, L - t0);
+        const int nt = (int)min((int64_t)T, Lb - t0);
 
         // 1. per-element preparation.  Tokens past the end and channels past D get zeros: a
         // step with delta = 0, delta*u = 0 and dp = 0 leaves the state and the adjoint
@@ -445,6 +451,20 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
                 st(ddelta, idx, o_dd);
                 if (gated) st(dz, idx, o_dz);
             }
+        }
+    }
+
+    // inputs past this sequence's length reach no output: their gradients are zero (written
+    // by the part that covers the sequence's end)
+    if (Lb < L && role != kSecondPart && qact) {
+        float zv[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) zv[v] = 0.0f;
+        for (int64_t t = Lb + rsub; t < L; t += RPP) {
+            const int64_t idx = (row0 + t) * D + d0 + cq;
+            st(du, idx, zv);
+            st(ddelta, idx, zv);
+            if (gated) st(dz, idx, zv);
         }
     }
 

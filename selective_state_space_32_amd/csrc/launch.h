@@ -245,6 +245,7 @@ struct BwdArgs {
     bool ckpt_given;   // the workspace already holds the checkpoints (written by the training forward)
     bool zoh;          // the exact zero-order-hold input term
     ssm::FillList zero;   // the accumulators to zero before the walk (the hand-over flags are added)
+    const int32_t *seq_lens = nullptr;   // per-sequence token counts (device), or null
 };
 
 // Adds a buffer of n 32-bit words to a fill list (skipped when null or empty).
@@ -307,7 +308,7 @@ int launch_bwd(const BwdArgs &a, const ssm_dims *dm, const Plan &sp, size_t ckpt
                                L, D, tiles_per_b, n_tiles, L, 1, a.softplus, (const float *)nullptr,
                                (const float *)nullptr, (IO *)nullptr, (float *)nullptr, split ? (int)sp.n_full : 0,
                                split ? (int)sp.n_split : 0, split ? sp.l_mid : (int64_t)0, hand, flags,
-                               split ? handover_wait_ticks() : 0ull, (const int32_t *)nullptr);
+                               split ? handover_wait_ticks() : 0ull, a.seq_lens);
         };
         using T1 = std::true_type;
         using F0 = std::false_type;
@@ -327,7 +328,7 @@ int launch_bwd(const BwdArgs &a, const ssm_dims *dm, const Plan &sp, size_t ckpt
                            ddl, dz, a.dA, a.dB, a.dC, a.dD, a.dbias, a.dh0, L, D, tiles_per_b, a.softplus,
                            split ? (int)sp.n_full : 0, split ? (int)sp.n_split : 0,
                            split ? (int)(sp.l_mid / ssm::kBwdTile) : 0, hand, wflags,
-                           split ? handover_wait_ticks() : 0ull);
+                           split ? handover_wait_ticks() : 0ull, a.seq_lens);
     };
     if (vb && a.zoh) walk(std::true_type{}, std::true_type{});
     else if (vb) walk(std::true_type{}, std::false_type{});

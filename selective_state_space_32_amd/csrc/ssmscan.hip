@@ -269,6 +269,13 @@ int dispatch_bwd(int64_t N, const BwdArgs &a, const ssm_dims *dm, void *ws, hipS
     return fail(SSM_ERR_UNSUPPORTED_N, "dstate %lld not supported", (long long)N);
 }
 
+// The backward's entry (ssm_scan_bwd and ssm_scan_bwd_varlen): validation, zeroing, launches.
+int bwd_impl(const float *initial_state, const int32_t *seq_lens, const void *u, const void *delta, const float *A,
+             const void *B, const void *C, const float *D, const void *z, const float *delta_bias, int flags,
+             const void *dy, const float *dlast_state, void *du, void *ddelta, float *dA, float *dB, float *dC,
+             float *dD, void *dz, float *ddelta_bias, float *dinitial_state, const ssm_dims *dims, void *workspace,
+             size_t workspace_bytes, void *stream);
+
 }  // namespace
 
 // ---- scratch for the entry point that allocates nothing ------------------------------------
@@ -490,6 +497,31 @@ int ssm_scan_bwd(const float *initial_state, const void *u, const void *delta, c
                  const void *dy, const float *dlast_state, void *du, void *ddelta, float *dA, float *dB,
                  float *dC, float *dD, void *dz, float *ddelta_bias, float *dinitial_state, const ssm_dims *dims,
                  void *workspace, size_t workspace_bytes, void *stream) {
+    return bwd_impl(initial_state, nullptr, u, delta, A, B, C, D, z, delta_bias, flags, dy, dlast_state, du, ddelta,
+                    dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, dims, workspace, workspace_bytes, stream);
+}
+
+int ssm_scan_bwd_varlen(const float *initial_state, const int32_t *seq_lens, const void *u, const void *delta,
+                        const float *A, const void *B, const void *C, const float *D, const void *z,
+                        const float *delta_bias, int flags, const void *dy, const float *dlast_state, void *du,
+                        void *ddelta, float *dA, float *dB, float *dC, float *dD, void *dz, float *ddelta_bias,
+                        float *dinitial_state, const ssm_dims *dims, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+    if (!seq_lens) return fail(SSM_ERR_NULL, "seq_lens is NULL (use ssm_scan_bwd for equal lengths)");
+    if (!aligned(seq_lens, 4)) return fail(SSM_ERR_ALIGN, "seq_lens not 4-byte aligned");
+    return bwd_impl(initial_state, seq_lens, u, delta, A, B, C, D, z, delta_bias, flags, dy, dlast_state, du, ddelta,
+                    dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, dims, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int bwd_impl(const float *initial_state, const int32_t *seq_lens, const void *u, const void *delta, const float *A,
+             const void *B, const void *C, const float *D, const void *z, const float *delta_bias, int flags,
+             const void *dy, const float *dlast_state, void *du, void *ddelta, float *dA, float *dB, float *dC,
+             float *dD, void *dz, float *ddelta_bias, float *dinitial_state, const ssm_dims *dims, void *workspace,
+             size_t workspace_bytes, void *stream) {
     int rc = check_dims(dims, true);
     if (rc != SSM_OK) return rc;
     if (flags & ~(SSM_SCAN_SOFTPLUS | SSM_SCAN_EXACT_ZOH | SSM_SCAN_CHECKPOINTS))
@@ -543,10 +575,14 @@ int ssm_scan_bwd(const float *initial_state, const void *u, const void *delta, c
     }
     BwdArgs a{initial_state, u, delta, A, B, C, D, z, delta_bias, (flags & SSM_SCAN_SOFTPLUS) != 0, dy, dlast_state, du, ddelta,
               dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, (flags & SSM_SCAN_CHECKPOINTS) != 0,
-              (flags & SSM_SCAN_EXACT_ZOH) != 0, zero};
+              (flags & SSM_SCAN_EXACT_ZOH) != 0, zero, seq_lens};
     if (dims->io_dtype == SSM_IO_BF16) return dispatch_bwd<uint16_t>(N, a, dims, workspace, st);
     return dispatch_bwd<float>(N, a, dims, workspace, st);
 }
+
+}  // namespace
+
+extern "C" {
 
 int ssm_conv1d_fwd(const void *x, const float *w, const float *bias, int width, const void *state_in, int flags,
                    void *out, void *state_out, const ssm_dims *dims, void *stream) {

@@ -74,6 +74,8 @@ def _load() -> ctypes.CDLL:
     lib.ssm_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.ssm_scan_bwd.argtypes = [P] * 9 + [ctypes.c_int] + [P] * 11 + [D, P, ctypes.c_size_t, P]
     lib.ssm_scan_bwd.restype = ctypes.c_int
+    lib.ssm_scan_bwd_varlen.argtypes = [P, P] + [P] * 8 + [ctypes.c_int] + [P] * 11 + [D, P, ctypes.c_size_t, P]
+    lib.ssm_scan_bwd_varlen.restype = ctypes.c_int
     lib.ssm_step.argtypes = [P, P, P, P, P, P, P, P, P, D, P]
     lib.ssm_step.restype = ctypes.c_int
     lib.ssm_conv1d_fwd.argtypes = [P, P, P, ctypes.c_int, P, ctypes.c_int, P, P, D, P]
@@ -320,22 +322,25 @@ def scan_fwd_varlen(seq_lens: torch.Tensor, u: torch.Tensor, delta: torch.Tensor
                     softplus: bool = True, *, initial_state: Optional[torch.Tensor] = None,
                     y: Optional[torch.Tensor] = None, last_state: Optional[torch.Tensor] = None,
                     return_last_state: bool = True, chunk_len: int = 0, workspace: Optional[torch.Tensor] = None,
-                    stream=None, exact_zoh: bool = False):
+                    stream=None, exact_zoh: bool = False, save_checkpoints: bool = False):
     """Scan of sequences of different lengths (ssm_scan_fwd_varlen): seq_lens (batch,) int32 on
     the device; sequence b's tokens t < seq_lens[b] are scanned (from initial_state, or zero)
     and written to y, the later tokens of y are left as they are.  Returns (y, last_state),
-    last_state being the state after each sequence's own length."""
+    last_state being the state after each sequence's own length; with save_checkpoints (a
+    training forward) also the workspace holding the backward's checkpoints, for
+    scan_bwd(..., seq_lens=..., checkpoints=ws)."""
     if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1 or seq_lens.shape[0] != u.shape[0]:
         raise ValueError("seq_lens must be an int32 tensor of shape (batch,)")
     if seq_lens.device != u.device:
         raise ValueError("seq_lens must be on the device of u")
-    args, _keep, y, last_state, _ws = _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
-                                                 return_last_state, chunk_len, workspace, stream,
-                                                 initial_state=initial_state, exact_zoh=exact_zoh)
+    args, _keep, y, last_state, ws = _scan_args(u, delta, A, B, C, D, z, delta_bias, softplus, y, last_state,
+                                                return_last_state, chunk_len, workspace, stream,
+                                                initial_state=initial_state, exact_zoh=exact_zoh,
+                                                save_checkpoints=save_checkpoints)
     if initial_state is None:
         args = (None,) + args
     _check(lib.ssm_scan_fwd_varlen(args[0], _ptr(seq_lens), *args[1:]))
-    return y, last_state
+    return (y, last_state, ws) if save_checkpoints else (y, last_state)
 
 
 def scan_bwd(dy: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
@@ -344,8 +349,9 @@ def scan_bwd(dy: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Te
              initial_state: Optional[torch.Tensor] = None, dlast_state: Optional[torch.Tensor] = None,
              want_initial_state_grad: bool = False, workspace: Optional[torch.Tensor] = None,
              out: Optional[dict] = None, stream=None, checkpoints: Optional[torch.Tensor] = None,
-             exact_zoh: bool = False) -> dict:
-    """Gradients of the scan (ssm_scan_bwd; of the exact zero-order-hold scan with exact_zoh)
+             exact_zoh: bool = False, seq_lens: Optional[torch.Tensor] = None) -> dict:
+    """Gradients of the scan (ssm_scan_bwd; of the exact zero-order-hold scan with exact_zoh;
+    of scan_fwd_varlen with seq_lens, an int32 (batch,) tensor on the device: ssm_scan_bwd_varlen)
     given dy (batch, L, dim) and optionally
     dlast_state (batch, dim, N).  The forward inputs are passed as to scan_fwd / scan_fwd_from.
     Returns a dict: du, ddelta, dz (if z), dA, dB, dC (float32), dD (if D), ddelta_bias
@@ -382,14 +388,22 @@ def scan_bwd(dy: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Te
     need = int(lib.ssm_scan_bwd_workspace_bytes(ctypes.byref(dims)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    rc = lib.ssm_scan_bwd(_ptr(initial_state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                          _ptr(delta_bias), int(bool(softplus)) | (SCAN_CHECKPOINTS if checkpoints is not None else 0)
-                          | (SCAN_EXACT_ZOH if exact_zoh else 0),
-                          _ptr(dy), _ptr(dlast_state), _ptr(g["du"]),
-                          _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dD")),
-                          _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")), _ptr(g.get("dinitial_state")),
-                          ctypes.byref(dims), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                          _stream_handle(stream))
+    args = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            int(bool(softplus)) | (SCAN_CHECKPOINTS if checkpoints is not None else 0)
+            | (SCAN_EXACT_ZOH if exact_zoh else 0),
+            _ptr(dy), _ptr(dlast_state), _ptr(g["du"]),
+            _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g.get("dD")),
+            _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")), _ptr(g.get("dinitial_state")),
+            ctypes.byref(dims), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream_handle(stream))
+    if seq_lens is not None:
+        if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1 or seq_lens.shape[0] != bsz:
+            raise ValueError("seq_lens must be an int32 tensor of shape (batch,)")
+        if seq_lens.device != dev:
+            raise ValueError("seq_lens must be on the device of u")
+        rc = lib.ssm_scan_bwd_varlen(_ptr(initial_state), _ptr(seq_lens), *args)
+    else:
+        rc = lib.ssm_scan_bwd(_ptr(initial_state), *args)
     _check(rc)
     return g
 

@@ -28,7 +28,7 @@ def b():
 def test_header_declares_the_entry_points():
     syms = set(declared_symbols())
     assert {"ssm_scan_fwd", "ssm_scan_fwd_from", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes", "ssm_step",
-            "ssm_conv1d_fwd", "ssm_conv1d_bwd", "ssm_scan_fwd_conv", "ssm_ssd_fwd", "ssm_ssd_fwd_from",
+            "ssm_conv1d_fwd", "ssm_conv1d_bwd", "ssm_scan_fwd_conv", "ssm_ssd_fwd", "ssm_ssd_fwd_from", "ssm_scan_bwd_varlen",
             "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_last_error", "ssm_version"} <= syms
 
 

@@ -146,3 +146,117 @@ def test_varlen_rejects_bad_lengths_tensor():
         ssmscan.scan_fwd_varlen(torch.zeros(2, dtype=torch.int64, device="cuda"), t, t, A, Bm, Bm)
     with pytest.raises(ValueError):
         ssmscan.scan_fwd_varlen(torch.zeros(3, dtype=torch.int32, device="cuda"), t, t, A, Bm, Bm)
+
+
+# --- gradients (ssm_scan_bwd_varlen) -----------------------------------------------------------
+
+from test_bwd_gpu import check_grads, _io_array, _values  # noqa: E402
+
+BWD_CASES = [
+    # (name, bsz, L, D, N, io, gate)
+    ("bwd f32 N16", 8, 150, 128, 16, "f32", True),
+    ("bwd bf16 N16", 8, 150, 128, 16, "bf16", True),
+    ("bwd bf16 N4 ungated", 8, 97, 64, 4, "bf16", False),
+]
+
+
+def _bwd_run(oracle_mod, case, lens, seed, poison=False, channels=None, checkpoints=None):
+    rng = np.random.default_rng(seed)
+    bsz, L, D, N = case.bsz, case.L, case.D, case.N
+    dy = _io_array(rng.standard_normal((bsz, L, D), dtype=np.float32), case.io)
+    h0 = (0.5 * rng.standard_normal((bsz, D, N))).astype(np.float32)
+    dlast = rng.standard_normal((bsz, D, N)).astype(np.float32)
+    t = case_tensors(case, torch)
+    dyt = to_dev(dy, torch)
+    if poison:
+        for k in ("u", "delta", "B", "C", "z"):
+            if t[k] is None:
+                continue
+            v = t[k].clone()
+            for b, lb in enumerate(lens):
+                v[b, int(lb):] = float("nan")
+            t[k] = v
+        dyt = dyt.clone()
+        for b, lb in enumerate(lens):
+            dyt[b, int(lb):] = float("nan")
+    g = ssmscan.scan_bwd(dyt, t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                         delta_bias=t["delta_bias"], softplus=case.softplus, initial_state=torch.from_numpy(h0).cuda(),
+                         dlast_state=torch.from_numpy(dlast).cuda(), want_initial_state_grad=True,
+                         seq_lens=torch.from_numpy(np.asarray(lens, np.int32)).cuda(), checkpoints=checkpoints)
+    torch.cuda.synchronize()
+    got = {k: to_host_f64(v) for k, v in g.items()}
+    sel = slice(None) if channels is None else np.asarray(channels)
+    zv = case.values("z")
+    ref = oracle_mod.scan_bwd_varlen(case.values("u")[:, :, sel], case.values("delta")[:, :, sel], case.A[sel],
+                                     case.values("B"), case.values("C"), _values(dy, case.io)[:, :, sel], lens,
+                                     D=None if case.Dskip is None else case.Dskip[sel],
+                                     z=None if zv is None else zv[:, :, sel],
+                                     delta_bias=None if case.delta_bias is None else case.delta_bias[sel],
+                                     softplus=case.softplus, h0=h0[:, sel], dlast=dlast[:, sel])
+    if channels is not None:
+        got = {k: (v[:, :, sel] if v.ndim == 3 and k in ("du", "ddelta", "dz") else
+                   v[sel] if k in ("dA", "dD", "ddelta_bias") else
+                   v[:, sel] if k == "dinitial_state" else v)
+               for k, v in got.items()}
+        got.pop("dB"), got.pop("dC"), ref.pop("dB"), ref.pop("dC")
+    return got, ref
+
+
+@pytest.mark.parametrize("name,bsz,L,D,N,io,gate", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_varlen_bwd_matches_oracle(oracle_mod, name, bsz, L, D, N, io, gate):
+    """Every gradient against the oracle's per-sequence backward, lengths 0, 1, ragged and L,
+    with NaN past each length in the inputs and in dy; the gradients there are exactly zero."""
+    case = inputs.scan_case(bsz, L, D, N, io, gate=gate, seed=800 + L + N, name=f"varlen {name}")
+    lens = _lens(bsz, L, "ragged")
+    print(f"[{case.name}] lens {lens.tolist()}", flush=True)
+    got, ref = _bwd_run(oracle_mod, case, lens, seed=801, poison=True)
+    for k in ("du", "ddelta", "dz", "dB", "dC"):
+        if k in got:
+            for b, lb in enumerate(lens):
+                assert np.all(got[k][b, int(lb):] == 0.0), (k, b)
+    check_grads(case, got, ref, "varlen")
+
+
+def test_varlen_bwd_full_lengths_bitwise():
+    """All lengths L: the per-element gradients of the plain backward bitwise."""
+    case = inputs.scan_case(4, 300, 256, 16, "bf16", gate=True, seed=811, name="varlen bwd = bwd")
+    t = case_tensors(case, torch)
+    dy = to_dev(inputs.bf16_bits(np.random.default_rng(812).standard_normal((4, 300, 256), dtype=np.float32)),
+                torch)
+    args = (dy, t["u"], t["delta"], t["A"], t["B"], t["C"])
+    kw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"], softplus=True)
+    g0 = ssmscan.scan_bwd(*args, **kw)
+    g1 = ssmscan.scan_bwd(*args, seq_lens=torch.full((4,), 300, dtype=torch.int32, device="cuda"), **kw)
+    torch.cuda.synchronize()
+    for k in ("du", "ddelta", "dz"):
+        assert torch.equal(g0[k], g1[k]), k
+
+
+def test_varlen_bwd_split_plan_and_checkpoints(oracle_mod):
+    """The split schedule (checkpoint pass and walk), lengths around the split point, sampled
+    channels against the oracle; and the same gradients from a training forward_varlen's
+    checkpoints."""
+    cus = ssmscan.plan_info(1, 256, 64, 16, 1)["cu_count"]
+    D = 64 * ((5 * cus) // 16)
+    L = 300
+    case = inputs.scan_case(8, L, D, 16, "bf16", gate=True, seed=821, name="varlen bwd split")
+    p = ssmscan.plan_info(8, L, D, 16, torch.bfloat16)
+    assert p["split_tiles"] > 0
+    mid = p["split_at"]
+    lens = np.array([L, 0, mid, mid - 1, mid + 1, 1, L - 1, 37], np.int32)
+    sel = np.unique(np.array([0, 1, 63, 64, D // 2, D - 65, D - 64, D - 2, D - 1]))
+    got, ref = _bwd_run(oracle_mod, case, lens, seed=822, channels=sel)
+    check_grads(case, got, ref, "varlen split")
+    # from the training forward's checkpoints (forward_varlen with SSM_SCAN_CHECKPOINTS), from
+    # the same initial state
+    t = case_tensors(case, torch)
+    rng = np.random.default_rng(822)
+    _ = rng.standard_normal((8, L, D), dtype=np.float32)   # (dy, drawn first in _bwd_run)
+    h0 = torch.from_numpy((0.5 * rng.standard_normal((8, D, 16))).astype(np.float32)).cuda()
+    dl = torch.from_numpy(np.asarray(lens, np.int32)).cuda()
+    _, _, ws = ssmscan.scan_fwd_varlen(dl, t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                       delta_bias=t["delta_bias"], softplus=True, initial_state=h0,
+                                       save_checkpoints=True)
+    got2, _ = _bwd_run(oracle_mod, case, lens, seed=822, channels=sel, checkpoints=ws)
+    for k in ("du", "ddelta", "dz"):
+        assert np.array_equal(got[k], got2[k]), k
