@@ -347,7 +347,7 @@ typedef struct {
     int64_t nheads;    /* heads H */
     int64_t headdim;   /* channels per head P (32 or a multiple of 64) */
     int64_t ngroups;   /* groups G of the B / C projections; H % G == 0 */
-    int64_t dstate;    /* states N (32 or 64) */
+    int64_t dstate;    /* states N (32, 64 or 128) */
     int32_t io_dtype;  /* SSM_IO_BF16 */
     int32_t reserved;  /* 0 */
 } ssm_ssd_dims;
@@ -365,8 +365,9 @@ typedef struct {
  *   B, C       : [batch][seqlen][ngroups][dstate] bf16
  *   last_state : [batch][nheads][headdim][dstate] fp32 output, or NULL
  * Supported: io_dtype SSM_IO_BF16; headdim 32 or a multiple of 64 (a head of 64 v channels
- * runs as v independent 64-channel parts); dstate 32 or 64 (32-wide heads and states are
- * padded to the 64-wide tiles with zeros, at the cost of 64-wide products);
+ * runs as v independent 64-channel parts); dstate 32, 64 or 128 (32-wide heads and states
+ * are padded to the 64-wide tiles with zeros, at the cost of 64-wide products; dstate 128
+ * takes 128-wide state tiles, one workgroup per CU, and headdim a multiple of 64);
  * nheads*headdim <= 2^24 (SSM_ERR_DTYPE / SSM_ERR_SHAPE otherwise); x, z, y, B, C 16-byte
  * aligned.  Products take bf16 operands with fp32 accumulation; the state is carried in
  * fp32.  Returns SSM_OK or a negative ssm_status. */

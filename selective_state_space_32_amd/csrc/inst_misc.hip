@@ -27,7 +27,8 @@ void launch_ssd(const void *x, const void *dt, const float *A, const void *B, co
                 const void *z, const float *dt_bias, int softplus, void *y, float *last_state, int64_t bsz,
                 int64_t L, int64_t H, int64_t G, hipStream_t st, const float *h0, int64_t P, int64_t N) {
     const int64_t vh = P > 64 ? P / 64 : 1;   // 64-channel virtual heads per head
-    auto kern = (P < 64 || N < 64) ? ssm::ssd_chunk_kernel<true> : ssm::ssd_chunk_kernel<false>;
+    auto kern = N == 128 ? ssm::ssd_chunk_kernel<false, 128>
+                         : (P < 64 || N < 64) ? ssm::ssd_chunk_kernel<true> : ssm::ssd_chunk_kernel<false>;
     hipLaunchKernelGGL(kern, dim3((unsigned)(bsz * H * vh)), dim3(ssm::kSsdThreads), 0, st,
                        static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(dt), A,
                        static_cast<const uint16_t *>(B), static_cast<const uint16_t *>(C), D,

@@ -44,10 +44,19 @@ constexpr int kSsdThreads = 256;   // four waves per (sequence, head)
 // 16-byte aligned, and 16-byte reads of eight consecutive rows fall in distinct banks), or,
 // for the C tile, swz(row, k): unpadded rows whose 16-byte unit k / 8 is stored at unit
 // (k / 8) ^ (row % 8), which spreads the same reads over all banks.
+// With dstate 128 the C, B and state tiles are 128 wide: the same layouts with rows of 136
+// (padded) or 128 (swizzled, the unit index XOR row % 8 within the row's 16 units).  Tiles of
+// width W: swp<W> (padded), swzw<W> (swizzled); sw / swz are the 64-wide ones.
 constexpr int kSsdLd = 72;
-__device__ __forceinline__ int sw(int row, int k) { return row * kSsdLd + k; }
-__device__ __forceinline__ int swz(int row, int k) { return row * 64 + ((((k >> 3) ^ row) & 7) << 3) + (k & 7); }
-template <bool Z> __device__ __forceinline__ int tix(int row, int k) { return Z ? swz(row, k) : sw(row, k); }
+template <int W> __device__ __forceinline__ int swp(int row, int k) { return row * (W + 8) + k; }
+template <int W> __device__ __forceinline__ int swzw(int row, int k) {
+    return row * W + ((((k >> 3) ^ (row & 7)) & (W / 8 - 1)) << 3) + (k & 7);
+}
+__device__ __forceinline__ int sw(int row, int k) { return swp<64>(row, k); }
+__device__ __forceinline__ int swz(int row, int k) { return swzw<64>(row, k); }
+template <bool Z, int W = 64> __device__ __forceinline__ int tix(int row, int k) {
+    return Z ? swzw<W>(row, k) : swp<W>(row, k);
+}
 // The z / y tile [t][p] has unpadded rows of 64; its 8-byte unit u (p / 4) of row t is stored
 // at unit u ^ (t % 16), so that the output layout's 8-byte accesses (32 rows, one unit) and
 // the 16-byte row accesses both spread over all banks.
@@ -77,18 +86,19 @@ __device__ __forceinline__ float wave_incl_sum(float v) {
 //   mma16_hl_a: A = ah + al (high and low parts, rows a0): acc_i += (ah + al) B_i
 //   mma16_hl_b: B = bh + bl (high and low parts): acc_i += A (bh_i + bl_i)
 //   mma16_xn  : acc_i += A B_i where enabled
-template <int KS, int NB, bool ZB>
+// (WA, WB: widths of the A and B tiles)
+template <int KS, int NB, bool ZB, int WA = 64, int WB = 64>
 __device__ __forceinline__ void mma16_hl_a(const __bf16 *ah, const __bf16 *al, int a0, const __bf16 *b, int bs,
                                            int lane, f32x4_t (&acc)[NB]) {
     const int r = lane & 15, ko = (lane >> 4) * 8;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
         const int kk = 32 * k + ko;
-        const bf16x8_t hv = *reinterpret_cast<const bf16x8_t *>(ah + sw(a0 + r, kk));
-        const bf16x8_t lv = *reinterpret_cast<const bf16x8_t *>(al + sw(a0 + r, kk));
+        const bf16x8_t hv = *reinterpret_cast<const bf16x8_t *>(ah + swp<WA>(a0 + r, kk));
+        const bf16x8_t lv = *reinterpret_cast<const bf16x8_t *>(al + swp<WA>(a0 + r, kk));
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(b + tix<ZB>(bs + 16 * i + r, kk));
+            const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(b + tix<ZB, WB>(bs + 16 * i + r, kk));
             acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, bv, acc[i], 0, 0, 0);
             acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lv, bv, acc[i], 0, 0, 0);
         }
@@ -100,31 +110,32 @@ __device__ __forceinline__ void mma16_hl_a(const __bf16 *ah, const __bf16 *al, i
 // address; so lane i addresses the 4 elements m0 + 4 (i % 4) .. +3 of row k + i / 4, and
 // lane j receives rows k .. k+3 of column m0 + j.
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+template <int W = 64>
 __device__ __forceinline__ bf16x8_t ld_tr(const __bf16 *t, int k0, int m0, int lane) {
     const int i = lane & 15, kb = k0 + 8 * (lane >> 4) + (i >> 2), m = m0 + 4 * (i & 3);
     typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-    const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(t + sw(kb, m)));
-    const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(t + sw(kb + 4, m)));
+    const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(t + swp<W>(kb, m)));
+    const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(t + swp<W>(kb + 4, m)));
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 // mma16_hl_a with both operands stored [k][m] (A: ah / al [k][row], B: b [k][col])
-template <int KS, int NB>
+template <int KS, int NB, int WA = 64, int WB = 64>
 __device__ __forceinline__ void mma16_hl_a_tr(const __bf16 *ah, const __bf16 *al, int a0, const __bf16 *b, int bs,
                                               int lane, f32x4_t (&acc)[NB]) {
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-        const bf16x8_t hv = ld_tr(ah, 32 * k, a0, lane);
-        const bf16x8_t lv = ld_tr(al, 32 * k, a0, lane);
+        const bf16x8_t hv = ld_tr<WA>(ah, 32 * k, a0, lane);
+        const bf16x8_t lv = ld_tr<WA>(al, 32 * k, a0, lane);
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            const bf16x8_t bv = ld_tr(b, 32 * k, bs + 16 * i, lane);
+            const bf16x8_t bv = ld_tr<WB>(b, 32 * k, bs + 16 * i, lane);
             acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, bv, acc[i], 0, 0, 0);
             acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lv, bv, acc[i], 0, 0, 0);
         }
     }
 }
 // (A stored [k][row]; bh padded, bl swizzled)
-template <int KS, int NB>
+template <int KS, int NB, int WB = 64>
 __device__ __forceinline__ void mma16_hl_b(const __bf16 *a, int a0, const __bf16 *bh, const __bf16 *bl, int bs,
                                            int lane, f32x4_t *acc) {
     const int r = lane & 15, ko = (lane >> 4) * 8;
@@ -134,25 +145,25 @@ __device__ __forceinline__ void mma16_hl_b(const __bf16 *a, int a0, const __bf16
         const bf16x8_t av = ld_tr(a, 32 * k, a0, lane);
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            const bf16x8_t hv = *reinterpret_cast<const bf16x8_t *>(bh + sw(bs + 16 * i + r, kk));
-            const bf16x8_t lv = *reinterpret_cast<const bf16x8_t *>(bl + swz(bs + 16 * i + r, kk));
+            const bf16x8_t hv = *reinterpret_cast<const bf16x8_t *>(bh + swp<WB>(bs + 16 * i + r, kk));
+            const bf16x8_t lv = *reinterpret_cast<const bf16x8_t *>(bl + swzw<WB>(bs + 16 * i + r, kk));
             acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hv, acc[i], 0, 0, 0);
             acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, lv, acc[i], 0, 0, 0);
         }
     }
 }
-template <int KS, int NB, bool ZB>
+template <int KS, int NB, bool ZB, int WA = 64, int WB = 64>
 __device__ __forceinline__ void mma16_xn(const __bf16 *a, int a0, const __bf16 *b, int bs, int first, int lane,
                                          f32x4_t (&acc)[NB]) {   // blocks i >= first only
     const int r = lane & 15, ko = (lane >> 4) * 8;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
         const int kk = 32 * k + ko;
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(a + sw(a0 + r, kk));
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(a + swp<WA>(a0 + r, kk));
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             if (i >= first) {
-                const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(b + tix<ZB>(bs + 16 * i + r, kk));
+                const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(b + tix<ZB, WB>(bs + 16 * i + r, kk));
                 acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[i], 0, 0, 0);
             }
         }
@@ -179,21 +190,28 @@ __device__ __forceinline__ void mma16_xn(const __bf16 *a, int a0, const __bf16 *
 //   tZ : z [t][p]                     -> (3) y, in place
 // (at most 168 registers: three workgroups of four waves per CU)
 // PAD: hp or ns is 32 (the masked loads and stores of padded channels and states).
-template <bool PAD>
-__global__ void __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(3)))
+// NT: states per tile, 64 or 128 (dstate 128: C, B, the state's copy and Bw are 128 wide, and
+// each wave holds two 16-row bands of the 128 x 64 state; 86 KB of LDS, one workgroup per CU).
+template <bool PAD, int NT = 64>
+__global__ void __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(NT == 64 ? 3 : 1)))
 ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt, const float *__restrict__ A,
                  const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm, const float *__restrict__ Dv,
                  const uint16_t *__restrict__ z, const float *__restrict__ dt_bias, uint16_t *__restrict__ y,
                  float *last_state, int64_t L, int H, int G, int softplus, const float *h0, int hp, int ns_in) {
-    const int ns = PAD ? ns_in : 64;   // (without padding the state size is the tile's)
+    const int ns = PAD ? ns_in : NT;   // (without padding the state size is the tile's)
     constexpr int Q = kSsdQ, P = kSsdP, N = kSsdN, LD = kSsdLd;
     static_assert(Q == 64 && P == 64 && N == 64, "a 16-row band and four 16 x 16 blocks per wave of four");
+    static_assert(NT == 64 || (NT == 128 && !PAD), "64 or 128 states per tile");
+    constexpr int NBS = NT / 64;                      // 16-row bands of the state per wave
+    constexpr int LDN = NT + 8;                       // row stride of the padded NT-wide tiles
+    // B / C staging: TPR threads per row of NT elements (8 each), RPB rows per pass, NPB passes
+    constexpr int TPR = NT / 8, RPB = kSsdThreads / TPR, NPB = Q / RPB;
     constexpr bool ZC = true;                         // tC is swizzled
-    __shared__ __attribute__((aligned(16))) __bf16 tC[Q * 64];
-    __shared__ __attribute__((aligned(16))) __bf16 tB[Q * LD];
+    __shared__ __attribute__((aligned(16))) __bf16 tC[Q * NT];
+    __shared__ __attribute__((aligned(16))) __bf16 tB[Q * LDN];
     __shared__ __attribute__((aligned(16))) __bf16 tX[P * LD];
-    __shared__ __attribute__((aligned(16))) __bf16 tH1[P * LD];
-    __shared__ __attribute__((aligned(16))) __bf16 tH2[P * LD];
+    __shared__ __attribute__((aligned(16))) __bf16 tH1[P * LDN];
+    __shared__ __attribute__((aligned(16))) __bf16 tH2[P * LDN];
     __shared__ __attribute__((aligned(16))) __bf16 tZ[Q * 64];
     // per-token values (formed by wave 0), four tokens per row padding of tX (tokens 4r..4r+3
     // in row r): c_t (in log2 units), f_s = exp2(c_r - c_s) dt_s with r the first token of s's
@@ -237,24 +255,33 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
     // and Bw are stored by token and read transposed where they are operands.  Addresses: the
     // chunk's base (uniform) plus a 32-bit offset per lane (64 rows of H P elements fit 32
     // bits).  z is read and y written once: streaming (non-temporal) accesses.
-    struct Raw { u32x4_t c[2], xv[2], bv[2], zv[2]; uint32_t dt; };   // rows tr0 + 32 i
+    struct Raw { u32x4_t c[NPB], xv[2], bv[NPB], zv[2]; uint32_t dt; };   // rows tr0 + 32 i (x, z), trb + RPB i (B, C)
     const uint32_t xr32 = (uint32_t)xrow, br32 = (uint32_t)brow;
     const int tr0 = tid / 8, tu = tid % 8;
-    const bool xin = !PAD || tu * 8 < pw, bin = !PAD || tu * 8 < ns;   // this thread's 8 channels / states exist
+    const int trb = tid / TPR, tub = tid % TPR;
+    const bool xin = !PAD || tu * 8 < pw, bin = !PAD || tub * 8 < ns;   // this thread's 8 channels / states exist
     const u32x4_t zero4 = {0u, 0u, 0u, 0u};
     auto fetch = [&](int64_t t0, Raw &r) {
         const uint32_t lim = (uint32_t)min((int64_t)(Q - 1), L - 1 - t0);   // last token present
         const uint32_t ts = min((uint32_t)lane, lim);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint32_t tc = min((uint32_t)(tr0 + 32 * i), lim);
-            r.c[i] = bin ? *reinterpret_cast<const u32x4_t *>(Cg + t0 * brow + (tc * br32 + (uint32_t)tu * 8)) : zero4;
-            if (zh)
-                r.zv[i] = xin ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(
-                                    zh + t0 * xrow + (tc * xr32 + (uint32_t)tu * 8)))
+        for (int i = 0; i < (NPB > 2 ? NPB : 2); ++i) {
+            const uint32_t tcb = min((uint32_t)(trb + RPB * i), lim);
+            if (i < NPB)
+                r.c[i] = bin ? *reinterpret_cast<const u32x4_t *>(Cg + t0 * brow + (tcb * br32 + (uint32_t)tub * 8))
+                             : zero4;
+            if (i < 2) {
+                const uint32_t tc = min((uint32_t)(tr0 + 32 * i), lim);
+                if (zh)
+                    r.zv[i] = xin ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(
+                                        zh + t0 * xrow + (tc * xr32 + (uint32_t)tu * 8)))
+                                  : zero4;
+                r.xv[i] = xin ? *reinterpret_cast<const u32x4_t *>(xh + t0 * xrow + (tc * xr32 + (uint32_t)tu * 8))
                               : zero4;
-            r.xv[i] = xin ? *reinterpret_cast<const u32x4_t *>(xh + t0 * xrow + (tc * xr32 + (uint32_t)tu * 8)) : zero4;
-            r.bv[i] = bin ? *reinterpret_cast<const u32x4_t *>(Bg + t0 * brow + (tc * br32 + (uint32_t)tu * 8)) : zero4;
+            }
+            if (i < NPB)
+                r.bv[i] = bin ? *reinterpret_cast<const u32x4_t *>(Bg + t0 * brow + (tcb * br32 + (uint32_t)tub * 8))
+                              : zero4;
         }
         r.dt = dt[((int64_t)b * L + t0) * H + h + (w == 0 ? ts : 0u) * (uint32_t)H];   // (used by wave 0)
     };
@@ -263,34 +290,39 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
         lo = (__bf16)(v - (float)hi);
     };
 
-    f32x4_t S[4] = {};                                 // the state H [n][p]: rows n 16 qi.., columns p 16 j..
+    // the state H [n][p]: band q, rows n = 64 q + 16 qi.., columns p 16 j..
+    f32x4_t S[NBS][4] = {};
     // the H^T [p][n] copy (high and low parts) that the next chunk's Y3 product reads:
     // column p, four consecutive n per write
     auto state_copy = [&]() {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int p = 16 * j + c16, n0 = 16 * qi + rq;
-            bf16x4_t hh, hl;
+        for (int q = 0; q < NBS; ++q)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                __bf16 hi, lo;
-                split(S[j][e], hi, lo);
-                hh[e] = hi;
-                hl[e] = lo;
+            for (int j = 0; j < 4; ++j) {
+                const int p = 16 * j + c16, n0 = 64 * q + 16 * qi + rq;
+                bf16x4_t hh, hl;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    __bf16 hi, lo;
+                    split(S[q][j][e], hi, lo);
+                    hh[e] = hi;
+                    hl[e] = lo;
+                }
+                *reinterpret_cast<bf16x4_t *>(&tH1[swp<NT>(p, n0)]) = hh;
+                *reinterpret_cast<bf16x4_t *>(&tH2[swp<NT>(p, n0)]) = hl;
             }
-            *reinterpret_cast<bf16x4_t *>(&tH1[sw(p, n0)]) = hh;
-            *reinterpret_cast<bf16x4_t *>(&tH2[sw(p, n0)]) = hl;
-        }
     };
     if (h0) {
         // the initial state into the accumulators (the layout last_state is written in)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int p = 16 * j + c16, n0 = 16 * qi + rq;
-            const float *hs = h0 + st_index(p, n0);
+        for (int q = 0; q < NBS; ++q)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) S[j][e] = (!PAD || (p < pw && n0 + e < ns)) ? hs[e] : 0.0f;
-        }
+            for (int j = 0; j < 4; ++j) {
+                const int p = 16 * j + c16, n0 = 64 * q + 16 * qi + rq;
+                const float *hs = h0 + st_index(p, n0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) S[q][j][e] = (!PAD || (p < pw && n0 + e < ns)) ? hs[e] : 0.0f;
+            }
         state_copy();   // (read after barrier (1) of the first chunk)
     }
     Raw r;
@@ -301,15 +333,15 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
         const int nt = (int)min((int64_t)Q, L - t0);
         // --- stage C, z, B and X (rows by token); wave 0: the step sizes and their running sum
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int tr = tr0 + 32 * i;
-            *reinterpret_cast<u32x4_t *>(&tC[swz(tr, tu * 8)]) = r.c[i];
-            if (zh) {
+        for (int i = 0; i < (NPB > 2 ? NPB : 2); ++i) {
+            const int tr = tr0 + 32 * i, trs = trb + RPB * i;
+            if (i < NPB) *reinterpret_cast<u32x4_t *>(&tC[swzw<NT>(trs, tub * 8)]) = r.c[i];
+            if (i < 2 && zh) {
                 const u32x4_t zv = (tr & 1) ? u32x4_t{r.zv[i].z, r.zv[i].w, r.zv[i].x, r.zv[i].y} : r.zv[i];
                 *reinterpret_cast<u32x4_t *>(&tZ[zsw16(tr, tu)]) = zv;
             }
-            *reinterpret_cast<u32x4_t *>(&tB[sw(tr, tu * 8)]) = r.bv[i];
-            *reinterpret_cast<u32x4_t *>(&tX[sw(tr, tu * 8)]) = r.xv[i];
+            if (i < NPB) *reinterpret_cast<u32x4_t *>(&tB[swp<NT>(trs, tub * 8)]) = r.bv[i];
+            if (i < 2) *reinterpret_cast<u32x4_t *>(&tX[sw(tr, tu * 8)]) = r.xv[i];
         }
         if (w == 0) {   // token = lane
             const float v = bf16_to_f32((uint16_t)r.dt) + bias_h;
@@ -322,15 +354,17 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
             *s_f4(lane) = hw_exp2((lane < 32 ? c0 : c32) - cl) * dl;
             *s_w4(lane) = hw_exp2(ctot - cl) * dl;
         }
-        const u32x4_t bcur[2] = {r.bv[0], r.bv[1]};
+        u32x4_t bcur[NPB];
+#pragma unroll
+        for (int i = 0; i < NPB; ++i) bcur[i] = r.bv[i];
         fetch(min(t0 + Q, (nchunks - 1) * Q), r);   // (the last chunk fetches itself again, unused)
         __syncthreads();                                // (1)
         const float ctot = *s_c4(Q - 1);                // c_last
         const float cref = *s_c4(qi >= 2 ? 32 : 0);     // c at the first token of this band's half-chunk
         // --- Y3^T = H^T C^T (the state entering the chunk) and G^T = B C^T
         f32x4_t Y[4] = {}, Gt[4] = {};
-        if (c > 0 || h0) mma16_hl_a<N / 32, 4, ZC>(tH1, tH2, 16 * qi, tC, 0, lane, Y);
-        mma16_xn<N / 32, 4, ZC>(tB, 16 * qi, tC, 0, qi, lane, Gt);   // blocks j >= qi (zero for s > t)
+        if (c > 0 || h0) mma16_hl_a<NT / 32, 4, ZC, NT, NT>(tH1, tH2, 16 * qi, tC, 0, lane, Y);
+        mma16_xn<NT / 32, 4, ZC, NT, NT>(tB, 16 * qi, tC, 0, qi, lane, Gt);   // blocks j >= qi (zero for s > t)
         __syncthreads();                                // (2)
         // --- M [t][s] = G^T[s][t] exp2(c_t - c_s) dt_s (s <= t) + D (s = t): rows s of this
         //     wave's band, column t; four consecutive s per 8-byte write.  The decay is
@@ -360,14 +394,14 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
                         ml[e] = lo;
                     }
                 }
-                *reinterpret_cast<bf16x4_t *>(&tB[sw(t, s0)]) = mh;
-                *reinterpret_cast<bf16x4_t *>(&tC[swz(t, s0)]) = ml;
+                *reinterpret_cast<bf16x4_t *>(&tB[swp<NT>(t, s0)]) = mh;
+                *reinterpret_cast<bf16x4_t *>(&tC[swzw<NT>(t, s0)]) = ml;
             }
         }
-        // --- Bw [s][n] = B[s][n] exp2(c_last - c_s) dt_s: tokens tr, states 8 tu .. +7
+        // --- Bw [s][n] = B[s][n] exp2(c_last - c_s) dt_s: tokens tr, states 8 tub .. +7
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int tr = tr0 + 32 * i;
+        for (int i = 0; i < NPB; ++i) {
+            const int tr = trb + RPB * i;
             const float wsl = *s_w4(tr);
             const uint32_t bw[4] = {bcur[i].x, bcur[i].y, bcur[i].z, bcur[i].w};
             bf16x8_t bhv, blv;
@@ -379,21 +413,24 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
                 bhv[2 * k] = h0; bhv[2 * k + 1] = h1;
                 blv[2 * k] = l0; blv[2 * k + 1] = l1;
             }
-            *reinterpret_cast<bf16x8_t *>(&tH1[sw(tr, tu * 8)]) = bhv;
-            *reinterpret_cast<bf16x8_t *>(&tH2[sw(tr, tu * 8)]) = blv;
+            *reinterpret_cast<bf16x8_t *>(&tH1[swp<NT>(tr, tub * 8)]) = bhv;
+            *reinterpret_cast<bf16x8_t *>(&tH2[swp<NT>(tr, tub * 8)]) = blv;
         }
         __syncthreads();                                // (3)
-        // --- H [n][p] <- exp2(c_last) H + Bw^T X   (rows n 16 qi.., columns p 16 j..)
+        // --- H [n][p] <- exp2(c_last) H + Bw^T X   (rows n 64 q + 16 qi.., columns p 16 j..)
         const float dec = hw_exp2(ctot);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) S[j] *= dec;
-        mma16_hl_a_tr<Q / 32, 4>(tH1, tH2, 16 * qi, tX, 0, lane, S);
+        for (int q = 0; q < NBS; ++q) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) S[q][j] *= dec;
+            mma16_hl_a_tr<Q / 32, 4, NT, 64>(tH1, tH2, 64 * q + 16 * qi, tX, 0, lane, S[q]);
+        }
         // --- Y^T = X^T M^T + exp2(c_t) Y3^T   (rows p 16 qi.., columns t 16 j..), then
         //     y = Y * silu(z): token t, channels 16 qi + rq .. +3, into the z slot
 #pragma unroll
         for (int j = 0; j < 4; ++j) Y[j] *= hw_exp2(*s_c4(16 * j + c16));
-        mma16_hl_b<1, 2>(tX, 16 * qi, tB, tC, 0, lane, Y);        // t < 32: s < 32 suffices
-        mma16_hl_b<2, 2>(tX, 16 * qi, tB, tC, 32, lane, Y + 2);
+        mma16_hl_b<1, 2, NT>(tX, 16 * qi, tB, tC, 0, lane, Y);        // t < 32: s < 32 suffices
+        mma16_hl_b<2, 2, NT>(tX, 16 * qi, tB, tC, 32, lane, Y + 2);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int t = 16 * j + c16;
@@ -425,13 +462,15 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
     }
     if (last_state) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int p = 16 * j + c16, n0 = 16 * qi + rq;
-            float *ls = last_state + st_index(p, n0);
+        for (int q = 0; q < NBS; ++q)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (!PAD || (p < pw && n0 + e < ns)) ls[e] = S[j][e];
-        }
+            for (int j = 0; j < 4; ++j) {
+                const int p = 16 * j + c16, n0 = 64 * q + 16 * qi + rq;
+                float *ls = last_state + st_index(p, n0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (!PAD || (p < pw && n0 + e < ns)) ls[e] = S[q][j][e];
+            }
     }
 }
 

@@ -693,10 +693,10 @@ int ssm_ssd_fwd_from(const float *initial_state, const void *x, const void *dt, 
     if (bsz < 0 || L < 0 || H < 0 || P < 0 || G < 1 || N < 0)
         return fail(SSM_ERR_SHAPE, "negative size or ngroups < 1");
     if (dims->io_dtype != SSM_IO_BF16) return fail(SSM_ERR_DTYPE, "the SSD layer takes bf16 I/O only");
-    if (!(P == 32 || (P >= 64 && P % 64 == 0)) || !(N == 32 || N == 64))
+    if (!(P == 32 || (P >= 64 && P % 64 == 0)) || !(N == 32 || N == 64 || N == 128) || (N == 128 && P == 32))
         return fail(SSM_ERR_SHAPE,
                     "headdim %lld and dstate %lld: the SSD kernel supports headdim 32 or a multiple of 64 and dstate "
-                    "32 or 64", (long long)P, (long long)N);
+                    "32, 64 or 128 (dstate 128 with headdim a multiple of 64)", (long long)P, (long long)N);
     if (H % G != 0) return fail(SSM_ERR_SHAPE, "nheads %lld is not a multiple of ngroups %lld", (long long)H,
                                 (long long)G);
     if (H > kMaxDim || bsz > kMaxDim || (bsz > 0 && H * (P > 64 ? P / 64 : 1) > (int64_t(1) << 31) / bsz))

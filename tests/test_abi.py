@@ -211,7 +211,8 @@ def test_ssd_validation(b):
         return b.lib.ssm_ssd_fwd(P(x), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None, None, flags, P(FAKE), None,
                                  ctypes.byref(d), None)
     assert call(io=0) == -3
-    assert call(hd=48) == -2 and call(hd=96) == -2 and call(ds=128) == -2 and call(ds=16) == -2
+    assert call(hd=48) == -2 and call(hd=96) == -2 and call(ds=256) == -2 and call(ds=16) == -2
+    assert call(hd=32, ds=128) == -2   # dstate 128 has no padded form for 32-wide heads
     assert call(G=3) == -2
     assert call(H=(1 << 18) + 1, G=1) == -2   # nheads*headdim above 2^24
     assert call(flags=3) == -8

@@ -141,7 +141,8 @@ def test_ssd_from_state_zero_length():
     assert torch.equal(ls, h0)
 
 
-@pytest.mark.parametrize("P,N", [(32, 64), (64, 32), (32, 32), (128, 64), (128, 32), (192, 64)])
+@pytest.mark.parametrize("P,N", [(32, 64), (64, 32), (32, 32), (128, 64), (128, 32), (192, 64), (64, 128),
+                                 (128, 128)])
 @pytest.mark.parametrize("L", [77, 200])
 def test_ssd_head_and_state_sizes(oracle_mod, P, N, L):
     """headdim 32 / 128 / 192 and dstate 32: heads of several 64-channel parts, and 32-wide
@@ -151,3 +152,34 @@ def test_ssd_head_and_state_sizes(oracle_mod, P, N, L):
     y, ls = run_gpu(c, h0)
     assert y.shape == (2, L, 4, P) and ls.shape == (2, 4, P, N)
     check(c, y, ls, *run_oracle(oracle_mod, c, h0=h0), f"P={P} N={N} L={L}")
+
+
+@pytest.mark.parametrize("L", [1, 64, 200, 513])
+@pytest.mark.parametrize("G", [1, 2])
+def test_ssd_dstate_128(oracle_mod, L, G):
+    """dstate 128 (128-wide state tiles): chunks with ragged tails, one or two groups, gate and
+    skip, from a given state."""
+    c = inputs.ssd_case(2, L, 4, P=64, G=G, N=128, seed=300 + L + G)
+    h0 = _h0(c, 301 + L)
+    y, ls = run_gpu(c, h0)
+    check(c, y, ls, *run_oracle(oracle_mod, c, h0=h0), f"N=128 L={L} G={G}")
+    y0, ls0 = run_gpu(c)
+    check(c, y0, ls0, *run_oracle(oracle_mod, c), f"N=128 L={L} G={G} from zero")
+
+
+def test_ssd_dstate_128_pieces_equal_whole():
+    """dstate 128 in two calls through the state equals one call bitwise (first piece two
+    whole chunks)."""
+    c = inputs.ssd_case(1, 256, 3, P=128, G=1, N=128, seed=310)
+    dev = lambda a: to_dev(a, torch)   # noqa: E731
+    f = lambda a: torch.from_numpy(a).cuda()   # noqa: E731
+    x, dt, B, C, z = dev(c.x), dev(c.dt), dev(c.B), dev(c.C), dev(c.z)
+    kw = dict(D=f(c.Dskip), dt_bias=f(c.dt_bias), softplus=c.softplus)
+    y0, ls0 = ssmscan.ssd_fwd(x, dt, f(c.A), B, C, z=z, **kw)
+    part = lambda t, a, b: t[:, a:b].contiguous()   # noqa: E731
+    y1, ls1 = ssmscan.ssd_fwd(part(x, 0, 128), part(dt, 0, 128), f(c.A), part(B, 0, 128), part(C, 0, 128),
+                              z=part(z, 0, 128), **kw)
+    y2, ls2 = ssmscan.ssd_fwd(part(x, 128, 256), part(dt, 128, 256), f(c.A), part(B, 128, 256),
+                              part(C, 128, 256), z=part(z, 128, 256), initial_state=ls1, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([y1, y2], 1), y0) and torch.equal(ls2, ls0)
