@@ -129,7 +129,8 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
                 float *__restrict__ dC, float *__restrict__ dD, float *__restrict__ dbias,
                 float *__restrict__ dh0, int64_t L, int64_t D, int tiles_per_b, int softplus, int n_full = 0,
                 int n_split = 0, int j_mid = 0, float *__restrict__ hand = nullptr, int *__restrict__ hflag = nullptr,
-                unsigned long long wait_ticks = 0, const int32_t *__restrict__ seq_lens = nullptr) {
+                unsigned long long wait_ticks = 0, const int32_t *__restrict__ seq_lens = nullptr,
+                int *__restrict__ prog = nullptr) {
     constexpr int S = BwdShape<N>::S;
     constexpr int K = BwdShape<N>::K;
     constexpr int T = kBwdTile;
@@ -291,8 +292,24 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
         }
         __builtin_amdgcn_s_setprio(2);
     }
+    // Pacing of the two whole tiles that share a CU (as in the forward's split schedule): each
+    // publishes its progress every 4 tiles in prog[id] and reads its sibling's (id +- C,
+    // C = grid / 3); the one behind runs at priority 1.  Issue order only: no value depends on it.
+    const int n_grid = n_full + 2 * n_split;
+    const int c_slots = n_grid / 3;
+    const int gid = (int)blockIdx.x;
+    const int sib = gid < c_slots ? gid + c_slots : gid - c_slots;
+    const bool pace = prog != nullptr && role == kWhole && n_split > 0 && sib >= 0 && sib < n_full;
+    int sib_done = 0, steps = 0;
     if (j_first >= j_last) fetch(j_first);
     for (int j = j_first; j >= j_last; --j) {
+        if (pace && (steps & 3) == 0) {
+            if (sib_done > steps) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+            if (w == 0) __hip_atomic_store(&prog[gid], steps, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sib_done = __hip_atomic_load(&prog[sib], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        ++steps;
         const int64_t t0 = (int64_t)j * T;
         const int nt = (int)min((int64_t)T, Lb - t0);
 

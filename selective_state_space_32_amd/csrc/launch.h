@@ -98,13 +98,14 @@ void launch_scan_kernels_t(const IO *u, const IO *dl, const float *A, const IO *
         // the hand-over flags start at zero (a fill kernel: no memset node if the caller captures a graph)
         int *flags = reinterpret_cast<int *>(static_cast<char *>(ws) + p.off_flags);
         float *hand = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_hand);
-        hipLaunchKernelGGL(ssm::fill_zero_kernel<int>, dim3((unsigned)((p.n_split + 255) / 256)), dim3(256), 0, st, flags,
-                           p.n_split);
+        // (the flags are followed by the whole tiles' progress counters, zeroed with them)
+        hipLaunchKernelGGL(ssm::fill_zero_kernel<int>, dim3((unsigned)((p.n_split + p.n_full + 255) / 256)), dim3(256), 0,
+                           st, flags, p.n_split + p.n_full);
         hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kFull, VEC, ZOH, CW, CK>),
                            dim3((unsigned)(p.n_full + 2 * p.n_split), 1), block, 0, st, u, dl, z, y, A, Dv, bias, B, C,
                            h0, last_state, cstate, cdsum, L, D, tiles_per_b, n_tiles, cl, nc, softplus, cv.w, cv.b,
                            static_cast<IO *>(cv.u_out), ckpt, (int)p.n_full, (int)p.n_split, p.l_mid, hand, flags,
-                           handover_wait_ticks(), seq_lens);
+                           handover_wait_ticks(), seq_lens, flags + p.n_split);
         return;
     }
     hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kFull, VEC, ZOH, CW, CK>),
@@ -289,8 +290,9 @@ int launch_bwd(const BwdArgs &a, const ssm_dims *dm, const Plan &sp, size_t ckpt
     float *hand = split ? reinterpret_cast<float *>(spw + sp.off_hand) : nullptr;
     ssm::FillList zl = a.zero;
     if (split) {
-        fill_list_add(zl, flags, sp.n_split);
-        fill_list_add(zl, wflags, sp.n_split);
+        // (each flag array is followed by the whole tiles' progress counters)
+        fill_list_add(zl, flags, sp.n_split + sp.n_full);
+        fill_list_add(zl, wflags, sp.n_split + sp.n_full);
     }
     launch_fill_list(zl, st);
     // forward in checkpoint mode: the state before every kCkptEvery-th token (unless the
@@ -308,7 +310,7 @@ int launch_bwd(const BwdArgs &a, const ssm_dims *dm, const Plan &sp, size_t ckpt
                                L, D, tiles_per_b, n_tiles, L, 1, a.softplus, (const float *)nullptr,
                                (const float *)nullptr, (IO *)nullptr, (float *)nullptr, split ? (int)sp.n_full : 0,
                                split ? (int)sp.n_split : 0, split ? sp.l_mid : (int64_t)0, hand, flags,
-                               split ? handover_wait_ticks() : 0ull, a.seq_lens);
+                               split ? handover_wait_ticks() : 0ull, a.seq_lens, split ? flags + sp.n_split : nullptr);
         };
         using T1 = std::true_type;
         using F0 = std::false_type;
@@ -328,7 +330,7 @@ int launch_bwd(const BwdArgs &a, const ssm_dims *dm, const Plan &sp, size_t ckpt
                            ddl, dz, a.dA, a.dB, a.dC, a.dD, a.dbias, a.dh0, L, D, tiles_per_b, a.softplus,
                            split ? (int)sp.n_full : 0, split ? (int)sp.n_split : 0,
                            split ? (int)(sp.l_mid / ssm::kBwdTile) : 0, hand, wflags,
-                           split ? handover_wait_ticks() : 0ull, a.seq_lens);
+                           split ? handover_wait_ticks() : 0ull, a.seq_lens, split ? wflags + sp.n_split : nullptr);
     };
     if (vb && a.zoh) walk(std::true_type{}, std::true_type{});
     else if (vb) walk(std::true_type{}, std::false_type{});

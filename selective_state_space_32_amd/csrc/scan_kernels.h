@@ -144,7 +144,7 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                   IO *__restrict__ u_out = nullptr, float *__restrict__ ckpt_out = nullptr,
                   int n_full = 0, int n_split = 0, int64_t l_mid = 0, float *__restrict__ hand = nullptr,
                   int *__restrict__ hflag = nullptr, unsigned long long wait_ticks = 0,
-                  const int32_t *__restrict__ seq_lens = nullptr) {
+                  const int32_t *__restrict__ seq_lens = nullptr, int *__restrict__ prog = nullptr) {
     constexpr int K = N / S;
     constexpr int J = T / K;                   // prep / epilogue elements per thread per tile
     constexpr int V = VEC ? (J < 8 ? J : 8) : 1;  // consecutive channels per thread access
@@ -614,6 +614,20 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
         }
         __syncthreads();
     };
+    // Pacing of whole tiles under the split schedule (prog not null): the two whole tiles that
+    // share a CU (ids g and g +- C, C = grid / 3, when workgroups are dispatched round-robin
+    // over the C CUs) would otherwise progress at different rates -- the older workgroup's
+    // waves win the issue arbitration -- and the later one would run its last ~20 % alone on
+    // the CU, at one wave per SIMD.  Each publishes the number of tile pairs it has done in
+    // prog[g] and reads its sibling's one pair later (no wait on the load); the one behind
+    // runs its waves at priority 1, the other at 0 (parts stay above, at 3 and 2).  This only
+    // orders issue: the values computed do not depend on it, nor on where the workgroups run.
+    const int n_grid = n_full + 2 * n_split;
+    const int c_slots = n_grid / 3;
+    const int sib = (int)item < c_slots ? (int)item + c_slots : (int)item - c_slots;
+    const bool pace = (MODE == kFull || MODE == kCheckpoint) && prog != nullptr && role == kWhole &&
+                      n_split > 0 && sib >= 0 && sib < n_full;
+    int sib_done = 0;
     // tiles in pairs (two input buffers, two skip/gate sets); the second tile of the last
     // pair may be empty, and its epilogue-of-the-previous-tile still runs
     DG dg0, dg1;
@@ -621,9 +635,17 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     for (int p = 0; p < P; ++p)
 #pragma unroll
         for (int v = 0; v < V; ++v) dg0.g[p][v] = dg1.g[p][v] = 1.0f;
+    int pairs_done = 0;
     for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * T) {
+        if (pace) {
+            if (sib_done > pairs_done) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+            if (w == 0) __hip_atomic_store(&prog[item], pairs_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sib_done = __hip_atomic_load(&prog[sib], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         do_tile(t0, r0, r1, dg1, dg0, t0 > t_begin);
         do_tile(t0 + T, r1, r0, dg0, dg1, true);
+        ++pairs_done;
     }
     {
         // the last pair's second tile (empty or not) still owes its epilogue (no pair: an

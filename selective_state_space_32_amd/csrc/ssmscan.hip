@@ -193,7 +193,7 @@ Plan make_plan(const ssm_dims *dm, int cus, bool align_ckpt = false, bool allow_
         p.n_full = tiles - p.n_split;
         p.l_mid = (L / 2 + 31) / 32 * 32;   // a whole number of 32-token tiles (and of checkpoint spans)
         const size_t hb = align256((size_t)(p.n_split * ssm::kChanTile * N) * sizeof(float));
-        const size_t fb = align256((size_t)p.n_split * sizeof(int));
+        const size_t fb = align256((size_t)(p.n_split + p.n_full) * sizeof(int));   // flags, then progress
         p.off_hand = 0;
         p.off_flags = hb;
         p.bytes = hb + fb;
@@ -252,7 +252,7 @@ size_t ckpt_bytes(const ssm_dims *dm) {
 // pass's flags), then the reverse walk's flags
 size_t bwd_workspace_bytes(const ssm_dims *dm) {
     const Plan p = bwd_ckpt_plan(dm);
-    return ckpt_bytes(dm) + p.bytes + (p.schedule == kSplit ? align256((size_t)p.n_split * sizeof(int)) : 0);
+    return ckpt_bytes(dm) + p.bytes + (p.schedule == kSplit ? align256((size_t)(p.n_split + p.n_full) * sizeof(int)) : 0);
 }
 
 template <typename IO>

@@ -260,7 +260,8 @@ def test_plan(b):
     assert b.scan_plan(1, 256, 16, 4, 0) == (1, 256)
     # a plain single pass needs no workspace; the split schedule holds its handed-over states
     # (128 tiles x 64 channels x 16 states fp32) and flags, the chunk carry its chunk states
-    assert b.workspace_bytes(8, 2048, 5120, 16, 1) == 128 * 64 * 16 * 4 + 512
+    # split schedule: 128 handed-over states; 128 flags and 512 progress counters (2,560 B)
+    assert b.workspace_bytes(8, 2048, 5120, 16, 1) == 128 * 64 * 16 * 4 + 2560
     assert b.workspace_bytes(16, 2048, 4096, 16, 1) == 0
     assert b.workspace_bytes(1, 131072, 2048, 16, 1) >= 256 * 2048 * 16 * 4
     assert b.workspace_bytes(1, 4096, 64, 16, 1, chunk_len=128) > b.workspace_bytes(1, 4096, 64, 16, 1, chunk_len=-1)
@@ -273,7 +274,7 @@ def test_plan_follows_the_cu_count(b):
     p = b.plan_info(8, 2048, 5120, 16, 1, cu_count=256)
     assert p["cu_count"] == 256 and p["nchunk"] == 1 and p["chunk_len"] == 2048
     assert p["split_tiles"] == 128 and p["split_at"] == 1024 and p["workgroups"] == 768
-    assert p["workspace_bytes"] == 128 * 64 * 16 * 4 + 512
+    assert p["workspace_bytes"] == 128 * 64 * 16 * 4 + 2560
     # 304 CUs (2.1 tiles per CU): 3 x 304 - 640 = 272 tiles split, 912 workgroups
     p = b.plan_info(8, 2048, 5120, 16, 1, cu_count=304)
     assert p["split_tiles"] == 272 and p["workgroups"] == 912 and p["nchunk"] == 1
