@@ -618,9 +618,10 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     // share a CU (ids g and g +- C, C = grid / 3, when workgroups are dispatched round-robin
     // over the C CUs) would otherwise progress at different rates -- the older workgroup's
     // waves win the issue arbitration -- and the later one would run its last ~20 % alone on
-    // the CU, at one wave per SIMD.  Each publishes the number of tile pairs it has done in
-    // prog[g] and reads its sibling's one pair later (no wait on the load); the one behind
-    // runs its waves at priority 1, the other at 0 (parts stay above, at 3 and 2).  This only
+    // the CU, at one wave per SIMD.  Before each tile, each publishes the number of tiles it
+    // has done in prog[g] and reads its sibling's (used one tile later: no wait on the load);
+    // the one behind runs its waves at priority 1, the other at 0 (parts stay above, at 3 and
+    // 2).  This only
     // orders issue: the values computed do not depend on it, nor on where the workgroups run.
     const int n_grid = n_full + 2 * n_split;
     const int c_slots = n_grid / 3;
@@ -635,17 +636,21 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     for (int p = 0; p < P; ++p)
 #pragma unroll
         for (int v = 0; v < V; ++v) dg0.g[p][v] = dg1.g[p][v] = 1.0f;
-    int pairs_done = 0;
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * T) {
+    int tiles_done = 0;
+    auto pace_step = [&]() {
         if (pace) {
-            if (sib_done > pairs_done) __builtin_amdgcn_s_setprio(1);
+            if (sib_done > tiles_done) __builtin_amdgcn_s_setprio(1);
             else __builtin_amdgcn_s_setprio(0);
-            if (w == 0) __hip_atomic_store(&prog[item], pairs_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (w == 0) __hip_atomic_store(&prog[item], tiles_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             sib_done = __hip_atomic_load(&prog[sib], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        ++tiles_done;
+    };
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * T) {
+        pace_step();
         do_tile(t0, r0, r1, dg1, dg0, t0 > t_begin);
+        pace_step();
         do_tile(t0 + T, r1, r0, dg0, dg1, true);
-        ++pairs_done;
     }
     {
         // the last pair's second tile (empty or not) still owes its epilogue (no pair: an
