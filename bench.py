@@ -59,6 +59,8 @@ WORKLOADS = {
 }
 WORKLOADS["ssd"] = ("Mamba-2 SSD layer B8 L2048 H80 P64 N64 G1 (model width 5120), bf16 I/O, fp32 state, "
                     "SiLU(z) gate, D skip, last_state")
+WORKLOADS["ssd_f32"] = ("Mamba-2 SSD layer B8 L2048 H80 P64 N64 G1 (model width 5120), fp32 I/O, fp32 state, "
+                        "SiLU(z) gate, D skip, last_state")
 
 
 def host_threads() -> int:
@@ -82,10 +84,10 @@ def host_cpu_model() -> str:
     return "unknown"
 
 
-def ssd_alg_bytes(bsz, L, H, P, G, N):
-    """x, z read and y written (bf16); dt (bf16) per head; B, C (bf16) per group; A, D,
-    dt_bias; the final state (fp32)."""
-    return bsz * L * H * P * 2 * 3 + bsz * L * H * 2 + bsz * L * G * N * 2 * 2 + H * 12 + bsz * H * P * N * 4
+def ssd_alg_bytes(bsz, L, H, P, G, N, es=2):
+    """x, z read and y written; dt per head; B, C per group (es bytes each: 2 for bf16, 4 for
+    fp32 I/O); A, D, dt_bias; the final state (fp32)."""
+    return bsz * L * H * P * es * 3 + bsz * L * H * es + bsz * L * G * N * es * 2 + H * 12 + bsz * H * P * N * 4
 
 
 def cpu_baseline_ssd(c, alg_bytes_full, target_s=20.0, threads=None):
@@ -420,8 +422,8 @@ def main():
     wl = args.workload
     if wl in ("c3_conv", "c3_conv_bwd"):
         case = inputs.conv_case(8, 2048, 5120, 4, "bf16", state=True, seed=185, name=wl)
-    elif wl == "ssd":
-        case = inputs.ssd_case(8, 2048, 80, 64, 1, 64, seed=230, name="ssd")
+    elif wl in ("ssd", "ssd_f32"):
+        case = inputs.ssd_case(8, 2048, 80, 64, 1, 64, seed=230, name=wl, io="f32" if wl == "ssd_f32" else "bf16")
     else:
         case = inputs.config_case("c3" if wl in ("c3_bwd", "c3_train", "c3_zoh", "c3_block", "c3_block_train")
                                   else wl)
@@ -455,19 +457,21 @@ def main():
         def one(i):
             calls[i % case.steps]()
         plan = "one step kernel per call"
-    elif wl == "ssd":
+    elif wl in ("ssd", "ssd_f32"):
         c = case
         sx, sdt, sB, sC, sz = (td(a) for a in (c.x, c.dt, c.B, c.C, c.z))
         sA, sD, sbias = td(c.A), td(c.Dskip), td(c.dt_bias)
         ys = torch.empty_like(sx)
         lss = torch.empty((c.bsz, c.H, c.P, c.N), dtype=torch.float32, device=dev)
-        alg = ssd_alg_bytes(c.bsz, c.L, c.H, c.P, c.G, c.N)
+        alg = ssd_alg_bytes(c.bsz, c.L, c.H, c.P, c.G, c.N, 4 if c.io == "f32" else 2)
         chtok = c.bsz * c.L * c.H * c.P
         elements = chtok * c.N
 
         def one(i):
             ssmscan.ssd_fwd(sx, sdt, sA, sB, sC, D=sD, z=sz, dt_bias=sbias, y=ys, last_state=lss)
-        plan = "one workgroup per (sequence, head), chunks of 64 tokens, four 64x64x64 bf16 MFMA products per chunk"
+        plan = ("one workgroup per (sequence, head), chunks of 64 tokens, four 64x64x64 bf16 MFMA products per chunk"
+                + (" (fp32 x, B, C as bf16 high + low parts: three products per pair; two workgroups per CU)"
+                   if c.io == "f32" else ""))
     elif wl == "c3_conv":
         bsz, L, D, width = case.bsz, case.L, case.D, case.width
         x, st_in = td(case.x), td(case.state)
@@ -692,7 +696,7 @@ def main():
     work_ops = elements * slots + (chtok * SLOTS_PER_CHTOK_CONV if wl in ("c3_block", "c3_block_train") else 0)
     lane_ops = work_ops / kern_s / 1e12
     traffic = counter_traffic(wl)
-    if wl in ("c5", "c3_conv", "c3_conv_bwd", "ssd"):
+    if wl in ("c5", "c3_conv", "c3_conv_bwd", "ssd", "ssd_f32"):
         roof = {"bound": "hbm", "achieved": round(kern_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(kern_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
     else:
@@ -720,6 +724,7 @@ def main():
                        "c3_bwd": lambda **k: cpu_baseline_bwd(case, alg, **k),
                        "c3_train": lambda **k: cpu_baseline_bwd(case, alg, with_forward=True, **k),
                        "ssd": lambda **k: cpu_baseline_ssd(case, alg, **k),
+                       "ssd_f32": lambda **k: cpu_baseline_ssd(case, alg, **k),
                        "c3_block": lambda **k: cpu_baseline_block(case, cc, alg, **k),
                        "c3_block_train": lambda **k: cpu_baseline_block_train(case, cc, alg, **k)}[wl]
                 cpu = with_one_core(leg)

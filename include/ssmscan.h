@@ -348,7 +348,7 @@ typedef struct {
     int64_t headdim;   /* channels per head P (32 or a multiple of 64) */
     int64_t ngroups;   /* groups G of the B / C projections; H % G == 0 */
     int64_t dstate;    /* states N (32, 64 or 128) */
-    int32_t io_dtype;  /* SSM_IO_BF16 */
+    int32_t io_dtype;  /* SSM_IO_BF16, or SSM_IO_F32 (dstate 32 or 64) */
     int32_t reserved;  /* 0 */
 } ssm_ssd_dims;
 
@@ -359,18 +359,21 @@ typedef struct {
  *   dt_t     = softplus(dt[t,h] + dt_bias[h])  (SSM_SCAN_SOFTPLUS), else dt + dt_bias
  *   S_t      = exp(dt_t A[h]) S_{t-1} + dt_t x_t B_t[g]^T      (P x N state, from zero)
  *   y_t      = (S_t C_t[g] + D[h] x_t) * silu(z_t)              (z optional)
- *   x, z, y    : [batch][seqlen][nheads][headdim] bf16
- *   dt         : [batch][seqlen][nheads] bf16
+ *   x, z, y    : [batch][seqlen][nheads][headdim] (io_dtype)
+ *   dt         : [batch][seqlen][nheads] (io_dtype)
  *   A, D, dt_bias : [nheads] fp32 (D and dt_bias may be NULL)
- *   B, C       : [batch][seqlen][ngroups][dstate] bf16
+ *   B, C       : [batch][seqlen][ngroups][dstate] (io_dtype)
  *   last_state : [batch][nheads][headdim][dstate] fp32 output, or NULL
- * Supported: io_dtype SSM_IO_BF16; headdim 32 or a multiple of 64 (a head of 64 v channels
- * runs as v independent 64-channel parts); dstate 32, 64 or 128 (32-wide heads and states
- * are padded to the 64-wide tiles with zeros, at the cost of 64-wide products; dstate 128
- * takes 128-wide state tiles, one workgroup per CU, and headdim a multiple of 64);
- * nheads*headdim <= 2^24 (SSM_ERR_DTYPE / SSM_ERR_SHAPE otherwise); x, z, y, B, C 16-byte
- * aligned.  Products take bf16 operands with fp32 accumulation; the state is carried in
- * fp32.  Returns SSM_OK or a negative ssm_status. */
+ * Supported: io_dtype SSM_IO_BF16 or SSM_IO_F32; headdim 32 or a multiple of 64 (a head of
+ * 64 v channels runs as v independent 64-channel parts); dstate 32, 64 or 128 (32-wide heads
+ * and states are padded to the 64-wide tiles with zeros, at the cost of 64-wide products;
+ * dstate 128 takes 128-wide state tiles, one workgroup per CU, headdim a multiple of 64 and
+ * bf16 I/O); nheads*headdim <= 2^24 (SSM_ERR_DTYPE / SSM_ERR_SHAPE otherwise); x, z, y, B, C
+ * 16-byte aligned.  Products take bf16 operands with fp32 accumulation: the operands formed
+ * in the kernel (the decay-weighted products and the state's copy) as high and low bf16
+ * parts, and with fp32 I/O x, B and C as well (three products per pair: about 16 bits of
+ * each operand; two workgroups per CU instead of three).  The state is carried in fp32.
+ * Returns SSM_OK or a negative ssm_status. */
 SSMSCAN_API int ssm_ssd_fwd(const void *x, const void *dt, const float *A, const void *B, const void *C,
                 const float *D, const void *z, const float *dt_bias, int flags, void *y, float *last_state,
                 const ssm_ssd_dims *dims, void *stream);

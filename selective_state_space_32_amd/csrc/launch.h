@@ -442,6 +442,6 @@ void launch_conv_bwd(int width, bool silu, const void *x, const float *w, const 
 // The SSD layer's launch (inst_misc.hip).
 void launch_ssd(const void *x, const void *dt, const float *A, const void *B, const void *C, const float *D,
                 const void *z, const float *dt_bias, int softplus, void *y, float *last_state, int64_t bsz,
-                int64_t L, int64_t H, int64_t G, hipStream_t st, const float *h0, int64_t P, int64_t N);
+                int64_t L, int64_t H, int64_t G, hipStream_t st, const float *h0, int64_t P, int64_t N, bool f32);
 
 }  // namespace ssmlib

@@ -32,6 +32,8 @@
 // whole grid of a layer with up to 768 (sequence, head) pairs is resident at once.
 #pragma once
 
+#include <type_traits>
+
 #include "device_math.h"
 
 namespace ssm {
@@ -87,9 +89,11 @@ __device__ __forceinline__ float wave_incl_sum(float v) {
 //   mma16_hl_b: B = bh + bl (high and low parts): acc_i += A (bh_i + bl_i)
 //   mma16_xn  : acc_i += A B_i where enabled
 // (WA, WB: widths of the A and B tiles)
-template <int KS, int NB, bool ZB, int WA = 64, int WB = 64>
+// With fp32 inputs (F3) the input operand is split too (b + bl: high and low bf16 parts), and
+// the products take the three terms that carry about 16 bits: ah b + al b + ah bl.
+template <int KS, int NB, bool ZB, int WA = 64, int WB = 64, bool F3 = false>
 __device__ __forceinline__ void mma16_hl_a(const __bf16 *ah, const __bf16 *al, int a0, const __bf16 *b, int bs,
-                                           int lane, f32x4_t (&acc)[NB]) {
+                                           int lane, f32x4_t (&acc)[NB], const __bf16 *bl = nullptr) {
     const int r = lane & 15, ko = (lane >> 4) * 8;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
@@ -101,6 +105,10 @@ __device__ __forceinline__ void mma16_hl_a(const __bf16 *ah, const __bf16 *al, i
             const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(b + tix<ZB, WB>(bs + 16 * i + r, kk));
             acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, bv, acc[i], 0, 0, 0);
             acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lv, bv, acc[i], 0, 0, 0);
+            if constexpr (F3) {
+                const bf16x8_t blv = *reinterpret_cast<const bf16x8_t *>(bl + tix<ZB, WB>(bs + 16 * i + r, kk));
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, blv, acc[i], 0, 0, 0);
+            }
         }
     }
 }
@@ -119,9 +127,9 @@ __device__ __forceinline__ bf16x8_t ld_tr(const __bf16 *t, int k0, int m0, int l
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 // mma16_hl_a with both operands stored [k][m] (A: ah / al [k][row], B: b [k][col])
-template <int KS, int NB, int WA = 64, int WB = 64>
+template <int KS, int NB, int WA = 64, int WB = 64, bool F3 = false>
 __device__ __forceinline__ void mma16_hl_a_tr(const __bf16 *ah, const __bf16 *al, int a0, const __bf16 *b, int bs,
-                                              int lane, f32x4_t (&acc)[NB]) {
+                                              int lane, f32x4_t (&acc)[NB], const __bf16 *bl = nullptr) {
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
         const bf16x8_t hv = ld_tr<WA>(ah, 32 * k, a0, lane);
@@ -131,40 +139,56 @@ __device__ __forceinline__ void mma16_hl_a_tr(const __bf16 *ah, const __bf16 *al
             const bf16x8_t bv = ld_tr<WB>(b, 32 * k, bs + 16 * i, lane);
             acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, bv, acc[i], 0, 0, 0);
             acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lv, bv, acc[i], 0, 0, 0);
+            if constexpr (F3) {
+                const bf16x8_t blv = ld_tr<WB>(bl, 32 * k, bs + 16 * i, lane);
+                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, blv, acc[i], 0, 0, 0);
+            }
         }
     }
 }
-// (A stored [k][row]; bh padded, bl swizzled)
-template <int KS, int NB, int WB = 64>
+// (A stored [k][row]; bh padded, bl swizzled; F3: A's low part al too, times bh)
+template <int KS, int NB, int WB = 64, bool F3 = false>
 __device__ __forceinline__ void mma16_hl_b(const __bf16 *a, int a0, const __bf16 *bh, const __bf16 *bl, int bs,
-                                           int lane, f32x4_t *acc) {
+                                           int lane, f32x4_t *acc, const __bf16 *al = nullptr) {
     const int r = lane & 15, ko = (lane >> 4) * 8;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
         const int kk = 32 * k + ko;
         const bf16x8_t av = ld_tr(a, 32 * k, a0, lane);
+        bf16x8_t alv;
+        if constexpr (F3) alv = ld_tr(al, 32 * k, a0, lane);
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             const bf16x8_t hv = *reinterpret_cast<const bf16x8_t *>(bh + swp<WB>(bs + 16 * i + r, kk));
             const bf16x8_t lv = *reinterpret_cast<const bf16x8_t *>(bl + swzw<WB>(bs + 16 * i + r, kk));
             acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, hv, acc[i], 0, 0, 0);
             acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, lv, acc[i], 0, 0, 0);
+            if constexpr (F3) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alv, hv, acc[i], 0, 0, 0);
         }
     }
 }
-template <int KS, int NB, bool ZB, int WA = 64, int WB = 64>
+// (F3: both operands split, a + al and b + bl: a b + al b + a bl)
+template <int KS, int NB, bool ZB, int WA = 64, int WB = 64, bool F3 = false>
 __device__ __forceinline__ void mma16_xn(const __bf16 *a, int a0, const __bf16 *b, int bs, int first, int lane,
-                                         f32x4_t (&acc)[NB]) {   // blocks i >= first only
+                                         f32x4_t (&acc)[NB], const __bf16 *al = nullptr,
+                                         const __bf16 *bl = nullptr) {   // blocks i >= first only
     const int r = lane & 15, ko = (lane >> 4) * 8;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
         const int kk = 32 * k + ko;
         const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(a + swp<WA>(a0 + r, kk));
+        bf16x8_t alv;
+        if constexpr (F3) alv = *reinterpret_cast<const bf16x8_t *>(al + swp<WA>(a0 + r, kk));
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             if (i >= first) {
                 const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(b + tix<ZB, WB>(bs + 16 * i + r, kk));
                 acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[i], 0, 0, 0);
+                if constexpr (F3) {
+                    const bf16x8_t blv = *reinterpret_cast<const bf16x8_t *>(bl + tix<ZB, WB>(bs + 16 * i + r, kk));
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alv, bv, acc[i], 0, 0, 0);
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, blv, acc[i], 0, 0, 0);
+                }
             }
         }
     }
@@ -192,16 +216,25 @@ __device__ __forceinline__ void mma16_xn(const __bf16 *a, int a0, const __bf16 *
 // PAD: hp or ns is 32 (the masked loads and stores of padded channels and states).
 // NT: states per tile, 64 or 128 (dstate 128: C, B, the state's copy and Bw are 128 wide, and
 // each wave holds two 16-row bands of the 128 x 64 state; 86 KB of LDS, one workgroup per CU).
-template <bool PAD, int NT = 64>
-__global__ void __launch_bounds__(kSsdThreads) __attribute__((amdgpu_waves_per_eu(NT == 64 ? 3 : 1)))
-ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt, const float *__restrict__ A,
-                 const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm, const float *__restrict__ Dv,
-                 const uint16_t *__restrict__ z, const float *__restrict__ dt_bias, uint16_t *__restrict__ y,
-                 float *last_state, int64_t L, int H, int G, int softplus, const float *h0, int hp, int ns_in) {
+// F32: fp32 x, dt, B, C, z and y (NT = 64).  x, B and C are staged as bf16 high and low parts
+// (tX / tXl, tB / tBl, tC / tCl) and every product takes the three terms of about 16 bits
+// (hi hi + lo hi + hi lo); z is read and y written from the output layout directly (no z / y
+// tile).  70 KB of LDS and up to 256 registers: two workgroups per CU.
+template <bool F32> using ssd_io_t = std::conditional_t<F32, float, uint16_t>;   // element type of x, dt, B, C, z, y
+template <bool PAD, int NT = 64, bool F32 = false>
+__global__ void __launch_bounds__(kSsdThreads)
+__attribute__((amdgpu_waves_per_eu(NT == 64 ? (F32 ? 2 : 3) : 1)))
+ssd_chunk_kernel(const ssd_io_t<F32> *__restrict__ x, const ssd_io_t<F32> *__restrict__ dt,
+                 const float *__restrict__ A, const ssd_io_t<F32> *__restrict__ Bm,
+                 const ssd_io_t<F32> *__restrict__ Cm, const float *__restrict__ Dv,
+                 const ssd_io_t<F32> *__restrict__ z, const float *__restrict__ dt_bias,
+                 ssd_io_t<F32> *__restrict__ y, float *last_state, int64_t L, int H, int G, int softplus,
+                 const float *h0, int hp, int ns_in) {
+    using TIO = ssd_io_t<F32>;
     const int ns = PAD ? ns_in : NT;   // (without padding the state size is the tile's)
     constexpr int Q = kSsdQ, P = kSsdP, N = kSsdN, LD = kSsdLd;
     static_assert(Q == 64 && P == 64 && N == 64, "a 16-row band and four 16 x 16 blocks per wave of four");
-    static_assert(NT == 64 || (NT == 128 && !PAD), "64 or 128 states per tile");
+    static_assert(NT == 64 || (NT == 128 && !PAD && !F32), "64 or 128 states per tile (64 with fp32 I/O)");
     constexpr int NBS = NT / 64;                      // 16-row bands of the state per wave
     constexpr int LDN = NT + 8;                       // row stride of the padded NT-wide tiles
     // B / C staging: TPR threads per row of NT elements (8 each), RPB rows per pass, NPB passes
@@ -212,7 +245,11 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
     __shared__ __attribute__((aligned(16))) __bf16 tX[P * LD];
     __shared__ __attribute__((aligned(16))) __bf16 tH1[P * LDN];
     __shared__ __attribute__((aligned(16))) __bf16 tH2[P * LDN];
-    __shared__ __attribute__((aligned(16))) __bf16 tZ[Q * 64];
+    __shared__ __attribute__((aligned(16))) __bf16 tZ[F32 ? 1 : Q * 64];
+    // (fp32 I/O: the low parts of C, B and X, laid out as their high parts)
+    __shared__ __attribute__((aligned(16))) __bf16 tCl[F32 ? Q * NT : 1];
+    __shared__ __attribute__((aligned(16))) __bf16 tBl[F32 ? Q * LDN : 1];
+    __shared__ __attribute__((aligned(16))) __bf16 tXl[F32 ? P * LD : 1];
     // per-token values (formed by wave 0), four tokens per row padding of tX (tokens 4r..4r+3
     // in row r): c_t (in log2 units), f_s = exp2(c_r - c_s) dt_s with r the first token of s's
     // half-chunk, and the Bw weight w_s = exp2(c_last - c_s) dt_s (dt_s = 0 past the end)
@@ -242,11 +279,11 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
     const int64_t xrow = PAD ? (int64_t)H * hp : (int64_t)Hv * P;
     const int64_t xoff = PAD ? (int64_t)h * hp + p0 : (int64_t)hv * P;
     const int64_t brow = (int64_t)G * ns;             // ... in B, C
-    const uint16_t *xh = x + (int64_t)b * L * xrow + xoff;
-    const uint16_t *zh = z ? z + (int64_t)b * L * xrow + xoff : nullptr;
-    uint16_t *yh = y + (int64_t)b * L * xrow + xoff;
-    const uint16_t *Bg = Bm + (int64_t)b * L * brow + (int64_t)g * ns;
-    const uint16_t *Cg = Cm + (int64_t)b * L * brow + (int64_t)g * ns;
+    const TIO *xh = x + (int64_t)b * L * xrow + xoff;
+    const TIO *zh = z ? z + (int64_t)b * L * xrow + xoff : nullptr;
+    TIO *yh = y + (int64_t)b * L * xrow + xoff;
+    const TIO *Bg = Bm + (int64_t)b * L * brow + (int64_t)g * ns;
+    const TIO *Cg = Cm + (int64_t)b * L * brow + (int64_t)g * ns;
     // state element (channel p, state n) of this workgroup in h0 / last_state
     const int64_t st0 = (((int64_t)b * H + h) * hp + p0) * ns;
     auto st_index = [st0, ns](int p, int n) -> int64_t { return st0 + (int64_t)p * ns + n; };
@@ -255,7 +292,10 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
     // and Bw are stored by token and read transposed where they are operands.  Addresses: the
     // chunk's base (uniform) plus a 32-bit offset per lane (64 rows of H P elements fit 32
     // bits).  z is read and y written once: streaming (non-temporal) accesses.
-    struct Raw { u32x4_t c[NPB], xv[2], bv[NPB], zv[2]; uint32_t dt; };   // rows tr0 + 32 i (x, z), trb + RPB i (B, C)
+    // (EW 16-byte units per thread and row: one for 8 bf16, two for 8 fp32; with fp32 I/O z is
+    // not staged)
+    constexpr int EW = F32 ? 2 : 1;
+    struct Raw { u32x4_t c[NPB][EW], xv[2][EW], bv[NPB][EW], zv[F32 ? 1 : 2]; uint32_t dt; };   // rows tr0 + 32 i (x, z), trb + RPB i (B, C)
     const uint32_t xr32 = (uint32_t)xrow, br32 = (uint32_t)brow;
     const int tr0 = tid / 8, tu = tid % 8;
     const int trb = tid / TPR, tub = tid % TPR;
@@ -267,23 +307,28 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
 #pragma unroll
         for (int i = 0; i < (NPB > 2 ? NPB : 2); ++i) {
             const uint32_t tcb = min((uint32_t)(trb + RPB * i), lim);
-            if (i < NPB)
-                r.c[i] = bin ? *reinterpret_cast<const u32x4_t *>(Cg + t0 * brow + (tcb * br32 + (uint32_t)tub * 8))
-                             : zero4;
-            if (i < 2) {
-                const uint32_t tc = min((uint32_t)(tr0 + 32 * i), lim);
-                if (zh)
-                    r.zv[i] = xin ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(
-                                        zh + t0 * xrow + (tc * xr32 + (uint32_t)tu * 8)))
-                                  : zero4;
-                r.xv[i] = xin ? *reinterpret_cast<const u32x4_t *>(xh + t0 * xrow + (tc * xr32 + (uint32_t)tu * 8))
-                              : zero4;
+#pragma unroll
+            for (int e = 0; e < EW; ++e) {
+                if (i < NPB)
+                    r.c[i][e] = bin ? *reinterpret_cast<const u32x4_t *>(Cg + t0 * brow + (tcb * br32 + (uint32_t)tub * 8) + 4 * e)
+                                    : zero4;
+                if (i < 2) {
+                    const uint32_t tc = min((uint32_t)(tr0 + 32 * i), lim);
+                    if (!F32 && zh)
+                        r.zv[F32 ? 0 : i] = xin ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(
+                                                      zh + t0 * xrow + (tc * xr32 + (uint32_t)tu * 8)))
+                                                : zero4;
+                    r.xv[i][e] = xin ? *reinterpret_cast<const u32x4_t *>(xh + t0 * xrow + (tc * xr32 + (uint32_t)tu * 8) + 4 * e)
+                                     : zero4;
+                }
+                if (i < NPB)
+                    r.bv[i][e] = bin ? *reinterpret_cast<const u32x4_t *>(Bg + t0 * brow + (tcb * br32 + (uint32_t)tub * 8) + 4 * e)
+                                     : zero4;
             }
-            if (i < NPB)
-                r.bv[i] = bin ? *reinterpret_cast<const u32x4_t *>(Bg + t0 * brow + (tcb * br32 + (uint32_t)tub * 8))
-                              : zero4;
         }
-        r.dt = dt[((int64_t)b * L + t0) * H + h + (w == 0 ? ts : 0u) * (uint32_t)H];   // (used by wave 0)
+        const TIO dtv = dt[((int64_t)b * L + t0) * H + h + (w == 0 ? ts : 0u) * (uint32_t)H];   // (used by wave 0)
+        if constexpr (F32) r.dt = __float_as_uint(dtv);
+        else r.dt = dtv;
     };
     auto split = [](float v, __bf16 &hi, __bf16 &lo) {
         hi = (__bf16)v;
@@ -335,16 +380,43 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
 #pragma unroll
         for (int i = 0; i < (NPB > 2 ? NPB : 2); ++i) {
             const int tr = tr0 + 32 * i, trs = trb + RPB * i;
-            if (i < NPB) *reinterpret_cast<u32x4_t *>(&tC[swzw<NT>(trs, tub * 8)]) = r.c[i];
-            if (i < 2 && zh) {
-                const u32x4_t zv = (tr & 1) ? u32x4_t{r.zv[i].z, r.zv[i].w, r.zv[i].x, r.zv[i].y} : r.zv[i];
-                *reinterpret_cast<u32x4_t *>(&tZ[zsw16(tr, tu)]) = zv;
+            if constexpr (F32) {
+                // 8 fp32 values as bf16 high and low parts
+                auto split8 = [](const u32x4_t (&v)[EW], bf16x8_t &hi, bf16x8_t &lo) {
+                    const uint32_t e8[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[EW - 1].x, v[EW - 1].y, v[EW - 1].z, v[EW - 1].w};
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const float f = __uint_as_float(e8[k]);
+                        hi[k] = (__bf16)f;
+                        lo[k] = (__bf16)(f - (float)hi[k]);
+                    }
+                };
+                bf16x8_t hv, lv;
+                if (i < NPB) {
+                    split8(r.c[i], hv, lv);
+                    *reinterpret_cast<bf16x8_t *>(&tC[swzw<NT>(trs, tub * 8)]) = hv;
+                    *reinterpret_cast<bf16x8_t *>(&tCl[swzw<NT>(trs, tub * 8)]) = lv;
+                    split8(r.bv[i], hv, lv);
+                    *reinterpret_cast<bf16x8_t *>(&tB[swp<NT>(trs, tub * 8)]) = hv;
+                    *reinterpret_cast<bf16x8_t *>(&tBl[swp<NT>(trs, tub * 8)]) = lv;
+                }
+                if (i < 2) {
+                    split8(r.xv[i], hv, lv);
+                    *reinterpret_cast<bf16x8_t *>(&tX[sw(tr, tu * 8)]) = hv;
+                    *reinterpret_cast<bf16x8_t *>(&tXl[sw(tr, tu * 8)]) = lv;
+                }
+            } else {
+                if (i < NPB) *reinterpret_cast<u32x4_t *>(&tC[swzw<NT>(trs, tub * 8)]) = r.c[i][0];
+                if (i < 2 && zh) {
+                    const u32x4_t zv = (tr & 1) ? u32x4_t{r.zv[i].z, r.zv[i].w, r.zv[i].x, r.zv[i].y} : r.zv[i];
+                    *reinterpret_cast<u32x4_t *>(&tZ[zsw16(tr, tu)]) = zv;
+                }
+                if (i < NPB) *reinterpret_cast<u32x4_t *>(&tB[swp<NT>(trs, tub * 8)]) = r.bv[i][0];
+                if (i < 2) *reinterpret_cast<u32x4_t *>(&tX[sw(tr, tu * 8)]) = r.xv[i][0];
             }
-            if (i < NPB) *reinterpret_cast<u32x4_t *>(&tB[swp<NT>(trs, tub * 8)]) = r.bv[i];
-            if (i < 2) *reinterpret_cast<u32x4_t *>(&tX[sw(tr, tu * 8)]) = r.xv[i];
         }
         if (w == 0) {   // token = lane
-            const float v = bf16_to_f32((uint16_t)r.dt) + bias_h;
+            const float v = (F32 ? __uint_as_float(r.dt) : bf16_to_f32((uint16_t)r.dt)) + bias_h;
             const float dl = lane < nt ? (softplus ? softplus_f32(v) : v) : 0.0f;   // padded tokens: identity steps
             const float cl = a2 * wave_incl_sum(dl);
             const float ctot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cl), 63));
@@ -354,17 +426,33 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
             *s_f4(lane) = hw_exp2((lane < 32 ? c0 : c32) - cl) * dl;
             *s_w4(lane) = hw_exp2(ctot - cl) * dl;
         }
-        u32x4_t bcur[NPB];
+        u32x4_t bcur[NPB][EW];
 #pragma unroll
-        for (int i = 0; i < NPB; ++i) bcur[i] = r.bv[i];
+        for (int i = 0; i < NPB; ++i)
+#pragma unroll
+            for (int e = 0; e < EW; ++e) bcur[i][e] = r.bv[i][e];
         fetch(min(t0 + Q, (nchunks - 1) * Q), r);   // (the last chunk fetches itself again, unused)
         __syncthreads();                                // (1)
         const float ctot = *s_c4(Q - 1);                // c_last
         const float cref = *s_c4(qi >= 2 ? 32 : 0);     // c at the first token of this band's half-chunk
+        // (fp32 I/O: this lane's z values in the output layout -- token 16 j + c16, channels
+        // 16 qi + rq .. +3 -- read now, used at the end of the chunk)
+        const int och = 16 * qi + rq;                   // the output layout's first channel
+        const bool och_in = !PAD || och < pw;
+        f32x4_t zq[F32 ? 4 : 1];
+        if constexpr (F32) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = min(16 * j + c16, nt - 1);
+                zq[j] = (zh && och_in) ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(
+                                             zh + t0 * xrow + ((uint32_t)t * xr32 + (uint32_t)och)))
+                                       : f32x4_t{1.0f, 1.0f, 1.0f, 1.0f};
+            }
+        }
         // --- Y3^T = H^T C^T (the state entering the chunk) and G^T = B C^T
         f32x4_t Y[4] = {}, Gt[4] = {};
-        if (c > 0 || h0) mma16_hl_a<NT / 32, 4, ZC, NT, NT>(tH1, tH2, 16 * qi, tC, 0, lane, Y);
-        mma16_xn<NT / 32, 4, ZC, NT, NT>(tB, 16 * qi, tC, 0, qi, lane, Gt);   // blocks j >= qi (zero for s > t)
+        if (c > 0 || h0) mma16_hl_a<NT / 32, 4, ZC, NT, NT, F32>(tH1, tH2, 16 * qi, tC, 0, lane, Y, tCl);
+        mma16_xn<NT / 32, 4, ZC, NT, NT, F32>(tB, 16 * qi, tC, 0, qi, lane, Gt, tBl, tCl);   // blocks j >= qi (zero for s > t)
         __syncthreads();                                // (2)
         // --- M [t][s] = G^T[s][t] exp2(c_t - c_s) dt_s (s <= t) + D (s = t): rows s of this
         //     wave's band, column t; four consecutive s per 8-byte write.  The decay is
@@ -403,15 +491,27 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
         for (int i = 0; i < NPB; ++i) {
             const int tr = trb + RPB * i;
             const float wsl = *s_w4(tr);
-            const uint32_t bw[4] = {bcur[i].x, bcur[i].y, bcur[i].z, bcur[i].w};
             bf16x8_t bhv, blv;
+            if constexpr (F32) {
+                const uint32_t bw[8] = {bcur[i][0].x, bcur[i][0].y, bcur[i][0].z, bcur[i][0].w,
+                                        bcur[i][EW - 1].x, bcur[i][EW - 1].y, bcur[i][EW - 1].z, bcur[i][EW - 1].w};
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                __bf16 h0, l0, h1, l1;
-                split(bf16_to_f32((uint16_t)(bw[k] & 0xffffu)) * wsl, h0, l0);
-                split(bf16_to_f32((uint16_t)(bw[k] >> 16)) * wsl, h1, l1);
-                bhv[2 * k] = h0; bhv[2 * k + 1] = h1;
-                blv[2 * k] = l0; blv[2 * k + 1] = l1;
+                for (int k = 0; k < 8; ++k) {
+                    __bf16 hh, ll;
+                    split(__uint_as_float(bw[k]) * wsl, hh, ll);
+                    bhv[k] = hh;
+                    blv[k] = ll;
+                }
+            } else {
+                const uint32_t bw[4] = {bcur[i][0].x, bcur[i][0].y, bcur[i][0].z, bcur[i][0].w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    __bf16 h0, l0, h1, l1;
+                    split(bf16_to_f32((uint16_t)(bw[k] & 0xffffu)) * wsl, h0, l0);
+                    split(bf16_to_f32((uint16_t)(bw[k] >> 16)) * wsl, h1, l1);
+                    bhv[2 * k] = h0; bhv[2 * k + 1] = h1;
+                    blv[2 * k] = l0; blv[2 * k + 1] = l1;
+                }
             }
             *reinterpret_cast<bf16x8_t *>(&tH1[swp<NT>(tr, tub * 8)]) = bhv;
             *reinterpret_cast<bf16x8_t *>(&tH2[swp<NT>(tr, tub * 8)]) = blv;
@@ -423,16 +523,29 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
         for (int q = 0; q < NBS; ++q) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) S[q][j] *= dec;
-            mma16_hl_a_tr<Q / 32, 4, NT, 64>(tH1, tH2, 64 * q + 16 * qi, tX, 0, lane, S[q]);
+            mma16_hl_a_tr<Q / 32, 4, NT, 64, F32>(tH1, tH2, 64 * q + 16 * qi, tX, 0, lane, S[q], tXl);
         }
         // --- Y^T = X^T M^T + exp2(c_t) Y3^T   (rows p 16 qi.., columns t 16 j..), then
         //     y = Y * silu(z): token t, channels 16 qi + rq .. +3, into the z slot
 #pragma unroll
         for (int j = 0; j < 4; ++j) Y[j] *= hw_exp2(*s_c4(16 * j + c16));
-        mma16_hl_b<1, 2, NT>(tX, 16 * qi, tB, tC, 0, lane, Y);        // t < 32: s < 32 suffices
-        mma16_hl_b<2, 2, NT>(tX, 16 * qi, tB, tC, 32, lane, Y + 2);
+        mma16_hl_b<1, 2, NT, F32>(tX, 16 * qi, tB, tC, 0, lane, Y, tXl);        // t < 32: s < 32 suffices
+        mma16_hl_b<2, 2, NT, F32>(tX, 16 * qi, tB, tC, 32, lane, Y + 2, tXl);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 4 && F32; ++j) {
+            // fp32 I/O: y straight from the accumulators (16 bytes: four channels of token t)
+            const int t = 16 * j + c16;
+            float o[4] = {Y[j][0], Y[j][1], Y[j][2], Y[j][3]};
+            if (zh) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] *= silu_f32(zq[F32 ? j : 0][e]);
+            }
+            if (t < nt && och_in)
+                __builtin_nontemporal_store(f32x4_t{o[0], o[1], o[2], o[3]},
+                    reinterpret_cast<f32x4_t *>(yh + t0 * xrow + ((uint32_t)t * xr32 + (uint32_t)och)));
+        }
+#pragma unroll
+        for (int j = 0; j < 4 && !F32; ++j) {
             const int t = 16 * j + c16;
             const int o8 = zsw8(t, 4 * qi + (lane >> 4));
             float o[4] = {Y[j][0], Y[j][1], Y[j][2], Y[j][3]};
@@ -449,7 +562,7 @@ ssd_chunk_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt
         __syncthreads();                                // (4)
         // --- y rows out (16 bytes per thread and row, the slots this thread fills with the next z)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < 2 && !F32; ++i) {
             const int tr = tr0 + 32 * i;
             if (tr < nt && xin) {
                 const u32x4_t yv = *reinterpret_cast<const u32x4_t *>(&tZ[zsw16(tr, tu)]);

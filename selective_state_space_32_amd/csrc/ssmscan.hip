@@ -692,11 +692,14 @@ int ssm_ssd_fwd_from(const float *initial_state, const void *x, const void *dt, 
                   N = dims->dstate;
     if (bsz < 0 || L < 0 || H < 0 || P < 0 || G < 1 || N < 0)
         return fail(SSM_ERR_SHAPE, "negative size or ngroups < 1");
-    if (dims->io_dtype != SSM_IO_BF16) return fail(SSM_ERR_DTYPE, "the SSD layer takes bf16 I/O only");
+    if (dims->io_dtype != SSM_IO_BF16 && dims->io_dtype != SSM_IO_F32)
+        return fail(SSM_ERR_DTYPE, "io_dtype %d is not SSM_IO_F32 (0) or SSM_IO_BF16 (1)", dims->io_dtype);
+    const bool f32 = dims->io_dtype == SSM_IO_F32;
     if (!(P == 32 || (P >= 64 && P % 64 == 0)) || !(N == 32 || N == 64 || N == 128) || (N == 128 && P == 32))
         return fail(SSM_ERR_SHAPE,
                     "headdim %lld and dstate %lld: the SSD kernel supports headdim 32 or a multiple of 64 and dstate "
                     "32, 64 or 128 (dstate 128 with headdim a multiple of 64)", (long long)P, (long long)N);
+    if (f32 && N == 128) return fail(SSM_ERR_SHAPE, "dstate 128 takes bf16 I/O (fp32 I/O: dstate 32 or 64)");
     if (H % G != 0) return fail(SSM_ERR_SHAPE, "nheads %lld is not a multiple of ngroups %lld", (long long)H,
                                 (long long)G);
     if (H > kMaxDim || bsz > kMaxDim || (bsz > 0 && H * (P > 64 ? P / 64 : 1) > (int64_t(1) << 31) / bsz))
@@ -707,7 +710,7 @@ int ssm_ssd_fwd_from(const float *initial_state, const void *x, const void *dt, 
     if (flags & ~SSM_SCAN_SOFTPLUS) return fail(SSM_ERR_FLAGS, "flags 0x%x: the SSD layer takes the softplus flag only",
                                                 flags);
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) || !aligned(z, 16) ||
-        !aligned(dt, 2) || !aligned(A, 4) || !aligned(D, 4) || !aligned(dt_bias, 4) || !aligned(last_state, 4) ||
+        !aligned(dt, f32 ? 4 : 2) || !aligned(A, 4) || !aligned(D, 4) || !aligned(dt_bias, 4) || !aligned(last_state, 4) ||
         !aligned(initial_state, 4))
         return fail(SSM_ERR_ALIGN, "x, z, y, B, C must be 16-byte aligned and the others aligned to their element size");
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -726,7 +729,7 @@ int ssm_ssd_fwd_from(const float *initial_state, const void *x, const void *dt, 
         return ok();
     }
     launch_ssd(x, dt, A, B, C, D, z, dt_bias, (flags & SSM_SCAN_SOFTPLUS) ? 1 : 0, y, last_state, bsz, L, H, G, st,
-               initial_state, P, N);
+               initial_state, P, N, f32);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

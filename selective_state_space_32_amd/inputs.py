@@ -265,21 +265,27 @@ class SsdCase:
             return None
         return bf16_to_f32(a) if a.dtype == np.uint16 else a
 
+    @property
+    def io(self) -> str:
+        return "bf16" if self.x.dtype == np.uint16 else "f32"
+
 
 def ssd_case(bsz: int, L: int, H: int, P: int = 64, G: int = 1, N: int = 64, *, gate: bool = True,
-             skip: bool = True, seed: int = 0, name: str = "ssd") -> SsdCase:
+             skip: bool = True, seed: int = 0, name: str = "ssd", io: str = "bf16") -> SsdCase:
     """Draw order A, D, dt_bias, x, dt, B, C, z.  A = -exp(U[log 1, log 16]) per head; dt_bias =
     log(expm1(U[1e-3, 0.1])) (step sizes between 1e-3 and 0.1 at dt = 0); dt ~ 0.5 N(0, 1);
-    x, B, C, z ~ N(0, 1); D ~ N(0, 1).  bf16 tensors are the RNE rounding of fp32 draws."""
+    x, B, C, z ~ N(0, 1); D ~ N(0, 1).  io "bf16": x, dt, B, C, z are the RNE rounding of the fp32
+    draws (bit patterns); "f32": the fp32 draws themselves."""
+    cast = bf16_bits if io == "bf16" else (lambda a: np.ascontiguousarray(a, dtype=np.float32))
     rng = np.random.default_rng(seed)
     A = (-np.exp(rng.uniform(0.0, np.log(16.0), H))).astype(np.float32)
     Dskip = rng.standard_normal(H).astype(np.float32) if skip else None
     dt_bias = np.log(np.expm1(rng.uniform(1e-3, 0.1, H))).astype(np.float32)
-    x = bf16_bits(rng.standard_normal((bsz, L, H, P), dtype=np.float32))
-    dt = bf16_bits((0.5 * rng.standard_normal((bsz, L, H))).astype(np.float32))
-    B = bf16_bits(rng.standard_normal((bsz, L, G, N), dtype=np.float32))
-    C = bf16_bits(rng.standard_normal((bsz, L, G, N), dtype=np.float32))
-    z = bf16_bits(rng.standard_normal((bsz, L, H, P), dtype=np.float32)) if gate else None
+    x = cast(rng.standard_normal((bsz, L, H, P), dtype=np.float32))
+    dt = cast((0.5 * rng.standard_normal((bsz, L, H))).astype(np.float32))
+    B = cast(rng.standard_normal((bsz, L, G, N), dtype=np.float32))
+    C = cast(rng.standard_normal((bsz, L, G, N), dtype=np.float32))
+    z = cast(rng.standard_normal((bsz, L, H, P), dtype=np.float32)) if gate else None
     return SsdCase(name, bsz, L, H, P, G, N, x, dt, A, B, C, Dskip, z, dt_bias, True, seed)
 
 

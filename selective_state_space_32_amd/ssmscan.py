@@ -649,13 +649,15 @@ def ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
             last_state: Optional[torch.Tensor] = None, return_last_state: bool = True,
             initial_state: Optional[torch.Tensor] = None, stream=None):
     """Mamba-2's SSD layer (ssm_ssd_fwd; ssm_ssd_fwd_from with initial_state).  x, z:
-    (batch, L, H, P) bfloat16; dt: (batch, L, H) bfloat16; A, D, dt_bias: (H,) float32; B, C:
-    (batch, L, G, N) bfloat16; initial_state: (batch, H, P, N) float32 (may be last_state).
-    Returns (y (batch, L, H, P), last_state (batch, H, P, N) float32 or None)."""
+    (batch, L, H, P); dt: (batch, L, H); B, C: (batch, L, G, N) -- all bfloat16, or all float32
+    (dstate 32 or 64); A, D, dt_bias: (H,) float32; initial_state: (batch, H, P, N) float32 (may
+    be last_state).  Returns (y (batch, L, H, P) in x's dtype, last_state (batch, H, P, N) float32
+    or None)."""
     bsz, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     dev = x.device
-    bf = torch.bfloat16
+    bf = x.dtype
+    io = _io_code(bf)
     _need(x, "x", (bsz, L, H, P), bf, dev)
     _need(dt, "dt", (bsz, L, H), bf, dev)
     _need(A, "A", (H,), torch.float32, dev)
@@ -673,7 +675,7 @@ def ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
         y = torch.empty((bsz, L, H, P), dtype=bf, device=dev)
     if last_state is None and return_last_state:
         last_state = torch.empty((bsz, H, P, N), dtype=torch.float32, device=dev)
-    dims = ssm_ssd_dims(bsz, L, H, P, G, N, SSM_IO_BF16, 0)
+    dims = ssm_ssd_dims(bsz, L, H, P, G, N, io, 0)
     _check(lib.ssm_ssd_fwd_from(_ptr(initial_state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                                 _ptr(z), _ptr(dt_bias), 1 if softplus else 0, _ptr(y), _ptr(last_state),
                                 ctypes.byref(dims), _stream_handle(stream)))

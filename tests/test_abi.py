@@ -210,7 +210,8 @@ def test_ssd_validation(b):
         d = b.ssm_ssd_dims(2, 100, H, hd, G, ds, io, 0)
         return b.lib.ssm_ssd_fwd(P(x), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None, None, flags, P(FAKE), None,
                                  ctypes.byref(d), None)
-    assert call(io=0) == -3
+    assert call(io=7) == -3
+    assert call(io=0, ds=128) == -2     # fp32 I/O: dstate 32 or 64
     assert call(hd=48) == -2 and call(hd=96) == -2 and call(ds=256) == -2 and call(ds=16) == -2
     assert call(hd=32, ds=128) == -2   # dstate 128 has no padded form for 32-wide heads
     assert call(G=3) == -2

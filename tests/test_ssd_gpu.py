@@ -1,7 +1,9 @@
 """Parity of Mamba-2's SSD layer on the matrix cores (ssm_ssd_fwd, through the C ABI) with the
-fp64 oracle on the same seeded inputs.  The products take bf16 operands (the decay-weighted
-matrix M, the weighted B and the state's copy are rounded to bf16), so y is held to the bf16
-tolerance of the scan (3e-3 rms before its own final rounding) and the state to 3e-3 rms."""
+fp64 oracle on the same seeded inputs.  With bf16 I/O the products take bf16 operands (the formed
+operands -- the decay-weighted matrix M, the weighted B and the state's copy -- as high and low
+bf16 parts), so y is held to the bf16 tolerance of the scan (3e-3 rms before its own final
+rounding) and the state to 3e-3 rms.  With fp32 I/O x, B and C are split into high and low parts
+too (three products per pair, about 16 bits) and y and the state are held to 1e-3 rms (SSD_TOL)."""
 import numpy as np
 import pytest
 
@@ -15,6 +17,14 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 from selective_state_space_32_amd import ssmscan  # noqa: E402
+
+# fp32 I/O: every product takes 16-bit operands (bf16 high + low parts, three of the four
+# partial products), a relative error of at most 2^-15 per term; a 64-token chunk's outputs
+# sum about 64 + 64 such terms, whose absolute sum is ~6x the rms of the result for these
+# Gaussian inputs, and the maximum over a layer's outputs is ~5x the typical error: 2^-15 x 6 x
+# 5 ~ 1e-3 of rms(y).  (Measured: 1e-4 to 5e-4; the scan's fp32 bound of 1e-4 would need
+# 24-bit operands.)
+SSD_TOL = {"bf16": TOL["bf16"], "f32": 1e-3}
 
 
 def run_gpu(c, h0=None):
@@ -38,11 +48,15 @@ def run_oracle(oracle_mod, c, heads=None, h0=None):
 
 
 def check(c, y, ls, y_ref, ls_ref, label):
-    ey, es = y_error(y, y_ref, "bf16"), raw_error(ls, ls_ref)
-    print(f"[ssd {label}] y err/rms {ey:.3e} (raw {raw_error(y, y_ref):.3e})  last_state {es:.3e}  "
-          f"tol {TOL['bf16']}", flush=True)
+    """The I/O type's tolerance for y and for the state: 3e-3 rms with bf16 I/O (y before its
+    final rounding), 1e-4 rms with fp32 I/O."""
+    io = c.io
+    tol = SSD_TOL[io]
+    ey, es = y_error(y, y_ref, io), raw_error(ls, ls_ref)
+    print(f"[ssd {io} {label}] y err/rms {ey:.3e} (raw {raw_error(y, y_ref):.3e})  last_state {es:.3e}  "
+          f"tol {tol}", flush=True)
     assert np.all(np.isfinite(y)) and np.all(np.isfinite(ls))
-    assert ey <= TOL["bf16"] and es <= TOL["bf16"], (label, ey, es)
+    assert ey <= tol and es <= tol, (label, ey, es)
 
 
 @pytest.mark.parametrize("L", [1, 63, 64, 200, 513])
@@ -183,3 +197,77 @@ def test_ssd_dstate_128_pieces_equal_whole():
                               part(C, 128, 256), z=part(z, 128, 256), initial_state=ls1, **kw)
     torch.cuda.synchronize()
     assert torch.equal(torch.cat([y1, y2], 1), y0) and torch.equal(ls2, ls0)
+
+
+# --- fp32 I/O (dstate 32 or 64)
+
+@pytest.mark.parametrize("L", [1, 63, 64, 200, 513])
+@pytest.mark.parametrize("G", [1, 2])
+def test_ssd_f32_small(oracle_mod, L, G):
+    """fp32 x, dt, B, C, z and y: chunks of 64 with ragged tails, one or two groups."""
+    c = inputs.ssd_case(2, L, 4, G=G, seed=410 + L + G, io="f32")
+    y, ls = run_gpu(c)
+    check(c, y, ls, *run_oracle(oracle_mod, c), f"L={L} G={G}")
+
+
+@pytest.mark.parametrize("gate,skip", [(False, False), (True, False), (False, True)])
+def test_ssd_f32_optional_inputs(oracle_mod, gate, skip):
+    c = inputs.ssd_case(1, 300, 3, G=3, gate=gate, skip=skip, seed=420, io="f32")
+    y, ls = run_gpu(c)
+    check(c, y, ls, *run_oracle(oracle_mod, c), f"gate={gate} skip={skip}")
+
+
+@pytest.mark.parametrize("P,N", [(32, 64), (64, 32), (32, 32), (128, 64), (192, 32)])
+@pytest.mark.parametrize("L", [77, 200])
+def test_ssd_f32_head_and_state_sizes(oracle_mod, P, N, L):
+    """fp32 I/O with 32-wide heads or states (padded tiles) and heads of several 64-channel
+    parts, from a given state."""
+    c = inputs.ssd_case(2, L, 4, P=P, G=2, N=N, seed=430 + P + N + L, io="f32")
+    h0 = _h0(c, 431 + P + N)
+    y, ls = run_gpu(c, h0)
+    assert y.shape == (2, L, 4, P) and ls.shape == (2, 4, P, N)
+    check(c, y, ls, *run_oracle(oracle_mod, c, h0=h0), f"P={P} N={N} L={L}")
+
+
+def test_ssd_f32_layer_size_sampled(oracle_mod):
+    """B8 L2048 H80 P64 N64 G1 with fp32 I/O: sampled heads (all batches, tokens, channels)."""
+    c = inputs.ssd_case(8, 2048, 80, G=1, seed=440, io="f32")
+    y, ls = run_gpu(c)
+    heads = np.array([0, 33, 79])
+    y_ref, ls_ref = run_oracle(oracle_mod, c, heads)
+    check(c, y[:, :, heads], ls[:, heads], y_ref, ls_ref, "layer, 3 heads")
+
+
+def test_ssd_f32_pieces_equal_whole():
+    """fp32 I/O in two calls through the state (in place) equals one call bitwise (first piece a
+    whole number of chunks); repeated calls are bitwise the same."""
+    c = inputs.ssd_case(2, 320, 3, G=1, seed=450, io="f32")
+    dev = lambda a: to_dev(a, torch)   # noqa: E731
+    f = lambda a: torch.from_numpy(a).cuda()   # noqa: E731
+    x, dt, B, C, z = dev(c.x), dev(c.dt), dev(c.B), dev(c.C), dev(c.z)
+    kw = dict(D=f(c.Dskip), dt_bias=f(c.dt_bias), softplus=c.softplus)
+    y0, ls0 = ssmscan.ssd_fwd(x, dt, f(c.A), B, C, z=z, **kw)
+    assert y0.dtype == torch.float32
+    ya, lsa = ssmscan.ssd_fwd(x, dt, f(c.A), B, C, z=z, **kw)
+    cut = 192
+    part = lambda t, a, b: t[:, a:b].contiguous()   # noqa: E731
+    y1, ls1 = ssmscan.ssd_fwd(part(x, 0, cut), part(dt, 0, cut), f(c.A), part(B, 0, cut), part(C, 0, cut),
+                              z=part(z, 0, cut), **kw)
+    y2, ls2 = ssmscan.ssd_fwd(part(x, cut, c.L), part(dt, cut, c.L), f(c.A), part(B, cut, c.L),
+                              part(C, cut, c.L), z=part(z, cut, c.L), initial_state=ls1, last_state=ls1, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(ya, y0) and torch.equal(lsa, ls0)
+    assert torch.equal(torch.cat([y1, y2], 1), y0) and torch.equal(ls2, ls0)
+
+
+def test_ssd_f32_agrees_with_bf16_inputs(oracle_mod):
+    """The fp32 path on inputs that are bf16 values (exactly representable): its y agrees with
+    the bf16 path's y to the bf16 output rounding, both against the oracle."""
+    cb = inputs.ssd_case(2, 200, 4, G=2, seed=460)
+    cf = inputs.SsdCase(**{**cb.__dict__, **{k: cb.values(k) for k in ("x", "dt", "B", "C", "z")}})
+    assert cf.io == "f32"
+    yb, lb = run_gpu(cb)
+    yf, lf = run_gpu(cf)
+    y_ref, ls_ref = run_oracle(oracle_mod, cb)
+    check(cb, yb, lb, y_ref, ls_ref, "bf16 inputs, bf16 path")
+    check(cf, yf, lf, y_ref, ls_ref, "bf16 inputs, fp32 path")
