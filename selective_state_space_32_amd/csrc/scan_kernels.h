@@ -131,8 +131,10 @@ __device__ __forceinline__ void load_slice(const IO *__restrict__ p, int64_t off
 //        tile and the CW - 1 rows before it), filled one tile ahead from the prefetched
 //        registers; a conv phase with lane = channel (each wave takes the rows its own
 //        threads prepare, its CW taps in registers) writes u where the prep reads it.
+// (N = 16: three workgroups of four waves must fit on a CU -- the split schedule and the
+// one-pass grid are planned for it -- so the register budget is held to 168.)
 template <int N, int S, int T, typename IO, int MODE, bool VEC, bool ZOH = false, int CW = 0, bool CK = false>
-__global__ void __launch_bounds__(64 * (N / S))
+__global__ void __launch_bounds__(64 * (N / S)) __attribute__((amdgpu_waves_per_eu(N == 16 ? 3 : 1)))
 scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                   const IO *__restrict__ z, IO *__restrict__ y,
                   const float *__restrict__ A, const float *__restrict__ Dv,
@@ -618,10 +620,10 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     // share a CU (ids g and g +- C, C = grid / 3, when workgroups are dispatched round-robin
     // over the C CUs) would otherwise progress at different rates -- the older workgroup's
     // waves win the issue arbitration -- and the later one would run its last ~20 % alone on
-    // the CU, at one wave per SIMD.  Before each tile, each publishes the number of tiles it
-    // has done in prog[g] and reads its sibling's (used one tile later: no wait on the load);
-    // the one behind runs its waves at priority 1, the other at 0 (parts stay above, at 3 and
-    // 2).  This only
+    // the CU, at one wave per SIMD.  Before each pair of tiles, each publishes the number of
+    // pairs it has done in prog[g] and reads its sibling's (used one pair later: no wait on the
+    // load); the one behind runs its waves at priority 1, the other at 0 (parts stay above, at
+    // 3 and 2).  This only
     // orders issue: the values computed do not depend on it, nor on where the workgroups run.
     const int n_grid = n_full + 2 * n_split;
     const int c_slots = n_grid / 3;
@@ -636,21 +638,17 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     for (int p = 0; p < P; ++p)
 #pragma unroll
         for (int v = 0; v < V; ++v) dg0.g[p][v] = dg1.g[p][v] = 1.0f;
-    int tiles_done = 0;
-    auto pace_step = [&]() {
+    int pairs_done = 0;
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * T) {
         if (pace) {
-            if (sib_done > tiles_done) __builtin_amdgcn_s_setprio(1);
+            if (sib_done > pairs_done) __builtin_amdgcn_s_setprio(1);
             else __builtin_amdgcn_s_setprio(0);
-            if (w == 0) __hip_atomic_store(&prog[item], tiles_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (w == 0) __hip_atomic_store(&prog[item], pairs_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             sib_done = __hip_atomic_load(&prog[sib], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        ++tiles_done;
-    };
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * T) {
-        pace_step();
         do_tile(t0, r0, r1, dg1, dg0, t0 > t_begin);
-        pace_step();
         do_tile(t0 + T, r1, r0, dg0, dg1, true);
+        ++pairs_done;
     }
     {
         // the last pair's second tile (empty or not) still owes its epilogue (no pair: an
