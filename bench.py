@@ -173,6 +173,27 @@ def counter_traffic(workload: str):
     return c.get("hbm_bytes_per_launch")
 
 
+def sized_sample(run, n_total, target_s, probe_n=16):
+    """Indices of a sample of n_total independent items (channels, heads) sized to about
+    target_s seconds of run(sel), and the time it took: a probe of probe_n items estimates the
+    time per item; a sample that ran in under 0.6 of the target (the probe overstates the cost
+    of a larger, better-threaded sample) is enlarged by its own measured rate, at most twice."""
+    probe = np.unique(np.linspace(0, n_total - 1, min(probe_n, n_total)).astype(np.int64))
+    t = time.perf_counter()
+    run(probe)
+    per = (time.perf_counter() - t) / len(probe)
+    k = int(min(n_total, max(len(probe), target_s / max(per, 1e-9))))
+    for _ in range(3):
+        sel = np.unique(np.linspace(0, n_total - 1, k).astype(np.int64))
+        t = time.perf_counter()
+        run(sel)
+        dt = time.perf_counter() - t
+        if dt >= 0.6 * target_s or len(sel) >= n_total:
+            break
+        k = int(min(n_total, len(sel) * target_s / max(dt, 1e-9)))
+    return sel, dt
+
+
 def cpu_baseline_scan(case, alg_bytes_full, target_s=12.0, target_1core_s=8.0, exact_zoh=False):
     """Time the fp64 oracle on channel samples of the workload: on all the host cores this
     process may use (OpenMP over channels), and on one core.  Channels are independent, so
@@ -183,15 +204,8 @@ def cpu_baseline_scan(case, alg_bytes_full, target_s=12.0, target_1core_s=8.0, e
     D = case.D
 
     def timed(threads_, budget):
-        probe = np.arange(0, D, max(1, D // 16))[:16]
-        t = time.perf_counter()
-        oracle.scan_case(case, channels=probe, threads=threads_, exact_zoh=exact_zoh)
-        per_ch = (time.perf_counter() - t) / len(probe)
-        k = int(min(D, max(len(probe), budget / max(per_ch, 1e-9))))
-        sel = np.unique(np.linspace(0, D - 1, k).astype(np.int64))
-        t = time.perf_counter()
-        oracle.scan_case(case, channels=sel, threads=threads_, exact_zoh=exact_zoh)
-        return sel, time.perf_counter() - t
+        return sized_sample(lambda sel: oracle.scan_case(case, channels=sel, threads=threads_, exact_zoh=exact_zoh),
+                            D, budget)
 
     sel, dt = timed(threads, target_s)
     sel1, dt1 = timed(1, target_1core_s)
@@ -225,15 +239,7 @@ def cpu_baseline_bwd(case, alg_bytes_full, target_s=20.0, with_forward=False, th
                         case.values("C"), np.resize(dyv, (case.bsz, case.L, len(sel))), D=case.Dskip[sel],
                         z=None if zv is None else zv[:, :, sel], delta_bias=case.delta_bias[sel],
                         softplus=case.softplus, threads=threads)
-    probe = np.arange(16)
-    t = time.perf_counter()
-    run(probe)
-    per_ch = (time.perf_counter() - t) / len(probe)
-    k = int(min(case.D, max(16, target_s / max(per_ch, 1e-9))))
-    sel = np.linspace(0, case.D - 1, k).astype(np.int64)
-    t = time.perf_counter()
-    run(sel)
-    dt = time.perf_counter() - t
+    sel, dt = sized_sample(run, case.D, target_s)
     return {"value": round(alg_bytes_full * len(sel) / case.D / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"{len(sel)} of {case.D} channels x all {case.bsz} sequences x {case.L} tokens "
