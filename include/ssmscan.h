@@ -104,7 +104,8 @@ typedef struct ssm_dims {
 
 /* Bytes of device workspace ssm_scan_fwd needs for these sizes and plan on the current device
  * (256-byte aligned regions): the per-chunk carry states of a chunked plan, the handed-over
- * states and flags of the split schedule (see ssm_scan_plan_info), 0 for a plain single
+ * states, flags and progress counters of the split schedule (see ssm_scan_plan_info; the
+ * library clears the flags and counters itself on every call), 0 for a plain single
  * pass.  Returns 0 for an invalid or empty problem. */
 SSMSCAN_API size_t ssm_scan_workspace_bytes(const ssm_dims *dims);
 
@@ -215,7 +216,8 @@ SSMSCAN_API int ssm_scan_fwd_varlen(const float *initial_state, const int32_t *s
 /* Bytes of device workspace ssm_scan_bwd needs: the checkpointed states, one per 8
  * tokens (batch * ceil(seqlen / 8) * dim * dstate fp32, 256-byte aligned), followed, for
  * shapes the library runs under the split schedule (see ssm_plan_info), by that schedule's
- * hand-over scratch (states and flags of the checkpoint pass and of the reverse walk).
+ * hand-over scratch (states, flags and progress counters of the checkpoint pass and of the
+ * reverse walk).
  * Depends on the current device's CU count.
  * Returns 0 for an invalid or empty problem. */
 SSMSCAN_API size_t ssm_scan_bwd_workspace_bytes(const ssm_dims *dims);
