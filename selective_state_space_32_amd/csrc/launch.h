@@ -36,6 +36,7 @@ struct Plan {
     int64_t nchunk = 1;      // chunks per sequence (work items per tile)
     int64_t chunk_len = 0;   // tokens per chunk
     int64_t n_full = 0, n_split = 0, l_mid = 0;   // the split schedule
+    bool fold = false;       // chunk carry: the final pass composes the chunk summaries itself
     size_t off_cstate = 0, off_cdsum = 0, off_hand = 0, off_flags = 0, bytes = 0;
 };
 
@@ -90,9 +91,11 @@ void launch_scan_kernels_t(const IO *u, const IO *dl, const float *A, const IO *
                            (float *)nullptr, cstate, cdsum, L, D, tiles_per_b, n_tiles, cl, nc, softplus, cv.w, cv.b,
                            (IO *)nullptr, (float *)nullptr, 0, 0, (int64_t)0, (float *)nullptr, (int *)nullptr, 0ull,
                            seq_lens);
-        const int col_tiles = (int)((D * N + 63) / 64);
-        hipLaunchKernelGGL((ssm::carry_scan_kernel<N>), dim3((unsigned)(bsz * col_tiles)), dim3(256), 0, st,
-                           cstate, (const float *)cdsum, A, h0, D, nc, col_tiles);
+        if (!p.fold) {
+            const int col_tiles = (int)((D * N + 63) / 64);
+            hipLaunchKernelGGL((ssm::carry_scan_kernel<N>), dim3((unsigned)(bsz * col_tiles)), dim3(256), 0, st,
+                               cstate, (const float *)cdsum, A, h0, D, nc, col_tiles);
+        }
     }
     if (p.schedule == kSplit) {
         // the hand-over flags start at zero (a fill kernel: no memset node if the caller captures a graph)
@@ -112,7 +115,7 @@ void launch_scan_kernels_t(const IO *u, const IO *dl, const float *A, const IO *
                        dim3((unsigned)n_tiles, (unsigned)nc), block, 0, st, u, dl, z, y, A, Dv, bias, B, C, h0,
                        last_state, cstate, cdsum, L, D, tiles_per_b, n_tiles, cl, nc, softplus, cv.w, cv.b,
                        static_cast<IO *>(cv.u_out), ckpt, 0, 0, (int64_t)0, (float *)nullptr, (int *)nullptr, 0ull,
-                       seq_lens);
+                       seq_lens, (int *)nullptr, p.schedule == kCarry && p.fold ? 1 : 0);
 }
 
 // The scan's launches with the plan's tile length (TC under the chunk carry, else T).

@@ -84,11 +84,13 @@ __device__ __forceinline__ void load_slice(const IO *__restrict__ p, int64_t off
 
 // The scan over (tile, chunk) work items.
 //   kFull:    start from the state before the chunk -- for chunk 0 the initial state h0
-//             (zero if h0 is null), for a later chunk the carried state cstate[b][c-1] --
+//             (zero if h0 is null), for a later chunk the carried state cstate[b][c-1], or,
+//             with fold, that state composed here from the chunk summaries cstate[b][k] and
+//             cdsum[b][k] of the chunks k < c and h0 (no carry pass runs then) --
 //             run the recurrence with readout, write y; the last chunk writes last_state.
-//             With several chunks the initial state is read from its copy in slot
-//             cstate[b][nchunk-1] (written by the carry pass), never from h0, so h0 may be
-//             the last_state buffer.
+//             With several chunks and the carry pass the initial state is read from its copy
+//             in slot cstate[b][nchunk-1] (written by the carry pass), never from h0, so h0
+//             may be the last_state buffer (the host does not fold then).
 //   kSummary: start from h = 0, no readout; write the chunk's local final state to
 //             cstate[b][c] and the chunk's sum of step sizes to cdsum[b][c].
 //   kCheckpoint: one pass from h0 without readout, storing the state before every
@@ -146,7 +148,8 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
                   IO *__restrict__ u_out = nullptr, float *__restrict__ ckpt_out = nullptr,
                   int n_full = 0, int n_split = 0, int64_t l_mid = 0, float *__restrict__ hand = nullptr,
                   int *__restrict__ hflag = nullptr, unsigned long long wait_ticks = 0,
-                  const int32_t *__restrict__ seq_lens = nullptr, int *__restrict__ prog = nullptr) {
+                  const int32_t *__restrict__ seq_lens = nullptr, int *__restrict__ prog = nullptr,
+                  int fold = 0) {
     constexpr int K = N / S;
     constexpr int J = T / K;                   // prep / epilogue elements per thread per tile
     constexpr int V = VEC ? (J < 8 ? J : 8) : 1;  // consecutive channels per thread access
@@ -263,6 +266,22 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     if (role == kSecondPart && act) {
 #pragma unroll
         for (int s = 0; s < S; ++s) h[s] = hand[((int64_t)(tile - n_full) * kChanTile + lane) * N + w * S + s];
+    } else if (MODE == kFull && fold && nchunk > 1 && act) {
+        // the state before this chunk composed from the chunk summaries (local final state
+        // from zero and summed step size of each earlier chunk), in chunk order:
+        // h <- exp(A * sum of delta over chunk k) h + local_k, from the initial state
+        if (h0) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) h[s] = h0[((int64_t)b * D + d) * N + w * S + s];
+        }
+#pragma unroll 4
+        for (int k = 0; k < c; ++k) {
+            const int64_t row = (int64_t)b * nchunk + k;
+            const float ds = cdsum[row * D + d];
+            const float *loc = cstate + (row * D + d) * N + w * S;
+#pragma unroll
+            for (int s = 0; s < S; ++s) h[s] = fmaf(hw_exp2(a2[s] * ds), h[s], loc[s]);
+        }
     } else if ((MODE == kFull || MODE == kCheckpoint) && act) {
         // the state before this chunk: carried from chunk c-1, or the initial state (read
         // from h0 itself in a single pass, from the copy in slot nchunk-1 otherwise)

@@ -86,6 +86,10 @@ bool n_supported(int64_t n) { return n == 1 || n == 2 || n == 4 || n == 8 || n =
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 constexpr int64_t kMaxElems = int64_t(1) << 46;
 constexpr int kMaxChunks = 65535;  // grid.y limit
+// With at most this many chunks per sequence the final pass composes the chunk summaries
+// before its chunk itself (a few loads and exponentials per state) instead of a separate
+// carry launch; with more, the carry kernel's scan over chunks is cheaper.
+constexpr int64_t kFoldMaxChunks = 16;
 // Scan workgroups resident per CU (N = 16: 133-137 VGPRs and 48 KB of LDS per 4-wave group),
 // the basis of the schedules below.
 constexpr int kGroupsPerCU = 3;
@@ -181,6 +185,9 @@ Plan make_plan(const ssm_dims *dm, int cus, bool align_ckpt = false, bool allow_
     p.nchunk = (L + clen - 1) / clen;
     if (p.schedule == kCarry && p.nchunk == 1) p.schedule = kGrid;
     if (p.schedule == kCarry) {
+        // (not when the initial state is the last_state buffer: every chunk reads the initial
+        // state while the last chunk writes last_state; the carry kernel copies it first)
+        p.fold = p.nchunk <= kFoldMaxChunks && allow_split;
         size_t cs = align256((size_t)(bsz * p.nchunk * D * N) * sizeof(float));
         size_t cd = align256((size_t)(bsz * p.nchunk * D) * sizeof(float));
         p.off_cstate = 0;
