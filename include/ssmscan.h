@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SSMSCAN_VERSION 14
+#define SSMSCAN_VERSION 15
 
 /* Bits of the `flags` argument of the scan entry points. */
 #define SSM_SCAN_SOFTPLUS 1     /* step size = softplus(delta + delta_bias) */
@@ -403,6 +403,25 @@ SSMSCAN_API int ssm_ssd_fwd_from(const float *initial_state, const void *x, cons
 SSMSCAN_API int ssm_step(float *state, const void *u, const void *delta, const float *A, const void *B,
              const void *C, const float *D, const void *z, void *y, const ssm_dims *dims,
              void *stream);
+
+/* The recurrent step continuing a sequence that ssm_scan_fwd / ssm_scan_fwd_from produced with
+ * activation flags (the prefill -> decode hand-over; recurrent form: shakilmahmud.com section 3;
+ * the step size softplus(linear(x)): azimuth.plus/paper/mamba, selection section; the exact
+ * zero-order hold: the same page, Theorem 1, and yapayzekasozluk.tr "Temel Matematiksel
+ * Cerceve").  Arguments as ssm_step, except:
+ *   delta      : [batch][dim] (io_dtype), the raw step-size input as ssm_scan_fwd takes it
+ *   delta_bias : [dim] fp32 or NULL (4-byte aligned)
+ *   flags      : SSM_SCAN_SOFTPLUS and / or SSM_SCAN_EXACT_ZOH, with the meaning they have for
+ *                the scan; any other bit -> SSM_ERR_FLAGS (checkpoints belong to a scan)
+ * The step size and the input term are formed with the scan kernel's arithmetic (the same
+ * functions, in the same order): after a one-pass prefill by the scan (chunk_len = -1, or a
+ * plan without the chunk carry) the steps continue the scan's state bitwise, and their outputs
+ * equal the scan's up to the summation order of the readout.  The caller
+ * owns every buffer; nothing is allocated; state is updated in place.  Returns SSM_OK or a
+ * negative ssm_status (nothing is launched on an error). */
+SSMSCAN_API int ssm_step_act(float *state, const void *u, const void *delta, const float *A, const void *B,
+             const void *C, const float *D, const void *z, const float *delta_bias, int flags, void *y,
+             const ssm_dims *dims, void *stream);
 
 /* Message describing the last non-OK status returned on this thread ("" if none). */
 SSMSCAN_API const char *ssm_last_error(void);

@@ -3,16 +3,16 @@
 #include "launch.h"
 
 namespace ssmlib {
-template int launch_step<1, float>(float *, const void *, const void *, const float *, const void *, const void *, const float *, const void *, void *, const ssm_dims *, hipStream_t);
-template int launch_step<2, float>(float *, const void *, const void *, const float *, const void *, const void *, const float *, const void *, void *, const ssm_dims *, hipStream_t);
-template int launch_step<4, float>(float *, const void *, const void *, const float *, const void *, const void *, const float *, const void *, void *, const ssm_dims *, hipStream_t);
-template int launch_step<8, float>(float *, const void *, const void *, const float *, const void *, const void *, const float *, const void *, void *, const ssm_dims *, hipStream_t);
-template int launch_step<16, float>(float *, const void *, const void *, const float *, const void *, const void *, const float *, const void *, void *, const ssm_dims *, hipStream_t);
-template int launch_step<1, uint16_t>(float *, const void *, const void *, const float *, const void *, const void *, const float *, const void *, void *, const ssm_dims *, hipStream_t);
-template int launch_step<2, uint16_t>(float *, const void *, const void *, const float *, const void *, const void *, const float *, const void *, void *, const ssm_dims *, hipStream_t);
-template int launch_step<4, uint16_t>(float *, const void *, const void *, const float *, const void *, const void *, const float *, const void *, void *, const ssm_dims *, hipStream_t);
-template int launch_step<8, uint16_t>(float *, const void *, const void *, const float *, const void *, const void *, const float *, const void *, void *, const ssm_dims *, hipStream_t);
-template int launch_step<16, uint16_t>(float *, const void *, const void *, const float *, const void *, const void *, const float *, const void *, void *, const ssm_dims *, hipStream_t);
+template int launch_step<1, float>(float *, const void *, const void *, const float *, const void *, const void *, const float *, const void *, void *, const ssm_dims *, hipStream_t, const float *, int, int);
+template int launch_step<2, float>(float *, const void *, const void *, const float *, const void *, const void *, const float *, const void *, void *, const ssm_dims *, hipStream_t, const float *, int, int);
+template int launch_step<4, float>(float *, const void *, const void *, const float *, const void *, const void *, const float *, const void *, void *, const ssm_dims *, hipStream_t, const float *, int, int);
+template int launch_step<8, float>(float *, const void *, const void *, const float *, const void *, const void *, const float *, const void *, void *, const ssm_dims *, hipStream_t, const float *, int, int);
+template int launch_step<16, float>(float *, const void *, const void *, const float *, const void *, const void *, const float *, const void *, void *, const ssm_dims *, hipStream_t, const float *, int, int);
+template int launch_step<1, uint16_t>(float *, const void *, const void *, const float *, const void *, const void *, const float *, const void *, void *, const ssm_dims *, hipStream_t, const float *, int, int);
+template int launch_step<2, uint16_t>(float *, const void *, const void *, const float *, const void *, const void *, const float *, const void *, void *, const ssm_dims *, hipStream_t, const float *, int, int);
+template int launch_step<4, uint16_t>(float *, const void *, const void *, const float *, const void *, const void *, const float *, const void *, void *, const ssm_dims *, hipStream_t, const float *, int, int);
+template int launch_step<8, uint16_t>(float *, const void *, const void *, const float *, const void *, const void *, const float *, const void *, void *, const ssm_dims *, hipStream_t, const float *, int, int);
+template int launch_step<16, uint16_t>(float *, const void *, const void *, const float *, const void *, const void *, const float *, const void *, void *, const ssm_dims *, hipStream_t, const float *, int, int);
 
 template int launch_conv<float>(int, bool, const void *, const float *, const float *, const void *, void *, void *,
                                 const ssm_dims *, hipStream_t);

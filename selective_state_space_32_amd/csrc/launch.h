@@ -201,9 +201,20 @@ int launch_scan(const void *u, const void *delta, const float *A, const void *B,
     return ok();
 }
 
+// act: 0 -- delta is the activated step size; 1 -- the raw input, activated as the scan does
+// (bias, softplus); 2 -- as 1 with the exact zero-order-hold input term.
+template <int N, typename IO, int ACT, bool VP>
+void launch_step_kernel(dim3 grid, hipStream_t st, float *state, const IO *u, const IO *dl, const float *A,
+                        const IO *B, const IO *C, const float *Dv, const IO *z, IO *y, const ssm_dims *dm,
+                        const float *bias, int softplus) {
+    hipLaunchKernelGGL((ssm::step_kernel<N, IO, VP, ACT>), grid, dim3(256), 0, st, state, u, dl, A, B, C, Dv, z, y,
+                       dm->batch, dm->dim, bias, softplus);
+}
+
 template <int N, typename IO>
 int launch_step(float *state, const void *u, const void *delta, const float *A, const void *B,
-                const void *C, const float *Dv, const void *z, void *y, const ssm_dims *dm, hipStream_t st) {
+                const void *C, const float *Dv, const void *z, void *y, const ssm_dims *dm, hipStream_t st,
+                const float *bias, int softplus, int act) {
     constexpr int G = N >= 4 ? N / 4 : 1;
     constexpr int SP = ssm::kStepSeqPerThread;
     const int64_t threads = (dm->batch + SP - 1) / SP * dm->dim * G;
@@ -214,12 +225,16 @@ int launch_step(float *state, const void *u, const void *delta, const float *A, 
     const IO *u_ = static_cast<const IO *>(u), *dl_ = static_cast<const IO *>(delta);
     const IO *B_ = static_cast<const IO *>(B), *C_ = static_cast<const IO *>(C), *z_ = static_cast<const IO *>(z);
     IO *y_ = static_cast<IO *>(y);
-    if (vp)
-        hipLaunchKernelGGL((ssm::step_kernel<N, IO, true>), grid, dim3(256), 0, st, state, u_, dl_, A, B_, C_, Dv,
-                           z_, y_, dm->batch, dm->dim);
-    else
-        hipLaunchKernelGGL((ssm::step_kernel<N, IO, false>), grid, dim3(256), 0, st, state, u_, dl_, A, B_, C_, Dv,
-                           z_, y_, dm->batch, dm->dim);
+    if (act == 0) {
+        if (vp) launch_step_kernel<N, IO, 0, true>(grid, st, state, u_, dl_, A, B_, C_, Dv, z_, y_, dm, nullptr, 0);
+        else launch_step_kernel<N, IO, 0, false>(grid, st, state, u_, dl_, A, B_, C_, Dv, z_, y_, dm, nullptr, 0);
+    } else if (act == 1) {
+        if (vp) launch_step_kernel<N, IO, 1, true>(grid, st, state, u_, dl_, A, B_, C_, Dv, z_, y_, dm, bias, softplus);
+        else launch_step_kernel<N, IO, 1, false>(grid, st, state, u_, dl_, A, B_, C_, Dv, z_, y_, dm, bias, softplus);
+    } else {
+        if (vp) launch_step_kernel<N, IO, 2, true>(grid, st, state, u_, dl_, A, B_, C_, Dv, z_, y_, dm, bias, softplus);
+        else launch_step_kernel<N, IO, 2, false>(grid, st, state, u_, dl_, A, B_, C_, Dv, z_, y_, dm, bias, softplus);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(SSM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -56,7 +56,7 @@ unsigned long long handover_wait_ticks() {
                                            const ConvArgs *, float *, const int32_t *); \
     extern template int launch_step<N, IO>(float *, const void *, const void *, const float *, const void *, \
                                            const void *, const float *, const void *, void *, const ssm_dims *, \
-                                           hipStream_t); \
+                                           hipStream_t, const float *, int, int); \
     extern template int launch_bwd<N, IO>(const BwdArgs &, const ssm_dims *, const Plan &, size_t, void *, hipStream_t);
 #define SSM_EXTERN_IO(IO) SSM_EXTERN_N(1, IO) SSM_EXTERN_N(2, IO) SSM_EXTERN_N(4, IO) SSM_EXTERN_N(8, IO) \
     SSM_EXTERN_N(16, IO)
@@ -230,13 +230,14 @@ int dispatch_scan(int64_t N, const void *u, const void *delta, const float *A, c
 
 template <typename IO>
 int dispatch_step(int64_t N, float *state, const void *u, const void *delta, const float *A, const void *B,
-                  const void *C, const float *Dv, const void *z, void *y, const ssm_dims *dm, hipStream_t st) {
+                  const void *C, const float *Dv, const void *z, void *y, const ssm_dims *dm, hipStream_t st,
+                  const float *bias, int softplus, int act) {
     switch (N) {
-        case 1: return launch_step<1, IO>(state, u, delta, A, B, C, Dv, z, y, dm, st);
-        case 2: return launch_step<2, IO>(state, u, delta, A, B, C, Dv, z, y, dm, st);
-        case 4: return launch_step<4, IO>(state, u, delta, A, B, C, Dv, z, y, dm, st);
-        case 8: return launch_step<8, IO>(state, u, delta, A, B, C, Dv, z, y, dm, st);
-        case 16: return launch_step<16, IO>(state, u, delta, A, B, C, Dv, z, y, dm, st);
+        case 1: return launch_step<1, IO>(state, u, delta, A, B, C, Dv, z, y, dm, st, bias, softplus, act);
+        case 2: return launch_step<2, IO>(state, u, delta, A, B, C, Dv, z, y, dm, st, bias, softplus, act);
+        case 4: return launch_step<4, IO>(state, u, delta, A, B, C, Dv, z, y, dm, st, bias, softplus, act);
+        case 8: return launch_step<8, IO>(state, u, delta, A, B, C, Dv, z, y, dm, st, bias, softplus, act);
+        case 16: return launch_step<16, IO>(state, u, delta, A, B, C, Dv, z, y, dm, st, bias, softplus, act);
     }
     return fail(SSM_ERR_UNSUPPORTED_N, "dstate %lld not supported", (long long)N);
 }
@@ -282,6 +283,10 @@ int bwd_impl(const float *initial_state, const int32_t *seq_lens, const void *u,
              const void *dy, const float *dlast_state, void *du, void *ddelta, float *dA, float *dB, float *dC,
              float *dD, void *dz, float *ddelta_bias, float *dinitial_state, const ssm_dims *dims, void *workspace,
              size_t workspace_bytes, void *stream);
+// The step's entry (ssm_step and ssm_step_act).
+int step_impl(float *state, const void *u, const void *delta, const float *A, const void *B, const void *C,
+              const float *D, const void *z, const float *delta_bias, int flags, void *y, const ssm_dims *dims,
+              void *stream, bool act);
 
 }  // namespace
 
@@ -477,21 +482,13 @@ int ssm_scan_fwd_conv(const void *x, const float *conv_w, const float *conv_b, i
 
 int ssm_step(float *state, const void *u, const void *delta, const float *A, const void *B,
              const void *C, const float *D, const void *z, void *y, const ssm_dims *dims, void *stream) {
-    int rc = check_dims(dims, false);
-    if (rc != SSM_OK) return rc;
-    const int64_t S = dims->batch, Dm = dims->dim, N = dims->dstate;
-    if (S == 0 || Dm == 0) return ok();
-    if (!state || !u || !delta || !A || !B || !C || !y)
-        return fail(SSM_ERR_NULL, "required pointer is NULL (state=%p u=%p delta=%p A=%p B=%p C=%p y=%p)",
-                    (void *)state, u, delta, (const void *)A, B, C, y);
-    const size_t es = dims->io_dtype == SSM_IO_BF16 ? 2 : 4;
-    if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) || !aligned(y, es) ||
-        (z && !aligned(z, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) || !aligned(state, N >= 4 ? 16 : 4))
-        return fail(SSM_ERR_ALIGN, "a tensor pointer is not aligned (state needs 16 bytes when dstate >= 4)");
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (dims->io_dtype == SSM_IO_BF16)
-        return dispatch_step<uint16_t>(N, state, u, delta, A, B, C, D, z, y, dims, st);
-    return dispatch_step<float>(N, state, u, delta, A, B, C, D, z, y, dims, st);
+    return step_impl(state, u, delta, A, B, C, D, z, nullptr, 0, y, dims, stream, false);
+}
+
+int ssm_step_act(float *state, const void *u, const void *delta, const float *A, const void *B, const void *C,
+                 const float *D, const void *z, const float *delta_bias, int flags, void *y, const ssm_dims *dims,
+                 void *stream) {
+    return step_impl(state, u, delta, A, B, C, D, z, delta_bias, flags, y, dims, stream, true);
 }
 
 size_t ssm_scan_bwd_workspace_bytes(const ssm_dims *dims) {
@@ -523,6 +520,33 @@ int ssm_scan_bwd_varlen(const float *initial_state, const int32_t *seq_lens, con
 }  // extern "C"
 
 namespace {
+
+// ssm_step (activated step size, act = false) and ssm_step_act (the raw input with the scan's
+// activation flags).
+int step_impl(float *state, const void *u, const void *delta, const float *A, const void *B, const void *C,
+              const float *D, const void *z, const float *delta_bias, int flags, void *y, const ssm_dims *dims,
+              void *stream, bool act) {
+    int rc = check_dims(dims, false);
+    if (rc != SSM_OK) return rc;
+    if (flags & ~(SSM_SCAN_SOFTPLUS | SSM_SCAN_EXACT_ZOH))
+        return fail(SSM_ERR_FLAGS, "flags 0x%x: a step takes SSM_SCAN_SOFTPLUS and SSM_SCAN_EXACT_ZOH only", flags);
+    const int64_t S = dims->batch, Dm = dims->dim, N = dims->dstate;
+    if (S == 0 || Dm == 0) return ok();
+    if (!state || !u || !delta || !A || !B || !C || !y)
+        return fail(SSM_ERR_NULL, "required pointer is NULL (state=%p u=%p delta=%p A=%p B=%p C=%p y=%p)",
+                    (void *)state, u, delta, (const void *)A, B, C, y);
+    const size_t es = dims->io_dtype == SSM_IO_BF16 ? 2 : 4;
+    if (!aligned(u, es) || !aligned(delta, es) || !aligned(B, es) || !aligned(C, es) || !aligned(y, es) ||
+        (z && !aligned(z, es)) || !aligned(A, 4) || (D && !aligned(D, 4)) || (delta_bias && !aligned(delta_bias, 4)) ||
+        !aligned(state, N >= 4 ? 16 : 4))
+        return fail(SSM_ERR_ALIGN, "a tensor pointer is not aligned (state needs 16 bytes when dstate >= 4)");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int mode = !act ? 0 : (flags & SSM_SCAN_EXACT_ZOH) ? 2 : 1;
+    const int softplus = (flags & SSM_SCAN_SOFTPLUS) ? 1 : 0;
+    if (dims->io_dtype == SSM_IO_BF16)
+        return dispatch_step<uint16_t>(N, state, u, delta, A, B, C, D, z, y, dims, st, delta_bias, softplus, mode);
+    return dispatch_step<float>(N, state, u, delta, A, B, C, D, z, y, dims, st, delta_bias, softplus, mode);
+}
 
 int bwd_impl(const float *initial_state, const int32_t *seq_lens, const void *u, const void *delta, const float *A,
              const void *B, const void *C, const float *D, const void *z, const float *delta_bias, int flags,

@@ -21,12 +21,19 @@ constexpr int kStepSeqPerThread = 2;
 
 // VP: the A, B and C slices of a lane are read as one vector each (needs 16-byte aligned A
 // and B / C aligned to NS elements); otherwise element by element.
-template <int N, typename IO, bool VP>
+// ACT: 0 -- delta is the step size itself (already activated);
+//      1 -- delta is the raw step-size input, as the scan takes it: the step size is
+//           softplus(delta + bias) (softplus != 0) or delta + bias (bias nullable), formed with
+//           the scan kernel's own functions (the short softplus for bf16 I/O), so that a
+//           prefilled sequence continues with the step sizes the scan would have used;
+//      2 -- as 1, with the exact zero-order-hold input term (exp(delta A) - 1) / A * B * u of
+//           the scan's SSM_SCAN_EXACT_ZOH path (zoh_weight, from the same exponent and decay).
+template <int N, typename IO, bool VP, int ACT = 0>
 __global__ void __launch_bounds__(256)
 step_kernel(float *__restrict__ state, const IO *__restrict__ u, const IO *__restrict__ delta,
             const float *__restrict__ A, const IO *__restrict__ B, const IO *__restrict__ C,
             const float *__restrict__ Dv, const IO *__restrict__ z, IO *__restrict__ y,
-            int64_t S, int64_t D) {
+            int64_t S, int64_t D, const float *__restrict__ bias = nullptr, int softplus = 0) {
     constexpr int NS = N < 4 ? N : 4;      // states per lane
     constexpr int G = N / NS;              // lanes per (s, d)
     constexpr int SP = kStepSeqPerThread;  // sequences per thread
@@ -47,6 +54,12 @@ step_kernel(float *__restrict__ state, const IO *__restrict__ u, const IO *__res
         for (int i = 0; i < NS; ++i) a2[i] = A[d * N + part * NS + i] * kLog2e;
     }
     const float Dd = Dv ? Dv[d] : 0.0f;
+    const float bd = (ACT > 0 && bias) ? bias[d] : 0.0f;
+    float inv_a[ACT == 2 ? NS : 1];   // 1 / A for the exact zero-order hold
+    if constexpr (ACT == 2) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) inv_a[i] = 1.0f / A[d * N + part * NS + i];
+    }
 
     // loads of all SP sequences first (indices clamped in bounds; rows past S are not used)
     float h[SP][NS];
@@ -91,13 +104,20 @@ step_kernel(float *__restrict__ state, const IO *__restrict__ u, const IO *__res
 #pragma unroll
     for (int j = 0; j < SP; ++j) {
         const bool act = s0 + j < S;        // the same for the G lanes of a group
-        const float k = dt[j] * uu[j];
+        if constexpr (ACT > 0) {
+            const float x = dt[j] + bd;
+            dt[j] = softplus ? (sizeof(IO) == 2 ? softplus_short_f32(x) : softplus_f32(x)) : x;
+        }
+        const float k = ACT == 2 ? uu[j] : dt[j] * uu[j];
         float acc = 0.0f;
         float hn[NS];
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
-            const float e = hw_exp2(dt[j] * a2[i]);
-            hn[i] = fmaf(e, h[j][i], k * Bv[j][i]);
+            const float ya = dt[j] * a2[i];
+            const float e = hw_exp2(ya);
+            float bu = k * Bv[j][i];
+            if constexpr (ACT == 2) bu *= zoh_weight(ya, e, dt[j], inv_a[i]);
+            hn[i] = fmaf(e, h[j][i], bu);
             acc = fmaf(Cv[j][i], hn[i], acc);
         }
         const int64_t pair = (s0 + j) * D + d;

@@ -78,6 +78,8 @@ def _load() -> ctypes.CDLL:
     lib.ssm_scan_bwd_varlen.restype = ctypes.c_int
     lib.ssm_step.argtypes = [P, P, P, P, P, P, P, P, P, D, P]
     lib.ssm_step.restype = ctypes.c_int
+    lib.ssm_step_act.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_int, P, D, P]
+    lib.ssm_step_act.restype = ctypes.c_int
     lib.ssm_conv1d_fwd.argtypes = [P, P, P, ctypes.c_int, P, ctypes.c_int, P, P, D, P]
     lib.ssm_conv1d_fwd.restype = ctypes.c_int
     lib.ssm_conv1d_bwd.argtypes = [P, P, P, ctypes.c_int, P, ctypes.c_int, P, P, P, P, P, D, P]
@@ -423,7 +425,8 @@ def _bwd_outputs(bsz, L, dim, N, io, dev, gate, skip, bias, want_h0):
     return g
 
 
-def _step_args(state, u, delta, A, B, C, D, z, y, stream):
+def _step_args(state, u, delta, A, B, C, D, z, y, stream, act=None):
+    """Arguments of ssm_step, or (act = (delta_bias, flags)) of ssm_step_act."""
     S, dim, N = state.shape
     dev, io = u.device, u.dtype
     _io_code(io)
@@ -442,21 +445,37 @@ def _step_args(state, u, delta, A, B, C, D, z, y, stream):
     else:
         _need(y, "y", (S, dim), io, dev)
     dims = make_dims(S, 1, dim, N, io)
-    args = (_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y),
-            ctypes.byref(dims), _stream_handle(stream))
-    keep = (state, u, delta, A, B, C, D, z, y, dims)
+    if act is None:
+        args = (_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y),
+                ctypes.byref(dims), _stream_handle(stream))
+        keep = (state, u, delta, A, B, C, D, z, y, dims)
+    else:
+        bias, flags = act
+        if bias is not None:
+            _need(bias, "delta_bias", (dim,), torch.float32, dev)
+        args = (_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(bias),
+                int(flags), _ptr(y), ctypes.byref(dims), _stream_handle(stream))
+        keep = (state, u, delta, A, B, C, D, z, bias, y, dims)
     return args, keep, y
 
 
 def step(state: torch.Tensor, u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
          C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None, *,
+         delta_bias: Optional[torch.Tensor] = None, softplus: bool = False, exact_zoh: bool = False,
          y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """One recurrent step (ssm_step); `state` (S, dim, N) float32 is updated in place.
+    """One recurrent step; `state` (S, dim, N) float32 is updated in place.
 
-    u, delta, z: (S, dim); B, C: (S, N) of one dtype; delta is the activated step size.
+    u, delta, z: (S, dim); B, C: (S, N) of one dtype.  Without delta_bias, softplus and
+    exact_zoh, delta is the activated step size (ssm_step); with any of them delta is the raw
+    input and the step size and input term are formed as the scan forms them (ssm_step_act).
     Returns y (S, dim)."""
-    args, _keep, y = _step_args(state, u, delta, A, B, C, D, z, y, stream)
-    _check(lib.ssm_step(*args))
+    if delta_bias is None and not softplus and not exact_zoh:
+        args, _keep, y = _step_args(state, u, delta, A, B, C, D, z, y, stream)
+        _check(lib.ssm_step(*args))
+        return y
+    flags = (SCAN_SOFTPLUS if softplus else 0) | (SCAN_EXACT_ZOH if exact_zoh else 0)
+    args, _keep, y = _step_args(state, u, delta, A, B, C, D, z, y, stream, act=(delta_bias, flags))
+    _check(lib.ssm_step_act(*args))
     return y
 
 

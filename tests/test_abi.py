@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
     syms = set(declared_symbols())
     assert {"ssm_scan_fwd", "ssm_scan_fwd_from", "ssm_scan_bwd", "ssm_scan_bwd_workspace_bytes", "ssm_step",
             "ssm_conv1d_fwd", "ssm_conv1d_bwd", "ssm_scan_fwd_conv", "ssm_ssd_fwd", "ssm_ssd_fwd_from", "ssm_scan_bwd_varlen",
-            "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_last_error", "ssm_version"} <= syms
+            "ssm_scan_workspace_bytes", "ssm_scan_plan", "ssm_last_error", "ssm_version", "ssm_step_act"} <= syms
 
 
 def test_library_exports_every_declared_symbol():
@@ -234,6 +234,22 @@ def test_step_validation(b):
     assert b.lib.ssm_step(None, *args[1:], ctypes.byref(d), None) == -1
     assert b.lib.ssm_step(P(FAKE + 4), *args[1:], ctypes.byref(d), None) == -4   # state needs 16 B
     assert b.lib.ssm_step(*args, ctypes.byref(_dims(b, dstate=6)), None) == -5
+
+
+def test_step_act_validation(b):
+    P = ctypes.c_void_p
+    d = _dims(b, seqlen=1)
+    rest = [P(FAKE)] * 5 + [None, None]   # u, delta, A, B, C, D, z
+
+    def call(flags, bias=None, dims=d, state=P(FAKE)):
+        return b.lib.ssm_step_act(state, *rest, bias, flags, P(FAKE), ctypes.byref(dims), None)
+    assert call(4) == -8                      # checkpoints belong to a scan
+    assert b"SSM_SCAN_EXACT_ZOH" in b.lib.ssm_last_error()
+    assert call(8) == -8                      # unknown bit
+    assert call(1, bias=P(FAKE + 2)) == -4    # delta_bias must be 4-byte aligned
+    assert call(3, state=None) == -1
+    assert call(1, state=P(FAKE + 4)) == -4   # state needs 16 bytes when dstate >= 4
+    assert call(2, dims=_dims(b, dstate=6)) == -5
 
 
 def test_empty_problems_are_noops(b):
