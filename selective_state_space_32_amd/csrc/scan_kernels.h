@@ -161,9 +161,12 @@ scan_chunk_kernel(const IO *__restrict__ u, const IO *__restrict__ delta,
     static_assert(T % K == 0 && J % V == 0 && RPP * P == T, "tile must split evenly over the threads");
     using VIO = vec<V, IO>;
     constexpr int W = VEC ? V * (int)sizeof(IO) / 4 : 1;
-    // token loop pipelining: groups of G tokens; B / C slices read as BW 32-bit words
+    // token loop pipelining: groups of G tokens; B / C slices read as BW 32-bit words.  Two
+    // groups' slices of B and C live in SGPRs: 32 of them for bf16 at four tokens a group; fp32
+    // slices take twice the words, so their groups are two tokens (at four, the 64 SGPRs spilled
+    // into VGPR lanes inside the loop: B2 L2048 D1536 fp32 61.2 us against 62.8)
     constexpr bool PIPE = !(sizeof(IO) == 2 && S % 2 == 1) && T % 8 == 0;
-    constexpr int G = 4;
+    constexpr int G = (sizeof(IO) == 4 && S == 4) ? 2 : 4;
     constexpr int BW = PIPE ? S * (int)sizeof(IO) / 4 : 1;
     // (delta, delta*u) of token tt, channel c at s_dk[tt][sdk(c)]: the 16-byte channel pairs of
     // a row are XOR-permuted by (c / 8) % 8, so that the prep's pair writes (eight threads of a
