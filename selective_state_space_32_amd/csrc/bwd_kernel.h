@@ -56,6 +56,7 @@
 namespace ssm {
 
 constexpr int kBwdTile = kCkptEvery;   // tokens per backward tile: one checkpoint each
+constexpr int kPartBatch = 2;          // dB / dC sums stored per this many walked tokens
 
 template <int N> struct BwdShape {
     static constexpr int S = N < 4 ? N : 4;   // states per wave
@@ -387,7 +388,7 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
         //   dB = lambda delta u,   dC = dp h_t.
         // The dB / dC sums over the wave's 64 channels are reduced across lanes in registers
         // (lanes_reduce_scatter); the last lane of group rk writes entry rk to LDS.
-        float rvp[NV];
+        float rvp[NV], parts[T];
 #pragma unroll
         for (int tt = T - 1; tt >= 0; --tt) {
             const f32x2_t dk = s_dk[tt][lane];   // (delta, delta*u)
@@ -424,8 +425,15 @@ scan_bwd_kernel(const IO *__restrict__ u, const IO *__restrict__ delta, const IO
             }
             s_du[w][tt][lane] = ZOH ? q : dk.x * q;
             s_dd[w][tt][lane] = fmaf(ud.x, ZOH ? qe : q, ddA * kLn2);
-            const float part = lanes_reduce_scatter<NV>(rvp, lane);
-            if (rgrp == LPV - 1) s_dbc[tt][rk < S ? 0 : 1][w * S + rk % S] = part;
+            parts[tt] = lanes_reduce_scatter<NV>(rvp, lane);
+            // (stored every kPartBatch tokens: a lane-masked store per token splits the unrolled
+            // walk and serializes each token's DPP chain behind its wait states -- 38 s_nop per
+            // tile, 16 in pairs; B8 L2048 D5120 N16 bf16 backward 1,344 -> 1,333 us -- while all
+            // eight held to the end spill to scratch at the 168-register bound)
+            if (tt % kPartBatch == 0 && rgrp == LPV - 1) {
+#pragma unroll
+                for (int k = 0; k < kPartBatch; ++k) s_dbc[tt + k][rk < S ? 0 : 1][w * S + rk % S] = parts[tt + k];
+            }
         }
         __syncthreads();
 
