@@ -66,6 +66,18 @@ struct ConvArgs {
     void *u_out;
 };
 
+// Whether three workgroups of a kernel fit on a CU: the split schedule's balance assumes it.
+// (Asked of the runtime once per instantiation; on an error the assumption stands and the
+// error is cleared so that it is not reported by the next launch.)
+inline bool three_per_cu(const void *kernel, int block) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return true;
+    }
+    return n >= 3;
+}
+
 // (CK: the full pass also stores the backward pass's checkpoints to ckpt)
 template <int N, int T, typename IO, bool VEC, bool ZOH, int CW, bool CK>
 void launch_scan_kernels_t(const IO *u, const IO *dl, const float *A, const IO *B, const IO *C, const float *Dv,
@@ -97,7 +109,13 @@ void launch_scan_kernels_t(const IO *u, const IO *dl, const float *A, const IO *
                                cstate, (const float *)cdsum, A, h0, D, nc, col_tiles);
         }
     }
-    if (p.schedule == kSplit) {
+    // An instantiation that needs more registers than three workgroups per CU allow (the fp32
+    // fused convolution's) runs a split plan as the one-pass grid, whose outputs are the same:
+    // at two per CU the halves queue behind the whole tiles (B8 L2048 D5120 fp32: 615 us split,
+    // 570 us one pass).  The plan then has one chunk of L tokens.
+    static const bool split_fits = three_per_cu(
+        reinterpret_cast<const void *>(&ssm::scan_chunk_kernel<N, S, T, IO, ssm::kFull, VEC, ZOH, CW, CK>), 64 * K);
+    if (p.schedule == kSplit && split_fits) {
         // the hand-over flags start at zero (a fill kernel: no memset node if the caller captures a graph)
         int *flags = reinterpret_cast<int *>(static_cast<char *>(ws) + p.off_flags);
         float *hand = reinterpret_cast<float *>(static_cast<char *>(ws) + p.off_hand);
