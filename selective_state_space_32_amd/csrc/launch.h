@@ -337,8 +337,14 @@ int launch_bwd(const BwdArgs &a, const ssm_dims *dm, const Plan &sp, size_t ckpt
     if (!a.ckpt_given) {
         // (under the split schedule, as the forward: part of the tiles as two token halves, the
         // second started from the state the first hands over; the checkpoints are the same)
-        const unsigned groups = split ? (unsigned)(sp.n_full + 2 * sp.n_split) : (unsigned)n_tiles;
+        // (a kernel that cannot hold three workgroups per CU runs the one-pass grid instead)
         auto ckpt_pass = [&](auto vec_c, auto zoh_c) {
+            static const bool fits = three_per_cu(
+                reinterpret_cast<const void *>(&ssm::scan_chunk_kernel<N, S, T, IO, ssm::kCheckpoint,
+                                                                      decltype(vec_c)::value, decltype(zoh_c)::value>),
+                64 * K);
+            const bool split = sp.schedule == kSplit && fits;
+            const unsigned groups = split ? (unsigned)(sp.n_full + 2 * sp.n_split) : (unsigned)n_tiles;
             hipLaunchKernelGGL((ssm::scan_chunk_kernel<N, S, T, IO, ssm::kCheckpoint, decltype(vec_c)::value,
                                                        decltype(zoh_c)::value>),
                                dim3(groups, 1), dim3(64 * K), 0, st, u, dl, (const IO *)nullptr, (IO *)nullptr, a.A,
@@ -358,9 +364,15 @@ int launch_bwd(const BwdArgs &a, const ssm_dims *dm, const Plan &sp, size_t ckpt
     // the reverse walk; 16-byte (or 8-byte) element access when every (token, channel) tensor allows it
     const bool vb = D % 8 == 0 && aligned(u, 16) && aligned(dl, 16) && aligned(dy, 16) && aligned(du, 16) &&
                     aligned(ddl, 16) && (!z || (aligned(z, 16) && aligned(dz, 16)));
-    // (under the split schedule too: the later half of a split tile hands the adjoint over)
-    const unsigned wgroups = split ? (unsigned)(sp.n_full + 2 * sp.n_split) : (unsigned)n_tiles;
+    // (under the split schedule too: the later half of a split tile hands the adjoint over;
+    // the one-pass grid where three workgroups of the kernel do not fit on a CU)
     auto walk = [&](auto vec_c, auto zoh_c) {
+        static const bool fits = three_per_cu(
+            reinterpret_cast<const void *>(
+                &ssm::scan_bwd_kernel<N, IO, decltype(vec_c)::value, decltype(zoh_c)::value>),
+            64 * KB);
+        const bool split = sp.schedule == kSplit && fits;
+        const unsigned wgroups = split ? (unsigned)(sp.n_full + 2 * sp.n_split) : (unsigned)n_tiles;
         hipLaunchKernelGGL((ssm::scan_bwd_kernel<N, IO, decltype(vec_c)::value, decltype(zoh_c)::value>),
                            dim3(wgroups), dim3(64 * KB), 0, st, u, dl, z, dy, a.A, a.D, a.bias, B, C, ckpt, a.dlast, du,
                            ddl, dz, a.dA, a.dB, a.dC, a.dD, a.dbias, a.dh0, L, D, tiles_per_b, a.softplus,
